@@ -1,0 +1,390 @@
+/*
+ * rans_oracle.c -- plain, single-threaded CPU reference of indexed rANS64.
+ *
+ * TEST INFRASTRUCTURE ONLY (see rans_oracle.h): called by the tests, the
+ * smoke check and the benchmark's CPU-baseline leg, never by the product.
+ *
+ * The pages name the coder but do not print its procedure:
+ *   - kompressor README, "Why" and "Credits": a faithful port of CompressAI's
+ *     rANS coder, 64-bit rANS in the style of ryg_rans;
+ *   - torch_ans 0.3.0, "Usage" table: rans64 has a 64-bit state, 32-bit
+ *     stream words and at most 16 frequency bits, and in the legend
+ *     State Bits > Stream Bits + Max Freq Bits;
+ *   - torch_ans 0.3.0, "Low-level API Reference", rans*_push: symbols are
+ *     chosen per position by an index into batched CDF tables with sizes and
+ *     offsets; the coded range is [offset, offset + cdf_size - 2); a symbol
+ *     outside it is zig-zag encoded into a raw value and sent by bypass
+ *     coding with bypass_precision bits at a time;
+ *   - kompressor BENCHMARKS.md, section 4: CompressAI's decoder finds the
+ *     symbol by a linear scan of the CDF row (std::find_if) -- this oracle
+ *     does exactly that, the plainest lookup there is.
+ *
+ * Readings taken where the pages are silent (each listed again in DESIGN):
+ *   R1  state interval [L0, 2^63) with L0 = 2^31, the interval of 64-bit
+ *       ryg_rans with 32-bit output; with 16-bit precision a REG put
+ *       renormalises when x >= f * 2^47 and a 4-bit put when x >= 2^59;
+ *   R3  the encoder starts every lane at x = L0, so a clean decode ends at
+ *       x = L0 with every lane word consumed;
+ *   R4  bypass_precision = 4;
+ *   R5  the raw value is sent as a count of 4-bit groups nb (base-15
+ *       continuation: 15 means "add the next group"), then the nb groups
+ *       least significant first; raw < 2^31 so nb <= 8;
+ *   R6  zig-zag: v < 0 -> raw = -2v-1 (odd); v >= mv -> raw = 2(v-mv) (even);
+ *   R7  a 4-bit put is x <- 16x + b (not a REG put with frequency 2^12);
+ *   R8  raw >= 2^31 is rejected with ORACLE_E_SYMBOL_RANGE;
+ *   R9  the terminal CDF entry is exactly 65536 and every frequency >= 1;
+ *   R10 lane j covers [floor(j n / L), floor((j+1) n / L));
+ *   R11 container [L, end_0..end_{L-1}] + lane streams;
+ *   R2  each lane stream starts with the final state as two words (low then
+ *       high), followed by the renormalisation words in the order the
+ *       decoder consumes them (the reverse of the order they were emitted).
+ */
+#include "rans_oracle.h"
+
+#include <stdlib.h>
+#include <string.h>
+
+#define PREC 16u
+#define TOTAL_FREQ (1u << PREC)
+#define STATE_LOW (1ull << 31)      /* L0 */
+#define BYPASS_BITS 4u
+#define BYPASS_MAX 15u              /* 2^BYPASS_BITS - 1: count continuation */
+#define RAW_LIMIT (1ll << 31)
+
+uint64_t oracle_lane_begin(uint64_t n, uint32_t num_lanes, uint32_t j)
+{
+    /* floor(j * n / L) without overflow: n < 2^63 and j <= L < 2^32, so
+     * split n = a*L + b: j*n/L = j*a + j*b/L with j*b < 2^64. */
+    uint64_t a = n / num_lanes, b = n % num_lanes;
+    return (uint64_t)j * a + ((uint64_t)j * b) / num_lanes;
+}
+
+int oracle_check_tables(const int32_t *cdf, const int32_t *lengths,
+                        int32_t num_tables, int32_t stride)
+{
+    if (num_tables <= 0 || stride < 3)
+        return ORACLE_E_ARG;
+    for (int32_t r = 0; r < num_tables; ++r) {
+        int32_t len = lengths[r];
+        const int32_t *row = cdf + (int64_t)r * stride;
+        if (len < 3 || len > stride)
+            return ORACLE_E_TABLE;
+        if (row[0] != 0 || row[len - 1] != (int32_t)TOTAL_FREQ)
+            return ORACLE_E_TABLE;
+        for (int32_t k = 0; k + 1 < len; ++k)
+            if (row[k + 1] <= row[k])
+                return ORACLE_E_TABLE;
+    }
+    return ORACLE_OK;
+}
+
+/* One elementary coding step, in the order the decoder meets it. */
+typedef struct {
+    uint32_t start;   /* REG: cumulative frequency; BITS: the 4-bit value */
+    uint32_t freq;    /* REG: frequency; BITS: 0 */
+} put_t;
+
+typedef struct {
+    put_t *v;
+    size_t n, cap;
+} put_list;
+
+static int put_push(put_list *l, uint32_t start, uint32_t freq)
+{
+    if (l->n == l->cap) {
+        size_t nc = l->cap ? 2 * l->cap : 64;
+        put_t *nv = (put_t *)realloc(l->v, nc * sizeof(put_t));
+        if (!nv)
+            return ORACLE_E_ARG;
+        l->v = nv;
+        l->cap = nc;
+    }
+    l->v[l->n].start = start;
+    l->v[l->n].freq = freq;
+    l->n++;
+    return ORACLE_OK;
+}
+
+/* Forward-order puts of one symbol (torch_ans rans*_push range rule). */
+static int symbol_puts(put_list *l, int32_t symbol, int32_t index,
+                       const int32_t *cdf, const int32_t *lengths,
+                       const int32_t *offsets, int32_t num_tables, int32_t stride)
+{
+    if (index < 0 || index >= num_tables)
+        return ORACLE_E_INDEX;
+    const int32_t *row = cdf + (int64_t)index * stride;
+    int64_t mv = (int64_t)lengths[index] - 2;  /* escape slot */
+    int64_t v = (int64_t)symbol - (int64_t)offsets[index];
+    int64_t raw = 0;
+    int escape = 0;
+    if (v < 0) {
+        raw = -2 * v - 1;
+        v = mv;
+        escape = 1;
+    } else if (v >= mv) {
+        raw = 2 * (v - mv);
+        v = mv;
+        escape = 1;
+    }
+    if (raw >= RAW_LIMIT)
+        return ORACLE_E_SYMBOL_RANGE;
+    int rc = put_push(l, (uint32_t)row[v], (uint32_t)(row[v + 1] - row[v]));
+    if (rc)
+        return rc;
+    if (escape) {
+        uint32_t nb = 0;
+        while (nb < 16 && ((uint64_t)raw >> (BYPASS_BITS * nb)) != 0)
+            ++nb;
+        uint32_t t = nb;
+        while (t >= BYPASS_MAX) {
+            if ((rc = put_push(l, BYPASS_MAX, 0)))
+                return rc;
+            t -= BYPASS_MAX;
+        }
+        if ((rc = put_push(l, t, 0)))
+            return rc;
+        for (uint32_t k = 0; k < nb; ++k)
+            if ((rc = put_push(l, (uint32_t)(((uint64_t)raw >> (BYPASS_BITS * k)) & BYPASS_MAX), 0)))
+                return rc;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_encode_lane(const int32_t *symbols, const int32_t *indexes,
+                       uint64_t begin, uint64_t end,
+                       const int32_t *cdf, const int32_t *lengths,
+                       const int32_t *offsets, int32_t num_tables, int32_t stride,
+                       uint32_t *out, uint64_t cap, uint64_t *words)
+{
+    put_list puts = {0, 0, 0};
+    int rc = ORACLE_OK;
+    for (uint64_t i = begin; i < end && rc == ORACLE_OK; ++i)
+        rc = symbol_puts(&puts, symbols[i], indexes[i], cdf, lengths, offsets,
+                         num_tables, stride);
+    if (rc) {
+        free(puts.v);
+        return rc;
+    }
+
+    /* Emitted words, in emission order; at most one per put. */
+    uint32_t *emitted = (uint32_t *)malloc((puts.n + 1) * sizeof(uint32_t));
+    if (!emitted) {
+        free(puts.v);
+        return ORACLE_E_ARG;
+    }
+    size_t ne = 0;
+    uint64_t x = STATE_LOW;
+    for (size_t k = puts.n; k-- > 0;) {
+        const put_t p = puts.v[k];
+        if (p.freq == 0) {
+            /* 4-bit put: keep 16x + b below 2^63. */
+            if (x >= (1ull << (63 - BYPASS_BITS))) {
+                emitted[ne++] = (uint32_t)x;
+                x >>= 32;
+            }
+            x = (x << BYPASS_BITS) + p.start;
+        } else {
+            /* REG put: keep floor(x/f)*2^16 + (x mod f) + start below 2^63. */
+            uint64_t x_max = (uint64_t)p.freq << (63 - PREC);
+            if (x >= x_max) {
+                emitted[ne++] = (uint32_t)x;
+                x >>= 32;
+            }
+            x = (x / p.freq) * TOTAL_FREQ + (x % p.freq) + p.start;
+        }
+    }
+    uint64_t total = 2 + ne;
+    *words = total;
+    if (total <= cap) {
+        out[0] = (uint32_t)x;
+        out[1] = (uint32_t)(x >> 32);
+        for (size_t k = 0; k < ne; ++k)
+            out[2 + k] = emitted[ne - 1 - k];
+    } else {
+        rc = ORACLE_E_CAPACITY;
+    }
+    free(emitted);
+    free(puts.v);
+    return rc;
+}
+
+typedef struct {
+    uint64_t x;
+    const uint32_t *w;
+    uint64_t pos, words;
+} dec_t;
+
+/* x < L0 after a step means the encoder emitted a word there: read it back. */
+static int dec_refill(dec_t *d)
+{
+    if (d->x < STATE_LOW) {
+        if (d->pos >= d->words)
+            return ORACLE_E_CORRUPT;
+        d->x = (d->x << 32) | d->w[d->pos++];
+    }
+    return ORACLE_OK;
+}
+
+static int dec_bits(dec_t *d, uint32_t *b)
+{
+    *b = (uint32_t)(d->x & BYPASS_MAX);
+    d->x >>= BYPASS_BITS;
+    return dec_refill(d);
+}
+
+int oracle_decode_lane(const uint32_t *lane, uint64_t words,
+                       const int32_t *indexes, uint64_t begin, uint64_t end,
+                       const int32_t *cdf, const int32_t *lengths,
+                       const int32_t *offsets, int32_t num_tables, int32_t stride,
+                       int32_t *symbols_out)
+{
+    if (words < 2)
+        return ORACLE_E_CORRUPT;
+    dec_t d;
+    d.x = (uint64_t)lane[0] | ((uint64_t)lane[1] << 32);
+    d.w = lane;
+    d.pos = 2;
+    d.words = words;
+    for (uint64_t i = begin; i < end; ++i) {
+        int32_t index = indexes[i];
+        if (index < 0 || index >= num_tables)
+            return ORACLE_E_INDEX;
+        const int32_t *row = cdf + (int64_t)index * stride;
+        int32_t len = lengths[index];
+        int64_t mv = (int64_t)len - 2;
+        uint32_t cum = (uint32_t)(d.x & (TOTAL_FREQ - 1));
+        /* linear scan: first entry above cum, minus one */
+        int32_t s = 0;
+        while (s + 1 < len && (uint32_t)row[s + 1] <= cum)
+            ++s;
+        uint32_t start = (uint32_t)row[s];
+        uint32_t freq = (uint32_t)(row[s + 1] - row[s]);
+        d.x = (uint64_t)freq * (d.x >> PREC) + cum - start;
+        if (dec_refill(&d))
+            return ORACLE_E_CORRUPT;
+        int64_t value = s;
+        if (s == mv) {
+            uint32_t t, nb;
+            if (dec_bits(&d, &t))
+                return ORACLE_E_CORRUPT;
+            nb = t;
+            while (t == BYPASS_MAX) {
+                if (dec_bits(&d, &t))
+                    return ORACLE_E_CORRUPT;
+                nb += t;
+                if (nb > 8)
+                    return ORACLE_E_CORRUPT;
+            }
+            if (nb > 8)
+                return ORACLE_E_CORRUPT;
+            uint64_t raw = 0;
+            for (uint32_t k = 0; k < nb; ++k) {
+                uint32_t b;
+                if (dec_bits(&d, &b))
+                    return ORACLE_E_CORRUPT;
+                raw |= (uint64_t)b << (BYPASS_BITS * k);
+            }
+            if (raw >= (uint64_t)RAW_LIMIT)
+                return ORACLE_E_CORRUPT;
+            if (raw & 1)
+                value = -(int64_t)(raw >> 1) - 1;
+            else
+                value = (int64_t)(raw >> 1) + mv;
+        }
+        int64_t sym = value + offsets[index];
+        if (sym < INT32_MIN || sym > INT32_MAX)
+            return ORACLE_E_CORRUPT;
+        symbols_out[i] = (int32_t)sym;
+    }
+    if (d.x != STATE_LOW || d.pos != d.words)
+        return ORACLE_E_CORRUPT;
+    return ORACLE_OK;
+}
+
+int oracle_encode(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                  const int32_t *cdf, const int32_t *lengths, const int32_t *offsets,
+                  int32_t num_tables, int32_t stride, uint32_t num_lanes,
+                  uint32_t *out, uint64_t cap, uint64_t *out_words)
+{
+    if (num_lanes == 0 || (n && (!symbols || !indexes)) || !cdf || !lengths || !offsets)
+        return ORACLE_E_ARG;
+    int rc = oracle_check_tables(cdf, lengths, num_tables, stride);
+    if (rc)
+        return rc;
+    uint64_t head = 1 + (uint64_t)num_lanes;
+    uint64_t used = 0;   /* payload words so far */
+    int cap_hit = 0;
+    uint32_t *scratch = NULL;
+    uint64_t scratch_cap = 0;
+    for (uint32_t j = 0; j < num_lanes; ++j) {
+        uint64_t b = oracle_lane_begin(n, num_lanes, j);
+        uint64_t e = oracle_lane_begin(n, num_lanes, j + 1);
+        /* a generous bound: each symbol makes at most 10 puts, one word each */
+        uint64_t need = 2 + 10 * (e - b);
+        if (need > scratch_cap) {
+            free(scratch);
+            scratch = (uint32_t *)malloc(need * sizeof(uint32_t));
+            if (!scratch)
+                return ORACLE_E_ARG;
+            scratch_cap = need;
+        }
+        uint64_t w = 0;
+        rc = oracle_encode_lane(symbols, indexes, b, e, cdf, lengths, offsets,
+                                num_tables, stride, scratch, scratch_cap, &w);
+        if (rc) {
+            free(scratch);
+            return rc;
+        }
+        if (head + used + w <= cap && !cap_hit)
+            memcpy(out + head + used, scratch, w * sizeof(uint32_t));
+        else
+            cap_hit = 1;
+        used += w;
+        if (used > 0xFFFFFFFFull) {
+            free(scratch);
+            return ORACLE_E_ARG;
+        }
+        if (1 + j < cap)
+            out[1 + j] = (uint32_t)used;
+    }
+    free(scratch);
+    if (cap >= 1)
+        out[0] = num_lanes;
+    *out_words = head + used;
+    return (cap_hit || head > cap) ? ORACLE_E_CAPACITY : ORACLE_OK;
+}
+
+int oracle_decode(const uint32_t *stream, uint64_t stream_words,
+                  const int32_t *indexes, uint64_t n,
+                  const int32_t *cdf, const int32_t *lengths, const int32_t *offsets,
+                  int32_t num_tables, int32_t stride, uint32_t num_lanes,
+                  int32_t *symbols_out)
+{
+    if (num_lanes == 0 || !stream || (n && (!indexes || !symbols_out)))
+        return ORACLE_E_ARG;
+    int rc = oracle_check_tables(cdf, lengths, num_tables, stride);
+    if (rc)
+        return rc;
+    uint64_t head = 1 + (uint64_t)num_lanes;
+    if (stream_words < head || stream[0] != num_lanes)
+        return ORACLE_E_CORRUPT;
+    uint64_t prev = 0;
+    for (uint32_t j = 0; j < num_lanes; ++j) {
+        uint64_t endj = stream[1 + j];
+        if (endj < prev + 2 || head + endj > stream_words)
+            return ORACLE_E_CORRUPT;
+        prev = endj;
+    }
+    prev = 0;
+    for (uint32_t j = 0; j < num_lanes; ++j) {
+        uint64_t endj = stream[1 + j];
+        uint64_t b = oracle_lane_begin(n, num_lanes, j);
+        uint64_t e = oracle_lane_begin(n, num_lanes, j + 1);
+        rc = oracle_decode_lane(stream + head + prev, endj - prev, indexes, b, e,
+                                cdf, lengths, offsets, num_tables, stride, symbols_out);
+        if (rc)
+            return rc;
+        prev = endj;
+    }
+    return ORACLE_OK;
+}

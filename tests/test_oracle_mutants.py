@@ -1,0 +1,81 @@
+"""Plant plausible mistakes in copies of the oracle and check the pins catch each.
+
+Every mutant below is a one-token slip someone could make while writing the
+coder from its description (a wrong constant, a dropped term, a swapped
+operand, an off-by-one, a wrong order).  Each mutated copy is compiled on the
+CPU and run through the quick pins in a child process; a mutant that survives
+means the pins are too weak.  Mistakes are planted only in these copies,
+never in the oracle source itself.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+RUNNER = os.path.join(HERE, "mutant_runner.py")
+
+MUTANTS = {
+    "state_low": ("#define STATE_LOW (1ull << 31)", "#define STATE_LOW (1ull << 30)"),
+    "reg_threshold": ("(uint64_t)p.freq << (63 - PREC)", "(uint64_t)p.freq << (62 - PREC)"),
+    "bits_threshold": ("(1ull << (63 - BYPASS_BITS))", "(1ull << (62 - BYPASS_BITS))"),
+    "flush_order": ("out[0] = (uint32_t)x;\n        out[1] = (uint32_t)(x >> 32);",
+                    "out[1] = (uint32_t)x;\n        out[0] = (uint32_t)(x >> 32);"),
+    "spill_order": ("out[2 + k] = emitted[ne - 1 - k];", "out[2 + k] = emitted[k];"),
+    "zigzag_below": ("raw = -2 * v - 1;", "raw = -2 * v;"),
+    "zigzag_above": ("raw = 2 * (v - mv);", "raw = 2 * (v - mv) + 2;"),
+    "dropped_remainder": ("(x / p.freq) * TOTAL_FREQ + (x % p.freq) + p.start",
+                          "(x / p.freq) * TOTAL_FREQ + p.start"),
+    "start_index": ("put_push(l, (uint32_t)row[v], (uint32_t)(row[v + 1] - row[v]))",
+                    "put_push(l, (uint32_t)row[v] + (v > 0), (uint32_t)(row[v + 1] - row[v]))"),
+    "scan_strict": ("(uint32_t)row[s + 1] <= cum", "(uint32_t)row[s + 1] < cum"),
+    "partition_ceil": ("((uint64_t)j * b) / num_lanes;",
+                       "((uint64_t)j * b + num_lanes - 1) / num_lanes;"),
+    "refill_le": ("if (d->x < STATE_LOW) {", "if (d->x <= STATE_LOW) {"),
+    "unzigzag_odd": ("value = -(int64_t)(raw >> 1) - 1;", "value = -(int64_t)(raw >> 1);"),
+    "header_start": ("out[1 + j] = (uint32_t)used;", "out[1 + j] = (uint32_t)(used - w);"),
+    "no_count": ("if ((rc = put_push(l, t, 0)))", "if (0 && (rc = put_push(l, t, 0)))"),
+    "group_order": ("(((uint64_t)raw >> (BYPASS_BITS * k)) & BYPASS_MAX)",
+                    "(((uint64_t)raw >> (BYPASS_BITS * (nb - 1 - k))) & BYPASS_MAX)"),
+    "escape_slot": ("int64_t mv = (int64_t)lengths[index] - 2;  /* escape slot */",
+                    "int64_t mv = (int64_t)lengths[index] - 1;  /* escape slot */"),
+    "dec_state_shift": ("d.x = (uint64_t)freq * (d.x >> PREC) + cum - start;",
+                        "d.x = (uint64_t)freq * (d.x >> (PREC - 1)) + cum - start;"),
+    "end_check": ("if (d.x != STATE_LOW || d.pos != d.words)", "if (d.x != STATE_LOW)"),
+}
+
+
+def _build(tmp_path, name, text):
+    src = tmp_path / f"{name}.c"
+    src.write_text(text)
+    # the header sits next to the original source
+    inc = os.path.dirname(oracle.SOURCE)
+    out = str(tmp_path / f"lib{name}.so")
+    subprocess.run(["gcc", "-O1", "-std=c99", "-shared", "-fPIC", f"-I{inc}", str(src), "-o",
+                    out], check=True)
+    return out
+
+
+def _run(lib_path):
+    return subprocess.run([sys.executable, RUNNER, lib_path], capture_output=True, text=True,
+                          timeout=300)
+
+
+def test_unmutated_copy_passes(tmp_path):
+    text = open(oracle.SOURCE).read()
+    res = _run(_build(tmp_path, "control", text))
+    assert res.returncode == 0, res.stdout + res.stderr
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    text = open(oracle.SOURCE).read()
+    assert text.count(old) == 1, f"mutation site for {name} not found exactly once"
+    res = _run(_build(tmp_path, name, text.replace(old, new)))
+    assert res.returncode != 0, f"mutant {name} survived the pins:\n{res.stdout}"
