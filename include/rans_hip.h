@@ -1,0 +1,136 @@
+/*
+ * rans_hip.h -- C ABI of the gfx950 (MI355X) indexed rANS64 coder.
+ *
+ * What it computes.  encode_with_indexes / decode_with_indexes of
+ * CompressAI-style entropy coding (kompressor README, "Why" and "Credits";
+ * torch_ans 0.3.0, "High-level API Reference"): symbol i is coded with the
+ * 16-bit quantised CDF row indexes[i] of a table set (cdf, cdf_lengths,
+ * offsets), by 64-bit rANS with 32-bit stream words (torch_ans "Usage"
+ * table, rans64 row).  A value outside its row's coded range
+ * [offset, offset + len - 2) is sent as the row's escape slot len-2 followed
+ * by a zig-zag raw value in 4-bit groups (torch_ans "Low-level API
+ * Reference", range limit of rans*_push).  The symbols are cut into
+ * num_lanes contiguous lanes, each with its own state and word stream, since
+ * a mean-scale hyperprior has no spatial autoregression (kompressor README
+ * "Why"); lane j owns positions [floor(j n / L), floor((j+1) n / L)).
+ *
+ * Stream container (u32 little-endian words):
+ *   word 0           num_lanes L
+ *   words 1 .. L     end_j = cumulative lane word count after lane j
+ *   words L+1 ..     lane streams back to back; a lane stream is the final
+ *                    state (low word, high word) then its renormalisation
+ *                    words in the order the decoder reads them.
+ * With L = 1 the words after [1, W] form the standard single rANS64 stream.
+ *
+ * Table rows.  cdf is int32 [num_tables][cdf_stride]; row r has
+ * cdf_lengths[r] valid entries (3 <= len <= cdf_stride), starts at 0, ends
+ * at exactly 65536 and strictly increases (every frequency >= 1).
+ * offsets[r] is the symbol value of slot 0.
+ *
+ * Memory and ownership.  Every array argument below is a DEVICE pointer
+ * owned by the caller (for example a torch tensor's data_ptr() on the ROCm
+ * device).  The library allocates nothing and keeps no global state; all
+ * work is enqueued on `hstream` and no call synchronises with the host.
+ * `workspace` is caller-owned device memory of at least
+ * rans_workspace_bytes(...) bytes, 256-byte aligned, zero-filled before its
+ * first use; every call leaves its bookkeeping words zero again, so the
+ * same workspace can be reused by later calls.  Calls that share a
+ * workspace, an output or a status word must not overlap in time.
+ *
+ * Errors.  The return value reports what the host can check before
+ * launching (RANS_E_ARG, RANS_E_WORKSPACE, RANS_E_TABLE for bad sizes,
+ * RANS_E_HIP for a failed launch).  Data-dependent errors are written by
+ * the device to *status (0 on success; a bad CDF row, an index outside
+ * [0, K), a symbol too far out of range, a too-small output, a corrupt
+ * stream, or tables too large for the LDS budget).  When *status != 0 the
+ * outputs are unspecified, but no kernel ever reads or writes outside the
+ * buffers described here.
+ */
+#ifndef RANS_HIP_H
+#define RANS_HIP_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum rans_status {
+    RANS_OK = 0,
+    RANS_E_ARG = -1,          /* null pointer, zero lanes, bad sizes */
+    RANS_E_TABLE = -2,        /* a CDF row is malformed */
+    RANS_E_INDEX = -3,        /* indexes[i] outside [0, num_tables) */
+    RANS_E_SYMBOL_RANGE = -4, /* escape distance needs 2^31 or more */
+    RANS_E_CAPACITY = -5,     /* encoded container exceeds stream capacity */
+    RANS_E_CORRUPT = -6,      /* the stream does not decode cleanly */
+    RANS_E_WORKSPACE = -7,    /* workspace missing, misaligned or too small */
+    RANS_E_HIP = -8,          /* a HIP launch failed */
+    RANS_E_TABLE_SIZE = -9    /* the table set does not fit the LDS budget */
+};
+
+/* Largest supported table count and row stride. */
+#define RANS_MAX_TABLES 4096
+#define RANS_MAX_STRIDE 16384
+
+/* Words an encoded container can need in the worst case (every symbol an
+ * escape with a 31-bit raw value): 1 + L header words plus, per lane,
+ * 2 * symbols + 4 (a symbol costs at most 16 + 36 bits). */
+uint64_t rans_encode_bound_words(uint64_t n, uint32_t num_lanes);
+
+/* Workspace bytes needed by any call below with these sizes. */
+uint64_t rans_workspace_bytes(uint64_t n, uint32_t num_lanes, int32_t num_tables,
+                              int32_t cdf_stride);
+
+/* Encode n symbols into the container at `stream` (capacity in words).
+ * *stream_words (device) receives the container length in words. */
+int rans_encode_with_indexes(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                             const int32_t *cdf, const int32_t *cdf_lengths,
+                             const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
+                             uint32_t num_lanes, uint32_t *stream,
+                             uint64_t stream_capacity_words, uint64_t *stream_words,
+                             int32_t *status, void *workspace, uint64_t workspace_bytes,
+                             hipStream_t hstream);
+
+/* Decode n symbols (n = number of indexes) from the container at `stream`.
+ * stream_capacity_words is the number of readable words at `stream`; the
+ * container may be shorter (its header gives its extent).  num_lanes must
+ * equal the container's lane count, else *status = RANS_E_CORRUPT. */
+int rans_decode_with_indexes(const uint32_t *stream, uint64_t stream_capacity_words,
+                             const int32_t *indexes, uint64_t n,
+                             const int32_t *cdf, const int32_t *cdf_lengths,
+                             const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
+                             uint32_t num_lanes, int32_t *symbols, int32_t *status,
+                             void *workspace, uint64_t workspace_bytes, hipStream_t hstream);
+
+/* The two calls above are rans_prepare_tables followed by the matching
+ * *_prepared call.  Callers that code many tensors with one table set
+ * (torch_ans "Performance Tuning": reuse the coder instead of rebuilding
+ * tables per call) may prepare once and code many times on one workspace.
+ * rans_prepare_tables validates the rows on the device and packs them, with
+ * the decoder's lookup table, into the workspace; row errors surface in the
+ * *status of the next *_prepared call. */
+int rans_prepare_tables(const int32_t *cdf, const int32_t *cdf_lengths, const int32_t *offsets,
+                        int32_t num_tables, int32_t cdf_stride, void *workspace,
+                        uint64_t workspace_bytes, hipStream_t hstream);
+
+int rans_encode_prepared(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                         int32_t num_tables, int32_t cdf_stride, uint32_t num_lanes,
+                         uint32_t *stream, uint64_t stream_capacity_words,
+                         uint64_t *stream_words, int32_t *status, void *workspace,
+                         uint64_t workspace_bytes, hipStream_t hstream);
+
+int rans_decode_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
+                         const int32_t *indexes, uint64_t n, int32_t num_tables,
+                         int32_t cdf_stride, uint32_t num_lanes, int32_t *symbols,
+                         int32_t *status, void *workspace, uint64_t workspace_bytes,
+                         hipStream_t hstream);
+
+/* Static text for a status code. */
+const char *rans_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RANS_HIP_H */

@@ -1,0 +1,272 @@
+"""ctypes binding of librans_hip.so: argument marshalling only.
+
+Torch tensors provide device memory and the current HIP stream; every step of
+the coder runs in the library's kernels.  There is no CPU path: if the
+library is missing this module raises instead of falling back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "librans_hip.so")
+
+STATUS = {
+    0: "RANS_OK",
+    -1: "RANS_E_ARG",
+    -2: "RANS_E_TABLE",
+    -3: "RANS_E_INDEX",
+    -4: "RANS_E_SYMBOL_RANGE",
+    -5: "RANS_E_CAPACITY",
+    -6: "RANS_E_CORRUPT",
+    -7: "RANS_E_WORKSPACE",
+    -8: "RANS_E_HIP",
+    -9: "RANS_E_TABLE_SIZE",
+}
+NAME_TO_CODE = {v: k for k, v in STATUS.items()}
+
+# every symbol the public header declares
+EXPORTS = (
+    "rans_encode_bound_words",
+    "rans_workspace_bytes",
+    "rans_encode_with_indexes",
+    "rans_decode_with_indexes",
+    "rans_prepare_tables",
+    "rans_encode_prepared",
+    "rans_decode_prepared",
+    "rans_status_string",
+)
+
+
+class RansError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = int(code)
+        super().__init__(f"{where}: {STATUS.get(self.code, self.code)} "
+                         f"({_status_text(self.code)})")
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def _status_text(code: int) -> str:
+    try:
+        return load().rans_status_string(int(code)).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "?"
+
+
+def load(path: str | None = None):
+    """Load the compiled HIP library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIBRARY
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"{p} is missing: build it with `python -m learned_image_compression_amd.build` "
+                "(hipcc, gfx950); there is no CPU fallback")
+        lib = ctypes.CDLL(p)
+        vp, u64, i32, u32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_uint32
+        lib.rans_encode_bound_words.argtypes = [u64, u32]
+        lib.rans_encode_bound_words.restype = u64
+        lib.rans_workspace_bytes.argtypes = [u64, u32, i32, i32]
+        lib.rans_workspace_bytes.restype = u64
+        lib.rans_encode_with_indexes.argtypes = [vp, vp, u64, vp, vp, vp, i32, i32, u32, vp, u64,
+                                                 vp, vp, vp, u64, vp]
+        lib.rans_encode_with_indexes.restype = ctypes.c_int
+        lib.rans_decode_with_indexes.argtypes = [vp, u64, vp, u64, vp, vp, vp, i32, i32, u32, vp,
+                                                 vp, vp, u64, vp]
+        lib.rans_decode_with_indexes.restype = ctypes.c_int
+        lib.rans_prepare_tables.argtypes = [vp, vp, vp, i32, i32, vp, u64, vp]
+        lib.rans_prepare_tables.restype = ctypes.c_int
+        lib.rans_encode_prepared.argtypes = [vp, vp, u64, i32, i32, u32, vp, u64, vp, vp, vp, u64,
+                                             vp]
+        lib.rans_encode_prepared.restype = ctypes.c_int
+        lib.rans_decode_prepared.argtypes = [vp, u64, vp, u64, i32, i32, u32, vp, vp, vp, u64, vp]
+        lib.rans_decode_prepared.restype = ctypes.c_int
+        lib.rans_status_string.argtypes = [ctypes.c_int]
+        lib.rans_status_string.restype = ctypes.c_char_p
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def encode_bound_words(n: int, lanes: int) -> int:
+    return int(load().rans_encode_bound_words(n, lanes))
+
+
+def workspace_bytes(n: int, lanes: int, num_tables: int, stride: int) -> int:
+    return int(load().rans_workspace_bytes(n, lanes, num_tables, stride))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, device, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Workspace:
+    """Zero-filled device workspace, grown (re-zeroed) on demand, one per device."""
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self.buf = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            # 256-byte alignment: the caching allocator aligns blocks to 512 bytes
+            self.buf = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+            assert self.buf.data_ptr() % 256 == 0
+        return self.buf
+
+
+_workspaces: dict = {}
+
+
+def workspace_for(device) -> Workspace:
+    device = torch.device(device)
+    key = (device.type, device.index if device.index is not None else torch.cuda.current_device())
+    if key not in _workspaces:
+        _workspaces[key] = Workspace(torch.device("cuda", key[1]))
+    return _workspaces[key]
+
+
+class Tables:
+    """A CDF table set on the device (int32 cdf[K, stride], lengths[K], offsets[K])."""
+
+    def __init__(self, cdf: torch.Tensor, lengths: torch.Tensor, offsets: torch.Tensor):
+        device = cdf.device
+        for t, name in ((cdf, "cdf"), (lengths, "cdf_lengths"), (offsets, "offsets")):
+            _need(t, torch.int32, device, name)
+        if cdf.dim() != 2 or lengths.numel() != cdf.shape[0] or offsets.numel() != cdf.shape[0]:
+            raise ValueError("cdf must be [K, stride] with K lengths and K offsets")
+        self.cdf, self.lengths, self.offsets = cdf, lengths, offsets
+        self.device = device
+
+    @property
+    def num_tables(self) -> int:
+        return int(self.cdf.shape[0])
+
+    @property
+    def stride(self) -> int:
+        return int(self.cdf.shape[1])
+
+    @classmethod
+    def from_numpy(cls, cdf, lengths, offsets, device="cuda"):
+        return cls(torch.as_tensor(cdf, dtype=torch.int32).to(device).contiguous(),
+                   torch.as_tensor(lengths, dtype=torch.int32).to(device).contiguous(),
+                   torch.as_tensor(offsets, dtype=torch.int32).to(device).contiguous())
+
+
+def _check_rc(rc: int, where: str):
+    if rc != 0:
+        raise RansError(rc, where)
+
+
+def encode_with_indexes(symbols: torch.Tensor, indexes: torch.Tensor, tables: Tables,
+                        num_lanes: int, *, stream_out: torch.Tensor | None = None,
+                        stream_words: torch.Tensor | None = None,
+                        status: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        prepared: bool = False):
+    """Enqueue an encode; returns (stream int32 words, stream_words int64[1], status int32[1]).
+
+    Nothing is synchronised: read status/stream_words after the stream is done
+    (``check(status)``).  ``prepared=True`` reuses tables already packed into
+    ``workspace`` by :func:`prepare_tables`.
+    """
+    device = tables.device
+    _need(symbols, torch.int32, device, "symbols")
+    _need(indexes, torch.int32, device, "indexes")
+    n = symbols.numel()
+    if indexes.numel() != n:
+        raise ValueError("symbols and indexes differ in size")
+    lib = load()
+    if stream_out is None:
+        stream_out = torch.empty(encode_bound_words(n, num_lanes), dtype=torch.int32, device=device)
+    _need(stream_out, torch.int32, device, "stream_out")
+    if stream_words is None:
+        stream_words = torch.zeros(1, dtype=torch.int64, device=device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=device)
+    ws = workspace if workspace is not None else workspace_for(device).get(
+        workspace_bytes(n, num_lanes, tables.num_tables, tables.stride))
+    st = _stream(device)
+    if prepared:
+        rc = lib.rans_encode_prepared(_ptr(symbols), _ptr(indexes), n, tables.num_tables,
+                                      tables.stride, num_lanes, _ptr(stream_out),
+                                      stream_out.numel(), _ptr(stream_words), _ptr(status),
+                                      _ptr(ws), ws.numel(), st)
+    else:
+        rc = lib.rans_encode_with_indexes(_ptr(symbols), _ptr(indexes), n, _ptr(tables.cdf),
+                                          _ptr(tables.lengths), _ptr(tables.offsets),
+                                          tables.num_tables, tables.stride, num_lanes,
+                                          _ptr(stream_out), stream_out.numel(), _ptr(stream_words),
+                                          _ptr(status), _ptr(ws), ws.numel(), st)
+    _check_rc(rc, "rans_encode_with_indexes")
+    return stream_out, stream_words, status
+
+
+def decode_with_indexes(stream: torch.Tensor, indexes: torch.Tensor, tables: Tables,
+                        num_lanes: int, *, symbols_out: torch.Tensor | None = None,
+                        status: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        capacity_words: int | None = None, prepared: bool = False):
+    """Enqueue a decode; returns (symbols int32[n], status int32[1])."""
+    device = tables.device
+    _need(stream, torch.int32, device, "stream")
+    _need(indexes, torch.int32, device, "indexes")
+    n = indexes.numel()
+    lib = load()
+    if symbols_out is None:
+        symbols_out = torch.empty(n, dtype=torch.int32, device=device)
+    _need(symbols_out, torch.int32, device, "symbols_out")
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=device)
+    cap = stream.numel() if capacity_words is None else int(capacity_words)
+    ws = workspace if workspace is not None else workspace_for(device).get(
+        workspace_bytes(n, num_lanes, tables.num_tables, tables.stride))
+    st = _stream(device)
+    if prepared:
+        rc = lib.rans_decode_prepared(_ptr(stream), cap, _ptr(indexes), n, tables.num_tables,
+                                      tables.stride, num_lanes, _ptr(symbols_out), _ptr(status),
+                                      _ptr(ws), ws.numel(), st)
+    else:
+        rc = lib.rans_decode_with_indexes(_ptr(stream), cap, _ptr(indexes), n, _ptr(tables.cdf),
+                                          _ptr(tables.lengths), _ptr(tables.offsets),
+                                          tables.num_tables, tables.stride, num_lanes,
+                                          _ptr(symbols_out), _ptr(status), _ptr(ws), ws.numel(),
+                                          st)
+    _check_rc(rc, "rans_decode_with_indexes")
+    return symbols_out, status
+
+
+def prepare_tables(tables: Tables, workspace: torch.Tensor):
+    rc = load().rans_prepare_tables(_ptr(tables.cdf), _ptr(tables.lengths), _ptr(tables.offsets),
+                                    tables.num_tables, tables.stride, _ptr(workspace),
+                                    workspace.numel(), _stream(tables.device))
+    _check_rc(rc, "rans_prepare_tables")
+
+
+def check(status: torch.Tensor, where: str = "device"):
+    """Synchronise on the status word and raise RansError if it is non-zero."""
+    code = int(status.item())
+    if code != 0:
+        raise RansError(code, where)

@@ -1,0 +1,178 @@
+// rans_abi.hip -- the extern "C" entry points: host-side argument checks, then
+// launches on the caller's stream.  No call allocates memory or synchronises.
+#include "rans_internal.hpp"
+
+using namespace rans;
+
+namespace {
+
+bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+int check_workspace(void *ws, uint64_t bytes, uint64_t need)
+{
+    if (!ws || !aligned256(ws) || bytes < need)
+        return RANS_E_WORKSPACE;
+    return RANS_OK;
+}
+
+int check_tables(const int32_t *cdf, const int32_t *lengths, const int32_t *offsets,
+                 int32_t num_tables, int32_t stride)
+{
+    if (!cdf || !lengths || !offsets)
+        return RANS_E_ARG;
+    if (num_tables < 1 || num_tables > RANS_MAX_TABLES || stride < 3 || stride > RANS_MAX_STRIDE)
+        return RANS_E_TABLE;
+    return RANS_OK;
+}
+
+// The container stores cumulative lane ends as u32 words.
+bool fits_u32_payload(uint64_t n, uint32_t lanes)
+{
+    return n <= (1ull << 40) && ws_scratch_words(n, lanes) <= 0xFFFFFFFFull;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? RANS_OK : RANS_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+uint64_t rans_encode_bound_words(uint64_t n, uint32_t num_lanes)
+{
+    return 1ull + num_lanes + ws_scratch_words(n, num_lanes);
+}
+
+uint64_t rans_workspace_bytes(uint64_t n, uint32_t num_lanes, int32_t num_tables,
+                              int32_t cdf_stride)
+{
+    (void)num_tables;
+    (void)cdf_stride;
+    return ws_scratch_offset(num_lanes) + 4ull * ws_scratch_words(n, num_lanes);
+}
+
+int rans_prepare_tables(const int32_t *cdf, const int32_t *cdf_lengths, const int32_t *offsets,
+                        int32_t num_tables, int32_t cdf_stride, void *workspace,
+                        uint64_t workspace_bytes, hipStream_t hstream)
+{
+    int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
+    if (rc)
+        return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes, ws_flags_offset())))
+        return rc;
+    PrepArgs a{cdf, cdf_lengths, offsets, num_tables, cdf_stride,
+               static_cast<uint8_t *>(workspace)};
+    return launched(launch_prep(a, hstream));
+}
+
+int rans_encode_prepared(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                         int32_t num_tables, int32_t cdf_stride, uint32_t num_lanes,
+                         uint32_t *stream, uint64_t stream_capacity_words,
+                         uint64_t *stream_words, int32_t *status, void *workspace,
+                         uint64_t workspace_bytes, hipStream_t hstream)
+{
+    if (num_lanes == 0 || !stream || !stream_words || !status || (n && (!symbols || !indexes)))
+        return RANS_E_ARG;
+    if (num_tables < 1 || num_tables > RANS_MAX_TABLES || cdf_stride < 3 ||
+        cdf_stride > RANS_MAX_STRIDE)
+        return RANS_E_TABLE;
+    if (!fits_u32_payload(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
+        return RANS_E_ARG;
+    int rc = check_workspace(workspace, workspace_bytes,
+                             rans_workspace_bytes(n, num_lanes, num_tables, cdf_stride));
+    if (rc)
+        return rc;
+    EncodeArgs a{symbols, indexes, n, num_lanes, num_tables, stream, stream_capacity_words,
+                 stream_words, status, static_cast<uint8_t *>(workspace)};
+    return launched(launch_encode(a, hstream));
+}
+
+int rans_decode_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
+                         const int32_t *indexes, uint64_t n, int32_t num_tables,
+                         int32_t cdf_stride, uint32_t num_lanes, int32_t *symbols,
+                         int32_t *status, void *workspace, uint64_t workspace_bytes,
+                         hipStream_t hstream)
+{
+    if (num_lanes == 0 || !stream || !status || (n && (!symbols || !indexes)))
+        return RANS_E_ARG;
+    if (num_tables < 1 || num_tables > RANS_MAX_TABLES || cdf_stride < 3 ||
+        cdf_stride > RANS_MAX_STRIDE)
+        return RANS_E_TABLE;
+    if (n > (1ull << 40) || stream_capacity_words < 1ull + num_lanes)
+        return RANS_E_ARG;
+    // the decoder uses only the header and the prepared tables
+    int rc = check_workspace(workspace, workspace_bytes, ws_flags_offset());
+    if (rc)
+        return rc;
+    DecodeArgs a{stream, stream_capacity_words, indexes, n, num_lanes, num_tables, symbols,
+                 status, static_cast<uint8_t *>(workspace)};
+    return launched(launch_decode(a, hstream));
+}
+
+int rans_encode_with_indexes(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                             const int32_t *cdf, const int32_t *cdf_lengths,
+                             const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
+                             uint32_t num_lanes, uint32_t *stream,
+                             uint64_t stream_capacity_words, uint64_t *stream_words,
+                             int32_t *status, void *workspace, uint64_t workspace_bytes,
+                             hipStream_t hstream)
+{
+    if (num_lanes == 0 || !stream || !stream_words || !status || (n && (!symbols || !indexes)))
+        return RANS_E_ARG;
+    if (!fits_u32_payload(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
+        return RANS_E_ARG;
+    int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
+    if (rc)
+        return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes,
+                              rans_workspace_bytes(n, num_lanes, num_tables, cdf_stride))))
+        return rc;
+    if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
+                                  workspace_bytes, hstream)))
+        return rc;
+    return rans_encode_prepared(symbols, indexes, n, num_tables, cdf_stride, num_lanes, stream,
+                                stream_capacity_words, stream_words, status, workspace,
+                                workspace_bytes, hstream);
+}
+
+int rans_decode_with_indexes(const uint32_t *stream, uint64_t stream_capacity_words,
+                             const int32_t *indexes, uint64_t n,
+                             const int32_t *cdf, const int32_t *cdf_lengths,
+                             const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
+                             uint32_t num_lanes, int32_t *symbols, int32_t *status,
+                             void *workspace, uint64_t workspace_bytes, hipStream_t hstream)
+{
+    if (num_lanes == 0 || !stream || !status || (n && (!symbols || !indexes)))
+        return RANS_E_ARG;
+    if (n > (1ull << 40) || stream_capacity_words < 1ull + num_lanes)
+        return RANS_E_ARG;
+    int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
+    if (rc)
+        return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes, ws_flags_offset())))
+        return rc;
+    if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
+                                  workspace_bytes, hstream)))
+        return rc;
+    return rans_decode_prepared(stream, stream_capacity_words, indexes, n, num_tables,
+                                cdf_stride, num_lanes, symbols, status, workspace,
+                                workspace_bytes, hstream);
+}
+
+const char *rans_status_string(int code)
+{
+    switch (code) {
+    case RANS_OK: return "ok";
+    case RANS_E_ARG: return "invalid argument";
+    case RANS_E_TABLE: return "malformed CDF table";
+    case RANS_E_INDEX: return "table index out of range";
+    case RANS_E_SYMBOL_RANGE: return "symbol too far outside its coded range";
+    case RANS_E_CAPACITY: return "output capacity too small";
+    case RANS_E_CORRUPT: return "corrupt stream";
+    case RANS_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case RANS_E_HIP: return "HIP launch failure";
+    case RANS_E_TABLE_SIZE: return "table set too large for the LDS budget";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,203 @@
+// rans_prep.hip -- table preparation: validate CDF rows, pack them as u16 into
+// the workspace, and build the decoder's per-row bucket lookup.
+//
+// The pages rebuild or re-marshal the tables on every call (kompressor
+// BENCHMARKS.md section 4: cdf/len/offset lists rebuilt each call; torch_ans
+// "Performance Tuning": init_params rebuilds the quantised CDFs and the
+// lookup table, about 0.2 ms).  Here one launch does it: every block scans
+// the row lengths redundantly (K <= 4096), so no block waits for another.
+//
+// Packed layout in the workspace table region (copied verbatim into LDS by
+// the coding kernels):
+//   [RowMeta x K][u16 cdf16 x sum(len), padded to 16 B][u64 lut x K * 2^q]
+// A row's terminal 65536 is stored as 0: f = (next - start) mod 2^16 is still
+// right because every frequency is in [1, 65535].
+//
+// Decoder lookup (inverse-CDF table in the sense of torch_ans "Usage",
+// "Inverse CDF decoding": a table keyed by the low state bits).  Each row gets
+// 2^q buckets of width 2^(16-q) cumulative values, q the largest value <= 10
+// for which the whole set fits the LDS budget.  A bucket stores the adjacent
+// slot pair that covers most of it, so one 8-byte LDS read resolves the
+// symbol whenever the cumulative value falls in that pair.
+#include "rans_internal.hpp"
+
+namespace rans {
+
+constexpr int kPrepThreads = 256;
+
+__device__ inline uint32_t row_value(const uint16_t *row, uint32_t k, uint32_t len)
+{
+    return (k + 1 == len) ? kTotal : (uint32_t)row[k];
+}
+
+// First k in [0, len) with value(k) > c; value(len-1) = 65536 > c.
+__device__ inline uint32_t upper_bound_row(const uint16_t *row, uint32_t len, uint32_t c)
+{
+    uint32_t lo = 0, hi = len - 1;
+    while (lo < hi) {
+        uint32_t mid = (lo + hi) >> 1;
+        if (row_value(row, mid, len) > c)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
+{
+    __shared__ uint32_t s_base[RANS_MAX_TABLES];
+    __shared__ uint32_t s_part[kPrepThreads];
+    __shared__ uint16_t s_row[RANS_MAX_STRIDE];
+
+    const int tid = threadIdx.x;
+    const int K = a.num_tables;
+    const uint32_t stride = (uint32_t)a.stride;
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
+    uint8_t *tab = a.ws + ws_tables_offset();
+
+    // --- 1. effective lengths and their exclusive scan (every block) ----------
+    const int chunk = (K + kPrepThreads - 1) / kPrepThreads;
+    const int r0 = tid * chunk;
+    const int r1 = min(K, r0 + chunk);
+    uint32_t sum = 0;
+    for (int r = r0; r < r1; ++r) {
+        int32_t len = a.lengths[r];
+        uint32_t eff = (len >= 3 && (uint32_t)len <= stride) ? (uint32_t)len : 3u;
+        s_base[r] = eff;
+        sum += eff;
+    }
+    s_part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kPrepThreads; off <<= 1) {   // inclusive Hillis-Steele scan
+        uint32_t v = (tid >= off) ? s_part[tid - off] : 0u;
+        __syncthreads();
+        s_part[tid] += v;
+        __syncthreads();
+    }
+    uint32_t run = s_part[tid] - sum;
+    for (int r = r0; r < r1; ++r) {
+        uint32_t eff = s_base[r];
+        s_base[r] = run;
+        run += eff;
+    }
+    const uint32_t total = s_part[kPrepThreads - 1];
+    __syncthreads();
+
+    const uint32_t meta_bytes = (uint32_t)align_up(16ull * K, 16);
+    const uint64_t cdf_bytes = align_up(2ull * total, 16);
+    const uint64_t enc_bytes = meta_bytes + cdf_bytes;
+    const bool enc_ok = enc_bytes <= kTableBudget;
+    int q = -1;
+    for (int t = (int)kMaxLutQ; t >= 0 && enc_ok; --t) {
+        if (enc_bytes + (8ull * K << t) <= kTableBudget) {
+            q = t;
+            break;
+        }
+    }
+    const bool dec_ok = q >= 0;
+    if (q < 0)
+        q = 0;
+    const uint64_t dec_bytes = enc_bytes + (8ull * K << q);
+
+    if (blockIdx.x == 0 && tid == 0) {
+        hdr->num_tables = (uint32_t)K;
+        hdr->cdf_stride = stride;
+        hdr->total_len = total;
+        hdr->lut_q = (uint32_t)q;
+        hdr->enc_bytes = (uint32_t)(enc_ok ? enc_bytes : 0);
+        hdr->dec_bytes = (uint32_t)(dec_ok ? dec_bytes : 0);
+        hdr->enc_ok = enc_ok ? 1u : 0u;
+        hdr->dec_ok = dec_ok ? 1u : 0u;
+        hdr->err = 0;
+        hdr->done = 0;
+        hdr->ticket = 0;
+        hdr->total_words = 0;
+        __threadfence();
+        hdr->magic = kMagic;
+    }
+    if (!enc_ok)
+        return;   // nothing fits: the coding kernels report RANS_E_TABLE_SIZE
+
+    RowMeta *meta = reinterpret_cast<RowMeta *>(tab);
+    uint16_t *cdf16 = reinterpret_cast<uint16_t *>(tab + meta_bytes);
+    uint64_t *lut = reinterpret_cast<uint64_t *>(tab + enc_bytes);
+    const uint32_t width = kTotal >> q;
+
+    // --- 2. rows of this block ------------------------------------------------
+    for (int r = blockIdx.x; r < K; r += gridDim.x) {
+        const int32_t len_in = a.lengths[r];
+        const bool len_ok = len_in >= 3 && (uint32_t)len_in <= stride;
+        const uint32_t len = len_ok ? (uint32_t)len_in : 3u;
+        const uint32_t base = s_base[r];
+        const int32_t *row = a.cdf + (int64_t)r * stride;
+        int bad = len_ok ? 0 : 1;
+        for (uint32_t k = tid; k < len; k += kPrepThreads) {
+            int32_t v = len_ok ? row[k] : (k == 0 ? 0 : (k == 1 ? 1 : (int32_t)kTotal));
+            if (len_ok) {
+                if (k == 0 && v != 0)
+                    bad = 1;
+                if (k + 1 == len && v != (int32_t)kTotal)
+                    bad = 1;
+                if (k > 0 && v <= row[k - 1])
+                    bad = 1;
+            }
+            uint16_t p = (uint16_t)(uint32_t)v;
+            cdf16[base + k] = p;
+            s_row[k] = p;
+        }
+        bad = __syncthreads_or(bad);
+        if (tid == 0) {
+            RowMeta m;
+            m.cdf_base = base;
+            m.offset = a.offsets[r];
+            m.mv = (len - 2) | (bad ? kRowInvalid : 0u);
+            m.lut_base = (uint32_t)r << q;
+            meta[r] = m;
+        }
+        if (dec_ok) {
+            for (uint32_t b = tid; b < (1u << q); b += kPrepThreads) {
+                uint64_t e = 0;
+                if (!bad) {
+                    const uint32_t lo = b * width;
+                    const uint32_t hi = lo + width - 1;
+                    uint32_t first = upper_bound_row(s_row, len, lo) - 1;
+                    uint32_t last = upper_bound_row(s_row, len, hi) - 1;
+                    const uint32_t amax = len - 3;   // pair (a, a+1) with a+1 <= escape slot
+                    uint32_t best_a = first < amax ? first : amax;
+                    if (last > first && first < amax) {
+                        uint32_t kend = last - 1 < amax ? last - 1 : amax;
+                        uint32_t best = 0;
+                        for (uint32_t k = first; k <= kend; ++k) {
+                            uint32_t s0 = row_value(s_row, k, len);
+                            uint32_t s1 = row_value(s_row, k + 1, len);
+                            uint32_t s2 = row_value(s_row, k + 2, len);
+                            uint32_t c0 = min(s1, hi + 1) - max(s0, lo);
+                            uint32_t c1 = (s1 > hi) ? 0u : min(s2, hi + 1) - s1;
+                            if (c0 + c1 > best) {
+                                best = c0 + c1;
+                                best_a = k;
+                            }
+                        }
+                    }
+                    const uint32_t s0 = row_value(s_row, best_a, len);
+                    const uint32_t s1 = row_value(s_row, best_a + 1, len);
+                    const uint32_t s2 = row_value(s_row, best_a + 2, len);
+                    e = (uint64_t)s0 | ((uint64_t)s1 << 16) | ((uint64_t)(s2 - 1) << 32) |
+                        ((uint64_t)best_a << 48);
+                }
+                lut[((uint64_t)r << q) + b] = e;
+            }
+        }
+        __syncthreads();   // s_row is reused by the next row
+    }
+}
+
+hipError_t launch_prep(const PrepArgs &a, hipStream_t s)
+{
+    int blocks = a.num_tables < 256 ? a.num_tables : 256;
+    hipLaunchKernelGGL(prep_kernel, dim3(blocks), dim3(kPrepThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace rans

@@ -1,0 +1,233 @@
+"""GPU parity: the HIP coder against the CPU oracle, byte for byte.
+
+Every synthetic workload runs at each of its lane counts (tiny and z also at
+1, 2, 3, 7, 255, n and n + 5 lanes, covering single-lane standard streams,
+ragged partitions and empty lanes).  For each case the GPU encode must equal
+the oracle's container word for word, the GPU must decode the oracle's
+container back to the input, and each side decodes the other's stream.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("tiny", L) for L in (64, 1, 2, 3, 7, 255, 16384, 16389)
+] + [
+    ("z", L) for L in (256, 1, 2, 3, 7, 255, 97920, 97925)
+] + [
+    ("y1080", 4096), ("y1080", 1), ("y1080", 977),
+    ("y1080x16", 65536),
+    ("y4kx8", 1024), ("y4kx8", 16384), ("y4kx8", 131072),
+]
+
+_cache = {}
+
+
+def _workload(name):
+    if name not in _cache:
+        import gpu_util as G
+        w = W.load(name)
+        _cache.clear()
+        _cache[name] = (w, G.tables_of(w), G.to_dev(w.symbols), G.to_dev(w.indexes))
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name,lanes", CASES, ids=[f"{n}-L{L}" for n, L in CASES])
+def test_encode_decode_match_oracle(name, lanes):
+    import gpu_util as G
+    w, tables, sym, idx = _workload(name)
+    G.say(f"[parity] {name} n={w.n} lanes={lanes}: oracle encode")
+    rc, ref = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, lanes)
+    assert rc == 0
+    G.say(f"[parity] {name} lanes={lanes}: gpu encode")
+    st, got, nw = G.gpu_encode(sym, idx, tables, lanes)
+    assert st == 0, f"encode status {st}"
+    assert nw == ref.size, f"container size {nw} != oracle {ref.size}"
+    if not np.array_equal(got, ref):
+        bad = np.flatnonzero(got != ref)
+        pytest.fail(f"{bad.size} words differ, first at {bad[0]}: {got[bad[0]]:#x} != {ref[bad[0]]:#x}")
+    G.say(f"[parity] {name} lanes={lanes}: gpu decode of the oracle stream")
+    st, out = G.gpu_decode(ref, idx, tables, lanes)
+    assert st == 0, f"decode status {st}"
+    assert np.array_equal(out, w.symbols)
+    G.say(f"[parity] {name} lanes={lanes}: oracle decode of the gpu stream")
+    rc, back = oracle.decode(got, w.indexes, w.cdf, w.lengths, w.offsets, lanes)
+    assert rc == 0 and np.array_equal(back, w.symbols)
+
+
+def test_empty_input_and_more_lanes_than_symbols():
+    import gpu_util as G
+    w, tables, sym, idx = _workload("tiny")
+    for n, lanes in ((0, 1), (0, 5), (3, 8), (5, 5), (1, 64), (130, 129)):
+        G.say(f"[edge] n={n} lanes={lanes}")
+        rc, ref = oracle.encode(w.symbols[:n], w.indexes[:n], w.cdf, w.lengths, w.offsets, lanes)
+        st, got, nw = G.gpu_encode(sym[:n], idx[:n], tables, lanes)
+        assert rc == 0 and st == 0
+        assert np.array_equal(got, ref)
+        st, out = G.gpu_decode(ref, idx[:n], tables, lanes)
+        assert st == 0 and np.array_equal(out, w.symbols[:n])
+
+
+def test_bypass_edges_and_extremes():
+    """Every zig-zag boundary and both 2^30 limits, on tiny, z and the 4-slot hand row."""
+    import gpu_util as G
+    rows = np.full((2, 5), 65536, np.int32)
+    rows[0, :4] = [0, 32768, 65535, 65536]
+    rows[1, :5] = [0, 1, 2, 65535, 65536]
+    lengths = np.array([4, 5], np.int32)
+    offsets = np.array([0, -7], np.int32)
+    raws = list(W.EDGE_RAWS) + [2, 3, 14, 17, 4095, 4096, 65535, 65536, 1 << 20]
+    syms, idxs = [], []
+    for r in (0, 1):
+        mv = lengths[r] - 2
+        for raw in raws:
+            syms.append(W.raw_to_value(raw, mv) + offsets[r])
+            idxs.append(r)
+        syms += [offsets[r], offsets[r] + mv - 1]
+        idxs += [r, r]
+    syms = np.array(syms * 7, np.int64).astype(np.int32)
+    idxs = np.array(idxs * 7, np.int32)
+    tables = G.B.Tables.from_numpy(rows, lengths, offsets, G.DEV)
+    for lanes in (1, 3, 64):
+        G.say(f"[bypass edges] lanes={lanes}")
+        rc, ref = oracle.encode(syms, idxs, rows, lengths, offsets, lanes)
+        assert rc == 0
+        st, got, _ = G.gpu_encode(G.to_dev(syms), G.to_dev(idxs), tables, lanes)
+        assert st == 0 and np.array_equal(got, ref)
+        st, out = G.gpu_decode(ref, G.to_dev(idxs), tables, lanes)
+        assert st == 0 and np.array_equal(out, syms)
+
+
+def test_repeat_calls_are_identical_and_workspace_is_reusable():
+    import gpu_util as G
+    w, tables, sym, idx = _workload("tiny")
+    first = None
+    for k in range(3):
+        G.say(f"[repeat] call {k}")
+        st, got, _ = G.gpu_encode(sym, idx, tables, 64)
+        assert st == 0
+        if first is None:
+            first = got
+        assert np.array_equal(got, first)
+        st, out = G.gpu_decode(got, idx, tables, 64)
+        assert st == 0 and np.array_equal(out, w.symbols)
+
+
+def test_prepared_tables_code_many_tensors():
+    import torch
+    import gpu_util as G
+    w, tables, sym, idx = _workload("tiny")
+    B = G.B
+    n = w.n
+    ws = B.workspace_for(G.DEV).get(B.workspace_bytes(n, 64, tables.num_tables, tables.stride))
+    B.prepare_tables(tables, ws)
+    for lo, hi, lanes in ((0, 5000, 16), (5000, 16384, 33), (100, 101, 1)):
+        G.say(f"[prepared] [{lo},{hi}) lanes={lanes}")
+        rc, ref = oracle.encode(w.symbols[lo:hi], w.indexes[lo:hi], w.cdf, w.lengths, w.offsets,
+                                lanes)
+        stream, nwords, status = B.encode_with_indexes(sym[lo:hi].contiguous(),
+                                                       idx[lo:hi].contiguous(), tables, lanes,
+                                                       workspace=ws, prepared=True)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        got = stream[: int(nwords.item())].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, ref)
+        out, status = B.decode_with_indexes(stream, idx[lo:hi].contiguous(), tables, lanes,
+                                            workspace=ws, prepared=True)
+        assert int(status.item()) == 0
+        assert np.array_equal(out.cpu().numpy(), w.symbols[lo:hi])
+
+
+# ------------------------------------------------------------------- errors
+def test_bad_index_reports_status():
+    import gpu_util as G
+    w, tables, sym, idx = _workload("tiny")
+    bad = w.indexes.copy()
+    bad[1234] = 8
+    G.say("[errors] bad index encode")
+    st, _, _ = G.gpu_encode(sym, G.to_dev(bad), tables, 64)
+    assert st == oracle.E_INDEX
+    rc, ref = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, 64)
+    bad[99] = -1
+    G.say("[errors] bad index decode")
+    st, _ = G.gpu_decode(ref, G.to_dev(bad), tables, 64)
+    assert st == oracle.E_INDEX
+    G.say("[errors] clean call after errors")
+    st, got, _ = G.gpu_encode(sym, idx, tables, 64)
+    assert st == 0 and np.array_equal(got, ref)
+
+
+def test_symbol_out_of_range_reports_status():
+    import gpu_util as G
+    w, tables, sym, idx = _workload("tiny")
+    s = w.symbols.copy()
+    r = int(w.indexes[77])
+    s[77] = np.int32(int(w.offsets[r]) - (1 << 30) - 1)
+    G.say("[errors] symbol out of range")
+    st, _, _ = G.gpu_encode(G.to_dev(s), idx, tables, 64)
+    assert st == oracle.E_SYMBOL_RANGE
+
+
+def test_bad_table_reports_status():
+    import gpu_util as G
+    w, _, sym, idx = _workload("tiny")
+    cdf = w.cdf.copy()
+    cdf[3, 5] = cdf[3, 4]          # zero frequency
+    tables = G.B.Tables.from_numpy(cdf, w.lengths, w.offsets, G.DEV)
+    G.say("[errors] bad table")
+    st, _, _ = G.gpu_encode(sym, idx, tables, 64)
+    assert st == oracle.E_TABLE
+    lengths = w.lengths.copy()
+    lengths[2] = 2
+    tables = G.B.Tables.from_numpy(w.cdf, lengths, w.offsets, G.DEV)
+    st, _, _ = G.gpu_encode(sym, idx, tables, 64)
+    assert st == oracle.E_TABLE
+
+
+def test_capacity_too_small_reports_status_and_stays_in_bounds():
+    import gpu_util as G
+    w, tables, sym, idx = _workload("tiny")
+    rc, ref = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, 64)
+    for cap in (ref.size - 1, 65 + 100, ref.size // 2):
+        G.say(f"[errors] capacity {cap}")
+        st, _, nw = G.gpu_encode(sym, idx, tables, 64, capacity=cap)
+        assert st == oracle.E_CAPACITY and nw == ref.size
+    st, got, _ = G.gpu_encode(sym, idx, tables, 64, capacity=ref.size)
+    assert st == 0 and np.array_equal(got, ref)
+
+
+def test_corrupt_streams_report_status():
+    import gpu_util as G
+    w, tables, sym, idx = _workload("tiny")
+    L = 4
+    rc, words = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, L)
+    G.say("[errors] corrupt streams")
+    assert G.gpu_decode(words, idx, tables, L)[0] == 0
+    assert G.gpu_decode(words, idx, tables, L + 1)[0] == oracle.E_CORRUPT
+    s = words.copy(); s[1], s[2] = s[2], s[1]
+    assert G.gpu_decode(s, idx, tables, L)[0] == oracle.E_CORRUPT
+    assert G.gpu_decode(words[:-1], idx, tables, L)[0] == oracle.E_CORRUPT
+    s = words[:-1].copy(); s[L] -= 1
+    assert G.gpu_decode(s, idx, tables, L)[0] == oracle.E_CORRUPT
+    s = np.concatenate([words, [123]]).astype(np.uint32); s[L] += 1
+    assert G.gpu_decode(s, idx, tables, L)[0] == oracle.E_CORRUPT
+    s = words.copy(); s[1] = 1
+    assert G.gpu_decode(s, idx, tables, L)[0] == oracle.E_CORRUPT
+    rng = np.random.default_rng(3)
+    for k in range(8):
+        s = words.copy()
+        pos = int(rng.integers(1 + L, s.size))
+        s[pos] ^= np.uint32(1 << int(rng.integers(0, 32)))
+        st, out = G.gpu_decode(s, idx, tables, L)
+        rco, outo = oracle.decode(s, w.indexes, w.cdf, w.lengths, w.offsets, L)
+        # both sides agree on acceptance; where both accept, outputs agree
+        assert (st == 0) == (rco == 0)
+        if st == 0:
+            assert np.array_equal(out, outo)
+    assert G.gpu_decode(words, idx, tables, L)[0] == 0
