@@ -1,0 +1,243 @@
+"""Benchmark: indexed rANS64 encode + decode of the 1080p y latent on one MI355X.
+
+One step is the whole coding path on one batch: table preparation + encode
+(rans_encode_with_indexes) and table preparation + decode
+(rans_decode_with_indexes) of 1,566,720 int32 symbols (192x68x120) with 64
+Gaussian 16-bit CDF rows at 4096 lanes -- the y latent of a 1920x1088 image
+in a mean-scale hyperprior (kompressor README, "Getting Started").  Inputs are
+synthetic, seeded, and resident in HBM before timing; the GPU output is
+checked byte for byte against the CPU oracle before anything is timed.
+
+value = symbols per step / step time (a step encodes and decodes every
+symbol once).  The roofline object reports the slower of the two coding
+kernels: algorithmic bytes per launch (8 B per symbol of int32 symbols and
+indexes plus the 4-byte container words) over its mean duration from HIP
+events recorded around that kernel on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "rANS encode/decode Gsymbol/s on 1080p y-latent (1.57M syms); % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+DEFAULT_LANES = {"tiny": 64, "z": 256, "y1080": 4096, "y1080x16": 65536, "y4kx8": 131072}
+DESCRIPTION = {
+    "tiny": "16,384 int32 symbols, 8 Gaussian CDF rows, 1% bypass",
+    "z": "z latent 192x17x30, 192 logistic CDF rows",
+    "y1080": "1080p y latent 192x68x120 = 1,566,720 int32 symbols, 64 Gaussian 16-bit CDF rows, "
+             "0.1% bypass",
+    "y1080x16": "16 x 1080p y latents = 25,067,520 symbols, 64 Gaussian CDF rows",
+    "y4kx8": "8 x 4K y latents 192x136x240 = 50,135,040 symbols, skewed scales, 0.5% bypass",
+}
+
+
+def kernel_source_hash(name: str) -> str:
+    """Hash of the sources that make up one kernel (traffic numbers go stale with them)."""
+    csrc = os.path.join(ROOT, "learned_image_compression_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("rans_internal.hpp", f"rans_{name}.hip"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, config: str, lanes: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{config}_L{lanes}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, lanes, min_seconds=10.0, max_reps=200):
+    """The oracle as it stands (single thread) on the full workload, repeated ~10 s."""
+    import oracle
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        rc, words = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, lanes)
+        rc2, out = oracle.decode(words, w.indexes, w.cdf, w.lengths, w.offsets, lanes)
+        times.append(time.perf_counter() - t0)
+        assert rc == 0 and rc2 == 0
+        if (time.perf_counter() - t_start >= min_seconds and len(times) >= 3) or len(times) >= max_reps:
+            break
+    med = statistics.median(times)
+    return {
+        "value": round(w.n / med / 1e9, 5),
+        "unit": "Gsymbol/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"whole {w.name} workload ({w.n} symbols, {lanes} lanes), encode+decode, "
+                  f"median of {len(times)} repetitions ({sum(times):.1f} s); "
+                  f"{med / w.n * 1e9:.2f} ns/symbol",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="y1080", choices=sorted(DEFAULT_LANES))
+    ap.add_argument("--lanes", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the lanes of one call are "
+              "coded on one device; DESIGN.md describes how the path would shard across GPUs.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+    from learned_image_compression_amd import binding as B
+
+    lanes = args.lanes or DEFAULT_LANES[args.config]
+    dev = torch.device("cuda:0")
+    w = workloads.load(args.config)
+    n = w.n
+    tables = B.Tables.from_numpy(w.cdf, w.lengths, w.offsets, dev)
+    sym = torch.from_numpy(w.symbols).to(dev)
+    idx = torch.from_numpy(w.indexes).to(dev)
+    cap = B.encode_bound_words(n, lanes)
+    stream = torch.empty(cap, dtype=torch.int32, device=dev)
+    nwords = torch.zeros(1, dtype=torch.int64, device=dev)
+    st_enc = torch.zeros(1, dtype=torch.int32, device=dev)
+    st_dec = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty(n, dtype=torch.int32, device=dev)
+    ws = B.workspace_for(dev).get(B.workspace_bytes(n, lanes, tables.num_tables, tables.stride))
+
+    # ---- parity before timing (byte-exact with the oracle) ----------------------
+    rc, ref = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, lanes)
+    assert rc == 0
+    B.encode_with_indexes(sym, idx, tables, lanes, stream_out=stream, stream_words=nwords,
+                          status=st_enc, workspace=ws)
+    B.check(st_enc, "encode")
+    total_words = int(nwords.item())
+    got = stream[:total_words].cpu().numpy().view(np.uint32)
+    assert total_words == ref.size and np.array_equal(got, ref), "GPU stream != oracle"
+    B.decode_with_indexes(stream, idx, tables, lanes, symbols_out=out, status=st_dec,
+                          workspace=ws, capacity_words=cap)
+    B.check(st_dec, "decode")
+    assert torch.equal(out.cpu(), torch.from_numpy(w.symbols)), "GPU decode != input"
+
+    # ---- one step = prep + encode, prep + decode (the two public entry points) ---
+    # The entry points are called straight through ctypes with arguments
+    # marshalled once, so the host adds as little as possible per launch.
+    import ctypes
+    lib = B.load()
+    vp = ctypes.c_void_p
+    hs = vp(torch.cuda.current_stream(dev).cuda_stream)
+    prep_args = (vp(tables.cdf.data_ptr()), vp(tables.lengths.data_ptr()),
+                 vp(tables.offsets.data_ptr()), tables.num_tables, tables.stride,
+                 vp(ws.data_ptr()), ws.numel(), hs)
+    enc_args = (vp(sym.data_ptr()), vp(idx.data_ptr()), n, tables.num_tables, tables.stride,
+                lanes, vp(stream.data_ptr()), cap, vp(nwords.data_ptr()), vp(st_enc.data_ptr()),
+                vp(ws.data_ptr()), ws.numel(), hs)
+    dec_args = (vp(stream.data_ptr()), cap, vp(idx.data_ptr()), n, tables.num_tables,
+                tables.stride, lanes, vp(out.data_ptr()), vp(st_dec.data_ptr()),
+                vp(ws.data_ptr()), ws.numel(), hs)
+    prep, enc, dec = lib.rans_prepare_tables, lib.rans_encode_prepared, lib.rans_decode_prepared
+
+    def step(ev):
+        rc = prep(*prep_args)
+        ev[0].record()
+        rc |= enc(*enc_args)
+        ev[1].record()
+        rc |= prep(*prep_args)
+        ev[2].record()
+        rc |= dec(*dec_args)
+        ev[3].record()
+        if rc:
+            raise RuntimeError(f"launch failed: {rc}")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        step(evs[k])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    B.check(st_enc, "encode (timed)")
+    B.check(st_dec, "decode (timed)")
+    assert int(nwords.item()) == total_words
+    assert torch.equal(out.cpu(), torch.from_numpy(w.symbols))
+
+    gpu_ms = start.elapsed_time(stop) / args.steps
+    ms_per_step = max(wall * 1e3 / args.steps, gpu_ms)
+    enc_us = statistics.mean(e[0].elapsed_time(e[1]) for e in evs) * 1e3
+    dec_us = statistics.mean(e[2].elapsed_time(e[3]) for e in evs) * 1e3
+    value = n / (ms_per_step * 1e-3) / 1e9
+
+    bytes_per_launch = 8 * n + 4 * total_words   # same for encode and decode
+    dominant, dom_us = ("decode", dec_us) if dec_us >= enc_us else ("encode", enc_us)
+    achieved = bytes_per_launch / (dom_us * 1e-6) / 1e9
+    traffic = measured_traffic(dominant, args.config, lanes)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "Gsymbol/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u64",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {DESCRIPTION[args.config]}", "lanes": lanes,
+                   "symbols": n, "container_words": total_words,
+                   "bits_per_symbol": round(32.0 * (total_words - 1 - lanes) / n, 4)},
+        "encode_gsym_s": round(n / (enc_us * 1e-6) / 1e9, 3),
+        "decode_gsym_s": round(n / (dec_us * 1e-6) / 1e9, 3),
+        "kernel_us": {"encode": round(enc_us, 2), "decode": round(dec_us, 2),
+                      "step_gpu": round(gpu_ms * 1e3, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"{dominant}_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 5),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+        },
+        "parity": "GPU container byte-exact with the CPU oracle; decode equals input",
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, lanes, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,10 +20,13 @@ constexpr uint64_t kStateLow = 1ull << 31;
 constexpr uint32_t kBypassBits = 4;
 constexpr int kWave = 64;
 
-// LDS: 160 KiB per workgroup on gfx950.  Tables get kTableBudget bytes, the
-// rest is left for per-kernel scratch.
+// LDS: 160 KiB per workgroup on gfx950.  Tables get kTableBudget bytes; the
+// coding kernels put a per-lane word ring of kRingWords words after them.
 constexpr uint32_t kLdsBytes = 160u * 1024u;
-constexpr uint32_t kTableBudget = 152u * 1024u;
+constexpr uint32_t kTableBudget = 140u * 1024u;
+constexpr uint32_t kRingWords = 8;
+constexpr uint32_t kMaxBlockThreads = 512;
+static_assert(kTableBudget + kRingWords * 4 * kMaxBlockThreads <= kLdsBytes, "LDS budget");
 constexpr uint32_t kMaxLutQ = 10;        // at most 1024 buckets per row
 
 constexpr uint32_t kHeaderBytes = 256;
@@ -98,11 +101,30 @@ inline __host__ __device__ uint64_t lane_begin(uint64_t n, uint32_t lanes, uint3
 // more lanes go into each block.
 inline uint32_t coding_block_threads(uint32_t lanes)
 {
-    uint64_t per_cu = (uint64_t(lanes) + 255) / 256;
-    uint64_t t = (per_cu + kWave - 1) / kWave * kWave;
-    if (t < 256) t = 256;
-    if (t > 1024) t = 1024;
-    return (uint32_t)t;
+    return lanes > 256u * 256u ? 512u : 256u;
+}
+inline uint32_t coding_lds_bytes(uint32_t tpb) { return kTableBudget + kRingWords * 4 * tpb; }
+
+// Copy `nbytes` (a multiple of 16) of prepared tables from global memory into
+// LDS with every thread keeping eight 16-byte loads in flight.
+template <int TPB>
+__device__ inline void stage_tables(uint8_t *lds, const uint8_t *src, uint32_t nbytes)
+{
+    const uint4 *s = reinterpret_cast<const uint4 *>(src);
+    uint4 *d = reinterpret_cast<uint4 *>(lds);
+    const uint32_t n16 = nbytes / 16;
+    if (n16 == 0)
+        return;
+    for (uint32_t i0 = threadIdx.x; i0 < n16; i0 += 8 * TPB) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = s[min(i0 + u * TPB, n16 - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (i0 + u * TPB < n16)
+                d[i0 + u * TPB] = v[u];
+    }
 }
 
 struct PrepArgs {

@@ -30,25 +30,13 @@ __device__ inline uint32_t row_value(const uint16_t *row, uint32_t k, uint32_t l
     return (k + 1 == len) ? kTotal : (uint32_t)row[k];
 }
 
-// First k in [0, len) with value(k) > c; value(len-1) = 65536 > c.
-__device__ inline uint32_t upper_bound_row(const uint16_t *row, uint32_t len, uint32_t c)
-{
-    uint32_t lo = 0, hi = len - 1;
-    while (lo < hi) {
-        uint32_t mid = (lo + hi) >> 1;
-        if (row_value(row, mid, len) > c)
-            hi = mid;
-        else
-            lo = mid + 1;
-    }
-    return lo;
-}
-
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
 {
     __shared__ uint32_t s_base[RANS_MAX_TABLES];
     __shared__ uint32_t s_part[kPrepThreads];
     __shared__ uint16_t s_row[RANS_MAX_STRIDE];
+    __shared__ uint32_t s_best[1u << kMaxLutQ];
+    __shared__ int32_t s_val[RANS_MAX_STRIDE];
 
     const int tid = threadIdx.x;
     const int K = a.num_tables;
@@ -132,17 +120,32 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
         const uint32_t base = s_base[r];
         const int32_t *row = a.cdf + (int64_t)r * stride;
         int bad = len_ok ? 0 : 1;
-        for (uint32_t k = tid; k < len; k += kPrepThreads) {
-            int32_t v = len_ok ? row[k] : (k == 0 ? 0 : (k == 1 ? 1 : (int32_t)kTotal));
-            if (len_ok) {
-                if (k == 0 && v != 0)
-                    bad = 1;
-                if (k + 1 == len && v != (int32_t)kTotal)
-                    bad = 1;
-                if (k > 0 && v <= row[k - 1])
-                    bad = 1;
+        // stage the row as int32 (eight loads in flight per thread), then check it
+        for (uint32_t k0 = tid; k0 < len; k0 += 8 * kPrepThreads) {
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t k = k0 + u * kPrepThreads;
+                v[u] = k < len ? (len_ok ? row[k] : (k == 0 ? 0 : (k == 1 ? 1 : (int32_t)kTotal)))
+                               : 0;
             }
-            uint16_t p = (uint16_t)(uint32_t)v;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t k = k0 + u * kPrepThreads;
+                if (k < len)
+                    s_val[k] = v[u];
+            }
+        }
+        __syncthreads();
+        for (uint32_t k = tid; k < len; k += kPrepThreads) {
+            const int32_t v = s_val[k];
+            if (k == 0 && v != 0)
+                bad = 1;
+            if (k + 1 == len && v != (int32_t)kTotal)
+                bad = 1;
+            if (k > 0 && v <= s_val[k - 1])
+                bad = 1;
+            const uint16_t p = (uint16_t)(uint32_t)v;
             cdf16[base + k] = p;
             s_row[k] = p;
         }
@@ -156,35 +159,39 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
             meta[r] = m;
         }
         if (dec_ok) {
-            for (uint32_t b = tid; b < (1u << q); b += kPrepThreads) {
+            // Best adjacent pair per bucket, by scatter: slot k proposes the pair
+            // (k, k+1) to every bucket it overlaps, scored by how much of the
+            // bucket the two slots cover; an LDS atomicMax keeps the best score
+            // (ties: lower k).  Buckets lying wholly in the escape slot keep the
+            // default pair (len-3, len-2).
+            const uint32_t nb = 1u << q;
+            const uint32_t amax = len - 3;
+            for (uint32_t b = tid; b < nb; b += kPrepThreads)
+                s_best[b] = 16383u - amax;   // score 0, slot amax
+            __syncthreads();
+            if (!bad) {
+                for (uint32_t k = tid; k <= amax; k += kPrepThreads) {
+                    const uint32_t s0 = row_value(s_row, k, len);
+                    const uint32_t s1 = row_value(s_row, k + 1, len);
+                    const uint32_t s2 = row_value(s_row, k + 2, len);
+                    for (uint32_t b = s0 >> (kPrecision - q); b <= (s1 - 1) >> (kPrecision - q); ++b) {
+                        const uint32_t lo = b * width, hi = lo + width;   // [lo, hi)
+                        const uint32_t c0 = min(s1, hi) - max(s0, lo);
+                        const uint32_t c1 = s1 < hi ? min(s2, hi) - s1 : 0u;
+                        atomicMax(&s_best[b], ((c0 + c1) << 14) | (16383u - k));
+                    }
+                }
+            }
+            __syncthreads();
+            for (uint32_t b = tid; b < nb; b += kPrepThreads) {
                 uint64_t e = 0;
                 if (!bad) {
-                    const uint32_t lo = b * width;
-                    const uint32_t hi = lo + width - 1;
-                    uint32_t first = upper_bound_row(s_row, len, lo) - 1;
-                    uint32_t last = upper_bound_row(s_row, len, hi) - 1;
-                    const uint32_t amax = len - 3;   // pair (a, a+1) with a+1 <= escape slot
-                    uint32_t best_a = first < amax ? first : amax;
-                    if (last > first && first < amax) {
-                        uint32_t kend = last - 1 < amax ? last - 1 : amax;
-                        uint32_t best = 0;
-                        for (uint32_t k = first; k <= kend; ++k) {
-                            uint32_t s0 = row_value(s_row, k, len);
-                            uint32_t s1 = row_value(s_row, k + 1, len);
-                            uint32_t s2 = row_value(s_row, k + 2, len);
-                            uint32_t c0 = min(s1, hi + 1) - max(s0, lo);
-                            uint32_t c1 = (s1 > hi) ? 0u : min(s2, hi + 1) - s1;
-                            if (c0 + c1 > best) {
-                                best = c0 + c1;
-                                best_a = k;
-                            }
-                        }
-                    }
-                    const uint32_t s0 = row_value(s_row, best_a, len);
-                    const uint32_t s1 = row_value(s_row, best_a + 1, len);
-                    const uint32_t s2 = row_value(s_row, best_a + 2, len);
+                    const uint32_t a = 16383u - (s_best[b] & 16383u);
+                    const uint32_t s0 = row_value(s_row, a, len);
+                    const uint32_t s1 = row_value(s_row, a + 1, len);
+                    const uint32_t s2 = row_value(s_row, a + 2, len);
                     e = (uint64_t)s0 | ((uint64_t)s1 << 16) | ((uint64_t)(s2 - 1) << 32) |
-                        ((uint64_t)best_a << 48);
+                        ((uint64_t)a << 48);
                 }
                 lut[((uint64_t)r << q) + b] = e;
             }

@@ -48,7 +48,7 @@ def test_bounds(lib):
         assert lib.rans_encode_bound_words(n, L) == 1 + L + 2 * n + 4 * L
         ws = lib.rans_workspace_bytes(n, L, 64, 3133)
         # header + table region + look-back flags + 2n+4L words of lane scratch
-        assert ws >= 256 + 152 * 1024 + 8 * ((L + 63) // 64) + 4 * (2 * n + 4 * L)
+        assert ws >= 256 + 140 * 1024 + 8 * ((L + 63) // 64) + 4 * (2 * n + 4 * L)
         assert ws % 4 == 0
 
 
