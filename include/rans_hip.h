@@ -69,9 +69,13 @@ enum rans_status {
     RANS_E_TABLE_SIZE = -9    /* the table set does not fit the LDS budget */
 };
 
-/* Largest supported table count and row stride. */
+/* Largest supported table count and row stride, and the largest symbol
+ * count and lane count of one call (larger inputs are split by the caller
+ * into several containers); beyond them a call returns RANS_E_ARG. */
 #define RANS_MAX_TABLES 4096
 #define RANS_MAX_STRIDE 16384
+#define RANS_MAX_SYMBOLS (1ull << 28)
+#define RANS_MAX_LANES (1u << 26)
 
 /* Words an encoded container can need in the worst case (every symbol an
  * escape with a 31-bit raw value): 1 + L header words plus, per lane,

@@ -25,10 +25,11 @@ int check_tables(const int32_t *cdf, const int32_t *lengths, const int32_t *offs
     return RANS_OK;
 }
 
-// The container stores cumulative lane ends as u32 words.
-bool fits_u32_payload(uint64_t n, uint32_t lanes)
+// Size limits of one call: the kernels address each wave's symbols, scratch
+// and stream words through 32-bit buffer offsets.
+bool sizes_ok(uint64_t n, uint32_t lanes)
 {
-    return n <= (1ull << 40) && ws_scratch_words(n, lanes) <= 0xFFFFFFFFull;
+    return n <= RANS_MAX_SYMBOLS && lanes <= RANS_MAX_LANES;
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? RANS_OK : RANS_E_HIP; }
@@ -75,7 +76,7 @@ int rans_encode_prepared(const int32_t *symbols, const int32_t *indexes, uint64_
     if (num_tables < 1 || num_tables > RANS_MAX_TABLES || cdf_stride < 3 ||
         cdf_stride > RANS_MAX_STRIDE)
         return RANS_E_TABLE;
-    if (!fits_u32_payload(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
+    if (!sizes_ok(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
         return RANS_E_ARG;
     int rc = check_workspace(workspace, workspace_bytes,
                              rans_workspace_bytes(n, num_lanes, num_tables, cdf_stride));
@@ -97,7 +98,7 @@ int rans_decode_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
     if (num_tables < 1 || num_tables > RANS_MAX_TABLES || cdf_stride < 3 ||
         cdf_stride > RANS_MAX_STRIDE)
         return RANS_E_TABLE;
-    if (n > (1ull << 40) || stream_capacity_words < 1ull + num_lanes)
+    if (!sizes_ok(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
         return RANS_E_ARG;
     // the decoder uses only the header and the prepared tables
     int rc = check_workspace(workspace, workspace_bytes, ws_flags_offset());
@@ -118,7 +119,7 @@ int rans_encode_with_indexes(const int32_t *symbols, const int32_t *indexes, uin
 {
     if (num_lanes == 0 || !stream || !stream_words || !status || (n && (!symbols || !indexes)))
         return RANS_E_ARG;
-    if (!fits_u32_payload(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
+    if (!sizes_ok(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
         return RANS_E_ARG;
     int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
     if (rc)
@@ -143,7 +144,7 @@ int rans_decode_with_indexes(const uint32_t *stream, uint64_t stream_capacity_wo
 {
     if (num_lanes == 0 || !stream || !status || (n && (!symbols || !indexes)))
         return RANS_E_ARG;
-    if (n > (1ull << 40) || stream_capacity_words < 1ull + num_lanes)
+    if (!sizes_ok(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
         return RANS_E_ARG;
     int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
     if (rc)

@@ -1,28 +1,34 @@
 // rans_decode.hip -- lane decoder: one rANS64 state per wavefront lane,
 // symbols read first to last, the symbol of each step found through the
-// LDS bucket lookup (one 8-byte read in the common case) with a binary
-// search over the LDS row as fallback.
+// LDS bucket lookup (one 8-byte read in the common case) with a short
+// search of the bucket's slots as fallback.
 //
 // Decoding rules (the inverse of the puts in rans_encode.hip; decode reads
 // the lane's words in order):
 //   cum = x mod 2^16; slot s with cdf[s] <= cum < cdf[s+1];
 //   x = f * (x >> 16) + cum - cdf[s]; if x < 2^31: x = (x << 32) | next word
-//   escape slot -> 4-bit gets: count nb (15 = continue), then nb raw groups,
-//   least significant first; odd raw -> -(raw>>1)-1, even -> (raw>>1)+mv
+//   escape slot -> 4-bit gets: count nb, then nb raw groups, least
+//   significant first; odd raw -> -(raw>>1)-1, even -> (raw>>1)+mv
 // (kompressor BENCHMARKS.md section 4 names the lookup as the decoder's cost:
 // CompressAI scans the row linearly, kompressor binary-searches it; torch_ans
 // "Usage" describes the inverse-CDF table keyed by the low state bits.)
 // A lane must end at x = 2^31 with all of its words consumed, otherwise the
 // call reports RANS_E_CORRUPT; reads never leave the lane's header extent.
 //
+// Per-symbol work.  The common step -- the bucket's pair holds cum, an
+// ordinary slot, the renormalisation word already in the LDS ring -- is
+// straight-line code whose result is committed at once.  Lanes outside it
+// (lookup miss, escape, drained ring, bad index) redo the step from the
+// saved state in one out-of-line branch, entered only when some lane of the
+// wave needs it.
+//
 // Memory schedule.  A lane works in rounds of kRound symbols.  Global memory
-// is touched only between rounds, in straight-line code: the indexes of the
-// round after next are requested, the finished round's symbols are stored,
-// and kRefill stream words are requested for the lane's word ring in LDS.
-// Every loaded register is first read one round after its load was issued,
-// so the state chain inside a round never waits on global memory.  The ring
-// (kRingWords words per lane) supplies renormalisation words; the next one
-// is kept in a register.  Should a lane drain its ring within one round
+// is touched only between rounds, in straight-line code with a fixed number
+// of accesses: the finished round's symbols are stored, the indexes of the
+// round after next are requested, and kRefill stream words are requested for
+// the lane's word ring in LDS.  Every loaded register is first read one
+// round after its load was issued, so the state chain inside a round never
+// waits on global memory.  Should a lane drain its ring within one round
 // (long bypass runs), it reads the word straight from global memory.
 #include "rans_internal.hpp"
 
@@ -32,6 +38,7 @@ namespace {
 
 constexpr int kRound = 8;        // symbols per lane between memory phases
 constexpr uint32_t kRefill = 4;  // words requested per lane per memory phase
+constexpr uint32_t kNoStore = 0x80000000u;   // a buffer offset past every buffer
 
 __device__ inline void record_error(WsHeader *hdr, int code)
 {
@@ -39,16 +46,16 @@ __device__ inline void record_error(WsHeader *hdr, int code)
 }
 
 // Per-lane stream words: [0, count) of the lane, ring slots in LDS.
+template <int TPB>
 struct Words {
     const uint32_t *w;   // the lane's words in global memory
-    uint32_t *ring;      // ring slot 0 of this lane (slots are `stride` words apart)
-    uint32_t stride;     // threads per block
+    uint32_t *ring;      // ring slot 0 of this lane (slots are TPB words apart)
     uint32_t count;      // words in the lane
     uint32_t pos;        // next word to consume
     uint32_t filled;     // words [.., filled) have been written to the ring
     uint32_t next;       // ring word at pos (valid when pos < filled)
 
-    __device__ inline uint32_t slot(uint32_t p) const { return (p % kRingWords) * stride; }
+    __device__ inline uint32_t *slot(uint32_t p) const { return ring + (p % kDecRing) * TPB; }
 
     // x < 2^31 after a step means the encoder spilled a word there.
     __device__ inline bool refill(uint64_t &x)
@@ -67,79 +74,176 @@ struct Words {
             }
             ++pos;
         }
-        next = ring[slot(pos)];
+        next = *slot(pos);
         return true;
     }
 };
 
-// One decoding step of one lane; writes the symbol to `out`; returns a status.
-__device__ __forceinline__ int decode_symbol(int32_t r, uint64_t &x, Words &wd,
-                                             const RowMeta *meta, const uint16_t *cdf16,
-                                             const uint64_t *lut, uint32_t shift, uint32_t K,
-                                             int32_t &out)
+// Decoder tables in LDS.
+struct DecTables {
+    const uint8_t *lds;      // the decoder set [meta | cdf16 | lut | first]
+    const RowMeta *meta;
+    const uint16_t *cdf16;
+    const uint16_t *first;   // per bucket: the slot holding its lowest cumulative value
+    uint32_t q;              // 2^q buckets per row
+    uint32_t shift;          // 16 - q: cumulative value -> bucket
+    uint32_t K;
+};
+
+// Slow step of one lane, from the state before the step; `ent` is the row's
+// lookup entry for cum.  The lanes in here are few, so the code keeps to
+// straight-line work with a handful of wave-uniform branches:
+//  * a lookup miss searches the bucket's slots [first[b], first[b+1]] (the
+//    escape slot mv for the last bucket), eight slot starts per LDS round
+//    trip;
+//  * the renormalisation word and an escape's groups need at most three
+//    words (after the step x >= 2^31, and nb <= 8 groups of 4 bits follow),
+//    read from the ring when it holds them, else on the checked path;
+//  * out-of-range values and bad indexes are reported.
+// Writes the symbol to `out`; returns a status.
+template <int TPB>
+__device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint64_t ent,
+                                           uint32_t bucket, uint64_t &x, Words<TPB> &wd,
+                                           const DecTables &t, int32_t &out)
 {
-    if ((uint32_t)r >= K)
+    if ((uint32_t)r >= t.K)
         return RANS_E_INDEX;
-    const RowMeta m = meta[r];
+    const uint32_t mv = m.mvf & 0xFFFFu;
     const uint32_t cum = (uint32_t)x & (kTotal - 1);
-    const uint64_t ent = lut[m.lut_base + (cum >> shift)];
     const uint32_t s0 = (uint32_t)ent & 0xFFFFu;
-    const uint32_t s1 = (uint32_t)(ent >> 16) & 0xFFFFu;
-    const uint32_t e1 = (uint32_t)(ent >> 32) & 0xFFFFu;
-    uint32_t slot, start, f;
-    if (cum >= s0 && cum <= e1) {
-        const bool second = cum >= s1;
-        slot = (uint32_t)(ent >> 48) + (second ? 1u : 0u);
-        start = second ? s1 : s0;
-        f = second ? e1 + 1 - s1 : s1 - s0;
-    } else {
-        // value(lo) <= cum < value(hi), with value(mv + 1) = 65536
-        const uint16_t *row = cdf16 + m.cdf_base;
-        uint32_t lo = 0, hi = m.mv + 1;
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if ((uint32_t)row[mid] <= cum)
-                lo = mid;
-            else
-                hi = mid;
+    const uint32_t d1 = (uint32_t)(ent >> 16) & 0xFFFFu;
+    const uint32_t span = (uint32_t)(ent >> 32) & 0xFFFFu;
+    const uint32_t dt = cum - s0;
+    const bool hit = dt <= span;
+    const bool second = dt >= d1;
+    uint32_t slot = (uint32_t)(ent >> 48) + (second ? 1u : 0u);
+    uint32_t start = second ? s0 + d1 : s0;
+    uint32_t f = second ? span + 1 - d1 : d1;
+    if (__ballot(!hit) != 0) {
+        const uint16_t *row = t.cdf16 + m.base;
+        const uint16_t *fst = t.first + ((uint64_t)(uint32_t)r << t.q);
+        uint32_t lo = fst[bucket];
+        const uint32_t hi = (bucket + 1 < (1u << t.q)) ? (uint32_t)fst[bucket + 1] : mv;
+        // value(lo) <= cum; the slot is the last k in [lo, hi] with value(k) <= cum
+        uint32_t c;
+        do {
+            c = 0;
+#pragma unroll
+            for (uint32_t k = 1; k <= 8; ++k) {
+                const uint32_t v = row[min(lo + k, hi)];
+                c += (lo + k <= hi && v <= cum) ? 1u : 0u;
+            }
+            lo += c;
+        } while (c == 8 && lo < hi);
+        const uint32_t st = row[lo];
+        const uint32_t nx = (lo == mv) ? kTotal : (uint32_t)row[lo + 1];
+        if (!hit) {
+            slot = lo;
+            start = st;
+            f = nx - st;
         }
-        slot = lo;
-        start = row[lo];
-        const uint32_t nxt = (lo == m.mv) ? kTotal : (uint32_t)row[lo + 1];
-        f = nxt - start;
     }
     x = (uint64_t)f * (x >> kPrecision) + (cum - start);
-    if (!wd.refill(x))
-        return RANS_E_CORRUPT;
     int64_t value = slot;
-    if (slot == m.mv) {
-        uint32_t t = (uint32_t)x & 15u;
-        x >>= kBypassBits;
-        bool ok = wd.refill(x);
-        uint32_t nb = t;
-        while (ok && t == 15u && nb <= 8u) {
-            t = (uint32_t)x & 15u;
+    int err = 0;
+    if (wd.pos + 3 <= wd.filled) {
+        // the next three words are in the ring
+        uint32_t q0 = wd.next, q1 = *wd.slot(wd.pos + 1), q2 = *wd.slot(wd.pos + 2);
+        uint32_t used = 0;
+        auto renorm = [&]() {
+            const bool need = x < kStateLow;
+            x = need ? ((x << 32) | q0) : x;
+            q0 = need ? q1 : q0;
+            q1 = need ? q2 : q1;
+            used += need ? 1u : 0u;
+        };
+        renorm();
+        if (slot == mv) {
+            uint32_t nb = (uint32_t)x & 15u;
             x >>= kBypassBits;
-            ok = wd.refill(x);
-            nb += t;
-        }
-        uint64_t raw = 0;
-        if (ok && nb <= 8u) {
-            for (uint32_t g = 0; g < nb && ok; ++g) {
-                raw |= (uint64_t)((uint32_t)x & 15u) << (kBypassBits * g);
-                x >>= kBypassBits;
-                ok = wd.refill(x);
+            renorm();
+            if (nb > 8u) {   // raw < 2^31 needs at most 8 groups
+                err = RANS_E_CORRUPT;
+                nb = 0;
             }
+            uint32_t raw = 0;
+            for (uint32_t k = 0; k < nb; ++k) {
+                raw |= ((uint32_t)x & 15u) << (kBypassBits * k);
+                x >>= kBypassBits;
+                renorm();
+            }
+            if (raw >= (1u << 31))
+                err = RANS_E_CORRUPT;
+            value = (raw & 1) ? -(int64_t)(raw >> 1) - 1 : (int64_t)(raw >> 1) + mv;
         }
-        if (!ok || nb > 8u || raw >= (1ull << 31))
+        wd.pos += used;
+    } else {
+        // near the end of the ring (or of the lane): one word at a time
+        if (!wd.refill(x))
             return RANS_E_CORRUPT;
-        value = (raw & 1) ? -(int64_t)(raw >> 1) - 1 : (int64_t)(raw >> 1) + m.mv;
+        if (slot == mv) {
+            const uint32_t nb = (uint32_t)x & 15u;
+            x >>= kBypassBits;
+            if (!wd.refill(x) || nb > 8u)
+                return RANS_E_CORRUPT;
+            uint64_t raw = 0;
+            for (uint32_t k = 0; k < nb; ++k) {
+                raw |= (uint64_t)((uint32_t)x & 15u) << (kBypassBits * k);
+                x >>= kBypassBits;
+                if (!wd.refill(x))
+                    return RANS_E_CORRUPT;
+            }
+            if (raw >= (1ull << 31))
+                return RANS_E_CORRUPT;
+            value = (raw & 1) ? -(int64_t)(raw >> 1) - 1 : (int64_t)(raw >> 1) + mv;
+        }
     }
     const int64_t sym = value + m.offset;
     if (sym < INT32_MIN || sym > INT32_MAX)
-        return RANS_E_CORRUPT;
+        err = RANS_E_CORRUPT;
     out = (int32_t)sym;
-    return 0;
+    return err;
+}
+
+// One decoding step of one lane: the common case is computed and committed
+// for every lane; lanes outside it redo the step on the general path.  A bad
+// row index arrives with a fast bound of 0, so it takes the general path.
+template <int TPB>
+__device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_t &x, Words<TPB> &wd,
+                                            const DecTables &t, int32_t &out, int &lerr)
+{
+    const uint32_t cum = (uint32_t)x & (kTotal - 1);
+    const uint32_t bucket = cum >> t.shift;
+    const uint64_t ent = *reinterpret_cast<const uint64_t *>(t.lds + m.lut + (bucket << 3));
+    const uint32_t elo = (uint32_t)ent, ehi = (uint32_t)(ent >> 32);
+    const uint32_t s0 = elo & 0xFFFFu, d1 = elo >> 16;
+    const uint32_t span = ehi & 0xFFFFu, a = ehi >> 16;
+    const uint32_t dt = cum - s0;
+    const bool second = dt >= d1;
+    const uint32_t slot = a + (second ? 1u : 0u);
+    const uint32_t f = second ? span + 1 - d1 : d1;
+    const uint32_t rr = second ? dt - d1 : dt;
+    // f * (x >> 16) + rr with x >> 16 < 2^48 split at bit 32
+    const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
+    const uint32_t mid = __builtin_amdgcn_alignbit(xhi, xlo, 16);
+    uint64_t xn = (uint64_t)f * mid + rr;
+    xn += (uint64_t)__umul24(f, xhi >> 16) << 32;
+    const bool need = xn < kStateLow;
+    const bool slow = (dt > span) | (slot >= (m.mvf >> 16)) | (need & (wd.pos >= wd.filled));
+    const uint64_t x0 = x;
+    const uint32_t pos0 = wd.pos;
+    x = need ? ((xn << 32) | wd.next) : xn;
+    wd.pos = pos0 + (need ? 1u : 0u);
+    out = (int32_t)(slot + (uint32_t)m.offset);
+    if (__builtin_expect(__ballot(slow) != 0, 0)) {
+        if (slow) {
+            x = x0;
+            wd.pos = pos0;
+            const int ec = decode_slow<TPB>(r, m, ent, bucket, x, wd, t, out);
+            lerr = lerr ? lerr : ec;
+        }
+    }
+    wd.next = *wd.slot(wd.pos);
 }
 
 template <int TPB>
@@ -163,16 +267,20 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     const uint32_t q = hdr->lut_q;
     stage_tables<TPB>(lds, tab, nbytes);
     __syncthreads();
-    const RowMeta *meta = reinterpret_cast<const RowMeta *>(lds);
-    const uint32_t meta_bytes = (uint32_t)align_up(16ull * K, 16);
-    const uint16_t *cdf16 = reinterpret_cast<const uint16_t *>(lds + meta_bytes);
-    const uint64_t *lut = reinterpret_cast<const uint64_t *>(
-        lds + meta_bytes + align_up(2ull * hdr->total_len, 16));
-    uint32_t *ring = reinterpret_cast<uint32_t *>(lds + kTableBudget) + tid;
+    DecTables t;
+    t.lds = lds;
+    t.meta = reinterpret_cast<const RowMeta *>(lds);
+    t.cdf16 = reinterpret_cast<const uint16_t *>(lds + align_up(16ull * K, 16));
+    t.first = reinterpret_cast<const uint16_t *>(lds + align_up(16ull * K, 16) +
+                                                 align_up(2ull * hdr->total_len, 16) + (8ull * K << q));
+    t.q = q;
+    t.shift = kPrecision - q;
+    t.K = K;
+    uint32_t *ring = reinterpret_cast<uint32_t *>(lds + kDecTableBudget) + tid;
     int bad = 0;
     if (!herr)
         for (uint32_t r = tid; r < K; r += TPB)
-            bad |= (meta[r].mv & kRowInvalid) ? 1 : 0;
+            bad |= (t.meta[r].lut & kRowInvalid) ? 1 : 0;
     bad = __syncthreads_or(bad);
     if (!herr && bad)
         herr = RANS_E_TABLE;
@@ -180,121 +288,153 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
         record_error(hdr, herr);
 
     const uint32_t j = blockIdx.x * TPB + tid;
-    if (!herr && j < L) {
-        int lerr = 0;
-        const uint64_t beg_w = j ? a.stream[j] : 0u;
-        const uint64_t end_w = a.stream[1 + j];
-        if (a.stream[0] != L || end_w < beg_w + 2 || 1ull + L + end_w > a.capacity) {
-            lerr = RANS_E_CORRUPT;
-        } else {
-            Words wd;
-            wd.w = a.stream + 1 + L + beg_w;
-            wd.ring = ring;
-            wd.stride = TPB;
-            wd.count = (uint32_t)(end_w - beg_w);
-            const uint32_t last_w = wd.count - 1;
-            uint64_t x = (uint64_t)wd.w[0] | ((uint64_t)wd.w[1] << 32);
-            // first ring fill: words [2, 2 + kRingWords)
-            {
-                uint32_t v[kRingWords];
+    // the wave's index and symbol spans, and its stream words, as buffers
+    const uint32_t j0 = __builtin_amdgcn_readfirstlane(j) & ~(uint32_t)(kWave - 1);
+    if (!herr && j0 < L) {
+        const uint32_t j1 = min(j0 + kWave, L);
+        const uint64_t bw = lane_begin(a.n, L, j0), ew = lane_begin(a.n, L, j1);
+        const Rsrc ridx = make_rsrc(a.indexes + bw, (uint32_t)(4 * (ew - bw)));
+        const Rsrc rout = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
+        const uint64_t wbase = j0 ? a.stream[j0] : 0u;   // the wave's first word
+        const uint64_t wavail = a.capacity - 1 - L;
+        const uint64_t wbytes = wbase < wavail ? min(4 * (wavail - wbase), 1ull << 31) : 0;
+        const Rsrc rstr = make_rsrc(a.stream + 1 + L + (wbase < wavail ? wbase : 0), (uint32_t)wbytes);
+        if (j < L) {
+            int lerr = 0;
+            const uint64_t beg_w = j ? a.stream[j] : 0u;
+            const uint64_t end_w = a.stream[1 + j];
+            if (a.stream[0] != L || end_w < beg_w + 2 || 1ull + L + end_w > a.capacity ||
+                beg_w < wbase) {
+                lerr = RANS_E_CORRUPT;
+            } else {
+                Words<TPB> wd;
+                wd.w = a.stream + 1 + L + beg_w;
+                wd.ring = ring;
+                wd.count = (uint32_t)(end_w - beg_w);
+                const uint32_t lw = (uint32_t)(4 * (beg_w - wbase));   // the lane's words in rstr
+                // words 0, 1: the final state; words [2, 2 + kDecRing): the first ring fill
+                const u32x4 w0 = buf_load4(rstr, lw), w1 = buf_load4(rstr, lw + 16);
+                const u32x4 w2 = buf_load4(rstr, lw + 32);
+                uint64_t x = (uint64_t)w0[0] | ((uint64_t)w0[1] << 32);
+                {
+                    static_assert(kDecRing == 8, "ring fill below assumes 8 slots");
+                    const uint32_t v[kDecRing] = {w0[2], w0[3], w1[0], w1[1], w1[2], w1[3], w2[0], w2[1]};
 #pragma unroll
-                for (uint32_t k = 0; k < kRingWords; ++k)
-                    v[k] = wd.w[min(2 + k, last_w)];
-#pragma unroll
-                for (uint32_t k = 0; k < kRingWords; ++k)
-                    ring[((2 + k) % kRingWords) * TPB] = v[k];
-            }
-            wd.pos = 2;
-            wd.filled = min(wd.count, 2u + kRingWords);
-            wd.next = ring[wd.slot(2)];
-            uint32_t pend[kRefill];
-            uint32_t pend_at = wd.filled;
+                    for (uint32_t k = 0; k < kDecRing; ++k)
+                        *wd.slot(2 + k) = v[k];
+                }
+                wd.pos = 2;
+                wd.filled = min(wd.count, 2u + kDecRing);
+                wd.next = *wd.slot(2);
+                uint32_t pend[kRefill];
+                uint32_t pend_at = wd.filled;
 
-            const uint64_t b = lane_begin(a.n, L, j);
-            const uint64_t e = lane_begin(a.n, L, j + 1);
-            const uint64_t last_i = e > b ? e - 1 : b;
-            const uint32_t shift = kPrecision - q;
-            // Two index buffers used in turn (no register copies between rounds):
-            // a buffer is refilled in the memory phase right after its round
-            // and read again two rounds later.  Every memory phase issues the
-            // same global accesses in the same order (8 stores, 8 index loads,
-            // kRefill word loads), and the prologue runs two such phases too, so
-            // the compiler's wait counts only ever cover requests that are at
-            // least a round old.  Empty lanes (n may be 0 with null arrays) use
-            // a dummy word of the workspace header instead.
-            const bool any = e > b;
-            const int32_t *ixp = any ? a.indexes : reinterpret_cast<const int32_t *>(hdr->pad0);
-            int32_t *sdp = any ? a.symbols : reinterpret_cast<int32_t *>(hdr->pad0);
-            const uint64_t ix0 = any ? b : 0, ixl = any ? last_i : 0;
-            int32_t ia[kRound], ib[kRound], out[kRound];
-#pragma unroll
-            for (int u = 0; u < kRound; ++u)
-                out[u] = 0;
-            // last to first with clamped positions: filler stores to the lane's
-            // last position precede its true value
-            // (a phase after the lane's last symbol stores to a dummy word)
-            int32_t *dummy = reinterpret_cast<int32_t *>(hdr->pad0);
-            auto store_out = [&](uint64_t i0) {
-                int32_t *base = i0 < e ? sdp : dummy;
-                const uint64_t lim = i0 < e ? ixl : 0;
-#pragma unroll
-                for (int u = kRound - 1; u >= 0; --u)
-                    base[min(i0 + u, lim)] = out[u];
-            };
-            auto load_next = [&](int32_t (&idx)[kRound], uint64_t ip) {
+                const uint64_t b = lane_begin(a.n, L, j);
+                const uint64_t e = lane_begin(a.n, L, j + 1);
+                const uint32_t nj = (uint32_t)(e - b);
+                const uint32_t ob = (uint32_t)(4 * (b - bw));   // the lane's first position
+                // Two index buffers used in turn (no register copies between
+                // rounds): a buffer is refilled in the memory phase right after
+                // its round and read again two rounds later.  Every memory phase
+                // issues the same global accesses in the same order (8 stores, 8
+                // index loads, kRefill word loads), and the prologue runs two
+                // such phases too, so the compiler's wait counts only ever cover
+                // requests that are at least a round old.  Loads past the
+                // wave's span read 0; stores meant for nothing use kNoStore.
+                int32_t ia[kRound], ib[kRound], out[kRound];
 #pragma unroll
                 for (int u = 0; u < kRound; ++u)
-                    idx[u] = ixp[min(ip + u, ixl)];
-#pragma unroll
-                for (uint32_t k = 0; k < kRefill; ++k)
-                    pend[k] = wd.w[min(wd.filled + k, last_w)];
-                pend_at = wd.filled;
-                __builtin_amdgcn_sched_barrier(0);
-            };
-            auto ring_refill = [&]() {
-                if (pend_at == wd.filled && wd.filled + kRefill <= wd.pos + kRingWords) {
-#pragma unroll
-                    for (uint32_t k = 0; k < kRefill; ++k)
-                        ring[((wd.filled + k) % kRingWords) * TPB] = pend[k];
-                    wd.filled = min(wd.count, wd.filled + kRefill);
-                }
-                if (wd.filled < wd.pos)   // the lane outran its ring via direct reads
-                    wd.filled = wd.pos;
-                wd.next = ring[wd.slot(wd.pos)];
-            };
-            auto round = [&](int32_t (&idx)[kRound], uint64_t i0) {
-#pragma unroll
-                for (int u = 0; u < kRound; ++u) {
                     out[u] = 0;
-                    if (i0 + u < e && !lerr)
-                        lerr = decode_symbol(idx[u], x, wd, meta, cdf16, lut, shift, K, out[u]);
+                // a full round's symbols: two 16-byte stores; a partial round:
+                // one store per position (stores past the lane's end go nowhere)
+                auto store_full = [&](uint32_t k0) {
+                    buf_store4(rout, ob + 4 * k0,
+                               u32x4{(uint32_t)out[0], (uint32_t)out[1], (uint32_t)out[2], (uint32_t)out[3]});
+                    buf_store4(rout, ob + 4 * k0 + 16,
+                               u32x4{(uint32_t)out[4], (uint32_t)out[5], (uint32_t)out[6], (uint32_t)out[7]});
+                };
+                auto store_part = [&](uint32_t k0) {
+#pragma unroll
+                    for (int u = 0; u < kRound; ++u)
+                        buf_store(rout, k0 + u < nj ? ob + 4 * (k0 + u) : kNoStore, 0, out[u]);
+                };
+                // indexes of positions k .. k+7 and kRefill stream words: 16-byte
+                // loads (past the wave's span or the stream they read 0)
+                static_assert(kRefill == 4, "one 16-byte load of stream words");
+                auto load_next = [&](int32_t (&idx)[kRound], uint32_t k) {
+                    const u32x4 i0 = buf_load4(ridx, ob + 4 * k), i1 = buf_load4(ridx, ob + 4 * k + 16);
+                    const u32x4 w = buf_load4(rstr, lw + 4 * wd.filled);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        idx[u] = (int32_t)i0[u];
+                        idx[4 + u] = (int32_t)i1[u];
+                        pend[u] = w[u];
+                    }
+                    pend_at = wd.filled;
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                auto ring_refill = [&]() {
+                    if (pend_at == wd.filled && wd.filled + kRefill <= wd.pos + kDecRing) {
+#pragma unroll
+                        for (uint32_t k = 0; k < kRefill; ++k)
+                            *wd.slot(wd.filled + k) = pend[k];
+                        wd.filled = min(wd.count, wd.filled + kRefill);
+                    }
+                    if (wd.filled < wd.pos)   // the lane outran its ring via direct reads
+                        wd.filled = wd.pos;
+                    wd.next = *wd.slot(wd.pos);
+                };
+                auto round = [&](int32_t (&idx)[kRound], uint32_t k0) {
+                    RowMeta m[kRound];
+#pragma unroll
+                    for (int u = 0; u < kRound; ++u) {
+                        m[u] = t.meta[min((uint32_t)idx[u], K - 1)];
+                        if ((uint32_t)idx[u] >= K)
+                            m[u].mvf = 0;
+                    }
+                    if (__all(k0 + kRound <= nj)) {
+                        // a full round for every lane of the wave
+#pragma unroll
+                        for (int u = 0; u < kRound; ++u)
+                            decode_step<TPB>(idx[u], m[u], x, wd, t, out[u], lerr);
+                        __builtin_amdgcn_sched_barrier(0);
+                        ring_refill();
+                        store_full(k0);
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < kRound; ++u) {
+                            out[u] = 0;
+                            if (k0 + u < nj && !lerr)
+                                decode_step<TPB>(idx[u], m[u], x, wd, t, out[u], lerr);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        ring_refill();
+                        store_part(k0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_next(idx, k0 + 2 * kRound);
+                };
+                // prologue: two phases of the same shape (stores to nothing)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+#pragma unroll
+                    for (int u = 0; u < kRound; ++u)
+                        buf_store(rout, kNoStore, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_next(p ? ib : ia, p * kRound);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                // ---- memory phase ----
-                ring_refill();
-                store_out(i0);
-                __builtin_amdgcn_sched_barrier(0);
-                load_next(idx, i0 + 2 * kRound);
-            };
-            // prologue: two phases of the same shape (zeros go to the lane's
-            // first positions and are overwritten by the true symbols later)
-            store_out(ix0);
-            __builtin_amdgcn_sched_barrier(0);
-            load_next(ia, ix0);
-            store_out(ix0);
-            __builtin_amdgcn_sched_barrier(0);
-            load_next(ib, ix0 + kRound);
-            // both rounds always run (symbols past the lane end are skipped inside),
-            // so every path back to the loop head passes both memory phases
-            for (uint64_t i0 = b; i0 < e && !lerr; i0 += 2 * kRound) {
-                round(ia, i0);
-                round(ib, i0 + kRound);
+                // both rounds always run (symbols past the lane end are skipped inside),
+                // so every path back to the loop head passes both memory phases
+                for (uint32_t k0 = 0; k0 < nj && !lerr; k0 += 2 * kRound) {
+                    round(ia, k0);
+                    round(ib, k0 + kRound);
+                }
+                if (!lerr && (x != kStateLow || wd.pos != wd.count))
+                    lerr = RANS_E_CORRUPT;
             }
-            if (!lerr && (x != kStateLow || wd.pos != wd.count))
-                lerr = RANS_E_CORRUPT;
+            if (lerr)
+                record_error(hdr, lerr);
         }
-        if (lerr)
-            record_error(hdr, lerr);
     }
 
     // ---- completion: the last block publishes status and cleans up -------------
@@ -317,7 +457,7 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
 template <int TPB>
 hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s)
 {
-    const uint32_t lds_bytes = coding_lds_bytes(TPB);
+    const uint32_t lds_bytes = decode_lds_bytes(TPB);
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&decode_kernel<TPB>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);

@@ -13,12 +13,29 @@
 //   a lane's puts are applied last to first starting from x = 2^31.
 //
 // Mapping to gfx950: one lane of a wavefront owns one rANS lane, with its
-// 64-bit state in a VGPR pair; the packed u16 CDF rows and row metadata are
+// 64-bit state in a VGPR pair; row metadata and per-slot (start, f) pairs are
 // staged once per workgroup into LDS; a lane spills words backwards into its
 // own scratch segment.  Waves take tickets in arrival order, publish their
 // word total, look back over earlier tickets for their offset (no grid-wide
 // barrier, no second launch), then write their header entries and copy
 // their lanes' words into the contiguous container.
+//
+// Per-symbol work.  A lane codes in rounds of kRound positions.  Everything
+// that does not depend on the state -- row metadata, the slot's pair, the
+// reciprocal of f, whether the symbol is an ordinary one -- is computed for
+// the whole round first.  When every lane of the wave has a full round of
+// ordinary symbols, the state chain runs with no branch and no LDS access:
+// a symbol spills at most one word, which waits in a register together with
+// its scratch position.  Other rounds take each escaped (or erroneous)
+// symbol through the general puts, which store their words directly.
+//
+// Memory schedule.  Global memory is touched only between rounds, in
+// straight-line code with a fixed number of accesses: the round's candidate
+// words are stored (a symbol that spilled nothing stores to a position that
+// a later word overwrites, or to the lane's last scratch word), and the
+// symbols and indexes of the round after next are requested.  A loaded
+// register is first read a round after its load was issued, so the state
+// chain never waits on global memory.
 #include "rans_internal.hpp"
 
 namespace rans {
@@ -36,48 +53,7 @@ __device__ inline void record_error(WsHeader *hdr, int code)
 }
 
 constexpr int kRound = 8;   // positions per lane between memory phases
-
-// Spilled words of one lane.  Word k of the lane (k-th spill) belongs at
-// top[-1 - k] in global scratch; until the next memory phase it waits in the
-// lane's LDS ring (kRingWords words), or is stored directly if the ring is full.
-struct Spill {
-    uint32_t *top;      // one past the lane's scratch segment
-    uint32_t *ring;     // ring slot 0 of this lane (slots are `stride` words apart)
-    uint32_t stride;    // threads per block
-    uint32_t count;     // words spilled so far
-    uint32_t flushed;   // words [0, flushed) are in global scratch (or stored directly)
-    uint32_t cap;       // segment size (keeps 2 words for the final state)
-    bool overflow;
-
-    __device__ inline void put(uint32_t w)
-    {
-        if (count + 2 >= cap) {
-            overflow = true;
-        } else if (count - flushed < kRingWords) {
-            ring[(count % kRingWords) * stride] = w;
-        } else {
-            top[-1 - (int64_t)count] = w;
-        }
-        ++count;
-    }
-
-    // Move the ring's words to global scratch.  Always eight stores (a fixed
-    // count keeps the compiler's wait counts exact): slots without a word
-    // write filler to not-yet-used positions of the lane's segment, which are
-    // rewritten later by spills or the final state, or never copied out.
-    __device__ inline void flush()
-    {
-        // words at or past cap - 2 were never kept (overflow, reported)
-        const uint32_t upto = min(min(count, flushed + kRingWords), cap - 2);
-#pragma unroll
-        for (uint32_t k = 0; k < kRingWords; ++k) {
-            const uint32_t idx = flushed + k;
-            const uint32_t at = idx < upto ? idx : min(idx, cap - 1);
-            top[-1 - (int64_t)at] = ring[(idx % kRingWords) * stride];
-        }
-        flushed = count;
-    }
-};
+constexpr uint32_t kNoStore = 0x80000000u;   // a buffer offset past every buffer
 
 // Reciprocal of f in fp64 for the quotient estimate: the hardware estimate
 // refined by two Newton-Raphson steps r <- r + r(1 - f r), which square the
@@ -112,22 +88,81 @@ __device__ inline uint64_t reg_step(uint64_t x, uint32_t start, uint32_t f, doub
     return (q << kPrecision) + (uint32_t)r + start;
 }
 
-__device__ inline void put_reg(uint64_t &x, uint32_t start, uint32_t f, double rcp, Spill &sp)
+// Encoder tables in LDS: [meta | pairs], pair = start | f << 16.
+struct EncTables {
+    const uint8_t *lds;
+    const RowMeta *meta;
+    uint32_t K;
+};
+
+__device__ inline uint32_t pair_of(const EncTables &t, const RowMeta &m, uint32_t slot)
 {
-    if (x >= ((uint64_t)f << (63 - kPrecision))) {
-        sp.put((uint32_t)x);
-        x >>= 32;
-    }
-    x = reg_step(x, start, f, rcp);
+    return *reinterpret_cast<const uint32_t *>(t.lds + m.base + 4 * slot);
 }
 
-__device__ inline void put_bits(uint64_t &x, uint32_t b, Spill &sp)
-{
-    if (x >= (1ull << (63 - kBypassBits))) {
-        sp.put((uint32_t)x);
-        x >>= 32;
+// Spill state of one lane.  Word k of the lane (its k-th spill) belongs at
+// byte offset top - 4 - 4k of the wave's scratch buffer.  During a round the
+// spilled words wait in the lane's LDS ring (slot i holds the round's i-th
+// word; slots are TPB words apart); the memory phase stores them.
+template <int TPB>
+struct Spill {
+    Rsrc scr;           // the wave's scratch segments
+    uint32_t *ring;     // the lane's ring slot 0
+    uint32_t top;       // byte offset one past the lane's segment
+    uint32_t cb;        // 4 * words spilled so far
+    uint32_t cb0;       // cb at the start of the round
+    uint32_t capb;      // 4 * segment size (the last 2 words hold the final state)
+    bool overflow;
+
+    __device__ inline uint32_t *slot(uint32_t i) const { return ring + i * TPB; }
+
+    // Spill the low word when `spill`.  The ring slot is written either way
+    // (a slot past the round's words is never stored), so there is no branch.
+    __device__ inline void put_if(bool spill, uint32_t w)
+    {
+        overflow = overflow | (spill & (cb + 8 >= capb));
+        *slot(min((cb - cb0) >> 2, kEncRing - 1)) = w;
+        cb += spill ? 4u : 0u;
     }
-    x = (x << kBypassBits) | b;
+};
+
+// The puts of one symbol off the common path (an escaped value, or a lane
+// near the end of its segment), applied last to first; the row index is in
+// range.  Returns a status code.
+template <int TPB>
+__device__ __forceinline__ int encode_slow(int32_t s, const RowMeta m, const EncTables &t,
+                                           uint64_t &x, Spill<TPB> &sp)
+{
+    int err = 0;
+    const uint32_t mv = m.mvf & 0xFFFFu;
+    const int64_t v = (int64_t)s - (int64_t)m.offset;
+    const bool esc = (uint64_t)v >= (uint64_t)mv;
+    uint64_t raw = v < 0 ? (uint64_t)(-2 * v - 1) : (uint64_t)(2 * (v - (int64_t)mv));
+    if (esc && raw >= (1ull << 31)) {
+        err = RANS_E_SYMBOL_RANGE;
+        raw = 0;
+    }
+    // BITS puts: groups nb-1 .. 0, then the count nb (none for ordinary values)
+    const uint32_t bits = raw ? 64u - (uint32_t)__clzll(raw) : 0u;
+    const uint32_t nb = esc ? (bits + kBypassBits - 1) / kBypassBits : 0u;
+    auto put_bits = [&](uint32_t b) {
+        const bool spill = x >= (1ull << (63 - kBypassBits));
+        sp.put_if(spill, (uint32_t)x);
+        x = spill ? (x >> 32) : x;
+        x = (x << kBypassBits) | b;
+    };
+    for (uint32_t g = nb; g-- > 0;)
+        put_bits((uint32_t)(raw >> (kBypassBits * g)) & 15u);
+    if (esc)
+        put_bits(nb);
+    // the REG put of the slot
+    const uint32_t pr = pair_of(t, m, esc ? mv : (uint32_t)v);
+    const uint32_t f = pr >> 16;
+    const bool spill = x >= ((uint64_t)f << (63 - kPrecision));
+    sp.put_if(spill, (uint32_t)x);
+    x = spill ? (x >> 32) : x;
+    x = reg_step(x, pr & 0xFFFFu, f, reciprocal(f));
+    return err;
 }
 
 __device__ inline uint32_t wave_inclusive_scan(uint32_t v, uint32_t lane)
@@ -140,39 +175,6 @@ __device__ inline uint32_t wave_inclusive_scan(uint32_t v, uint32_t lane)
     return v;
 }
 
-// The puts of one symbol, applied last to first; returns a status code.
-__device__ __forceinline__ int encode_symbol(int32_t s, int32_t r, uint64_t &x, Spill &sp,
-                                             const RowMeta *meta, const uint16_t *cdf16,
-                                             uint32_t K)
-{
-    int err = 0;
-    if ((uint32_t)r >= K) {
-        err = RANS_E_INDEX;
-        r = 0;
-    }
-    const RowMeta m = meta[r];
-    const uint32_t mv = m.mv;
-    const int64_t v = (int64_t)s - (int64_t)m.offset;
-    const bool esc = (uint64_t)v >= (uint64_t)mv;
-    const uint32_t slot = esc ? mv : (uint32_t)v;
-    const uint32_t start = cdf16[m.cdf_base + slot];
-    const uint32_t f = ((uint32_t)cdf16[m.cdf_base + slot + 1] - start) & 0xFFFFu;
-    if (esc) {
-        uint64_t raw = v < 0 ? (uint64_t)(-2 * v - 1) : (uint64_t)(2 * (v - (int64_t)mv));
-        if (raw >= (1ull << 31)) {
-            err = err ? err : RANS_E_SYMBOL_RANGE;
-            raw = 0;
-        }
-        const uint32_t bits = raw ? 64u - (uint32_t)__clzll(raw) : 0u;
-        const uint32_t nb = (bits + kBypassBits - 1) / kBypassBits;
-        for (uint32_t g = nb; g-- > 0;)
-            put_bits(x, (uint32_t)(raw >> (kBypassBits * g)) & 15u, sp);
-        put_bits(x, nb, sp);
-    }
-    put_reg(x, start, f, reciprocal(f), sp);
-    return err;
-}
-
 template <int TPB>
 __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
 {
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     __shared__ int s_last;
 
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
-    const uint8_t *tab = a.ws + ws_tables_offset();
+    const uint8_t *tab = a.ws + ws_enc_tables_offset();
     uint64_t *flags = reinterpret_cast<uint64_t *>(a.ws + ws_flags_offset());
     uint32_t *scratch = reinterpret_cast<uint32_t *>(a.ws + ws_scratch_offset(a.lanes));
     const uint32_t tid = threadIdx.x;
@@ -198,13 +200,14 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     const uint32_t nbytes = herr ? 0u : hdr->enc_bytes;
     stage_tables<TPB>(lds, tab, nbytes);
     __syncthreads();
-    const RowMeta *meta = reinterpret_cast<const RowMeta *>(lds);
-    const uint16_t *cdf16 = reinterpret_cast<const uint16_t *>(lds + align_up(16ull * K, 16));
-    uint32_t *ring = reinterpret_cast<uint32_t *>(lds + kTableBudget) + tid;
+    EncTables et;
+    et.lds = lds;
+    et.meta = reinterpret_cast<const RowMeta *>(lds);
+    et.K = K;
     int bad = 0;
     if (!herr)
         for (uint32_t r = tid; r < K; r += TPB)
-            bad |= (meta[r].mv & kRowInvalid) ? 1 : 0;
+            bad |= (et.meta[r].lut & kRowInvalid) ? 1 : 0;
     bad = __syncthreads_or(bad);
     if (!herr && bad)
         herr = RANS_E_TABLE;
@@ -216,86 +219,172 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
         uint32_t t = 0;
         if (lane == 0)
             t = atomicAdd(&hdr->ticket, 1u);
-        t = __shfl(t, 0, kWave);
+        t = __builtin_amdgcn_readfirstlane(__shfl(t, 0, kWave));
         if (t < nwork) {
             const uint32_t j = t * kWave + lane;
+            // the wave's symbols and scratch segments, as buffers
+            const uint32_t j0 = t * kWave, j1 = min(j0 + kWave, L);
+            const uint64_t bw = lane_begin(a.n, L, j0), ew = lane_begin(a.n, L, j1);
+            const Rsrc rsym = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
+            const Rsrc ridx = make_rsrc(a.indexes + bw, (uint32_t)(4 * (ew - bw)));
+            const uint64_t sw0 = 2 * bw + 4ull * j0, sw1 = 2 * ew + 4ull * j1;
+            Spill<TPB> sp;
+            sp.scr = make_rsrc(scratch + sw0, (uint32_t)(4 * (sw1 - sw0)));
+            sp.ring = reinterpret_cast<uint32_t *>(lds + kEncTableBudget) + tid;
+            sp.top = 0;
             uint32_t words = 0;
-            uint32_t *seg_top = nullptr;
             int lerr = 0;
             if (j < L) {
                 const uint64_t b = lane_begin(a.n, L, j);
                 const uint64_t e = lane_begin(a.n, L, j + 1);
-                Spill sp;
-                sp.top = scratch + 2 * e + 4ull * (j + 1);
-                sp.ring = ring;
-                sp.stride = TPB;
-                sp.count = 0;
-                sp.flushed = 0;
-                sp.cap = (uint32_t)(2 * (e - b) + 4);
+                const uint32_t nj = (uint32_t)(e - b);
+                sp.top = (uint32_t)(4 * (2 * e + 4ull * (j + 1) - sw0));
+                sp.cb = 0;
+                sp.cb0 = 0;
+                sp.capb = 4 * (2 * nj + 4);
                 sp.overflow = false;
                 uint64_t x = kStateLow;
-                const uint64_t nj = e - b;
-                const uint64_t kl = nj ? nj - 1 : 0;     // last position offset
-                // Positions are coded last to first.  Symbols and indexes of
-                // round r+1 are requested in the memory phase before round r,
-                // so they are one round old when the state chain reads them.
-                // Two symbol/index buffers used in turn (no register copies
-                // between rounds): a buffer is refilled in the memory phase right
-                // after its round and read again two rounds later.  Every memory
-                // phase issues the same global accesses in the same order (8
-                // spill stores, 16 loads) and the prologue runs two such phases
-                // too, so the compiler's wait counts only ever cover requests
-                // that are at least a round old.  Empty lanes (n may be 0 with
-                // null arrays) read a dummy word of the workspace header.
-                const int32_t *syp = nj ? a.symbols : reinterpret_cast<const int32_t *>(hdr->pad0);
-                const int32_t *ixp = nj ? a.indexes : reinterpret_cast<const int32_t *>(hdr->pad0);
-                const uint64_t p_hi = nj ? e - 1 : 0;
+                // byte offsets of the lane's positions in the wave's buffers;
+                // positions are coded last to first, clamped at the lane start
+                const int32_t plast = (int32_t)(4 * (int64_t)(e - bw) - 4);
+                const int32_t pfirst = (int32_t)(4 * (b - bw));
                 int32_t sa[kRound], ia[kRound], sb[kRound], ib[kRound];
-                auto load_next = [&](int32_t (&sym)[kRound], int32_t (&idx)[kRound], uint64_t k) {
+                // Symbols and indexes of positions k .. k+7: one 16-byte load per
+                // four positions, or, when a window would start before the wave's
+                // first symbol, one clamped load per position.
+                auto load_next = [&](int32_t (&sym)[kRound], int32_t (&idx)[kRound], uint32_t k) {
+                    const int32_t pk = plast - (int32_t)(4 * k);
+                    if (__all(pk - 4 * (kRound - 1) >= 0)) {
+                        const uint32_t lo = (uint32_t)(pk - 4 * (kRound - 1));
+                        const u32x4 s0 = buf_load4(rsym, lo), s1 = buf_load4(rsym, lo + 16);
+                        const u32x4 i0 = buf_load4(ridx, lo), i1 = buf_load4(ridx, lo + 16);
 #pragma unroll
-                    for (int u = 0; u < kRound; ++u) {
-                        const uint64_t p = p_hi - min(k + u, kl);
-                        sym[u] = syp[p];
-                        idx[u] = ixp[p];
+                        for (int u = 0; u < 4; ++u) {
+                            sym[7 - u] = (int32_t)s0[u];
+                            sym[3 - u] = (int32_t)s1[u];
+                            idx[7 - u] = (int32_t)i0[u];
+                            idx[3 - u] = (int32_t)i1[u];
+                        }
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < kRound; ++u) {
+                            const uint32_t off = (uint32_t)max(pk - 4 * u, pfirst);
+                            sym[u] = buf_load(rsym, off, 0);
+                            idx[u] = buf_load(ridx, off, 0);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 };
-                auto round = [&](int32_t (&sym)[kRound], int32_t (&idx)[kRound], uint64_t k0) {
+                // The round's words (ring slots 0 .. n-1) go to positions
+                // cb0/4 .. cb0/4 + n - 1, i.e. descending byte offsets from
+                // top - 4 - cb0.  Slots 0..7 are always stored, as two 16-byte
+                // stores (slots past n hold stale words for positions that later
+                // words or the final state overwrite); a round of more than 8
+                // words, or a lane near the end of its segment, stores word by
+                // word.
+                auto store_words = [&]() {
+                    const uint32_t n = (sp.cb - sp.cb0) >> 2;
+                    uint32_t r[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        r[i] = *sp.slot(i);
+                    const bool whole = sp.cb0 + 32 <= sp.capb;
+                    const uint32_t off = whole ? sp.top - sp.cb0 - 32 : kNoStore;
+                    buf_store4(sp.scr, off, u32x4{r[7], r[6], r[5], r[4]});
+                    buf_store4(sp.scr, off + 16, u32x4{r[3], r[2], r[1], r[0]});
+                    if (__builtin_expect(__ballot(!whole | (n > 8)) != 0, 0)) {
+                        for (uint32_t i = whole ? 8u : 0u; i < n; ++i)
+                            if (sp.cb0 + 4 * i + 8 < sp.capb)
+                                buf_store(sp.scr, sp.top - 4 - sp.cb0 - 4 * i, 0, (int32_t)*sp.slot(i));
+                    }
+                    sp.cb0 = sp.cb;
+                };
+                // One round of positions k0 .. k0+7 (last to first).
+                auto round = [&](int32_t (&sym)[kRound], int32_t (&idx)[kRound], uint32_t k0) {
+                    RowMeta m[kRound];
+                    uint32_t start[kRound], f[kRound];
+                    double rcp[kRound];
+                    bool fast[kRound];
+                    // room for three words per position: the fast steps need no check
+                    const bool room = sp.cb + 4 * (2 + 3 * kRound) < sp.capb;
+                    bool all_fast = room;
+#pragma unroll
+                    for (int u = 0; u < kRound; ++u)
+                        m[u] = et.meta[min((uint32_t)idx[u], K - 1)];
 #pragma unroll
                     for (int u = 0; u < kRound; ++u) {
-                        if (k0 + u < nj) {
-                            const int ec = encode_symbol(sym[u], idx[u], x, sp, meta, cdf16, K);
-                            lerr = lerr ? lerr : ec;
+                        const uint32_t mv = m[u].mvf & 0xFFFFu;
+                        // s - offset wraps mod 2^32 into [0, mv) only on rows whose
+                        // fast bound is 0
+                        const uint32_t w = (uint32_t)sym[u] - (uint32_t)m[u].offset;
+                        fast[u] = room & (w < (m[u].mvf >> 16)) & ((uint32_t)idx[u] < K) &
+                                  (k0 + u < nj);
+                        all_fast = all_fast & fast[u];
+                        const uint32_t pr = pair_of(et, m[u], min(w, mv));
+                        start[u] = pr & 0xFFFFu;
+                        f[u] = pr >> 16;
+                        rcp[u] = reciprocal(f[u]);
+                    }
+                    if (__all(all_fast)) {
+                        // the state chain: no branch, no LDS access
+#pragma unroll
+                        for (int u = 0; u < kRound; ++u) {
+                            const bool need = (uint32_t)(x >> 32) >= (f[u] << (31 - kPrecision));
+                            *sp.slot((sp.cb - sp.cb0) >> 2) = (uint32_t)x;
+                            sp.cb += need ? 4u : 0u;
+                            x = need ? (x >> 32) : x;
+                            x = reg_step(x, start[u], f[u], rcp[u]);
+                        }
+                    } else {
+                        // the fast step is committed where it applies; the other
+                        // lanes take the slow puts
+#pragma unroll
+                        for (int u = 0; u < kRound; ++u) {
+                            const bool need = (uint32_t)(x >> 32) >= (f[u] << (31 - kPrecision));
+                            const uint64_t xn =
+                                reg_step(need ? (x >> 32) : x, start[u], f[u], rcp[u]);
+                            *sp.slot(min((sp.cb - sp.cb0) >> 2, kEncRing - 1)) = (uint32_t)x;
+                            sp.cb += (fast[u] & need) ? 4u : 0u;
+                            x = fast[u] ? xn : x;
+                            const bool slow = !fast[u] & (k0 + u < nj);
+                            if (__builtin_expect(__ballot(slow) != 0, 0)) {
+                                if (slow) {
+                                    int ec = RANS_E_INDEX;
+                                    if ((uint32_t)idx[u] < K)
+                                        ec = encode_slow<TPB>(sym[u], m[u], et, x, sp);
+                                    lerr = lerr ? lerr : ec;
+                                }
+                            }
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     // ---- memory phase ----
-                    sp.flush();
+                    store_words();
                     __builtin_amdgcn_sched_barrier(0);
                     load_next(sym, idx, k0 + 2 * kRound);
                 };
-                // prologue: two phases of the same shape (the empty flushes write
-                // filler to the lane's first spill slot, rewritten later)
-                sp.flush();
+                // prologue: two phases of the same shape (their stores carry
+                // stale ring words to positions that later words overwrite)
+                store_words();
                 __builtin_amdgcn_sched_barrier(0);
                 load_next(sa, ia, 0);
-                sp.flush();
+                store_words();
                 __builtin_amdgcn_sched_barrier(0);
                 load_next(sb, ib, kRound);
                 // both rounds always run (positions past the lane are skipped
                 // inside), so every path back to the loop head passes both phases
-                for (uint64_t k0 = 0; k0 < nj; k0 += 2 * kRound) {
+                for (uint32_t k0 = 0; k0 < nj; k0 += 2 * kRound) {
                     round(sa, ia, k0);
                     round(sb, ib, k0 + kRound);
                 }
                 if (sp.overflow) {
                     lerr = lerr ? lerr : RANS_E_CAPACITY;
-                    sp.count = sp.cap - 2;
+                    sp.cb = sp.capb - 8;
                 }
-                sp.top[-2 - (int64_t)sp.count] = (uint32_t)x;
-                sp.top[-1 - (int64_t)sp.count] = (uint32_t)(x >> 32);
-                words = sp.count + 2;
-                seg_top = sp.top;
+                buf_store(sp.scr, sp.top - 8 - sp.cb, 0, (int32_t)(uint32_t)x);
+                buf_store(sp.scr, sp.top - 4 - sp.cb, 0, (int32_t)(uint32_t)(x >> 32));
+                // (the final state is stored after every memory phase)
+                words = sp.cb / 4 + 2;
             }
             if (lerr)
                 record_error(hdr, lerr);
@@ -341,14 +430,22 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             prefix = __shfl(prefix, 0, kWave);
 
             // ---- header entry and compaction --------------------------------------
+            // (each lane reads back only the scratch words it stored itself)
             if (j < L) {
                 const uint64_t end = prefix + incl;
                 a.stream[1 + j] = (uint32_t)end;
                 const uint64_t dst = 1ull + L + end - words;
-                const uint32_t *src = seg_top - words;
-                for (uint32_t k = 0; k < words; ++k)
-                    if (dst + k < a.capacity)
-                        a.stream[dst + k] = src[k];
+                const uint32_t src = sp.top - 4 * words;
+                for (uint32_t k0 = 0; k0 < words; k0 += 8) {
+                    uint32_t v[8];
+#pragma unroll
+                    for (uint32_t u = 0; u < 8; ++u)
+                        v[u] = (uint32_t)buf_load(sp.scr, src + 4 * min(k0 + u, words - 1), 0);
+#pragma unroll
+                    for (uint32_t u = 0; u < 8; ++u)
+                        if (k0 + u < words && dst + k0 + u < a.capacity)
+                            a.stream[dst + k0 + u] = v[u];
+                }
             }
         }
     }
@@ -385,7 +482,7 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
 template <int TPB>
 hipError_t launch_encode_t(const EncodeArgs &a, hipStream_t s)
 {
-    const uint32_t lds_bytes = coding_lds_bytes(TPB);
+    const uint32_t lds_bytes = encode_lds_bytes(TPB);
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&encode_kernel<TPB>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);

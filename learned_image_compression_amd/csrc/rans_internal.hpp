@@ -20,13 +20,17 @@ constexpr uint64_t kStateLow = 1ull << 31;
 constexpr uint32_t kBypassBits = 4;
 constexpr int kWave = 64;
 
-// LDS: 160 KiB per workgroup on gfx950.  Tables get kTableBudget bytes; the
-// coding kernels put a per-lane word ring of kRingWords words after them.
+// LDS: 160 KiB per workgroup on gfx950.  Each coding kernel stages its table
+// set and keeps a per-lane word ring after it: the decoder a ring of
+// kDecRing renormalisation words (read ahead of use), the encoder a ring of
+// kEncRing words spilled during the current round (a round of 8 positions
+// spills at most 3 words per position).
 constexpr uint32_t kLdsBytes = 160u * 1024u;
-constexpr uint32_t kTableBudget = 140u * 1024u;
-constexpr uint32_t kRingWords = 8;
 constexpr uint32_t kMaxBlockThreads = 512;
-static_assert(kTableBudget + kRingWords * 4 * kMaxBlockThreads <= kLdsBytes, "LDS budget");
+constexpr uint32_t kDecRing = 8;
+constexpr uint32_t kEncRing = 24;
+constexpr uint32_t kDecTableBudget = kLdsBytes - kDecRing * 4 * kMaxBlockThreads - 1024;
+constexpr uint32_t kEncTableBudget = kLdsBytes - kEncRing * 4 * kMaxBlockThreads - 1024;
 constexpr uint32_t kMaxLutQ = 10;        // at most 1024 buckets per row
 
 constexpr uint32_t kHeaderBytes = 256;
@@ -40,12 +44,12 @@ struct WsHeader {
     uint32_t cdf_stride;
     uint32_t total_len;     // sum of row lengths
     uint32_t lut_q;         // decode lookup: 2^lut_q buckets per row
-    uint32_t enc_bytes;     // bytes of [meta | cdf16] staged by the encoder
-    uint32_t dec_bytes;     // bytes of [meta | cdf16 | lut] staged by the decoder
-    uint32_t enc_ok;        // 1 when the encoder tables fit the LDS budget
-    uint32_t dec_ok;        // 1 when the decoder tables fit the LDS budget
+    uint32_t enc_bytes;     // bytes of the encoder's table set [meta | pairs]
+    uint32_t dec_bytes;     // bytes of the decoder's table set [meta | cdf16 | lut]
+    uint32_t enc_ok;        // 1 when the encoder set fits its LDS budget
+    uint32_t dec_ok;        // 1 when the decoder set fits its LDS budget
     uint32_t magic;
-    uint32_t pad0[7];
+    uint32_t pad0[7];       // pad0 also serves as a harmless dummy store target
     // bookkeeping (self-cleaning)
     int32_t err;            // first error code of the running call, 0 if none
     uint32_t done;          // finished blocks of the running call
@@ -55,28 +59,43 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) <= kHeaderBytes, "header too large");
 
-// Per-row metadata, 16 bytes, staged into LDS by every kernel.
+// Per-row metadata, 16 bytes, at the head of both table sets.
+//   base    decoder: first entry of the row in cdf16;
+//           encoder: byte offset of the row's pair entries in the set
+//   offset  symbol value of slot 0
+//   mvf     bits 0..15: escape slot mv = len - 2; bits 16..31: the fast-path
+//           bound -- slots below it are ordinary symbols whose value
+//           offset + slot fits int32 (mv, or 0 when it might not)
+//   lut     decoder: byte offset of the row's lookup entries in the set;
+//           both: bit 31 set when the row is invalid
 struct RowMeta {
-    uint32_t cdf_base;      // first entry of the row in the packed cdf16 array
-    int32_t offset;         // symbol value of slot 0
-    uint32_t mv;            // escape slot = len - 2; bit 31 set when the row is invalid
-    uint32_t lut_base;      // first lookup entry of the row
+    uint32_t base;
+    int32_t offset;
+    uint32_t mvf;
+    uint32_t lut;
 };
 constexpr uint32_t kRowInvalid = 0x80000000u;
 
-// Decode lookup entry (8 bytes) for one bucket of 2^(16-q) cumulative values:
+// Encoder pair entry (4 bytes) per slot k: start(k) | f(k) << 16 (f <= 65535).
+//
+// Decoder lookup entry (8 bytes) for one bucket of 2^(16-q) cumulative values:
 // the adjacent slot pair (a, a+1) covering most of the bucket.
-//   bits  0..15  start(a)
-//   bits 16..31  start(a+1)
-//   bits 32..47  start(a+2) - 1
+//   bits  0..15  s0   = start(a)
+//   bits 16..31  d1   = start(a+1) - start(a)        (= f(a))
+//   bits 32..47  span = start(a+2) - 1 - start(a)
 //   bits 48..63  a
-// A cumulative value outside [start(a), start(a+2)) falls back to a search.
+// With t = cum - s0 (unsigned): t <= span means the symbol is a (t < d1) or
+// a+1; otherwise the decoder searches the row.
 
 inline __host__ __device__ uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
-// Workspace regions: [header | tables (kTableBudget) | look-back flags | scratch].
+// Workspace regions: [header | decoder set | encoder set | look-back flags | scratch].
 inline __host__ __device__ uint64_t ws_tables_offset() { return kHeaderBytes; }
-inline __host__ __device__ uint64_t ws_flags_offset() { return kHeaderBytes + kTableBudget; }
+inline __host__ __device__ uint64_t ws_enc_tables_offset() { return kHeaderBytes + kDecTableBudget; }
+inline __host__ __device__ uint64_t ws_flags_offset()
+{
+    return align_up(kHeaderBytes + kDecTableBudget + kEncTableBudget, 256);
+}
 inline __host__ __device__ uint64_t ws_flag_count(uint32_t lanes) { return (lanes + kWave - 1) / kWave; }
 inline __host__ __device__ uint64_t ws_scratch_offset(uint32_t lanes)
 {
@@ -96,35 +115,67 @@ inline __host__ __device__ uint64_t lane_begin(uint64_t n, uint32_t lanes, uint3
     return (uint64_t)j * a + ((uint64_t)j * b) / lanes;
 }
 
-// Threads per block for the coding kernels: every block stages the tables
-// into LDS once, so blocks are made large; beyond 256 blocks (one per CU)
-// more lanes go into each block.
+// Threads per block for the coding kernels: each block stages its table set
+// into LDS once (one block fills a CU's LDS), so blocks are large -- 256
+// threads, 512 beyond 256 blocks of 256.
 inline uint32_t coding_block_threads(uint32_t lanes)
 {
     return lanes > 256u * 256u ? 512u : 256u;
 }
-inline uint32_t coding_lds_bytes(uint32_t tpb) { return kTableBudget + kRingWords * 4 * tpb; }
+inline uint32_t decode_lds_bytes(uint32_t tpb) { return kDecTableBudget + kDecRing * 4 * tpb; }
+inline uint32_t encode_lds_bytes(uint32_t tpb) { return kEncTableBudget + kEncRing * 4 * tpb; }
 
 // Copy `nbytes` (a multiple of 16) of prepared tables from global memory into
-// LDS with every thread keeping eight 16-byte loads in flight.
+// LDS with every thread keeping sixteen 16-byte loads in flight.
 template <int TPB>
 __device__ inline void stage_tables(uint8_t *lds, const uint8_t *src, uint32_t nbytes)
 {
+    constexpr int kBatch = 16;
     const uint4 *s = reinterpret_cast<const uint4 *>(src);
     uint4 *d = reinterpret_cast<uint4 *>(lds);
     const uint32_t n16 = nbytes / 16;
     if (n16 == 0)
         return;
-    for (uint32_t i0 = threadIdx.x; i0 < n16; i0 += 8 * TPB) {
-        uint4 v[8];
+    for (uint32_t i0 = threadIdx.x; i0 < n16; i0 += kBatch * TPB) {
+        uint4 v[kBatch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < kBatch; ++u)
             v[u] = s[min(i0 + u * TPB, n16 - 1)];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < kBatch; ++u)
             if (i0 + u * TPB < n16)
                 d[i0 + u * TPB] = v[u];
     }
+}
+
+// Raw buffer access (gfx9 buffer descriptor, 32-bit data format): the
+// hardware drops stores and returns 0 for loads at byte offsets at or past
+// `bytes`, and the constant part of an offset rides in the instruction.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ inline Rsrc make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ inline int32_t buf_load(Rsrc r, uint32_t voff, int cofs)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, cofs, 0);
+}
+__device__ inline void buf_store(Rsrc r, uint32_t voff, int cofs, int32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voff, cofs, 0);
+}
+// 16-byte forms; offsets need only 4-byte alignment, and the bounds check is
+// made per 4-byte word (a straddling load reads 0 past the end, a straddling
+// store writes only the words before it).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+__device__ inline u32x4 buf_load4(Rsrc r, uint32_t voff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+__device__ inline void buf_store4(Rsrc r, uint32_t voff, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, 0, 0);
 }
 
 struct PrepArgs {

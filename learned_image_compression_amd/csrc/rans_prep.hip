@@ -7,11 +7,13 @@
 // lookup table, about 0.2 ms).  Here one launch does it: every block scans
 // the row lengths redundantly (K <= 4096), so no block waits for another.
 //
-// Packed layout in the workspace table region (copied verbatim into LDS by
-// the coding kernels):
-//   [RowMeta x K][u16 cdf16 x sum(len), padded to 16 B][u64 lut x K * 2^q]
-// A row's terminal 65536 is stored as 0: f = (next - start) mod 2^16 is still
-// right because every frequency is in [1, 65535].
+// Two packed table sets in the workspace, each copied verbatim into LDS by
+// one coding kernel:
+//   decoder  [RowMeta x K][u16 cdf16 x sum(len), padded to 16 B][u64 lut x K * 2^q]
+//            [u16 first x K * 2^q]
+//   encoder  [RowMeta x K][u32 (start | f << 16) x sum(len)]
+// A row's terminal 65536 is stored as 0 in cdf16: f = (next - start) mod 2^16
+// is still right because every frequency is in [1, 65535].
 //
 // Decoder lookup (inverse-CDF table in the sense of torch_ans "Usage",
 // "Inverse CDF decoding": a table keyed by the low state bits).  Each row gets
@@ -72,13 +74,14 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
     const uint32_t total = s_part[kPrepThreads - 1];
     __syncthreads();
 
+    // decoder set [meta | cdf16 | lut], encoder set [meta | pairs]
     const uint32_t meta_bytes = (uint32_t)align_up(16ull * K, 16);
     const uint64_t cdf_bytes = align_up(2ull * total, 16);
-    const uint64_t enc_bytes = meta_bytes + cdf_bytes;
-    const bool enc_ok = enc_bytes <= kTableBudget;
+    const uint64_t enc_bytes = meta_bytes + align_up(4ull * total, 16);
+    const bool enc_ok = enc_bytes <= kEncTableBudget;
     int q = -1;
-    for (int t = (int)kMaxLutQ; t >= 0 && enc_ok; --t) {
-        if (enc_bytes + (8ull * K << t) <= kTableBudget) {
+    for (int t = (int)kMaxLutQ; t >= 0; --t) {
+        if (meta_bytes + cdf_bytes + (10ull * K << t) <= kDecTableBudget) {
             q = t;
             break;
         }
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
     const bool dec_ok = q >= 0;
     if (q < 0)
         q = 0;
-    const uint64_t dec_bytes = enc_bytes + (8ull * K << q);
+    const uint64_t dec_bytes = align_up(meta_bytes + cdf_bytes + (10ull * K << q), 16);
 
     if (blockIdx.x == 0 && tid == 0) {
         hdr->num_tables = (uint32_t)K;
@@ -104,12 +107,14 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
         __threadfence();
         hdr->magic = kMagic;
     }
-    if (!enc_ok)
-        return;   // nothing fits: the coding kernels report RANS_E_TABLE_SIZE
 
-    RowMeta *meta = reinterpret_cast<RowMeta *>(tab);
+    RowMeta *dmeta = reinterpret_cast<RowMeta *>(tab);
     uint16_t *cdf16 = reinterpret_cast<uint16_t *>(tab + meta_bytes);
-    uint64_t *lut = reinterpret_cast<uint64_t *>(tab + enc_bytes);
+    uint64_t *lut = reinterpret_cast<uint64_t *>(tab + meta_bytes + cdf_bytes);
+    uint16_t *first = reinterpret_cast<uint16_t *>(tab + meta_bytes + cdf_bytes + (8ull * K << q));
+    uint8_t *etab = a.ws + ws_enc_tables_offset();
+    RowMeta *emeta = reinterpret_cast<RowMeta *>(etab);
+    uint32_t *pairs = reinterpret_cast<uint32_t *>(etab + meta_bytes);
     const uint32_t width = kTotal >> q;
 
     // --- 2. rows of this block ------------------------------------------------
@@ -146,17 +151,35 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
             if (k > 0 && v <= s_val[k - 1])
                 bad = 1;
             const uint16_t p = (uint16_t)(uint32_t)v;
-            cdf16[base + k] = p;
             s_row[k] = p;
+            if (dec_ok)
+                cdf16[base + k] = p;
+            if (enc_ok) {
+                // slot k: start | f << 16 (the terminal entry gets 0)
+                const uint32_t f = k + 1 < len ? (uint32_t)(s_val[k + 1] - v) & 0xFFFFu : 0u;
+                pairs[base + k] = (k + 1 < len) ? ((uint32_t)v & 0xFFFFu) | (f << 16) : 0u;
+            }
         }
         bad = __syncthreads_or(bad);
         if (tid == 0) {
+            const int32_t off = a.offsets[r];
+            const uint32_t mv = len - 2;
+            // slots below mv decode on the fast path if offset + slot fits int32
+            const bool fits = (int64_t)off + (int64_t)mv - 1 <= (int64_t)INT32_MAX;
             RowMeta m;
-            m.cdf_base = base;
-            m.offset = a.offsets[r];
-            m.mv = (len - 2) | (bad ? kRowInvalid : 0u);
-            m.lut_base = (uint32_t)r << q;
-            meta[r] = m;
+            m.offset = off;
+            m.mvf = mv | ((fits ? mv : 0u) << 16);
+            if (dec_ok) {
+                m.base = base;
+                m.lut = (uint32_t)(meta_bytes + cdf_bytes + ((uint64_t)r << (q + 3))) |
+                        (bad ? kRowInvalid : 0u);
+                dmeta[r] = m;
+            }
+            if (enc_ok) {
+                m.base = meta_bytes + 4 * base;
+                m.lut = bad ? kRowInvalid : 0u;
+                emeta[r] = m;
+            }
         }
         if (dec_ok) {
             // Best adjacent pair per bucket, by scatter: slot k proposes the pair
@@ -190,10 +213,18 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
                     const uint32_t s0 = row_value(s_row, a, len);
                     const uint32_t s1 = row_value(s_row, a + 1, len);
                     const uint32_t s2 = row_value(s_row, a + 2, len);
-                    e = (uint64_t)s0 | ((uint64_t)s1 << 16) | ((uint64_t)(s2 - 1) << 32) |
-                        ((uint64_t)a << 48);
+                    e = (uint64_t)s0 | ((uint64_t)(s1 - s0) << 16) |
+                        ((uint64_t)(s2 - 1 - s0) << 32) | ((uint64_t)a << 48);
                 }
                 lut[((uint64_t)r << q) + b] = e;
+            }
+            // first[b]: the slot holding the bucket's lowest cumulative value
+            // (bounds the search when the pair misses)
+            for (uint32_t k = tid; k + 1 < len && !bad; k += kPrepThreads) {
+                const uint32_t s0 = row_value(s_row, k, len);
+                const uint32_t s1 = row_value(s_row, k + 1, len);
+                for (uint32_t b = (s0 + width - 1) >> (kPrecision - q); b < nb && b * width < s1; ++b)
+                    first[((uint64_t)r << q) + b] = (uint16_t)k;
             }
         }
         __syncthreads();   // s_row is reused by the next row

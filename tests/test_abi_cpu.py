@@ -47,8 +47,9 @@ def test_bounds(lib):
     for n, L in ((0, 1), (16384, 64), (1566720, 4096), (50135040, 131072)):
         assert lib.rans_encode_bound_words(n, L) == 1 + L + 2 * n + 4 * L
         ws = lib.rans_workspace_bytes(n, L, 64, 3133)
-        # header + table region + look-back flags + 2n+4L words of lane scratch
-        assert ws >= 256 + 140 * 1024 + 8 * ((L + 63) // 64) + 4 * (2 * n + 4 * L)
+        # header + decoder and encoder table sets (143 KiB and 111 KiB) +
+        # look-back flags + 2n+4L words of lane scratch
+        assert ws >= 256 + 254 * 1024 + 8 * ((L + 63) // 64) + 4 * (2 * n + 4 * L)
         assert ws % 4 == 0
 
 
@@ -94,6 +95,8 @@ def _decode(lib, **kw):
     (dict(ws=128), -7),                 # not 256-byte aligned
     (dict(ws_bytes=1000), -7),
     (dict(n=1 << 41), -1),
+    (dict(n=(1 << 28) + 1), -1),        # above RANS_MAX_SYMBOLS
+    (dict(lanes=(1 << 26) + 1), -1),    # above RANS_MAX_LANES
 ])
 def test_encode_rejects_bad_arguments_on_host(lib, kw, code):
     assert _encode(lib, **kw) == code
@@ -112,6 +115,7 @@ def test_encode_rejects_bad_arguments_on_host(lib, kw, code):
     (dict(ws=0), -7),
     (dict(ws=64), -7),
     (dict(ws_bytes=4096), -7),
+    (dict(n=(1 << 28) + 1), -1),
 ])
 def test_decode_rejects_bad_arguments_on_host(lib, kw, code):
     assert _decode(lib, **kw) == code

@@ -104,6 +104,66 @@ def test_bypass_edges_and_extremes():
         assert st == 0 and np.array_equal(out, syms)
 
 
+def test_extreme_offsets():
+    """Rows whose coded range reaches the int32 limits (values offset + slot
+    that may not fit int32 take the general path on both sides)."""
+    import gpu_util as G
+    imax, imin = 2**31 - 1, -2**31
+    rows = np.full((4, 6), 65536, np.int32)
+    rows[:, :6] = [0, 1000, 30000, 60000, 65000, 65536]
+    lengths = np.array([6, 6, 6, 6], np.int32)
+    offsets = np.array([imax - 1, imin, imax - 3, imax], np.int32)
+    syms, idxs = [], []
+    for r, vals in ((0, [imax - 1, imax, imax - 2, imax - 1000, imax - 2**20]),
+                    (1, [imin, imin + 1, imin + 3, imin + 4, imin + 100]),
+                    (2, [imax - 3, imax - 2, imax - 1, imax, imax - 700]),
+                    (3, [imax, imax - 1, imax - 9])):
+        syms += vals
+        idxs += [r] * len(vals)
+    rng = np.random.default_rng(11)
+    order = rng.permutation(np.repeat(np.arange(len(syms)), 40))
+    syms = np.array(syms, np.int64)[order].astype(np.int32)
+    idxs = np.array(idxs, np.int32)[order]
+    tables = G.B.Tables.from_numpy(rows, lengths, offsets, G.DEV)
+    for lanes in (1, 5, 64):
+        G.say(f"[extreme offsets] lanes={lanes}")
+        rc, ref = oracle.encode(syms, idxs, rows, lengths, offsets, lanes)
+        assert rc == 0
+        st, got, _ = G.gpu_encode(G.to_dev(syms), G.to_dev(idxs), tables, lanes)
+        assert st == 0 and np.array_equal(got, ref)
+        st, out = G.gpu_decode(ref, G.to_dev(idxs), tables, lanes)
+        assert st == 0 and np.array_equal(out, syms)
+    # s - offset wraps to a small value mod 2^32: still out of range
+    bad = syms.copy()
+    k = int(np.flatnonzero(idxs == 3)[0])
+    bad[k] = imin
+    rc, _ = oracle.encode(bad, idxs, rows, lengths, offsets, 8)
+    st, _, _ = G.gpu_encode(G.to_dev(bad), G.to_dev(idxs), tables, 8)
+    assert rc == oracle.E_SYMBOL_RANGE and st == rc
+
+
+def test_wide_rows_uniform_symbols():
+    """Uniform symbols over the widest rows: most steps miss the lookup pair
+    (on both sides of it) or escape."""
+    import gpu_util as G
+    cdf, lengths, offsets, _ = W.gaussian_table_set(64)
+    rng = np.random.default_rng(5)
+    n = 40000
+    idxs = rng.integers(56, 64, n).astype(np.int32)
+    mv = lengths[idxs] - 2
+    v = (rng.random(n) * (mv + 40)).astype(np.int64) - 20
+    syms = (v + offsets[idxs]).astype(np.int32)
+    tables = G.B.Tables.from_numpy(cdf, lengths, offsets, G.DEV)
+    for lanes in (64, 1000):
+        G.say(f"[wide rows] lanes={lanes}")
+        rc, ref = oracle.encode(syms, idxs, cdf, lengths, offsets, lanes)
+        assert rc == 0
+        st, got, _ = G.gpu_encode(G.to_dev(syms), G.to_dev(idxs), tables, lanes)
+        assert st == 0 and np.array_equal(got, ref)
+        st, out = G.gpu_decode(ref, G.to_dev(idxs), tables, lanes)
+        assert st == 0 and np.array_equal(out, syms)
+
+
 def test_repeat_calls_are_identical_and_workspace_is_reusable():
     import gpu_util as G
     w, tables, sym, idx = _workload("tiny")
