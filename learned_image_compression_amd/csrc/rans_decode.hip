@@ -1,7 +1,7 @@
 // rans_decode.hip -- lane decoder: one rANS64 state per wavefront lane,
 // symbols read first to last, the symbol of each step found through the
-// LDS bucket lookup (one 8-byte read in the common case) with a short
-// search of the bucket's slots as fallback.
+// LDS bucket lookup (the bucket's first slot, then one 8-byte read of the
+// next slot starts) with a short search of the bucket's slots as fallback.
 //
 // Decoding rules (the inverse of the puts in rans_encode.hip; decode reads
 // the lane's words in order):
@@ -15,12 +15,12 @@
 // A lane must end at x = 2^31 with all of its words consumed, otherwise the
 // call reports RANS_E_CORRUPT; reads never leave the lane's header extent.
 //
-// Per-symbol work.  The common step -- the bucket's pair holds cum, an
-// ordinary slot, the renormalisation word already in the LDS ring -- is
-// straight-line code whose result is committed at once.  Lanes outside it
-// (lookup miss, escape, drained ring, bad index) redo the step from the
-// saved state in one out-of-line branch, entered only when some lane of the
-// wave needs it.
+// Per-symbol work.  The common step -- cum within three slots of the
+// bucket's first slot, an ordinary slot, the renormalisation word already in
+// the LDS ring -- is straight-line code whose result is committed at once.
+// Lanes outside it (cum further out, escape, drained ring, bad index) redo
+// the step from the saved state in one out-of-line branch, entered only when
+// some lane of the wave needs it.
 //
 // Memory schedule.  A lane works in rounds of kRound symbols.  Global memory
 // is touched only between rounds, in straight-line code with a fixed number
@@ -79,71 +79,67 @@ struct Words {
     }
 };
 
-// Decoder tables in LDS.
+// Decoder tables in LDS: [meta | cdfm1 | first].  cdfm1[k] = start(k) - 1
+// mod 2^16 (the terminal 65536 becomes 65535), so cum >= start(k) is
+// cum > cdfm1[k] and f(k) = cdfm1[k+1] - cdfm1[k] mod 2^16.
 struct DecTables {
-    const uint8_t *lds;      // the decoder set [meta | cdf16 | lut | first]
+    const uint8_t *lds;
     const RowMeta *meta;
-    const uint16_t *cdf16;
-    const uint16_t *first;   // per bucket: the slot holding its lowest cumulative value
     uint32_t q;              // 2^q buckets per row
     uint32_t shift;          // 16 - q: cumulative value -> bucket
     uint32_t K;
 };
 
-// Slow step of one lane, from the state before the step; `ent` is the row's
-// lookup entry for cum.  The lanes in here are few, so the code keeps to
-// straight-line work with a handful of wave-uniform branches:
-//  * a lookup miss searches the bucket's slots [first[b], first[b+1]] (the
-//    escape slot mv for the last bucket), eight slot starts per LDS round
-//    trip;
+__device__ inline uint32_t cdfm1_at(const DecTables &t, const RowMeta &m, uint32_t k)
+{
+    return *reinterpret_cast<const uint16_t *>(t.lds + m.base + 2 * k);
+}
+
+// Slow step of one lane, from the state before the step.  `slot`, `f` and
+// `rr` come from the lookup window; `beyond` says cum lies past it.  The
+// lanes in here are few, so the code keeps to straight-line work with a
+// handful of wave-uniform branches:
+//  * past the window, the search walks the bucket's slots up to first[b+1]
+//    (the escape slot mv for the last bucket), eight slot starts per LDS
+//    round trip;
 //  * the renormalisation word and an escape's groups need at most three
 //    words (after the step x >= 2^31, and nb <= 8 groups of 4 bits follow),
 //    read from the ring when it holds them, else on the checked path;
 //  * out-of-range values and bad indexes are reported.
 // Writes the symbol to `out`; returns a status.
 template <int TPB>
-__device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint64_t ent,
-                                           uint32_t bucket, uint64_t &x, Words<TPB> &wd,
-                                           const DecTables &t, int32_t &out)
+__device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint32_t bucket,
+                                           bool beyond, uint32_t slot, uint32_t f, uint32_t rr,
+                                           uint64_t &x, Words<TPB> &wd, const DecTables &t,
+                                           int32_t &out)
 {
     if ((uint32_t)r >= t.K)
         return RANS_E_INDEX;
     const uint32_t mv = m.mvf & 0xFFFFu;
     const uint32_t cum = (uint32_t)x & (kTotal - 1);
-    const uint32_t s0 = (uint32_t)ent & 0xFFFFu;
-    const uint32_t d1 = (uint32_t)(ent >> 16) & 0xFFFFu;
-    const uint32_t span = (uint32_t)(ent >> 32) & 0xFFFFu;
-    const uint32_t dt = cum - s0;
-    const bool hit = dt <= span;
-    const bool second = dt >= d1;
-    uint32_t slot = (uint32_t)(ent >> 48) + (second ? 1u : 0u);
-    uint32_t start = second ? s0 + d1 : s0;
-    uint32_t f = second ? span + 1 - d1 : d1;
-    if (__ballot(!hit) != 0) {
-        const uint16_t *row = t.cdf16 + m.base;
-        const uint16_t *fst = t.first + ((uint64_t)(uint32_t)r << t.q);
-        uint32_t lo = fst[bucket];
+    if (__ballot(beyond) != 0) {
+        const uint16_t *fst = reinterpret_cast<const uint16_t *>(t.lds + (m.lut & ~kRowInvalid));
+        uint32_t lo = slot;   // value(lo) <= cum
         const uint32_t hi = (bucket + 1 < (1u << t.q)) ? (uint32_t)fst[bucket + 1] : mv;
-        // value(lo) <= cum; the slot is the last k in [lo, hi] with value(k) <= cum
+        // the slot is the last k in [lo, hi] with value(k) <= cum
         uint32_t c;
         do {
             c = 0;
 #pragma unroll
             for (uint32_t k = 1; k <= 8; ++k) {
-                const uint32_t v = row[min(lo + k, hi)];
-                c += (lo + k <= hi && v <= cum) ? 1u : 0u;
+                const uint32_t v = cdfm1_at(t, m, min(lo + k, hi));
+                c += (lo + k <= hi && cum > v) ? 1u : 0u;
             }
             lo += c;
         } while (c == 8 && lo < hi);
-        const uint32_t st = row[lo];
-        const uint32_t nx = (lo == mv) ? kTotal : (uint32_t)row[lo + 1];
-        if (!hit) {
+        const uint32_t sm1 = cdfm1_at(t, m, lo), em1 = cdfm1_at(t, m, lo + 1);
+        if (beyond) {
             slot = lo;
-            start = st;
-            f = nx - st;
+            f = (em1 - sm1) & 0xFFFFu;
+            rr = (cum - sm1 - 1) & 0xFFFFu;
         }
     }
-    x = (uint64_t)f * (x >> kPrecision) + (cum - start);
+    x = (uint64_t)f * (x >> kPrecision) + rr;
     int64_t value = slot;
     int err = 0;
     if (wd.pos + 3 <= wd.filled) {
@@ -205,31 +201,37 @@ __device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint64_t
     return err;
 }
 
-// One decoding step of one lane: the common case is computed and committed
-// for every lane; lanes outside it redo the step on the general path.  A bad
-// row index arrives with a fast bound of 0, so it takes the general path.
+// One decoding step of one lane.  The bucket's first slot fs and the four
+// entries cdfm1[fs .. fs+3] (one 8-byte LDS read) resolve any cum that falls
+// in slots fs .. fs+2; that result is committed for every lane, and lanes
+// outside the common case (past the window, escape or out-of-range value,
+// renormalisation word not in the ring, bad index) redo the step on the slow
+// path.  A bad row index arrives with a fast bound of 0.
 template <int TPB>
 __device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_t &x, Words<TPB> &wd,
                                             const DecTables &t, int32_t &out, int &lerr)
 {
     const uint32_t cum = (uint32_t)x & (kTotal - 1);
     const uint32_t bucket = cum >> t.shift;
-    const uint64_t ent = *reinterpret_cast<const uint64_t *>(t.lds + m.lut + (bucket << 3));
-    const uint32_t elo = (uint32_t)ent, ehi = (uint32_t)(ent >> 32);
-    const uint32_t s0 = elo & 0xFFFFu, d1 = elo >> 16;
-    const uint32_t span = ehi & 0xFFFFu, a = ehi >> 16;
-    const uint32_t dt = cum - s0;
-    const bool second = dt >= d1;
-    const uint32_t slot = a + (second ? 1u : 0u);
-    const uint32_t f = second ? span + 1 - d1 : d1;
-    const uint32_t rr = second ? dt - d1 : dt;
+    const uint32_t fs = *reinterpret_cast<const uint16_t *>(t.lds + m.lut + 2 * bucket);
+    const uint64_t v = *reinterpret_cast<const uint64_t *>(t.lds + m.base + 2 * fs);
+    const uint32_t v0 = (uint32_t)v & 0xFFFFu, v1 = (uint32_t)(v >> 16) & 0xFFFFu;
+    const uint32_t v2 = (uint32_t)(v >> 32) & 0xFFFFu, v3 = (uint32_t)(v >> 48);
+    const bool c1 = cum > v1;
+    const bool c2 = c1 & (cum > v2);
+    const bool beyond = c2 & (cum > v3);
+    const uint32_t slot = fs + (c1 ? 1u : 0u) + (c2 ? 1u : 0u);
+    const uint32_t sm1 = c2 ? v2 : (c1 ? v1 : v0);
+    const uint32_t em1 = c2 ? v3 : (c1 ? v2 : v1);
+    const uint32_t f = (em1 - sm1) & 0xFFFFu;
+    const uint32_t rr = (cum - sm1 - 1) & 0xFFFFu;
     // f * (x >> 16) + rr with x >> 16 < 2^48 split at bit 32
     const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
     const uint32_t mid = __builtin_amdgcn_alignbit(xhi, xlo, 16);
     uint64_t xn = (uint64_t)f * mid + rr;
     xn += (uint64_t)__umul24(f, xhi >> 16) << 32;
     const bool need = xn < kStateLow;
-    const bool slow = (dt > span) | (slot >= (m.mvf >> 16)) | (need & (wd.pos >= wd.filled));
+    const bool slow = beyond | (slot >= (m.mvf >> 16)) | (need & (wd.pos >= wd.filled));
     const uint64_t x0 = x;
     const uint32_t pos0 = wd.pos;
     x = need ? ((xn << 32) | wd.next) : xn;
@@ -239,7 +241,7 @@ __device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_
         if (slow) {
             x = x0;
             wd.pos = pos0;
-            const int ec = decode_slow<TPB>(r, m, ent, bucket, x, wd, t, out);
+            const int ec = decode_slow<TPB>(r, m, bucket, beyond, slot, f, rr, x, wd, t, out);
             lerr = lerr ? lerr : ec;
         }
     }
@@ -270,9 +272,6 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     DecTables t;
     t.lds = lds;
     t.meta = reinterpret_cast<const RowMeta *>(lds);
-    t.cdf16 = reinterpret_cast<const uint16_t *>(lds + align_up(16ull * K, 16));
-    t.first = reinterpret_cast<const uint16_t *>(lds + align_up(16ull * K, 16) +
-                                                 align_up(2ull * hdr->total_len, 16) + (8ull * K << q));
     t.q = q;
     t.shift = kPrecision - q;
     t.K = K;

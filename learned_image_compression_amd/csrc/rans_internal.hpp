@@ -31,7 +31,7 @@ constexpr uint32_t kDecRing = 8;
 constexpr uint32_t kEncRing = 24;
 constexpr uint32_t kDecTableBudget = kLdsBytes - kDecRing * 4 * kMaxBlockThreads - 1024;
 constexpr uint32_t kEncTableBudget = kLdsBytes - kEncRing * 4 * kMaxBlockThreads - 1024;
-constexpr uint32_t kMaxLutQ = 10;        // at most 1024 buckets per row
+constexpr uint32_t kMaxLutQ = 12;        // at most 4096 buckets per row
 
 constexpr uint32_t kHeaderBytes = 256;
 constexpr uint32_t kMagic = 0x52414e53u;   // "RANS": tables prepared
@@ -60,13 +60,13 @@ struct WsHeader {
 static_assert(sizeof(WsHeader) <= kHeaderBytes, "header too large");
 
 // Per-row metadata, 16 bytes, at the head of both table sets.
-//   base    decoder: first entry of the row in cdf16;
-//           encoder: byte offset of the row's pair entries in the set
+//   base    byte offset in the set of the row's cdfm1 entries (decoder) or
+//           (start, f) pairs (encoder)
 //   offset  symbol value of slot 0
 //   mvf     bits 0..15: escape slot mv = len - 2; bits 16..31: the fast-path
 //           bound -- slots below it are ordinary symbols whose value
 //           offset + slot fits int32 (mv, or 0 when it might not)
-//   lut     decoder: byte offset of the row's lookup entries in the set;
+//   lut     decoder: byte offset of the row's first-slot entries in the set;
 //           both: bit 31 set when the row is invalid
 struct RowMeta {
     uint32_t base;
@@ -77,15 +77,6 @@ struct RowMeta {
 constexpr uint32_t kRowInvalid = 0x80000000u;
 
 // Encoder pair entry (4 bytes) per slot k: start(k) | f(k) << 16 (f <= 65535).
-//
-// Decoder lookup entry (8 bytes) for one bucket of 2^(16-q) cumulative values:
-// the adjacent slot pair (a, a+1) covering most of the bucket.
-//   bits  0..15  s0   = start(a)
-//   bits 16..31  d1   = start(a+1) - start(a)        (= f(a))
-//   bits 32..47  span = start(a+2) - 1 - start(a)
-//   bits 48..63  a
-// With t = cum - s0 (unsigned): t <= span means the symbol is a (t < d1) or
-// a+1; otherwise the decoder searches the row.
 
 inline __host__ __device__ uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 

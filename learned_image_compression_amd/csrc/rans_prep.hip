@@ -9,35 +9,29 @@
 //
 // Two packed table sets in the workspace, each copied verbatim into LDS by
 // one coding kernel:
-//   decoder  [RowMeta x K][u16 cdf16 x sum(len), padded to 16 B][u64 lut x K * 2^q]
+//   decoder  [RowMeta x K][u16 cdfm1 x sum(len) + 4, padded to 16 B]
 //            [u16 first x K * 2^q]
 //   encoder  [RowMeta x K][u32 (start | f << 16) x sum(len)]
-// A row's terminal 65536 is stored as 0 in cdf16: f = (next - start) mod 2^16
-// is still right because every frequency is in [1, 65535].
+// cdfm1 holds start(k) - 1 mod 2^16, so that "cum >= start(k)" is
+// "cum > cdfm1[k]" for every entry, the terminal 65536 included (stored as
+// 65535), and f = cdfm1[k+1] - cdfm1[k] mod 2^16 (every f is in [1, 65535]).
 //
 // Decoder lookup (inverse-CDF table in the sense of torch_ans "Usage",
 // "Inverse CDF decoding": a table keyed by the low state bits).  Each row gets
-// 2^q buckets of width 2^(16-q) cumulative values, q the largest value <= 10
-// for which the whole set fits the LDS budget.  A bucket stores the adjacent
-// slot pair that covers most of it, so one 8-byte LDS read resolves the
-// symbol whenever the cumulative value falls in that pair.
+// 2^q buckets of width 2^(16-q) cumulative values, q the largest value <= 12
+// for which the whole set fits the LDS budget; first[b] is the slot holding
+// the bucket's lowest value.  The decoder reads cdfm1[first[b] .. +3] in one
+// 8-byte access and resolves every cum that falls in those three slots.
 #include "rans_internal.hpp"
 
 namespace rans {
 
 constexpr int kPrepThreads = 256;
 
-__device__ inline uint32_t row_value(const uint16_t *row, uint32_t k, uint32_t len)
-{
-    return (k + 1 == len) ? kTotal : (uint32_t)row[k];
-}
-
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
 {
     __shared__ uint32_t s_base[RANS_MAX_TABLES];
     __shared__ uint32_t s_part[kPrepThreads];
-    __shared__ uint16_t s_row[RANS_MAX_STRIDE];
-    __shared__ uint32_t s_best[1u << kMaxLutQ];
     __shared__ int32_t s_val[RANS_MAX_STRIDE];
 
     const int tid = threadIdx.x;
@@ -74,14 +68,15 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
     const uint32_t total = s_part[kPrepThreads - 1];
     __syncthreads();
 
-    // decoder set [meta | cdf16 | lut], encoder set [meta | pairs]
+    // decoder set [meta | cdfm1 | first], encoder set [meta | pairs]
     const uint32_t meta_bytes = (uint32_t)align_up(16ull * K, 16);
-    const uint64_t cdf_bytes = align_up(2ull * total, 16);
+    // (8 spare bytes: the decoder reads four entries from any row position)
+    const uint64_t cdf_bytes = align_up(2ull * total + 8, 16);
     const uint64_t enc_bytes = meta_bytes + align_up(4ull * total, 16);
     const bool enc_ok = enc_bytes <= kEncTableBudget;
     int q = -1;
     for (int t = (int)kMaxLutQ; t >= 0; --t) {
-        if (meta_bytes + cdf_bytes + (10ull * K << t) <= kDecTableBudget) {
+        if (meta_bytes + cdf_bytes + (2ull * K << t) <= kDecTableBudget) {
             q = t;
             break;
         }
@@ -89,7 +84,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
     const bool dec_ok = q >= 0;
     if (q < 0)
         q = 0;
-    const uint64_t dec_bytes = align_up(meta_bytes + cdf_bytes + (10ull * K << q), 16);
+    const uint64_t dec_bytes = align_up(meta_bytes + cdf_bytes + (2ull * K << q), 16);
 
     if (blockIdx.x == 0 && tid == 0) {
         hdr->num_tables = (uint32_t)K;
@@ -109,9 +104,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
     }
 
     RowMeta *dmeta = reinterpret_cast<RowMeta *>(tab);
-    uint16_t *cdf16 = reinterpret_cast<uint16_t *>(tab + meta_bytes);
-    uint64_t *lut = reinterpret_cast<uint64_t *>(tab + meta_bytes + cdf_bytes);
-    uint16_t *first = reinterpret_cast<uint16_t *>(tab + meta_bytes + cdf_bytes + (8ull * K << q));
+    uint16_t *cdfm1 = reinterpret_cast<uint16_t *>(tab + meta_bytes);
+    uint16_t *first = reinterpret_cast<uint16_t *>(tab + meta_bytes + cdf_bytes);
     uint8_t *etab = a.ws + ws_enc_tables_offset();
     RowMeta *emeta = reinterpret_cast<RowMeta *>(etab);
     uint32_t *pairs = reinterpret_cast<uint32_t *>(etab + meta_bytes);
@@ -150,10 +144,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
                 bad = 1;
             if (k > 0 && v <= s_val[k - 1])
                 bad = 1;
-            const uint16_t p = (uint16_t)(uint32_t)v;
-            s_row[k] = p;
             if (dec_ok)
-                cdf16[base + k] = p;
+                cdfm1[base + k] = (uint16_t)((uint32_t)v - 1u);
             if (enc_ok) {
                 // slot k: start | f << 16 (the terminal entry gets 0)
                 const uint32_t f = k + 1 < len ? (uint32_t)(s_val[k + 1] - v) & 0xFFFFu : 0u;
@@ -164,14 +156,14 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
         if (tid == 0) {
             const int32_t off = a.offsets[r];
             const uint32_t mv = len - 2;
-            // slots below mv decode on the fast path if offset + slot fits int32
+            // slots below mv take the fast paths if offset + slot fits int32
             const bool fits = (int64_t)off + (int64_t)mv - 1 <= (int64_t)INT32_MAX;
             RowMeta m;
             m.offset = off;
             m.mvf = mv | ((fits ? mv : 0u) << 16);
             if (dec_ok) {
-                m.base = base;
-                m.lut = (uint32_t)(meta_bytes + cdf_bytes + ((uint64_t)r << (q + 3))) |
+                m.base = (uint32_t)(meta_bytes + 2ull * base);
+                m.lut = (uint32_t)(meta_bytes + cdf_bytes + ((uint64_t)r << (q + 1))) |
                         (bad ? kRowInvalid : 0u);
                 dmeta[r] = m;
             }
@@ -181,53 +173,17 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
                 emeta[r] = m;
             }
         }
-        if (dec_ok) {
-            // Best adjacent pair per bucket, by scatter: slot k proposes the pair
-            // (k, k+1) to every bucket it overlaps, scored by how much of the
-            // bucket the two slots cover; an LDS atomicMax keeps the best score
-            // (ties: lower k).  Buckets lying wholly in the escape slot keep the
-            // default pair (len-3, len-2).
-            const uint32_t nb = 1u << q;
-            const uint32_t amax = len - 3;
-            for (uint32_t b = tid; b < nb; b += kPrepThreads)
-                s_best[b] = 16383u - amax;   // score 0, slot amax
-            __syncthreads();
-            if (!bad) {
-                for (uint32_t k = tid; k <= amax; k += kPrepThreads) {
-                    const uint32_t s0 = row_value(s_row, k, len);
-                    const uint32_t s1 = row_value(s_row, k + 1, len);
-                    const uint32_t s2 = row_value(s_row, k + 2, len);
-                    for (uint32_t b = s0 >> (kPrecision - q); b <= (s1 - 1) >> (kPrecision - q); ++b) {
-                        const uint32_t lo = b * width, hi = lo + width;   // [lo, hi)
-                        const uint32_t c0 = min(s1, hi) - max(s0, lo);
-                        const uint32_t c1 = s1 < hi ? min(s2, hi) - s1 : 0u;
-                        atomicMax(&s_best[b], ((c0 + c1) << 14) | (16383u - k));
-                    }
-                }
-            }
-            __syncthreads();
-            for (uint32_t b = tid; b < nb; b += kPrepThreads) {
-                uint64_t e = 0;
-                if (!bad) {
-                    const uint32_t a = 16383u - (s_best[b] & 16383u);
-                    const uint32_t s0 = row_value(s_row, a, len);
-                    const uint32_t s1 = row_value(s_row, a + 1, len);
-                    const uint32_t s2 = row_value(s_row, a + 2, len);
-                    e = (uint64_t)s0 | ((uint64_t)(s1 - s0) << 16) |
-                        ((uint64_t)(s2 - 1 - s0) << 32) | ((uint64_t)a << 48);
-                }
-                lut[((uint64_t)r << q) + b] = e;
-            }
+        if (dec_ok && !bad) {
             // first[b]: the slot holding the bucket's lowest cumulative value
-            // (bounds the search when the pair misses)
-            for (uint32_t k = tid; k + 1 < len && !bad; k += kPrepThreads) {
-                const uint32_t s0 = row_value(s_row, k, len);
-                const uint32_t s1 = row_value(s_row, k + 1, len);
-                for (uint32_t b = (s0 + width - 1) >> (kPrecision - q); b < nb && b * width < s1; ++b)
+            // (slot k covers [start(k), start(k+1)); buckets are `width` wide)
+            for (uint32_t k = tid; k + 1 < len; k += kPrepThreads) {
+                const uint32_t s0 = (uint32_t)s_val[k];
+                const uint32_t s1 = (uint32_t)s_val[k + 1];
+                for (uint32_t b = (s0 + width - 1) >> (kPrecision - q); b < (1u << q) && b * width < s1; ++b)
                     first[((uint64_t)r << q) + b] = (uint16_t)k;
             }
         }
-        __syncthreads();   // s_row is reused by the next row
+        __syncthreads();   // s_val is reused by the next row
     }
 }
 
