@@ -1,0 +1,155 @@
+"""Helpers for the rocprofv3 summaries kept under profiles/.
+
+Two commands, both meant to run under or after rocprofv3:
+
+  python -m learned_image_compression_amd.profiling copy [--mib M]
+      A plain device-to-device copy of M MiB (torch copy_, which runs the
+      HIP runtime's copy kernel), repeated a few times.  Counter passes over it
+      (FETCH_SIZE, WRITE_SIZE) give the scale between those counters and
+      bytes actually moved: a copy of M MiB reads and writes M MiB.
+
+  python -m learned_image_compression_amd.profiling summarize ...
+      Turns rocprofv3 CSV output (kernel trace statistics and the counter
+      passes) into the short text and JSON summaries committed under
+      profiles/.  Runs on the host only.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import re
+import statistics
+import sys
+
+KIB = 1024.0
+
+
+def copy_main(mib: int, reps: int) -> None:
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "reps": reps}), flush=True)
+
+
+def _rows(path_glob: str):
+    paths = sorted(glob.glob(path_glob, recursive=True))
+    if not paths:
+        raise FileNotFoundError(path_glob)
+    with open(paths[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _kernel_key(name: str) -> str:
+    m = re.search(r"(encode_kernel|decode_kernel|prep_kernel)", name)
+    if m:
+        return m.group(1)
+    if "copyBuffer" in name:
+        return "copy"
+    return name.split("(")[0][-40:]
+
+
+def counter_per_dispatch(path_glob: str, counter: str) -> dict:
+    """Mean per-dispatch value of one counter, per kernel."""
+    per = {}
+    for r in _rows(path_glob):
+        if r.get("Counter_Name") != counter:
+            continue
+        per.setdefault((_kernel_key(r["Kernel_Name"]), r["Dispatch_Id"]), 0.0)
+        per[(_kernel_key(r["Kernel_Name"]), r["Dispatch_Id"])] += float(r["Counter_Value"])
+    out = {}
+    for (k, _), v in per.items():
+        out.setdefault(k, []).append(v)
+    return {k: statistics.mean(v) for k, v in out.items()}
+
+
+def summarize_main(a) -> None:
+    os.makedirs(a.out, exist_ok=True)
+    if a.stats:
+        rows = _rows(a.stats)
+        lines = [f"# rocprofv3 kernel trace statistics: {a.label}", f"# command: {a.command}", "",
+                 f"{'kernel':<52s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
+        for r in rows:
+            name = r["Name"]
+            if not re.search(r"rans|kernel", name):
+                continue
+            lines.append(f"{name[:52]:<52s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                         f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+        if a.bench_json:
+            with open(a.bench_json) as fh:
+                bench = [json.loads(l) for l in fh if l.strip().startswith("{")][-1]
+            lines += ["", "# bench.py line of the same run (kernel_us from HIP events):",
+                      json.dumps({k: bench[k] for k in ("value", "unit", "ms_per_step", "kernel_us")})]
+        path = os.path.join(a.out, f"kernel_trace_{a.label}.txt")
+        with open(path, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(path)
+    if a.fetch and a.write:
+        fetch = counter_per_dispatch(a.fetch, "FETCH_SIZE")
+        write = counter_per_dispatch(a.write, "WRITE_SIZE")
+        cf = counter_per_dispatch(a.calib_fetch, "FETCH_SIZE")["copy"]
+        cw = counter_per_dispatch(a.calib_write, "WRITE_SIZE")["copy"]
+        copy_bytes = a.copy_mib * (1 << 20)
+        f_scale = copy_bytes / (cf * KIB)
+        w_scale = copy_bytes / (cw * KIB)
+        sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+        import bench
+        for kernel in ("encode", "decode"):
+            key = f"{kernel}_kernel"
+            rb = fetch[key] * KIB * f_scale
+            wb = write[key] * KIB * w_scale
+            t = {
+                "kernel": key, "workload": a.label, "config": a.config, "lanes": a.lanes,
+                "fetch_kib_per_dispatch": round(fetch[key], 1),
+                "write_kib_per_dispatch": round(write[key], 1),
+                "copy_calibration": {"copy_bytes": copy_bytes, "fetch_kib": round(cf, 1),
+                                     "write_kib": round(cw, 1), "fetch_scale": round(f_scale, 4),
+                                     "write_scale": round(w_scale, 4)},
+                "hbm_read_bytes_per_launch": round(rb),
+                "hbm_write_bytes_per_launch": round(wb),
+                "hbm_bytes_per_launch": round(rb + wb),
+                "source_hash": bench.kernel_source_hash(kernel),
+                "commands": a.command,
+            }
+            path = os.path.join(a.out, f"traffic_{kernel}_{a.config}_L{a.lanes}.json")
+            with open(path, "w") as fh:
+                json.dump(t, fh, indent=1)
+                fh.write("\n")
+            print(path, t["hbm_bytes_per_launch"])
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser(prog="python -m learned_image_compression_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=256)
+    c.add_argument("--reps", type=int, default=3)
+    s = sub.add_parser("summarize")
+    s.add_argument("--out", required=True)
+    s.add_argument("--label", required=True)
+    s.add_argument("--config", default="y1080")
+    s.add_argument("--lanes", type=int, default=4096)
+    s.add_argument("--command", default="")
+    s.add_argument("--stats")
+    s.add_argument("--bench-json")
+    s.add_argument("--fetch")
+    s.add_argument("--write")
+    s.add_argument("--calib-fetch")
+    s.add_argument("--calib-write")
+    s.add_argument("--copy-mib", type=int, default=256)
+    a = ap.parse_args(argv)
+    if a.cmd == "copy":
+        copy_main(a.mib, a.reps)
+    else:
+        summarize_main(a)
+
+
+if __name__ == "__main__":
+    main()
