@@ -430,21 +430,38 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             prefix = __shfl(prefix, 0, kWave);
 
             // ---- header entry and compaction --------------------------------------
-            // (each lane reads back only the scratch words it stored itself)
+            // The wave's lanes fill container words [1 + L + prefix, + agg); the
+            // output buffer ends at the capacity, so nothing is written past it.
+            // Each lane reads back only the scratch words it stored itself,
+            // sixteen per round trip, and stores whole 16-byte groups of its
+            // own words (its last one to three words one by one).
+            const uint64_t wbase = 1ull + L + __builtin_amdgcn_readfirstlane((uint32_t)prefix) +
+                                   ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(prefix >> 32)) << 32);
+            const uint64_t wroom = a.capacity > wbase ? a.capacity - wbase : 0;
+            const Rsrc rout = make_rsrc(a.stream + (wroom ? wbase : 0),
+                                        (uint32_t)min(4 * wroom, 1ull << 31));
             if (j < L) {
                 const uint64_t end = prefix + incl;
                 a.stream[1 + j] = (uint32_t)end;
-                const uint64_t dst = 1ull + L + end - words;
+                const uint32_t ob = 4 * (incl - words);   // the lane's first word in rout
                 const uint32_t src = sp.top - 4 * words;
-                for (uint32_t k0 = 0; k0 < words; k0 += 8) {
-                    uint32_t v[8];
+                for (uint32_t k0 = 0; k0 < words; k0 += 16) {
+                    u32x4 v[4];
 #pragma unroll
-                    for (uint32_t u = 0; u < 8; ++u)
-                        v[u] = (uint32_t)buf_load(sp.scr, src + 4 * min(k0 + u, words - 1), 0);
+                    for (int i = 0; i < 4; ++i)
+                        v[i] = buf_load4(sp.scr, src + 4 * k0 + 16 * i);
 #pragma unroll
-                    for (uint32_t u = 0; u < 8; ++u)
-                        if (k0 + u < words && dst + k0 + u < a.capacity)
-                            a.stream[dst + k0 + u] = v[u];
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t k = k0 + 4 * i;
+                        if (k + 4 <= words) {
+                            buf_store4(rout, ob + 4 * k, v[i]);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (k + e < words)
+                                    buf_store(rout, ob + 4 * (k + e), 0, (int32_t)v[i][e]);
+                        }
+                    }
                 }
             }
         }

@@ -117,26 +117,22 @@ inline uint32_t decode_lds_bytes(uint32_t tpb) { return kDecTableBudget + kDecRi
 inline uint32_t encode_lds_bytes(uint32_t tpb) { return kEncTableBudget + kEncRing * 4 * tpb; }
 
 // Copy `nbytes` (a multiple of 16) of prepared tables from global memory into
-// LDS with every thread keeping sixteen 16-byte loads in flight.
+// LDS.  gfx950 loads 16 bytes per lane straight into LDS (global_load_lds,
+// the LDS address being a per-wave base plus 16 bytes per lane), so every
+// wave issues all of its loads back to back and waits once.
 template <int TPB>
 __device__ inline void stage_tables(uint8_t *lds, const uint8_t *src, uint32_t nbytes)
 {
-    constexpr int kBatch = 16;
-    const uint4 *s = reinterpret_cast<const uint4 *>(src);
-    uint4 *d = reinterpret_cast<uint4 *>(lds);
     const uint32_t n16 = nbytes / 16;
-    if (n16 == 0)
-        return;
-    for (uint32_t i0 = threadIdx.x; i0 < n16; i0 += kBatch * TPB) {
-        uint4 v[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-            v[u] = s[min(i0 + u * TPB, n16 - 1)];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-            if (i0 + u * TPB < n16)
-                d[i0 + u * TPB] = v[u];
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    for (uint32_t i0 = threadIdx.x - lane; i0 < n16; i0 += TPB) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(i0);   // the wave's first chunk
+        if (i0 + lane < n16)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(src) + i0 + lane,
+                                             (__attribute__((address_space(3))) void *)(lds + 16 * base),
+                                             16, 0, 0);
     }
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // Raw buffer access (gfx9 buffer descriptor, 32-bit data format): the

@@ -175,12 +175,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
         }
         if (dec_ok && !bad) {
             // first[b]: the slot holding the bucket's lowest cumulative value
-            // (slot k covers [start(k), start(k+1)); buckets are `width` wide)
-            for (uint32_t k = tid; k + 1 < len; k += kPrepThreads) {
-                const uint32_t s0 = (uint32_t)s_val[k];
-                const uint32_t s1 = (uint32_t)s_val[k + 1];
-                for (uint32_t b = (s0 + width - 1) >> (kPrecision - q); b < (1u << q) && b * width < s1; ++b)
-                    first[((uint64_t)r << q) + b] = (uint16_t)k;
+            // b * width, i.e. the last k with start(k) <= b * width (slot k
+            // covers [start(k), start(k+1))); one thread per bucket, binary
+            // search over the staged row
+            for (uint32_t b = tid; b < (1u << q); b += kPrepThreads) {
+                const int32_t c = (int32_t)(b * width);
+                uint32_t lo = 0, hi = len - 1;   // start(lo) <= c < start(hi)
+                while (hi - lo > 1) {
+                    const uint32_t mid = (lo + hi) >> 1;
+                    if (s_val[mid] <= c)
+                        lo = mid;
+                    else
+                        hi = mid;
+                }
+                first[((uint64_t)r << q) + b] = (uint16_t)lo;
             }
         }
         __syncthreads();   // s_val is reused by the next row
