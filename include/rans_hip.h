@@ -75,7 +75,7 @@ enum rans_status {
 #define RANS_MAX_TABLES 4096
 #define RANS_MAX_STRIDE 16384
 #define RANS_MAX_SYMBOLS (1ull << 28)
-#define RANS_MAX_LANES (1u << 26)
+#define RANS_MAX_LANES (1u << 22)
 
 /* Words an encoded container can need in the worst case (every symbol an
  * escape with a 31-bit raw value): 1 + L header words plus, per lane,

@@ -286,11 +286,14 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     if (herr && blockIdx.x == 0 && tid == 0)
         record_error(hdr, herr);
 
-    const uint32_t j = blockIdx.x * TPB + tid;
+    // the wave codes lanes j0 .. j0 + lpw - 1, one per wavefront lane
+    const uint32_t lpw = dec_lanes_per_wave(L);
+    const uint32_t lane = tid & (kWave - 1);
+    const uint32_t j0 = __builtin_amdgcn_readfirstlane((blockIdx.x * (TPB / kWave) + tid / kWave) * lpw);
+    const uint32_t j = j0 + lane;
     // the wave's index and symbol spans, and its stream words, as buffers
-    const uint32_t j0 = __builtin_amdgcn_readfirstlane(j) & ~(uint32_t)(kWave - 1);
     if (!herr && j0 < L) {
-        const uint32_t j1 = min(j0 + kWave, L);
+        const uint32_t j1 = min(j0 + lpw, L);
         const uint64_t bw = lane_begin(a.n, L, j0), ew = lane_begin(a.n, L, j1);
         const Rsrc ridx = make_rsrc(a.indexes + bw, (uint32_t)(4 * (ew - bw)));
         const Rsrc rout = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
         const uint64_t wavail = a.capacity - 1 - L;
         const uint64_t wbytes = wbase < wavail ? min(4 * (wavail - wbase), 1ull << 31) : 0;
         const Rsrc rstr = make_rsrc(a.stream + 1 + L + (wbase < wavail ? wbase : 0), (uint32_t)wbytes);
-        if (j < L) {
+        if (lane < lpw && j < L) {
             int lerr = 0;
             const uint64_t beg_w = j ? a.stream[j] : 0u;
             const uint64_t end_w = a.stream[1 + j];
@@ -462,7 +465,7 @@ hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s)
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (attr != hipSuccess)
         return attr;
-    const uint32_t blocks = (uint32_t)((a.lanes + TPB - 1) / TPB);
+    const uint32_t blocks = (dec_waves(a.lanes) + TPB / kWave - 1) / (TPB / kWave);
     hipLaunchKernelGGL(decode_kernel<TPB>, dim3(blocks), dim3(TPB), lds_bytes, s, a);
     return hipGetLastError();
 }
@@ -471,9 +474,9 @@ hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s)
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
 {
-    if (coding_block_threads(a.lanes) <= 256)
-        return launch_decode_t<256>(a, s);
-    return launch_decode_t<512>(a, s);
+    if (coding_block_threads(dec_waves(a.lanes)) == kWave)
+        return launch_decode_t<kWave>(a, s);
+    return launch_decode_t<8 * kWave>(a, s);
 }
 
 }  // namespace rans

@@ -188,7 +188,8 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kWave - 1);
     const uint32_t L = a.lanes;
-    const uint32_t nwork = (uint32_t)ws_flag_count(L);
+    const uint32_t lpw = enc_lanes_per_wave(L);
+    const uint32_t nwork = enc_waves(L);
 
     // ---- tables -> LDS -------------------------------------------------------
     int herr = 0;
@@ -221,9 +222,11 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             t = atomicAdd(&hdr->ticket, 1u);
         t = __builtin_amdgcn_readfirstlane(__shfl(t, 0, kWave));
         if (t < nwork) {
-            const uint32_t j = t * kWave + lane;
+            // the wave codes lanes j0 .. j0 + lpw - 1, one per wavefront lane
+            const uint32_t j0 = t * lpw, j1 = min(j0 + lpw, L);
+            const uint32_t j = j0 + lane;
+            const bool active = lane < lpw && j < L;
             // the wave's symbols and scratch segments, as buffers
-            const uint32_t j0 = t * kWave, j1 = min(j0 + kWave, L);
             const uint64_t bw = lane_begin(a.n, L, j0), ew = lane_begin(a.n, L, j1);
             const Rsrc rsym = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
             const Rsrc ridx = make_rsrc(a.indexes + bw, (uint32_t)(4 * (ew - bw)));
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             sp.top = 0;
             uint32_t words = 0;
             int lerr = 0;
-            if (j < L) {
+            if (active) {
                 const uint64_t b = lane_begin(a.n, L, j);
                 const uint64_t e = lane_begin(a.n, L, j + 1);
                 const uint32_t nj = (uint32_t)(e - b);
@@ -390,44 +393,58 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
                 record_error(hdr, lerr);
 
             // ---- wave scan and look-back over earlier tickets ---------------------
+            // Every wave publishes its aggregate, then reads the flags of the 64
+            // tickets before it at once (one per wavefront lane): the nearest
+            // inclusive flag ends the walk once every flag after it is
+            // published, and the values up to it are summed across the wave.
+            // A flag carries all it says in its own 64 bits, so the flags are
+            // relaxed device-scope atomics: no cache writeback or invalidation
+            // per publication or poll (spinning waves would otherwise keep
+            // flushing the L2 that the working waves read from).
             const uint32_t incl = wave_inclusive_scan(words, lane);
             const uint64_t agg = __shfl(incl, kWave - 1, kWave);
             uint64_t prefix = 0;
-            if (lane == 0) {
-                if (t == 0) {
-                    __hip_atomic_store(&flags[t], kFlagInclusive | agg, __ATOMIC_RELEASE,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                } else {
-                    __hip_atomic_store(&flags[t], kFlagAggregate | agg, __ATOMIC_RELEASE,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                    uint32_t k = t;
-                    uint32_t spins = 0;
-                    while (k > 0) {
-                        const uint64_t fv = __hip_atomic_load(&flags[k - 1], __ATOMIC_ACQUIRE,
-                                                              __HIP_MEMORY_SCOPE_AGENT);
-                        if ((fv >> 62) == 0) {
-                            if (++spins > kSpinLimit) {   // never expected: bail out, flag it
+            if (lane == 0)
+                __hip_atomic_store(&flags[t], (t == 0 ? kFlagInclusive : kFlagAggregate) | agg,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (t > 0) {
+                int32_t k = (int32_t)t;   // this window covers tickets k-1 .. k-64
+                uint32_t spins = 0;
+                while (true) {
+                    const int32_t p = k - 1 - (int32_t)lane;
+                    const uint64_t fv = p >= 0 ? __hip_atomic_load(&flags[p], __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_AGENT)
+                                               : kFlagInclusive;
+                    const uint64_t incl_mask = __ballot((fv >> 62) == 2);
+                    const uint64_t ready_mask = __ballot((fv >> 62) != 0);
+                    const uint32_t fi = incl_mask ? (uint32_t)__builtin_ctzll(incl_mask) : 64u;
+                    const uint64_t need = fi >= 63 ? ~0ull : ((2ull << fi) - 1);
+                    if ((ready_mask & need) != need) {
+                        if (++spins > kSpinLimit) {   // never expected: bail out, flag it
+                            if (lane == 0)
                                 record_error(hdr, RANS_E_HIP);
-                                break;
-                            }
-                            __builtin_amdgcn_s_sleep(1);
-                            continue;
-                        }
-                        prefix += fv & kFlagValueMask;
-                        if ((fv >> 62) == 2)
                             break;
-                        --k;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                        continue;
                     }
-                    __hip_atomic_store(&flags[t], kFlagInclusive | (prefix + agg), __ATOMIC_RELEASE,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                    uint64_t v = lane <= fi ? (fv & kFlagValueMask) : 0;
+                    for (int off = 1; off < kWave; off <<= 1)
+                        v += __shfl_xor(v, off, kWave);
+                    prefix += v;
+                    if (fi < 64)
+                        break;
+                    k -= kWave;
                 }
-                if (t == nwork - 1) {
-                    a.stream[0] = L;
-                    __hip_atomic_store(&hdr->total_words, prefix + agg, __ATOMIC_RELEASE,
+                if (lane == 0)
+                    __hip_atomic_store(&flags[t], kFlagInclusive | (prefix + agg), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
-                }
             }
-            prefix = __shfl(prefix, 0, kWave);
+            if (lane == 0 && t == nwork - 1) {
+                a.stream[0] = L;
+                __hip_atomic_store(&hdr->total_words, prefix + agg, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
 
             // ---- header entry and compaction --------------------------------------
             // The wave's lanes fill container words [1 + L + prefix, + agg); the
@@ -440,7 +457,7 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             const uint64_t wroom = a.capacity > wbase ? a.capacity - wbase : 0;
             const Rsrc rout = make_rsrc(a.stream + (wroom ? wbase : 0),
                                         (uint32_t)min(4 * wroom, 1ull << 31));
-            if (j < L) {
+            if (active) {
                 const uint64_t end = prefix + incl;
                 a.stream[1 + j] = (uint32_t)end;
                 const uint32_t ob = 4 * (incl - words);   // the lane's first word in rout
@@ -505,7 +522,7 @@ hipError_t launch_encode_t(const EncodeArgs &a, hipStream_t s)
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (attr != hipSuccess)
         return attr;
-    const uint32_t blocks = (uint32_t)((a.lanes + TPB - 1) / TPB);
+    const uint32_t blocks = (enc_waves(a.lanes) + TPB / kWave - 1) / (TPB / kWave);
     hipLaunchKernelGGL(encode_kernel<TPB>, dim3(blocks), dim3(TPB), lds_bytes, s, a);
     return hipGetLastError();
 }
@@ -514,9 +531,9 @@ hipError_t launch_encode_t(const EncodeArgs &a, hipStream_t s)
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s)
 {
-    if (coding_block_threads(a.lanes) <= 256)
-        return launch_encode_t<256>(a, s);
-    return launch_encode_t<512>(a, s);
+    if (coding_block_threads(enc_waves(a.lanes)) == kWave)
+        return launch_encode_t<kWave>(a, s);
+    return launch_encode_t<8 * kWave>(a, s);
 }
 
 }  // namespace rans

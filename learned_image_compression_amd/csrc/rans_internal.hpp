@@ -87,10 +87,55 @@ inline __host__ __device__ uint64_t ws_flags_offset()
 {
     return align_up(kHeaderBytes + kDecTableBudget + kEncTableBudget, 256);
 }
-inline __host__ __device__ uint64_t ws_flag_count(uint32_t lanes) { return (lanes + kWave - 1) / kWave; }
-inline __host__ __device__ uint64_t ws_scratch_offset(uint32_t lanes)
+// Lanes per wavefront and waves per block.  Each lane is a serial chain of
+// steps, so a coding kernel is bound by the latency of one step, not by issue
+// width: a wave with few active lanes costs the same per step as a full one.
+// What grows with the lanes of a wave is the chance that one of them leaves
+// the common path at a step (an escape, a lookup outside the window), which
+// the whole wave then waits for.  So lanes are spread thin (1, 2, 4, .. 64 per
+// wave) until a wave budget is reached.  Each block stages the table set into
+// one CU's LDS.  Measured on MI355X (1080p latent, 4096 lanes): one wave per
+// CU and two waves per SIMD (8 per CU) both keep every CU at full speed, while
+// four waves per CU (one per SIMD) run up to twice slower on some CUs of each
+// shader engine; so blocks hold one wave or eight.
+//   decoder: up to 2048 waves;
+//   encoder: one wave per CU (256 waves) up to 4096 lanes, up to 1024 waves
+//            beyond (its escape rounds then cost more than the CU shape).
+constexpr uint32_t kCodingCUs = 256;
+constexpr __host__ __device__ uint32_t lanes_per_wave_for(uint32_t lanes, uint32_t max_waves)
 {
-    return align_up(ws_flags_offset() + 8ull * ws_flag_count(lanes), 256);
+    uint32_t w = 1;
+    while (w < (uint32_t)kWave && (lanes + w - 1) / w > max_waves)
+        w *= 2;
+    return w;
+}
+constexpr __host__ __device__ uint32_t dec_lanes_per_wave(uint32_t lanes)
+{
+    return lanes_per_wave_for(lanes, 2048);
+}
+constexpr __host__ __device__ uint32_t enc_lanes_per_wave(uint32_t lanes)
+{
+    return lanes_per_wave_for(lanes, lanes <= 4096 ? kCodingCUs : 1024);
+}
+constexpr __host__ __device__ uint32_t enc_waves(uint32_t lanes)
+{
+    const uint32_t w = enc_lanes_per_wave(lanes);
+    return (lanes + w - 1) / w;
+}
+constexpr __host__ __device__ uint32_t dec_waves(uint32_t lanes)
+{
+    const uint32_t w = dec_lanes_per_wave(lanes);
+    return (lanes + w - 1) / w;
+}
+inline __host__ __device__ uint64_t ws_flag_count(uint32_t lanes) { return enc_waves(lanes); }
+// The flag region has room for the waves of the largest lane count and the
+// same place for every call: flags must read zero when a call starts (the
+// previous call's last block clears the ones it used), so no call may keep
+// scratch words where a later call with more waves looks for flags.
+constexpr uint32_t kMaxCodingWaves = RANS_MAX_LANES / kWave;
+inline __host__ __device__ uint64_t ws_scratch_offset(uint32_t /*lanes*/)
+{
+    return align_up(ws_flags_offset() + 8ull * kMaxCodingWaves, 256);
 }
 // Lane j's encode scratch holds 2 * n_j + 4 words: a symbol spills at most
 // 52 bits (16 for its slot, 4 for the group count, 32 for raw groups).
@@ -106,12 +151,13 @@ inline __host__ __device__ uint64_t lane_begin(uint64_t n, uint32_t lanes, uint3
     return (uint64_t)j * a + ((uint64_t)j * b) / lanes;
 }
 
-// Threads per block for the coding kernels: each block stages its table set
-// into LDS once (one block fills a CU's LDS), so blocks are large -- 256
-// threads, 512 beyond 256 blocks of 256.
-inline uint32_t coding_block_threads(uint32_t lanes)
+static_assert(enc_waves(RANS_MAX_LANES) <= kMaxCodingWaves, "flag region too small");
+
+// Threads per block: one wave per block while the waves fit one per CU,
+// else eight (two per SIMD).
+inline uint32_t coding_block_threads(uint32_t waves)
 {
-    return lanes > 256u * 256u ? 512u : 256u;
+    return waves <= kCodingCUs ? kWave : 8 * kWave;
 }
 inline uint32_t decode_lds_bytes(uint32_t tpb) { return kDecTableBudget + kDecRing * 4 * tpb; }
 inline uint32_t encode_lds_bytes(uint32_t tpb) { return kEncTableBudget + kEncRing * 4 * tpb; }

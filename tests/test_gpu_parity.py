@@ -164,6 +164,19 @@ def test_wide_rows_uniform_symbols():
         assert st == 0 and np.array_equal(out, syms)
 
 
+def test_workspace_reuse_across_lane_counts():
+    """One workspace, calls with growing and shrinking wave counts: every
+    call must find its look-back flags zero, whatever earlier calls with
+    other lane counts left in the workspace."""
+    import gpu_util as G
+    w, tables, sym, idx = _workload("tiny")
+    for lanes in (64, 1000, 7, 4096, 2048, 16384, 300, 5000):
+        G.say(f"[reuse] lanes={lanes}")
+        rc, ref = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, lanes)
+        st, got, _ = G.gpu_encode(sym, idx, tables, lanes)
+        assert rc == 0 and st == 0 and np.array_equal(got, ref)
+
+
 def test_repeat_calls_are_identical_and_workspace_is_reusable():
     import gpu_util as G
     w, tables, sym, idx = _workload("tiny")
