@@ -212,24 +212,30 @@ __device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_
                                             const DecTables &t, int32_t &out, int &lerr)
 {
     const uint32_t cum = (uint32_t)x & (kTotal - 1);
+    const uint32_t xlo_m1 = (uint32_t)x - 1u;   // cum - 1 mod 2^16 in the low half
     const uint32_t bucket = cum >> t.shift;
     const uint32_t fs = *reinterpret_cast<const uint16_t *>(t.lds + m.lut + 2 * bucket);
     const uint64_t v = *reinterpret_cast<const uint64_t *>(t.lds + m.base + 2 * fs);
-    const uint32_t v0 = (uint32_t)v & 0xFFFFu, v1 = (uint32_t)(v >> 16) & 0xFFFFu;
-    const uint32_t v2 = (uint32_t)(v >> 32) & 0xFFFFu, v3 = (uint32_t)(v >> 48);
-    const bool c1 = cum > v1;
-    const bool c2 = c1 & (cum > v2);
-    const bool beyond = c2 & (cum > v3);
+    const uint32_t wlo = (uint32_t)v, whi = (uint32_t)(v >> 32);   // cdfm1[fs..fs+1], [fs+2..fs+3]
+    const bool c1 = cum > (wlo >> 16);
+    const bool c2 = c1 & (cum > (whi & 0xFFFFu));
+    const bool beyond = c2 & (cum > (whi >> 16));
     const uint32_t slot = fs + (c1 ? 1u : 0u) + (c2 ? 1u : 0u);
-    const uint32_t sm1 = c2 ? v2 : (c1 ? v1 : v0);
-    const uint32_t em1 = c2 ? v3 : (c1 ? v2 : v1);
-    const uint32_t f = (em1 - sm1) & 0xFFFFu;
-    const uint32_t rr = (cum - sm1 - 1) & 0xFFFFu;
+    // the slot's cdfm1 pair (start - 1, next start - 1) as one packed word;
+    // f = its high half minus its low half and rr = cum - start, both mod
+    // 2^16 (16-bit subtractions on the halves, upper bits cleared)
+    const uint32_t pair = c2 ? whi : (c1 ? __builtin_amdgcn_alignbit(whi, wlo, 16) : wlo);
+    uint32_t f, rr;
+    asm("v_sub_u16_sdwa %0, %1, %1 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:WORD_1 src1_sel:WORD_0"
+        : "=v"(f) : "v"(pair));
+    asm("v_sub_u16_sdwa %0, %1, %2 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_0"
+        : "=v"(rr) : "v"(xlo_m1), "v"(pair));
     // f * (x >> 16) + rr with x >> 16 < 2^48 split at bit 32
     const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
     const uint32_t mid = __builtin_amdgcn_alignbit(xhi, xlo, 16);
-    uint64_t xn = (uint64_t)f * mid + rr;
-    xn += (uint64_t)__umul24(f, xhi >> 16) << 32;
+    const uint64_t lo64 = (uint64_t)f * mid + rr;
+    const uint32_t nhi = (uint32_t)(lo64 >> 32) + __umul24(f, xhi >> 16);
+    const uint64_t xn = ((uint64_t)nhi << 32) | (uint32_t)lo64;
     const bool need = xn < kStateLow;
     const bool slow = beyond | (slot >= (m.mvf >> 16)) | (need & (wd.pos >= wd.filled));
     const uint64_t x0 = x;
@@ -252,7 +258,8 @@ template <int TPB>
 __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
-    __shared__ int s_last;
+    // block bookkeeping after the table set and the rings: [0] flag OR, [1] last block
+    uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kDecTableBudget + kDecRing * 4 * TPB);
 
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
     const uint8_t *tab = a.ws + ws_tables_offset();
@@ -280,7 +287,10 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     if (!herr)
         for (uint32_t r = tid; r < K; r += TPB)
             bad |= (t.meta[r].lut & kRowInvalid) ? 1 : 0;
-    bad = __syncthreads_or(bad);
+    if (tid == 0)
+        misc[0] = 0u;
+    __syncthreads();
+    bad = block_or(&misc[0], bad);
     if (!herr && bad)
         herr = RANS_E_TABLE;
     if (herr && blockIdx.x == 0 && tid == 0)
@@ -444,10 +454,10 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     if (tid == 0) {
         __threadfence();
         const uint32_t old = atomicAdd(&hdr->done, 1u);
-        s_last = (old == gridDim.x - 1) ? 1 : 0;
+        misc[1] = (old == gridDim.x - 1) ? 1u : 0u;
     }
     __syncthreads();
-    if (s_last && tid == 0) {
+    if (misc[1] && tid == 0) {
         __threadfence();
         *a.status = hdr->err;
         hdr->err = 0;

@@ -179,7 +179,8 @@ template <int TPB>
 __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
-    __shared__ int s_last;
+    // block bookkeeping after the table set and the rings: [0] flag OR, [1] last block
+    uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kEncTableBudget + kEncRing * 4 * TPB);
 
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
     const uint8_t *tab = a.ws + ws_enc_tables_offset();
@@ -209,7 +210,10 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     if (!herr)
         for (uint32_t r = tid; r < K; r += TPB)
             bad |= (et.meta[r].lut & kRowInvalid) ? 1 : 0;
-    bad = __syncthreads_or(bad);
+    if (tid == 0)
+        misc[0] = 0u;
+    __syncthreads();
+    bad = block_or(&misc[0], bad);
     if (!herr && bad)
         herr = RANS_E_TABLE;
     if (herr && blockIdx.x == 0 && tid == 0)
@@ -489,10 +493,10 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     if (tid == 0) {
         __threadfence();
         const uint32_t old = atomicAdd(&hdr->done, 1u);
-        s_last = (old == gridDim.x - 1) ? 1 : 0;
+        misc[1] = (old == gridDim.x - 1) ? 1u : 0u;
     }
     __syncthreads();
-    if (s_last) {
+    if (misc[1]) {
         __threadfence();
         if (!herr)
             for (uint32_t k = tid; k < nwork; k += TPB)

@@ -159,8 +159,33 @@ inline uint32_t coding_block_threads(uint32_t waves)
 {
     return waves <= kCodingCUs ? kWave : 8 * kWave;
 }
-inline uint32_t decode_lds_bytes(uint32_t tpb) { return kDecTableBudget + kDecRing * 4 * tpb; }
-inline uint32_t encode_lds_bytes(uint32_t tpb) { return kEncTableBudget + kEncRing * 4 * tpb; }
+// Dynamic LDS of a coding block: the table set, the word rings, then a few
+// words of block bookkeeping.  The kernels declare no static LDS, so the
+// dynamic area starts at LDS address 0 and a table byte offset is its LDS
+// address (no base to add on every access).
+constexpr uint32_t kLdsMiscBytes = 16;
+__host__ __device__ constexpr uint32_t decode_lds_bytes(uint32_t tpb)
+{
+    return kDecTableBudget + kDecRing * 4 * tpb + kLdsMiscBytes;
+}
+__host__ __device__ constexpr uint32_t encode_lds_bytes(uint32_t tpb)
+{
+    return kEncTableBudget + kEncRing * 4 * tpb + kLdsMiscBytes;
+}
+
+// Block-wide OR of one flag through an LDS word (`word` is zero on entry and
+// is left zero for the next use).
+__device__ inline bool block_or(uint32_t *word, bool v)
+{
+    if (v)
+        *word = 1u;
+    __syncthreads();
+    const bool r = *word != 0u;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *word = 0u;
+    return r;
+}
 
 // Copy `nbytes` (a multiple of 16) of prepared tables from global memory into
 // LDS.  gfx950 loads 16 bytes per lane straight into LDS (global_load_lds,
