@@ -49,13 +49,15 @@ __device__ inline void record_error(WsHeader *hdr, int code)
 template <int TPB>
 struct Words {
     const uint32_t *w;   // the lane's words in global memory
-    uint32_t *ring;      // ring slot 0 of this lane (slots are TPB words apart)
+    uint32_t ring;       // LDS address of this lane's ring slot 0 (slots are TPB words apart)
     uint32_t count;      // words in the lane
     uint32_t pos;        // next word to consume
     uint32_t filled;     // words [.., filled) have been written to the ring
     uint32_t next;       // ring word at pos (valid when pos < filled)
 
-    __device__ inline uint32_t *slot(uint32_t p) const { return ring + (p % kDecRing) * TPB; }
+    __device__ inline uint32_t slot(uint32_t p) const { return ring | ((p % kDecRing) * (4 * TPB)); }
+    __device__ inline uint32_t at(uint32_t p) const { return lds_load<uint32_t>(slot(p)); }
+    __device__ inline void put(uint32_t p, uint32_t v) const { lds_store<uint32_t>(slot(p), v); }
 
     // x < 2^31 after a step means the encoder spilled a word there.
     __device__ inline bool refill(uint64_t &x)
@@ -74,25 +76,23 @@ struct Words {
             }
             ++pos;
         }
-        next = *slot(pos);
+        next = at(pos);
         return true;
     }
 };
 
-// Decoder tables in LDS: [meta | cdfm1 | first].  cdfm1[k] = start(k) - 1
-// mod 2^16 (the terminal 65536 becomes 65535), so cum >= start(k) is
-// cum > cdfm1[k] and f(k) = cdfm1[k+1] - cdfm1[k] mod 2^16.
+// Decoder tables in LDS at address 0: [meta | cdfm1 | first].  cdfm1[k] =
+// start(k) - 1 mod 2^16 (the terminal 65536 becomes 65535), so cum >= start(k)
+// is cum > cdfm1[k] and f(k) = cdfm1[k+1] - cdfm1[k] mod 2^16.
 struct DecTables {
-    const uint8_t *lds;
-    const RowMeta *meta;
     uint32_t q;              // 2^q buckets per row
     uint32_t shift;          // 16 - q: cumulative value -> bucket
     uint32_t K;
 };
 
-__device__ inline uint32_t cdfm1_at(const DecTables &t, const RowMeta &m, uint32_t k)
+__device__ inline uint32_t cdfm1_at(const DecTables &, const RowMeta &m, uint32_t k)
 {
-    return *reinterpret_cast<const uint16_t *>(t.lds + m.base + 2 * k);
+    return lds_load<uint16_t>(m.base + 2 * k);
 }
 
 // Slow step of one lane, from the state before the step.  `slot`, `f` and
@@ -118,9 +118,10 @@ __device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint32_t
     const uint32_t mv = m.mvf & 0xFFFFu;
     const uint32_t cum = (uint32_t)x & (kTotal - 1);
     if (__ballot(beyond) != 0) {
-        const uint16_t *fst = reinterpret_cast<const uint16_t *>(t.lds + (m.lut & ~kRowInvalid));
         uint32_t lo = slot;   // value(lo) <= cum
-        const uint32_t hi = (bucket + 1 < (1u << t.q)) ? (uint32_t)fst[bucket + 1] : mv;
+        const uint32_t hi = (bucket + 1 < (1u << t.q))
+                                ? lds_load<uint16_t>((m.lut & ~kRowInvalid) + 2 * (bucket + 1))
+                                : mv;
         // the slot is the last k in [lo, hi] with value(k) <= cum
         uint32_t c;
         do {
@@ -144,7 +145,7 @@ __device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint32_t
     int err = 0;
     if (wd.pos + 3 <= wd.filled) {
         // the next three words are in the ring
-        uint32_t q0 = wd.next, q1 = *wd.slot(wd.pos + 1), q2 = *wd.slot(wd.pos + 2);
+        uint32_t q0 = wd.next, q1 = wd.at(wd.pos + 1), q2 = wd.at(wd.pos + 2);
         uint32_t used = 0;
         auto renorm = [&]() {
             const bool need = x < kStateLow;
@@ -214,8 +215,8 @@ __device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_
     const uint32_t cum = (uint32_t)x & (kTotal - 1);
     const uint32_t xlo_m1 = (uint32_t)x - 1u;   // cum - 1 mod 2^16 in the low half
     const uint32_t bucket = cum >> t.shift;
-    const uint32_t fs = *reinterpret_cast<const uint16_t *>(t.lds + m.lut + 2 * bucket);
-    const uint64_t v = *reinterpret_cast<const uint64_t *>(t.lds + m.base + 2 * fs);
+    const uint32_t fs = lds_load<uint16_t>(m.lut + 2 * bucket);
+    const uint64_t v = lds_load<uint64_t>(m.base + 2 * fs);
     const uint32_t wlo = (uint32_t)v, whi = (uint32_t)(v >> 32);   // cdfm1[fs..fs+1], [fs+2..fs+3]
     const bool c1 = cum > (wlo >> 16);
     const bool c2 = c1 & (cum > (whi & 0xFFFFu));
@@ -251,7 +252,7 @@ __device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_
             lerr = lerr ? lerr : ec;
         }
     }
-    wd.next = *wd.slot(wd.pos);
+    wd.next = wd.at(wd.pos);
 }
 
 template <int TPB>
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
     // block bookkeeping after the table set and the rings: [0] flag OR, [1] last block
-    uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kDecTableBudget + kDecRing * 4 * TPB);
+    uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kDecTableBudget);
 
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
     const uint8_t *tab = a.ws + ws_tables_offset();
@@ -271,22 +272,22 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
         herr = RANS_E_ARG;
     else if (!hdr->dec_ok)
         herr = RANS_E_TABLE_SIZE;
+    else if (lds_address_of(lds) != 0)   // table offsets are used as LDS addresses
+        herr = RANS_E_HIP;
     const uint32_t K = (uint32_t)a.num_tables;
     const uint32_t nbytes = herr ? 0u : hdr->dec_bytes;
     const uint32_t q = hdr->lut_q;
     stage_tables<TPB>(lds, tab, nbytes);
     __syncthreads();
     DecTables t;
-    t.lds = lds;
-    t.meta = reinterpret_cast<const RowMeta *>(lds);
     t.q = q;
     t.shift = kPrecision - q;
     t.K = K;
-    uint32_t *ring = reinterpret_cast<uint32_t *>(lds + kDecTableBudget) + tid;
+    const uint32_t ring = decode_ring_base(TPB) + 4 * tid;
     int bad = 0;
     if (!herr)
         for (uint32_t r = tid; r < K; r += TPB)
-            bad |= (t.meta[r].lut & kRowInvalid) ? 1 : 0;
+            bad |= (lds_meta(r).lut & kRowInvalid) ? 1 : 0;
     if (tid == 0)
         misc[0] = 0u;
     __syncthreads();
@@ -333,11 +334,11 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
                     const uint32_t v[kDecRing] = {w0[2], w0[3], w1[0], w1[1], w1[2], w1[3], w2[0], w2[1]};
 #pragma unroll
                     for (uint32_t k = 0; k < kDecRing; ++k)
-                        *wd.slot(2 + k) = v[k];
+                        wd.put(2 + k, v[k]);
                 }
                 wd.pos = 2;
                 wd.filled = min(wd.count, 2u + kDecRing);
-                wd.next = *wd.slot(2);
+                wd.next = wd.at(2);
                 uint32_t pend[kRefill];
                 uint32_t pend_at = wd.filled;
 
@@ -389,20 +390,33 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
                     if (pend_at == wd.filled && wd.filled + kRefill <= wd.pos + kDecRing) {
 #pragma unroll
                         for (uint32_t k = 0; k < kRefill; ++k)
-                            *wd.slot(wd.filled + k) = pend[k];
+                            wd.put(wd.filled + k, pend[k]);
                         wd.filled = min(wd.count, wd.filled + kRefill);
                     }
                     if (wd.filled < wd.pos)   // the lane outran its ring via direct reads
                         wd.filled = wd.pos;
-                    wd.next = *wd.slot(wd.pos);
+                    wd.next = wd.at(wd.pos);
                 };
                 auto round = [&](int32_t (&idx)[kRound], uint32_t k0) {
+                    // row metadata; an index outside [0, K) reads row K-1 with a
+                    // fast bound of 0 (its step then reports the index), which
+                    // only a round holding such an index has to arrange
                     RowMeta m[kRound];
+                    uint32_t imax = (uint32_t)idx[0];
 #pragma unroll
-                    for (int u = 0; u < kRound; ++u) {
-                        m[u] = t.meta[min((uint32_t)idx[u], K - 1)];
-                        if ((uint32_t)idx[u] >= K)
-                            m[u].mvf = 0;
+                    for (int u = 1; u < kRound; ++u)
+                        imax = max(imax, (uint32_t)idx[u]);
+                    if (__builtin_expect(__ballot(imax >= K) == 0, 1)) {
+#pragma unroll
+                        for (int u = 0; u < kRound; ++u)
+                            m[u] = lds_meta((uint32_t)idx[u]);
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < kRound; ++u) {
+                            m[u] = lds_meta(min((uint32_t)idx[u], K - 1));
+                            if ((uint32_t)idx[u] >= K)
+                                m[u].mvf = 0;
+                        }
                     }
                     if (__all(k0 + kRound <= nj)) {
                         // a full round for every lane of the wave

@@ -68,7 +68,7 @@ static_assert(sizeof(WsHeader) <= kHeaderBytes, "header too large");
 //           offset + slot fits int32 (mv, or 0 when it might not)
 //   lut     decoder: byte offset of the row's first-slot entries in the set;
 //           both: bit 31 set when the row is invalid
-struct RowMeta {
+struct alignas(16) RowMeta {
     uint32_t base;
     int32_t offset;
     uint32_t mvf;
@@ -159,14 +159,51 @@ inline uint32_t coding_block_threads(uint32_t waves)
 {
     return waves <= kCodingCUs ? kWave : 8 * kWave;
 }
-// Dynamic LDS of a coding block: the table set, the word rings, then a few
-// words of block bookkeeping.  The kernels declare no static LDS, so the
-// dynamic area starts at LDS address 0 and a table byte offset is its LDS
-// address (no base to add on every access).
+// Dynamic LDS of a coding block: the table set, a few words of block
+// bookkeeping, then the word rings.  The kernels declare no static LDS, so
+// the dynamic area starts at LDS address 0 and a table byte offset is its LDS
+// address (no base to add on every access; each kernel checks the base once).
+// The decoder's ring area is aligned to its own size, so the address of ring
+// slot p of a lane is the lane's slot 0 OR'ed with (p mod 8) * 4 * TPB.
 constexpr uint32_t kLdsMiscBytes = 16;
+__host__ __device__ constexpr uint32_t decode_ring_base(uint32_t tpb)
+{
+    return (uint32_t)((kDecTableBudget + kLdsMiscBytes + kDecRing * 4 * tpb - 1) /
+                      (kDecRing * 4 * tpb) * (kDecRing * 4 * tpb));
+}
 __host__ __device__ constexpr uint32_t decode_lds_bytes(uint32_t tpb)
 {
-    return kDecTableBudget + kDecRing * 4 * tpb + kLdsMiscBytes;
+    return decode_ring_base(tpb) + kDecRing * 4 * tpb;
+}
+static_assert(decode_lds_bytes(kMaxBlockThreads) <= kLdsBytes, "decoder LDS over budget");
+
+// LDS access by byte address (the dynamic area starts at address 0).
+template <typename T>
+__device__ inline T lds_load(uint32_t addr)
+{
+    return *(const __attribute__((address_space(3))) T *)(uintptr_t)addr;
+}
+template <typename T>
+__device__ inline void lds_store(uint32_t addr, T v)
+{
+    *(__attribute__((address_space(3))) T *)(uintptr_t)addr = v;
+}
+// Row metadata from LDS as one 16-byte read.
+__device__ inline RowMeta lds_meta(uint32_t row)
+{
+    typedef __attribute__((ext_vector_type(4))) uint32_t v4;
+    const v4 w = lds_load<v4>(16 * row);
+    RowMeta m;
+    m.base = w[0];
+    m.offset = (int32_t)w[1];
+    m.mvf = w[2];
+    m.lut = w[3];
+    return m;
+}
+// LDS address of a kernel's dynamic shared array (expected 0).
+__device__ inline uint32_t lds_address_of(uint8_t *dyn)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)dyn;
 }
 __host__ __device__ constexpr uint32_t encode_lds_bytes(uint32_t tpb)
 {
