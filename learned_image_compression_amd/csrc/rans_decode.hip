@@ -255,7 +255,7 @@ __device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_
     wd.next = wd.at(wd.pos);
 }
 
-template <int TPB>
+template <int TPB, int CW>
 __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -300,10 +300,11 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     // the wave codes lanes j0 .. j0 + lpw - 1, one per wavefront lane
     const uint32_t lpw = dec_lanes_per_wave(L);
     const uint32_t lane = tid & (kWave - 1);
-    const uint32_t j0 = __builtin_amdgcn_readfirstlane((blockIdx.x * (TPB / kWave) + tid / kWave) * lpw);
+    const uint32_t wave = tid / kWave;   // coding waves are 0 .. CW-1
+    const uint32_t j0 = __builtin_amdgcn_readfirstlane((blockIdx.x * CW + wave) * lpw);
     const uint32_t j = j0 + lane;
     // the wave's index and symbol spans, and its stream words, as buffers
-    if (!herr && j0 < L) {
+    if (!herr && wave < CW && j0 < L) {
         const uint32_t j1 = min(j0 + lpw, L);
         const uint64_t bw = lane_begin(a.n, L, j0), ew = lane_begin(a.n, L, j1);
         const Rsrc ridx = make_rsrc(a.indexes + bw, (uint32_t)(4 * (ew - bw)));
@@ -480,17 +481,17 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     }
 }
 
-template <int TPB>
+template <int TPB, int CW>
 hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s)
 {
     const uint32_t lds_bytes = decode_lds_bytes(TPB);
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&decode_kernel<TPB>),
+        reinterpret_cast<const void *>(&decode_kernel<TPB, CW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (attr != hipSuccess)
         return attr;
-    const uint32_t blocks = (dec_waves(a.lanes) + TPB / kWave - 1) / (TPB / kWave);
-    hipLaunchKernelGGL(decode_kernel<TPB>, dim3(blocks), dim3(TPB), lds_bytes, s, a);
+    const uint32_t blocks = (dec_waves(a.lanes) + CW - 1) / CW;
+    hipLaunchKernelGGL((decode_kernel<TPB, CW>), dim3(blocks), dim3(TPB), lds_bytes, s, a);
     return hipGetLastError();
 }
 
@@ -498,9 +499,9 @@ hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s)
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
 {
-    if (coding_block_threads(dec_waves(a.lanes)) == kWave)
-        return launch_decode_t<kWave>(a, s);
-    return launch_decode_t<8 * kWave>(a, s);
+    if (coding_one_per_cu(dec_waves(a.lanes)))
+        return launch_decode_t<4 * kWave, 1>(a, s);
+    return launch_decode_t<8 * kWave, 8>(a, s);
 }
 
 }  // namespace rans

@@ -15,8 +15,8 @@
 // Mapping to gfx950: one lane of a wavefront owns one rANS lane, with its
 // 64-bit state in a VGPR pair; row metadata and per-slot (start, f) pairs are
 // staged once per workgroup into LDS; a lane spills words backwards into its
-// own scratch segment.  Waves take tickets in arrival order, publish their
-// word total, look back over earlier tickets for their offset (no grid-wide
+// own scratch segment.  Waves are numbered in block order, publish their
+// word total, look back over earlier waves for their offset (no grid-wide
 // barrier, no second launch), then write their header entries and copy
 // their lanes' words into the contiguous container.
 //
@@ -88,16 +88,14 @@ __device__ inline uint64_t reg_step(uint64_t x, uint32_t start, uint32_t f, doub
     return (q << kPrecision) + (uint32_t)r + start;
 }
 
-// Encoder tables in LDS: [meta | pairs], pair = start | f << 16.
+// Encoder tables in LDS at address 0: [meta | pairs], pair = start | f << 16.
 struct EncTables {
-    const uint8_t *lds;
-    const RowMeta *meta;
     uint32_t K;
 };
 
-__device__ inline uint32_t pair_of(const EncTables &t, const RowMeta &m, uint32_t slot)
+__device__ inline uint32_t pair_of(const EncTables &, const RowMeta &m, uint32_t slot)
 {
-    return *reinterpret_cast<const uint32_t *>(t.lds + m.base + 4 * slot);
+    return lds_load<uint32_t>(m.base + 4 * slot);
 }
 
 // Spill state of one lane.  Word k of the lane (its k-th spill) belongs at
@@ -175,7 +173,7 @@ __device__ inline uint32_t wave_inclusive_scan(uint32_t v, uint32_t lane)
     return v;
 }
 
-template <int TPB>
+template <int TPB, int CW>
 __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -193,23 +191,24 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     const uint32_t nwork = enc_waves(L);
 
     // ---- tables -> LDS -------------------------------------------------------
+    const uint32_t wave = tid / kWave;   // coding waves are 0 .. CW-1
     int herr = 0;
     if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables)
         herr = RANS_E_ARG;
     else if (!hdr->enc_ok)
         herr = RANS_E_TABLE_SIZE;
+    else if (lds_address_of(lds) != 0)   // table offsets are used as LDS addresses
+        herr = RANS_E_HIP;
     const uint32_t K = (uint32_t)a.num_tables;
     const uint32_t nbytes = herr ? 0u : hdr->enc_bytes;
     stage_tables<TPB>(lds, tab, nbytes);
     __syncthreads();
     EncTables et;
-    et.lds = lds;
-    et.meta = reinterpret_cast<const RowMeta *>(lds);
     et.K = K;
     int bad = 0;
     if (!herr)
         for (uint32_t r = tid; r < K; r += TPB)
-            bad |= (et.meta[r].lut & kRowInvalid) ? 1 : 0;
+            bad |= (lds_meta(r).lut & kRowInvalid) ? 1 : 0;
     if (tid == 0)
         misc[0] = 0u;
     __syncthreads();
@@ -219,12 +218,13 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     if (herr && blockIdx.x == 0 && tid == 0)
         record_error(hdr, herr);
 
-    if (!herr) {
-        // ---- ticket: which 64 lanes this wave codes ---------------------------
-        uint32_t t = 0;
-        if (lane == 0)
-            t = atomicAdd(&hdr->ticket, 1u);
-        t = __builtin_amdgcn_readfirstlane(__shfl(t, 0, kWave));
+    if (!herr && wave < CW) {
+        // Wave t codes lanes t*lpw ..; its look-back waits only for waves of
+        // lower-numbered blocks.  Workgroups are dispatched in index order, so
+        // those have all started and none of them waits on this one (a
+        // per-wave ticket counter would guarantee the same without relying
+        // on dispatch order, but its one contended atomic cost about 10 us).
+        const uint32_t t = blockIdx.x * CW + wave;
         if (t < nwork) {
             // the wave codes lanes j0 .. j0 + lpw - 1, one per wavefront lane
             const uint32_t j0 = t * lpw, j1 = min(j0 + lpw, L);
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
                     bool all_fast = room;
 #pragma unroll
                     for (int u = 0; u < kRound; ++u)
-                        m[u] = et.meta[min((uint32_t)idx[u], K - 1)];
+                        m[u] = lds_meta(min((uint32_t)idx[u], K - 1));
 #pragma unroll
                     for (int u = 0; u < kRound; ++u) {
                         const uint32_t mv = m[u].mvf & 0xFFFFu;
@@ -396,11 +396,13 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             if (lerr)
                 record_error(hdr, lerr);
 
-            // ---- wave scan and look-back over earlier tickets ---------------------
-            // Every wave publishes its aggregate, then reads the flags of the 64
-            // tickets before it at once (one per wavefront lane): the nearest
+            // ---- wave scan and look-back over earlier waves -----------------------
+            // Every wave publishes its aggregate, then reads the flags of the 256
+            // waves before it at once (four per wavefront lane): the nearest
             // inclusive flag ends the walk once every flag after it is
             // published, and the values up to it are summed across the wave.
+            // (Inclusive flags spread one window per round trip when many
+            // waves finish together, so the window is made wide.)
             // A flag carries all it says in its own 64 bits, so the flags are
             // relaxed device-scope atomics: no cache writeback or invalidation
             // per publication or poll (spinning waves would otherwise keep
@@ -412,18 +414,40 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
                 __hip_atomic_store(&flags[t], (t == 0 ? kFlagInclusive : kFlagAggregate) | agg,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (t > 0) {
-                int32_t k = (int32_t)t;   // this window covers tickets k-1 .. k-64
+                constexpr int kLook = 4;   // flags per lane per round trip
+                constexpr uint32_t kWindow = kLook * kWave;
+                int32_t k = (int32_t)t;   // this window covers waves k-1 .. k-kWindow
                 uint32_t spins = 0;
                 while (true) {
-                    const int32_t p = k - 1 - (int32_t)lane;
-                    const uint64_t fv = p >= 0 ? __hip_atomic_load(&flags[p], __ATOMIC_RELAXED,
-                                                                   __HIP_MEMORY_SCOPE_AGENT)
-                                               : kFlagInclusive;
-                    const uint64_t incl_mask = __ballot((fv >> 62) == 2);
-                    const uint64_t ready_mask = __ballot((fv >> 62) != 0);
-                    const uint32_t fi = incl_mask ? (uint32_t)__builtin_ctzll(incl_mask) : 64u;
-                    const uint64_t need = fi >= 63 ? ~0ull : ((2ull << fi) - 1);
-                    if ((ready_mask & need) != need) {
+                    // flag at distance d = 64 i + lane behind k
+                    uint64_t fv[kLook];
+#pragma unroll
+                    for (int i = 0; i < kLook; ++i) {
+                        const int32_t p = k - 1 - (int32_t)(kWave * i + lane);
+                        fv[i] = p >= 0 ? __hip_atomic_load(&flags[p], __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT)
+                                       : kFlagInclusive;
+                    }
+                    // the nearest inclusive flag (kWindow: none in this window)
+                    uint32_t dstar = kWindow;
+#pragma unroll
+                    for (int i = kLook - 1; i >= 0; --i) {
+                        const uint64_t im = __ballot((fv[i] >> 62) == 2);
+                        if (im)
+                            dstar = kWave * i + (uint32_t)__builtin_ctzll(im);
+                    }
+                    // every flag up to it must be published
+                    bool ready = true;
+#pragma unroll
+                    for (int i = 0; i < kLook; ++i) {
+                        const uint64_t rm = __ballot((fv[i] >> 62) != 0);
+                        const uint32_t lo = kWave * i;
+                        const uint64_t need = dstar < lo ? 0ull
+                                              : dstar >= lo + kWave - 1 ? ~0ull
+                                                                        : (2ull << (dstar - lo)) - 1;
+                        ready = ready & ((rm & need) == need);
+                    }
+                    if (!ready) {
                         if (++spins > kSpinLimit) {   // never expected: bail out, flag it
                             if (lane == 0)
                                 record_error(hdr, RANS_E_HIP);
@@ -432,13 +456,16 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
                         __builtin_amdgcn_s_sleep(1);
                         continue;
                     }
-                    uint64_t v = lane <= fi ? (fv & kFlagValueMask) : 0;
+                    uint64_t v = 0;
+#pragma unroll
+                    for (int i = 0; i < kLook; ++i)
+                        v += (kWave * i + lane <= dstar) ? (fv[i] & kFlagValueMask) : 0;
                     for (int off = 1; off < kWave; off <<= 1)
                         v += __shfl_xor(v, off, kWave);
                     prefix += v;
-                    if (fi < 64)
+                    if (dstar < kWindow)
                         break;
-                    k -= kWave;
+                    k -= (int32_t)kWindow;
                 }
                 if (lane == 0)
                     __hip_atomic_store(&flags[t], kFlagInclusive | (prefix + agg), __ATOMIC_RELAXED,
@@ -454,8 +481,10 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             // The wave's lanes fill container words [1 + L + prefix, + agg); the
             // output buffer ends at the capacity, so nothing is written past it.
             // Each lane reads back only the scratch words it stored itself,
-            // sixteen per round trip, and stores whole 16-byte groups of its
-            // own words (its last one to three words one by one).
+            // sixty-four per round trip (all loads issued before any store),
+            // and stores whole 16-byte groups of its own words, then its last
+            // one to three words one by one.  Accesses are masked per lane
+            // (a lane without words for a group sends no request).
             const uint64_t wbase = 1ull + L + __builtin_amdgcn_readfirstlane((uint32_t)prefix) +
                                    ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(prefix >> 32)) << 32);
             const uint64_t wroom = a.capacity > wbase ? a.capacity - wbase : 0;
@@ -466,23 +495,27 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
                 a.stream[1 + j] = (uint32_t)end;
                 const uint32_t ob = 4 * (incl - words);   // the lane's first word in rout
                 const uint32_t src = sp.top - 4 * words;
-                for (uint32_t k0 = 0; k0 < words; k0 += 16) {
-                    u32x4 v[4];
+                const uint32_t kt = words & ~3u;   // first word of the last, partial group
+                for (uint32_t k0 = 0; k0 < words; k0 += 64) {
+                    u32x4 v[16];
+                    uint32_t tw[3];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        v[i] = buf_load4(sp.scr, src + 4 * k0 + 16 * i);
+                    for (int i = 0; i < 16; ++i)
+                        if (k0 + 4 * i + 4 <= words)
+                            v[i] = buf_load4(sp.scr, src + 4 * k0 + 16 * i);
+                    const bool tail = kt >= k0 && kt < k0 + 64;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t k = k0 + 4 * i;
-                        if (k + 4 <= words) {
-                            buf_store4(rout, ob + 4 * k, v[i]);
-                        } else {
+                    for (int e = 0; e < 3; ++e)
+                        if (tail && kt + e < words)
+                            tw[e] = (uint32_t)buf_load(sp.scr, src + 4 * (kt + e), 0);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (k + e < words)
-                                    buf_store(rout, ob + 4 * (k + e), 0, (int32_t)v[i][e]);
-                        }
-                    }
+                    for (int i = 0; i < 16; ++i)
+                        if (k0 + 4 * i + 4 <= words)
+                            buf_store4(rout, ob + 4 * (k0 + 4 * i), v[i]);
+#pragma unroll
+                    for (int e = 0; e < 3; ++e)
+                        if (tail && kt + e < words)
+                            buf_store(rout, ob + 4 * (kt + e), 0, (int32_t)tw[e]);
                 }
             }
         }
@@ -509,7 +542,6 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             *a.status = err;
             *a.stream_words = herr ? 0ull : total;
             hdr->err = 0;
-            hdr->ticket = 0;
             hdr->total_words = 0;
             hdr->done = 0;
             __threadfence();
@@ -517,17 +549,17 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     }
 }
 
-template <int TPB>
+template <int TPB, int CW>
 hipError_t launch_encode_t(const EncodeArgs &a, hipStream_t s)
 {
     const uint32_t lds_bytes = encode_lds_bytes(TPB);
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&encode_kernel<TPB>),
+        reinterpret_cast<const void *>(&encode_kernel<TPB, CW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (attr != hipSuccess)
         return attr;
-    const uint32_t blocks = (enc_waves(a.lanes) + TPB / kWave - 1) / (TPB / kWave);
-    hipLaunchKernelGGL(encode_kernel<TPB>, dim3(blocks), dim3(TPB), lds_bytes, s, a);
+    const uint32_t blocks = (enc_waves(a.lanes) + CW - 1) / CW;
+    hipLaunchKernelGGL((encode_kernel<TPB, CW>), dim3(blocks), dim3(TPB), lds_bytes, s, a);
     return hipGetLastError();
 }
 
@@ -535,9 +567,12 @@ hipError_t launch_encode_t(const EncodeArgs &a, hipStream_t s)
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s)
 {
-    if (coding_block_threads(enc_waves(a.lanes)) == kWave)
-        return launch_encode_t<kWave>(a, s);
-    return launch_encode_t<8 * kWave>(a, s);
+    const uint32_t waves = enc_waves(a.lanes);
+    if (coding_one_per_cu(waves))
+        return launch_encode_t<4 * kWave, 1>(a, s);
+    if (waves <= 4 * kCodingCUs)
+        return launch_encode_t<4 * kWave, 4>(a, s);
+    return launch_encode_t<8 * kWave, 8>(a, s);
 }
 
 }  // namespace rans

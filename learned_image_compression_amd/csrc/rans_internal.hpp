@@ -53,7 +53,7 @@ struct WsHeader {
     // bookkeeping (self-cleaning)
     int32_t err;            // first error code of the running call, 0 if none
     uint32_t done;          // finished blocks of the running call
-    uint32_t ticket;        // next wave ticket (encode)
+    uint32_t pad2;
     uint32_t pad1;
     uint64_t total_words;   // encode: payload words (all lanes)
 };
@@ -153,12 +153,13 @@ inline __host__ __device__ uint64_t lane_begin(uint64_t n, uint32_t lanes, uint3
 
 static_assert(enc_waves(RANS_MAX_LANES) <= kMaxCodingWaves, "flag region too small");
 
-// Threads per block: one wave per block while the waves fit one per CU,
-// else eight (two per SIMD).
-inline uint32_t coding_block_threads(uint32_t waves)
-{
-    return waves <= kCodingCUs ? kWave : 8 * kWave;
-}
+// Block shapes: while the coding waves fit one per CU, a block has one coding
+// wave and three more that only help stage the tables into LDS and then wait
+// at the block's final barrier; beyond, a block has eight coding waves (two
+// per SIMD), or four for an encode of at most 1024 waves, so that every CU
+// takes a share (with 64 lanes a wave the encoder's per-lane memory requests
+// bound it, and each CU's address units add capacity).
+inline bool coding_one_per_cu(uint32_t waves) { return waves <= kCodingCUs; }
 // Dynamic LDS of a coding block: the table set, a few words of block
 // bookkeeping, then the word rings.  The kernels declare no static LDS, so
 // the dynamic area starts at LDS address 0 and a table byte offset is its LDS

@@ -97,7 +97,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
         hdr->dec_ok = dec_ok ? 1u : 0u;
         hdr->err = 0;
         hdr->done = 0;
-        hdr->ticket = 0;
         hdr->total_words = 0;
         __threadfence();
         hdr->magic = kMagic;
