@@ -306,83 +306,112 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
                     }
                     sp.cb0 = sp.cb;
                 };
-                // One round of positions k0 .. k0+7 (last to first).
-                auto round = [&](int32_t (&sym)[kRound], int32_t (&idx)[kRound], uint32_t k0) {
-                    RowMeta m[kRound];
+                // State-independent values of one round (positions k0 .. k0+7,
+                // last to first): the slot's (start, f), the reciprocal of f,
+                // whether the position holds an ordinary symbol of a valid row,
+                // and the round's symbols and indexes for the general puts.
+                struct Pre {
                     uint32_t start[kRound], f[kRound];
                     double rcp[kRound];
+                    int32_t sym[kRound], idx[kRound];
                     bool fast[kRound];
-                    // room for three words per position: the fast steps need no check
-                    const bool room = sp.cb + 4 * (2 + 3 * kRound) < sp.capb;
-                    bool all_fast = room;
-#pragma unroll
-                    for (int u = 0; u < kRound; ++u)
-                        m[u] = lds_meta(min((uint32_t)idx[u], K - 1));
+                    bool all;   // every position of this lane is fast
+                };
+                auto pre = [&](const int32_t (&sym)[kRound], const int32_t (&idx)[kRound], uint32_t k0,
+                               Pre &P) {
+                    P.all = true;
 #pragma unroll
                     for (int u = 0; u < kRound; ++u) {
-                        const uint32_t mv = m[u].mvf & 0xFFFFu;
+                        const RowMeta m = lds_meta(min((uint32_t)idx[u], K - 1));
+                        const uint32_t mv = m.mvf & 0xFFFFu;
                         // s - offset wraps mod 2^32 into [0, mv) only on rows whose
                         // fast bound is 0
-                        const uint32_t w = (uint32_t)sym[u] - (uint32_t)m[u].offset;
-                        fast[u] = room & (w < (m[u].mvf >> 16)) & ((uint32_t)idx[u] < K) &
-                                  (k0 + u < nj);
-                        all_fast = all_fast & fast[u];
-                        const uint32_t pr = pair_of(et, m[u], min(w, mv));
-                        start[u] = pr & 0xFFFFu;
-                        f[u] = pr >> 16;
-                        rcp[u] = reciprocal(f[u]);
+                        const uint32_t w = (uint32_t)sym[u] - (uint32_t)m.offset;
+                        P.fast[u] = (w < (m.mvf >> 16)) & ((uint32_t)idx[u] < K) & (k0 + u < nj);
+                        P.all = P.all & P.fast[u];
+                        const uint32_t pr = pair_of(et, m, min(w, mv));
+                        P.start[u] = pr & 0xFFFFu;
+                        P.f[u] = pr >> 16;
+                        P.rcp[u] = reciprocal(P.f[u]);
+                        P.sym[u] = sym[u];
+                        P.idx[u] = idx[u];
                     }
-                    if (__all(all_fast)) {
-                        // the state chain: no branch, no LDS access
+                };
+                // One round of positions k0 .. k0+7 on P, with the next round's
+                // state-independent work (from sym/idx into Pn) in the same
+                // straight-line block, where it fills the chain's latency.  The
+                // chain assumes every position fast; a round where that is not so
+                // for some lane (an escape, a bad index, a lane end, a lane near
+                // the end of its segment) is redone from its start state with
+                // the general puts.
+                auto round = [&](const Pre &P, uint32_t k0, int32_t (&sym)[kRound],
+                                 int32_t (&idx)[kRound], Pre &Pn) {
+                    // room for three words per position: the fast steps need no check
+                    const bool room = sp.cb + 4 * (2 + 3 * kRound) < sp.capb;
+                    const uint64_t x0 = x;
+                    const uint32_t cb_start = sp.cb;
+                    pre(sym, idx, k0 + kRound, Pn);
 #pragma unroll
-                        for (int u = 0; u < kRound; ++u) {
-                            const bool need = (uint32_t)(x >> 32) >= (f[u] << (31 - kPrecision));
-                            *sp.slot((sp.cb - sp.cb0) >> 2) = (uint32_t)x;
-                            sp.cb += need ? 4u : 0u;
-                            x = need ? (x >> 32) : x;
-                            x = reg_step(x, start[u], f[u], rcp[u]);
-                        }
-                    } else {
+                    for (int u = 0; u < kRound; ++u) {
+                        const bool need = (uint32_t)(x >> 32) >= (P.f[u] << (31 - kPrecision));
+                        *sp.slot((sp.cb - sp.cb0) >> 2) = (uint32_t)x;
+                        sp.cb += need ? 4u : 0u;
+                        x = need ? (x >> 32) : x;
+                        x = reg_step(x, P.start[u], P.f[u], P.rcp[u]);
+                    }
+                    if (__builtin_expect(!__all(P.all & room), 0)) {
+                        x = x0;
+                        sp.cb = cb_start;
                         // the fast step is committed where it applies; the other
                         // lanes take the slow puts
 #pragma unroll
                         for (int u = 0; u < kRound; ++u) {
-                            const bool need = (uint32_t)(x >> 32) >= (f[u] << (31 - kPrecision));
+                            const bool fast = P.fast[u] & room;
+                            const bool need = (uint32_t)(x >> 32) >= (P.f[u] << (31 - kPrecision));
                             const uint64_t xn =
-                                reg_step(need ? (x >> 32) : x, start[u], f[u], rcp[u]);
+                                reg_step(need ? (x >> 32) : x, P.start[u], P.f[u], P.rcp[u]);
                             *sp.slot(min((sp.cb - sp.cb0) >> 2, kEncRing - 1)) = (uint32_t)x;
-                            sp.cb += (fast[u] & need) ? 4u : 0u;
-                            x = fast[u] ? xn : x;
-                            const bool slow = !fast[u] & (k0 + u < nj);
+                            sp.cb += (fast & need) ? 4u : 0u;
+                            x = fast ? xn : x;
+                            const bool slow = !fast & (k0 + u < nj);
                             if (__builtin_expect(__ballot(slow) != 0, 0)) {
                                 if (slow) {
                                     int ec = RANS_E_INDEX;
-                                    if ((uint32_t)idx[u] < K)
-                                        ec = encode_slow<TPB>(sym[u], m[u], et, x, sp);
+                                    if ((uint32_t)P.idx[u] < K)
+                                        ec = encode_slow<TPB>(P.sym[u], lds_meta(P.idx[u]), et, x,
+                                                              sp);
                                     lerr = lerr ? lerr : ec;
                                 }
                             }
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    // ---- memory phase ----
+                    // ---- memory phase: this round's words, the symbols and
+                    // indexes of the round three ahead into the buffer just used
                     store_words();
                     __builtin_amdgcn_sched_barrier(0);
-                    load_next(sym, idx, k0 + 2 * kRound);
+                    load_next(sym, idx, k0 + 3 * kRound);
                 };
-                // prologue: two phases of the same shape (their stores carry
-                // stale ring words to positions that later words overwrite)
+                // prologue: three phases of the same shape (their stores carry
+                // stale ring words to positions that later words overwrite);
+                // rounds 0 and 1 are loaded, round 0 prepared, round 2 loaded
+                Pre pa, pb;
                 store_words();
                 __builtin_amdgcn_sched_barrier(0);
                 load_next(sa, ia, 0);
                 store_words();
                 __builtin_amdgcn_sched_barrier(0);
                 load_next(sb, ib, kRound);
+                pre(sa, ia, 0, pa);
+                __builtin_amdgcn_sched_barrier(0);
+                store_words();
+                __builtin_amdgcn_sched_barrier(0);
+                load_next(sa, ia, 2 * kRound);
                 // both rounds always run (positions past the lane are skipped
                 // inside), so every path back to the loop head passes both phases
                 for (uint32_t k0 = 0; k0 < nj; k0 += 2 * kRound) {
-                    round(sa, ia, k0);
-                    round(sb, ib, k0 + kRound);
+                    round(pa, k0, sb, ib, pb);
+                    round(pb, k0 + kRound, sa, ia, pa);
                 }
                 if (sp.overflow) {
                     lerr = lerr ? lerr : RANS_E_CAPACITY;
