@@ -217,6 +217,46 @@ def test_prepared_tables_code_many_tensors():
         assert np.array_equal(out.cpu().numpy(), w.symbols[lo:hi])
 
 
+def test_full_and_prepared_calls_share_a_workspace():
+    """The *_with_indexes entry points leave their tables prepared in the
+    workspace for later *_prepared calls, and a stand-alone preparation of
+    other tables is replaced by the next full call.  Two table sets of
+    different row counts and widths alternate on one workspace."""
+    import torch
+    import gpu_util as G
+    B = G.B
+    wt, tt, st_sym, st_idx = _workload("tiny")
+    tiny = (wt, tt, st_sym, st_idx)
+    wz = W.load("z")
+    tz = G.tables_of(wz)
+    z = (wz, tz, G.to_dev(wz.symbols), G.to_dev(wz.indexes))
+    nbytes = max(B.workspace_bytes(w.n, 256, t.num_tables, t.stride) for w, t, _, _ in (tiny, z))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=G.DEV)
+    refs = {}
+    for w, t, _, _ in (tiny, z):
+        rc, refs[w.name] = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, 256)
+        assert rc == 0
+    for step, (w, t, sym, idx), prepared in (
+            (0, tiny, False), (1, tiny, True), (2, z, False), (3, z, True), (4, tiny, False),
+            (5, z, False), (6, z, True)):
+        G.say(f"[shared-ws] step {step}: {w.name} prepared={prepared}")
+        stream, nwords, status = B.encode_with_indexes(sym, idx, t, 256, workspace=ws,
+                                                       prepared=prepared)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        got = stream[: int(nwords.item())].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, refs[w.name])
+        out, status = B.decode_with_indexes(stream, idx, t, 256, workspace=ws, prepared=prepared)
+        assert int(status.item()) == 0
+        assert np.array_equal(out.cpu().numpy(), w.symbols)
+    G.say("[shared-ws] stand-alone preparation replaced by the next full call")
+    B.prepare_tables(tiny[1], ws)
+    stream, nwords, status = B.encode_with_indexes(z[2], z[3], tz, 256, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(stream[: int(nwords.item())].cpu().numpy().view(np.uint32), refs["z"])
+
+
 # ------------------------------------------------------------------- errors
 def test_bad_index_reports_status():
     import gpu_util as G
