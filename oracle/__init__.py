@@ -29,7 +29,7 @@ def build(source: str = SOURCE, out: str = LIBRARY, extra_flags=()) -> str:
     """Compile the oracle with the host C compiler (no GPU involved)."""
     tmp = f"{out}.tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-Werror", "-shared", "-fPIC",
-           *extra_flags, source, "-o", tmp]
+           *extra_flags, source, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -55,6 +55,14 @@ def _bind(lib):
     lib.oracle_encode.restype = ctypes.c_int
     lib.oracle_decode.argtypes = [u32p, u64, i32p, u64, i32p, i32p, i32p, i32, i32, u32, i32p]
     lib.oracle_decode.restype = ctypes.c_int
+    f64p = ctypes.POINTER(ctypes.c_double)
+    f64 = ctypes.c_double
+    lib.oracle_quantize_pmf.argtypes = [f64p, i32, i32p]
+    lib.oracle_quantize_pmf.restype = ctypes.c_int
+    lib.oracle_gaussian_row.argtypes = [f64, f64, i32, i32p, i32p, i32p]
+    lib.oracle_gaussian_row.restype = ctypes.c_int
+    lib.oracle_gaussian_tables.argtypes = [f64p, i32, f64, i32, i32p, i32p, i32p]
+    lib.oracle_gaussian_tables.restype = ctypes.c_int
     return lib
 
 
@@ -163,3 +171,26 @@ def decode_lane(lane_words, indexes, begin, end, cdf, lengths, offsets, lib=None
                                 _ptr(offsets, ctypes.c_int32), cdf.shape[0], cdf.shape[1],
                                 _ptr(out, ctypes.c_int32))
     return int(rc), out[begin:end].copy()
+
+
+def quantize_pmf(pmf, lib=None):
+    """Return (status, cdf) for one pmf row (alphabet then escape slot)."""
+    lib = lib or load()
+    pmf = np.ascontiguousarray(pmf, dtype=np.float64)
+    cdf = np.zeros(pmf.size + 1, dtype=np.int32)
+    rc = lib.oracle_quantize_pmf(_ptr(pmf, ctypes.c_double), pmf.size, _ptr(cdf, ctypes.c_int32))
+    return int(rc), cdf
+
+
+def gaussian_tables(scales, tail_z: float, stride: int, lib=None):
+    """Return (status, cdf [K, stride], lengths [K], offsets [K]) for one row per scale."""
+    lib = lib or load()
+    scales = np.ascontiguousarray(scales, dtype=np.float64)
+    K = scales.size
+    cdf = np.zeros((K, stride), dtype=np.int32)
+    lengths = np.zeros(K, dtype=np.int32)
+    offsets = np.zeros(K, dtype=np.int32)
+    rc = lib.oracle_gaussian_tables(_ptr(scales, ctypes.c_double), K, float(tail_z), stride,
+                                    _ptr(cdf, ctypes.c_int32), _ptr(lengths, ctypes.c_int32),
+                                    _ptr(offsets, ctypes.c_int32))
+    return int(rc), cdf, lengths, offsets

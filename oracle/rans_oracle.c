@@ -19,7 +19,7 @@
  *     symbol by a linear scan of the CDF row (std::find_if) -- this oracle
  *     does exactly that, the plainest lookup there is.
  *
- * Readings taken where the pages are silent (each listed again in DESIGN):
+ * Readings taken where the pages are silent:
  *   R1  state interval [L0, 2^63) with L0 = 2^31, the interval of 64-bit
  *       ryg_rans with 32-bit output; with 16-bit precision a REG put
  *       renormalises when x >= f * 2^47 and a 4-bit put when x >= 2^59;
@@ -41,6 +41,7 @@
  */
 #include "rans_oracle.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -385,6 +386,122 @@ int oracle_decode(const uint32_t *stream, uint64_t stream_words,
         if (rc)
             return rc;
         prev = endj;
+    }
+    return ORACLE_OK;
+}
+
+/* ---- Quantised CDF tables ------------------------------------------------
+ *
+ * What the pages fix: the coder consumes 16-bit quantised CDF rows, one per
+ * distribution, each holding the alphabet, an escape slot for bypass coding
+ * and the terminal entry (torch_ans 0.3.0, "Range limit" under rans*_push);
+ * the coder itself turns batched pmfs into such rows ("Parameter Setup" and
+ * "Other Features": init_params converts PMF to CDF internally), and the
+ * mean-scale model's y latent uses 64 rows of at most 3133 entries
+ * (kompressor BENCHMARKS.md, section 4: 200,512 marshalled cdf entries).
+ * The quantisation procedure and the discretised Gaussian are readings:
+ *   T1  pmf entry k becomes f_k = max(1, round-half-even(p_k * 2^16)), the
+ *       escape slot being the last entry of the pmf row;
+ *   T2  the frequencies are then brought to a sum of exactly 2^16 one unit
+ *       at a time, each unit taken from (surplus) or given to (deficit) the
+ *       currently largest frequency, the lowest slot among equals; a
+ *       frequency never drops below 1 (possible whenever the row has at most
+ *       2^16 entries);
+ *   T3  the Gaussian row of scale s: half-width c = ceil(s * z) for a given
+ *       standard-normal quantile z (z = 6.1094... for a two-sided tail mass
+ *       of 1e-9); slot k = 0..2c holds symbol v = k - c with mass
+ *       Phi((v + 1/2) / s) - Phi((v - 1/2) / s); the escape slot holds the
+ *       mass of both tails beyond c + 1/2, 2 Phi(-(c + 1/2) / s); offset -c,
+ *       length 2c + 3, entries past the length set to 2^16;
+ *   T4  Phi(x) = erfc(-x / sqrt(2)) / 2, all of it in double precision.
+ */
+
+static double std_normal_cdf(double x)
+{
+    return 0.5 * erfc(-x * 0.70710678118654752440);
+}
+
+int oracle_quantize_pmf(const double *pmf, int32_t m, int32_t *cdf)
+{
+    if (!pmf || !cdf || m < 2 || m > (int32_t)TOTAL_FREQ)
+        return ORACLE_E_ARG;
+    int64_t *f = (int64_t *)malloc((size_t)m * sizeof(int64_t));
+    if (!f)
+        return ORACLE_E_ARG;
+    int64_t sum = 0;
+    for (int32_t k = 0; k < m; ++k) {
+        double p = pmf[k];
+        if (!(p >= 0.0 && p <= 1.0)) {   /* also refuses NaN */
+            free(f);
+            return ORACLE_E_TABLE;
+        }
+        f[k] = (int64_t)rint(p * TOTAL_FREQ);   /* default rounding: half to even */
+        if (f[k] < 1)
+            f[k] = 1;
+        sum += f[k];
+    }
+    int64_t excess = sum - (int64_t)TOTAL_FREQ;
+    while (excess != 0) {
+        int32_t top = 0;   /* the first slot of the largest frequency */
+        for (int32_t k = 1; k < m; ++k)
+            if (f[k] > f[top])
+                top = k;
+        if (excess > 0) {
+            f[top] -= 1;   /* f[top] >= 2 here: sum > 2^16 >= m */
+            excess -= 1;
+        } else {
+            f[top] += 1;
+            excess += 1;
+        }
+    }
+    cdf[0] = 0;
+    for (int32_t k = 0; k < m; ++k)
+        cdf[k + 1] = cdf[k] + (int32_t)f[k];
+    free(f);
+    return ORACLE_OK;
+}
+
+int oracle_gaussian_row(double scale, double tail_z, int32_t stride, int32_t *cdf_row,
+                        int32_t *length, int32_t *offset)
+{
+    if (!cdf_row || !length || !offset || stride < 3)
+        return ORACLE_E_ARG;
+    if (!(scale > 0.0) || !(tail_z > 0.0))
+        return ORACLE_E_TABLE;
+    double cw = ceil(scale * tail_z);
+    if (!(2.0 * cw + 3.0 <= (double)stride))
+        return ORACLE_E_TABLE;
+    int32_t c = (int32_t)cw;
+    int32_t m = 2 * c + 2;   /* 2c + 1 symbols and the escape slot */
+    double *pmf = (double *)malloc((size_t)m * sizeof(double));
+    if (!pmf)
+        return ORACLE_E_ARG;
+    for (int32_t k = 0; k <= 2 * c; ++k) {
+        double v = (double)(k - c);
+        pmf[k] = std_normal_cdf((v + 0.5) / scale) - std_normal_cdf((v - 0.5) / scale);
+    }
+    pmf[m - 1] = 2.0 * std_normal_cdf(-((double)c + 0.5) / scale);
+    int rc = oracle_quantize_pmf(pmf, m, cdf_row);
+    free(pmf);
+    if (rc)
+        return rc;
+    for (int32_t k = m + 1; k < stride; ++k)
+        cdf_row[k] = (int32_t)TOTAL_FREQ;
+    *length = m + 1;
+    *offset = -c;
+    return ORACLE_OK;
+}
+
+int oracle_gaussian_tables(const double *scales, int32_t num_tables, double tail_z,
+                           int32_t stride, int32_t *cdf, int32_t *lengths, int32_t *offsets)
+{
+    if (!scales || num_tables <= 0)
+        return ORACLE_E_ARG;
+    for (int32_t r = 0; r < num_tables; ++r) {
+        int rc = oracle_gaussian_row(scales[r], tail_z, stride, cdf + (int64_t)r * stride,
+                                     lengths + r, offsets + r);
+        if (rc)
+            return rc;
     }
     return ORACLE_OK;
 }

@@ -84,6 +84,22 @@ int oracle_decode(const uint32_t *stream, uint64_t stream_words,
                   int32_t num_tables, int32_t stride, uint32_t num_lanes,
                   int32_t *symbols_out);
 
+/* Quantise one pmf row of m entries (alphabet, then the escape slot) to a
+ * 16-bit CDF of m + 1 entries: cdf[0] = 0, cdf[m] = 65536.  ORACLE_E_TABLE
+ * for an entry outside [0, 1] or NaN; ORACLE_E_ARG for m outside [2, 65536]. */
+int oracle_quantize_pmf(const double *pmf, int32_t m, int32_t *cdf);
+
+/* One discretised zero-mean Gaussian row of the given scale, half-width
+ * ceil(scale * tail_z), written over `stride` entries (padding 65536).
+ * ORACLE_E_TABLE when the scale or tail_z is not positive or the row needs
+ * more than `stride` entries. */
+int oracle_gaussian_row(double scale, double tail_z, int32_t stride, int32_t *cdf_row,
+                        int32_t *length, int32_t *offset);
+
+/* One row per scale: cdf [num_tables][stride], lengths and offsets [num_tables]. */
+int oracle_gaussian_tables(const double *scales, int32_t num_tables, double tail_z,
+                           int32_t stride, int32_t *cdf, int32_t *lengths, int32_t *offsets);
+
 #ifdef __cplusplus
 }
 #endif

@@ -75,3 +75,74 @@ def lane_words_from_container(words, lanes):
     ends = [0] + [int(e) for e in words[1:1 + lanes]]
     body = words[1 + lanes:]
     return [np.asarray(body[ends[j]:ends[j + 1]]) for j in range(lanes)]
+
+
+# --------------------------------------------------------------- tables
+def quantized_cases():
+    """Cases of golden/quantized_cdfs.txt as (name, pmf float64 array, cdf list)."""
+    def num(tok):
+        if "/" in tok:
+            a, b = tok.split("/")
+            return float(a) / float(b)
+        return float(tok)
+    cases = []
+    with open(os.path.join(GOLDEN, "quantized_cdfs.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line.startswith("case "):
+                continue
+            name, pmf, cdf = [f.strip() for f in line[5:].split("|")]
+            cases.append((name, np.array([num(t) for t in pmf.split()], dtype=np.float64),
+                          [int(t) for t in cdf.split()]))
+    return cases
+
+
+def quantize_water_level(p):
+    """16-bit frequencies of a pmf row by the closed form of the unit-by-unit
+    adjustment: a surplus E lowers every frequency above the level T to T,
+    T the smallest level whose removal sum(max(0, f - T)) is at most E, and
+    the remaining units come one each from the lowest slots at T; a deficit
+    goes entirely to the first largest slot (it stays the largest)."""
+    f = np.maximum(np.rint(np.asarray(p, dtype=np.float64) * 65536.0), 1).astype(np.int64)
+    excess = int(f.sum()) - 65536
+    if excess < 0:
+        f[int(np.argmax(f))] -= excess
+    elif excess > 0:
+        lo, hi = 1, int(f.max())
+        while lo < hi:
+            mid = (lo + hi) // 2
+            if int(np.maximum(f - mid, 0).sum()) <= excess:
+                hi = mid
+            else:
+                lo = mid + 1
+        T = lo
+        rest = excess - int(np.maximum(f - T, 0).sum())
+        top = np.flatnonzero(f >= T)
+        f[top] = T
+        f[top[:rest]] -= 1
+    return f
+
+
+def normal_mass(a, b, per_unit=2000):
+    """Standard-normal mass of [a, b] by composite Simpson's rule on the
+    density (independent of any erf/erfc routine)."""
+    n = max(64, int(math.ceil((b - a) * per_unit)))
+    n += n & 1
+    x = np.linspace(a, b, n + 1)
+    y = np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+    h = (b - a) / n
+    return float(h / 3.0 * (y[0] + y[-1] + 4.0 * y[1:-1:2].sum() + 2.0 * y[2:-1:2].sum()))
+
+
+def gaussian_row_by_integration(scale, tail_z):
+    """(cdf list, offset, smallest distance of p * 65536 to a half-integer) of
+    the discretised Gaussian row, from Simpson masses of each bin and of both
+    tails (the tails integrated out to 40 standard deviations)."""
+    c = int(math.ceil(scale * tail_z))
+    p = [normal_mass((v - 0.5) / scale, (v + 0.5) / scale) for v in range(-c, c + 1)]
+    edge = (c + 0.5) / scale
+    p.append(2.0 * normal_mass(edge, max(edge, 0.0) + 40.0))
+    p = np.array(p)
+    frac = np.abs(np.mod(p * 65536.0, 1.0) - 0.5)
+    f = quantize_water_level(p)
+    return [0] + np.cumsum(f).tolist(), -c, float(frac.min())

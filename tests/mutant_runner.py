@@ -17,7 +17,45 @@ import numpy as np  # noqa: E402
 import oracle  # noqa: E402
 from oracle import spec_model as sm  # noqa: E402
 import workloads as W  # noqa: E402
-from helpers import lane_information, lane_words_from_container, single_table, worked_cases  # noqa: E402
+from helpers import (gaussian_row_by_integration, lane_information,  # noqa: E402
+                     lane_words_from_container, quantize_water_level, quantized_cases,
+                     single_table, worked_cases)
+
+
+def table_pins(lib):
+    from scipy.special import ndtri
+    tail_z = float(ndtri(1.0 - 5e-10))
+    failures = []
+    for name, pmf, cdf in quantized_cases():
+        rc, got = oracle.quantize_pmf(pmf, lib=lib)
+        if rc != 0 or got.tolist() != cdf:
+            failures.append(f"golden quantisation {name}")
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        m = int(rng.integers(2, 12))
+        p = rng.dirichlet(np.ones(m)) * rng.uniform(0.5, 2.0)
+        p = np.minimum(p, 1.0)
+        rc, got = oracle.quantize_pmf(p, lib=lib)
+        if rc != 0 or not np.array_equal(np.diff(got.astype(np.int64)), quantize_water_level(p)):
+            failures.append(f"closed-form quantisation trial {trial}")
+            break
+    for K, z in ((8, tail_z), (12, 1.0)):
+        scales = np.exp(np.log(0.11) + (np.log(256.0) - np.log(0.11)) * np.arange(K) / (K - 1))
+        stride = 2 * int(np.ceil(scales[-1] * z)) + 3
+        rc, cdf, lengths, offsets = oracle.gaussian_tables(scales, z, stride, lib=lib)
+        if rc != 0:
+            failures.append(f"gaussian K={K} rc={rc}")
+            continue
+        for r, s in enumerate(scales):
+            ref, off, _ = gaussian_row_by_integration(float(s), z)
+            n = int(lengths[r])
+            if (n != len(ref) or int(offsets[r]) != off or cdf[r, :n].tolist() != ref
+                    or np.any(cdf[r, n:] != 65536)):
+                failures.append(f"gaussian K={K} row {r}")
+                break
+    if oracle.gaussian_tables(np.array([2.0]), tail_z, 28, lib=lib)[0] != oracle.E_TABLE:
+        failures.append("gaussian row longer than the stride accepted")
+    return failures
 
 
 def pins(lib):
@@ -74,6 +112,6 @@ def pins(lib):
 
 if __name__ == "__main__":
     lib = oracle.load(sys.argv[1])
-    f = pins(lib)
+    f = pins(lib) + table_pins(lib)
     print("\n".join(f) if f else "all pins hold")
     sys.exit(1 if f else 0)

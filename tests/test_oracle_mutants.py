@@ -47,6 +47,20 @@ MUTANTS = {
     "dec_state_shift": ("d.x = (uint64_t)freq * (d.x >> PREC) + cum - start;",
                         "d.x = (uint64_t)freq * (d.x >> (PREC - 1)) + cum - start;"),
     "end_check": ("if (d.x != STATE_LOW || d.pos != d.words)", "if (d.x != STATE_LOW)"),
+    # table builder
+    "q_round_half_up": ("f[k] = (int64_t)rint(p * TOTAL_FREQ);",
+                        "f[k] = (int64_t)floor(p * TOTAL_FREQ + 0.5);"),
+    "q_no_floor_one": ("if (f[k] < 1)\n            f[k] = 1;", "if (f[k] < 0)\n            f[k] = 0;"),
+    "q_tie_highest": ("if (f[k] > f[top])", "if (f[k] >= f[top])"),
+    "q_deficit_first_slot": ("f[top] += 1;", "f[0] += 1;"),
+    "g_bin_edges": ("std_normal_cdf((v + 0.5) / scale) - std_normal_cdf((v - 0.5) / scale)",
+                    "std_normal_cdf((v + 1.0) / scale) - std_normal_cdf(v / scale)"),
+    "g_one_tail": ("pmf[m - 1] = 2.0 * std_normal_cdf(", "pmf[m - 1] = 1.0 * std_normal_cdf("),
+    "g_half_width_floor": ("double cw = ceil(scale * tail_z);",
+                           "double cw = floor(scale * tail_z);"),
+    "g_offset_sign": ("*offset = -c;", "*offset = c;"),
+    "g_padding": ("cdf_row[k] = (int32_t)TOTAL_FREQ;", "cdf_row[k] = 0;"),
+    "g_root_two": ("-x * 0.70710678118654752440", "-x * 1.41421356237309504880"),
 }
 
 
@@ -57,7 +71,7 @@ def _build(tmp_path, name, text):
     inc = os.path.dirname(oracle.SOURCE)
     out = str(tmp_path / f"lib{name}.so")
     subprocess.run(["gcc", "-O1", "-std=c99", "-shared", "-fPIC", f"-I{inc}", str(src), "-o",
-                    out], check=True)
+                    out, "-lm"], check=True)
     return out
 
 
