@@ -130,6 +130,47 @@ int rans_decode_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
                          int32_t *status, void *workspace, uint64_t workspace_bytes,
                          hipStream_t hstream);
 
+/* Quantised CDF rows built on the device, one row per table (the step
+ * before coding: torch_ans 0.3.0, "Parameter Setup" and "Other Features",
+ * the coder turns batched pmfs into 16-bit CDFs itself; "Performance
+ * Tuning", item 6, that rebuild costs about 0.2 ms on CUDA).
+ *
+ * Quantisation of a pmf row of m entries (alphabet, then the escape slot):
+ * f_k = max(1, round-half-even(p_k * 65536)), then the sum is brought to
+ * 65536 as if one unit at a time were taken from (surplus) or given to
+ * (deficit) the currently largest f_k, the lowest slot among equals.  The
+ * row's CDF is [0, f_0, f_0 + f_1, ..., 65536] (m + 1 entries), and the
+ * entries from m + 1 to cdf_stride - 1 are set to 65536.
+ *
+ * rans_gaussian_tables: row r is the zero-mean Gaussian of scale scales[r]
+ * (double) discretised on integer bins: half-width c = ceil(scale * tail_z),
+ * tail_z the standard-normal quantile of 1 - tail_mass / 2 (6.1094 for a
+ * tail mass of 1e-9); slot k = 0..2c has mass Phi((k - c + 1/2) / scale) -
+ * Phi((k - c - 1/2) / scale), the escape slot the two tails
+ * 2 Phi(-(c + 1/2) / scale), all in double precision with
+ * Phi(x) = erfc(-x / sqrt 2) / 2.  Outputs cdf [num_tables][cdf_stride],
+ * cdf_lengths = 2c + 3 and offsets = -c, ready for the coding calls.
+ *
+ * rans_quantize_pmfs: row r quantises pmf[r][0 .. pmf_lengths[r]) (double,
+ * row pitch pmf_stride entries, no normalisation: a sum other than 1 is
+ * absorbed by the adjustment above); cdf_lengths[r] = pmf_lengths[r] + 1.
+ *
+ * Every pointer is a device pointer; one workgroup per row.  row_status[r]
+ * (device, num_tables entries) receives RANS_OK, or RANS_E_TABLE when the
+ * row cannot be built (scale not positive or NaN, row longer than
+ * cdf_stride, pmf length outside [2, min(pmf_stride, cdf_stride - 1)], a
+ * pmf entry outside [0, 1] or NaN); such a row's cdf_lengths[r] is 0 and
+ * its cdf entries are unspecified.  The return value reports bad sizes or
+ * pointers (RANS_E_ARG; tail_z must be positive and finite) and launch
+ * failures (RANS_E_HIP). */
+int rans_gaussian_tables(const double *scales, int32_t num_tables, double tail_z,
+                         int32_t cdf_stride, int32_t *cdf, int32_t *cdf_lengths, int32_t *offsets,
+                         int32_t *row_status, hipStream_t hstream);
+
+int rans_quantize_pmfs(const double *pmf, const int32_t *pmf_lengths, int32_t num_tables,
+                       int32_t pmf_stride, int32_t cdf_stride, int32_t *cdf, int32_t *cdf_lengths,
+                       int32_t *row_status, hipStream_t hstream);
+
 /* Static text for a status code. */
 const char *rans_status_string(int code);
 

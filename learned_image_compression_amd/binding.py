@@ -38,6 +38,8 @@ EXPORTS = (
     "rans_prepare_tables",
     "rans_encode_prepared",
     "rans_decode_prepared",
+    "rans_gaussian_tables",
+    "rans_quantize_pmfs",
     "rans_status_string",
 )
 
@@ -90,6 +92,11 @@ def load(path: str | None = None):
         lib.rans_encode_prepared.restype = ctypes.c_int
         lib.rans_decode_prepared.argtypes = [vp, u64, vp, u64, i32, i32, u32, vp, vp, vp, u64, vp]
         lib.rans_decode_prepared.restype = ctypes.c_int
+        f64 = ctypes.c_double
+        lib.rans_gaussian_tables.argtypes = [vp, i32, f64, i32, vp, vp, vp, vp, vp]
+        lib.rans_gaussian_tables.restype = ctypes.c_int
+        lib.rans_quantize_pmfs.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
+        lib.rans_quantize_pmfs.restype = ctypes.c_int
         lib.rans_status_string.argtypes = [ctypes.c_int]
         lib.rans_status_string.restype = ctypes.c_char_p
         if path is None:
@@ -270,3 +277,50 @@ def check(status: torch.Tensor, where: str = "device"):
     code = int(status.item())
     if code != 0:
         raise RansError(code, where)
+
+
+def gaussian_tables(scales: torch.Tensor, tail_z: float, cdf_stride: int):
+    """Enqueue the build of one discretised Gaussian CDF row per scale.
+
+    ``scales`` is a float64 device tensor [K]; returns (Tables, row_status
+    int32 [K]).  Nothing is synchronised: a row whose status is non-zero was
+    not built (``check_rows(row_status)``).
+    """
+    device = scales.device
+    _need(scales, torch.float64, device, "scales")
+    K = scales.numel()
+    cdf = torch.empty((K, cdf_stride), dtype=torch.int32, device=device)
+    lengths = torch.empty(K, dtype=torch.int32, device=device)
+    offsets = torch.empty(K, dtype=torch.int32, device=device)
+    status = torch.empty(K, dtype=torch.int32, device=device)
+    rc = load().rans_gaussian_tables(_ptr(scales), K, float(tail_z), cdf_stride, _ptr(cdf),
+                                     _ptr(lengths), _ptr(offsets), _ptr(status), _stream(device))
+    _check_rc(rc, "rans_gaussian_tables")
+    return Tables(cdf, lengths, offsets), status
+
+
+def quantize_pmfs(pmf: torch.Tensor, pmf_lengths: torch.Tensor, cdf_stride: int):
+    """Enqueue the 16-bit quantisation of pmf rows (float64 [K, S], alphabet then
+    escape slot; int32 lengths [K]); returns (cdf [K, cdf_stride], cdf_lengths [K],
+    row_status [K])."""
+    device = pmf.device
+    _need(pmf, torch.float64, device, "pmf")
+    _need(pmf_lengths, torch.int32, device, "pmf_lengths")
+    if pmf.dim() != 2 or pmf_lengths.numel() != pmf.shape[0]:
+        raise ValueError("pmf must be [K, S] with K lengths")
+    K = pmf.shape[0]
+    cdf = torch.empty((K, cdf_stride), dtype=torch.int32, device=device)
+    lengths = torch.empty(K, dtype=torch.int32, device=device)
+    status = torch.empty(K, dtype=torch.int32, device=device)
+    rc = load().rans_quantize_pmfs(_ptr(pmf), _ptr(pmf_lengths), K, pmf.shape[1], cdf_stride,
+                                   _ptr(cdf), _ptr(lengths), _ptr(status), _stream(device))
+    _check_rc(rc, "rans_quantize_pmfs")
+    return cdf, lengths, status
+
+
+def check_rows(row_status: torch.Tensor, where: str = "table build"):
+    """Synchronise on per-row statuses and raise RansError for the first failed row."""
+    st = row_status.cpu()
+    bad = torch.nonzero(st).flatten()
+    if bad.numel():
+        raise RansError(int(st[bad[0]]), f"{where}: row {int(bad[0])}")

@@ -159,6 +159,34 @@ int rans_decode_with_indexes(const uint32_t *stream, uint64_t stream_capacity_wo
                                 workspace_bytes, hstream);
 }
 
+int rans_gaussian_tables(const double *scales, int32_t num_tables, double tail_z,
+                         int32_t cdf_stride, int32_t *cdf, int32_t *cdf_lengths, int32_t *offsets,
+                         int32_t *row_status, hipStream_t hstream)
+{
+    if (!scales || !cdf || !cdf_lengths || !offsets || !row_status)
+        return RANS_E_ARG;
+    if (num_tables < 1 || num_tables > RANS_MAX_TABLES || cdf_stride < 3 ||
+        cdf_stride > RANS_MAX_STRIDE || !(tail_z > 0.0 && tail_z < 1e300))
+        return RANS_E_ARG;
+    TableArgs a{scales, tail_z, nullptr, nullptr, 0, num_tables, cdf_stride, cdf, cdf_lengths,
+                offsets, row_status};
+    return launched(launch_table_rows(a, hstream));
+}
+
+int rans_quantize_pmfs(const double *pmf, const int32_t *pmf_lengths, int32_t num_tables,
+                       int32_t pmf_stride, int32_t cdf_stride, int32_t *cdf, int32_t *cdf_lengths,
+                       int32_t *row_status, hipStream_t hstream)
+{
+    if (!pmf || !pmf_lengths || !cdf || !cdf_lengths || !row_status)
+        return RANS_E_ARG;
+    if (num_tables < 1 || num_tables > RANS_MAX_TABLES || pmf_stride < 2 || cdf_stride < 3 ||
+        cdf_stride > RANS_MAX_STRIDE)
+        return RANS_E_ARG;
+    TableArgs a{nullptr, 0.0, pmf, pmf_lengths, pmf_stride, num_tables, cdf_stride, cdf,
+                cdf_lengths, nullptr, row_status};
+    return launched(launch_table_rows(a, hstream));
+}
+
 const char *rans_status_string(int code)
 {
     switch (code) {

@@ -312,4 +312,21 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 
+// Quantised CDF rows: Gaussian rows when scales != nullptr, else pmf rows.
+struct TableArgs {
+    const double *scales;
+    double tail_z;
+    const double *pmf;
+    const int32_t *pmf_lengths;
+    int32_t pmf_stride;
+    int32_t num_tables;
+    int32_t cdf_stride;
+    int32_t *cdf;
+    int32_t *lengths;
+    int32_t *offsets;
+    int32_t *status;
+};
+
+hipError_t launch_table_rows(const TableArgs &a, hipStream_t s);
+
 }  // namespace rans

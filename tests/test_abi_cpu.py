@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     from learned_image_compression_amd import binding as B
     assert sorted(B.EXPORTS) == names
     for name in names:
@@ -132,3 +132,36 @@ def test_binding_refuses_to_run_without_library(tmp_path):
     from learned_image_compression_amd import binding as B
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         B.load(str(tmp_path / "missing.so"))
+
+
+def _gauss(lib, **kw):
+    a = dict(scales=1, K=64, tail_z=6.1, stride=3133, cdf=1, lengths=1, offsets=1, status=1,
+             hstream=0)
+    a.update(kw)
+    return lib.rans_gaussian_tables(a["scales"], a["K"], a["tail_z"], a["stride"], a["cdf"],
+                                    a["lengths"], a["offsets"], a["status"], a["hstream"])
+
+
+def _pmfs(lib, **kw):
+    a = dict(pmf=1, lengths=1, K=8, pmf_stride=256, stride=258, cdf=1, cdf_lengths=1, status=1,
+             hstream=0)
+    a.update(kw)
+    return lib.rans_quantize_pmfs(a["pmf"], a["lengths"], a["K"], a["pmf_stride"], a["stride"],
+                                  a["cdf"], a["cdf_lengths"], a["status"], a["hstream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(scales=0), dict(cdf=0), dict(lengths=0), dict(offsets=0), dict(status=0),
+    dict(K=0), dict(K=4097), dict(stride=2), dict(stride=16385),
+    dict(tail_z=0.0), dict(tail_z=-1.0), dict(tail_z=float("nan")), dict(tail_z=float("inf")),
+])
+def test_gaussian_tables_reject_bad_arguments_on_host(lib, kw):
+    assert _gauss(lib, **kw) == -1
+
+
+@pytest.mark.parametrize("kw", [
+    dict(pmf=0), dict(lengths=0), dict(cdf=0), dict(cdf_lengths=0), dict(status=0),
+    dict(K=0), dict(K=4097), dict(pmf_stride=1), dict(stride=2), dict(stride=16385),
+])
+def test_quantize_pmfs_reject_bad_arguments_on_host(lib, kw):
+    assert _pmfs(lib, **kw) == -1
