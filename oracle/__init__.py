@@ -63,6 +63,11 @@ def _bind(lib):
     lib.oracle_gaussian_row.restype = ctypes.c_int
     lib.oracle_gaussian_tables.argtypes = [f64p, i32, f64, i32, i32p, i32p, i32p]
     lib.oracle_gaussian_tables.restype = ctypes.c_int
+    f32p = ctypes.POINTER(ctypes.c_float)
+    lib.oracle_latent_symbols.argtypes = [f32p, f32p, f32p, u64, f32p, i32, i32p, i32p]
+    lib.oracle_latent_symbols.restype = ctypes.c_int
+    lib.oracle_dequantize.argtypes = [i32p, f32p, u64, f32p]
+    lib.oracle_dequantize.restype = ctypes.c_int
     return lib
 
 
@@ -194,3 +199,31 @@ def gaussian_tables(scales, tail_z: float, stride: int, lib=None):
                                     _ptr(cdf, ctypes.c_int32), _ptr(lengths, ctypes.c_int32),
                                     _ptr(offsets, ctypes.c_int32))
     return int(rc), cdf, lengths, offsets
+
+
+def latent_symbols(y, means, scales, scale_table, lib=None):
+    """Return (status, symbols int32, indexes int32) of the latent front end."""
+    lib = lib or load()
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    means = np.ascontiguousarray(means, dtype=np.float32)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    table = np.ascontiguousarray(scale_table, dtype=np.float32)
+    n = y.size
+    sym = np.zeros(max(n, 1), dtype=np.int32)
+    idx = np.zeros(max(n, 1), dtype=np.int32)
+    f32 = ctypes.c_float
+    rc = lib.oracle_latent_symbols(_ptr(y, f32), _ptr(means, f32), _ptr(scales, f32), n,
+                                   _ptr(table, f32), table.size, _ptr(sym, ctypes.c_int32),
+                                   _ptr(idx, ctypes.c_int32))
+    return int(rc), sym[:n], idx[:n]
+
+
+def dequantize(symbols, means, lib=None):
+    """Return (status, y_hat float32)."""
+    lib = lib or load()
+    symbols = np.ascontiguousarray(symbols, dtype=np.int32)
+    means = np.ascontiguousarray(means, dtype=np.float32)
+    out = np.zeros(max(symbols.size, 1), dtype=np.float32)
+    rc = lib.oracle_dequantize(_ptr(symbols, ctypes.c_int32), _ptr(means, ctypes.c_float),
+                               symbols.size, _ptr(out, ctypes.c_float))
+    return int(rc), out[: symbols.size]

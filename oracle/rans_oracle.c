@@ -505,3 +505,59 @@ int oracle_gaussian_tables(const double *scales, int32_t num_tables, double tail
     }
     return ORACLE_OK;
 }
+
+/* ---- Latent front end ------------------------------------------------------
+ *
+ * The pages time a mean-scale codec's steps around the coder: build_indexes
+ * on the GPU, then the coder, for the y latent (kompressor BENCHMARKS.md,
+ * section 3), and the symbols reach the coder as int32 tensors (section 4).
+ * Readings:
+ *   Q1  symbol = round-half-even(y - mean), the subtraction and the rounding
+ *       in single precision (the latent's dtype); a value that int32 cannot
+ *       hold saturates (NaN to INT32_MIN), so the coder refuses it as out of
+ *       range rather than coding a wrapped value;
+ *   Q2  index = the first table slot whose scale is at least the predicted
+ *       scale, the last slot when none is (or the scale is NaN): written as
+ *       (K - 1) - #{k < K - 1 : scale <= table[k]}, which holds for any table;
+ *   Q3  dequantisation y_hat = (float)symbol + mean in single precision.
+ */
+
+static int32_t saturate_round(float d)
+{
+    if (d != d)
+        return INT32_MIN;
+    float r = rintf(d);   /* default rounding: half to even */
+    if (r >= 2147483648.0f)
+        return INT32_MAX;
+    if (r < -2147483648.0f)
+        return INT32_MIN;
+    return (int32_t)r;
+}
+
+int oracle_latent_symbols(const float *y, const float *means, const float *scales, uint64_t n,
+                          const float *scale_table, int32_t num_scales, int32_t *symbols,
+                          int32_t *indexes)
+{
+    if (num_scales < 1 || (n && (!y || !means || !scales || !symbols || !indexes)) ||
+        !scale_table)
+        return ORACLE_E_ARG;
+    for (uint64_t i = 0; i < n; ++i) {
+        float d = y[i] - means[i];
+        symbols[i] = saturate_round(d);
+        int32_t idx = num_scales - 1;
+        for (int32_t k = 0; k < num_scales - 1; ++k)
+            if (scales[i] <= scale_table[k])
+                idx -= 1;
+        indexes[i] = idx;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_dequantize(const int32_t *symbols, const float *means, uint64_t n, float *y_hat)
+{
+    if (n && (!symbols || !means || !y_hat))
+        return ORACLE_E_ARG;
+    for (uint64_t i = 0; i < n; ++i)
+        y_hat[i] = (float)symbols[i] + means[i];
+    return ORACLE_OK;
+}

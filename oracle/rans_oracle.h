@@ -100,6 +100,16 @@ int oracle_gaussian_row(double scale, double tail_z, int32_t stride, int32_t *cd
 int oracle_gaussian_tables(const double *scales, int32_t num_tables, double tail_z,
                            int32_t stride, int32_t *cdf, int32_t *lengths, int32_t *offsets);
 
+/* Latent front end: symbols[i] = round-half-even(y[i] - means[i]) in single
+ * precision, saturated to int32 (NaN -> INT32_MIN); indexes[i] = the first k
+ * with scales[i] <= scale_table[k], K - 1 when none. */
+int oracle_latent_symbols(const float *y, const float *means, const float *scales, uint64_t n,
+                          const float *scale_table, int32_t num_scales, int32_t *symbols,
+                          int32_t *indexes);
+
+/* y_hat[i] = (float)symbols[i] + means[i] in single precision. */
+int oracle_dequantize(const int32_t *symbols, const float *means, uint64_t n, float *y_hat);
+
 #ifdef __cplusplus
 }
 #endif

@@ -146,3 +146,23 @@ def gaussian_row_by_integration(scale, tail_z):
     frac = np.abs(np.mod(p * 65536.0, 1.0) - 0.5)
     f = quantize_water_level(p)
     return [0] + np.cumsum(f).tolist(), -c, float(frac.min())
+
+
+# --------------------------------------------------------------- latent front end
+LATENT_TABLE = [0.5, 1.0, 2.0, 4.0]
+
+
+def latent_cases():
+    """(symbol cases [(y, mean, symbol)], index cases [(scale, index)]) of
+    golden/latent_front_end.txt."""
+    syms, idxs = [], []
+    with open(os.path.join(GOLDEN, "latent_front_end.txt")) as fh:
+        for line in fh:
+            f = line.split("#")[0].split()
+            if not f:
+                continue
+            if f[0] == "sym":
+                syms.append((float(f[1]), float(f[2]), int(f[3])))
+            elif f[0] == "idx":
+                idxs.append((float(f[1]), int(f[2])))
+    return syms, idxs

@@ -18,8 +18,26 @@ import oracle  # noqa: E402
 from oracle import spec_model as sm  # noqa: E402
 import workloads as W  # noqa: E402
 from helpers import (gaussian_row_by_integration, lane_information,  # noqa: E402
-                     lane_words_from_container, quantize_water_level, quantized_cases,
-                     single_table, worked_cases)
+                     lane_words_from_container, latent_cases, LATENT_TABLE,
+                     quantize_water_level, quantized_cases, single_table, worked_cases)
+
+
+def latent_pins(lib):
+    failures = []
+    syms, idxs = latent_cases()
+    rc, sym, _ = oracle.latent_symbols([c[0] for c in syms], [c[1] for c in syms],
+                                       np.ones(len(syms)), LATENT_TABLE, lib=lib)
+    if rc != 0 or sym.tolist() != [c[2] for c in syms]:
+        failures.append("golden latent symbols")
+    rc, _, idx = oracle.latent_symbols(np.zeros(len(idxs)), np.zeros(len(idxs)),
+                                       [c[0] for c in idxs], LATENT_TABLE, lib=lib)
+    if rc != 0 or idx.tolist() != [c[1] for c in idxs]:
+        failures.append("golden latent indexes")
+    rc, out = oracle.dequantize(np.array([0, 1, -1], np.int32),
+                                np.array([0.25, -0.5, 0.5], np.float32), lib=lib)
+    if rc != 0 or out.tolist() != [0.25, 0.5, -0.5]:
+        failures.append("dequantize")
+    return failures
 
 
 def table_pins(lib):
@@ -112,6 +130,6 @@ def pins(lib):
 
 if __name__ == "__main__":
     lib = oracle.load(sys.argv[1])
-    f = pins(lib) + table_pins(lib)
+    f = pins(lib) + table_pins(lib) + latent_pins(lib)
     print("\n".join(f) if f else "all pins hold")
     sys.exit(1 if f else 0)

@@ -61,6 +61,17 @@ MUTANTS = {
     "g_offset_sign": ("*offset = -c;", "*offset = c;"),
     "g_padding": ("cdf_row[k] = (int32_t)TOTAL_FREQ;", "cdf_row[k] = 0;"),
     "g_root_two": ("-x * 0.70710678118654752440", "-x * 1.41421356237309504880"),
+    # latent front end
+    "l_round_half_up": ("float r = rintf(d);", "float r = floorf(d + 0.5f);"),
+    "l_truncate": ("float r = rintf(d);", "float r = truncf(d);"),
+    "l_index_strict": ("if (scales[i] <= scale_table[k])", "if (scales[i] < scale_table[k])"),
+    "l_index_all_slots": ("for (int32_t k = 0; k < num_scales - 1; ++k)",
+                          "for (int32_t k = 0; k < num_scales; ++k)"),
+    "l_nan_symbol": ("if (d != d)\n        return INT32_MIN;", "if (d != d)\n        return 0;"),
+    "l_saturate_high": ("if (r >= 2147483648.0f)\n        return INT32_MAX;",
+                        "if (r > 2147483648.0f)\n        return INT32_MAX;"),
+    "l_dequant_sign": ("y_hat[i] = (float)symbols[i] + means[i];",
+                       "y_hat[i] = (float)symbols[i] - means[i];"),
 }
 
 
