@@ -171,6 +171,33 @@ int rans_quantize_pmfs(const double *pmf, const int32_t *pmf_lengths, int32_t nu
                        int32_t pmf_stride, int32_t cdf_stride, int32_t *cdf, int32_t *cdf_lengths,
                        int32_t *row_status, hipStream_t hstream);
 
+/* The mean-scale front end around the coder (kompressor BENCHMARKS.md,
+ * sections 3 and 4: the codec computes each position's table index on the
+ * GPU, build_indexes, and hands symbols and indexes to the coder as int32).
+ *
+ * rans_latent_symbols: for i < n, symbols[i] = round-half-even(y[i] -
+ * means[i]) computed in single precision and saturated to int32 (NaN gives
+ * INT32_MIN), so a value int32 cannot hold reaches the coder as one it
+ * refuses with RANS_E_SYMBOL_RANGE; indexes[i] = (K - 1) - #{k < K - 1 :
+ * scales[i] <= scale_table[k]}, i.e. for an ascending table the first k with
+ * scales[i] <= scale_table[k], K - 1 when there is none or scales[i] is NaN.
+ * K = num_scales in [1, RANS_MAX_TABLES]; the result follows that rule for
+ * any table, fastest when the first K - 1 scales are non-decreasing.
+ *
+ * rans_dequantize: y_hat[i] = (float)symbols[i] + means[i] in single
+ * precision.
+ *
+ * Device pointers, float32 / int32 arrays of n entries (16-byte aligned
+ * arrays take 16-byte accesses; any 4-byte alignment works).  n = 0 is a
+ * no-op.  Returns RANS_E_ARG for null pointers or a bad K, RANS_E_HIP for a
+ * failed launch; nothing data-dependent fails. */
+int rans_latent_symbols(const float *y, const float *means, const float *scales, uint64_t n,
+                        const float *scale_table, int32_t num_scales, int32_t *symbols,
+                        int32_t *indexes, hipStream_t hstream);
+
+int rans_dequantize(const int32_t *symbols, const float *means, uint64_t n, float *y_hat,
+                    hipStream_t hstream);
+
 /* Static text for a status code. */
 const char *rans_status_string(int code);
 

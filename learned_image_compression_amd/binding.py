@@ -40,6 +40,8 @@ EXPORTS = (
     "rans_decode_prepared",
     "rans_gaussian_tables",
     "rans_quantize_pmfs",
+    "rans_latent_symbols",
+    "rans_dequantize",
     "rans_status_string",
 )
 
@@ -97,6 +99,10 @@ def load(path: str | None = None):
         lib.rans_gaussian_tables.restype = ctypes.c_int
         lib.rans_quantize_pmfs.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
         lib.rans_quantize_pmfs.restype = ctypes.c_int
+        lib.rans_latent_symbols.argtypes = [vp, vp, vp, u64, vp, i32, vp, vp, vp]
+        lib.rans_latent_symbols.restype = ctypes.c_int
+        lib.rans_dequantize.argtypes = [vp, vp, u64, vp, vp]
+        lib.rans_dequantize.restype = ctypes.c_int
         lib.rans_status_string.argtypes = [ctypes.c_int]
         lib.rans_status_string.restype = ctypes.c_char_p
         if path is None:
@@ -324,3 +330,47 @@ def check_rows(row_status: torch.Tensor, where: str = "table build"):
     bad = torch.nonzero(st).flatten()
     if bad.numel():
         raise RansError(int(st[bad[0]]), f"{where}: row {int(bad[0])}")
+
+
+def latent_symbols(y: torch.Tensor, means: torch.Tensor, scales: torch.Tensor,
+                   scale_table: torch.Tensor, *, symbols_out: torch.Tensor | None = None,
+                   indexes_out: torch.Tensor | None = None):
+    """Enqueue the front end: (symbols, indexes) int32 of rint(y - means) and the
+    table index of each scale (float32 device tensors of one size; float32 table)."""
+    device = y.device
+    for t, name in ((y, "y"), (means, "means"), (scales, "scales"), (scale_table, "scale_table")):
+        _need(t, torch.float32, device, name)
+    n = y.numel()
+    if means.numel() != n or scales.numel() != n:
+        raise ValueError("y, means and scales differ in size")
+    if symbols_out is None:
+        symbols_out = torch.empty(n, dtype=torch.int32, device=device)
+    if indexes_out is None:
+        indexes_out = torch.empty(n, dtype=torch.int32, device=device)
+    _need(symbols_out, torch.int32, device, "symbols_out")
+    _need(indexes_out, torch.int32, device, "indexes_out")
+    if symbols_out.numel() != n or indexes_out.numel() != n:
+        raise ValueError("output sizes differ from the input")
+    rc = load().rans_latent_symbols(_ptr(y), _ptr(means), _ptr(scales), n, _ptr(scale_table),
+                                    scale_table.numel(), _ptr(symbols_out), _ptr(indexes_out),
+                                    _stream(device))
+    _check_rc(rc, "rans_latent_symbols")
+    return symbols_out, indexes_out
+
+
+def dequantize(symbols: torch.Tensor, means: torch.Tensor, *, out: torch.Tensor | None = None):
+    """Enqueue y_hat = symbols + means (float32)."""
+    device = symbols.device
+    _need(symbols, torch.int32, device, "symbols")
+    _need(means, torch.float32, device, "means")
+    n = symbols.numel()
+    if means.numel() != n:
+        raise ValueError("symbols and means differ in size")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=device)
+    _need(out, torch.float32, device, "out")
+    if out.numel() != n:
+        raise ValueError("output size differs from the input")
+    rc = load().rans_dequantize(_ptr(symbols), _ptr(means), n, _ptr(out), _stream(device))
+    _check_rc(rc, "rans_dequantize")
+    return out

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "librans_hip.so")
-SOURCES = ["rans_prep.hip", "rans_encode.hip", "rans_decode.hip", "rans_tables.hip", "rans_abi.hip"]
+SOURCES = ["rans_prep.hip", "rans_encode.hip", "rans_decode.hip", "rans_tables.hip", "rans_latent.hip",
+           "rans_abi.hip"]
 ARCH = os.environ.get("RANS_HIP_ARCH", "gfx950")
 
 FLAGS = [

@@ -187,6 +187,31 @@ int rans_quantize_pmfs(const double *pmf, const int32_t *pmf_lengths, int32_t nu
     return launched(launch_table_rows(a, hstream));
 }
 
+int rans_latent_symbols(const float *y, const float *means, const float *scales, uint64_t n,
+                        const float *scale_table, int32_t num_scales, int32_t *symbols,
+                        int32_t *indexes, hipStream_t hstream)
+{
+    if (!scale_table || num_scales < 1 || num_scales > RANS_MAX_TABLES)
+        return RANS_E_ARG;
+    if (n == 0)
+        return RANS_OK;
+    if (!y || !means || !scales || !symbols || !indexes)
+        return RANS_E_ARG;
+    LatentArgs a{y, means, scales, n, scale_table, num_scales, symbols, indexes};
+    return launched(launch_latent_symbols(a, hstream));
+}
+
+int rans_dequantize(const int32_t *symbols, const float *means, uint64_t n, float *y_hat,
+                    hipStream_t hstream)
+{
+    if (n == 0)
+        return RANS_OK;
+    if (!symbols || !means || !y_hat)
+        return RANS_E_ARG;
+    DequantArgs a{symbols, means, n, y_hat};
+    return launched(launch_dequantize(a, hstream));
+}
+
 const char *rans_status_string(int code)
 {
     switch (code) {

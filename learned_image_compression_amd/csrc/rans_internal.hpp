@@ -329,4 +329,26 @@ struct TableArgs {
 
 hipError_t launch_table_rows(const TableArgs &a, hipStream_t s);
 
+// The latent front end and dequantisation.
+struct LatentArgs {
+    const float *y;
+    const float *means;
+    const float *scales;
+    uint64_t n;
+    const float *table;
+    int32_t K;
+    int32_t *symbols;
+    int32_t *indexes;
+};
+
+struct DequantArgs {
+    const int32_t *symbols;
+    const float *means;
+    uint64_t n;
+    float *y_hat;
+};
+
+hipError_t launch_latent_symbols(const LatentArgs &a, hipStream_t s);
+hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
+
 }  // namespace rans

@@ -1,0 +1,196 @@
+// rans_latent.hip -- the mean-scale front end around the coder: latent ->
+// (symbols, table indexes) before encoding, symbols -> latent after decoding.
+//
+// The codec computes the table index of every y position on the GPU
+// (build_indexes) and hands symbols and indexes to the coder as int32 tensors
+// (kompressor BENCHMARKS.md, sections 3 and 4).  Readings:
+//   symbol = round-half-even(y - mean) in single precision, saturated to
+//            int32 (NaN -> INT32_MIN), so a value int32 cannot hold reaches
+//            the coder as one it refuses as out of range;
+//   index  = (K - 1) - #{k < K - 1 : scale <= table[k]}: the first table
+//            scale at or above the predicted scale, K - 1 when there is none
+//            or the scale is NaN;
+//   y_hat  = (float)symbol + mean in single precision.
+//
+// Both kernels stream HBM: 12 bytes in and 8 out per position for the front
+// end, 8 in and 4 out for dequantisation.  When every array is 16-byte
+// aligned, a thread takes a group of four positions (front end: its four
+// index searches already keep it busy) or eight (dequantisation: two 16-byte
+// loads per array in flight), all loads issued before any use.  The scale table is
+// staged in LDS; when its first K - 1 entries are non-decreasing, the index
+// is a branch-free binary search of fixed trip count (the counted set is then
+// a suffix of the table), else the count is taken entry by entry.
+#include "rans_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace rans {
+namespace {
+
+constexpr int kLatThreads = 256;
+// one group of positions per thread: a grid-stride loop over a capped grid
+// kept fewer bytes in flight and ran about 10% slower at 50M positions
+constexpr uint32_t kLatMaxBlocks = 1u << 30;
+
+__device__ inline int32_t saturate_round(float d)
+{
+    if (d != d)
+        return INT32_MIN;
+    const float r = rintf(d);   // half to even
+    if (r >= 2147483648.0f)
+        return INT32_MAX;
+    if (r < -2147483648.0f)
+        return INT32_MIN;
+    return (int32_t)r;
+}
+
+struct ScaleTable {
+    const float *t;   // LDS
+    int32_t K;
+    int32_t steps;    // highest power of two <= K - 1 (0 when K == 1)
+    bool sorted;
+
+    __device__ int32_t index(float s) const
+    {
+        const int32_t m = K - 1;   // slots counted against
+        if (sorted) {
+            // j = #{k < m : table[k] < s} = first k with s <= table[k]
+            int32_t j = 0;
+            for (int32_t step = steps; step > 0; step >>= 1)
+                if (j + step <= m && t[j + step - 1] < s)
+                    j += step;
+            return s != s ? m : j;
+        }
+        int32_t idx = m;
+        for (int32_t k = 0; k < m; ++k)
+            idx -= s <= t[k] ? 1 : 0;
+        return idx;
+    }
+};
+
+__device__ inline ScaleTable stage_scale_table(const float *table, int32_t K, float *lds)
+{
+    for (int32_t k = threadIdx.x; k < K; k += kLatThreads)
+        lds[k] = table[k];
+    __syncthreads();
+    int unsorted = 0;
+    for (int32_t k = threadIdx.x; k + 2 < K; k += kLatThreads)
+        unsorted |= !(lds[k] <= lds[k + 1]);   // NaN entries count as unsorted
+    ScaleTable st;
+    st.t = lds;
+    st.K = K;
+    st.sorted = !__syncthreads_or(unsorted);
+    int32_t p = 1;
+    while (2 * p <= K - 1)
+        p *= 2;
+    st.steps = K > 1 ? p : 0;
+    return st;
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kLatThreads) void latent_symbols_kernel(LatentArgs a)
+{
+    __shared__ float table[RANS_MAX_TABLES];
+    const ScaleTable st = stage_scale_table(a.table, a.K, table);
+    const uint64_t groups = (a.n + VEC - 1) / VEC;
+    const uint64_t stride = (uint64_t)gridDim.x * kLatThreads;
+    for (uint64_t g = (uint64_t)blockIdx.x * kLatThreads + threadIdx.x; g < groups; g += stride) {
+        const uint64_t i0 = g * VEC;
+        if (VEC >= 4 && i0 + VEC <= a.n) {
+            constexpr int U = VEC >= 4 ? VEC / 4 : 1;
+            float4 y[U], m[U], s[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                y[u] = *reinterpret_cast<const float4 *>(a.y + i0 + 4 * u);
+                m[u] = *reinterpret_cast<const float4 *>(a.means + i0 + 4 * u);
+                s[u] = *reinterpret_cast<const float4 *>(a.scales + i0 + 4 * u);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                int4 q, ix;
+                q.x = saturate_round(y[u].x - m[u].x);
+                q.y = saturate_round(y[u].y - m[u].y);
+                q.z = saturate_round(y[u].z - m[u].z);
+                q.w = saturate_round(y[u].w - m[u].w);
+                ix.x = st.index(s[u].x);
+                ix.y = st.index(s[u].y);
+                ix.z = st.index(s[u].z);
+                ix.w = st.index(s[u].w);
+                *reinterpret_cast<int4 *>(a.symbols + i0 + 4 * u) = q;
+                *reinterpret_cast<int4 *>(a.indexes + i0 + 4 * u) = ix;
+            }
+        } else {
+            for (uint64_t i = i0; i < min(i0 + VEC, a.n); ++i) {
+                a.symbols[i] = saturate_round(a.y[i] - a.means[i]);
+                a.indexes[i] = st.index(a.scales[i]);
+            }
+        }
+    }
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kLatThreads) void dequantize_kernel(DequantArgs a)
+{
+    const uint64_t groups = (a.n + VEC - 1) / VEC;
+    const uint64_t stride = (uint64_t)gridDim.x * kLatThreads;
+    for (uint64_t g = (uint64_t)blockIdx.x * kLatThreads + threadIdx.x; g < groups; g += stride) {
+        const uint64_t i0 = g * VEC;
+        if (VEC >= 4 && i0 + VEC <= a.n) {
+            constexpr int U = VEC >= 4 ? VEC / 4 : 1;
+            int4 q[U];
+            float4 m[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                q[u] = *reinterpret_cast<const int4 *>(a.symbols + i0 + 4 * u);
+                m[u] = *reinterpret_cast<const float4 *>(a.means + i0 + 4 * u);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float4 o;
+                o.x = (float)q[u].x + m[u].x;
+                o.y = (float)q[u].y + m[u].y;
+                o.z = (float)q[u].z + m[u].z;
+                o.w = (float)q[u].w + m[u].w;
+                *reinterpret_cast<float4 *>(a.y_hat + i0 + 4 * u) = o;
+            }
+        } else {
+            for (uint64_t i = i0; i < min(i0 + VEC, a.n); ++i)
+                a.y_hat[i] = (float)a.symbols[i] + a.means[i];
+        }
+    }
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+uint32_t grid_for(uint64_t groups)
+{
+    const uint64_t b = (groups + kLatThreads - 1) / kLatThreads;
+    return (uint32_t)(b < 1 ? 1 : (b > kLatMaxBlocks ? kLatMaxBlocks : b));
+}
+
+}  // namespace
+
+hipError_t launch_latent_symbols(const LatentArgs &a, hipStream_t s)
+{
+    if (aligned16(a.y) && aligned16(a.means) && aligned16(a.scales) && aligned16(a.symbols) &&
+        aligned16(a.indexes))
+        hipLaunchKernelGGL(latent_symbols_kernel<4>, dim3(grid_for((a.n + 3) / 4)),
+                           dim3(kLatThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(latent_symbols_kernel<1>, dim3(grid_for(a.n)), dim3(kLatThreads), 0,
+                           s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s)
+{
+    if (aligned16(a.symbols) && aligned16(a.means) && aligned16(a.y_hat))
+        hipLaunchKernelGGL(dequantize_kernel<8>, dim3(grid_for((a.n + 7) / 8)),
+                           dim3(kLatThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(dequantize_kernel<1>, dim3(grid_for(a.n)), dim3(kLatThreads), 0, s,
+                           a);
+    return hipGetLastError();
+}
+
+}  // namespace rans

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     from learned_image_compression_amd import binding as B
     assert sorted(B.EXPORTS) == names
     for name in names:
@@ -165,3 +165,26 @@ def test_gaussian_tables_reject_bad_arguments_on_host(lib, kw):
 ])
 def test_quantize_pmfs_reject_bad_arguments_on_host(lib, kw):
     assert _pmfs(lib, **kw) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=0), -1), (dict(K=0), -1), (dict(K=4097), -1),
+    (dict(y=0), -1), (dict(means=0), -1), (dict(scales=0), -1), (dict(sym=0), -1),
+    (dict(idx=0), -1),
+    (dict(n=0, y=0, means=0, scales=0, sym=0, idx=0), 0),   # nothing to do, no launch
+])
+def test_latent_symbols_host_checks(lib, kw, code):
+    a = dict(y=1, means=1, scales=1, n=100, table=1, K=64, sym=1, idx=1)
+    a.update(kw)
+    assert lib.rans_latent_symbols(a["y"], a["means"], a["scales"], a["n"], a["table"], a["K"],
+                                   a["sym"], a["idx"], 0) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sym=0), -1), (dict(means=0), -1), (dict(out=0), -1),
+    (dict(n=0, sym=0, means=0, out=0), 0),
+])
+def test_dequantize_host_checks(lib, kw, code):
+    a = dict(sym=1, means=1, n=100, out=1)
+    a.update(kw)
+    assert lib.rans_dequantize(a["sym"], a["means"], a["n"], a["out"], 0) == code
