@@ -1,8 +1,10 @@
 """Benchmark: indexed rANS64 encode + decode of the 1080p y latent on one MI355X.
 
-One step is the whole coding path on one batch: rans_encode_with_indexes and
-rans_decode_with_indexes (each a table-preparation launch and a coding
-launch) of 1,566,720 int32 symbols (192x68x120) with 64
+One step is the whole coding path on one batch: table preparation + encode
+and table preparation + decode (rans_prepare_tables followed by
+rans_encode_prepared / rans_decode_prepared, exactly the launches that
+rans_encode_with_indexes / rans_decode_with_indexes make, called separately
+so that HIP events can bracket each coding kernel alone) of 1,566,720 int32 symbols (192x68x120) with 64
 Gaussian 16-bit CDF rows at 4096 lanes -- the y latent of a 1920x1088 image
 in a mean-scale hyperprior (kompressor README, "Getting Started").  Inputs are
 synthetic, seeded, and resident in HBM before timing.  Before timing, the GPU
@@ -77,7 +79,8 @@ def table_set():
     from scipy.special import ndtri
     lo, hi, K = 0.11, 256.0, 64
     scales = np.exp(np.log(lo) + (np.log(hi) - np.log(lo)) * np.arange(K) / (K - 1))
-    return scales, float(ndtri(1.0 - 5e-10))
+    tail_z = float(ndtri(1.0 - 5e-10))
+    return scales, tail_z, 2 * int(np.ceil(hi * tail_z)) + 3   # longest row: 3133
 
 
 def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200):
@@ -98,9 +101,9 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
     assert words.size == gpu_words.size and np.array_equal(words, gpu_words), \
         "GPU container differs from the oracle's"
     assert np.array_equal(out, w.symbols)
-    scales, tail_z = table_set()
+    scales, tail_z, tstride = table_set()
     t0 = time.perf_counter()
-    rc, cdf, lengths, offsets = oracle.gaussian_tables(scales, tail_z, w.stride)
+    rc, cdf, lengths, offsets = oracle.gaussian_tables(scales, tail_z, tstride)
     table_us = (time.perf_counter() - t0) * 1e6
     assert rc == 0 and all(np.array_equal(a, b) for a, b in zip((cdf, lengths, offsets), gpu_tables)), \
         "GPU table set differs from the oracle's"
@@ -169,26 +172,30 @@ def main():
     B.check(st_dec, "decode")
     assert torch.equal(out.cpu(), torch.from_numpy(w.symbols)), "GPU decode != input"
 
-    # ---- one step = encode + decode through the two public entry points --------
-    # They are called straight through ctypes with arguments marshalled once,
-    # so the host adds as little as possible per launch.
+    # ---- one step = prep + encode, prep + decode ---------------------------------
+    # The entry points are called straight through ctypes with arguments
+    # marshalled once, so the host adds as little as possible per launch.
     import ctypes
     lib = B.load()
     vp = ctypes.c_void_p
     hs = vp(torch.cuda.current_stream(dev).cuda_stream)
-    tab_args = (vp(tables.cdf.data_ptr()), vp(tables.lengths.data_ptr()),
-                vp(tables.offsets.data_ptr()), tables.num_tables, tables.stride, lanes)
-    enc_args = (vp(sym.data_ptr()), vp(idx.data_ptr()), n, *tab_args, vp(stream.data_ptr()),
-                cap, vp(nwords.data_ptr()), vp(st_enc.data_ptr()), vp(ws.data_ptr()),
-                ws.numel(), hs)
-    dec_args = (vp(stream.data_ptr()), cap, vp(idx.data_ptr()), n, *tab_args,
-                vp(out.data_ptr()), vp(st_dec.data_ptr()), vp(ws.data_ptr()), ws.numel(), hs)
-    enc, dec = lib.rans_encode_with_indexes, lib.rans_decode_with_indexes
+    prep_args = (vp(tables.cdf.data_ptr()), vp(tables.lengths.data_ptr()),
+                 vp(tables.offsets.data_ptr()), tables.num_tables, tables.stride,
+                 vp(ws.data_ptr()), ws.numel(), hs)
+    enc_args = (vp(sym.data_ptr()), vp(idx.data_ptr()), n, tables.num_tables, tables.stride,
+                lanes, vp(stream.data_ptr()), cap, vp(nwords.data_ptr()), vp(st_enc.data_ptr()),
+                vp(ws.data_ptr()), ws.numel(), hs)
+    dec_args = (vp(stream.data_ptr()), cap, vp(idx.data_ptr()), n, tables.num_tables,
+                tables.stride, lanes, vp(out.data_ptr()), vp(st_dec.data_ptr()),
+                vp(ws.data_ptr()), ws.numel(), hs)
+    prep, enc, dec = lib.rans_prepare_tables, lib.rans_encode_prepared, lib.rans_decode_prepared
 
     def step(ev):
+        rc = prep(*prep_args)
         ev[0].record()
-        rc = enc(*enc_args)
+        rc |= enc(*enc_args)
         ev[1].record()
+        rc |= prep(*prep_args)
         ev[2].record()
         rc |= dec(*dec_args)
         ev[3].record()
@@ -221,23 +228,29 @@ def main():
     value = n / (ms_per_step * 1e-3) / 1e9
 
     # ---- device table builder on the workloads' table set ------------------------
-    scales, tail_z = table_set()
+    scales, tail_z, tstride = table_set()
     d_scales = torch.from_numpy(scales).to(dev)
-    built, row_st = B.gaussian_tables(d_scales, tail_z, w.stride)
+    built, row_st = B.gaussian_tables(d_scales, tail_z, tstride)
     B.check_rows(row_st)
     gpu_tables = tuple(t.cpu().numpy() for t in (built.cdf, built.lengths, built.offsets))
-    if w.num_tables == scales.size:
+    if w.num_tables == scales.size and w.stride == tstride:
         assert all(np.array_equal(a, b) for a, b in zip(gpu_tables, (w.cdf, w.lengths, w.offsets))), \
             "device-built tables differ from the workload's"
+    # timed on preallocated outputs, straight through ctypes
+    row_args = (vp(d_scales.data_ptr()), scales.size, tail_z, tstride, vp(built.cdf.data_ptr()),
+                vp(built.lengths.data_ptr()), vp(built.offsets.data_ptr()),
+                vp(row_st.data_ptr()), hs)
     tev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     tab_us = []
     for k in range(23):
         tev[0].record()
-        B.gaussian_tables(d_scales, tail_z, w.stride)
+        if lib.rans_gaussian_tables(*row_args):
+            raise RuntimeError("table build launch failed")
         tev[1].record()
         torch.cuda.synchronize()
         if k >= 3:
             tab_us.append(tev[0].elapsed_time(tev[1]) * 1e3)
+    B.check_rows(row_st)
 
     bytes_per_launch = 8 * n + 4 * total_words   # same for encode and decode
     dominant, dom_us = ("decode", dec_us) if dec_us >= enc_us else ("encode", enc_us)
@@ -278,7 +291,7 @@ def main():
         "table_build": {"kernel": "table_rows_kernel",
                         "workload": f"{scales.size} Gaussian rows, scales log-spaced "
                                     f"{scales[0]:g}..{scales[-1]:g}, tail mass 1e-9, "
-                                    f"stride {w.stride}",
+                                    f"stride {tstride}",
                         "us": round(statistics.median(tab_us), 2)},
     }
     if not args.no_cpu_baseline:

@@ -1,12 +1,17 @@
 """Helpers for the rocprofv3 summaries kept under profiles/.
 
-Two commands, both meant to run under or after rocprofv3:
+Three commands, all meant to run under or after rocprofv3:
 
   python -m learned_image_compression_amd.profiling copy [--mib M]
       A plain device-to-device copy of M MiB (torch copy_, which runs the
       HIP runtime's copy kernel), repeated a few times.  Counter passes over it
       (FETCH_SIZE, WRITE_SIZE) give the scale between those counters and
       bytes actually moved: a copy of M MiB reads and writes M MiB.
+
+  python -m learned_image_compression_amd.profiling latent [--n N] [--reps R]
+      The latent front end and dequantisation on N seeded synthetic
+      positions (a 64-scale table log-spaced over 0.11..256), R times each,
+      for kernel-trace and counter passes; prints the bytes each call moves.
 
   python -m learned_image_compression_amd.profiling summarize ...
       Turns rocprofv3 CSV output (kernel trace statistics and the counter
@@ -39,6 +44,28 @@ def copy_main(mib: int, reps: int) -> None:
     print(json.dumps({"copy_bytes": n * 4, "reps": reps}), flush=True)
 
 
+def latent_main(n: int, reps: int) -> None:
+    import math
+    import torch
+    from learned_image_compression_amd import binding as B
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    y = torch.randn(n, device=dev, generator=g) * 3
+    m = torch.randn(n, device=dev, generator=g)
+    s = torch.exp(torch.rand(n, device=dev, generator=g) * 8 - 3)
+    table = torch.exp(torch.linspace(math.log(0.11), math.log(256.0), 64)).float().to(dev)
+    sym = torch.empty(n, dtype=torch.int32, device=dev)
+    idx = torch.empty_like(sym)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    for _ in range(reps):
+        B.latent_symbols(y, m, s, table, symbols_out=sym, indexes_out=idx)
+        B.dequantize(sym, m, out=out)
+    torch.cuda.synchronize()
+    print(json.dumps({"positions": n, "reps": reps, "latent_bytes": 20 * n,
+                      "dequantize_bytes": 12 * n}), flush=True)
+
+
 def _rows(path_glob: str):
     paths = sorted(glob.glob(path_glob, recursive=True))
     if not paths:
@@ -48,7 +75,8 @@ def _rows(path_glob: str):
 
 
 def _kernel_key(name: str) -> str:
-    m = re.search(r"(encode_kernel|decode_kernel|prep_kernel)", name)
+    m = re.search(r"(encode_kernel|decode_kernel|prep_kernel|table_rows_kernel|"
+                  r"latent_symbols_kernel|dequantize_kernel)", name)
     if m:
         return m.group(1)
     if "copyBuffer" in name:
@@ -86,7 +114,8 @@ def summarize_main(a) -> None:
             with open(a.bench_json) as fh:
                 bench = [json.loads(l) for l in fh if l.strip().startswith("{")][-1]
             lines += ["", "# bench.py line of the same run (kernel_us from HIP events):",
-                      json.dumps({k: bench[k] for k in ("value", "unit", "ms_per_step", "kernel_us")})]
+                      json.dumps({k: bench[k] for k in ("value", "unit", "ms_per_step", "kernel_us",
+                                              "table_build") if k in bench})]
         path = os.path.join(a.out, f"kernel_trace_{a.label}.txt")
         with open(path, "w") as fh:
             fh.write("\n".join(lines) + "\n")
@@ -99,6 +128,25 @@ def summarize_main(a) -> None:
         copy_bytes = a.copy_mib * (1 << 20)
         f_scale = copy_bytes / (cf * KIB)
         w_scale = copy_bytes / (cw * KIB)
+        if a.latent_n:
+            # the front end moves 20 bytes per position, dequantisation 12
+            t = {"workload": a.label, "positions": a.latent_n, "commands": a.command,
+                 "copy_calibration": {"copy_bytes": copy_bytes, "fetch_kib": round(cf, 1),
+                                      "write_kib": round(cw, 1), "fetch_scale": round(f_scale, 4),
+                                      "write_scale": round(w_scale, 4)}}
+            for key, per in (("latent_symbols_kernel", 20), ("dequantize_kernel", 12)):
+                rb = fetch[key] * KIB * f_scale
+                wb = write[key] * KIB * w_scale
+                t[key] = {"fetch_kib_per_dispatch": round(fetch[key], 1),
+                          "write_kib_per_dispatch": round(write[key], 1),
+                          "hbm_bytes_per_launch": round(rb + wb),
+                          "algorithmic_bytes_per_launch": per * a.latent_n}
+            path = os.path.join(a.out, f"traffic_{a.label}.json")
+            with open(path, "w") as fh:
+                json.dump(t, fh, indent=1)
+                fh.write("\n")
+            print(path)
+            return
         sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
         import bench
         for kernel in ("encode", "decode"):
@@ -131,6 +179,9 @@ def main(argv=None) -> None:
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=256)
     c.add_argument("--reps", type=int, default=3)
+    lt = sub.add_parser("latent")
+    lt.add_argument("--n", type=int, default=50135040)
+    lt.add_argument("--reps", type=int, default=5)
     s = sub.add_parser("summarize")
     s.add_argument("--out", required=True)
     s.add_argument("--label", required=True)
@@ -144,9 +195,12 @@ def main(argv=None) -> None:
     s.add_argument("--calib-fetch")
     s.add_argument("--calib-write")
     s.add_argument("--copy-mib", type=int, default=256)
+    s.add_argument("--latent-n", type=int, default=0)
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         copy_main(a.mib, a.reps)
+    elif a.cmd == "latent":
+        latent_main(a.n, a.reps)
     else:
         summarize_main(a)
 
