@@ -63,6 +63,12 @@ def _bind(lib):
     lib.oracle_gaussian_row.restype = ctypes.c_int
     lib.oracle_gaussian_tables.argtypes = [f64p, i32, f64, i32, i32p, i32p, i32p]
     lib.oracle_gaussian_tables.restype = ctypes.c_int
+    lib.oracle_encode_split.argtypes = [i32p, i32p, u64, i32p, i32p, i32p, i32, i32, u32, u32,
+                                        u32p, u64, u64p, u32p]
+    lib.oracle_encode_split.restype = ctypes.c_int
+    lib.oracle_decode_split.argtypes = [u32p, u64, i32p, u64, i32p, i32p, i32p, i32, i32, u32,
+                                        u32, u32p, i32p]
+    lib.oracle_decode_split.restype = ctypes.c_int
     f32p = ctypes.POINTER(ctypes.c_float)
     lib.oracle_latent_symbols.argtypes = [f32p, f32p, f32p, u64, f32p, i32, i32p, i32p]
     lib.oracle_latent_symbols.restype = ctypes.c_int
@@ -227,3 +233,47 @@ def dequantize(symbols, means, lib=None):
     rc = lib.oracle_dequantize(_ptr(symbols, ctypes.c_int32), _ptr(means, ctypes.c_float),
                                symbols.size, _ptr(out, ctypes.c_float))
     return int(rc), out[: symbols.size]
+
+
+def encode_split(symbols, indexes, cdf, lengths, offsets, lanes: int, pieces: int,
+                 capacity: int | None = None, lib=None):
+    """Return (status, words, split_meta uint32 [lanes, pieces - 1, 3])."""
+    lib = lib or load()
+    symbols = np.ascontiguousarray(symbols, dtype=np.int32)
+    indexes = np.ascontiguousarray(indexes, dtype=np.int32)
+    cdf, lengths, offsets = _tables(cdf, lengths, offsets)
+    n = symbols.size
+    if capacity is None:
+        capacity = 1 + 3 * lanes + 10 * n
+    out = np.zeros(max(capacity, 1), dtype=np.uint32)
+    meta = np.zeros(max(3 * lanes * (pieces - 1), 1), dtype=np.uint32)
+    total = ctypes.c_uint64(0)
+    rc = lib.oracle_encode_split(_ptr(symbols, ctypes.c_int32), _ptr(indexes, ctypes.c_int32), n,
+                                 _ptr(cdf, ctypes.c_int32), _ptr(lengths, ctypes.c_int32),
+                                 _ptr(offsets, ctypes.c_int32), cdf.shape[0], cdf.shape[1],
+                                 lanes, pieces, _ptr(out, ctypes.c_uint32), capacity,
+                                 ctypes.byref(total), _ptr(meta, ctypes.c_uint32))
+    meta = meta[: 3 * lanes * (pieces - 1)].reshape(lanes, pieces - 1, 3)
+    if rc != OK:
+        return int(rc), out[:0], meta
+    return 0, out[: total.value].copy(), meta
+
+
+def decode_split(stream, split_meta, indexes, cdf, lengths, offsets, lanes: int, pieces: int,
+                 lib=None):
+    """Return (status, symbols) decoding piece by piece from the split records."""
+    lib = lib or load()
+    stream = np.ascontiguousarray(stream, dtype=np.uint32)
+    meta = np.ascontiguousarray(split_meta, dtype=np.uint32).reshape(-1)
+    if meta.size == 0:
+        meta = np.zeros(1, dtype=np.uint32)
+    indexes = np.ascontiguousarray(indexes, dtype=np.int32)
+    cdf, lengths, offsets = _tables(cdf, lengths, offsets)
+    out = np.zeros(max(indexes.size, 1), dtype=np.int32)
+    rc = lib.oracle_decode_split(_ptr(stream, ctypes.c_uint32), stream.size,
+                                 _ptr(indexes, ctypes.c_int32), indexes.size,
+                                 _ptr(cdf, ctypes.c_int32), _ptr(lengths, ctypes.c_int32),
+                                 _ptr(offsets, ctypes.c_int32), cdf.shape[0], cdf.shape[1],
+                                 lanes, pieces, _ptr(meta, ctypes.c_uint32),
+                                 _ptr(out, ctypes.c_int32))
+    return int(rc), out[: indexes.size]

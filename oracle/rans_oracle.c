@@ -151,18 +151,32 @@ static int symbol_puts(put_list *l, int32_t symbol, int32_t index,
     return ORACLE_OK;
 }
 
-int oracle_encode_lane(const int32_t *symbols, const int32_t *indexes,
-                       uint64_t begin, uint64_t end,
-                       const int32_t *cdf, const int32_t *lengths,
-                       const int32_t *offsets, int32_t num_tables, int32_t stride,
-                       uint32_t *out, uint64_t cap, uint64_t *words)
+/* One lane; with num_cuts > 0 it also records, for each cut position c
+ * (ascending, begin <= c <= end), the state once every position from c on
+ * has been coded and the number of words emitted so far: the state a
+ * decoder holds just before position c, and the count of lane words still
+ * unread there (split metadata). */
+static int encode_lane_cuts(const int32_t *symbols, const int32_t *indexes,
+                            uint64_t begin, uint64_t end,
+                            const int32_t *cdf, const int32_t *lengths,
+                            const int32_t *offsets, int32_t num_tables, int32_t stride,
+                            uint32_t *out, uint64_t cap, uint64_t *words,
+                            const uint64_t *cuts, uint32_t num_cuts, uint32_t *cut_meta)
 {
     put_list puts = {0, 0, 0};
     int rc = ORACLE_OK;
-    for (uint64_t i = begin; i < end && rc == ORACLE_OK; ++i)
+    /* first put of each position, and one past the last position's */
+    size_t *first = (size_t *)malloc((end - begin + 1) * sizeof(size_t));
+    if (!first)
+        return ORACLE_E_ARG;
+    for (uint64_t i = begin; i < end && rc == ORACLE_OK; ++i) {
+        first[i - begin] = puts.n;
         rc = symbol_puts(&puts, symbols[i], indexes[i], cdf, lengths, offsets,
                          num_tables, stride);
+    }
+    first[end - begin] = puts.n;
     if (rc) {
+        free(first);
         free(puts.v);
         return rc;
     }
@@ -170,30 +184,43 @@ int oracle_encode_lane(const int32_t *symbols, const int32_t *indexes,
     /* Emitted words, in emission order; at most one per put. */
     uint32_t *emitted = (uint32_t *)malloc((puts.n + 1) * sizeof(uint32_t));
     if (!emitted) {
+        free(first);
         free(puts.v);
         return ORACLE_E_ARG;
     }
     size_t ne = 0;
     uint64_t x = STATE_LOW;
-    for (size_t k = puts.n; k-- > 0;) {
-        const put_t p = puts.v[k];
-        if (p.freq == 0) {
-            /* 4-bit put: keep 16x + b below 2^63. */
-            if (x >= (1ull << (63 - BYPASS_BITS))) {
-                emitted[ne++] = (uint32_t)x;
-                x >>= 32;
+    /* positions last to first; each position's puts last to first */
+    for (uint64_t i = end + 1; i-- > begin;) {
+        if (i < end) {
+            for (size_t k = first[i + 1 - begin]; k-- > first[i - begin];) {
+                const put_t p = puts.v[k];
+                if (p.freq == 0) {
+                    /* 4-bit put: keep 16x + b below 2^63. */
+                    if (x >= (1ull << (63 - BYPASS_BITS))) {
+                        emitted[ne++] = (uint32_t)x;
+                        x >>= 32;
+                    }
+                    x = (x << BYPASS_BITS) + p.start;
+                } else {
+                    /* REG put: keep floor(x/f)*2^16 + (x mod f) + start below 2^63. */
+                    uint64_t x_max = (uint64_t)p.freq << (63 - PREC);
+                    if (x >= x_max) {
+                        emitted[ne++] = (uint32_t)x;
+                        x >>= 32;
+                    }
+                    x = (x / p.freq) * TOTAL_FREQ + (x % p.freq) + p.start;
+                }
             }
-            x = (x << BYPASS_BITS) + p.start;
-        } else {
-            /* REG put: keep floor(x/f)*2^16 + (x mod f) + start below 2^63. */
-            uint64_t x_max = (uint64_t)p.freq << (63 - PREC);
-            if (x >= x_max) {
-                emitted[ne++] = (uint32_t)x;
-                x >>= 32;
-            }
-            x = (x / p.freq) * TOTAL_FREQ + (x % p.freq) + p.start;
         }
+        for (uint32_t c = 0; c < num_cuts; ++c)
+            if (cuts[c] == i) {
+                cut_meta[3 * c] = (uint32_t)x;
+                cut_meta[3 * c + 1] = (uint32_t)(x >> 32);
+                cut_meta[3 * c + 2] = (uint32_t)ne;
+            }
     }
+    free(first);
     uint64_t total = 2 + ne;
     *words = total;
     if (total <= cap) {
@@ -207,6 +234,16 @@ int oracle_encode_lane(const int32_t *symbols, const int32_t *indexes,
     free(emitted);
     free(puts.v);
     return rc;
+}
+
+int oracle_encode_lane(const int32_t *symbols, const int32_t *indexes,
+                       uint64_t begin, uint64_t end,
+                       const int32_t *cdf, const int32_t *lengths,
+                       const int32_t *offsets, int32_t num_tables, int32_t stride,
+                       uint32_t *out, uint64_t cap, uint64_t *words)
+{
+    return encode_lane_cuts(symbols, indexes, begin, end, cdf, lengths, offsets, num_tables,
+                            stride, out, cap, words, NULL, 0, NULL);
 }
 
 typedef struct {
@@ -233,19 +270,14 @@ static int dec_bits(dec_t *d, uint32_t *b)
     return dec_refill(d);
 }
 
-int oracle_decode_lane(const uint32_t *lane, uint64_t words,
-                       const int32_t *indexes, uint64_t begin, uint64_t end,
-                       const int32_t *cdf, const int32_t *lengths,
-                       const int32_t *offsets, int32_t num_tables, int32_t stride,
-                       int32_t *symbols_out)
+/* Decode positions [begin, end) from state d->x, reading lane words from
+ * d->pos on. */
+static int decode_range(dec_t *dd, const int32_t *indexes, uint64_t begin, uint64_t end,
+                        const int32_t *cdf, const int32_t *lengths,
+                        const int32_t *offsets, int32_t num_tables, int32_t stride,
+                        int32_t *symbols_out)
 {
-    if (words < 2)
-        return ORACLE_E_CORRUPT;
-    dec_t d;
-    d.x = (uint64_t)lane[0] | ((uint64_t)lane[1] << 32);
-    d.w = lane;
-    d.pos = 2;
-    d.words = words;
+    dec_t d = *dd;
     for (uint64_t i = begin; i < end; ++i) {
         int32_t index = indexes[i];
         if (index < 0 || index >= num_tables)
@@ -297,17 +329,49 @@ int oracle_decode_lane(const uint32_t *lane, uint64_t words,
             return ORACLE_E_CORRUPT;
         symbols_out[i] = (int32_t)sym;
     }
+    *dd = d;
+    return ORACLE_OK;
+}
+
+int oracle_decode_lane(const uint32_t *lane, uint64_t words,
+                       const int32_t *indexes, uint64_t begin, uint64_t end,
+                       const int32_t *cdf, const int32_t *lengths,
+                       const int32_t *offsets, int32_t num_tables, int32_t stride,
+                       int32_t *symbols_out)
+{
+    if (words < 2)
+        return ORACLE_E_CORRUPT;
+    dec_t d;
+    d.x = (uint64_t)lane[0] | ((uint64_t)lane[1] << 32);
+    d.w = lane;
+    d.pos = 2;
+    d.words = words;
+    int rc = decode_range(&d, indexes, begin, end, cdf, lengths, offsets, num_tables, stride,
+                          symbols_out);
+    if (rc)
+        return rc;
     if (d.x != STATE_LOW || d.pos != d.words)
         return ORACLE_E_CORRUPT;
     return ORACLE_OK;
 }
 
-int oracle_encode(const int32_t *symbols, const int32_t *indexes, uint64_t n,
-                  const int32_t *cdf, const int32_t *lengths, const int32_t *offsets,
-                  int32_t num_tables, int32_t stride, uint32_t num_lanes,
-                  uint32_t *out, uint64_t cap, uint64_t *out_words)
+/* Piece s of a lane [b, e) starts at b + floor(s (e - b) / pieces). */
+static uint64_t piece_begin(uint64_t b, uint64_t e, uint32_t pieces, uint32_t s)
 {
-    if (num_lanes == 0 || (n && (!symbols || !indexes)) || !cdf || !lengths || !offsets)
+    return b + (uint64_t)(((unsigned __int128)(e - b) * s) / pieces);
+}
+
+int oracle_encode_split(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                        const int32_t *cdf, const int32_t *lengths, const int32_t *offsets,
+                        int32_t num_tables, int32_t stride, uint32_t num_lanes,
+                        uint32_t pieces, uint32_t *out, uint64_t cap, uint64_t *out_words,
+                        uint32_t *split_meta)
+{
+    if (num_lanes == 0 || pieces == 0 || (n && (!symbols || !indexes)) || !cdf || !lengths ||
+        !offsets || (pieces > 1 && !split_meta))
+        return ORACLE_E_ARG;
+    uint64_t cuts[64];
+    if (pieces > 65)
         return ORACLE_E_ARG;
     int rc = oracle_check_tables(cdf, lengths, num_tables, stride);
     if (rc)
@@ -330,8 +394,11 @@ int oracle_encode(const int32_t *symbols, const int32_t *indexes, uint64_t n,
             scratch_cap = need;
         }
         uint64_t w = 0;
-        rc = oracle_encode_lane(symbols, indexes, b, e, cdf, lengths, offsets,
-                                num_tables, stride, scratch, scratch_cap, &w);
+        for (uint32_t s = 1; s < pieces; ++s)
+            cuts[s - 1] = piece_begin(b, e, pieces, s);
+        rc = encode_lane_cuts(symbols, indexes, b, e, cdf, lengths, offsets, num_tables, stride,
+                              scratch, scratch_cap, &w, cuts, pieces - 1,
+                              pieces > 1 ? split_meta + 3ull * (pieces - 1) * j : NULL);
         if (rc) {
             free(scratch);
             return rc;
@@ -355,13 +422,23 @@ int oracle_encode(const int32_t *symbols, const int32_t *indexes, uint64_t n,
     return (cap_hit || head > cap) ? ORACLE_E_CAPACITY : ORACLE_OK;
 }
 
-int oracle_decode(const uint32_t *stream, uint64_t stream_words,
-                  const int32_t *indexes, uint64_t n,
+int oracle_encode(const int32_t *symbols, const int32_t *indexes, uint64_t n,
                   const int32_t *cdf, const int32_t *lengths, const int32_t *offsets,
                   int32_t num_tables, int32_t stride, uint32_t num_lanes,
-                  int32_t *symbols_out)
+                  uint32_t *out, uint64_t cap, uint64_t *out_words)
 {
-    if (num_lanes == 0 || !stream || (n && (!indexes || !symbols_out)))
+    return oracle_encode_split(symbols, indexes, n, cdf, lengths, offsets, num_tables, stride,
+                               num_lanes, 1, out, cap, out_words, NULL);
+}
+
+int oracle_decode_split(const uint32_t *stream, uint64_t stream_words,
+                        const int32_t *indexes, uint64_t n,
+                        const int32_t *cdf, const int32_t *lengths, const int32_t *offsets,
+                        int32_t num_tables, int32_t stride, uint32_t num_lanes,
+                        uint32_t pieces, const uint32_t *split_meta, int32_t *symbols_out)
+{
+    if (num_lanes == 0 || pieces == 0 || pieces > 65 || !stream ||
+        (n && (!indexes || !symbols_out)) || (pieces > 1 && !split_meta))
         return ORACLE_E_ARG;
     int rc = oracle_check_tables(cdf, lengths, num_tables, stride);
     if (rc)
@@ -381,13 +458,53 @@ int oracle_decode(const uint32_t *stream, uint64_t stream_words,
         uint64_t endj = stream[1 + j];
         uint64_t b = oracle_lane_begin(n, num_lanes, j);
         uint64_t e = oracle_lane_begin(n, num_lanes, j + 1);
-        rc = oracle_decode_lane(stream + head + prev, endj - prev, indexes, b, e,
-                                cdf, lengths, offsets, num_tables, stride, symbols_out);
-        if (rc)
-            return rc;
+        const uint32_t *lane = stream + head + prev;
+        uint64_t W = endj - prev;
+        /* piece s starts from the lane's flushed state (s = 0) or from its
+         * split record: the state, and the count of lane words left unread */
+        for (uint32_t s = 0; s < pieces; ++s) {
+            dec_t d;
+            d.w = lane;
+            d.words = W;
+            if (s == 0) {
+                d.x = (uint64_t)lane[0] | ((uint64_t)lane[1] << 32);
+                d.pos = 2;
+            } else {
+                const uint32_t *m = split_meta + 3ull * ((uint64_t)(pieces - 1) * j + s - 1);
+                if ((uint64_t)m[2] > W - 2)
+                    return ORACLE_E_CORRUPT;
+                d.x = (uint64_t)m[0] | ((uint64_t)m[1] << 32);
+                d.pos = W - m[2];
+            }
+            rc = decode_range(&d, indexes, piece_begin(b, e, pieces, s),
+                              piece_begin(b, e, pieces, s + 1), cdf, lengths, offsets,
+                              num_tables, stride, symbols_out);
+            if (rc)
+                return rc;
+            uint64_t want_x = STATE_LOW, want_pos = W;
+            if (s + 1 < pieces) {
+                const uint32_t *m = split_meta + 3ull * ((uint64_t)(pieces - 1) * j + s);
+                if ((uint64_t)m[2] > W - 2)
+                    return ORACLE_E_CORRUPT;
+                want_x = (uint64_t)m[0] | ((uint64_t)m[1] << 32);
+                want_pos = W - m[2];
+            }
+            if (d.x != want_x || d.pos != want_pos)
+                return ORACLE_E_CORRUPT;
+        }
         prev = endj;
     }
     return ORACLE_OK;
+}
+
+int oracle_decode(const uint32_t *stream, uint64_t stream_words,
+                  const int32_t *indexes, uint64_t n,
+                  const int32_t *cdf, const int32_t *lengths, const int32_t *offsets,
+                  int32_t num_tables, int32_t stride, uint32_t num_lanes,
+                  int32_t *symbols_out)
+{
+    return oracle_decode_split(stream, stream_words, indexes, n, cdf, lengths, offsets,
+                               num_tables, stride, num_lanes, 1, NULL, symbols_out);
 }
 
 /* ---- Quantised CDF tables ------------------------------------------------

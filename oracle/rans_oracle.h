@@ -84,6 +84,27 @@ int oracle_decode(const uint32_t *stream, uint64_t stream_words,
                   int32_t num_tables, int32_t stride, uint32_t num_lanes,
                   int32_t *symbols_out);
 
+/* Split metadata (decode parallelism beyond the lane count): every lane
+ * [b, e) is cut into `pieces` consecutive pieces, piece s starting at
+ * b + floor(s (e - b) / pieces).  For each lane j and cut s = 1 .. pieces-1,
+ * split_meta[3 ((pieces - 1) j + s - 1) + 0, 1, 2] holds the state a decoder
+ * has just before the cut position (low word, high word) and the number of
+ * the lane's words still unread there.  The container is the same as
+ * oracle_encode's.  The decoder codes each piece from its record and checks
+ * that it ends exactly at the next record (the last piece: at the flushed
+ * start state with every word read).  pieces in [1, 65]. */
+int oracle_encode_split(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                        const int32_t *cdf, const int32_t *lengths, const int32_t *offsets,
+                        int32_t num_tables, int32_t stride, uint32_t num_lanes,
+                        uint32_t pieces, uint32_t *out, uint64_t cap, uint64_t *out_words,
+                        uint32_t *split_meta);
+
+int oracle_decode_split(const uint32_t *stream, uint64_t stream_words,
+                        const int32_t *indexes, uint64_t n,
+                        const int32_t *cdf, const int32_t *lengths, const int32_t *offsets,
+                        int32_t num_tables, int32_t stride, uint32_t num_lanes,
+                        uint32_t pieces, const uint32_t *split_meta, int32_t *symbols_out);
+
 /* Quantise one pmf row of m entries (alphabet, then the escape slot) to a
  * 16-bit CDF of m + 1 entries: cdf[0] = 0, cdf[m] = 65536.  ORACLE_E_TABLE
  * for an entry outside [0, 1] or NaN; ORACLE_E_ARG for m outside [2, 65536]. */

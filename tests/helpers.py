@@ -166,3 +166,20 @@ def latent_cases():
             elif f[0] == "idx":
                 idxs.append((float(f[1]), int(f[2])))
     return syms, idxs
+
+
+def worked_splits():
+    """Cases of golden/worked_splits.txt as (case name, pieces, records [[lo, hi, left]])."""
+    out = []
+    with open(os.path.join(GOLDEN, "worked_splits.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line.startswith("split "):
+                continue
+            name, pieces, recs = [f.strip() for f in line[6:].split("|")]
+            rows = []
+            for r in recs.split(","):
+                lo, hi, left = r.split()
+                rows.append([int(lo, 16), int(hi, 16), int(left)])
+            out.append((name, int(pieces), rows))
+    return out

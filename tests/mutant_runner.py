@@ -19,7 +19,45 @@ from oracle import spec_model as sm  # noqa: E402
 import workloads as W  # noqa: E402
 from helpers import (gaussian_row_by_integration, lane_information,  # noqa: E402
                      lane_words_from_container, latent_cases, LATENT_TABLE,
-                     quantize_water_level, quantized_cases, single_table, worked_cases)
+                     quantize_water_level, quantized_cases, single_table, worked_cases,
+                     worked_splits)
+
+
+def split_pins(lib):
+    failures = []
+    cases = {c["name"]: c for c in worked_cases()}
+    for name, pieces, recs in worked_splits():
+        c = cases[name]
+        cdf, lengths, offsets = single_table(c["row"])
+        n = len(c["symbols"])
+        rc, words, meta = oracle.encode_split(np.asarray(c["symbols"]), np.zeros(n), cdf, lengths,
+                                              offsets, c["lanes"], pieces, lib=lib)
+        if rc != 0 or words.tolist() != c["words"] or meta.reshape(-1, 3).tolist() != recs:
+            failures.append(f"golden split records {name} P={pieces}")
+        rc, out = oracle.decode_split(np.asarray(c["words"], np.uint32), np.asarray(recs, np.uint32),
+                                      np.zeros(n), cdf, lengths, offsets, c["lanes"], pieces,
+                                      lib=lib)
+        if rc != 0 or out.tolist() != c["symbols"]:
+            failures.append(f"golden split decode {name} P={pieces}")
+    w = W.load("tiny")
+    for L, P in ((64, 4), (7, 8), (300, 2)):
+        rc, words, meta = oracle.encode_split(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets,
+                                              L, P, lib=lib)
+        rc0, plain = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, L, lib=lib)
+        if rc or rc0 or not np.array_equal(words, plain):
+            failures.append(f"split container differs L={L} P={P}")
+            continue
+        rc, out = oracle.decode_split(words, meta, w.indexes, w.cdf, w.lengths, w.offsets, L, P,
+                                      lib=lib)
+        if rc != 0 or not np.array_equal(out, w.symbols):
+            failures.append(f"split round trip L={L} P={P}")
+        bad = meta.copy()
+        bad[L // 2, P // 2 - 1, 0] ^= 1
+        rc, _ = oracle.decode_split(words, bad, w.indexes, w.cdf, w.lengths, w.offsets, L, P,
+                                    lib=lib)
+        if rc != oracle.E_CORRUPT:
+            failures.append(f"altered split record accepted L={L} P={P}")
+    return failures
 
 
 def latent_pins(lib):
@@ -130,6 +168,6 @@ def pins(lib):
 
 if __name__ == "__main__":
     lib = oracle.load(sys.argv[1])
-    f = pins(lib) + table_pins(lib) + latent_pins(lib)
+    f = pins(lib) + table_pins(lib) + latent_pins(lib) + split_pins(lib)
     print("\n".join(f) if f else "all pins hold")
     sys.exit(1 if f else 0)

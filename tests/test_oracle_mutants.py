@@ -46,7 +46,15 @@ MUTANTS = {
                     "int64_t mv = (int64_t)lengths[index] - 1;  /* escape slot */"),
     "dec_state_shift": ("d.x = (uint64_t)freq * (d.x >> PREC) + cum - start;",
                         "d.x = (uint64_t)freq * (d.x >> (PREC - 1)) + cum - start;"),
-    "end_check": ("if (d.x != STATE_LOW || d.pos != d.words)", "if (d.x != STATE_LOW)"),
+    "end_check": ("if (d.x != want_x || d.pos != want_pos)", "if (d.x != want_x)"),
+    # split records
+    "split_cut_ceil": ("((unsigned __int128)(e - b) * s) / pieces)",
+                       "((unsigned __int128)(e - b) * s + pieces - 1) / pieces)"),
+    "split_left_count": ("cut_meta[3 * c + 2] = (uint32_t)ne;",
+                         "cut_meta[3 * c + 2] = (uint32_t)(ne + (ne > 0));"),
+    "split_start_pos": ("d.pos = W - m[2];", "d.pos = W - m[2] + (m[2] > 0);"),
+    "split_state_half": ("cut_meta[3 * c + 1] = (uint32_t)(x >> 32);",
+                         "cut_meta[3 * c + 1] = (uint32_t)(x >> 31);"),
     # table builder
     "q_round_half_up": ("f[k] = (int64_t)rint(p * TOTAL_FREQ);",
                         "f[k] = (int64_t)floor(p * TOTAL_FREQ + 0.5);"),
