@@ -12,7 +12,10 @@ decode of the GPU container must give the input back; the CPU-baseline leg
 runs the oracle on the same workload and checks the GPU container against
 the oracle's byte for byte.
 
-The line also times the device table builder on the workload's own table
+The line also reports the decode call of the same container cut into 4
+pieces per lane by split records (rans_decode_with_splits, the records
+written by rans_encode_with_splits beside the unchanged container), and
+times the device table builder on the workload's own table
 set (64 discretised Gaussians, scales log-spaced over 0.11..256, stride
 3133), whose output must equal the workload's tables.
 
@@ -38,6 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "rANS encode/decode Gsymbol/s on 1080p y-latent (1.57M syms); % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
+SPLIT_PIECES = 4   # pieces per lane for the split-record decode figure
 
 DEFAULT_LANES = {"tiny": 64, "z": 256, "y1080": 4096, "y1080x16": 65536, "y4kx8": 131072}
 DESCRIPTION = {
@@ -83,7 +87,7 @@ def table_set():
     return scales, tail_z, 2 * int(np.ceil(hi * tail_z)) + 3   # longest row: 3133
 
 
-def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200):
+def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200, split=None):
     """The oracle as it stands (single thread) on the full workload, repeated ~10 s;
     its container and table set must equal the GPU's."""
     import numpy as np
@@ -107,6 +111,12 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
     table_us = (time.perf_counter() - t0) * 1e6
     assert rc == 0 and all(np.array_equal(a, b) for a, b in zip((cdf, lengths, offsets), gpu_tables)), \
         "GPU table set differs from the oracle's"
+    if split is not None:
+        pieces, records = split
+        rc, _, ometa = oracle.encode_split(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, lanes,
+                                           pieces)
+        assert rc == 0 and np.array_equal(ometa.reshape(-1), records), \
+            "GPU split records differ from the oracle's"
     med = statistics.median(times)
     return {
         "value": round(w.n / med / 1e9, 5),
@@ -117,7 +127,7 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
                   f"median of {len(times)} repetitions ({sum(times):.1f} s); "
                   f"{med / w.n * 1e9:.2f} ns/symbol",
         "table_build_us": round(table_us, 1),
-        "parity": "GPU container and table set equal the oracle's",
+        "parity": "GPU container, split records and table set equal the oracle's",
     }
 
 
@@ -227,6 +237,39 @@ def main():
     dec_us = statistics.mean(e[2].elapsed_time(e[3]) for e in evs) * 1e3
     value = n / (ms_per_step * 1e-3) / 1e9
 
+    # ---- split records: the same container decoded as SPLIT_PIECES pieces/lane ----
+    P = SPLIT_PIECES
+    meta = torch.empty(3 * lanes * (P - 1), dtype=torch.int32, device=dev)
+    sp_status = torch.zeros(1, dtype=torch.int32, device=dev)
+    tab_full = (vp(tables.cdf.data_ptr()), vp(tables.lengths.data_ptr()),
+                vp(tables.offsets.data_ptr()), tables.num_tables, tables.stride, lanes)
+    if lib.rans_encode_with_splits(vp(sym.data_ptr()), vp(idx.data_ptr()), n, *tab_full, P,
+                                   vp(stream.data_ptr()), cap, vp(nwords.data_ptr()),
+                                   vp(meta.data_ptr()), vp(sp_status.data_ptr()),
+                                   vp(ws.data_ptr()), ws.numel(), hs):
+        raise RuntimeError("split encode launch failed")
+    B.check(sp_status, "split encode")
+    assert int(nwords.item()) == total_words and np.array_equal(
+        stream[:total_words].cpu().numpy().view(np.uint32), gpu_words), "split container differs"
+    gpu_records = meta.cpu().numpy().view(np.uint32).copy()
+
+    def split_decode_us(pieces, reps=20):
+        args = (vp(stream.data_ptr()), cap, vp(idx.data_ptr()), n, *tab_full, pieces,
+                vp(meta.data_ptr()), vp(out.data_ptr()), vp(sp_status.data_ptr()),
+                vp(ws.data_ptr()), ws.numel(), hs)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps + 3)]
+        for e in sev:
+            e[0].record()
+            if lib.rans_decode_with_splits(*args):
+                raise RuntimeError("split decode launch failed")
+            e[1].record()
+        torch.cuda.synchronize()
+        B.check(sp_status, f"decode with {pieces} pieces")
+        assert torch.equal(out.cpu(), torch.from_numpy(w.symbols)), "split decode != input"
+        return statistics.median(a.elapsed_time(b) for a, b in sev[3:]) * 1e3
+
+    split_us, plain_call_us = split_decode_us(P), split_decode_us(1)
+
     # ---- device table builder on the workloads' table set ------------------------
     scales, tail_z, tstride = table_set()
     d_scales = torch.from_numpy(scales).to(dev)
@@ -288,6 +331,11 @@ def main():
             "algorithmic_bytes_per_launch": bytes_per_launch,
         },
         "parity": "GPU decode of the GPU container equals the input",
+        "split_decode": {"pieces": P, "records_bytes": 12 * lanes * (P - 1),
+                         "call_us": round(split_us, 2), "one_piece_call_us": round(plain_call_us, 2),
+                         "decode_gsym_s": round(n / (split_us * 1e-6) / 1e9, 3),
+                         "note": "decode call incl. its table prep; same container, "
+                                 "records beside it"},
         "table_build": {"kernel": "table_rows_kernel",
                         "workload": f"{scales.size} Gaussian rows, scales log-spaced "
                                     f"{scales[0]:g}..{scales[-1]:g}, tail mass 1e-9, "
@@ -295,7 +343,8 @@ def main():
                         "us": round(statistics.median(tab_us), 2)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, lanes, gpu_words, gpu_tables, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, lanes, gpu_words, gpu_tables, args.cpu_seconds,
+                                            split=(P, gpu_records))
         line["parity"] = line["cpu_baseline"].pop("parity")
     print(json.dumps(line), flush=True)
 

@@ -74,6 +74,7 @@ enum rans_status {
  * into several containers); beyond them a call returns RANS_E_ARG. */
 #define RANS_MAX_TABLES 4096
 #define RANS_MAX_STRIDE 16384
+#define RANS_MAX_PIECES 64
 #define RANS_MAX_SYMBOLS (1ull << 28)
 #define RANS_MAX_LANES (1u << 22)
 
@@ -129,6 +130,39 @@ int rans_decode_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
                          int32_t cdf_stride, uint32_t num_lanes, int32_t *symbols,
                          int32_t *status, void *workspace, uint64_t workspace_bytes,
                          hipStream_t hstream);
+
+/* Split records: decode parallelism beyond the lane count (torch_ans 0.3.0,
+ * "Related Projects", names Recoil, a rANS library of parallel rANS
+ * algorithms; the record format here is a reading of that idea, not
+ * Recoil's format).  The container is unchanged; beside
+ * it the encoder writes, for every lane j and every cut s = 1 .. pieces-1
+ * inside the lane, a record of three u32 at
+ *   split_meta[3 * ((pieces - 1) * j + s - 1) + 0, 1, 2]
+ * = (low word, high word) of the state a decoder holds just before position
+ *   c = b + floor(s * (e - b) / pieces) of the lane [b, e), and the number of
+ *   the lane's words still unread there.
+ * The decoder then codes each of the num_lanes * pieces pieces on its own,
+ * from its record, and checks that it ends exactly at the next record (the
+ * last piece: at the flushed start state with every word read); a piece
+ * that does not, or a record that cannot be right, gives RANS_E_CORRUPT.
+ * pieces is a power of two in [1, RANS_MAX_PIECES]; with pieces = 1 these
+ * calls are rans_encode_with_indexes / rans_decode_with_indexes and
+ * split_meta may be null.  split_meta holds 3 * num_lanes * (pieces - 1)
+ * words (device memory, caller-owned).  Other arguments as above. */
+int rans_encode_with_splits(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                            const int32_t *cdf, const int32_t *cdf_lengths, const int32_t *offsets,
+                            int32_t num_tables, int32_t cdf_stride, uint32_t num_lanes,
+                            uint32_t pieces, uint32_t *stream, uint64_t stream_capacity_words,
+                            uint64_t *stream_words, uint32_t *split_meta, int32_t *status,
+                            void *workspace, uint64_t workspace_bytes, hipStream_t hstream);
+
+int rans_decode_with_splits(const uint32_t *stream, uint64_t stream_capacity_words,
+                            const int32_t *indexes, uint64_t n,
+                            const int32_t *cdf, const int32_t *cdf_lengths,
+                            const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
+                            uint32_t num_lanes, uint32_t pieces, const uint32_t *split_meta,
+                            int32_t *symbols, int32_t *status, void *workspace,
+                            uint64_t workspace_bytes, hipStream_t hstream);
 
 /* Quantised CDF rows built on the device, one row per table (the step
  * before coding: torch_ans 0.3.0, "Parameter Setup" and "Other Features",

@@ -41,6 +41,8 @@ EXPORTS = (
     "rans_gaussian_tables",
     "rans_quantize_pmfs",
     "rans_latent_symbols",
+    "rans_encode_with_splits",
+    "rans_decode_with_splits",
     "rans_dequantize",
     "rans_status_string",
 )
@@ -99,6 +101,12 @@ def load(path: str | None = None):
         lib.rans_gaussian_tables.restype = ctypes.c_int
         lib.rans_quantize_pmfs.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
         lib.rans_quantize_pmfs.restype = ctypes.c_int
+        lib.rans_encode_with_splits.argtypes = [vp, vp, u64, vp, vp, vp, i32, i32, u32, u32, vp,
+                                                u64, vp, vp, vp, vp, u64, vp]
+        lib.rans_encode_with_splits.restype = ctypes.c_int
+        lib.rans_decode_with_splits.argtypes = [vp, u64, vp, u64, vp, vp, vp, i32, i32, u32, u32,
+                                                vp, vp, vp, vp, u64, vp]
+        lib.rans_decode_with_splits.restype = ctypes.c_int
         lib.rans_latent_symbols.argtypes = [vp, vp, vp, u64, vp, i32, vp, vp, vp]
         lib.rans_latent_symbols.restype = ctypes.c_int
         lib.rans_dequantize.argtypes = [vp, vp, u64, vp, vp]
@@ -374,3 +382,66 @@ def dequantize(symbols: torch.Tensor, means: torch.Tensor, *, out: torch.Tensor 
     rc = load().rans_dequantize(_ptr(symbols), _ptr(means), n, _ptr(out), _stream(device))
     _check_rc(rc, "rans_dequantize")
     return out
+
+
+def encode_with_splits(symbols: torch.Tensor, indexes: torch.Tensor, tables: Tables,
+                       num_lanes: int, pieces: int, *, stream_out: torch.Tensor | None = None,
+                       split_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Enqueue an encode that also writes split records (int32 [lanes, pieces - 1, 3]);
+    returns (stream, stream_words, split_records, status)."""
+    device = tables.device
+    _need(symbols, torch.int32, device, "symbols")
+    _need(indexes, torch.int32, device, "indexes")
+    n = symbols.numel()
+    if indexes.numel() != n:
+        raise ValueError("symbols and indexes differ in size")
+    if stream_out is None:
+        stream_out = torch.empty(encode_bound_words(n, num_lanes), dtype=torch.int32,
+                                 device=device)
+    if split_out is None:
+        split_out = torch.empty((num_lanes, max(pieces - 1, 0), 3), dtype=torch.int32,
+                                device=device)
+    _need(stream_out, torch.int32, device, "stream_out")
+    _need(split_out, torch.int32, device, "split_out")
+    if split_out.numel() < 3 * num_lanes * max(pieces - 1, 0):
+        raise ValueError("split_out too small")
+    stream_words = torch.zeros(1, dtype=torch.int64, device=device)
+    status = torch.zeros(1, dtype=torch.int32, device=device)
+    ws = workspace if workspace is not None else workspace_for(device).get(
+        workspace_bytes(n, num_lanes, tables.num_tables, tables.stride))
+    rc = load().rans_encode_with_splits(
+        _ptr(symbols), _ptr(indexes), n, _ptr(tables.cdf), _ptr(tables.lengths),
+        _ptr(tables.offsets), tables.num_tables, tables.stride, num_lanes, pieces,
+        _ptr(stream_out), stream_out.numel(), _ptr(stream_words), _ptr(split_out), _ptr(status),
+        _ptr(ws), ws.numel(), _stream(device))
+    _check_rc(rc, "rans_encode_with_splits")
+    return stream_out, stream_words, split_out, status
+
+
+def decode_with_splits(stream: torch.Tensor, split_records: torch.Tensor, indexes: torch.Tensor,
+                       tables: Tables, num_lanes: int, pieces: int, *,
+                       symbols_out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None,
+                       capacity_words: int | None = None):
+    """Enqueue a decode of every lane as `pieces` pieces; returns (symbols, status)."""
+    device = tables.device
+    _need(stream, torch.int32, device, "stream")
+    _need(split_records, torch.int32, device, "split_records")
+    _need(indexes, torch.int32, device, "indexes")
+    if split_records.numel() < 3 * num_lanes * max(pieces - 1, 0):
+        raise ValueError("split_records too small")
+    n = indexes.numel()
+    if symbols_out is None:
+        symbols_out = torch.empty(n, dtype=torch.int32, device=device)
+    _need(symbols_out, torch.int32, device, "symbols_out")
+    status = torch.zeros(1, dtype=torch.int32, device=device)
+    cap = stream.numel() if capacity_words is None else int(capacity_words)
+    ws = workspace if workspace is not None else workspace_for(device).get(
+        workspace_bytes(n, num_lanes, tables.num_tables, tables.stride))
+    rc = load().rans_decode_with_splits(
+        _ptr(stream), cap, _ptr(indexes), n, _ptr(tables.cdf), _ptr(tables.lengths),
+        _ptr(tables.offsets), tables.num_tables, tables.stride, num_lanes, pieces,
+        _ptr(split_records), _ptr(symbols_out), _ptr(status), _ptr(ws), ws.numel(),
+        _stream(device))
+    _check_rc(rc, "rans_decode_with_splits")
+    return symbols_out, status

@@ -34,6 +34,15 @@ bool sizes_ok(uint64_t n, uint32_t lanes)
 
 int launched(hipError_t e) { return e == hipSuccess ? RANS_OK : RANS_E_HIP; }
 
+// log2 of a piece count: a power of two in [1, RANS_MAX_PIECES], else -1
+int pieces_log2_of(uint32_t pieces)
+{
+    for (int l = 0; (1u << l) <= RANS_MAX_PIECES; ++l)
+        if (pieces == (1u << l))
+            return l;
+    return -1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -157,6 +166,66 @@ int rans_decode_with_indexes(const uint32_t *stream, uint64_t stream_capacity_wo
     return rans_decode_prepared(stream, stream_capacity_words, indexes, n, num_tables,
                                 cdf_stride, num_lanes, symbols, status, workspace,
                                 workspace_bytes, hstream);
+}
+
+int rans_encode_with_splits(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                            const int32_t *cdf, const int32_t *cdf_lengths, const int32_t *offsets,
+                            int32_t num_tables, int32_t cdf_stride, uint32_t num_lanes,
+                            uint32_t pieces, uint32_t *stream, uint64_t stream_capacity_words,
+                            uint64_t *stream_words, uint32_t *split_meta, int32_t *status,
+                            void *workspace, uint64_t workspace_bytes, hipStream_t hstream)
+{
+    const int pl = pieces_log2_of(pieces);
+    if (pl < 0 || (pieces > 1 && !split_meta))
+        return RANS_E_ARG;
+    if (num_lanes == 0 || !stream || !stream_words || !status || (n && (!symbols || !indexes)))
+        return RANS_E_ARG;
+    if (!sizes_ok(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
+        return RANS_E_ARG;
+    int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
+    if (rc)
+        return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes,
+                              rans_workspace_bytes(n, num_lanes, num_tables, cdf_stride))))
+        return rc;
+    if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
+                                  workspace_bytes, hstream)))
+        return rc;
+    EncodeArgs a{symbols, indexes, n, num_lanes, num_tables, stream, stream_capacity_words,
+                 stream_words, status, static_cast<uint8_t *>(workspace)};
+    a.pieces_log2 = (uint32_t)pl;
+    a.split_meta = pl ? split_meta : nullptr;
+    return launched(launch_encode(a, hstream));
+}
+
+int rans_decode_with_splits(const uint32_t *stream, uint64_t stream_capacity_words,
+                            const int32_t *indexes, uint64_t n,
+                            const int32_t *cdf, const int32_t *cdf_lengths,
+                            const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
+                            uint32_t num_lanes, uint32_t pieces, const uint32_t *split_meta,
+                            int32_t *symbols, int32_t *status, void *workspace,
+                            uint64_t workspace_bytes, hipStream_t hstream)
+{
+    const int pl = pieces_log2_of(pieces);
+    if (pl < 0 || (pieces > 1 && !split_meta))
+        return RANS_E_ARG;
+    if (num_lanes == 0 || !stream || !status || (n && (!symbols || !indexes)))
+        return RANS_E_ARG;
+    if (!sizes_ok(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
+        return RANS_E_ARG;
+    int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
+    if (rc)
+        return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes, ws_flags_offset())))
+        return rc;
+    if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
+                                  workspace_bytes, hstream)))
+        return rc;
+    DecodeArgs a{stream, stream_capacity_words, indexes, n, num_lanes, num_tables, symbols,
+                 status, static_cast<uint8_t *>(workspace)};
+    a.pieces_log2 = (uint32_t)pl;
+    a.split_meta = pl ? split_meta : nullptr;
+    return launched(launch_decode(a, hstream));
 }
 
 int rans_gaussian_tables(const double *scales, int32_t num_tables, double tail_z,

@@ -255,7 +255,7 @@ __device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_
     wd.next = wd.at(wd.pos);
 }
 
-template <int TPB, int CW>
+template <int TPB, int CW, bool SPLIT>
 __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -297,54 +297,84 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     if (herr && blockIdx.x == 0 && tid == 0)
         record_error(hdr, herr);
 
-    // the wave codes lanes j0 .. j0 + lpw - 1, one per wavefront lane
-    const uint32_t lpw = dec_lanes_per_wave(L);
+    // Work units: lane j's pieces u = j * 2^pl + s (one piece per lane
+    // without split records).  The wave codes units u0 .. u0 + lpw - 1, one
+    // per wavefront lane.
+    const uint32_t pl = SPLIT ? a.pieces_log2 : 0u;
+    const uint32_t LV = L << pl;
+    const uint32_t lpw = dec_lanes_per_wave(LV);
     const uint32_t lane = tid & (kWave - 1);
     const uint32_t wave = tid / kWave;   // coding waves are 0 .. CW-1
-    const uint32_t j0 = __builtin_amdgcn_readfirstlane((blockIdx.x * CW + wave) * lpw);
-    const uint32_t j = j0 + lane;
+    const uint32_t u0 = __builtin_amdgcn_readfirstlane((blockIdx.x * CW + wave) * lpw);
+    const uint32_t u = u0 + lane;
+    const uint32_t j = u >> pl;            // the unit's lane
+    const uint32_t ps = u & ((1u << pl) - 1);   // and piece
+    // first position of unit v (v = LV gives n)
+    auto unit_begin = [&](uint32_t v) -> uint64_t {
+        const uint32_t lj = v >> pl;
+        const uint64_t lb = lane_begin(a.n, L, lj);
+        return lj < L ? piece_begin(lb, lane_begin(a.n, L, lj + 1), pl, v & ((1u << pl) - 1)) : lb;
+    };
     // the wave's index and symbol spans, and its stream words, as buffers
-    if (!herr && wave < CW && j0 < L) {
-        const uint32_t j1 = min(j0 + lpw, L);
-        const uint64_t bw = lane_begin(a.n, L, j0), ew = lane_begin(a.n, L, j1);
+    if (!herr && wave < CW && u0 < LV) {
+        const uint32_t u1 = min(u0 + lpw, LV);
+        const uint64_t bw = unit_begin(u0), ew = unit_begin(u1);
         const Rsrc ridx = make_rsrc(a.indexes + bw, (uint32_t)(4 * (ew - bw)));
         const Rsrc rout = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
-        const uint64_t wbase = j0 ? a.stream[j0] : 0u;   // the wave's first word
+        const uint32_t jw = u0 >> pl;   // the wave's first lane
+        const uint64_t wbase = jw ? a.stream[jw] : 0u;   // the wave's first word
         const uint64_t wavail = a.capacity - 1 - L;
         const uint64_t wbytes = wbase < wavail ? min(4 * (wavail - wbase), 1ull << 31) : 0;
         const Rsrc rstr = make_rsrc(a.stream + 1 + L + (wbase < wavail ? wbase : 0), (uint32_t)wbytes);
-        if (lane < lpw && j < L) {
+        if (lane < lpw && u < LV) {
             int lerr = 0;
             const uint64_t beg_w = j ? a.stream[j] : 0u;
             const uint64_t end_w = a.stream[1 + j];
+            // the piece's start and end: word offset in the lane and state
+            // (piece 0 starts after the flushed state; the last piece ends
+            // at the start state with every word read)
+            const uint32_t W = (uint32_t)(end_w - beg_w);
+            const uint32_t *rec = a.split_meta + 3ull * ((uint64_t)((1u << pl) - 1) * j + ps);
+            uint32_t left0 = W - 2, left1 = 0;
+            if (ps)
+                left0 = rec[-1];
+            if (ps + 1 < (1u << pl))
+                left1 = rec[2];
+            const bool bad_rec = left0 > W - 2 || left1 > left0;
             if (a.stream[0] != L || end_w < beg_w + 2 || 1ull + L + end_w > a.capacity ||
-                beg_w < wbase) {
+                beg_w < wbase || bad_rec) {
                 lerr = RANS_E_CORRUPT;
             } else {
                 Words<TPB> wd;
                 wd.w = a.stream + 1 + L + beg_w;
                 wd.ring = ring;
-                wd.count = (uint32_t)(end_w - beg_w);
+                wd.count = W;
+                const uint32_t o = W - left0;   // the piece's first unread word
                 const uint32_t lw = (uint32_t)(4 * (beg_w - wbase));   // the lane's words in rstr
-                // words 0, 1: the final state; words [2, 2 + kDecRing): the first ring fill
-                const u32x4 w0 = buf_load4(rstr, lw), w1 = buf_load4(rstr, lw + 16);
-                const u32x4 w2 = buf_load4(rstr, lw + 32);
-                uint64_t x = (uint64_t)w0[0] | ((uint64_t)w0[1] << 32);
+                // words o-2, o-1 (piece 0: the final state) and [o, o + kDecRing): the
+                // first ring fill
+                const uint32_t lo = lw + 4 * (o - 2);
+                const u32x4 w0 = buf_load4(rstr, lo), w1 = buf_load4(rstr, lo + 16);
+                const u32x4 w2 = buf_load4(rstr, lo + 32);
+                uint64_t x = ps ? ((uint64_t)rec[-3] | ((uint64_t)rec[-2] << 32))
+                                : ((uint64_t)w0[0] | ((uint64_t)w0[1] << 32));
+                const uint64_t x_end = ps + 1 < (1u << pl) ? ((uint64_t)rec[0] | ((uint64_t)rec[1] << 32))
+                                                           : kStateLow;
                 {
                     static_assert(kDecRing == 8, "ring fill below assumes 8 slots");
                     const uint32_t v[kDecRing] = {w0[2], w0[3], w1[0], w1[1], w1[2], w1[3], w2[0], w2[1]};
 #pragma unroll
                     for (uint32_t k = 0; k < kDecRing; ++k)
-                        wd.put(2 + k, v[k]);
+                        wd.put(o + k, v[k]);
                 }
-                wd.pos = 2;
-                wd.filled = min(wd.count, 2u + kDecRing);
-                wd.next = wd.at(2);
+                wd.pos = o;
+                wd.filled = min(wd.count, o + kDecRing);
+                wd.next = wd.at(o);
                 uint32_t pend[kRefill];
                 uint32_t pend_at = wd.filled;
 
-                const uint64_t b = lane_begin(a.n, L, j);
-                const uint64_t e = lane_begin(a.n, L, j + 1);
+                const uint64_t b = unit_begin(u);
+                const uint64_t e = unit_begin(u + 1);
                 const uint32_t nj = (uint32_t)(e - b);
                 const uint32_t ob = (uint32_t)(4 * (b - bw));   // the lane's first position
                 // Two index buffers used in turn (no register copies between
@@ -456,7 +486,7 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
                     round(ia, k0);
                     round(ib, k0 + kRound);
                 }
-                if (!lerr && (x != kStateLow || wd.pos != wd.count))
+                if (!lerr && (x != x_end || wd.pos != W - left1))
                     lerr = RANS_E_CORRUPT;
             }
             if (lerr)
@@ -481,17 +511,17 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     }
 }
 
-template <int TPB, int CW>
+template <int TPB, int CW, bool SPLIT>
 hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s)
 {
     const uint32_t lds_bytes = decode_lds_bytes(TPB);
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&decode_kernel<TPB, CW>),
+        reinterpret_cast<const void *>(&decode_kernel<TPB, CW, SPLIT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (attr != hipSuccess)
         return attr;
-    const uint32_t blocks = (dec_waves(a.lanes) + CW - 1) / CW;
-    hipLaunchKernelGGL((decode_kernel<TPB, CW>), dim3(blocks), dim3(TPB), lds_bytes, s, a);
+    const uint32_t blocks = (dec_waves(a.lanes << a.pieces_log2) + CW - 1) / CW;
+    hipLaunchKernelGGL((decode_kernel<TPB, CW, SPLIT>), dim3(blocks), dim3(TPB), lds_bytes, s, a);
     return hipGetLastError();
 }
 
@@ -499,9 +529,12 @@ hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s)
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
 {
-    if (coding_one_per_cu(dec_waves(a.lanes)))
-        return launch_decode_t<4 * kWave, 1>(a, s);
-    return launch_decode_t<8 * kWave, 8>(a, s);
+    // decoding split pieces is its own instantiation (the plain decoder
+    // carries none of the piece bookkeeping)
+    const bool one = coding_one_per_cu(dec_waves(a.lanes << a.pieces_log2));
+    if (a.pieces_log2 > 0)
+        return one ? launch_decode_t<4 * kWave, 1, true>(a, s) : launch_decode_t<8 * kWave, 8, true>(a, s);
+    return one ? launch_decode_t<4 * kWave, 1, false>(a, s) : launch_decode_t<8 * kWave, 8, false>(a, s);
 }
 
 }  // namespace rans

@@ -251,6 +251,25 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
                 sp.capb = 4 * (2 * nj + 4);
                 sp.overflow = false;
                 uint64_t x = kStateLow;
+                // Split records: the next cut to record (cuts are met last to
+                // first) and the step k = nj - 1 - (c - b) at which position c
+                // is coded; a round holding it takes the per-position path,
+                // which records the state and the words emitted so far right
+                // after that position.
+                const uint32_t npieces = 1u << a.pieces_log2;
+                int32_t cut_s = (int32_t)npieces - 1;
+                auto cut_step = [&](int32_t s) -> uint32_t {
+                    return nj - 1 - (uint32_t)(piece_begin(b, e, a.pieces_log2, (uint32_t)s) - b);
+                };
+                uint32_t cut_k = (npieces > 1 && nj > 0) ? cut_step(cut_s) : ~0u;
+                auto record_cut = [&]() {
+                    uint32_t *m = a.split_meta + 3ull * ((uint64_t)(npieces - 1) * j + cut_s - 1);
+                    m[0] = (uint32_t)x;
+                    m[1] = (uint32_t)(x >> 32);
+                    m[2] = sp.cb >> 2;
+                    --cut_s;
+                    cut_k = (cut_s >= 1 && nj > 0) ? cut_step(cut_s) : ~0u;
+                };
                 // byte offsets of the lane's positions in the wave's buffers;
                 // positions are coded last to first, clamped at the lane start
                 const int32_t plast = (int32_t)(4 * (int64_t)(e - bw) - 4);
@@ -359,7 +378,7 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
                         x = need ? (x >> 32) : x;
                         x = reg_step(x, P.start[u], P.f[u], P.rcp[u]);
                     }
-                    if (__builtin_expect(!__all(P.all & room), 0)) {
+                    if (__builtin_expect(!__all(P.all & room & (cut_k >= k0 + kRound)), 0)) {
                         x = x0;
                         sp.cb = cb_start;
                         // the fast step is committed where it applies; the other
@@ -383,6 +402,8 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
                                     lerr = lerr ? lerr : ec;
                                 }
                             }
+                            while (cut_k == k0 + u)   // (cuts may share a position)
+                                record_cut();
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -413,6 +434,8 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
                     round(pa, k0, sb, ib, pb);
                     round(pb, k0 + kRound, sa, ia, pa);
                 }
+                while (cut_s >= 1)   // an empty lane: every cut holds the start state
+                    record_cut();
                 if (sp.overflow) {
                     lerr = lerr ? lerr : RANS_E_CAPACITY;
                     sp.cb = sp.capb - 8;

@@ -294,6 +294,10 @@ struct EncodeArgs {
     uint64_t *stream_words;
     int32_t *status;
     uint8_t *ws;
+    // split records: each lane cut into 2^pieces_log2 pieces, records
+    // [L][pieces - 1][3] = (state low, state high, lane words left unread)
+    uint32_t pieces_log2;
+    uint32_t *split_meta;
 };
 
 struct DecodeArgs {
@@ -306,7 +310,22 @@ struct DecodeArgs {
     int32_t *symbols;
     int32_t *status;
     uint8_t *ws;
+    // with pieces_log2 > 0, every lane decodes as 2^pieces_log2 pieces, each
+    // from its split record (same layout as the encoder writes)
+    uint32_t pieces_log2;
+    const uint32_t *split_meta;
 };
+
+// Piece s of a lane [b, e) cut into 2^pieces_log2 pieces starts at
+// b + floor(s (e - b) / 2^pieces_log2).
+inline __host__ __device__ uint64_t piece_begin(uint64_t b, uint64_t e, uint32_t pieces_log2,
+                                                uint32_t s)
+{
+    const uint64_t len = e - b;
+    const uint32_t sh = pieces_log2;
+    // s < 2^sh: split the product to stay within 64 bits
+    return b + (len >> sh) * s + (((len & ((1ull << sh) - 1)) * s) >> sh);
+}
 
 hipError_t launch_prep(const PrepArgs &a, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);

@@ -75,6 +75,8 @@ def _rows(path_glob: str):
 
 
 def _kernel_key(name: str) -> str:
+    if re.search(r"decode_kernel<[^>]*true>", name):
+        return "decode_kernel_split"
     m = re.search(r"(encode_kernel|decode_kernel|prep_kernel|table_rows_kernel|"
                   r"latent_symbols_kernel|dequantize_kernel)", name)
     if m:
@@ -101,21 +103,30 @@ def counter_per_dispatch(path_glob: str, counter: str) -> dict:
 def summarize_main(a) -> None:
     os.makedirs(a.out, exist_ok=True)
     if a.stats:
+        # per kernel and launch shape (grid size): one kernel launched with
+        # two shapes (the decoder with and without split pieces) is two rows
         rows = _rows(a.stats)
-        lines = [f"# rocprofv3 kernel trace statistics: {a.label}", f"# command: {a.command}", "",
-                 f"{'kernel':<52s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
+        groups = {}
         for r in rows:
-            name = r["Name"]
+            name = r["Kernel_Name"]
             if not re.search(r"rans|kernel", name):
                 continue
-            lines.append(f"{name[:52]:<52s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
-                         f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+            key = (name, int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+            groups.setdefault(key, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines = [f"# rocprofv3 kernel trace statistics: {a.label}", f"# command: {a.command}", "",
+                 f"{'kernel':<52s} {'blocks':>7s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} "
+                 f"{'max_us':>10s}"]
+        for (name, blocks), d in sorted(groups.items(), key=lambda kv: -statistics.mean(kv[1])):
+            short = re.sub(r"^void |\(anonymous namespace\)::|\(.*\)$", "", name)[:52]
+            lines.append(f"{short:<52s} {blocks:7d} {len(d):6d} {statistics.mean(d):10.2f} "
+                         f"{min(d):10.2f} {max(d):10.2f}")
         if a.bench_json:
             with open(a.bench_json) as fh:
                 bench = [json.loads(l) for l in fh if l.strip().startswith("{")][-1]
             lines += ["", "# bench.py line of the same run (kernel_us from HIP events):",
                       json.dumps({k: bench[k] for k in ("value", "unit", "ms_per_step", "kernel_us",
-                                              "table_build") if k in bench})]
+                                              "split_decode", "table_build") if k in bench})]
         path = os.path.join(a.out, f"kernel_trace_{a.label}.txt")
         with open(path, "w") as fh:
             fh.write("\n".join(lines) + "\n")

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     from learned_image_compression_amd import binding as B
     assert sorted(B.EXPORTS) == names
     for name in names:
@@ -188,3 +188,11 @@ def test_dequantize_host_checks(lib, kw, code):
     a = dict(sym=1, means=1, n=100, out=1)
     a.update(kw)
     assert lib.rans_dequantize(a["sym"], a["means"], a["n"], a["out"], 0) == code
+
+
+@pytest.mark.parametrize("pieces,meta,code", [(0, 1, -1), (3, 1, -1), (128, 1, -1), (4, 0, -1)])
+def test_split_calls_check_pieces_on_host(lib, pieces, meta, code):
+    assert lib.rans_encode_with_splits(1, 1, 10, 1, 1, 1, 8, 3133, 4, pieces, 1, 1000, 1, meta, 1,
+                                       256, 1 << 30, 0) == code
+    assert lib.rans_decode_with_splits(1, 1000, 1, 10, 1, 1, 1, 8, 3133, 4, pieces, meta, 1, 1,
+                                       256, 1 << 30, 0) == code
