@@ -69,6 +69,12 @@ def _bind(lib):
     lib.oracle_decode_split.argtypes = [u32p, u64, i32p, u64, i32p, i32p, i32p, i32, i32, u32,
                                         u32, u32p, i32p]
     lib.oracle_decode_split.restype = ctypes.c_int
+    lib.oracle_encode_interleaved.argtypes = [i32p, i32p, u64, i32p, i32p, i32p, i32, i32, u32,
+                                              u32, u32p, u64, u64p]
+    lib.oracle_encode_interleaved.restype = ctypes.c_int
+    lib.oracle_decode_interleaved.argtypes = [u32p, u64, i32p, u64, i32p, i32p, i32p, i32, i32,
+                                              u32, u32, i32p]
+    lib.oracle_decode_interleaved.restype = ctypes.c_int
     f32p = ctypes.POINTER(ctypes.c_float)
     lib.oracle_latent_symbols.argtypes = [f32p, f32p, f32p, u64, f32p, i32, i32p, i32p]
     lib.oracle_latent_symbols.restype = ctypes.c_int
@@ -276,4 +282,41 @@ def decode_split(stream, split_meta, indexes, cdf, lengths, offsets, lanes: int,
                                  _ptr(offsets, ctypes.c_int32), cdf.shape[0], cdf.shape[1],
                                  lanes, pieces, _ptr(meta, ctypes.c_uint32),
                                  _ptr(out, ctypes.c_int32))
+    return int(rc), out[: indexes.size]
+
+
+def encode_interleaved(symbols, indexes, cdf, lengths, offsets, streams: int, width: int,
+                       capacity: int | None = None, lib=None):
+    """Return (status, words) of the interleaved-stream container."""
+    lib = lib or load()
+    symbols = np.ascontiguousarray(symbols, dtype=np.int32)
+    indexes = np.ascontiguousarray(indexes, dtype=np.int32)
+    cdf, lengths, offsets = _tables(cdf, lengths, offsets)
+    n = symbols.size
+    if capacity is None:
+        capacity = 1 + streams * (1 + 2 * width) + 10 * n
+    out = np.zeros(max(capacity, 1), dtype=np.uint32)
+    total = ctypes.c_uint64(0)
+    rc = lib.oracle_encode_interleaved(_ptr(symbols, ctypes.c_int32), _ptr(indexes, ctypes.c_int32),
+                                       n, _ptr(cdf, ctypes.c_int32), _ptr(lengths, ctypes.c_int32),
+                                       _ptr(offsets, ctypes.c_int32), cdf.shape[0], cdf.shape[1],
+                                       streams, width, _ptr(out, ctypes.c_uint32), capacity,
+                                       ctypes.byref(total))
+    if rc != OK:
+        return int(rc), out[:0]
+    return 0, out[: total.value].copy()
+
+
+def decode_interleaved(stream, indexes, cdf, lengths, offsets, streams: int, width: int, lib=None):
+    """Return (status, symbols)."""
+    lib = lib or load()
+    stream = np.ascontiguousarray(stream, dtype=np.uint32)
+    indexes = np.ascontiguousarray(indexes, dtype=np.int32)
+    cdf, lengths, offsets = _tables(cdf, lengths, offsets)
+    out = np.zeros(max(indexes.size, 1), dtype=np.int32)
+    rc = lib.oracle_decode_interleaved(_ptr(stream, ctypes.c_uint32), stream.size,
+                                       _ptr(indexes, ctypes.c_int32), indexes.size,
+                                       _ptr(cdf, ctypes.c_int32), _ptr(lengths, ctypes.c_int32),
+                                       _ptr(offsets, ctypes.c_int32), cdf.shape[0], cdf.shape[1],
+                                       streams, width, _ptr(out, ctypes.c_int32))
     return int(rc), out[: indexes.size]

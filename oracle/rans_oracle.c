@@ -151,6 +151,28 @@ static int symbol_puts(put_list *l, int32_t symbol, int32_t index,
     return ORACLE_OK;
 }
 
+/* Apply one put to state *x (S3), appending the word a renormalisation
+ * emits to emitted[*ne]. */
+static void apply_put(uint64_t *x, put_t p, uint32_t *emitted, size_t *ne)
+{
+    if (p.freq == 0) {
+        /* 4-bit put: keep 16x + b below 2^63. */
+        if (*x >= (1ull << (63 - BYPASS_BITS))) {
+            emitted[(*ne)++] = (uint32_t)*x;
+            *x >>= 32;
+        }
+        *x = (*x << BYPASS_BITS) + p.start;
+    } else {
+        /* REG put: keep floor(x/f)*2^16 + (x mod f) + start below 2^63. */
+        uint64_t x_max = (uint64_t)p.freq << (63 - PREC);
+        if (*x >= x_max) {
+            emitted[(*ne)++] = (uint32_t)*x;
+            *x >>= 32;
+        }
+        *x = (*x / p.freq) * TOTAL_FREQ + (*x % p.freq) + p.start;
+    }
+}
+
 /* One lane; with num_cuts > 0 it also records, for each cut position c
  * (ascending, begin <= c <= end), the state once every position from c on
  * has been coded and the number of words emitted so far: the state a
@@ -193,25 +215,8 @@ static int encode_lane_cuts(const int32_t *symbols, const int32_t *indexes,
     /* positions last to first; each position's puts last to first */
     for (uint64_t i = end + 1; i-- > begin;) {
         if (i < end) {
-            for (size_t k = first[i + 1 - begin]; k-- > first[i - begin];) {
-                const put_t p = puts.v[k];
-                if (p.freq == 0) {
-                    /* 4-bit put: keep 16x + b below 2^63. */
-                    if (x >= (1ull << (63 - BYPASS_BITS))) {
-                        emitted[ne++] = (uint32_t)x;
-                        x >>= 32;
-                    }
-                    x = (x << BYPASS_BITS) + p.start;
-                } else {
-                    /* REG put: keep floor(x/f)*2^16 + (x mod f) + start below 2^63. */
-                    uint64_t x_max = (uint64_t)p.freq << (63 - PREC);
-                    if (x >= x_max) {
-                        emitted[ne++] = (uint32_t)x;
-                        x >>= 32;
-                    }
-                    x = (x / p.freq) * TOTAL_FREQ + (x % p.freq) + p.start;
-                }
-            }
+            for (size_t k = first[i + 1 - begin]; k-- > first[i - begin];)
+                apply_put(&x, puts.v[k], emitted, &ne);
         }
         for (uint32_t c = 0; c < num_cuts; ++c)
             if (cuts[c] == i) {
@@ -677,4 +682,274 @@ int oracle_dequantize(const int32_t *symbols, const float *means, uint64_t n, fl
     for (uint64_t i = 0; i < n; ++i)
         y_hat[i] = (float)symbols[i] + means[i];
     return ORACLE_OK;
+}
+
+/* ---- Interleaved streams -------------------------------------------------
+ *
+ * The pages' fastest GPU decoder codes one stream per warp with one state
+ * per warp lane and one shared word cursor, in a layout the CPU coder shares
+ * word for word (torch_ans 0.3.0, "Usage" legend, Interleaved States).
+ * Readings for the rans64 format here:
+ *   IL1 the n symbols form S streams, stream t = [floor(t n / S),
+ *       floor((t+1) n / S));
+ *   IL2 symbol k of a stream (k from 0) is coded by state k mod W; every
+ *       state starts at 2^31; a step is W consecutive symbols;
+ *   IL3 a decoder takes the steps in order; within a step the put slots in
+ *       order (slot 0 is every symbol's REG put, later slots the bypass puts
+ *       of escaping symbols, in their S2 order); within a slot the states in
+ *       ascending order; each put is followed by its renormalisation, which
+ *       may read the next word from the stream's one shared cursor.  The
+ *       encoder applies the puts in exactly the reverse order, so its
+ *       emitted words, reversed, are the decoder's reading order;
+ *   IL4 a stream is [x_0 low, x_0 high, .., x_{W-1} low, x_{W-1} high] (the
+ *       final states in state order) followed by the words in reading
+ *       order; the container is [S, end_0 .. end_{S-1}] and the streams, as
+ *       for lanes;
+ *   IL5 a clean decode leaves every state at 2^31 with every word read.
+ * With W = 1 a stream is exactly a lane stream, and the container the lane
+ * container with S lanes. */
+
+#define MAX_PUTS 16   /* a symbol makes at most 10 puts (REG, count, 8 groups) */
+
+int oracle_encode_interleaved(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                              const int32_t *cdf, const int32_t *lengths,
+                              const int32_t *offsets, int32_t num_tables, int32_t stride,
+                              uint32_t num_streams, uint32_t width, uint32_t *out, uint64_t cap,
+                              uint64_t *out_words)
+{
+    if (num_streams == 0 || width == 0 || width > 1024 || (n && (!symbols || !indexes)))
+        return ORACLE_E_ARG;
+    int rc = oracle_check_tables(cdf, lengths, num_tables, stride);
+    if (rc)
+        return rc;
+    uint64_t head = 1 + (uint64_t)num_streams;
+    uint64_t used = 0;
+    int cap_hit = 0;
+    uint64_t *x = (uint64_t *)malloc(width * sizeof(uint64_t));
+    put_t *step_puts = (put_t *)malloc((size_t)width * MAX_PUTS * sizeof(put_t));
+    uint32_t *nputs = (uint32_t *)malloc(width * sizeof(uint32_t));
+    if (!x || !step_puts || !nputs) {
+        free(x); free(step_puts); free(nputs);
+        return ORACLE_E_ARG;
+    }
+    for (uint32_t t = 0; t < num_streams && rc == ORACLE_OK; ++t) {
+        uint64_t b = oracle_lane_begin(n, num_streams, t);
+        uint64_t e = oracle_lane_begin(n, num_streams, t + 1);
+        uint64_t m = e - b;
+        /* at most one word per put */
+        uint32_t *emitted = (uint32_t *)malloc((10 * m + 1) * sizeof(uint32_t));
+        if (!emitted) {
+            rc = ORACLE_E_ARG;
+            break;
+        }
+        size_t ne = 0;
+        for (uint32_t l = 0; l < width; ++l)
+            x[l] = STATE_LOW;
+        uint64_t steps = (m + width - 1) / width;
+        for (uint64_t g = steps; g-- > 0 && rc == ORACLE_OK;) {
+            /* the step's puts, per state */
+            uint32_t max_slot = 0;
+            for (uint32_t l = 0; l < width; ++l) {
+                nputs[l] = 0;
+                uint64_t k = g * width + l;
+                if (k >= m)
+                    continue;
+                put_list one = {0, 0, 0};
+                rc = symbol_puts(&one, symbols[b + k], indexes[b + k], cdf, lengths, offsets,
+                                 num_tables, stride);
+                if (rc == ORACLE_OK && one.n > MAX_PUTS)
+                    rc = ORACLE_E_ARG;
+                if (rc == ORACLE_OK) {
+                    memcpy(step_puts + (size_t)l * MAX_PUTS, one.v, one.n * sizeof(put_t));
+                    nputs[l] = (uint32_t)one.n;
+                    if (one.n > max_slot)
+                        max_slot = (uint32_t)one.n;
+                }
+                free(one.v);
+                if (rc)
+                    break;
+            }
+            /* slots last to first, states last to first */
+            for (uint32_t s = max_slot; s-- > 0 && rc == ORACLE_OK;) {
+                for (uint32_t l = width; l-- > 0;) {
+                    if (s >= nputs[l])
+                        continue;
+                    apply_put(&x[l], step_puts[(size_t)l * MAX_PUTS + s], emitted, &ne);
+                }
+            }
+        }
+        if (rc == ORACLE_OK) {
+            uint64_t w = 2ull * width + ne;
+            if (head + used + w <= cap && !cap_hit) {
+                uint32_t *o = out + head + used;
+                for (uint32_t l = 0; l < width; ++l) {
+                    o[2 * l] = (uint32_t)x[l];
+                    o[2 * l + 1] = (uint32_t)(x[l] >> 32);
+                }
+                for (size_t k = 0; k < ne; ++k)
+                    o[2 * width + k] = emitted[ne - 1 - k];
+            } else {
+                cap_hit = 1;
+            }
+            used += w;
+            if (used > 0xFFFFFFFFull)
+                rc = ORACLE_E_ARG;
+            if (1 + t < cap)
+                out[1 + t] = (uint32_t)used;
+        }
+        free(emitted);
+    }
+    free(x); free(step_puts); free(nputs);
+    if (rc)
+        return rc;
+    if (cap >= 1)
+        out[0] = num_streams;
+    *out_words = head + used;
+    return (cap_hit || head > cap) ? ORACLE_E_CAPACITY : ORACLE_OK;
+}
+
+/* Decoder side of one symbol, one put at a time: the phase of state l says
+ * which put comes next (0: REG; 1: a count nibble; 2: a group nibble). */
+typedef struct {
+    int phase;
+    int32_t index;
+    int64_t slot, mv;
+    uint32_t nb, got;
+    uint64_t raw;
+} il_sym_t;
+
+int oracle_decode_interleaved(const uint32_t *stream, uint64_t stream_words,
+                              const int32_t *indexes, uint64_t n,
+                              const int32_t *cdf, const int32_t *lengths,
+                              const int32_t *offsets, int32_t num_tables, int32_t stride,
+                              uint32_t num_streams, uint32_t width, int32_t *symbols_out)
+{
+    if (num_streams == 0 || width == 0 || width > 1024 || !stream ||
+        (n && (!indexes || !symbols_out)))
+        return ORACLE_E_ARG;
+    int rc = oracle_check_tables(cdf, lengths, num_tables, stride);
+    if (rc)
+        return rc;
+    uint64_t head = 1 + (uint64_t)num_streams;
+    if (stream_words < head || stream[0] != num_streams)
+        return ORACLE_E_CORRUPT;
+    uint64_t prev = 0;
+    for (uint32_t t = 0; t < num_streams; ++t) {
+        uint64_t endt = stream[1 + t];
+        if (endt < prev + 2ull * width || head + endt > stream_words)
+            return ORACLE_E_CORRUPT;
+        prev = endt;
+    }
+    uint64_t *x = (uint64_t *)malloc(width * sizeof(uint64_t));
+    il_sym_t *st = (il_sym_t *)malloc(width * sizeof(il_sym_t));
+    if (!x || !st) {
+        free(x); free(st);
+        return ORACLE_E_ARG;
+    }
+    prev = 0;
+    for (uint32_t t = 0; t < num_streams && rc == ORACLE_OK; ++t) {
+        uint64_t endt = stream[1 + t];
+        const uint32_t *w = stream + head + prev;
+        uint64_t words = endt - prev, pos = 2ull * width;
+        uint64_t b = oracle_lane_begin(n, num_streams, t);
+        uint64_t e = oracle_lane_begin(n, num_streams, t + 1);
+        uint64_t m = e - b;
+        for (uint32_t l = 0; l < width; ++l)
+            x[l] = (uint64_t)w[2 * l] | ((uint64_t)w[2 * l + 1] << 32);
+        for (uint64_t g = 0; g * width < m && rc == ORACLE_OK; ++g) {
+            int pending = 0;
+            for (uint32_t l = 0; l < width; ++l) {
+                uint64_t k = g * width + l;
+                st[l].phase = k < m ? 0 : -1;
+                if (k < m) {
+                    st[l].index = indexes[b + k];
+                    if (st[l].index < 0 || st[l].index >= num_tables) {
+                        rc = ORACLE_E_INDEX;
+                        break;
+                    }
+                    pending = 1;
+                }
+            }
+            /* one slot at a time, states in ascending order */
+            while (pending && rc == ORACLE_OK) {
+                pending = 0;
+                for (uint32_t l = 0; l < width && rc == ORACLE_OK; ++l) {
+                    il_sym_t *s = &st[l];
+                    if (s->phase < 0)
+                        continue;
+                    if (s->phase == 0) {
+                        const int32_t *row = cdf + (int64_t)s->index * stride;
+                        int32_t len = lengths[s->index];
+                        uint32_t cum = (uint32_t)(x[l] & (TOTAL_FREQ - 1));
+                        int32_t v = 0;
+                        while (v + 1 < len && (uint32_t)row[v + 1] <= cum)
+                            ++v;
+                        uint32_t start = (uint32_t)row[v];
+                        uint32_t freq = (uint32_t)(row[v + 1] - row[v]);
+                        x[l] = (uint64_t)freq * (x[l] >> PREC) + cum - start;
+                        s->slot = v;
+                        s->mv = (int64_t)len - 2;
+                        s->nb = 0;
+                        s->got = 0;
+                        s->raw = 0;
+                        s->phase = v == s->mv ? 1 : 3;
+                    } else {
+                        uint32_t bits = (uint32_t)(x[l] & BYPASS_MAX);
+                        x[l] >>= BYPASS_BITS;
+                        if (s->phase == 1) {
+                            s->nb += bits;
+                            if (s->nb > 8)
+                                rc = ORACLE_E_CORRUPT;
+                            else if (bits != BYPASS_MAX)
+                                s->phase = s->nb ? 2 : 3;
+                        } else {
+                            s->raw |= (uint64_t)bits << (BYPASS_BITS * s->got);
+                            if (++s->got == s->nb)
+                                s->phase = 3;
+                        }
+                    }
+                    if (rc)
+                        break;
+                    /* renormalise after the put */
+                    if (x[l] < STATE_LOW) {
+                        if (pos >= words) {
+                            rc = ORACLE_E_CORRUPT;
+                            break;
+                        }
+                        x[l] = (x[l] << 32) | w[pos++];
+                    }
+                    if (s->phase == 3) {
+                        int64_t value = s->slot;
+                        if (s->slot == s->mv) {
+                            if (s->raw >= (uint64_t)RAW_LIMIT) {
+                                rc = ORACLE_E_CORRUPT;
+                                break;
+                            }
+                            value = (s->raw & 1) ? -(int64_t)(s->raw >> 1) - 1
+                                                 : (int64_t)(s->raw >> 1) + s->mv;
+                        }
+                        int64_t sym = value + offsets[s->index];
+                        if (sym < INT32_MIN || sym > INT32_MAX) {
+                            rc = ORACLE_E_CORRUPT;
+                            break;
+                        }
+                        symbols_out[b + g * width + l] = (int32_t)sym;
+                        s->phase = -1;
+                    } else {
+                        pending = 1;
+                    }
+                }
+            }
+        }
+        if (rc == ORACLE_OK) {
+            for (uint32_t l = 0; l < width; ++l)
+                if (x[l] != STATE_LOW)
+                    rc = ORACLE_E_CORRUPT;
+            if (pos != words)
+                rc = ORACLE_E_CORRUPT;
+        }
+        prev = endt;
+    }
+    free(x); free(st);
+    return rc;
 }

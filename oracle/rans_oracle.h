@@ -105,6 +105,23 @@ int oracle_decode_split(const uint32_t *stream, uint64_t stream_words,
                         int32_t num_tables, int32_t stride, uint32_t num_lanes,
                         uint32_t pieces, const uint32_t *split_meta, int32_t *symbols_out);
 
+/* Interleaved streams: num_streams streams split as lanes are; symbol k of a
+ * stream is coded by state k mod width; words of a stream are read through
+ * one shared cursor in step, put-slot, ascending-state order; a stream is
+ * its width final states (low, high) then its words.  width = 1 gives the
+ * lane container.  width in [1, 1024]. */
+int oracle_encode_interleaved(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                              const int32_t *cdf, const int32_t *lengths,
+                              const int32_t *offsets, int32_t num_tables, int32_t stride,
+                              uint32_t num_streams, uint32_t width, uint32_t *out, uint64_t cap,
+                              uint64_t *out_words);
+
+int oracle_decode_interleaved(const uint32_t *stream, uint64_t stream_words,
+                              const int32_t *indexes, uint64_t n,
+                              const int32_t *cdf, const int32_t *lengths,
+                              const int32_t *offsets, int32_t num_tables, int32_t stride,
+                              uint32_t num_streams, uint32_t width, int32_t *symbols_out);
+
 /* Quantise one pmf row of m entries (alphabet, then the escape slot) to a
  * 16-bit CDF of m + 1 entries: cdf[0] = 0, cdf[m] = 65536.  ORACLE_E_TABLE
  * for an entry outside [0, 1] or NaN; ORACLE_E_ARG for m outside [2, 65536]. */

@@ -183,3 +183,18 @@ def worked_splits():
                 rows.append([int(lo, 16), int(hi, 16), int(left)])
             out.append((name, int(pieces), rows))
     return out
+
+
+def worked_interleaved():
+    """Cases of golden/worked_interleaved.txt (row A), as dicts."""
+    out = []
+    with open(os.path.join(GOLDEN, "worked_interleaved.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line.startswith("case "):
+                continue
+            name, streams, width, syms, words = [f.strip() for f in line[5:].split("|")]
+            out.append(dict(name=name, streams=int(streams), width=int(width),
+                            symbols=[int(s) for s in syms.split()],
+                            words=[int(w, 16) for w in words.split()]))
+    return out

@@ -20,7 +20,31 @@ import workloads as W  # noqa: E402
 from helpers import (gaussian_row_by_integration, lane_information,  # noqa: E402
                      lane_words_from_container, latent_cases, LATENT_TABLE,
                      quantize_water_level, quantized_cases, single_table, worked_cases,
-                     worked_splits)
+                     worked_splits, worked_interleaved, WORKED_ROWS)
+
+
+def interleaved_pins(lib):
+    failures = []
+    cdf, lengths, offsets = single_table(WORKED_ROWS["A"])
+    for c in worked_interleaved():
+        n = len(c["symbols"])
+        rc, words = oracle.encode_interleaved(np.asarray(c["symbols"]), np.zeros(n), cdf, lengths,
+                                              offsets, c["streams"], c["width"], lib=lib)
+        if rc != 0 or words.tolist() != c["words"]:
+            failures.append(f"golden interleaved {c['name']}")
+        rc, out = oracle.decode_interleaved(np.asarray(c["words"], np.uint32), np.zeros(n), cdf,
+                                            lengths, offsets, c["streams"], c["width"], lib=lib)
+        if rc != 0 or out.tolist() != c["symbols"]:
+            failures.append(f"golden interleaved decode {c['name']}")
+    w = W.load("tiny")
+    for S, Wd in ((4, 64), (64, 1), (300, 8)):
+        rc, words = oracle.encode_interleaved(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets,
+                                              S, Wd, lib=lib)
+        rc2, out = oracle.decode_interleaved(words, w.indexes, w.cdf, w.lengths, w.offsets, S, Wd,
+                                             lib=lib)
+        if rc or rc2 or not np.array_equal(out, w.symbols):
+            failures.append(f"interleaved round trip S={S} W={Wd}")
+    return failures
 
 
 def split_pins(lib):
@@ -168,6 +192,6 @@ def pins(lib):
 
 if __name__ == "__main__":
     lib = oracle.load(sys.argv[1])
-    f = pins(lib) + table_pins(lib) + latent_pins(lib) + split_pins(lib)
+    f = pins(lib) + table_pins(lib) + latent_pins(lib) + split_pins(lib) + interleaved_pins(lib)
     print("\n".join(f) if f else "all pins hold")
     sys.exit(1 if f else 0)

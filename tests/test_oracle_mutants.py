@@ -29,8 +29,8 @@ MUTANTS = {
     "spill_order": ("out[2 + k] = emitted[ne - 1 - k];", "out[2 + k] = emitted[k];"),
     "zigzag_below": ("raw = -2 * v - 1;", "raw = -2 * v;"),
     "zigzag_above": ("raw = 2 * (v - mv);", "raw = 2 * (v - mv) + 2;"),
-    "dropped_remainder": ("(x / p.freq) * TOTAL_FREQ + (x % p.freq) + p.start",
-                          "(x / p.freq) * TOTAL_FREQ + p.start"),
+    "dropped_remainder": ("(*x / p.freq) * TOTAL_FREQ + (*x % p.freq) + p.start",
+                          "(*x / p.freq) * TOTAL_FREQ + p.start"),
     "start_index": ("put_push(l, (uint32_t)row[v], (uint32_t)(row[v + 1] - row[v]))",
                     "put_push(l, (uint32_t)row[v] + (v > 0), (uint32_t)(row[v + 1] - row[v]))"),
     "scan_strict": ("(uint32_t)row[s + 1] <= cum", "(uint32_t)row[s + 1] < cum"),
@@ -69,6 +69,14 @@ MUTANTS = {
     "g_offset_sign": ("*offset = -c;", "*offset = c;"),
     "g_padding": ("cdf_row[k] = (int32_t)TOTAL_FREQ;", "cdf_row[k] = 0;"),
     "g_root_two": ("-x * 0.70710678118654752440", "-x * 1.41421356237309504880"),
+    # interleaved streams
+    "il_state_order": ("for (uint32_t l = width; l-- > 0;) {", "for (uint32_t l = 0; l < width; ++l) {"),
+    "il_slot_order": ("for (uint32_t s = max_slot; s-- > 0 && rc == ORACLE_OK;) {",
+                      "for (uint32_t s = 0; s < max_slot && rc == ORACLE_OK; ++s) {"),
+    "il_assignment": ("uint64_t k = g * width + l;\n                if (k >= m)\n                    continue;",
+                      "uint64_t k = g * width + (width - 1 - l);\n                if (k >= m)\n                    continue;"),
+    "il_flush_order": ("o[2 * l] = (uint32_t)x[l];\n                    o[2 * l + 1] = (uint32_t)(x[l] >> 32);",
+                       "o[2 * l + 1] = (uint32_t)x[l];\n                    o[2 * l] = (uint32_t)(x[l] >> 32);"),
     # latent front end
     "l_round_half_up": ("float r = rintf(d);", "float r = floorf(d + 0.5f);"),
     "l_truncate": ("float r = rintf(d);", "float r = truncf(d);"),
