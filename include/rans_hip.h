@@ -75,6 +75,7 @@ enum rans_status {
 #define RANS_MAX_TABLES 4096
 #define RANS_MAX_STRIDE 16384
 #define RANS_MAX_PIECES 64
+#define RANS_MAX_STREAMS (1u << 16)
 #define RANS_MAX_SYMBOLS (1ull << 28)
 #define RANS_MAX_LANES (1u << 22)
 
@@ -163,6 +164,45 @@ int rans_decode_with_splits(const uint32_t *stream, uint64_t stream_capacity_wor
                             uint32_t num_lanes, uint32_t pieces, const uint32_t *split_meta,
                             int32_t *symbols, int32_t *status, void *workspace,
                             uint64_t workspace_bytes, hipStream_t hstream);
+
+/* Interleaved streams: the wavefront-width variant of the pages' warp-level
+ * interleaved coder (torch_ans 0.3.0, "Usage" legend, Interleaved States:
+ * one stream per warp, one state per lane, one shared bitstream cursor).
+ * The n symbols form num_streams streams split as lanes are; symbol k of a
+ * stream is coded by state k mod 64.  A decoder takes a stream's steps (64
+ * consecutive symbols) in order, within a step the put slots in order (slot
+ * 0: every symbol's REG put; slot 1: an escape's group count; slots 2..:
+ * its groups), within a slot the states in ascending order; each put is
+ * followed by its renormalisation, which reads the next word at the
+ * stream's one cursor.  The encoder applies the puts in exactly the reverse
+ * order.  A stream is its 64 final states (low word, high word, in state
+ * order) followed by its words; the container is [num_streams, end_0 ..
+ * end_{num_streams-1}] followed by the streams.  This is a different
+ * container from the lane container above.
+ *
+ * Workspace: rans_interleaved_workspace_bytes(n, num_streams) bytes for an
+ * encode, rans_workspace_bytes(...) for a decode, the same contract as
+ * above.  rans_interleaved_bound_words bounds the container.  num_streams in
+ * [1, RANS_MAX_STREAMS].  Errors as for the lane calls; a stream that does
+ * not end with every state at 2^31 and every word read gives
+ * RANS_E_CORRUPT. */
+uint64_t rans_interleaved_bound_words(uint64_t n, uint32_t num_streams);
+uint64_t rans_interleaved_workspace_bytes(uint64_t n, uint32_t num_streams);
+
+int rans_encode_interleaved(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                            const int32_t *cdf, const int32_t *cdf_lengths,
+                            const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
+                            uint32_t num_streams, uint32_t *stream,
+                            uint64_t stream_capacity_words, uint64_t *stream_words,
+                            int32_t *status, void *workspace, uint64_t workspace_bytes,
+                            hipStream_t hstream);
+
+int rans_decode_interleaved(const uint32_t *stream, uint64_t stream_capacity_words,
+                            const int32_t *indexes, uint64_t n,
+                            const int32_t *cdf, const int32_t *cdf_lengths,
+                            const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
+                            uint32_t num_streams, int32_t *symbols, int32_t *status,
+                            void *workspace, uint64_t workspace_bytes, hipStream_t hstream);
 
 /* Quantised CDF rows built on the device, one row per table (the step
  * before coding: torch_ans 0.3.0, "Parameter Setup" and "Other Features",

@@ -42,6 +42,10 @@ EXPORTS = (
     "rans_quantize_pmfs",
     "rans_latent_symbols",
     "rans_encode_with_splits",
+    "rans_interleaved_bound_words",
+    "rans_interleaved_workspace_bytes",
+    "rans_encode_interleaved",
+    "rans_decode_interleaved",
     "rans_decode_with_splits",
     "rans_dequantize",
     "rans_status_string",
@@ -107,6 +111,16 @@ def load(path: str | None = None):
         lib.rans_decode_with_splits.argtypes = [vp, u64, vp, u64, vp, vp, vp, i32, i32, u32, u32,
                                                 vp, vp, vp, vp, u64, vp]
         lib.rans_decode_with_splits.restype = ctypes.c_int
+        lib.rans_interleaved_bound_words.argtypes = [u64, u32]
+        lib.rans_interleaved_bound_words.restype = u64
+        lib.rans_interleaved_workspace_bytes.argtypes = [u64, u32]
+        lib.rans_interleaved_workspace_bytes.restype = u64
+        lib.rans_encode_interleaved.argtypes = [vp, vp, u64, vp, vp, vp, i32, i32, u32, vp, u64,
+                                                vp, vp, vp, u64, vp]
+        lib.rans_encode_interleaved.restype = ctypes.c_int
+        lib.rans_decode_interleaved.argtypes = [vp, u64, vp, u64, vp, vp, vp, i32, i32, u32, vp,
+                                                vp, vp, u64, vp]
+        lib.rans_decode_interleaved.restype = ctypes.c_int
         lib.rans_latent_symbols.argtypes = [vp, vp, vp, u64, vp, i32, vp, vp, vp]
         lib.rans_latent_symbols.restype = ctypes.c_int
         lib.rans_dequantize.argtypes = [vp, vp, u64, vp, vp]
@@ -444,4 +458,59 @@ def decode_with_splits(stream: torch.Tensor, split_records: torch.Tensor, indexe
         _ptr(split_records), _ptr(symbols_out), _ptr(status), _ptr(ws), ws.numel(),
         _stream(device))
     _check_rc(rc, "rans_decode_with_splits")
+    return symbols_out, status
+
+
+def encode_interleaved(symbols: torch.Tensor, indexes: torch.Tensor, tables: Tables,
+                       num_streams: int, *, stream_out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None):
+    """Enqueue an interleaved-stream encode (64 states per stream); returns
+    (stream int32 words, stream_words int64[1], status int32[1])."""
+    device = tables.device
+    _need(symbols, torch.int32, device, "symbols")
+    _need(indexes, torch.int32, device, "indexes")
+    n = symbols.numel()
+    if indexes.numel() != n:
+        raise ValueError("symbols and indexes differ in size")
+    lib = load()
+    if stream_out is None:
+        stream_out = torch.empty(int(lib.rans_interleaved_bound_words(n, num_streams)),
+                                 dtype=torch.int32, device=device)
+    _need(stream_out, torch.int32, device, "stream_out")
+    stream_words = torch.zeros(1, dtype=torch.int64, device=device)
+    status = torch.zeros(1, dtype=torch.int32, device=device)
+    ws = workspace if workspace is not None else workspace_for(device).get(
+        int(lib.rans_interleaved_workspace_bytes(n, num_streams)))
+    rc = lib.rans_encode_interleaved(_ptr(symbols), _ptr(indexes), n, _ptr(tables.cdf),
+                                     _ptr(tables.lengths), _ptr(tables.offsets),
+                                     tables.num_tables, tables.stride, num_streams,
+                                     _ptr(stream_out), stream_out.numel(), _ptr(stream_words),
+                                     _ptr(status), _ptr(ws), ws.numel(), _stream(device))
+    _check_rc(rc, "rans_encode_interleaved")
+    return stream_out, stream_words, status
+
+
+def decode_interleaved(stream: torch.Tensor, indexes: torch.Tensor, tables: Tables,
+                       num_streams: int, *, symbols_out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None,
+                       capacity_words: int | None = None):
+    """Enqueue an interleaved-stream decode; returns (symbols, status)."""
+    device = tables.device
+    _need(stream, torch.int32, device, "stream")
+    _need(indexes, torch.int32, device, "indexes")
+    n = indexes.numel()
+    lib = load()
+    if symbols_out is None:
+        symbols_out = torch.empty(n, dtype=torch.int32, device=device)
+    _need(symbols_out, torch.int32, device, "symbols_out")
+    status = torch.zeros(1, dtype=torch.int32, device=device)
+    cap = stream.numel() if capacity_words is None else int(capacity_words)
+    ws = workspace if workspace is not None else workspace_for(device).get(
+        workspace_bytes(n, num_streams, tables.num_tables, tables.stride))
+    rc = lib.rans_decode_interleaved(_ptr(stream), cap, _ptr(indexes), n, _ptr(tables.cdf),
+                                     _ptr(tables.lengths), _ptr(tables.offsets),
+                                     tables.num_tables, tables.stride, num_streams,
+                                     _ptr(symbols_out), _ptr(status), _ptr(ws), ws.numel(),
+                                     _stream(device))
+    _check_rc(rc, "rans_decode_interleaved")
     return symbols_out, status

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "librans_hip.so")
 SOURCES = ["rans_prep.hip", "rans_encode.hip", "rans_decode.hip", "rans_tables.hip", "rans_latent.hip",
-           "rans_abi.hip"]
+           "rans_interleaved.hip", "rans_abi.hip"]
 ARCH = os.environ.get("RANS_HIP_ARCH", "gfx950")
 
 FLAGS = [

@@ -348,6 +348,48 @@ struct TableArgs {
 
 hipError_t launch_table_rows(const TableArgs &a, hipStream_t s);
 
+// Interleaved streams (one stream per wavefront, one state per lane).
+struct IlArgs {
+    const int32_t *symbols;    // encode input
+    const int32_t *indexes;
+    uint64_t n;
+    uint32_t streams;
+    int32_t num_tables;
+    uint32_t *stream;          // encode output container
+    const uint32_t *cstream;   // decode input container
+    uint64_t capacity;
+    uint64_t *stream_words;
+    int32_t *symbols_out;
+    int32_t *status;
+    uint8_t *ws;
+    uint32_t *scratch;         // per stream: 128 state words, then emitted words
+    uint32_t *counts;          // [streams] words of each stream
+    uint64_t *ends;            // [streams] inclusive prefix of counts
+};
+
+// Stream t's scratch starts at word 2 b_t + 256 t (b_t its first symbol):
+// 2 m_t + 256 words, room for the 128 state words and the at most
+// 2 m_t + 128 words its 64 states emit (2 n_j + 2 per state, as for a lane).
+inline __host__ __device__ uint64_t il_scratch_begin(uint64_t n, uint32_t streams, uint32_t t)
+{
+    return 2 * lane_begin(n, streams, t) + 4ull * kWave * t;
+}
+inline __host__ __device__ uint64_t il_scratch_words(uint64_t n, uint32_t streams)
+{
+    return 2 * n + 4ull * kWave * streams;
+}
+inline __host__ __device__ uint64_t il_counts_offset(uint64_t n, uint32_t streams)
+{
+    return ws_scratch_offset(0) + align_up(4 * il_scratch_words(n, streams), 256);
+}
+inline __host__ __device__ uint64_t il_ends_offset(uint64_t n, uint32_t streams)
+{
+    return il_counts_offset(n, streams) + align_up(4ull * streams, 256);
+}
+
+hipError_t launch_il_encode(const IlArgs &a, hipStream_t s);
+hipError_t launch_il_decode(const IlArgs &a, hipStream_t s);
+
 // The latent front end and dequantisation.
 struct LatentArgs {
     const float *y;

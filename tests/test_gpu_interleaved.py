@@ -1,0 +1,111 @@
+"""GPU parity of interleaved streams (64 states per stream, one shared cursor).
+
+For each case the GPU container must equal the oracle's word for word, the
+GPU must decode the oracle's container back to the input, and each side
+decodes the other's.  Cases: the hand-derived two-state pattern scaled to 64
+states (all lanes escaping in one step), streams shorter than 64 symbols,
+ragged last steps, every config at several stream counts, and corrupt
+containers refused like the oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+CASES = [("tiny", 1), ("tiny", 4), ("tiny", 255), ("tiny", 300), ("z", 4), ("z", 1531),
+         ("y1080", 64), ("y1080", 1024), ("y1080x16", 1024), ("y4kx8", 2048)]
+
+_cache = {}
+
+
+def _workload(name):
+    if name not in _cache:
+        import gpu_util as G
+        w = W.load(name)
+        _cache.clear()
+        _cache[name] = (w, G.tables_of(w), G.to_dev(w.symbols), G.to_dev(w.indexes))
+    return _cache[name]
+
+
+def _gpu_encode(sym, idx, tables, S):
+    import torch
+    import gpu_util as G
+    stream, nw, st = G.B.encode_interleaved(sym, idx, tables, S)
+    torch.cuda.synchronize()
+    return int(st.item()), stream[: int(nw.item())].cpu().numpy().view(np.uint32).copy()
+
+
+def _gpu_decode(words, idx, tables, S):
+    import torch
+    import gpu_util as G
+    s = torch.from_numpy(np.asarray(words, np.uint32).view(np.int32).copy()).to(G.DEV)
+    out, st = G.B.decode_interleaved(s, idx, tables, S)
+    torch.cuda.synchronize()
+    return int(st.item()), out.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,S", CASES, ids=[f"{n}-S{s}" for n, s in CASES])
+def test_interleaved_matches_oracle(name, S):
+    import gpu_util as G
+    w, tables, sym, idx = _workload(name)
+    G.say(f"[interleaved] {name} streams={S}: oracle")
+    rc, ref = oracle.encode_interleaved(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, S, 64)
+    assert rc == 0
+    G.say(f"[interleaved] {name} streams={S}: gpu encode")
+    st, got = _gpu_encode(sym, idx, tables, S)
+    assert st == 0
+    if not np.array_equal(got, ref):
+        n = min(got.size, ref.size)
+        bad = np.flatnonzero(got[:n] != ref[:n])
+        pytest.fail(f"sizes {got.size}/{ref.size}; {bad.size} words differ, first at "
+                    f"{bad[0] if bad.size else n}")
+    G.say(f"[interleaved] {name} streams={S}: gpu decode of the oracle's container")
+    st, out = _gpu_decode(ref, idx, tables, S)
+    assert st == 0 and np.array_equal(out, w.symbols)
+
+
+def test_escapes_in_every_lane():
+    """Row A of the worked streams: symbols 2 and -1 alternating (escapes in
+    every lane of every step, words emitted in many slots)."""
+    import gpu_util as G
+    from helpers import single_table
+    cdf, lengths, offsets = single_table([0, 32768, 65535, 65536])
+    syms = np.tile(np.array([2, -1, 7, -9, 0, 1, 300, -4000], np.int32), 1000)
+    idx = np.zeros(syms.size, np.int32)
+    tables = G.B.Tables.from_numpy(cdf, lengths, offsets, G.DEV)
+    for S in (1, 3, 40):
+        G.say(f"[interleaved] escapes S={S}")
+        rc, ref = oracle.encode_interleaved(syms, idx, cdf, lengths, offsets, S, 64)
+        st, got = _gpu_encode(G.to_dev(syms), G.to_dev(idx), tables, S)
+        assert rc == 0 and st == 0 and np.array_equal(got, ref)
+        st, out = _gpu_decode(ref, G.to_dev(idx), tables, S)
+        assert st == 0 and np.array_equal(out, syms)
+
+
+def test_corrupt_containers_like_the_oracle():
+    import gpu_util as G
+    w, tables, sym, idx = _workload("tiny")
+    S = 4
+    rc, ref = oracle.encode_interleaved(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, S, 64)
+    rng = np.random.default_rng(9)
+    cases = [ref[:-1].copy(), np.concatenate([ref, [5]]).astype(np.uint32)]
+    cases[0][S] -= 1
+    cases[1][S] += 1
+    for k in range(6):
+        c = ref.copy()
+        c[int(rng.integers(1 + S, c.size))] ^= np.uint32(1 << int(rng.integers(0, 32)))
+        cases.append(c)
+    for c in cases:
+        G.say("[interleaved] corrupt container")
+        rco, outo = oracle.decode_interleaved(c, w.indexes, w.cdf, w.lengths, w.offsets, S, 64)
+        st, out = _gpu_decode(c, idx, tables, S)
+        assert (st == 0) == (rco == 0), (st, rco)
+        if st == 0:
+            assert np.array_equal(out, outo)
+    st, _ = _gpu_decode(ref, idx, tables, S + 1)
+    assert st == oracle.E_CORRUPT
