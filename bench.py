@@ -12,7 +12,10 @@ decode of the GPU container must give the input back; the CPU-baseline leg
 runs the oracle on the same workload and checks the GPU container against
 the oracle's byte for byte.
 
-The line also reports the decode call of the same container cut into 4
+The line also reports encode and decode calls of the interleaved-stream
+container (rans_encode_interleaved / rans_decode_interleaved: 64 states per
+stream, as many states as lanes, at most 2048 streams), the decode call of
+the same lane container cut into 4
 pieces per lane by split records (rans_decode_with_splits, the records
 written by rans_encode_with_splits beside the unchanged container), and
 times the device table builder on the workload's own table
@@ -87,7 +90,8 @@ def table_set():
     return scales, tail_z, 2 * int(np.ceil(hi * tail_z)) + 3   # longest row: 3133
 
 
-def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200, split=None):
+def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200, split=None,
+                 interleaved=None):
     """The oracle as it stands (single thread) on the full workload, repeated ~10 s;
     its container and table set must equal the GPU's."""
     import numpy as np
@@ -117,6 +121,12 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
                                            pieces)
         assert rc == 0 and np.array_equal(ometa.reshape(-1), records), \
             "GPU split records differ from the oracle's"
+    if interleaved is not None:
+        streams, words = interleaved
+        rc, owords = oracle.encode_interleaved(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets,
+                                               streams, 64)
+        assert rc == 0 and np.array_equal(owords, words), \
+            "GPU interleaved container differs from the oracle's"
     med = statistics.median(times)
     return {
         "value": round(w.n / med / 1e9, 5),
@@ -127,7 +137,8 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
                   f"median of {len(times)} repetitions ({sum(times):.1f} s); "
                   f"{med / w.n * 1e9:.2f} ns/symbol",
         "table_build_us": round(table_us, 1),
-        "parity": "GPU container, split records and table set equal the oracle's",
+        "parity": "GPU container, split records, interleaved container and table set equal "
+                  "the oracle's",
     }
 
 
@@ -270,6 +281,39 @@ def main():
 
     split_us, plain_call_us = split_decode_us(P), split_decode_us(1)
 
+    # ---- interleaved streams: 64 states per stream, as many states as lanes -------
+    S_il = max(1, min(2048, lanes // 64))
+    il_cap = int(lib.rans_interleaved_bound_words(n, S_il))
+    il_ws = torch.zeros(int(lib.rans_interleaved_workspace_bytes(n, S_il)), dtype=torch.uint8,
+                        device=dev)
+    il_stream = torch.empty(il_cap, dtype=torch.int32, device=dev)
+    il_nw = torch.zeros(1, dtype=torch.int64, device=dev)
+    il_args = (vp(sym.data_ptr()), vp(idx.data_ptr()), n, *tab_full[:5], S_il)
+    il_enc = lambda: lib.rans_encode_interleaved(*il_args, vp(il_stream.data_ptr()), il_cap,
+                                                 vp(il_nw.data_ptr()), vp(sp_status.data_ptr()),
+                                                 vp(il_ws.data_ptr()), il_ws.numel(), hs)
+    il_dec = lambda: lib.rans_decode_interleaved(vp(il_stream.data_ptr()), il_cap,
+                                                 vp(idx.data_ptr()), n, *tab_full[:5], S_il,
+                                                 vp(out.data_ptr()), vp(st_dec.data_ptr()),
+                                                 vp(il_ws.data_ptr()), il_ws.numel(), hs)
+    iev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(23)]
+    for e in iev:
+        e[0].record()
+        if il_enc():
+            raise RuntimeError("interleaved encode launch failed")
+        e[1].record()
+        if il_dec():
+            raise RuntimeError("interleaved decode launch failed")
+        e[2].record()
+    torch.cuda.synchronize()
+    B.check(sp_status, "interleaved encode")
+    B.check(st_dec, "interleaved decode")
+    assert torch.equal(out.cpu(), torch.from_numpy(w.symbols)), "interleaved decode != input"
+    il_words = int(il_nw.item())
+    gpu_il = il_stream[:il_words].cpu().numpy().view(np.uint32).copy()
+    il_enc_us = statistics.median(a.elapsed_time(b) for a, b, _ in iev[3:]) * 1e3
+    il_dec_us = statistics.median(b.elapsed_time(c) for _, b, c in iev[3:]) * 1e3
+
     # ---- device table builder on the workloads' table set ------------------------
     scales, tail_z, tstride = table_set()
     d_scales = torch.from_numpy(scales).to(dev)
@@ -336,6 +380,11 @@ def main():
                          "decode_gsym_s": round(n / (split_us * 1e-6) / 1e9, 3),
                          "note": "decode call incl. its table prep; same container, "
                                  "records beside it"},
+        "interleaved": {"streams": S_il, "states": 64 * S_il, "container_words": il_words,
+                        "encode_call_us": round(il_enc_us, 2), "decode_call_us": round(il_dec_us, 2),
+                        "step_gsym_s": round(n / ((il_enc_us + il_dec_us) * 1e-6) / 1e9, 3),
+                        "note": "calls incl. table prep; a different container: 64 interleaved "
+                                "states per stream, one shared word cursor"},
         "table_build": {"kernel": "table_rows_kernel",
                         "workload": f"{scales.size} Gaussian rows, scales log-spaced "
                                     f"{scales[0]:g}..{scales[-1]:g}, tail mass 1e-9, "
@@ -344,7 +393,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, lanes, gpu_words, gpu_tables, args.cpu_seconds,
-                                            split=(P, gpu_records))
+                                            split=(P, gpu_records), interleaved=(S_il, gpu_il))
         line["parity"] = line["cpu_baseline"].pop("parity")
     print(json.dumps(line), flush=True)
 
