@@ -55,8 +55,8 @@ __device__ inline uint32_t lanes_above(uint64_t mask, uint32_t lane)
 
 // ---- encode: streams into scratch --------------------------------------------
 
-template <int kIlThreads>
-__global__ __launch_bounds__(kIlThreads) void il_encode_kernel(IlArgs a)
+template <int TPB>
+__global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
@@ -75,13 +75,13 @@ __global__ __launch_bounds__(kIlThreads) void il_encode_kernel(IlArgs a)
     const uint32_t K = (uint32_t)a.num_tables;
     // (no __syncthreads_or: its shared word would move the dynamic LDS base)
     uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kEncTableBudget);
-    stage_tables<kIlThreads>(lds, tab, herr ? 0u : hdr->enc_bytes);
+    stage_tables<TPB>(lds, tab, herr ? 0u : hdr->enc_bytes);
     if (tid == 0)
         misc[0] = 0u;
     __syncthreads();
     int bad = 0;
     if (!herr)
-        for (uint32_t r = tid; r < K; r += kIlThreads)
+        for (uint32_t r = tid; r < K; r += TPB)
             bad |= (lds_meta(r).lut & kRowInvalid) ? 1 : 0;
     if (block_or(&misc[0], bad) && !herr)
         herr = RANS_E_TABLE;
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kIlThreads) void il_encode_kernel(IlArgs a)
         return;
     }
 
-    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (kIlThreads / kWave) + tid / kWave);
+    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (TPB / kWave) + tid / kWave);
     if (t >= S)
         return;
     const uint64_t b = lane_begin(a.n, S, t), e = lane_begin(a.n, S, t + 1);
@@ -278,8 +278,8 @@ __global__ __launch_bounds__(kIlCopyThreads) void il_copy_kernel(IlArgs a)
 
 // ---- decode -----------------------------------------------------------------------
 
-template <int kIlThreads>
-__global__ __launch_bounds__(kIlThreads) void il_decode_kernel(IlArgs a)
+template <int TPB>
+__global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
@@ -298,20 +298,20 @@ __global__ __launch_bounds__(kIlThreads) void il_decode_kernel(IlArgs a)
         herr = RANS_E_HIP;
     const uint32_t K = (uint32_t)a.num_tables;
     const uint32_t shift = kPrecision - hdr->lut_q;
-    stage_tables<kIlThreads>(lds, tab, herr ? 0u : hdr->dec_bytes);
+    stage_tables<TPB>(lds, tab, herr ? 0u : hdr->dec_bytes);
     if (tid == 0)
         misc[0] = 0u;
     __syncthreads();
     int bad = 0;
     if (!herr)
-        for (uint32_t r = tid; r < K; r += kIlThreads)
+        for (uint32_t r = tid; r < K; r += TPB)
             bad |= (lds_meta(r).lut & kRowInvalid) ? 1 : 0;
     if (block_or(&misc[0], bad) && !herr)
         herr = RANS_E_TABLE;
     if (herr && blockIdx.x == 0 && tid == 0)
         record_error(hdr, herr);
 
-    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (kIlThreads / kWave) + tid / kWave);
+    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (TPB / kWave) + tid / kWave);
     if (!herr && t < S) {
         int lerr = 0;
         const uint64_t b = lane_begin(a.n, S, t), e = lane_begin(a.n, S, t + 1);

@@ -196,3 +196,40 @@ def test_split_calls_check_pieces_on_host(lib, pieces, meta, code):
                                        256, 1 << 30, 0) == code
     assert lib.rans_decode_with_splits(1, 1000, 1, 10, 1, 1, 1, 8, 3133, 4, pieces, meta, 1, 1,
                                        256, 1 << 30, 0) == code
+
+
+def test_interleaved_sizes(lib):
+    for n, S in ((0, 1), (16384, 4), (1566720, 2048), (50135040, 65536)):
+        assert lib.rans_interleaved_bound_words(n, S) == 1 + S + 2 * n + 256 * S
+        ws = lib.rans_interleaved_workspace_bytes(n, S)
+        # header and table sets, flags, per-stream scratch (2 m + 256 words),
+        # word counts and prefix sums
+        assert ws >= 256 + 254 * 1024 + 4 * (2 * n + 256 * S) + 12 * S
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=0), -1), (dict(S=(1 << 16) + 1), -1), (dict(stream=0), -1), (dict(words=0), -1),
+    (dict(status=0), -1), (dict(symbols=0), -1), (dict(cap=4), -1), (dict(K=0), -2),
+    (dict(ws=0), -7), (dict(ws=128), -7), (dict(ws_bytes=4096), -7),
+])
+def test_encode_interleaved_host_checks(lib, kw, code):
+    a = dict(symbols=1, indexes=1, n=10, cdf=1, lengths=1, offsets=1, K=8, stride=3133, S=4,
+             stream=1, cap=1000, words=1, status=1, ws=256, ws_bytes=1 << 30)
+    a.update(kw)
+    assert lib.rans_encode_interleaved(a["symbols"], a["indexes"], a["n"], a["cdf"], a["lengths"],
+                                       a["offsets"], a["K"], a["stride"], a["S"], a["stream"],
+                                       a["cap"], a["words"], a["status"], a["ws"], a["ws_bytes"],
+                                       0) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=0), -1), (dict(S=(1 << 16) + 1), -1), (dict(stream=0), -1), (dict(status=0), -1),
+    (dict(out=0), -1), (dict(cap=2), -1), (dict(stride=20000), -2), (dict(ws=0), -7),
+])
+def test_decode_interleaved_host_checks(lib, kw, code):
+    a = dict(stream=1, cap=1000, indexes=1, n=10, cdf=1, lengths=1, offsets=1, K=8, stride=3133,
+             S=4, out=1, status=1, ws=256, ws_bytes=1 << 30)
+    a.update(kw)
+    assert lib.rans_decode_interleaved(a["stream"], a["cap"], a["indexes"], a["n"], a["cdf"],
+                                       a["lengths"], a["offsets"], a["K"], a["stride"], a["S"],
+                                       a["out"], a["status"], a["ws"], a["ws_bytes"], 0) == code
