@@ -27,7 +27,7 @@ symbol once).  The roofline object reports the slower of the two coding
 kernels: algorithmic bytes per launch (8 B per symbol of int32 symbols and
 indexes plus the 4-byte container words) over its mean duration from HIP
 events recorded around that kernel on the launch stream, on every 8th step
-of the timed loop.
+of the timed loop (every step when there are fewer than 128).
 """
 from __future__ import annotations
 
@@ -46,7 +46,7 @@ METRIC = "rANS encode/decode Gsymbol/s on 1080p y-latent (1.57M syms); % of HBM 
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 SPLIT_PIECES = 4   # pieces per lane for the split-record decode figure
-EVENT_EVERY = 8    # timed steps per sampled step with per-kernel HIP events
+EVENT_EVERY = 8    # timed steps per sampled step with per-kernel HIP events (at most)
 
 DEFAULT_LANES = {"tiny": 64, "z": 256, "y1080": 4096, "y1080x16": 65536, "y4kx8": 131072}
 DESCRIPTION = {
@@ -231,7 +231,8 @@ def main():
         if rc:
             raise RuntimeError(f"launch failed: {rc}")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] if k % EVENT_EVERY == 0 else None
+    every = max(1, min(EVENT_EVERY, args.steps // 16))   # at least 16 sampled steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] if k % every == 0 else None
            for k in range(args.steps)]
     for _ in range(args.warmup):
         step(None)
