@@ -14,7 +14,8 @@ the oracle's byte for byte.
 
 The line also reports encode and decode calls of the interleaved-stream
 container (rans_encode_interleaved / rans_decode_interleaved: 64 states per
-stream, as many states as lanes, at most 2048 streams), the decode call of
+stream; by default as many states as lanes, at most 4096 streams, else
+--streams), the decode call of
 the same lane container cut into 4
 pieces per lane by split records (rans_decode_with_splits, the records
 written by rans_encode_with_splits beside the unchanged container), and
@@ -153,6 +154,8 @@ def main():
     ap.add_argument("--lanes", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--streams", type=int, default=None,
+                    help="interleaved streams (default: lanes / 64, at most 4096)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -292,7 +295,7 @@ def main():
     split_us, plain_call_us = split_decode_us(P), split_decode_us(1)
 
     # ---- interleaved streams: 64 states per stream, as many states as lanes -------
-    S_il = max(1, min(2048, lanes // 64))
+    S_il = args.streams if args.streams else max(1, min(4096, lanes // 64))
     il_cap = int(lib.rans_interleaved_bound_words(n, S_il))
     il_ws = torch.zeros(int(lib.rans_interleaved_workspace_bytes(n, S_il)), dtype=torch.uint8,
                         device=dev)

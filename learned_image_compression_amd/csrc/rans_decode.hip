@@ -304,7 +304,10 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     const uint32_t LV = L << pl;
     const uint32_t lpw = dec_lanes_per_wave(LV);
     const uint32_t lane = tid & (kWave - 1);
-    const uint32_t wave = tid / kWave;   // coding waves are 0 .. CW-1
+    // coding waves are 0 .. CW-1; wave and herr are the same in every lane,
+    // and scalar they keep the buffer descriptors and loops below uniform
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    herr = __builtin_amdgcn_readfirstlane(herr);
     const uint32_t u0 = __builtin_amdgcn_readfirstlane((blockIdx.x * CW + wave) * lpw);
     const uint32_t u = u0 + lane;
     const uint32_t j = u >> pl;            // the unit's lane
@@ -322,7 +325,8 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
         const Rsrc ridx = make_rsrc(a.indexes + bw, (uint32_t)(4 * (ew - bw)));
         const Rsrc rout = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
         const uint32_t jw = u0 >> pl;   // the wave's first lane
-        const uint64_t wbase = jw ? a.stream[jw] : 0u;   // the wave's first word
+        // the wave's first word (scalar, so the stream's buffer descriptor is)
+        const uint64_t wbase = jw ? __builtin_amdgcn_readfirstlane(a.stream[jw]) : 0u;
         const uint64_t wavail = a.capacity - 1 - L;
         const uint64_t wbytes = wbase < wavail ? min(4 * (wavail - wbase), 1ull << 31) : 0;
         const Rsrc rstr = make_rsrc(a.stream + 1 + L + (wbase < wavail ? wbase : 0), (uint32_t)wbytes);

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     const uint32_t nwork = enc_waves(L);
 
     // ---- tables -> LDS -------------------------------------------------------
-    const uint32_t wave = tid / kWave;   // coding waves are 0 .. CW-1
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // coding waves 0 .. CW-1
     int herr = 0;
     if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables)
         herr = RANS_E_ARG;
@@ -185,6 +185,9 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     if (herr && blockIdx.x == 0 && tid == 0)
         record_error(hdr, herr);
 
+    // herr is the same in every lane; scalar, it keeps the buffer
+    // descriptors and loops below uniform for the compiler
+    herr = __builtin_amdgcn_readfirstlane(herr);
     if (!herr && wave < CW) {
         // Wave t codes lanes t*lpw ..; its look-back waits only for waves of
         // lower-numbered blocks.  Workgroups are dispatched in index order, so

@@ -311,14 +311,20 @@ __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
     if (herr && blockIdx.x == 0 && tid == 0)
         record_error(hdr, herr);
 
+    // herr is the same in every thread; scalar, it keeps the decode loop's
+    // control flow (and the shared word cursor) uniform for the compiler
+    herr = __builtin_amdgcn_readfirstlane(herr);
     const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (TPB / kWave) + tid / kWave);
     if (!herr && t < S) {
         int lerr = 0;
         const uint64_t b = lane_begin(a.n, S, t), e = lane_begin(a.n, S, t + 1);
         const uint32_t m = (uint32_t)(e - b);
-        const uint64_t prev = t ? a.cstream[t] : 0u;
-        const uint64_t endt = a.cstream[1 + t];
-        if (a.cstream[0] != S || endt < prev + 2 * kIlW || 1ull + S + endt > a.capacity) {
+        // wave-uniform (t is), and kept in scalar registers so that the
+        // stream's buffer descriptor is too
+        const uint64_t prev = t ? __builtin_amdgcn_readfirstlane(a.cstream[t]) : 0u;
+        const uint64_t endt = __builtin_amdgcn_readfirstlane(a.cstream[1 + t]);
+        if (__builtin_amdgcn_readfirstlane(a.cstream[0]) != S || endt < prev + 2 * kIlW ||
+            1ull + S + endt > a.capacity) {
             lerr = RANS_E_CORRUPT;
         } else {
             const uint32_t W = (uint32_t)(endt - prev);
@@ -356,10 +362,9 @@ __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
                 for (int u = 0; u < kIlAhead; ++u)
                     r[u] = buf_load(ridx, 4 * ((g0 + u) * kIlW + lane), 0);
             };
-            auto step = [&](int32_t r, uint32_t g) {
+            auto step = [&](int32_t r, const RowMeta &mr, uint32_t g) {
                 const uint32_t k = g * kIlW + lane;
                 const bool valid = k < m;
-                const RowMeta mr = lds_meta(min((uint32_t)r, K - 1));
                 const uint32_t mv = mr.mvf & 0xFFFFu;
                 if (valid && (uint32_t)r >= K)
                     lerr = lerr ? lerr : RANS_E_INDEX;
@@ -388,8 +393,8 @@ __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
                 }
                 const uint32_t f = (nxt - sm1) & 0xFFFFu;
                 const uint32_t rr = (cum - sm1 - 1) & 0xFFFFu;   // cum - start
-                if (valid)
-                    x = (uint64_t)f * (x >> kPrecision) + rr;
+                // a select, not a branch: the step stays one basic block
+                x = valid ? (uint64_t)f * (x >> kPrecision) + rr : x;
                 refill(valid & (x < kStateLow));
                 int64_t value = slot;
                 const bool esc = valid & (slot == mv);
@@ -407,6 +412,7 @@ __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
                     uint32_t top = nb;
                     for (int o = kWave / 2; o > 0; o >>= 1)
                         top = max(top, (uint32_t)__shfl_xor((int)top, o));
+                    top = __builtin_amdgcn_readfirstlane(top);   // the wave's max in every lane
                     uint64_t raw = 0;
                     for (uint32_t j = 0; j < top; ++j) {
                         const bool has = j < nb;
@@ -429,14 +435,25 @@ __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
             };
             load(ia, 0);
             load(ib, kIlAhead);
+            // A group's row metadata is read before its steps (it depends on
+            // the index only), so a step's chain of dependent LDS reads
+            // starts at the bucket table.
+            RowMeta mt[kIlAhead];
+            auto metas = [&](const int32_t (&r)[kIlAhead]) {
+#pragma unroll
+                for (int u = 0; u < kIlAhead; ++u)
+                    mt[u] = lds_meta(min((uint32_t)r[u], K - 1));
+            };
             for (uint32_t g0 = 0; g0 < G; g0 += 2 * kIlAhead) {
+                metas(ia);
 #pragma unroll
                 for (int u = 0; u < kIlAhead; ++u)
-                    step(ia[u], g0 + u);
+                    step(ia[u], mt[u], g0 + u);
                 load(ia, g0 + 2 * kIlAhead);
+                metas(ib);
 #pragma unroll
                 for (int u = 0; u < kIlAhead; ++u)
-                    step(ib[u], g0 + kIlAhead + u);
+                    step(ib[u], mt[u], g0 + kIlAhead + u);
                 load(ib, g0 + 3 * kIlAhead);
             }
             if (__ballot(x != kStateLow) != 0 || cursor != W)
@@ -472,10 +489,14 @@ hipError_t lds_attr(F *kernel, uint32_t bytes)
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-// Each block stages a table set into one CU's LDS, so a block's waves are
-// that CU's coding waves: eight (two per SIMD) once there are streams for
-// every CU that way, else four.
-bool il_wide(uint32_t streams) { return streams >= 8 * kCodingCUs; }
+// Each block stages a table set into one CU's LDS (one block per CU fits),
+// so a block's waves are that CU's coding waves.  More waves per SIMD hide
+// more of a step's dependent LDS reads: sixteen waves (four per SIMD) once
+// there are streams for every CU that way, else eight, else four.
+uint32_t il_block_waves(uint32_t streams)
+{
+    return streams >= 16 * kCodingCUs ? 16u : (streams >= 8 * kCodingCUs ? 8u : 4u);
+}
 
 template <int TPB>
 hipError_t launch_il_encode_t(const IlArgs &a, hipStream_t s)
@@ -505,8 +526,9 @@ hipError_t launch_il_decode_t(const IlArgs &a, hipStream_t s)
 
 hipError_t launch_il_encode(const IlArgs &a, hipStream_t s)
 {
-    const hipError_t e = il_wide(a.streams) ? launch_il_encode_t<8 * kWave>(a, s)
-                                            : launch_il_encode_t<4 * kWave>(a, s);
+    const hipError_t e = il_block_waves(a.streams) == 16 ? launch_il_encode_t<16 * kWave>(a, s)
+                         : il_block_waves(a.streams) == 8  ? launch_il_encode_t<8 * kWave>(a, s)
+                                                           : launch_il_encode_t<4 * kWave>(a, s);
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(il_scan_kernel, dim3(1), dim3(kIlScanThreads), 0, s, a);
@@ -517,8 +539,9 @@ hipError_t launch_il_encode(const IlArgs &a, hipStream_t s)
 
 hipError_t launch_il_decode(const IlArgs &a, hipStream_t s)
 {
-    return il_wide(a.streams) ? launch_il_decode_t<8 * kWave>(a, s)
-                              : launch_il_decode_t<4 * kWave>(a, s);
+    return il_block_waves(a.streams) == 16 ? launch_il_decode_t<16 * kWave>(a, s)
+           : il_block_waves(a.streams) == 8  ? launch_il_decode_t<8 * kWave>(a, s)
+                                             : launch_il_decode_t<4 * kWave>(a, s);
 }
 
 }  // namespace rans
