@@ -99,7 +99,8 @@ def test_random_case(seed):
     torch.cuda.synchronize()
     assert int(status.item()) == 0 and np.array_equal(out.cpu().numpy(), sym)
     # interleaved streams
-    S = max(1, min(lanes, 300))
+    # (4096 and more streams run the 16-wave blocks)
+    S = int(rng.choice([max(1, min(lanes, 300)), 4096, 4111]))
     rc, iref = oracle.encode_interleaved(sym, idx, cdf, lengths, offsets, S, 64)
     istream, inw, ist = G.B.encode_interleaved(G.to_dev(sym), G.to_dev(idx), tables, S)
     torch.cuda.synchronize()
