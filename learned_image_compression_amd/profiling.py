@@ -77,7 +77,9 @@ def _rows(path_glob: str):
 def _kernel_key(name: str) -> str:
     if re.search(r"decode_kernel<[^>]*true>", name):
         return "decode_kernel_split"
-    m = re.search(r"(encode_kernel|decode_kernel|prep_kernel|table_rows_kernel|"
+    # the interleaved kernels first: their names contain the lane kernels'
+    m = re.search(r"(il_encode_kernel|il_decode_kernel|il_scan_kernel|il_copy_kernel|"
+                  r"encode_kernel|decode_kernel|prep_kernel|table_rows_kernel|"
                   r"latent_symbols_kernel|dequantize_kernel)", name)
     if m:
         return m.group(1)
