@@ -13,6 +13,12 @@ Three commands, all meant to run under or after rocprofv3:
       positions (a 64-scale table log-spaced over 0.11..256), R times each,
       for kernel-trace and counter passes; prints the bytes each call moves.
 
+  python -m learned_image_compression_amd.profiling interleaved [--config C]
+          [--streams S] [--reps R]
+      Interleaved-stream encode and decode calls on a workload (workloads/),
+      R times each, for kernel-trace and counter passes; checks the round
+      trip and prints the container size and the bytes each call moves.
+
   python -m learned_image_compression_amd.profiling summarize ...
       Turns rocprofv3 CSV output (kernel trace statistics and the counter
       passes) into the short text and JSON summaries committed under
@@ -64,6 +70,32 @@ def latent_main(n: int, reps: int) -> None:
     torch.cuda.synchronize()
     print(json.dumps({"positions": n, "reps": reps, "latent_bytes": 20 * n,
                       "dequantize_bytes": 12 * n}), flush=True)
+
+
+def interleaved_main(config: str, streams: int, reps: int) -> None:
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import workloads
+    from learned_image_compression_amd import binding as B
+    dev = torch.device("cuda:0")
+    w = workloads.load(config)
+    tables = B.Tables.from_numpy(w.cdf, w.lengths, w.offsets, dev)
+    sym = torch.from_numpy(w.symbols).to(dev)
+    idx = torch.from_numpy(w.indexes).to(dev)
+    for _ in range(reps):
+        stream, nwords, st = B.encode_interleaved(sym, idx, tables, streams)
+        out, st2 = B.decode_interleaved(stream, idx, tables, streams)
+    torch.cuda.synchronize()
+    B.check(st, "interleaved encode")
+    B.check(st2, "interleaved decode")
+    if not torch.equal(out.cpu(), torch.from_numpy(w.symbols)):
+        raise RuntimeError("interleaved round trip differs from the input")
+    words = int(nwords.item())
+    # a call reads symbols (or writes them) and indexes, and writes (or reads)
+    # the container
+    print(json.dumps({"config": config, "streams": streams, "reps": reps, "n": w.n,
+                      "container_words": words,
+                      "algorithmic_bytes_per_call": 8 * w.n + 4 * words}), flush=True)
 
 
 def _rows(path_glob: str):
@@ -126,10 +158,33 @@ def summarize_main(a) -> None:
         if a.bench_json:
             with open(a.bench_json) as fh:
                 bench = [json.loads(l) for l in fh if l.strip().startswith("{")][-1]
-            lines += ["", "# bench.py line of the same run (kernel_us from HIP events):",
-                      json.dumps({k: bench[k] for k in ("value", "unit", "ms_per_step", "kernel_us",
-                                              "split_decode", "table_build") if k in bench})]
+            if "metric" in bench:
+                lines += ["", "# bench.py line of the same run (kernel_us from HIP events):",
+                          json.dumps({k: bench[k] for k in ("value", "unit", "ms_per_step",
+                                                            "kernel_us", "split_decode",
+                                                            "table_build") if k in bench})]
+            else:
+                lines += ["", "# line printed by the profiled command:", json.dumps(bench)]
         path = os.path.join(a.out, f"kernel_trace_{a.label}.txt")
+        with open(path, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(path)
+    if a.sq:
+        # per kernel, the mean per dispatch of every counter in the given passes
+        table = {}
+        for g in a.sq:
+            names = sorted({r["Counter_Name"] for r in _rows(g)})
+            for c in names:
+                for k, v in counter_per_dispatch(g, c).items():
+                    table.setdefault(k, {})[c] = v
+        lines = [f"# rocprofv3 counters (mean per dispatch): {a.label}", f"# command: {a.command}", ""]
+        for k in sorted(table):
+            if not k.startswith(("il_", "encode", "decode", "prep", "table", "latent", "dequant")):
+                continue
+            lines.append(k)
+            for c, v in sorted(table[k].items()):
+                lines.append(f"  {c:<24s} {v:16.1f}")
+        path = os.path.join(a.out, f"counters_{a.label}.txt")
         with open(path, "w") as fh:
             fh.write("\n".join(lines) + "\n")
         print(path)
@@ -141,6 +196,28 @@ def summarize_main(a) -> None:
         copy_bytes = a.copy_mib * (1 << 20)
         f_scale = copy_bytes / (cf * KIB)
         w_scale = copy_bytes / (cw * KIB)
+        if a.interleaved_streams:
+            with open(a.bench_json) as fh:
+                run = [json.loads(l) for l in fh if l.strip().startswith("{")][-1]
+            t = {"workload": a.label, "config": a.config, "streams": a.interleaved_streams,
+                 "n": run["n"], "container_words": run["container_words"],
+                 "algorithmic_bytes_per_call": run["algorithmic_bytes_per_call"],
+                 "commands": a.command,
+                 "copy_calibration": {"copy_bytes": copy_bytes, "fetch_kib": round(cf, 1),
+                                      "write_kib": round(cw, 1), "fetch_scale": round(f_scale, 4),
+                                      "write_scale": round(w_scale, 4)}}
+            for key in ("il_encode_kernel", "il_scan_kernel", "il_copy_kernel", "il_decode_kernel"):
+                rb = fetch[key] * KIB * f_scale
+                wb = write[key] * KIB * w_scale
+                t[key] = {"fetch_kib_per_dispatch": round(fetch[key], 1),
+                          "write_kib_per_dispatch": round(write[key], 1),
+                          "hbm_bytes_per_launch": round(rb + wb)}
+            path = os.path.join(a.out, f"traffic_{a.label}.json")
+            with open(path, "w") as fh:
+                json.dump(t, fh, indent=1)
+                fh.write("\n")
+            print(path)
+            return
         if a.latent_n:
             # the front end moves 20 bytes per position, dequantisation 12
             t = {"workload": a.label, "positions": a.latent_n, "commands": a.command,
@@ -209,11 +286,19 @@ def main(argv=None) -> None:
     s.add_argument("--calib-write")
     s.add_argument("--copy-mib", type=int, default=256)
     s.add_argument("--latent-n", type=int, default=0)
+    s.add_argument("--interleaved-streams", type=int, default=0)
+    s.add_argument("--sq", nargs="*", default=[], help="counter CSVs of SQ passes")
+    il = sub.add_parser("interleaved")
+    il.add_argument("--config", default="y1080x16")
+    il.add_argument("--streams", type=int, default=4096)
+    il.add_argument("--reps", type=int, default=5)
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         copy_main(a.mib, a.reps)
     elif a.cmd == "latent":
         latent_main(a.n, a.reps)
+    elif a.cmd == "interleaved":
+        interleaved_main(a.config, a.streams, a.reps)
     else:
         summarize_main(a)
 
