@@ -12,16 +12,17 @@ decode of the GPU container must give the input back; the CPU-baseline leg
 runs the oracle on the same workload and checks the GPU container against
 the oracle's byte for byte.
 
-The line also reports encode and decode calls of the interleaved-stream
-container (rans_encode_interleaved / rans_decode_interleaved: 64 states per
-stream; by default as many states as lanes, at most 4096 streams, else
---streams), the decode call of
-the same lane container cut into 4
-pieces per lane by split records (rans_decode_with_splits, the records
-written by rans_encode_with_splits beside the unchanged container), and
-times the device table builder on the workload's own table
-set (64 discretised Gaussians, scales log-spaced over 0.11..256, stride
-3133), whose output must equal the workload's tables.
+The line also reports:
+- encode and decode calls of the interleaved-stream container
+  (rans_encode_interleaved / rans_decode_interleaved: 64 states per stream;
+  by default as many states as lanes, at most 4096 streams, else --streams),
+  both as full calls and as *_prepared calls on tables prepared once;
+- the decode call of the same lane container cut into 4 pieces per lane by
+  split records (rans_decode_with_splits, the records written by
+  rans_encode_with_splits beside the unchanged container);
+- the device table builder on the workload's own table set (64 discretised
+  Gaussians, scales log-spaced over 0.11..256, stride 3133), whose output
+  must equal the workload's tables.
 
 value = symbols per step / step time (a step encodes and decodes every
 symbol once).  The roofline object reports the slower of the two coding
@@ -365,6 +366,32 @@ def main():
     gpu_il = il_stream[:il_words].cpu().numpy().view(np.uint32).copy()
     il_enc_us = statistics.median(a.elapsed_time(b) for a, b, _ in iev[3:]) * 1e3
     il_dec_us = statistics.median(b.elapsed_time(c) for _, b, c in iev[3:]) * 1e3
+    # the same calls on tables prepared once (the full calls above left them
+    # prepared in il_ws)
+    il_enc_p = lambda: lib.rans_encode_interleaved_prepared(
+        vp(sym.data_ptr()), vp(idx.data_ptr()), n, tables.num_tables, S_il,
+        vp(il_stream.data_ptr()), il_cap, vp(il_nw.data_ptr()), vp(sp_status.data_ptr()),
+        vp(il_ws.data_ptr()), il_ws.numel(), hs)
+    il_dec_p = lambda: lib.rans_decode_interleaved_prepared(
+        vp(il_stream.data_ptr()), il_cap, vp(idx.data_ptr()), n, tables.num_tables, S_il,
+        vp(out.data_ptr()), vp(st_dec.data_ptr()), vp(il_ws.data_ptr()), il_ws.numel(), hs)
+    out.zero_()
+    for e in iev:
+        e[0].record()
+        if il_enc_p():
+            raise RuntimeError("prepared interleaved encode launch failed")
+        e[1].record()
+        if il_dec_p():
+            raise RuntimeError("prepared interleaved decode launch failed")
+        e[2].record()
+    torch.cuda.synchronize()
+    B.check(sp_status, "prepared interleaved encode")
+    B.check(st_dec, "prepared interleaved decode")
+    assert torch.equal(out.cpu(), torch.from_numpy(w.symbols)), "prepared interleaved decode != input"
+    assert np.array_equal(il_stream[:il_words].cpu().numpy().view(np.uint32), gpu_il), \
+        "prepared interleaved container differs"
+    il_enc_p_us = statistics.median(a.elapsed_time(b) for a, b, _ in iev[3:]) * 1e3
+    il_dec_p_us = statistics.median(b.elapsed_time(c) for _, b, c in iev[3:]) * 1e3
 
     # ---- device table builder on the workloads' table set ------------------------
     scales, tail_z, tstride = table_set()
@@ -435,8 +462,12 @@ def main():
         "interleaved": {"streams": S_il, "states": 64 * S_il, "container_words": il_words,
                         "encode_call_us": round(il_enc_us, 2), "decode_call_us": round(il_dec_us, 2),
                         "step_gsym_s": round(n / ((il_enc_us + il_dec_us) * 1e-6) / 1e9, 3),
-                        "note": "calls incl. table prep; a different container: 64 interleaved "
-                                "states per stream, one shared word cursor"},
+                        "prepared_encode_call_us": round(il_enc_p_us, 2),
+                        "prepared_decode_call_us": round(il_dec_p_us, 2),
+                        "prepared_step_gsym_s": round(n / ((il_enc_p_us + il_dec_p_us) * 1e-6) / 1e9, 3),
+                        "note": "*_call_us: the full calls, table prep included; prepared_*: the "
+                                "*_prepared calls on tables prepared once; a different container: "
+                                "64 interleaved states per stream, one shared word cursor"},
         "table_build": {"kernel": "table_rows_kernel",
                         "workload": f"{scales.size} Gaussian rows, scales log-spaced "
                                     f"{scales[0]:g}..{scales[-1]:g}, tail mass 1e-9, "

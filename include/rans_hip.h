@@ -204,6 +204,27 @@ int rans_decode_interleaved(const uint32_t *stream, uint64_t stream_capacity_wor
                             uint32_t num_streams, int32_t *symbols, int32_t *status,
                             void *workspace, uint64_t workspace_bytes, hipStream_t hstream);
 
+/* The two interleaved calls above are rans_prepare_tables followed by these.
+ * A caller that codes many tensors with one table set (torch_ans
+ * "Performance Tuning": reuse the coder rather than rebuild its tables) runs
+ * rans_prepare_tables once on the workspace and then any number of these
+ * calls on that workspace.  The workspace must also meet the size above
+ * (rans_interleaved_workspace_bytes for an encode).  num_tables must equal
+ * the prepared set's, or *status reports RANS_E_ARG; row errors found by
+ * the preparation surface in *status as RANS_E_TABLE.  The host-side checks
+ * and the other errors are those of the full calls. */
+int rans_encode_interleaved_prepared(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                                     int32_t num_tables, uint32_t num_streams, uint32_t *stream,
+                                     uint64_t stream_capacity_words, uint64_t *stream_words,
+                                     int32_t *status, void *workspace, uint64_t workspace_bytes,
+                                     hipStream_t hstream);
+
+int rans_decode_interleaved_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
+                                     const int32_t *indexes, uint64_t n, int32_t num_tables,
+                                     uint32_t num_streams, int32_t *symbols, int32_t *status,
+                                     void *workspace, uint64_t workspace_bytes,
+                                     hipStream_t hstream);
+
 /* Quantised CDF rows built on the device, one row per table (the step
  * before coding: torch_ans 0.3.0, "Parameter Setup" and "Other Features",
  * the coder turns batched pmfs into 16-bit CDFs itself; "Performance

@@ -46,6 +46,8 @@ EXPORTS = (
     "rans_interleaved_workspace_bytes",
     "rans_encode_interleaved",
     "rans_decode_interleaved",
+    "rans_encode_interleaved_prepared",
+    "rans_decode_interleaved_prepared",
     "rans_decode_with_splits",
     "rans_dequantize",
     "rans_status_string",
@@ -121,6 +123,12 @@ def load(path: str | None = None):
         lib.rans_decode_interleaved.argtypes = [vp, u64, vp, u64, vp, vp, vp, i32, i32, u32, vp,
                                                 vp, vp, u64, vp]
         lib.rans_decode_interleaved.restype = ctypes.c_int
+        lib.rans_encode_interleaved_prepared.argtypes = [vp, vp, u64, i32, u32, vp, u64, vp, vp,
+                                                         vp, u64, vp]
+        lib.rans_encode_interleaved_prepared.restype = ctypes.c_int
+        lib.rans_decode_interleaved_prepared.argtypes = [vp, u64, vp, u64, i32, u32, vp, vp, vp,
+                                                         u64, vp]
+        lib.rans_decode_interleaved_prepared.restype = ctypes.c_int
         lib.rans_latent_symbols.argtypes = [vp, vp, vp, u64, vp, i32, vp, vp, vp]
         lib.rans_latent_symbols.restype = ctypes.c_int
         lib.rans_dequantize.argtypes = [vp, vp, u64, vp, vp]
@@ -463,9 +471,11 @@ def decode_with_splits(stream: torch.Tensor, split_records: torch.Tensor, indexe
 
 def encode_interleaved(symbols: torch.Tensor, indexes: torch.Tensor, tables: Tables,
                        num_streams: int, *, stream_out: torch.Tensor | None = None,
-                       workspace: torch.Tensor | None = None):
+                       workspace: torch.Tensor | None = None, prepared: bool = False):
     """Enqueue an interleaved-stream encode (64 states per stream); returns
-    (stream int32 words, stream_words int64[1], status int32[1])."""
+    (stream int32 words, stream_words int64[1], status int32[1]).
+    ``prepared=True`` reuses tables already packed into ``workspace`` by
+    :func:`prepare_tables`."""
     device = tables.device
     _need(symbols, torch.int32, device, "symbols")
     _need(indexes, torch.int32, device, "indexes")
@@ -481,11 +491,18 @@ def encode_interleaved(symbols: torch.Tensor, indexes: torch.Tensor, tables: Tab
     status = torch.zeros(1, dtype=torch.int32, device=device)
     ws = workspace if workspace is not None else workspace_for(device).get(
         int(lib.rans_interleaved_workspace_bytes(n, num_streams)))
-    rc = lib.rans_encode_interleaved(_ptr(symbols), _ptr(indexes), n, _ptr(tables.cdf),
-                                     _ptr(tables.lengths), _ptr(tables.offsets),
-                                     tables.num_tables, tables.stride, num_streams,
-                                     _ptr(stream_out), stream_out.numel(), _ptr(stream_words),
-                                     _ptr(status), _ptr(ws), ws.numel(), _stream(device))
+    if prepared:
+        rc = lib.rans_encode_interleaved_prepared(_ptr(symbols), _ptr(indexes), n,
+                                                  tables.num_tables, num_streams, _ptr(stream_out),
+                                                  stream_out.numel(), _ptr(stream_words),
+                                                  _ptr(status), _ptr(ws), ws.numel(),
+                                                  _stream(device))
+    else:
+        rc = lib.rans_encode_interleaved(_ptr(symbols), _ptr(indexes), n, _ptr(tables.cdf),
+                                         _ptr(tables.lengths), _ptr(tables.offsets),
+                                         tables.num_tables, tables.stride, num_streams,
+                                         _ptr(stream_out), stream_out.numel(), _ptr(stream_words),
+                                         _ptr(status), _ptr(ws), ws.numel(), _stream(device))
     _check_rc(rc, "rans_encode_interleaved")
     return stream_out, stream_words, status
 
@@ -493,8 +510,9 @@ def encode_interleaved(symbols: torch.Tensor, indexes: torch.Tensor, tables: Tab
 def decode_interleaved(stream: torch.Tensor, indexes: torch.Tensor, tables: Tables,
                        num_streams: int, *, symbols_out: torch.Tensor | None = None,
                        workspace: torch.Tensor | None = None,
-                       capacity_words: int | None = None):
-    """Enqueue an interleaved-stream decode; returns (symbols, status)."""
+                       capacity_words: int | None = None, prepared: bool = False):
+    """Enqueue an interleaved-stream decode; returns (symbols, status).
+    ``prepared=True`` reuses tables already packed into ``workspace``."""
     device = tables.device
     _need(stream, torch.int32, device, "stream")
     _need(indexes, torch.int32, device, "indexes")
@@ -507,10 +525,16 @@ def decode_interleaved(stream: torch.Tensor, indexes: torch.Tensor, tables: Tabl
     cap = stream.numel() if capacity_words is None else int(capacity_words)
     ws = workspace if workspace is not None else workspace_for(device).get(
         workspace_bytes(n, num_streams, tables.num_tables, tables.stride))
-    rc = lib.rans_decode_interleaved(_ptr(stream), cap, _ptr(indexes), n, _ptr(tables.cdf),
-                                     _ptr(tables.lengths), _ptr(tables.offsets),
-                                     tables.num_tables, tables.stride, num_streams,
-                                     _ptr(symbols_out), _ptr(status), _ptr(ws), ws.numel(),
-                                     _stream(device))
+    if prepared:
+        rc = lib.rans_decode_interleaved_prepared(_ptr(stream), cap, _ptr(indexes), n,
+                                                  tables.num_tables, num_streams,
+                                                  _ptr(symbols_out), _ptr(status), _ptr(ws),
+                                                  ws.numel(), _stream(device))
+    else:
+        rc = lib.rans_decode_interleaved(_ptr(stream), cap, _ptr(indexes), n, _ptr(tables.cdf),
+                                         _ptr(tables.lengths), _ptr(tables.offsets),
+                                         tables.num_tables, tables.stride, num_streams,
+                                         _ptr(symbols_out), _ptr(status), _ptr(ws), ws.numel(),
+                                         _stream(device))
     _check_rc(rc, "rans_decode_interleaved")
     return symbols_out, status

@@ -238,6 +238,54 @@ uint64_t rans_interleaved_workspace_bytes(uint64_t n, uint32_t num_streams)
     return il_ends_offset(n, num_streams) + 8ull * num_streams;
 }
 
+int rans_encode_interleaved_prepared(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                                     int32_t num_tables, uint32_t num_streams, uint32_t *stream,
+                                     uint64_t stream_capacity_words, uint64_t *stream_words,
+                                     int32_t *status, void *workspace, uint64_t workspace_bytes,
+                                     hipStream_t hstream)
+{
+    if (num_streams == 0 || num_streams > RANS_MAX_STREAMS || !stream || !stream_words ||
+        !status || (n && (!symbols || !indexes)))
+        return RANS_E_ARG;
+    if (num_tables < 1 || num_tables > RANS_MAX_TABLES)
+        return RANS_E_TABLE;
+    if (n > RANS_MAX_SYMBOLS || stream_capacity_words < 1ull + num_streams)
+        return RANS_E_ARG;
+    int rc = check_workspace(workspace, workspace_bytes,
+                             rans_interleaved_workspace_bytes(n, num_streams));
+    if (rc)
+        return rc;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    IlArgs a{symbols, indexes, n, num_streams, num_tables, stream, nullptr,
+             stream_capacity_words, stream_words, nullptr, status, ws,
+             reinterpret_cast<uint32_t *>(ws + ws_scratch_offset(0)),
+             reinterpret_cast<uint32_t *>(ws + il_counts_offset(n, num_streams)),
+             reinterpret_cast<uint64_t *>(ws + il_ends_offset(n, num_streams))};
+    return launched(launch_il_encode(a, hstream));
+}
+
+int rans_decode_interleaved_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
+                                     const int32_t *indexes, uint64_t n, int32_t num_tables,
+                                     uint32_t num_streams, int32_t *symbols, int32_t *status,
+                                     void *workspace, uint64_t workspace_bytes,
+                                     hipStream_t hstream)
+{
+    if (num_streams == 0 || num_streams > RANS_MAX_STREAMS || !stream || !status ||
+        (n && (!symbols || !indexes)))
+        return RANS_E_ARG;
+    if (num_tables < 1 || num_tables > RANS_MAX_TABLES)
+        return RANS_E_TABLE;
+    if (n > RANS_MAX_SYMBOLS || stream_capacity_words < 1ull + num_streams)
+        return RANS_E_ARG;
+    int rc = check_workspace(workspace, workspace_bytes, ws_flags_offset());
+    if (rc)
+        return rc;
+    IlArgs a{nullptr, indexes, n, num_streams, num_tables, nullptr, stream,
+             stream_capacity_words, nullptr, symbols, status, static_cast<uint8_t *>(workspace),
+             nullptr, nullptr, nullptr};
+    return launched(launch_il_decode(a, hstream));
+}
+
 int rans_encode_interleaved(const int32_t *symbols, const int32_t *indexes, uint64_t n,
                             const int32_t *cdf, const int32_t *cdf_lengths,
                             const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
@@ -260,13 +308,9 @@ int rans_encode_interleaved(const int32_t *symbols, const int32_t *indexes, uint
     if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
                                   workspace_bytes, hstream)))
         return rc;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    IlArgs a{symbols, indexes, n, num_streams, num_tables, stream, nullptr,
-             stream_capacity_words, stream_words, nullptr, status, ws,
-             reinterpret_cast<uint32_t *>(ws + ws_scratch_offset(0)),
-             reinterpret_cast<uint32_t *>(ws + il_counts_offset(n, num_streams)),
-             reinterpret_cast<uint64_t *>(ws + il_ends_offset(n, num_streams))};
-    return launched(launch_il_encode(a, hstream));
+    return rans_encode_interleaved_prepared(symbols, indexes, n, num_tables, num_streams, stream,
+                                            stream_capacity_words, stream_words, status,
+                                            workspace, workspace_bytes, hstream);
 }
 
 int rans_decode_interleaved(const uint32_t *stream, uint64_t stream_capacity_words,
@@ -289,10 +333,9 @@ int rans_decode_interleaved(const uint32_t *stream, uint64_t stream_capacity_wor
     if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
                                   workspace_bytes, hstream)))
         return rc;
-    IlArgs a{nullptr, indexes, n, num_streams, num_tables, nullptr, stream,
-             stream_capacity_words, nullptr, symbols, status, static_cast<uint8_t *>(workspace),
-             nullptr, nullptr, nullptr};
-    return launched(launch_il_decode(a, hstream));
+    return rans_decode_interleaved_prepared(stream, stream_capacity_words, indexes, n,
+                                            num_tables, num_streams, symbols, status, workspace,
+                                            workspace_bytes, hstream);
 }
 
 int rans_gaussian_tables(const double *scales, int32_t num_tables, double tail_z,

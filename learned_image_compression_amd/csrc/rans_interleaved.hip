@@ -85,13 +85,16 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
             bad |= (lds_meta(r).lut & kRowInvalid) ? 1 : 0;
     if (block_or(&misc[0], bad) && !herr)
         herr = RANS_E_TABLE;
+    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (TPB / kWave) + tid / kWave);
     if (herr) {
         if (blockIdx.x == 0 && tid == 0)
             record_error(hdr, herr);
+        // the header kernel sums every stream's word count: leave none
+        // stale from an earlier call on this workspace
+        if (lane == 0 && t < S)
+            a.counts[t] = 0;
         return;
     }
-
-    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (TPB / kWave) + tid / kWave);
     if (t >= S)
         return;
     const uint64_t b = lane_begin(a.n, S, t), e = lane_begin(a.n, S, t + 1);
@@ -263,7 +266,9 @@ __global__ __launch_bounds__(kIlCopyThreads) void il_copy_kernel(IlArgs a)
 {
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t t = blockIdx.x * (kIlCopyThreads / kWave) + threadIdx.x / kWave;
-    if (t >= a.streams)
+    // after any error (the header kernel has published it) the output is
+    // unspecified, and word counts need not describe the scratch: copy nothing
+    if (t >= a.streams || *a.status != 0)
         return;
     const uint64_t end = a.ends[t], cnt = a.counts[t], beg = end - cnt;
     const uint64_t dst0 = 1ull + a.streams + beg;

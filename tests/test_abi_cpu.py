@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     from learned_image_compression_amd import binding as B
     assert sorted(B.EXPORTS) == names
     for name in names:
@@ -233,3 +233,32 @@ def test_decode_interleaved_host_checks(lib, kw, code):
     assert lib.rans_decode_interleaved(a["stream"], a["cap"], a["indexes"], a["n"], a["cdf"],
                                        a["lengths"], a["offsets"], a["K"], a["stride"], a["S"],
                                        a["out"], a["status"], a["ws"], a["ws_bytes"], 0) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=0), -1), (dict(S=(1 << 16) + 1), -1), (dict(stream=0), -1), (dict(words=0), -1),
+    (dict(status=0), -1), (dict(symbols=0), -1), (dict(indexes=0), -1), (dict(cap=4), -1),
+    (dict(n=(1 << 40)), -1), (dict(K=0), -2), (dict(K=(1 << 20)), -2), (dict(ws=0), -7),
+    (dict(ws=128), -7), (dict(ws_bytes=4096), -7),
+])
+def test_encode_interleaved_prepared_host_checks(lib, kw, code):
+    a = dict(symbols=1, indexes=1, n=10, K=8, S=4, stream=1, cap=1000, words=1, status=1, ws=256,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    assert lib.rans_encode_interleaved_prepared(a["symbols"], a["indexes"], a["n"], a["K"], a["S"],
+                                                a["stream"], a["cap"], a["words"], a["status"],
+                                                a["ws"], a["ws_bytes"], 0) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=0), -1), (dict(S=(1 << 16) + 1), -1), (dict(stream=0), -1), (dict(status=0), -1),
+    (dict(out=0), -1), (dict(indexes=0), -1), (dict(cap=2), -1), (dict(n=(1 << 40)), -1),
+    (dict(K=0), -2), (dict(ws=0), -7), (dict(ws=128), -7), (dict(ws_bytes=4096), -7),
+])
+def test_decode_interleaved_prepared_host_checks(lib, kw, code):
+    a = dict(stream=1, cap=1000, indexes=1, n=10, K=8, S=4, out=1, status=1, ws=256,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    assert lib.rans_decode_interleaved_prepared(a["stream"], a["cap"], a["indexes"], a["n"],
+                                                a["K"], a["S"], a["out"], a["status"], a["ws"],
+                                                a["ws_bytes"], 0) == code

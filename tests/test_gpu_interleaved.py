@@ -112,3 +112,84 @@ def test_corrupt_containers_like_the_oracle():
             assert np.array_equal(out, outo)
     st, _ = _gpu_decode(ref, idx, tables, S + 1)
     assert st == oracle.E_CORRUPT
+
+
+def test_prepared_interleaved_calls_code_many_tensors():
+    """One preparation, then interleaved encodes and decodes of several
+    tensors and stream counts (4-wave, 8-wave and 16-wave blocks) on that
+    workspace; each container equals the oracle's.  A table count that does
+    not match the prepared set is refused on the device, and a full call on
+    the same workspace replaces the prepared set."""
+    import torch
+    import gpu_util as G
+    B = G.B
+    w, tables, sym, idx = _workload("tiny")
+    n = w.n
+    ws = torch.zeros(B.load().rans_interleaved_workspace_bytes(n, 4096), dtype=torch.uint8,
+                     device=G.DEV)
+    B.prepare_tables(tables, ws)
+    for lo, hi, S in ((0, 16384, 4096), (5000, 16384, 2048), (100, 9000, 33), (7, 8, 1)):
+        G.say(f"[il-prepared] [{lo},{hi}) streams={S}")
+        rc, ref = oracle.encode_interleaved(w.symbols[lo:hi], w.indexes[lo:hi], w.cdf, w.lengths,
+                                            w.offsets, S, 64)
+        assert rc == 0
+        stream, nw, st = B.encode_interleaved(sym[lo:hi].contiguous(), idx[lo:hi].contiguous(),
+                                              tables, S, workspace=ws, prepared=True)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        assert np.array_equal(stream[: int(nw.item())].cpu().numpy().view(np.uint32), ref)
+        out, st = B.decode_interleaved(stream, idx[lo:hi].contiguous(), tables, S, workspace=ws,
+                                       prepared=True)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0 and np.array_equal(out.cpu().numpy(), w.symbols[lo:hi])
+    G.say("[il-prepared] table count differs from the prepared set")
+    wrong = B.Tables.from_numpy(w.cdf[:7], w.lengths[:7], w.offsets[:7], G.DEV)
+    _, _, st = B.encode_interleaved(sym, idx, wrong, 4, workspace=ws, prepared=True)
+    torch.cuda.synchronize()
+    assert int(st.item()) == B.NAME_TO_CODE["RANS_E_ARG"]
+    G.say("[il-prepared] a full call with other tables, then prepared calls with them")
+    wz = W.load("z")
+    tz = G.tables_of(wz)
+    zsym, zidx = G.to_dev(wz.symbols[:16384]), G.to_dev(wz.indexes[:16384])
+    rc, zref = oracle.encode_interleaved(wz.symbols[:16384], wz.indexes[:16384], wz.cdf,
+                                         wz.lengths, wz.offsets, 64, 64)
+    for prepared in (False, True):
+        stream, nw, st = B.encode_interleaved(zsym, zidx, tz, 64, workspace=ws, prepared=prepared)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        assert np.array_equal(stream[: int(nw.item())].cpu().numpy().view(np.uint32), zref)
+
+
+def test_encode_refused_up_front_copies_nothing():
+    """An encode refused before coding (a zero-frequency row) reports
+    RANS_E_TABLE; its streams' word counts are cleared, so the header and
+    copy kernels never work from counts an earlier call left in the
+    workspace, and the copy writes nothing.  A valid call on the same
+    workspace afterwards still matches the oracle."""
+    import torch
+    import gpu_util as G
+    B = G.B
+    w, tables, sym, idx = _workload("tiny")
+    S = 4096
+    ws = torch.zeros(B.load().rans_interleaved_workspace_bytes(w.n, S), dtype=torch.uint8,
+                     device=G.DEV)
+    rc, ref = oracle.encode_interleaved(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, S, 64)
+    G.say("[il-refused] a valid encode leaves word counts in the workspace")
+    stream, nw, st = B.encode_interleaved(sym, idx, tables, S, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    bad_cdf = w.cdf.copy()
+    bad_cdf[3, 2] = bad_cdf[3, 1]   # a zero frequency: the row is invalid
+    bad = B.Tables.from_numpy(bad_cdf, w.lengths, w.offsets, G.DEV)
+    G.say("[il-refused] the same call with an invalid row")
+    sentinel = torch.full_like(stream, 0x5A5A5A5A)
+    out, nw2, st = B.encode_interleaved(sym, idx, bad, S, workspace=ws, stream_out=sentinel)
+    torch.cuda.synchronize()
+    assert int(st.item()) == B.NAME_TO_CODE["RANS_E_TABLE"]
+    # the payload area is untouched (the header words may be written)
+    assert bool((out[1 + S:] == 0x5A5A5A5A).all())
+    G.say("[il-refused] a valid encode afterwards")
+    stream, nw, st = B.encode_interleaved(sym, idx, tables, S, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(stream[: int(nw.item())].cpu().numpy().view(np.uint32), ref)
