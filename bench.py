@@ -95,6 +95,14 @@ def table_set():
     return scales, tail_z, 2 * int(np.ceil(hi * tail_z)) + 3   # longest row: 3133
 
 
+def lane_groups(n: int, lanes: int, groups: int):
+    """Split lanes 0 .. lanes-1 into `groups` contiguous groups; returns per group
+    (first symbol, end symbol, lanes) with the lane partition's symbol bounds
+    (lane j starts at floor(j * n / lanes))."""
+    bounds = [(g * lanes // groups, (g + 1) * lanes // groups) for g in range(groups)]
+    return [(j0 * n // lanes, j1 * n // lanes, j1 - j0) for j0, j1 in bounds]
+
+
 def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200, split=None,
                  interleaved=None):
     """The oracle as it stands on the full workload: one thread, repeated ~10 s,
@@ -140,8 +148,7 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
     # its own).  The oracle is a C library called through ctypes, which
     # releases the interpreter lock for the call, so the threads run at once.
     threads = max(1, min(16, len(os.sched_getaffinity(0)), lanes))
-    bounds = [(g * lanes // threads, (g + 1) * lanes // threads) for g in range(threads)]
-    spans = [(j0 * w.n // lanes, j1 * w.n // lanes, j1 - j0) for j0, j1 in bounds]
+    spans = lane_groups(w.n, lanes, threads)
 
     def group(span):
         b, e, lg = span
