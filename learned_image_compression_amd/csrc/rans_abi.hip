@@ -235,7 +235,7 @@ uint64_t rans_interleaved_bound_words(uint64_t n, uint32_t num_streams)
 
 uint64_t rans_interleaved_workspace_bytes(uint64_t n, uint32_t num_streams)
 {
-    return il_ends_offset(n, num_streams) + 8ull * num_streams;
+    return il_counts_offset(n, num_streams) + 4ull * num_streams;
 }
 
 int rans_encode_interleaved_prepared(const int32_t *symbols, const int32_t *indexes, uint64_t n,
@@ -259,8 +259,7 @@ int rans_encode_interleaved_prepared(const int32_t *symbols, const int32_t *inde
     IlArgs a{symbols, indexes, n, num_streams, num_tables, stream, nullptr,
              stream_capacity_words, stream_words, nullptr, status, ws,
              reinterpret_cast<uint32_t *>(ws + ws_scratch_offset(0)),
-             reinterpret_cast<uint32_t *>(ws + il_counts_offset(n, num_streams)),
-             reinterpret_cast<uint64_t *>(ws + il_ends_offset(n, num_streams))};
+             reinterpret_cast<uint32_t *>(ws + il_counts_offset(n, num_streams))};
     return launched(launch_il_encode(a, hstream));
 }
 
@@ -282,7 +281,7 @@ int rans_decode_interleaved_prepared(const uint32_t *stream, uint64_t stream_cap
         return rc;
     IlArgs a{nullptr, indexes, n, num_streams, num_tables, nullptr, stream,
              stream_capacity_words, nullptr, symbols, status, static_cast<uint8_t *>(workspace),
-             nullptr, nullptr, nullptr};
+             nullptr, nullptr};
     return launched(launch_il_decode(a, hstream));
 }
 

@@ -36,7 +36,6 @@ namespace {
 
 constexpr uint32_t kIlW = kWave;         // states per stream
 constexpr int kIlAhead = 8;              // steps of symbols/indexes loaded ahead
-constexpr uint32_t kIlScanThreads = 1024;
 
 __device__ inline void record_error(WsHeader *hdr, int code)
 {
@@ -211,70 +210,59 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
         a.counts[t] = 2 * kIlW + min(E, cap);
 }
 
-// ---- encode: header (one workgroup) -------------------------------------------
-
-__global__ __launch_bounds__(kIlScanThreads) void il_scan_kernel(IlArgs a)
-{
-    __shared__ uint64_t part[kIlScanThreads / kWave];
-    WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
-    const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), S = a.streams;
-    const uint32_t per = (S + kIlScanThreads - 1) / kIlScanThreads;
-    const uint32_t s0 = min(S, tid * per), s1 = min(S, s0 + per);
-    uint64_t sum = 0;
-    for (uint32_t s = s0; s < s1; ++s)
-        sum += a.counts[s];
-    uint64_t inc = sum;
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint64_t v = __shfl_up(inc, o);
-        if (lane >= (uint32_t)o)
-            inc += v;
-    }
-    if (lane == kWave - 1)
-        part[tid / kWave] = inc;
-    __syncthreads();
-    uint64_t before = 0, total = 0;
-    for (uint32_t w = 0; w < kIlScanThreads / kWave; ++w) {
-        before += w < tid / kWave ? part[w] : 0;
-        total += part[w];
-    }
-    uint64_t run = before + inc - sum;
-    for (uint32_t s = s0; s < s1; ++s) {
-        run += a.counts[s];
-        a.ends[s] = run;
-        if (1ull + s < a.capacity)
-            a.stream[1 + s] = (uint32_t)run;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        const uint64_t words = 1ull + S + total;
-        int err = hdr->err;
-        if (!err && (words > a.capacity || total > 0xFFFFFFFFull))
-            err = RANS_E_CAPACITY;
-        if (a.capacity >= 1)
-            a.stream[0] = S;
-        *a.stream_words = words;
-        *a.status = err;
-        hdr->err = 0;
-    }
-}
-
-// ---- encode: copy every stream into the container -----------------------------
+// ---- encode: header and container (one wave per stream) -----------------------
+// Block b holds streams t0 = 4b .. 4b+3.  It first sums the word counts of
+// every stream before t0 (each block on its own: no block waits on another),
+// then each wave adds the counts of its block's earlier streams, writes its
+// header entry and copies its stream.  The wave of the last stream also
+// publishes the container length and the call's status.  Counts are the
+// encoder's (at most the stream's scratch span, or zero after a refusal), so
+// every copy reads inside its stream's scratch; writes stop at the capacity.
 
 constexpr int kIlCopyThreads = 4 * kWave;
 
 __global__ __launch_bounds__(kIlCopyThreads) void il_copy_kernel(IlArgs a)
 {
-    const uint32_t lane = threadIdx.x & (kWave - 1);
-    const uint32_t t = blockIdx.x * (kIlCopyThreads / kWave) + threadIdx.x / kWave;
-    // after any error (the header kernel has published it) the output is
-    // unspecified, and word counts need not describe the scratch: copy nothing
-    if (t >= a.streams || *a.status != 0)
+    __shared__ uint64_t part[kIlCopyThreads / kWave];
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
+    const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const uint32_t S = a.streams;
+    const uint32_t t0 = blockIdx.x * (kIlCopyThreads / kWave);
+    uint64_t sum = 0;
+    for (uint32_t s = tid; s < t0; s += kIlCopyThreads)
+        sum += a.counts[s];
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        sum += __shfl_xor(sum, o);
+    if (lane == 0)
+        part[wv] = sum;
+    __syncthreads();
+    uint64_t beg = 0;
+    for (uint32_t w = 0; w < kIlCopyThreads / kWave; ++w)
+        beg += part[w];
+    const uint32_t t = t0 + wv;
+    if (t >= S)
         return;
-    const uint64_t end = a.ends[t], cnt = a.counts[t], beg = end - cnt;
-    const uint64_t dst0 = 1ull + a.streams + beg;
-    if (dst0 + cnt > a.capacity)   // a too-small output: the status already says so
+    for (uint32_t s = t0; s < t; ++s)
+        beg += a.counts[s];
+    const uint64_t cnt = a.counts[t], end = beg + cnt;
+    if (lane == 0) {
+        if (1ull + t < a.capacity)
+            a.stream[1 + t] = (uint32_t)end;
+        if (t == S - 1) {
+            const uint64_t words = 1ull + S + end;
+            int err = hdr->err;
+            if (!err && (words > a.capacity || end > 0xFFFFFFFFull))
+                err = RANS_E_CAPACITY;
+            a.stream[0] = S;   // the capacity holds at least the header
+            *a.stream_words = words;
+            *a.status = err;
+            hdr->err = 0;
+        }
+    }
+    const uint64_t dst0 = 1ull + S + beg;
+    if (dst0 + cnt > a.capacity)   // a too-small output: the status says so
         return;
-    const uint32_t *scr = a.scratch + il_scratch_begin(a.n, a.streams, t);
+    const uint32_t *scr = a.scratch + il_scratch_begin(a.n, S, t);
     const uint32_t E = (uint32_t)cnt - 2 * kIlW;
     // the states, then the emitted words in reverse
     for (uint32_t i = lane; i < cnt; i += kWave)
@@ -536,7 +524,6 @@ hipError_t launch_il_encode(const IlArgs &a, hipStream_t s)
                                                            : launch_il_encode_t<4 * kWave>(a, s);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(il_scan_kernel, dim3(1), dim3(kIlScanThreads), 0, s, a);
     hipLaunchKernelGGL(il_copy_kernel, dim3(il_blocks(a.streams, kIlCopyThreads / kWave)),
                        dim3(kIlCopyThreads), 0, s, a);
     return hipGetLastError();

@@ -364,7 +364,6 @@ struct IlArgs {
     uint8_t *ws;
     uint32_t *scratch;         // per stream: 128 state words, then emitted words
     uint32_t *counts;          // [streams] words of each stream
-    uint64_t *ends;            // [streams] inclusive prefix of counts
 };
 
 // Stream t's scratch starts at word 2 b_t + 256 t (b_t its first symbol):
@@ -381,10 +380,6 @@ inline __host__ __device__ uint64_t il_scratch_words(uint64_t n, uint32_t stream
 inline __host__ __device__ uint64_t il_counts_offset(uint64_t n, uint32_t streams)
 {
     return ws_scratch_offset(0) + align_up(4 * il_scratch_words(n, streams), 256);
-}
-inline __host__ __device__ uint64_t il_ends_offset(uint64_t n, uint32_t streams)
-{
-    return il_counts_offset(n, streams) + align_up(4ull * streams, 256);
 }
 
 hipError_t launch_il_encode(const IlArgs &a, hipStream_t s);

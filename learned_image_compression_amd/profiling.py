@@ -207,6 +207,8 @@ def summarize_main(a) -> None:
                                       "write_kib": round(cw, 1), "fetch_scale": round(f_scale, 4),
                                       "write_scale": round(w_scale, 4)}}
             for key in ("il_encode_kernel", "il_scan_kernel", "il_copy_kernel", "il_decode_kernel"):
+                if key not in fetch or key not in write:
+                    continue
                 rb = fetch[key] * KIB * f_scale
                 wb = write[key] * KIB * w_scale
                 t[key] = {"fetch_kib_per_dispatch": round(fetch[key], 1),
