@@ -228,9 +228,13 @@ __global__ __launch_bounds__(kIlCopyThreads) void il_copy_kernel(IlArgs a)
     const uint32_t tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     const uint32_t S = a.streams;
     const uint32_t t0 = blockIdx.x * (kIlCopyThreads / kWave);
+    // t0 is a multiple of 4 and the counts are 256-byte aligned: 16-byte loads
     uint64_t sum = 0;
-    for (uint32_t s = tid; s < t0; s += kIlCopyThreads)
-        sum += a.counts[s];
+    const uint4 *c4 = reinterpret_cast<const uint4 *>(a.counts);
+    for (uint32_t q = tid; q < t0 / 4; q += kIlCopyThreads) {
+        const uint4 v = c4[q];
+        sum += (uint64_t)v.x + v.y + v.z + v.w;
+    }
     for (int o = kWave / 2; o > 0; o >>= 1)
         sum += __shfl_xor(sum, o);
     if (lane == 0)
