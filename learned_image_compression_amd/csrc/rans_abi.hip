@@ -92,7 +92,7 @@ int rans_encode_prepared(const int32_t *symbols, const int32_t *indexes, uint64_
     if (rc)
         return rc;
     EncodeArgs a{symbols, indexes, n, num_lanes, num_tables, stream, stream_capacity_words,
-                 stream_words, status, static_cast<uint8_t *>(workspace)};
+                 stream_words, status, static_cast<uint8_t *>(workspace), 0u, nullptr};
     return launched(launch_encode(a, hstream));
 }
 
@@ -114,7 +114,7 @@ int rans_decode_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
     if (rc)
         return rc;
     DecodeArgs a{stream, stream_capacity_words, indexes, n, num_lanes, num_tables, symbols,
-                 status, static_cast<uint8_t *>(workspace)};
+                 status, static_cast<uint8_t *>(workspace), 0u, nullptr};
     return launched(launch_decode(a, hstream));
 }
 
@@ -192,7 +192,7 @@ int rans_encode_with_splits(const int32_t *symbols, const int32_t *indexes, uint
                                   workspace_bytes, hstream)))
         return rc;
     EncodeArgs a{symbols, indexes, n, num_lanes, num_tables, stream, stream_capacity_words,
-                 stream_words, status, static_cast<uint8_t *>(workspace)};
+                 stream_words, status, static_cast<uint8_t *>(workspace), 0u, nullptr};
     a.pieces_log2 = (uint32_t)pl;
     a.split_meta = pl ? split_meta : nullptr;
     return launched(launch_encode(a, hstream));
@@ -222,7 +222,7 @@ int rans_decode_with_splits(const uint32_t *stream, uint64_t stream_capacity_wor
                                   workspace_bytes, hstream)))
         return rc;
     DecodeArgs a{stream, stream_capacity_words, indexes, n, num_lanes, num_tables, symbols,
-                 status, static_cast<uint8_t *>(workspace)};
+                 status, static_cast<uint8_t *>(workspace), 0u, nullptr};
     a.pieces_log2 = (uint32_t)pl;
     a.split_meta = pl ? split_meta : nullptr;
     return launched(launch_decode(a, hstream));

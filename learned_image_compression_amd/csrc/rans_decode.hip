@@ -326,7 +326,7 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
         const Rsrc rout = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
         const uint32_t jw = u0 >> pl;   // the wave's first lane
         // the wave's first word (scalar, so the stream's buffer descriptor is)
-        const uint64_t wbase = jw ? __builtin_amdgcn_readfirstlane(a.stream[jw]) : 0u;
+        const uint64_t wbase = jw ? (uint32_t)__builtin_amdgcn_readfirstlane(a.stream[jw]) : 0u;
         const uint64_t wavail = a.capacity - 1 - L;
         const uint64_t wbytes = wbase < wavail ? min(4 * (wavail - wbase), 1ull << 31) : 0;
         const Rsrc rstr = make_rsrc(a.stream + 1 + L + (wbase < wavail ? wbase : 0), (uint32_t)wbytes);

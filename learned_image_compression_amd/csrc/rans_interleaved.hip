@@ -318,9 +318,10 @@ __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
         const uint32_t m = (uint32_t)(e - b);
         // wave-uniform (t is), and kept in scalar registers so that the
         // stream's buffer descriptor is too
-        const uint64_t prev = t ? __builtin_amdgcn_readfirstlane(a.cstream[t]) : 0u;
-        const uint64_t endt = __builtin_amdgcn_readfirstlane(a.cstream[1 + t]);
-        if (__builtin_amdgcn_readfirstlane(a.cstream[0]) != S || endt < prev + 2 * kIlW ||
+        // (readfirstlane returns int: back to uint32_t before widening)
+        const uint64_t prev = t ? (uint32_t)__builtin_amdgcn_readfirstlane(a.cstream[t]) : 0u;
+        const uint64_t endt = (uint32_t)__builtin_amdgcn_readfirstlane(a.cstream[1 + t]);
+        if ((uint32_t)__builtin_amdgcn_readfirstlane(a.cstream[0]) != S || endt < prev + 2 * kIlW ||
             1ull + S + endt > a.capacity) {
             lerr = RANS_E_CORRUPT;
         } else {
