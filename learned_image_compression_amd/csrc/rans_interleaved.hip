@@ -29,6 +29,8 @@
 // workspace scratch (emission order, with each stream's word count), one
 // workgroup that scans the counts into the header, and a copy of every
 // stream into the container.  Decoding is one launch.
+#include <type_traits>
+
 #include "rans_coding.hpp"
 
 namespace rans {
@@ -132,9 +134,11 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
             r[u] = buf_load(ridx, off, 0);
         }
     };
-    auto step = [&](int32_t s, int32_t r, int64_t g) {
+    // `full` is std::true_type in groups whose every step lies inside the
+    // stream, which then carry no per-position bound checks
+    auto step = [&](auto full, int32_t s, int32_t r, int64_t g) {
         const uint32_t k = (uint32_t)g * kIlW + lane;
-        const bool valid = g >= 0 && k < m;
+        const bool valid = decltype(full)::value || (g >= 0 && k < m);
         const RowMeta mr = lds_meta(min((uint32_t)r, K - 1));
         const uint32_t mv = mr.mvf & 0xFFFFu;
         const uint32_t w = (uint32_t)s - (uint32_t)mr.offset;
@@ -190,16 +194,29 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
 
     load(sa, ia, (int64_t)G);
     load(sb, ib, (int64_t)G - kIlAhead);
-    for (int64_t g0 = G; g0 > 0; g0 -= 2 * kIlAhead) {
+    // steps g0 - 1 .. g0 - 2 kIlAhead
+    auto group = [&](auto full, int64_t g0) {
 #pragma unroll
         for (int u = 0; u < kIlAhead; ++u)
-            step(sa[u], ia[u], g0 - 1 - u);
+            step(full, sa[u], ia[u], g0 - 1 - u);
         load(sa, ia, g0 - 2 * kIlAhead);
 #pragma unroll
         for (int u = 0; u < kIlAhead; ++u)
-            step(sb[u], ib[u], g0 - kIlAhead - 1 - u);
+            step(full, sb[u], ib[u], g0 - kIlAhead - 1 - u);
         load(sb, ib, g0 - 3 * kIlAhead);
+    };
+    // the first group may hold the stream's partial last step; after it, the
+    // groups wholly inside the stream (steps >= 0, every one full), then the
+    // rest (steps below 0)
+    int64_t g0 = G;
+    if (g0 > 0) {
+        group(std::false_type{}, g0);
+        g0 -= 2 * kIlAhead;
     }
+    for (; g0 >= 2 * kIlAhead; g0 -= 2 * kIlAhead)
+        group(std::true_type{}, g0);
+    for (; g0 > 0; g0 -= 2 * kIlAhead)
+        group(std::false_type{}, g0);
     if (E > cap)
         lerr = lerr ? lerr : RANS_E_CAPACITY;
     scr[2 * lane] = (uint32_t)x;
@@ -360,9 +377,11 @@ __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
                 for (int u = 0; u < kIlAhead; ++u)
                     r[u] = buf_load(ridx, 4 * ((g0 + u) * kIlW + lane), 0);
             };
-            auto step = [&](int32_t r, const RowMeta &mr, uint32_t g) {
+            // `full` is std::true_type in groups whose every step lies inside
+            // the stream, which then carry no per-position bound checks
+            auto step = [&](auto full, int32_t r, const RowMeta &mr, uint32_t g) {
                 const uint32_t k = g * kIlW + lane;
-                const bool valid = k < m;
+                const bool valid = decltype(full)::value || k < m;
                 const uint32_t mv = mr.mvf & 0xFFFFu;
                 if (valid && (uint32_t)r >= K)
                     lerr = lerr ? lerr : RANS_E_INDEX;
@@ -442,18 +461,25 @@ __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
                 for (int u = 0; u < kIlAhead; ++u)
                     mt[u] = lds_meta(min((uint32_t)r[u], K - 1));
             };
-            for (uint32_t g0 = 0; g0 < G; g0 += 2 * kIlAhead) {
+            auto group = [&](auto full, uint32_t g0) {
                 metas(ia);
 #pragma unroll
                 for (int u = 0; u < kIlAhead; ++u)
-                    step(ia[u], mt[u], g0 + u);
+                    step(full, ia[u], mt[u], g0 + u);
                 load(ia, g0 + 2 * kIlAhead);
                 metas(ib);
 #pragma unroll
                 for (int u = 0; u < kIlAhead; ++u)
-                    step(ib[u], mt[u], g0 + kIlAhead + u);
+                    step(full, ib[u], mt[u], g0 + kIlAhead + u);
                 load(ib, g0 + 3 * kIlAhead);
-            }
+            };
+            // the groups wholly inside the stream, then the rest (at most one
+            // group past the stream's end: a stream holds G steps)
+            uint32_t g0 = 0;
+            for (; (g0 + 2 * kIlAhead) * kIlW <= m; g0 += 2 * kIlAhead)
+                group(std::true_type{}, g0);
+            for (; g0 < G; g0 += 2 * kIlAhead)
+                group(std::false_type{}, g0);
             if (__ballot(x != kStateLow) != 0 || cursor != W)
                 lerr = lerr ? lerr : RANS_E_CORRUPT;
         }
