@@ -17,10 +17,12 @@ import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-# From 4096 streams the kernels run 16-wave blocks: "tiny" at 4096 gives
-# streams of 4 symbols, "z" at 4100 and "y4kx8" at 5000 a partly filled last block.
+# Blocks hold 4 streams below 2048, 8 from 2048 and 16 from 4096: 2047 and
+# 4095 sit just below a boundary; "tiny" at 4096 gives streams of 4 symbols,
+# "z" at 4100 and "y4kx8" at 5000 a partly filled last block.
 CASES = [("tiny", 1), ("tiny", 4), ("tiny", 255), ("tiny", 300), ("z", 4), ("z", 1531),
          ("y1080", 64), ("y1080", 1024), ("y1080x16", 1024), ("y4kx8", 2048),
+         ("tiny", 2047), ("z", 4095),
          ("tiny", 4096), ("z", 4100), ("y1080x16", 4096), ("y4kx8", 5000)]
 
 _cache = {}
