@@ -413,42 +413,54 @@ __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
                 // a select, not a branch: the step stays one basic block
                 x = valid ? (uint64_t)f * (x >> kPrecision) + rr : x;
                 refill(valid & (x < kStateLow));
-                int64_t value = slot;
-                const bool esc = valid & (slot == mv);
-                if (__builtin_expect(__ballot(esc) != 0, 0)) {
-                    uint32_t nb = 0;
-                    if (esc) {
-                        nb = (uint32_t)x & 15u;
-                        x >>= kBypassBits;
-                    }
-                    refill(esc & (x < kStateLow));
-                    if (nb > 8u) {
-                        lerr = lerr ? lerr : RANS_E_CORRUPT;
-                        nb = 0;
-                    }
-                    uint32_t top = nb;
-                    for (int o = kWave / 2; o > 0; o >>= 1)
-                        top = max(top, (uint32_t)__shfl_xor((int)top, o));
-                    top = __builtin_amdgcn_readfirstlane(top);   // the wave's max in every lane
-                    uint64_t raw = 0;
-                    for (uint32_t j = 0; j < top; ++j) {
-                        const bool has = j < nb;
-                        if (has) {
-                            raw |= (uint64_t)((uint32_t)x & 15u) << (kBypassBits * j);
+                // Slots below the row's fast bound are ordinary symbols whose
+                // value offset + slot fits int32 (the bound is 0 for a row
+                // where it might not): a 32-bit add, no checks.  The escape
+                // slot and such rows take the rare path, which records the
+                // same errors in the same order as a check of every position.
+                int32_t out = (int32_t)(slot + (uint32_t)mr.offset);
+                const bool rare = valid & (slot >= (mr.mvf >> 16));
+                if (__builtin_expect(__ballot(rare) != 0, 0)) {
+                    int64_t value = slot;
+                    const bool esc = valid & (slot == mv);
+                    if (__ballot(esc) != 0) {
+                        uint32_t nb = 0;
+                        if (esc) {
+                            nb = (uint32_t)x & 15u;
                             x >>= kBypassBits;
                         }
-                        refill(has & (x < kStateLow));
-                    }
-                    if (esc) {
-                        if (raw >= (1ull << 31))
+                        refill(esc & (x < kStateLow));
+                        if (nb > 8u) {
                             lerr = lerr ? lerr : RANS_E_CORRUPT;
-                        value = (raw & 1) ? -(int64_t)(raw >> 1) - 1 : (int64_t)(raw >> 1) + mv;
+                            nb = 0;
+                        }
+                        uint32_t top = nb;
+                        for (int o = kWave / 2; o > 0; o >>= 1)
+                            top = max(top, (uint32_t)__shfl_xor((int)top, o));
+                        top = __builtin_amdgcn_readfirstlane(top);   // the wave's max in every lane
+                        uint64_t raw = 0;
+                        for (uint32_t j = 0; j < top; ++j) {
+                            const bool has = j < nb;
+                            if (has) {
+                                raw |= (uint64_t)((uint32_t)x & 15u) << (kBypassBits * j);
+                                x >>= kBypassBits;
+                            }
+                            refill(has & (x < kStateLow));
+                        }
+                        if (esc) {
+                            if (raw >= (1ull << 31))
+                                lerr = lerr ? lerr : RANS_E_CORRUPT;
+                            value = (raw & 1) ? -(int64_t)(raw >> 1) - 1 : (int64_t)(raw >> 1) + mv;
+                        }
+                    }
+                    if (rare) {
+                        const int64_t sym = value + mr.offset;
+                        if (sym < INT32_MIN || sym > INT32_MAX)
+                            lerr = lerr ? lerr : RANS_E_CORRUPT;
+                        out = (int32_t)sym;
                     }
                 }
-                const int64_t sym = value + mr.offset;
-                if (valid && (sym < INT32_MIN || sym > INT32_MAX))
-                    lerr = lerr ? lerr : RANS_E_CORRUPT;
-                buf_store(rout, valid ? 4 * k : 0x80000000u, 0, (int32_t)sym);
+                buf_store(rout, valid ? 4 * k : 0x80000000u, 0, out);
             };
             load(ia, 0);
             load(ib, kIlAhead);
