@@ -35,10 +35,10 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures
-import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -72,16 +72,6 @@ DESCRIPTION = {
 }
 
 
-def kernel_source_hash(name: str) -> str:
-    """Hash of the sources that make up one kernel (traffic numbers go stale with them)."""
-    csrc = os.path.join(ROOT, "learned_image_compression_amd", "csrc")
-    h = hashlib.sha256()
-    for f in ("rans_internal.hpp", f"rans_{name}.hip"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(kernel: str, config: str, lanes: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
     path = os.path.join(PROFILES, f"traffic_{kernel}_{config}_L{lanes}.json")
@@ -89,6 +79,7 @@ def measured_traffic(kernel: str, config: str, lanes: int):
         return None
     with open(path) as fh:
         t = json.load(fh)
+    from learned_image_compression_amd.profiling import kernel_source_hash
     if t.get("source_hash") != kernel_source_hash(kernel):
         return None
     return t.get("hbm_bytes_per_launch")
@@ -103,6 +94,24 @@ def table_set():
     scales = np.exp(np.log(lo) + (np.log(hi) - np.log(lo)) * np.arange(K) / (K - 1))
     tail_z = float(ndtri(1.0 - 5e-10))
     return scales, tail_z, 2 * int(np.ceil(hi * tail_z)) + 3   # longest row: 3133
+
+
+def cpu_model_name() -> str:
+    """The host CPU's full model line: lscpu's "Model name", else /proc/cpuinfo's
+    longest "model name" (some virtual machines shorten one of them)."""
+    names = []
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        names += [l.split(":", 1)[1].strip() for l in out.splitlines()
+                  if l.strip().lower().startswith("model name")]
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as fh:
+            names += [l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")]
+    except OSError:
+        pass
+    return max(names, key=len) if names else ""
 
 
 def lane_groups(n: int, lanes: int, groups: int):
@@ -121,16 +130,25 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
     the GPU's."""
     import numpy as np
     import oracle
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        rc, words = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, lanes)
-        rc2, out = oracle.decode(words, w.indexes, w.cdf, w.lengths, w.offsets, lanes)
-        times.append(time.perf_counter() - t0)
-        assert rc == 0 and rc2 == 0
-        if (time.perf_counter() - t_start >= min_seconds and len(times) >= 3) or len(times) >= max_reps:
-            break
+    # single thread, pinned to one core of this process's affinity set (the
+    # mask is set on the running process itself, and restored afterwards)
+    affinity = sorted(os.sched_getaffinity(0))
+    pinned = affinity[0]
+    os.sched_setaffinity(0, {pinned})
+    try:
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            rc, words = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, lanes)
+            rc2, out = oracle.decode(words, w.indexes, w.cdf, w.lengths, w.offsets, lanes)
+            times.append(time.perf_counter() - t0)
+            assert rc == 0 and rc2 == 0
+            if (time.perf_counter() - t_start >= min_seconds and len(times) >= 3) or \
+                    len(times) >= max_reps:
+                break
+    finally:
+        os.sched_setaffinity(0, set(affinity))
     assert words.size == gpu_words.size and np.array_equal(words, gpu_words), \
         "GPU container differs from the oracle's"
     assert np.array_equal(out, w.symbols)
@@ -157,7 +175,10 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
     # decodes a contiguous group of lanes (their symbols, as a container of
     # its own).  The oracle is a C library called through ctypes, which
     # releases the interpreter lock for the call, so the threads run at once.
-    threads = max(1, min(16, len(os.sched_getaffinity(0)), lanes))
+    # one thread per core of the affinity set, at most the 16 cores that one
+    # GPU's share of the host holds
+    nproc = len(affinity)
+    threads = max(1, min(16, nproc, lanes))
     spans = lane_groups(w.n, lanes, threads)
 
     def group(span):
@@ -177,16 +198,12 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
                     len(ttimes) >= max_reps:
                 break
     tmed = statistics.median(ttimes)
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as fh:
-            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
-    except OSError:
-        pass
+    model = cpu_model_name()
     return {
         "value": round(w.n / tmed / 1e9, 5),
         "unit": "Gsymbol/s",
         "cores": threads,
+        "nproc": nproc,
         "kind": "oracle",
         "sample": f"whole {w.name} workload ({w.n} symbols, {lanes} lanes), encode+decode, "
                   f"the lanes split into {threads} contiguous groups run on {threads} threads "
@@ -194,8 +211,10 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
                   f"repetitions ({sum(ttimes):.1f} s); {tmed / w.n * 1e9:.2f} ns/symbol",
         "cpu_model": model,
         "single_thread": {"value": round(w.n / med / 1e9, 5), "ns_per_symbol": round(med / w.n * 1e9, 2),
-                          "sample": f"the whole workload in one oracle call each way, median of "
-                                    f"{len(times)} repetitions ({sum(times):.1f} s)"},
+                          "pinned_cpu": pinned,
+                          "sample": f"the whole workload in one oracle call each way on one "
+                                    f"pinned core, median of {len(times)} repetitions "
+                                    f"({sum(times):.1f} s)"},
         "table_build_us": round(table_us, 1),
         "parity": "GPU container, split records, interleaved container and table set equal "
                   "the oracle's",
@@ -250,7 +269,7 @@ def main():
     total_words = int(nwords.item())
     gpu_words = stream[:total_words].cpu().numpy().view(np.uint32).copy()
     assert gpu_words[0] == lanes and int(gpu_words[lanes]) == total_words - 1 - lanes
-    B.decode_with_indexes(stream, idx, tables, lanes, symbols_out=out, status=st_dec,
+    B.decode_with_indexes(stream, idx, tables, symbols_out=out, status=st_dec,
                           workspace=ws, capacity_words=cap)
     B.check(st_dec, "decode")
     assert torch.equal(out.cpu(), torch.from_numpy(w.symbols)), "GPU decode != input"
@@ -269,7 +288,7 @@ def main():
                 lanes, vp(stream.data_ptr()), cap, vp(nwords.data_ptr()), vp(st_enc.data_ptr()),
                 vp(ws.data_ptr()), ws.numel(), hs)
     dec_args = (vp(stream.data_ptr()), cap, vp(idx.data_ptr()), n, tables.num_tables,
-                tables.stride, lanes, vp(out.data_ptr()), vp(st_dec.data_ptr()),
+                tables.stride, vp(out.data_ptr()), vp(st_dec.data_ptr()),
                 vp(ws.data_ptr()), ws.numel(), hs)
     prep, enc, dec = lib.rans_prepare_tables, lib.rans_encode_prepared, lib.rans_decode_prepared
 
@@ -335,8 +354,8 @@ def main():
     gpu_records = meta.cpu().numpy().view(np.uint32).copy()
 
     def split_decode_us(pieces, reps=20):
-        args = (vp(stream.data_ptr()), cap, vp(idx.data_ptr()), n, *tab_full, pieces,
-                vp(meta.data_ptr()), vp(out.data_ptr()), vp(sp_status.data_ptr()),
+        args = (vp(stream.data_ptr()), cap, vp(idx.data_ptr()), n, *tab_full[:5], pieces,
+                vp(meta.data_ptr()), meta.numel(), vp(out.data_ptr()), vp(sp_status.data_ptr()),
                 vp(ws.data_ptr()), ws.numel(), hs)
         sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps + 3)]
         for e in sev:
@@ -354,8 +373,9 @@ def main():
     # ---- interleaved streams: 64 states per stream, as many states as lanes -------
     S_il = args.streams if args.streams else max(1, min(4096, lanes // 64))
     il_cap = int(lib.rans_interleaved_bound_words(n, S_il))
-    il_ws = torch.zeros(int(lib.rans_interleaved_workspace_bytes(n, S_il)), dtype=torch.uint8,
-                        device=dev)
+    il_ws = torch.zeros(int(lib.rans_interleaved_workspace_bytes(n, S_il, tables.num_tables,
+                                                                 tables.stride)),
+                        dtype=torch.uint8, device=dev)
     il_stream = torch.empty(il_cap, dtype=torch.int32, device=dev)
     il_nw = torch.zeros(1, dtype=torch.int64, device=dev)
     il_args = (vp(sym.data_ptr()), vp(idx.data_ptr()), n, *tab_full[:5], S_il)
@@ -386,11 +406,12 @@ def main():
     # the same calls on tables prepared once (the full calls above left them
     # prepared in il_ws)
     il_enc_p = lambda: lib.rans_encode_interleaved_prepared(
-        vp(sym.data_ptr()), vp(idx.data_ptr()), n, tables.num_tables, S_il,
+        vp(sym.data_ptr()), vp(idx.data_ptr()), n, tables.num_tables, tables.stride, S_il,
         vp(il_stream.data_ptr()), il_cap, vp(il_nw.data_ptr()), vp(sp_status.data_ptr()),
         vp(il_ws.data_ptr()), il_ws.numel(), hs)
     il_dec_p = lambda: lib.rans_decode_interleaved_prepared(
-        vp(il_stream.data_ptr()), il_cap, vp(idx.data_ptr()), n, tables.num_tables, S_il,
+        vp(il_stream.data_ptr()), il_cap, vp(idx.data_ptr()), n, tables.num_tables, tables.stride,
+        S_il,
         vp(out.data_ptr()), vp(st_dec.data_ptr()), vp(il_ws.data_ptr()), il_ws.numel(), hs)
     out.zero_()
     for e in iev:

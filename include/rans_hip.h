@@ -37,14 +37,20 @@
  * same workspace can be reused by later calls.  Calls that share a
  * workspace, an output or a status word must not overlap in time.
  *
+ * Table sets.  Any valid set within RANS_MAX_TABLES rows of RANS_MAX_STRIDE
+ * entries is coded.  A set whose packed form fits the coding kernels' LDS
+ * budget (about 110 KiB for the encoder, 143 KiB for the decoder; the
+ * 64-row Gaussian set of the 1080p latent fits) is staged into LDS by every
+ * coding block; a larger one is read from the workspace through the caches,
+ * which is slower but gives the same bytes.
+ *
  * Errors.  The return value reports what the host can check before
  * launching (RANS_E_ARG, RANS_E_WORKSPACE, RANS_E_TABLE for bad sizes,
  * RANS_E_HIP for a failed launch).  Data-dependent errors are written by
  * the device to *status (0 on success; a bad CDF row, an index outside
  * [0, K), a symbol too far out of range, a too-small output, a corrupt
- * stream, or tables too large for the LDS budget).  When *status != 0 the
- * outputs are unspecified, but no kernel ever reads or writes outside the
- * buffers described here.
+ * stream).  When *status != 0 the outputs are unspecified, but no kernel
+ * ever reads or writes outside the buffers described here.
  */
 #ifndef RANS_HIP_H
 #define RANS_HIP_H
@@ -65,8 +71,7 @@ enum rans_status {
     RANS_E_CAPACITY = -5,     /* encoded container exceeds stream capacity */
     RANS_E_CORRUPT = -6,      /* the stream does not decode cleanly */
     RANS_E_WORKSPACE = -7,    /* workspace missing, misaligned or too small */
-    RANS_E_HIP = -8,          /* a HIP launch failed */
-    RANS_E_TABLE_SIZE = -9    /* the table set does not fit the LDS budget */
+    RANS_E_HIP = -8           /* a HIP launch failed */
 };
 
 /* Largest supported table count and row stride, and the largest symbol
@@ -84,7 +89,11 @@ enum rans_status {
  * 2 * symbols + 4 (a symbol costs at most 16 + 36 bits). */
 uint64_t rans_encode_bound_words(uint64_t n, uint32_t num_lanes);
 
-/* Workspace bytes needed by any call below with these sizes. */
+/* Workspace bytes needed by any call below with these sizes: a fixed header
+ * and look-back flag region (about 0.5 MiB), two table regions sized for
+ * num_tables rows of cdf_stride entries (at least the LDS budgets), and the
+ * encoder's scratch of 2 n + 4 num_lanes words.  A decode needs only the
+ * part before the scratch. */
 uint64_t rans_workspace_bytes(uint64_t n, uint32_t num_lanes, int32_t num_tables,
                               int32_t cdf_stride);
 
@@ -99,15 +108,19 @@ int rans_encode_with_indexes(const int32_t *symbols, const int32_t *indexes, uin
                              hipStream_t hstream);
 
 /* Decode n symbols (n = number of indexes) from the container at `stream`.
- * stream_capacity_words is the number of readable words at `stream`; the
- * container may be shorter (its header gives its extent).  num_lanes must
- * equal the container's lane count, else *status = RANS_E_CORRUPT. */
+ * The lane count is read from the container's first word (the container
+ * carries its own length bookkeeping: torch_ans 0.3.0, "Parallel ANS
+ * stream"), so there is no lane argument.  stream_capacity_words (at least
+ * 1) is the number of readable words at `stream`; the container may be
+ * shorter (its header gives its extent).  A lane count of 0 or above
+ * RANS_MAX_LANES, a header longer than the capacity, lane ends outside it or
+ * a lane that does not decode cleanly give *status = RANS_E_CORRUPT. */
 int rans_decode_with_indexes(const uint32_t *stream, uint64_t stream_capacity_words,
                              const int32_t *indexes, uint64_t n,
                              const int32_t *cdf, const int32_t *cdf_lengths,
                              const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
-                             uint32_t num_lanes, int32_t *symbols, int32_t *status,
-                             void *workspace, uint64_t workspace_bytes, hipStream_t hstream);
+                             int32_t *symbols, int32_t *status, void *workspace,
+                             uint64_t workspace_bytes, hipStream_t hstream);
 
 /* The two calls above are rans_prepare_tables followed by the matching
  * *_prepared call.  Callers that code many tensors with one table set
@@ -115,7 +128,9 @@ int rans_decode_with_indexes(const uint32_t *stream, uint64_t stream_capacity_wo
  * tables per call) may prepare once and code many times on one workspace.
  * rans_prepare_tables validates the rows on the device and packs them, with
  * the decoder's lookup table, into the workspace; row errors surface in the
- * *status of the next *_prepared call. */
+ * *status of the next *_prepared call.  num_tables and cdf_stride of a
+ * *_prepared call must be those of the prepared set, else *status reports
+ * RANS_E_ARG. */
 int rans_prepare_tables(const int32_t *cdf, const int32_t *cdf_lengths, const int32_t *offsets,
                         int32_t num_tables, int32_t cdf_stride, void *workspace,
                         uint64_t workspace_bytes, hipStream_t hstream);
@@ -128,9 +143,8 @@ int rans_encode_prepared(const int32_t *symbols, const int32_t *indexes, uint64_
 
 int rans_decode_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
                          const int32_t *indexes, uint64_t n, int32_t num_tables,
-                         int32_t cdf_stride, uint32_t num_lanes, int32_t *symbols,
-                         int32_t *status, void *workspace, uint64_t workspace_bytes,
-                         hipStream_t hstream);
+                         int32_t cdf_stride, int32_t *symbols, int32_t *status, void *workspace,
+                         uint64_t workspace_bytes, hipStream_t hstream);
 
 /* Split records: decode parallelism beyond the lane count (torch_ans 0.3.0,
  * "Related Projects", names Recoil, a rANS library of parallel rANS
@@ -149,7 +163,10 @@ int rans_decode_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
  * pieces is a power of two in [1, RANS_MAX_PIECES]; with pieces = 1 these
  * calls are rans_encode_with_indexes / rans_decode_with_indexes and
  * split_meta may be null.  split_meta holds 3 * num_lanes * (pieces - 1)
- * words (device memory, caller-owned).  Other arguments as above. */
+ * words (device memory, caller-owned); the decoder takes the lane count from
+ * the container and the size of split_meta as split_words, and reports
+ * RANS_E_ARG when the records the container needs exceed it.  Other
+ * arguments as above. */
 int rans_encode_with_splits(const int32_t *symbols, const int32_t *indexes, uint64_t n,
                             const int32_t *cdf, const int32_t *cdf_lengths, const int32_t *offsets,
                             int32_t num_tables, int32_t cdf_stride, uint32_t num_lanes,
@@ -161,7 +178,7 @@ int rans_decode_with_splits(const uint32_t *stream, uint64_t stream_capacity_wor
                             const int32_t *indexes, uint64_t n,
                             const int32_t *cdf, const int32_t *cdf_lengths,
                             const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
-                            uint32_t num_lanes, uint32_t pieces, const uint32_t *split_meta,
+                            uint32_t pieces, const uint32_t *split_meta, uint64_t split_words,
                             int32_t *symbols, int32_t *status, void *workspace,
                             uint64_t workspace_bytes, hipStream_t hstream);
 
@@ -180,14 +197,15 @@ int rans_decode_with_splits(const uint32_t *stream, uint64_t stream_capacity_wor
  * end_{num_streams-1}] followed by the streams.  This is a different
  * container from the lane container above.
  *
- * Workspace: rans_interleaved_workspace_bytes(n, num_streams) bytes for an
- * encode, rans_workspace_bytes(...) for a decode, the same contract as
- * above.  rans_interleaved_bound_words bounds the container.  num_streams in
+ * Workspace: rans_interleaved_workspace_bytes(n, num_streams, num_tables,
+ * cdf_stride) bytes for an encode, rans_workspace_bytes(...) for a decode,
+ * the same contract as above.  rans_interleaved_bound_words bounds the container.  num_streams in
  * [1, RANS_MAX_STREAMS].  Errors as for the lane calls; a stream that does
  * not end with every state at 2^31 and every word read gives
  * RANS_E_CORRUPT. */
 uint64_t rans_interleaved_bound_words(uint64_t n, uint32_t num_streams);
-uint64_t rans_interleaved_workspace_bytes(uint64_t n, uint32_t num_streams);
+uint64_t rans_interleaved_workspace_bytes(uint64_t n, uint32_t num_streams, int32_t num_tables,
+                                          int32_t cdf_stride);
 
 int rans_encode_interleaved(const int32_t *symbols, const int32_t *indexes, uint64_t n,
                             const int32_t *cdf, const int32_t *cdf_lengths,
@@ -209,20 +227,20 @@ int rans_decode_interleaved(const uint32_t *stream, uint64_t stream_capacity_wor
  * "Performance Tuning": reuse the coder rather than rebuild its tables) runs
  * rans_prepare_tables once on the workspace and then any number of these
  * calls on that workspace.  The workspace must also meet the size above
- * (rans_interleaved_workspace_bytes for an encode).  num_tables must equal
- * the prepared set's, or *status reports RANS_E_ARG; row errors found by
- * the preparation surface in *status as RANS_E_TABLE.  The host-side checks
- * and the other errors are those of the full calls. */
+ * (rans_interleaved_workspace_bytes for an encode).  num_tables and
+ * cdf_stride must equal the prepared set's, or *status reports RANS_E_ARG;
+ * row errors found by the preparation surface in *status as RANS_E_TABLE.
+ * The host-side checks and the other errors are those of the full calls. */
 int rans_encode_interleaved_prepared(const int32_t *symbols, const int32_t *indexes, uint64_t n,
-                                     int32_t num_tables, uint32_t num_streams, uint32_t *stream,
-                                     uint64_t stream_capacity_words, uint64_t *stream_words,
-                                     int32_t *status, void *workspace, uint64_t workspace_bytes,
-                                     hipStream_t hstream);
+                                     int32_t num_tables, int32_t cdf_stride, uint32_t num_streams,
+                                     uint32_t *stream, uint64_t stream_capacity_words,
+                                     uint64_t *stream_words, int32_t *status, void *workspace,
+                                     uint64_t workspace_bytes, hipStream_t hstream);
 
 int rans_decode_interleaved_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
                                      const int32_t *indexes, uint64_t n, int32_t num_tables,
-                                     uint32_t num_streams, int32_t *symbols, int32_t *status,
-                                     void *workspace, uint64_t workspace_bytes,
+                                     int32_t cdf_stride, uint32_t num_streams, int32_t *symbols,
+                                     int32_t *status, void *workspace, uint64_t workspace_bytes,
                                      hipStream_t hstream);
 
 /* Quantised CDF rows built on the device, one row per table (the step

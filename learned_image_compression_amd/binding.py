@@ -25,7 +25,6 @@ STATUS = {
     -6: "RANS_E_CORRUPT",
     -7: "RANS_E_WORKSPACE",
     -8: "RANS_E_HIP",
-    -9: "RANS_E_TABLE_SIZE",
 }
 NAME_TO_CODE = {v: k for k, v in STATUS.items()}
 
@@ -92,15 +91,15 @@ def load(path: str | None = None):
         lib.rans_encode_with_indexes.argtypes = [vp, vp, u64, vp, vp, vp, i32, i32, u32, vp, u64,
                                                  vp, vp, vp, u64, vp]
         lib.rans_encode_with_indexes.restype = ctypes.c_int
-        lib.rans_decode_with_indexes.argtypes = [vp, u64, vp, u64, vp, vp, vp, i32, i32, u32, vp,
-                                                 vp, vp, u64, vp]
+        lib.rans_decode_with_indexes.argtypes = [vp, u64, vp, u64, vp, vp, vp, i32, i32, vp, vp,
+                                                 vp, u64, vp]
         lib.rans_decode_with_indexes.restype = ctypes.c_int
         lib.rans_prepare_tables.argtypes = [vp, vp, vp, i32, i32, vp, u64, vp]
         lib.rans_prepare_tables.restype = ctypes.c_int
         lib.rans_encode_prepared.argtypes = [vp, vp, u64, i32, i32, u32, vp, u64, vp, vp, vp, u64,
                                              vp]
         lib.rans_encode_prepared.restype = ctypes.c_int
-        lib.rans_decode_prepared.argtypes = [vp, u64, vp, u64, i32, i32, u32, vp, vp, vp, u64, vp]
+        lib.rans_decode_prepared.argtypes = [vp, u64, vp, u64, i32, i32, vp, vp, vp, u64, vp]
         lib.rans_decode_prepared.restype = ctypes.c_int
         f64 = ctypes.c_double
         lib.rans_gaussian_tables.argtypes = [vp, i32, f64, i32, vp, vp, vp, vp, vp]
@@ -110,12 +109,12 @@ def load(path: str | None = None):
         lib.rans_encode_with_splits.argtypes = [vp, vp, u64, vp, vp, vp, i32, i32, u32, u32, vp,
                                                 u64, vp, vp, vp, vp, u64, vp]
         lib.rans_encode_with_splits.restype = ctypes.c_int
-        lib.rans_decode_with_splits.argtypes = [vp, u64, vp, u64, vp, vp, vp, i32, i32, u32, u32,
-                                                vp, vp, vp, vp, u64, vp]
+        lib.rans_decode_with_splits.argtypes = [vp, u64, vp, u64, vp, vp, vp, i32, i32, u32, vp,
+                                                u64, vp, vp, vp, u64, vp]
         lib.rans_decode_with_splits.restype = ctypes.c_int
         lib.rans_interleaved_bound_words.argtypes = [u64, u32]
         lib.rans_interleaved_bound_words.restype = u64
-        lib.rans_interleaved_workspace_bytes.argtypes = [u64, u32]
+        lib.rans_interleaved_workspace_bytes.argtypes = [u64, u32, i32, i32]
         lib.rans_interleaved_workspace_bytes.restype = u64
         lib.rans_encode_interleaved.argtypes = [vp, vp, u64, vp, vp, vp, i32, i32, u32, vp, u64,
                                                 vp, vp, vp, u64, vp]
@@ -123,11 +122,11 @@ def load(path: str | None = None):
         lib.rans_decode_interleaved.argtypes = [vp, u64, vp, u64, vp, vp, vp, i32, i32, u32, vp,
                                                 vp, vp, u64, vp]
         lib.rans_decode_interleaved.restype = ctypes.c_int
-        lib.rans_encode_interleaved_prepared.argtypes = [vp, vp, u64, i32, u32, vp, u64, vp, vp,
-                                                         vp, u64, vp]
+        lib.rans_encode_interleaved_prepared.argtypes = [vp, vp, u64, i32, i32, u32, vp, u64, vp,
+                                                         vp, vp, u64, vp]
         lib.rans_encode_interleaved_prepared.restype = ctypes.c_int
-        lib.rans_decode_interleaved_prepared.argtypes = [vp, u64, vp, u64, i32, u32, vp, vp, vp,
-                                                         u64, vp]
+        lib.rans_decode_interleaved_prepared.argtypes = [vp, u64, vp, u64, i32, i32, u32, vp, vp,
+                                                         vp, u64, vp]
         lib.rans_decode_interleaved_prepared.restype = ctypes.c_int
         lib.rans_latent_symbols.argtypes = [vp, vp, vp, u64, vp, i32, vp, vp, vp]
         lib.rans_latent_symbols.restype = ctypes.c_int
@@ -146,6 +145,11 @@ def encode_bound_words(n: int, lanes: int) -> int:
 
 def workspace_bytes(n: int, lanes: int, num_tables: int, stride: int) -> int:
     return int(load().rans_workspace_bytes(n, lanes, num_tables, stride))
+
+
+def decode_workspace_bytes(num_tables: int, stride: int) -> int:
+    """Workspace a decode needs: everything before the encoder's scratch."""
+    return int(load().rans_workspace_bytes(0, 1, num_tables, stride))
 
 
 def _ptr(t):
@@ -168,7 +172,14 @@ def _need(t, dtype, device, name):
 
 
 class Workspace:
-    """Zero-filled device workspace, grown (re-zeroed) on demand, one per device."""
+    """Zero-filled device workspace, grown (re-zeroed) on demand.
+
+    The default workspaces are kept per (device, stream): calls that share a
+    workspace must not overlap in time, and calls on one stream never do.
+    Growing a workspace replaces it with a new zero-filled buffer, which drops
+    any table set prepared in it (a later ``prepared=True`` call then reports
+    RANS_E_ARG); callers that prepare tables once pass their own workspace.
+    """
 
     def __init__(self, device):
         self.device = torch.device(device)
@@ -186,11 +197,15 @@ _workspaces: dict = {}
 
 
 def workspace_for(device) -> Workspace:
+    """The default workspace of `device` for its current stream."""
     device = torch.device(device)
-    key = (device.type, device.index if device.index is not None else torch.cuda.current_device())
-    if key not in _workspaces:
-        _workspaces[key] = Workspace(torch.device("cuda", key[1]))
-    return _workspaces[key]
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    stream = torch.cuda.current_stream(torch.device("cuda", index)).cuda_stream
+    key = (index, stream)
+    with _lock:
+        if key not in _workspaces:
+            _workspaces[key] = Workspace(torch.device("cuda", index))
+        return _workspaces[key]
 
 
 class Tables:
@@ -268,11 +283,12 @@ def encode_with_indexes(symbols: torch.Tensor, indexes: torch.Tensor, tables: Ta
     return stream_out, stream_words, status
 
 
-def decode_with_indexes(stream: torch.Tensor, indexes: torch.Tensor, tables: Tables,
-                        num_lanes: int, *, symbols_out: torch.Tensor | None = None,
+def decode_with_indexes(stream: torch.Tensor, indexes: torch.Tensor, tables: Tables, *,
+                        symbols_out: torch.Tensor | None = None,
                         status: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                         capacity_words: int | None = None, prepared: bool = False):
-    """Enqueue a decode; returns (symbols int32[n], status int32[1])."""
+    """Enqueue a decode; returns (symbols int32[n], status int32[1]).  The lane
+    count comes from the container's first word."""
     device = tables.device
     _need(stream, torch.int32, device, "stream")
     _need(indexes, torch.int32, device, "indexes")
@@ -285,16 +301,16 @@ def decode_with_indexes(stream: torch.Tensor, indexes: torch.Tensor, tables: Tab
         status = torch.zeros(1, dtype=torch.int32, device=device)
     cap = stream.numel() if capacity_words is None else int(capacity_words)
     ws = workspace if workspace is not None else workspace_for(device).get(
-        workspace_bytes(n, num_lanes, tables.num_tables, tables.stride))
+        decode_workspace_bytes(tables.num_tables, tables.stride))
     st = _stream(device)
     if prepared:
         rc = lib.rans_decode_prepared(_ptr(stream), cap, _ptr(indexes), n, tables.num_tables,
-                                      tables.stride, num_lanes, _ptr(symbols_out), _ptr(status),
+                                      tables.stride, _ptr(symbols_out), _ptr(status),
                                       _ptr(ws), ws.numel(), st)
     else:
         rc = lib.rans_decode_with_indexes(_ptr(stream), cap, _ptr(indexes), n, _ptr(tables.cdf),
                                           _ptr(tables.lengths), _ptr(tables.offsets),
-                                          tables.num_tables, tables.stride, num_lanes,
+                                          tables.num_tables, tables.stride,
                                           _ptr(symbols_out), _ptr(status), _ptr(ws), ws.numel(),
                                           st)
     _check_rc(rc, "rans_decode_with_indexes")
@@ -441,17 +457,16 @@ def encode_with_splits(symbols: torch.Tensor, indexes: torch.Tensor, tables: Tab
 
 
 def decode_with_splits(stream: torch.Tensor, split_records: torch.Tensor, indexes: torch.Tensor,
-                       tables: Tables, num_lanes: int, pieces: int, *,
+                       tables: Tables, pieces: int, *,
                        symbols_out: torch.Tensor | None = None,
                        workspace: torch.Tensor | None = None,
                        capacity_words: int | None = None):
-    """Enqueue a decode of every lane as `pieces` pieces; returns (symbols, status)."""
+    """Enqueue a decode of every lane as `pieces` pieces; returns (symbols, status).
+    The lane count comes from the container; the records must cover it."""
     device = tables.device
     _need(stream, torch.int32, device, "stream")
     _need(split_records, torch.int32, device, "split_records")
     _need(indexes, torch.int32, device, "indexes")
-    if split_records.numel() < 3 * num_lanes * max(pieces - 1, 0):
-        raise ValueError("split_records too small")
     n = indexes.numel()
     if symbols_out is None:
         symbols_out = torch.empty(n, dtype=torch.int32, device=device)
@@ -459,12 +474,12 @@ def decode_with_splits(stream: torch.Tensor, split_records: torch.Tensor, indexe
     status = torch.zeros(1, dtype=torch.int32, device=device)
     cap = stream.numel() if capacity_words is None else int(capacity_words)
     ws = workspace if workspace is not None else workspace_for(device).get(
-        workspace_bytes(n, num_lanes, tables.num_tables, tables.stride))
+        decode_workspace_bytes(tables.num_tables, tables.stride))
     rc = load().rans_decode_with_splits(
         _ptr(stream), cap, _ptr(indexes), n, _ptr(tables.cdf), _ptr(tables.lengths),
-        _ptr(tables.offsets), tables.num_tables, tables.stride, num_lanes, pieces,
-        _ptr(split_records), _ptr(symbols_out), _ptr(status), _ptr(ws), ws.numel(),
-        _stream(device))
+        _ptr(tables.offsets), tables.num_tables, tables.stride, pieces,
+        _ptr(split_records), split_records.numel(), _ptr(symbols_out), _ptr(status), _ptr(ws),
+        ws.numel(), _stream(device))
     _check_rc(rc, "rans_decode_with_splits")
     return symbols_out, status
 
@@ -490,10 +505,12 @@ def encode_interleaved(symbols: torch.Tensor, indexes: torch.Tensor, tables: Tab
     stream_words = torch.zeros(1, dtype=torch.int64, device=device)
     status = torch.zeros(1, dtype=torch.int32, device=device)
     ws = workspace if workspace is not None else workspace_for(device).get(
-        int(lib.rans_interleaved_workspace_bytes(n, num_streams)))
+        int(lib.rans_interleaved_workspace_bytes(n, num_streams, tables.num_tables,
+                                                 tables.stride)))
     if prepared:
         rc = lib.rans_encode_interleaved_prepared(_ptr(symbols), _ptr(indexes), n,
-                                                  tables.num_tables, num_streams, _ptr(stream_out),
+                                                  tables.num_tables, tables.stride, num_streams,
+                                                  _ptr(stream_out),
                                                   stream_out.numel(), _ptr(stream_words),
                                                   _ptr(status), _ptr(ws), ws.numel(),
                                                   _stream(device))
@@ -524,10 +541,10 @@ def decode_interleaved(stream: torch.Tensor, indexes: torch.Tensor, tables: Tabl
     status = torch.zeros(1, dtype=torch.int32, device=device)
     cap = stream.numel() if capacity_words is None else int(capacity_words)
     ws = workspace if workspace is not None else workspace_for(device).get(
-        workspace_bytes(n, num_streams, tables.num_tables, tables.stride))
+        decode_workspace_bytes(tables.num_tables, tables.stride))
     if prepared:
         rc = lib.rans_decode_interleaved_prepared(_ptr(stream), cap, _ptr(indexes), n,
-                                                  tables.num_tables, num_streams,
+                                                  tables.num_tables, tables.stride, num_streams,
                                                   _ptr(symbols_out), _ptr(status), _ptr(ws),
                                                   ws.numel(), _stream(device))
     else:

@@ -34,6 +34,20 @@ bool sizes_ok(uint64_t n, uint32_t lanes)
 
 int launched(hipError_t e) { return e == hipSuccess ? RANS_OK : RANS_E_HIP; }
 
+// A table count or row stride clamped to [1, hi]: sizes are computed before
+// the arguments are checked, and stay finite for any input.
+uint64_t clamp_size(int32_t v, uint32_t hi)
+{
+    return v < 1 ? 1u : ((uint32_t)v > hi ? (uint64_t)hi : (uint64_t)v);
+}
+
+// End of the table regions, where the scratch area starts.
+uint64_t tables_end(int32_t num_tables, int32_t cdf_stride)
+{
+    return ws_scratch_offset(clamp_size(num_tables, RANS_MAX_TABLES),
+                             clamp_size(cdf_stride, RANS_MAX_STRIDE));
+}
+
 // log2 of a piece count: a power of two in [1, RANS_MAX_PIECES], else -1
 int pieces_log2_of(uint32_t pieces)
 {
@@ -55,9 +69,7 @@ uint64_t rans_encode_bound_words(uint64_t n, uint32_t num_lanes)
 uint64_t rans_workspace_bytes(uint64_t n, uint32_t num_lanes, int32_t num_tables,
                               int32_t cdf_stride)
 {
-    (void)num_tables;
-    (void)cdf_stride;
-    return ws_scratch_offset(num_lanes) + 4ull * ws_scratch_words(n, num_lanes);
+    return tables_end(num_tables, cdf_stride) + 4ull * ws_scratch_words(n, num_lanes);
 }
 
 int rans_prepare_tables(const int32_t *cdf, const int32_t *cdf_lengths, const int32_t *offsets,
@@ -67,7 +79,7 @@ int rans_prepare_tables(const int32_t *cdf, const int32_t *cdf_lengths, const in
     int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
     if (rc)
         return rc;
-    if ((rc = check_workspace(workspace, workspace_bytes, ws_flags_offset())))
+    if ((rc = check_workspace(workspace, workspace_bytes, tables_end(num_tables, cdf_stride))))
         return rc;
     PrepArgs a{cdf, cdf_lengths, offsets, num_tables, cdf_stride,
                static_cast<uint8_t *>(workspace)};
@@ -91,30 +103,30 @@ int rans_encode_prepared(const int32_t *symbols, const int32_t *indexes, uint64_
                              rans_workspace_bytes(n, num_lanes, num_tables, cdf_stride));
     if (rc)
         return rc;
-    EncodeArgs a{symbols, indexes, n, num_lanes, num_tables, stream, stream_capacity_words,
-                 stream_words, status, static_cast<uint8_t *>(workspace), 0u, nullptr};
+    EncodeArgs a{symbols, indexes, n, num_lanes, num_tables, cdf_stride, stream,
+                 stream_capacity_words, stream_words, status, static_cast<uint8_t *>(workspace),
+                 0u, nullptr};
     return launched(launch_encode(a, hstream));
 }
 
 int rans_decode_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
                          const int32_t *indexes, uint64_t n, int32_t num_tables,
-                         int32_t cdf_stride, uint32_t num_lanes, int32_t *symbols,
-                         int32_t *status, void *workspace, uint64_t workspace_bytes,
-                         hipStream_t hstream)
+                         int32_t cdf_stride, int32_t *symbols, int32_t *status, void *workspace,
+                         uint64_t workspace_bytes, hipStream_t hstream)
 {
-    if (num_lanes == 0 || !stream || !status || (n && (!symbols || !indexes)))
+    if (!stream || !status || (n && (!symbols || !indexes)))
         return RANS_E_ARG;
     if (num_tables < 1 || num_tables > RANS_MAX_TABLES || cdf_stride < 3 ||
         cdf_stride > RANS_MAX_STRIDE)
         return RANS_E_TABLE;
-    if (!sizes_ok(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
+    if (n > RANS_MAX_SYMBOLS || stream_capacity_words < 1)
         return RANS_E_ARG;
     // the decoder uses only the header and the prepared tables
-    int rc = check_workspace(workspace, workspace_bytes, ws_flags_offset());
+    int rc = check_workspace(workspace, workspace_bytes, tables_end(num_tables, cdf_stride));
     if (rc)
         return rc;
-    DecodeArgs a{stream, stream_capacity_words, indexes, n, num_lanes, num_tables, symbols,
-                 status, static_cast<uint8_t *>(workspace), 0u, nullptr};
+    DecodeArgs a{stream, stream_capacity_words, indexes, n, num_tables, cdf_stride, symbols,
+                 status, static_cast<uint8_t *>(workspace), 0u, nullptr, 0u};
     return launched(launch_decode(a, hstream));
 }
 
@@ -148,24 +160,23 @@ int rans_decode_with_indexes(const uint32_t *stream, uint64_t stream_capacity_wo
                              const int32_t *indexes, uint64_t n,
                              const int32_t *cdf, const int32_t *cdf_lengths,
                              const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
-                             uint32_t num_lanes, int32_t *symbols, int32_t *status,
-                             void *workspace, uint64_t workspace_bytes, hipStream_t hstream)
+                             int32_t *symbols, int32_t *status, void *workspace,
+                             uint64_t workspace_bytes, hipStream_t hstream)
 {
-    if (num_lanes == 0 || !stream || !status || (n && (!symbols || !indexes)))
+    if (!stream || !status || (n && (!symbols || !indexes)))
         return RANS_E_ARG;
-    if (!sizes_ok(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
+    if (n > RANS_MAX_SYMBOLS || stream_capacity_words < 1)
         return RANS_E_ARG;
     int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
     if (rc)
         return rc;
-    if ((rc = check_workspace(workspace, workspace_bytes, ws_flags_offset())))
+    if ((rc = check_workspace(workspace, workspace_bytes, tables_end(num_tables, cdf_stride))))
         return rc;
     if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
                                   workspace_bytes, hstream)))
         return rc;
     return rans_decode_prepared(stream, stream_capacity_words, indexes, n, num_tables,
-                                cdf_stride, num_lanes, symbols, status, workspace,
-                                workspace_bytes, hstream);
+                                cdf_stride, symbols, status, workspace, workspace_bytes, hstream);
 }
 
 int rans_encode_with_splits(const int32_t *symbols, const int32_t *indexes, uint64_t n,
@@ -191,8 +202,9 @@ int rans_encode_with_splits(const int32_t *symbols, const int32_t *indexes, uint
     if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
                                   workspace_bytes, hstream)))
         return rc;
-    EncodeArgs a{symbols, indexes, n, num_lanes, num_tables, stream, stream_capacity_words,
-                 stream_words, status, static_cast<uint8_t *>(workspace), 0u, nullptr};
+    EncodeArgs a{symbols, indexes, n, num_lanes, num_tables, cdf_stride, stream,
+                 stream_capacity_words, stream_words, status, static_cast<uint8_t *>(workspace),
+                 0u, nullptr};
     a.pieces_log2 = (uint32_t)pl;
     a.split_meta = pl ? split_meta : nullptr;
     return launched(launch_encode(a, hstream));
@@ -202,29 +214,30 @@ int rans_decode_with_splits(const uint32_t *stream, uint64_t stream_capacity_wor
                             const int32_t *indexes, uint64_t n,
                             const int32_t *cdf, const int32_t *cdf_lengths,
                             const int32_t *offsets, int32_t num_tables, int32_t cdf_stride,
-                            uint32_t num_lanes, uint32_t pieces, const uint32_t *split_meta,
+                            uint32_t pieces, const uint32_t *split_meta, uint64_t split_words,
                             int32_t *symbols, int32_t *status, void *workspace,
                             uint64_t workspace_bytes, hipStream_t hstream)
 {
     const int pl = pieces_log2_of(pieces);
     if (pl < 0 || (pieces > 1 && !split_meta))
         return RANS_E_ARG;
-    if (num_lanes == 0 || !stream || !status || (n && (!symbols || !indexes)))
+    if (!stream || !status || (n && (!symbols || !indexes)))
         return RANS_E_ARG;
-    if (!sizes_ok(n, num_lanes) || stream_capacity_words < 1ull + num_lanes)
+    if (n > RANS_MAX_SYMBOLS || stream_capacity_words < 1)
         return RANS_E_ARG;
     int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
     if (rc)
         return rc;
-    if ((rc = check_workspace(workspace, workspace_bytes, ws_flags_offset())))
+    if ((rc = check_workspace(workspace, workspace_bytes, tables_end(num_tables, cdf_stride))))
         return rc;
     if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
                                   workspace_bytes, hstream)))
         return rc;
-    DecodeArgs a{stream, stream_capacity_words, indexes, n, num_lanes, num_tables, symbols,
-                 status, static_cast<uint8_t *>(workspace), 0u, nullptr};
+    DecodeArgs a{stream, stream_capacity_words, indexes, n, num_tables, cdf_stride, symbols,
+                 status, static_cast<uint8_t *>(workspace), 0u, nullptr, 0u};
     a.pieces_log2 = (uint32_t)pl;
     a.split_meta = pl ? split_meta : nullptr;
+    a.split_words = pl ? split_words : 0u;
     return launched(launch_decode(a, hstream));
 }
 
@@ -233,53 +246,60 @@ uint64_t rans_interleaved_bound_words(uint64_t n, uint32_t num_streams)
     return 1ull + num_streams + il_scratch_words(n, num_streams);
 }
 
-uint64_t rans_interleaved_workspace_bytes(uint64_t n, uint32_t num_streams)
+uint64_t rans_interleaved_workspace_bytes(uint64_t n, uint32_t num_streams, int32_t num_tables,
+                                          int32_t cdf_stride)
 {
-    return il_counts_offset(n, num_streams) + 4ull * num_streams;
+    return il_counts_offset(n, num_streams, clamp_size(num_tables, RANS_MAX_TABLES),
+                            clamp_size(cdf_stride, RANS_MAX_STRIDE)) +
+           4ull * num_streams;
 }
 
 int rans_encode_interleaved_prepared(const int32_t *symbols, const int32_t *indexes, uint64_t n,
-                                     int32_t num_tables, uint32_t num_streams, uint32_t *stream,
-                                     uint64_t stream_capacity_words, uint64_t *stream_words,
-                                     int32_t *status, void *workspace, uint64_t workspace_bytes,
-                                     hipStream_t hstream)
+                                     int32_t num_tables, int32_t cdf_stride, uint32_t num_streams,
+                                     uint32_t *stream, uint64_t stream_capacity_words,
+                                     uint64_t *stream_words, int32_t *status, void *workspace,
+                                     uint64_t workspace_bytes, hipStream_t hstream)
 {
     if (num_streams == 0 || num_streams > RANS_MAX_STREAMS || !stream || !stream_words ||
         !status || (n && (!symbols || !indexes)))
         return RANS_E_ARG;
-    if (num_tables < 1 || num_tables > RANS_MAX_TABLES)
+    if (num_tables < 1 || num_tables > RANS_MAX_TABLES || cdf_stride < 3 ||
+        cdf_stride > RANS_MAX_STRIDE)
         return RANS_E_TABLE;
     if (n > RANS_MAX_SYMBOLS || stream_capacity_words < 1ull + num_streams)
         return RANS_E_ARG;
     int rc = check_workspace(workspace, workspace_bytes,
-                             rans_interleaved_workspace_bytes(n, num_streams));
+                             rans_interleaved_workspace_bytes(n, num_streams, num_tables,
+                                                              cdf_stride));
     if (rc)
         return rc;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    IlArgs a{symbols, indexes, n, num_streams, num_tables, stream, nullptr,
+    IlArgs a{symbols, indexes, n, num_streams, num_tables, cdf_stride, stream, nullptr,
              stream_capacity_words, stream_words, nullptr, status, ws,
-             reinterpret_cast<uint32_t *>(ws + ws_scratch_offset(0)),
-             reinterpret_cast<uint32_t *>(ws + il_counts_offset(n, num_streams))};
+             reinterpret_cast<uint32_t *>(ws + tables_end(num_tables, cdf_stride)),
+             reinterpret_cast<uint32_t *>(ws + il_counts_offset(n, num_streams, num_tables,
+                                                                cdf_stride))};
     return launched(launch_il_encode(a, hstream));
 }
 
 int rans_decode_interleaved_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
                                      const int32_t *indexes, uint64_t n, int32_t num_tables,
-                                     uint32_t num_streams, int32_t *symbols, int32_t *status,
-                                     void *workspace, uint64_t workspace_bytes,
+                                     int32_t cdf_stride, uint32_t num_streams, int32_t *symbols,
+                                     int32_t *status, void *workspace, uint64_t workspace_bytes,
                                      hipStream_t hstream)
 {
     if (num_streams == 0 || num_streams > RANS_MAX_STREAMS || !stream || !status ||
         (n && (!symbols || !indexes)))
         return RANS_E_ARG;
-    if (num_tables < 1 || num_tables > RANS_MAX_TABLES)
+    if (num_tables < 1 || num_tables > RANS_MAX_TABLES || cdf_stride < 3 ||
+        cdf_stride > RANS_MAX_STRIDE)
         return RANS_E_TABLE;
     if (n > RANS_MAX_SYMBOLS || stream_capacity_words < 1ull + num_streams)
         return RANS_E_ARG;
-    int rc = check_workspace(workspace, workspace_bytes, ws_flags_offset());
+    int rc = check_workspace(workspace, workspace_bytes, tables_end(num_tables, cdf_stride));
     if (rc)
         return rc;
-    IlArgs a{nullptr, indexes, n, num_streams, num_tables, nullptr, stream,
+    IlArgs a{nullptr, indexes, n, num_streams, num_tables, cdf_stride, nullptr, stream,
              stream_capacity_words, nullptr, symbols, status, static_cast<uint8_t *>(workspace),
              nullptr, nullptr};
     return launched(launch_il_decode(a, hstream));
@@ -302,14 +322,16 @@ int rans_encode_interleaved(const int32_t *symbols, const int32_t *indexes, uint
     if (rc)
         return rc;
     if ((rc = check_workspace(workspace, workspace_bytes,
-                              rans_interleaved_workspace_bytes(n, num_streams))))
+                              rans_interleaved_workspace_bytes(n, num_streams, num_tables,
+                                                               cdf_stride))))
         return rc;
     if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
                                   workspace_bytes, hstream)))
         return rc;
-    return rans_encode_interleaved_prepared(symbols, indexes, n, num_tables, num_streams, stream,
-                                            stream_capacity_words, stream_words, status,
-                                            workspace, workspace_bytes, hstream);
+    return rans_encode_interleaved_prepared(symbols, indexes, n, num_tables, cdf_stride,
+                                            num_streams, stream, stream_capacity_words,
+                                            stream_words, status, workspace, workspace_bytes,
+                                            hstream);
 }
 
 int rans_decode_interleaved(const uint32_t *stream, uint64_t stream_capacity_words,
@@ -327,14 +349,14 @@ int rans_decode_interleaved(const uint32_t *stream, uint64_t stream_capacity_wor
     int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
     if (rc)
         return rc;
-    if ((rc = check_workspace(workspace, workspace_bytes, ws_flags_offset())))
+    if ((rc = check_workspace(workspace, workspace_bytes, tables_end(num_tables, cdf_stride))))
         return rc;
     if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
                                   workspace_bytes, hstream)))
         return rc;
     return rans_decode_interleaved_prepared(stream, stream_capacity_words, indexes, n,
-                                            num_tables, num_streams, symbols, status, workspace,
-                                            workspace_bytes, hstream);
+                                            num_tables, cdf_stride, num_streams, symbols, status,
+                                            workspace, workspace_bytes, hstream);
 }
 
 int rans_gaussian_tables(const double *scales, int32_t num_tables, double tail_z,
@@ -402,7 +424,6 @@ const char *rans_status_string(int code)
     case RANS_E_CORRUPT: return "corrupt stream";
     case RANS_E_WORKSPACE: return "workspace missing, misaligned or too small";
     case RANS_E_HIP: return "HIP launch failure";
-    case RANS_E_TABLE_SIZE: return "table set too large for the LDS budget";
     default: return "unknown status";
     }
 }

@@ -1,7 +1,7 @@
 // rans_decode.hip -- lane decoder: one rANS64 state per wavefront lane,
 // symbols read first to last, the symbol of each step found through the
-// LDS bucket lookup (the bucket's first slot, then one 8-byte read of the
-// next slot starts) with a short search of the bucket's slots as fallback.
+// bucket lookup (the bucket's first slot, then one 8-byte read of the next
+// slot starts) with a short search of the bucket's slots as fallback.
 //
 // Decoding rules (the inverse of the puts in rans_encode.hip; decode reads
 // the lane's words in order):
@@ -15,21 +15,32 @@
 // A lane must end at x = 2^31 with all of its words consumed, otherwise the
 // call reports RANS_E_CORRUPT; reads never leave the lane's header extent.
 //
+// The lane count comes from the container's first word (a stream carries its
+// own length bookkeeping: torch_ans "Parallel ANS stream"), so the launch
+// cannot depend on it: the grid is at most one block per CU, and each block
+// loops over the work units the lane count gives it.
+//
 // Per-symbol work.  The common step -- cum within three slots of the
 // bucket's first slot, an ordinary slot, the renormalisation word already in
-// the LDS ring -- is straight-line code whose result is committed at once.
-// Lanes outside it (cum further out, escape, drained ring, bad index) redo
-// the step from the saved state in one out-of-line branch, entered only when
-// some lane of the wave needs it.
+// the LDS ring -- is straight-line code.  Two ways to handle the rest:
+//  * waves of few lanes (the latency-bound regime) decode a whole round of
+//    kRound symbols speculatively, with no branch at all, and collect in one
+//    flag whether any step left the common case; only then (rarely) do the
+//    lanes concerned redo the round step by step;
+//  * waves of many lanes, where some lane leaves the common case in most
+//    rounds, commit each step at once, and lanes outside it redo that step
+//    on the slow path, entered only when some lane of the wave needs it.
 //
 // Memory schedule.  A lane works in rounds of kRound symbols.  Global memory
-// is touched only between rounds, in straight-line code with a fixed number
-// of accesses: the finished round's symbols are stored, the indexes of the
-// round after next are requested, and kRefill stream words are requested for
-// the lane's word ring in LDS.  Every loaded register is first read one
-// round after its load was issued, so the state chain inside a round never
-// waits on global memory.  Should a lane drain its ring within one round
-// (long bypass runs), it reads the word straight from global memory.
+// is touched only between rounds: the indexes of the round after next and
+// kRefill stream words for the lane's word ring in LDS are requested, then
+// the finished round's symbols are stored.  Every loaded register is first
+// read two rounds after its load was issued (a round takes about as long as
+// a loaded memory round trip), so the state chain inside a round never waits
+// on global memory.  Should a lane drain its ring (long bypass runs), it
+// reads the word straight from global memory.
+#include <type_traits>
+
 #include "rans_internal.hpp"
 
 namespace rans {
@@ -39,6 +50,9 @@ namespace {
 constexpr int kRound = 8;        // symbols per lane between memory phases
 constexpr uint32_t kRefill = 4;  // words requested per lane per memory phase
 constexpr uint32_t kNoStore = 0x80000000u;   // a buffer offset past every buffer
+constexpr uint32_t kMaxDecWaves = 2048;      // lanes are spread over at most this many waves
+constexpr uint32_t kDecTPB = 8 * kWave;      // one block shape: eight waves, two per SIMD
+constexpr uint32_t kSpecLanes = 4;           // waves of at most this many lanes decode speculatively
 
 __device__ inline void record_error(WsHeader *hdr, int code)
 {
@@ -81,18 +95,20 @@ struct Words {
     }
 };
 
-// Decoder tables in LDS at address 0: [meta | cdfm1 | first].  cdfm1[k] =
-// start(k) - 1 mod 2^16 (the terminal 65536 becomes 65535), so cum >= start(k)
-// is cum > cdfm1[k] and f(k) = cdfm1[k+1] - cdfm1[k] mod 2^16.
+// Decoder tables: [meta | cdfm1 | first], in LDS from address 0 or in the
+// workspace.  cdfm1[k] = start(k) - 1 mod 2^16 (the terminal 65536 becomes
+// 65535), so cum >= start(k) is cum > cdfm1[k] and f(k) = cdfm1[k+1] -
+// cdfm1[k] mod 2^16.
 struct DecTables {
     uint32_t q;              // 2^q buckets per row
     uint32_t shift;          // 16 - q: cumulative value -> bucket
     uint32_t K;
 };
 
-__device__ inline uint32_t cdfm1_at(const DecTables &, const RowMeta &m, uint32_t k)
+template <class Tab>
+__device__ inline uint32_t cdfm1_at(const Tab &tab, const RowMeta &m, uint32_t k)
 {
-    return lds_load<uint16_t>(m.base + 2 * k);
+    return tab.template load<uint16_t>(m.base + 2 * k);
 }
 
 // Slow step of one lane, from the state before the step.  `slot`, `f` and
@@ -107,11 +123,11 @@ __device__ inline uint32_t cdfm1_at(const DecTables &, const RowMeta &m, uint32_
 //    read from the ring when it holds them, else on the checked path;
 //  * out-of-range values and bad indexes are reported.
 // Writes the symbol to `out`; returns a status.
-template <int TPB>
+template <int TPB, class Tab>
 __device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint32_t bucket,
                                            bool beyond, uint32_t slot, uint32_t f, uint32_t rr,
                                            uint64_t &x, Words<TPB> &wd, const DecTables &t,
-                                           int32_t &out)
+                                           const Tab &tab, int32_t &out)
 {
     if ((uint32_t)r >= t.K)
         return RANS_E_INDEX;
@@ -120,7 +136,7 @@ __device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint32_t
     if (__ballot(beyond) != 0) {
         uint32_t lo = slot;   // value(lo) <= cum
         const uint32_t hi = (bucket + 1 < (1u << t.q))
-                                ? lds_load<uint16_t>((m.lut & ~kRowInvalid) + 2 * (bucket + 1))
+                                ? tab.template load<uint16_t>((m.lut & ~kRowInvalid) + 2 * (bucket + 1))
                                 : mv;
         // the slot is the last k in [lo, hi] with value(k) <= cum
         uint32_t c;
@@ -128,12 +144,12 @@ __device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint32_t
             c = 0;
 #pragma unroll
             for (uint32_t k = 1; k <= 8; ++k) {
-                const uint32_t v = cdfm1_at(t, m, min(lo + k, hi));
+                const uint32_t v = cdfm1_at(tab, m, min(lo + k, hi));
                 c += (lo + k <= hi && cum > v) ? 1u : 0u;
             }
             lo += c;
         } while (c == 8 && lo < hi);
-        const uint32_t sm1 = cdfm1_at(t, m, lo), em1 = cdfm1_at(t, m, lo + 1);
+        const uint32_t sm1 = cdfm1_at(tab, m, lo), em1 = cdfm1_at(tab, m, lo + 1);
         if (beyond) {
             slot = lo;
             f = (em1 - sm1) & 0xFFFFu;
@@ -202,92 +218,402 @@ __device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint32_t
     return err;
 }
 
-// One decoding step of one lane.  The bucket's first slot fs and the four
-// entries cdfm1[fs .. fs+3] (one 8-byte LDS read) resolve any cum that falls
-// in slots fs .. fs+2; that result is committed for every lane, and lanes
-// outside the common case (past the window, escape or out-of-range value,
-// renormalisation word not in the ring, bad index) redo the step on the slow
-// path.  A bad row index arrives with a fast bound of 0.
-template <int TPB>
-__device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_t &x, Words<TPB> &wd,
-                                            const DecTables &t, int32_t &out, int &lerr)
+// The common-case arithmetic of one step.  The bucket's first slot fs and the
+// four entries cdfm1[fs .. fs+3] (one 8-byte read) resolve any cum that falls
+// in slots fs .. fs+2.  Entries increase along a valid row and its terminal
+// entry is 65535, so a comparison with a later entry can only hold when the
+// earlier ones do, except past the terminal, where the slot it gives is at
+// least the escape slot and so never taken for an ordinary one.
+struct Lookup {
+    uint32_t bucket, slot, f, rr;
+    bool beyond;
+    uint64_t xn;   // the state after the step, before renormalisation
+};
+
+template <class Tab>
+__device__ __forceinline__ Lookup lookup_step(const RowMeta &m, uint64_t x, const DecTables &t,
+                                              const Tab &tab)
 {
-    const uint32_t cum = (uint32_t)x & (kTotal - 1);
-    const uint32_t xlo_m1 = (uint32_t)x - 1u;   // cum - 1 mod 2^16 in the low half
-    const uint32_t bucket = cum >> t.shift;
-    const uint32_t fs = lds_load<uint16_t>(m.lut + 2 * bucket);
-    const uint64_t v = lds_load<uint64_t>(m.base + 2 * fs);
+    Lookup s;
+    const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
+    const uint32_t cum = xlo & (kTotal - 1);
+    s.bucket = cum >> t.shift;
+    const uint32_t fs = tab.template load<uint16_t>(m.lut + 2 * s.bucket);
+    const uint64_t v = tab.u16x4(m.base + 2 * fs);
     const uint32_t wlo = (uint32_t)v, whi = (uint32_t)(v >> 32);   // cdfm1[fs..fs+1], [fs+2..fs+3]
     const bool c1 = cum > (wlo >> 16);
-    const bool c2 = c1 & (cum > (whi & 0xFFFFu));
-    const bool beyond = c2 & (cum > (whi >> 16));
-    const uint32_t slot = fs + (c1 ? 1u : 0u) + (c2 ? 1u : 0u);
+    const bool c2 = cum > (whi & 0xFFFFu);
+    s.beyond = cum > (whi >> 16);
+    s.slot = fs + (c1 ? 1u : 0u) + (c2 ? 1u : 0u);
     // the slot's cdfm1 pair (start - 1, next start - 1) as one packed word;
     // f = its high half minus its low half and rr = cum - start, both mod
     // 2^16 (16-bit subtractions on the halves, upper bits cleared)
     const uint32_t pair = c2 ? whi : (c1 ? __builtin_amdgcn_alignbit(whi, wlo, 16) : wlo);
-    uint32_t f, rr;
+    const uint32_t xlo_m1 = xlo - 1u;   // cum - 1 mod 2^16 in the low half
     asm("v_sub_u16_sdwa %0, %1, %1 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:WORD_1 src1_sel:WORD_0"
-        : "=v"(f) : "v"(pair));
+        : "=v"(s.f) : "v"(pair));
     asm("v_sub_u16_sdwa %0, %1, %2 dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:WORD_0"
-        : "=v"(rr) : "v"(xlo_m1), "v"(pair));
+        : "=v"(s.rr) : "v"(xlo_m1), "v"(pair));
     // f * (x >> 16) + rr with x >> 16 < 2^48 split at bit 32
-    const uint32_t xlo = (uint32_t)x, xhi = (uint32_t)(x >> 32);
     const uint32_t mid = __builtin_amdgcn_alignbit(xhi, xlo, 16);
-    const uint64_t lo64 = (uint64_t)f * mid + rr;
-    const uint32_t nhi = (uint32_t)(lo64 >> 32) + __umul24(f, xhi >> 16);
-    const uint64_t xn = ((uint64_t)nhi << 32) | (uint32_t)lo64;
-    const bool need = xn < kStateLow;
-    const bool slow = beyond | (slot >= (m.mvf >> 16)) | (need & (wd.pos >= wd.filled));
+    const uint64_t lo64 = (uint64_t)s.f * mid + s.rr;
+    const uint32_t nhi = (uint32_t)(lo64 >> 32) + __umul24(s.f, xhi >> 16);
+    s.xn = ((uint64_t)nhi << 32) | (uint32_t)lo64;
+    return s;
+}
+
+// One decoding step of one lane, committed at once.  Lanes outside the common
+// case (past the window, escape or out-of-range value, renormalisation word
+// not in the ring, bad index) redo the step on the slow path.  A bad row
+// index arrives with a fast bound of 0.
+template <int TPB, class Tab>
+__device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_t &x, Words<TPB> &wd,
+                                            const DecTables &t, const Tab &tab, int32_t &out,
+                                            int &lerr)
+{
+    const Lookup s = lookup_step(m, x, t, tab);
+    const bool need = s.xn < kStateLow;
+    const bool slow = s.beyond | (s.slot >= (m.mvf >> 16)) | (need & (wd.pos >= wd.filled));
     const uint64_t x0 = x;
     const uint32_t pos0 = wd.pos;
-    x = need ? ((xn << 32) | wd.next) : xn;
+    x = need ? ((s.xn << 32) | wd.next) : s.xn;
     wd.pos = pos0 + (need ? 1u : 0u);
-    out = (int32_t)(slot + (uint32_t)m.offset);
+    out = (int32_t)(s.slot + (uint32_t)m.offset);
     if (__builtin_expect(__ballot(slow) != 0, 0)) {
         if (slow) {
             x = x0;
             wd.pos = pos0;
-            const int ec = decode_slow<TPB>(r, m, bucket, beyond, slot, f, rr, x, wd, t, out);
+            const int ec = decode_slow<TPB>(r, m, s.bucket, s.beyond, s.slot, s.f, s.rr, x, wd, t,
+                                            tab, out);
             lerr = lerr ? lerr : ec;
         }
     }
     wd.next = wd.at(wd.pos);
 }
 
-template <int TPB, int CW, bool SPLIT>
-__global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
+// One speculative step: the common case applied with no branch; `bad` gathers
+// every reason the result might be wrong (a word read past the ring's filled
+// part is caught once per round, from the final position).
+template <int TPB, class Tab>
+__device__ __forceinline__ void decode_step_spec(const RowMeta &m, uint64_t &x, Words<TPB> &wd,
+                                                 const DecTables &t, const Tab &tab, int32_t &out,
+                                                 bool &bad)
 {
+    const Lookup s = lookup_step(m, x, t, tab);
+    const bool need = s.xn < kStateLow;
+    x = need ? ((s.xn << 32) | wd.next) : s.xn;
+    wd.pos += need ? 1u : 0u;
+    out = (int32_t)(s.slot + (uint32_t)m.offset);
+    bad = bad | s.beyond | (s.slot >= (m.mvf >> 16));
+    wd.next = wd.at(wd.pos);
+}
+
+// Everything one wave does for one work unit group: units u0 .. u0 + lpw - 1
+// (lane j's pieces u = j * 2^pl + s), one per wavefront lane.
+template <bool SPLIT, class Tab>
+__device__ __forceinline__ void decode_wave(const DecodeArgs &a, const Tab &tab, const DecTables &t,
+                                            uint32_t L, uint32_t lpw, uint32_t u0)
+{
+    constexpr int TPB = kDecTPB;
+    // the speculative rounds are built for LDS tables only (a set read from
+    // the workspace takes the per-step form)
+    constexpr bool kSpeculate = std::is_same<Tab, LdsTab>::value;
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
+    const uint32_t K = t.K;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & (kWave - 1);
+    const uint32_t ring = decode_ring_base(TPB) + 4 * tid;
+    const uint32_t pl = SPLIT ? a.pieces_log2 : 0u;
+    // the wave's unit range is the same in every lane: kept in scalar
+    // registers, so are the buffer descriptors built from it (the compiler
+    // cannot see that across the unit-group loop)
+    u0 = __builtin_amdgcn_readfirstlane(u0);
+    lpw = __builtin_amdgcn_readfirstlane(lpw);
+    L = __builtin_amdgcn_readfirstlane(L);
+    const uint32_t LV = L << pl;
+    const uint32_t u = u0 + lane;
+    const uint32_t j = u >> pl;                 // the unit's lane
+    const uint32_t ps = u & ((1u << pl) - 1);   // and piece
+    const bool spec = lpw <= kSpecLanes;        // wave-uniform
+    // first position of unit v (v = LV gives n)
+    auto unit_begin = [&](uint32_t v) -> uint64_t {
+        const uint32_t lj = v >> pl;
+        const uint64_t lb = lane_begin(a.n, L, lj);
+        return lj < L ? piece_begin(lb, lane_begin(a.n, L, lj + 1), pl, v & ((1u << pl) - 1)) : lb;
+    };
+    // the wave's index and symbol spans, and its stream words, as buffers
+    const uint32_t u1 = min(u0 + lpw, LV);
+    const uint64_t bw = unit_begin(u0), ew = unit_begin(u1);
+    const Rsrc ridx = make_rsrc(a.indexes + bw, (uint32_t)(4 * (ew - bw)));
+    const Rsrc rout = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
+    const uint32_t jw = u0 >> pl;   // the wave's first lane
+    // the wave's first word (scalar, so the stream's buffer descriptor is)
+    const uint64_t wbase = jw ? (uint32_t)__builtin_amdgcn_readfirstlane(a.stream[jw]) : 0u;
+    const uint64_t wavail = a.capacity - 1 - L;
+    const uint64_t wbytes = wbase < wavail ? min(4 * (wavail - wbase), 1ull << 31) : 0;
+    const Rsrc rstr = make_rsrc(a.stream + 1 + L + (wbase < wavail ? wbase : 0), (uint32_t)wbytes);
+    if (!(lane < lpw && u < LV))
+        return;
+    int lerr = 0;
+    const uint64_t beg_w = j ? a.stream[j] : 0u;
+    const uint64_t end_w = a.stream[1 + j];
+    // the piece's start and end: word offset in the lane and state (piece 0
+    // starts after the flushed state; the last piece ends at the start state
+    // with every word read)
+    const uint32_t W = (uint32_t)(end_w - beg_w);
+    const uint32_t *rec = a.split_meta + 3ull * ((uint64_t)((1u << pl) - 1) * j + ps);
+    uint32_t left0 = W - 2, left1 = 0;
+    if (ps)
+        left0 = rec[-1];
+    if (ps + 1 < (1u << pl))
+        left1 = rec[2];
+    const bool bad_rec = left0 > W - 2 || left1 > left0;
+    if (end_w < beg_w + 2 || 1ull + L + end_w > a.capacity || beg_w < wbase || bad_rec) {
+        lerr = RANS_E_CORRUPT;
+    } else {
+        Words<TPB> wd;
+        wd.w = a.stream + 1 + L + beg_w;
+        wd.ring = ring;
+        wd.count = W;
+        const uint32_t o = W - left0;   // the piece's first unread word
+        const uint32_t lw = (uint32_t)(4 * (beg_w - wbase));   // the lane's words in rstr
+        // words o-2, o-1 (piece 0: the final state) and [o, o + kDecRing): the
+        // first ring fill
+        const uint32_t lo = lw + 4 * (o - 2);
+        const u32x4 w0 = buf_load4(rstr, lo), w1 = buf_load4(rstr, lo + 16);
+        const u32x4 w2 = buf_load4(rstr, lo + 32);
+        uint64_t x = ps ? ((uint64_t)rec[-3] | ((uint64_t)rec[-2] << 32))
+                        : ((uint64_t)w0[0] | ((uint64_t)w0[1] << 32));
+        const uint64_t x_end =
+            ps + 1 < (1u << pl) ? ((uint64_t)rec[0] | ((uint64_t)rec[1] << 32)) : kStateLow;
+        {
+            static_assert(kDecRing == 8, "ring fill below assumes 8 slots");
+            const uint32_t v[kDecRing] = {w0[2], w0[3], w1[0], w1[1], w1[2], w1[3], w2[0], w2[1]};
+#pragma unroll
+            for (uint32_t k = 0; k < kDecRing; ++k)
+                wd.put(o + k, v[k]);
+        }
+        wd.pos = o;
+        wd.filled = min(wd.count, o + kDecRing);
+        wd.next = wd.at(o);
+        // Ring refills: kRefill words a round, requested two memory phases
+        // before they are put into the ring (pa serves the rounds that use
+        // ia, pb those that use ib), so a round never waits on a request of
+        // the round before.  req is the next word to request; a phase asks
+        // for [req, req + 4) only while req - pos <= 4, which keeps the four
+        // ring slots it will overwrite consumed by the time it lands.  A
+        // request that does not land at `filled` (the lane drained its ring
+        // and read ahead directly) is dropped, and requests restart there.
+        uint32_t pa[kRefill], pb[kRefill];
+        uint32_t pa_at = ~0u, pb_at = ~0u, req = wd.filled;
+
+        const uint64_t b = unit_begin(u);
+        const uint64_t e = unit_begin(u + 1);
+        const uint32_t nj = (uint32_t)(e - b);
+        const uint32_t ob = (uint32_t)(4 * (b - bw));   // the lane's first position
+        // Two index buffers used in turn (no register copies between rounds):
+        // a buffer is refilled in the memory phase right after its round and
+        // read again two rounds later.  Every memory phase issues the same
+        // global accesses in the same order (8 stores, 8 index loads, kRefill
+        // word loads), and the prologue runs two such phases too, so the
+        // compiler's wait counts only ever cover requests that are at least a
+        // round old.  Loads past the wave's span read 0; stores meant for
+        // nothing use kNoStore.
+        int32_t ia[kRound], ib[kRound], out[kRound];
+#pragma unroll
+        for (int k = 0; k < kRound; ++k)
+            out[k] = 0;
+        // The round's symbols: a full round as two 16-byte stores, a partial
+        // one a word per position (stores past the lane's end go nowhere).
+        // Every phase issues all ten stores, the ones it does not need at
+        // kNoStore (past every buffer, so dropped), so that each memory phase
+        // is the same sequence of requests and the compiler's wait counts
+        // stay exact across the loop.
+        auto store_round = [&](uint32_t k0, bool full) {
+            const uint32_t o16 = full ? ob + 4 * k0 : kNoStore;
+            buf_store4(rout, o16,
+                       u32x4{(uint32_t)out[0], (uint32_t)out[1], (uint32_t)out[2], (uint32_t)out[3]});
+            buf_store4(rout, o16 + 16,
+                       u32x4{(uint32_t)out[4], (uint32_t)out[5], (uint32_t)out[6], (uint32_t)out[7]});
+#pragma unroll
+            for (int k = 0; k < kRound; ++k)
+                buf_store(rout, !full && k0 + k < nj ? ob + 4 * (k0 + k) : kNoStore, 0, out[k]);
+        };
+        // indexes of positions k .. k+7 and kRefill stream words: 16-byte
+        // loads, the same three in every phase (past the wave's span or the
+        // stream they read 0; a phase that requests no words loads at
+        // kNoStore, past every buffer)
+        static_assert(kRefill == 4, "one 16-byte load of stream words");
+        auto load_next = [&](int32_t (&idx)[kRound], uint32_t (&pend)[kRefill], uint32_t &pend_at,
+                             uint32_t k) {
+            const bool ask = req - wd.pos <= kRefill;
+            const u32x4 i0 = buf_load4(ridx, ob + 4 * k), i1 = buf_load4(ridx, ob + 4 * k + 16);
+            const u32x4 w = buf_load4(rstr, ask ? lw + 4 * req : kNoStore);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                idx[q] = (int32_t)i0[q];
+                idx[4 + q] = (int32_t)i1[q];
+                pend[q] = w[q];
+            }
+            pend_at = ask ? req : ~0u;
+            req += ask ? kRefill : 0u;
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto ring_refill = [&](const uint32_t (&pend)[kRefill], uint32_t pend_at) {
+            if (pend_at == wd.filled) {
+#pragma unroll
+                for (uint32_t k = 0; k < kRefill; ++k)
+                    wd.put(wd.filled + k, pend[k]);
+                wd.filled = min(wd.count, wd.filled + kRefill);
+            } else if (pend_at != ~0u) {
+                req = max(wd.filled, wd.pos);   // requests no longer contiguous: restart
+            }
+            if (wd.filled < wd.pos) {   // the lane outran its ring via direct reads
+                wd.filled = wd.pos;
+                req = max(req, wd.pos);
+            }
+            wd.next = wd.at(wd.pos);
+        };
+        auto round = [&](int32_t (&idx)[kRound], uint32_t (&pend)[kRefill], uint32_t &pend_at,
+                         uint32_t k0) {
+            // row metadata; an index outside [0, K) reads row K-1 with a fast
+            // bound of 0 (its step then reports the index), which only a round
+            // holding such an index has to arrange
+            RowMeta m[kRound];
+            uint32_t imax = (uint32_t)idx[0];
+#pragma unroll
+            for (int k = 1; k < kRound; ++k)
+                imax = max(imax, (uint32_t)idx[k]);
+            if (__builtin_expect(__ballot(imax >= K) == 0, 1)) {
+#pragma unroll
+                for (int k = 0; k < kRound; ++k)
+                    m[k] = tab.meta((uint32_t)idx[k]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < kRound; ++k) {
+                    m[k] = tab.meta(min((uint32_t)idx[k], K - 1));
+                    if ((uint32_t)idx[k] >= K)
+                        m[k].mvf = 0;
+                }
+            }
+            // A round lies wholly inside every lane of the wave, or not.  Waves
+            // of few lanes first decode a whole round speculatively; the
+            // per-step form then runs only for the lanes where that went
+            // wrong (bad), or for every lane when the round was not
+            // speculated (many lanes a wave, or a partial round).
+            const bool full = __all(k0 + kRound <= nj);
+            bool general = true;
+            if constexpr (kSpeculate) {
+                if (spec && full) {
+                    const uint64_t x0 = x;
+                    const uint32_t pos0 = wd.pos, next0 = wd.next;
+                    bool bad = false;
+#pragma unroll
+                    for (int k = 0; k < kRound; ++k)
+                        decode_step_spec<TPB>(m[k], x, wd, t, tab, out[k], bad);
+                    bad = bad | (wd.pos > wd.filled);   // read a ring slot not yet filled
+                    if (bad) {
+                        x = x0;
+                        wd.pos = pos0;
+                        wd.next = next0;
+                    }
+                    general = bad;
+                }
+            }
+            if (__builtin_expect(__ballot(general) != 0, !kSpeculate || !spec || !full)) {
+#pragma unroll
+                for (int k = 0; k < kRound; ++k) {
+                    if (general) {
+                        out[k] = 0;
+                        if (k0 + k < nj && !lerr)
+                            decode_step<TPB>(idx[k], m[k], x, wd, t, tab, out[k], lerr);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            ring_refill(pend, pend_at);
+            // the phase's loads go out before its stores: a full round stores
+            // 16 bytes twice, a partial one word by word, and a later wait
+            // for these loads then never has to cover those stores
+            load_next(idx, pend, pend_at, k0 + 2 * kRound);
+            store_round(k0, full);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // prologue: two phases of the same shape (stores to nothing)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            if (p)
+                load_next(ib, pb, pb_at, kRound);
+            else
+                load_next(ia, pa, pa_at, 0);
+            store_round(nj, false);   // (positions from nj on: every store at kNoStore)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // both rounds always run (symbols past the lane end are skipped inside),
+        // so every path back to the loop head passes both memory phases
+        for (uint32_t k0 = 0; k0 < nj && !lerr; k0 += 2 * kRound) {
+            round(ia, pa, pa_at, k0);
+            round(ib, pb, pb_at, k0 + kRound);
+        }
+        if (!lerr && (x != x_end || wd.pos != W - left1))
+            lerr = RANS_E_CORRUPT;
+    }
+    if (lerr)
+        record_error(hdr, lerr);
+}
+
+template <bool SPLIT>
+__global__ __launch_bounds__(kDecTPB) void decode_kernel(DecodeArgs a)
+{
+    constexpr int TPB = kDecTPB;
     extern __shared__ __align__(16) uint8_t lds[];
-    // block bookkeeping after the table set and the rings: [0] flag OR, [1] last block
+    // block bookkeeping after the table set and before the rings: [0] flag OR, [1] last block
     uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kDecTableBudget);
 
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
-    const uint8_t *tab = a.ws + ws_tables_offset();
+    const uint8_t *tab = a.ws + ws_dec_offset();
     const uint32_t tid = threadIdx.x;
-    const uint32_t L = a.lanes;
 
     int herr = 0;
-    if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables)
+    if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables ||
+        hdr->cdf_stride != (uint32_t)a.stride)
         herr = RANS_E_ARG;
-    else if (!hdr->dec_ok)
-        herr = RANS_E_TABLE_SIZE;
     else if (lds_address_of(lds) != 0)   // table offsets are used as LDS addresses
         herr = RANS_E_HIP;
+    // the lane count from the container (header word 0), checked against the
+    // readable words and, with split records, against the record array
+    const uint32_t pl = SPLIT ? a.pieces_log2 : 0u;
+    const uint32_t L = (uint32_t)__builtin_amdgcn_readfirstlane(a.stream[0]);
+    if (!herr && (L == 0 || L > RANS_MAX_LANES || 1ull + L > a.capacity))
+        herr = RANS_E_CORRUPT;
+    if (!herr && SPLIT && 3ull * L * ((1u << pl) - 1) > a.split_words)
+        herr = RANS_E_ARG;
     const uint32_t K = (uint32_t)a.num_tables;
-    const uint32_t nbytes = herr ? 0u : hdr->dec_bytes;
-    const uint32_t q = hdr->lut_q;
-    stage_tables<TPB>(lds, tab, nbytes);
-    __syncthreads();
+    const bool in_lds = hdr->dec_lds != 0;
     DecTables t;
-    t.q = q;
-    t.shift = kPrecision - q;
+    t.q = hdr->lut_q;
+    t.shift = kPrecision - t.q;
     t.K = K;
-    const uint32_t ring = decode_ring_base(TPB) + 4 * tid;
+
+    // Work units: lane j's pieces u = j * 2^pl + s (one piece per lane
+    // without split records), spread thin over waves (lpw units a wave).
+    // With at most one wave per block in use, every block codes one wave
+    // (its other waves only help stage the tables); beyond, all eight code.
+    // Wave w of the grid takes unit groups w, w + G*cw, ...
+    const uint32_t LV = herr ? 0u : (L << pl);
+    const uint32_t lpw = lanes_per_wave_for(LV, kMaxDecWaves);
+    const uint32_t nw = (LV + lpw - 1) / lpw;
+    const uint32_t G = gridDim.x;
+    const uint32_t cw = nw <= G ? 1u : (uint32_t)(TPB / kWave);
+    const bool block_work = (uint64_t)blockIdx.x * cw < nw;
+    stage_tables<TPB>(lds, tab, (!herr && block_work && in_lds) ? hdr->dec_bytes : 0u);
+    __syncthreads();
     int bad = 0;
-    if (!herr)
+    if (!herr && block_work) {
+        const GlobalTab gt{tab};
         for (uint32_t r = tid; r < K; r += TPB)
-            bad |= (lds_meta(r).lut & kRowInvalid) ? 1 : 0;
+            bad |= ((in_lds ? lds_meta(r) : gt.meta(r)).lut & kRowInvalid) ? 1 : 0;
+    }
     if (tid == 0)
         misc[0] = 0u;
     __syncthreads();
@@ -297,204 +623,25 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     if (herr && blockIdx.x == 0 && tid == 0)
         record_error(hdr, herr);
 
-    // Work units: lane j's pieces u = j * 2^pl + s (one piece per lane
-    // without split records).  The wave codes units u0 .. u0 + lpw - 1, one
-    // per wavefront lane.
-    const uint32_t pl = SPLIT ? a.pieces_log2 : 0u;
-    const uint32_t LV = L << pl;
-    const uint32_t lpw = dec_lanes_per_wave(LV);
-    const uint32_t lane = tid & (kWave - 1);
-    // coding waves are 0 .. CW-1; wave and herr are the same in every lane,
-    // and scalar they keep the buffer descriptors and loops below uniform
+    // coding waves are 0 .. cw-1; the wave index and herr are the same in
+    // every lane, and scalar they keep the buffer descriptors and loops uniform
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     herr = __builtin_amdgcn_readfirstlane(herr);
-    const uint32_t u0 = __builtin_amdgcn_readfirstlane((blockIdx.x * CW + wave) * lpw);
-    const uint32_t u = u0 + lane;
-    const uint32_t j = u >> pl;            // the unit's lane
-    const uint32_t ps = u & ((1u << pl) - 1);   // and piece
-    // first position of unit v (v = LV gives n)
-    auto unit_begin = [&](uint32_t v) -> uint64_t {
-        const uint32_t lj = v >> pl;
-        const uint64_t lb = lane_begin(a.n, L, lj);
-        return lj < L ? piece_begin(lb, lane_begin(a.n, L, lj + 1), pl, v & ((1u << pl) - 1)) : lb;
-    };
-    // the wave's index and symbol spans, and its stream words, as buffers
-    if (!herr && wave < CW && u0 < LV) {
-        const uint32_t u1 = min(u0 + lpw, LV);
-        const uint64_t bw = unit_begin(u0), ew = unit_begin(u1);
-        const Rsrc ridx = make_rsrc(a.indexes + bw, (uint32_t)(4 * (ew - bw)));
-        const Rsrc rout = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
-        const uint32_t jw = u0 >> pl;   // the wave's first lane
-        // the wave's first word (scalar, so the stream's buffer descriptor is)
-        const uint64_t wbase = jw ? (uint32_t)__builtin_amdgcn_readfirstlane(a.stream[jw]) : 0u;
-        const uint64_t wavail = a.capacity - 1 - L;
-        const uint64_t wbytes = wbase < wavail ? min(4 * (wavail - wbase), 1ull << 31) : 0;
-        const Rsrc rstr = make_rsrc(a.stream + 1 + L + (wbase < wavail ? wbase : 0), (uint32_t)wbytes);
-        if (lane < lpw && u < LV) {
-            int lerr = 0;
-            const uint64_t beg_w = j ? a.stream[j] : 0u;
-            const uint64_t end_w = a.stream[1 + j];
-            // the piece's start and end: word offset in the lane and state
-            // (piece 0 starts after the flushed state; the last piece ends
-            // at the start state with every word read)
-            const uint32_t W = (uint32_t)(end_w - beg_w);
-            const uint32_t *rec = a.split_meta + 3ull * ((uint64_t)((1u << pl) - 1) * j + ps);
-            uint32_t left0 = W - 2, left1 = 0;
-            if (ps)
-                left0 = rec[-1];
-            if (ps + 1 < (1u << pl))
-                left1 = rec[2];
-            const bool bad_rec = left0 > W - 2 || left1 > left0;
-            if (a.stream[0] != L || end_w < beg_w + 2 || 1ull + L + end_w > a.capacity ||
-                beg_w < wbase || bad_rec) {
-                lerr = RANS_E_CORRUPT;
-            } else {
-                Words<TPB> wd;
-                wd.w = a.stream + 1 + L + beg_w;
-                wd.ring = ring;
-                wd.count = W;
-                const uint32_t o = W - left0;   // the piece's first unread word
-                const uint32_t lw = (uint32_t)(4 * (beg_w - wbase));   // the lane's words in rstr
-                // words o-2, o-1 (piece 0: the final state) and [o, o + kDecRing): the
-                // first ring fill
-                const uint32_t lo = lw + 4 * (o - 2);
-                const u32x4 w0 = buf_load4(rstr, lo), w1 = buf_load4(rstr, lo + 16);
-                const u32x4 w2 = buf_load4(rstr, lo + 32);
-                uint64_t x = ps ? ((uint64_t)rec[-3] | ((uint64_t)rec[-2] << 32))
-                                : ((uint64_t)w0[0] | ((uint64_t)w0[1] << 32));
-                const uint64_t x_end = ps + 1 < (1u << pl) ? ((uint64_t)rec[0] | ((uint64_t)rec[1] << 32))
-                                                           : kStateLow;
-                {
-                    static_assert(kDecRing == 8, "ring fill below assumes 8 slots");
-                    const uint32_t v[kDecRing] = {w0[2], w0[3], w1[0], w1[1], w1[2], w1[3], w2[0], w2[1]};
-#pragma unroll
-                    for (uint32_t k = 0; k < kDecRing; ++k)
-                        wd.put(o + k, v[k]);
-                }
-                wd.pos = o;
-                wd.filled = min(wd.count, o + kDecRing);
-                wd.next = wd.at(o);
-                uint32_t pend[kRefill];
-                uint32_t pend_at = wd.filled;
-
-                const uint64_t b = unit_begin(u);
-                const uint64_t e = unit_begin(u + 1);
-                const uint32_t nj = (uint32_t)(e - b);
-                const uint32_t ob = (uint32_t)(4 * (b - bw));   // the lane's first position
-                // Two index buffers used in turn (no register copies between
-                // rounds): a buffer is refilled in the memory phase right after
-                // its round and read again two rounds later.  Every memory phase
-                // issues the same global accesses in the same order (8 stores, 8
-                // index loads, kRefill word loads), and the prologue runs two
-                // such phases too, so the compiler's wait counts only ever cover
-                // requests that are at least a round old.  Loads past the
-                // wave's span read 0; stores meant for nothing use kNoStore.
-                int32_t ia[kRound], ib[kRound], out[kRound];
-#pragma unroll
-                for (int u = 0; u < kRound; ++u)
-                    out[u] = 0;
-                // a full round's symbols: two 16-byte stores; a partial round:
-                // one store per position (stores past the lane's end go nowhere)
-                auto store_full = [&](uint32_t k0) {
-                    buf_store4(rout, ob + 4 * k0,
-                               u32x4{(uint32_t)out[0], (uint32_t)out[1], (uint32_t)out[2], (uint32_t)out[3]});
-                    buf_store4(rout, ob + 4 * k0 + 16,
-                               u32x4{(uint32_t)out[4], (uint32_t)out[5], (uint32_t)out[6], (uint32_t)out[7]});
-                };
-                auto store_part = [&](uint32_t k0) {
-#pragma unroll
-                    for (int u = 0; u < kRound; ++u)
-                        buf_store(rout, k0 + u < nj ? ob + 4 * (k0 + u) : kNoStore, 0, out[u]);
-                };
-                // indexes of positions k .. k+7 and kRefill stream words: 16-byte
-                // loads (past the wave's span or the stream they read 0)
-                static_assert(kRefill == 4, "one 16-byte load of stream words");
-                auto load_next = [&](int32_t (&idx)[kRound], uint32_t k) {
-                    const u32x4 i0 = buf_load4(ridx, ob + 4 * k), i1 = buf_load4(ridx, ob + 4 * k + 16);
-                    const u32x4 w = buf_load4(rstr, lw + 4 * wd.filled);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        idx[u] = (int32_t)i0[u];
-                        idx[4 + u] = (int32_t)i1[u];
-                        pend[u] = w[u];
-                    }
-                    pend_at = wd.filled;
-                    __builtin_amdgcn_sched_barrier(0);
-                };
-                auto ring_refill = [&]() {
-                    if (pend_at == wd.filled && wd.filled + kRefill <= wd.pos + kDecRing) {
-#pragma unroll
-                        for (uint32_t k = 0; k < kRefill; ++k)
-                            wd.put(wd.filled + k, pend[k]);
-                        wd.filled = min(wd.count, wd.filled + kRefill);
-                    }
-                    if (wd.filled < wd.pos)   // the lane outran its ring via direct reads
-                        wd.filled = wd.pos;
-                    wd.next = wd.at(wd.pos);
-                };
-                auto round = [&](int32_t (&idx)[kRound], uint32_t k0) {
-                    // row metadata; an index outside [0, K) reads row K-1 with a
-                    // fast bound of 0 (its step then reports the index), which
-                    // only a round holding such an index has to arrange
-                    RowMeta m[kRound];
-                    uint32_t imax = (uint32_t)idx[0];
-#pragma unroll
-                    for (int u = 1; u < kRound; ++u)
-                        imax = max(imax, (uint32_t)idx[u]);
-                    if (__builtin_expect(__ballot(imax >= K) == 0, 1)) {
-#pragma unroll
-                        for (int u = 0; u < kRound; ++u)
-                            m[u] = lds_meta((uint32_t)idx[u]);
-                    } else {
-#pragma unroll
-                        for (int u = 0; u < kRound; ++u) {
-                            m[u] = lds_meta(min((uint32_t)idx[u], K - 1));
-                            if ((uint32_t)idx[u] >= K)
-                                m[u].mvf = 0;
-                        }
-                    }
-                    if (__all(k0 + kRound <= nj)) {
-                        // a full round for every lane of the wave
-#pragma unroll
-                        for (int u = 0; u < kRound; ++u)
-                            decode_step<TPB>(idx[u], m[u], x, wd, t, out[u], lerr);
-                        __builtin_amdgcn_sched_barrier(0);
-                        ring_refill();
-                        store_full(k0);
-                    } else {
-#pragma unroll
-                        for (int u = 0; u < kRound; ++u) {
-                            out[u] = 0;
-                            if (k0 + u < nj && !lerr)
-                                decode_step<TPB>(idx[u], m[u], x, wd, t, out[u], lerr);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                        ring_refill();
-                        store_part(k0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_next(idx, k0 + 2 * kRound);
-                };
-                // prologue: two phases of the same shape (stores to nothing)
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-#pragma unroll
-                    for (int u = 0; u < kRound; ++u)
-                        buf_store(rout, kNoStore, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_next(p ? ib : ia, p * kRound);
-                }
-                // both rounds always run (symbols past the lane end are skipped inside),
-                // so every path back to the loop head passes both memory phases
-                for (uint32_t k0 = 0; k0 < nj && !lerr; k0 += 2 * kRound) {
-                    round(ia, k0);
-                    round(ib, k0 + kRound);
-                }
-                if (!lerr && (x != x_end || wd.pos != W - left1))
-                    lerr = RANS_E_CORRUPT;
+    if (!herr && wave < cw) {
+        const uint32_t first = blockIdx.x * cw + wave, step = G * cw;
+        // The arguments are read afresh for every unit group: hoisted out of
+        // the loop, they would stay live across the whole coding body and
+        // crowd out its scalar registers.
+        if (in_lds) {
+            for (uint32_t w = first; w < nw; w += step) {
+                const DecodeArgs al = fresh_kernel_args<DecodeArgs>();
+                decode_wave<SPLIT>(al, LdsTab{}, t, L, lpw, w * lpw);
             }
-            if (lerr)
-                record_error(hdr, lerr);
+        } else {
+            for (uint32_t w = first; w < nw; w += step) {
+                const DecodeArgs al = fresh_kernel_args<DecodeArgs>();
+                decode_wave<SPLIT>(al, GlobalTab{al.ws + ws_dec_offset()}, t, L, lpw, w * lpw);
+            }
         }
     }
 
@@ -515,17 +662,42 @@ __global__ __launch_bounds__(TPB) void decode_kernel(DecodeArgs a)
     }
 }
 
-template <int TPB, int CW, bool SPLIT>
+// Compute units of the current device (the grid has at most one block per CU).
+uint32_t device_cus()
+{
+    static uint32_t cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return kCodingCUs;
+    if (!cached[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = (int)kCodingCUs;
+        cached[dev] = (uint32_t)v;
+    }
+    return cached[dev];
+}
+
+template <bool SPLIT>
 hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s)
 {
-    const uint32_t lds_bytes = decode_lds_bytes(TPB);
+    const uint32_t lds_bytes = decode_lds_bytes(kDecTPB);
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&decode_kernel<TPB, CW, SPLIT>),
+        reinterpret_cast<const void *>(&decode_kernel<SPLIT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (attr != hipSuccess)
         return attr;
-    const uint32_t blocks = (dec_waves(a.lanes << a.pieces_log2) + CW - 1) / CW;
-    hipLaunchKernelGGL((decode_kernel<TPB, CW, SPLIT>), dim3(blocks), dim3(TPB), lds_bytes, s, a);
+    // A valid container holds at least two words per lane after its header,
+    // which bounds the lane count by the readable words; more blocks than
+    // that many work units would find nothing to do.
+    uint64_t units_max = a.capacity > 3 ? (a.capacity - 1) / 3 : 1;
+    if (units_max > RANS_MAX_LANES)
+        units_max = RANS_MAX_LANES;
+    units_max <<= a.pieces_log2;
+    const uint32_t cus = device_cus();
+    const uint32_t blocks = units_max < cus ? (uint32_t)units_max : cus;
+    hipLaunchKernelGGL((decode_kernel<SPLIT>), dim3(blocks), dim3(kDecTPB), lds_bytes, s, a);
     return hipGetLastError();
 }
 
@@ -535,10 +707,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
 {
     // decoding split pieces is its own instantiation (the plain decoder
     // carries none of the piece bookkeeping)
-    const bool one = coding_one_per_cu(dec_waves(a.lanes << a.pieces_log2));
     if (a.pieces_log2 > 0)
-        return one ? launch_decode_t<4 * kWave, 1, true>(a, s) : launch_decode_t<8 * kWave, 8, true>(a, s);
-    return one ? launch_decode_t<4 * kWave, 1, false>(a, s) : launch_decode_t<8 * kWave, 8, false>(a, s);
+        return launch_decode_t<true>(a, s);
+    return launch_decode_t<false>(a, s);
 }
 
 }  // namespace rans

@@ -55,15 +55,8 @@ __device__ inline void record_error(WsHeader *hdr, int code)
 constexpr int kRound = 8;   // positions per lane between memory phases
 constexpr uint32_t kNoStore = 0x80000000u;   // a buffer offset past every buffer
 
-// Encoder tables in LDS at address 0: [meta | pairs], pair = start | f << 16.
-struct EncTables {
-    uint32_t K;
-};
-
-__device__ inline uint32_t pair_of(const EncTables &, const RowMeta &m, uint32_t slot)
-{
-    return lds_load<uint32_t>(m.base + 4 * slot);
-}
+// Encoder tables: [meta | pairs], pair = start | f << 16, in LDS from address
+// 0 or in the workspace (rans_internal.hpp: LdsTab, GlobalTab).
 
 // Spill state of one lane.  Word k of the lane (its k-th spill) belongs at
 // byte offset top - 4 - 4k of the wave's scratch buffer.  During a round the
@@ -94,9 +87,9 @@ struct Spill {
 // The puts of one symbol off the common path (an escaped value, or a lane
 // near the end of its segment), applied last to first; the row index is in
 // range.  Returns a status code.
-template <int TPB>
-__device__ __forceinline__ int encode_slow(int32_t s, const RowMeta m, const EncTables &t,
-                                           uint64_t &x, Spill<TPB> &sp)
+template <int TPB, class Tab>
+__device__ __forceinline__ int encode_slow(int32_t s, const RowMeta m, const Tab &tab, uint64_t &x,
+                                           Spill<TPB> &sp)
 {
     int err = 0;
     const uint32_t mv = m.mvf & 0xFFFFu;
@@ -121,13 +114,370 @@ __device__ __forceinline__ int encode_slow(int32_t s, const RowMeta m, const Enc
     if (esc)
         put_bits(nb);
     // the REG put of the slot
-    const uint32_t pr = pair_of(t, m, esc ? mv : (uint32_t)v);
+    const uint32_t pr = tab.template load<uint32_t>(m.base + 4 * (esc ? mv : (uint32_t)v));
     const uint32_t f = pr >> 16;
     const bool spill = x >= ((uint64_t)f << (63 - kPrecision));
     sp.put_if(spill, (uint32_t)x);
     x = spill ? (x >> 32) : x;
     x = reg_step(x, pr & 0xFFFFu, f, reciprocal(f));
     return err;
+}
+
+// The coding of lane j (positions [b, e)), last position to first, into its
+// scratch segment; returns the lane's word count (flushed state included) and
+// its first error.
+struct LaneResult {
+    uint32_t words;
+    int err;
+};
+
+template <int TPB, class Tab>
+__device__ __forceinline__ LaneResult encode_lane(const EncodeArgs &a, const Tab &tab, uint32_t K,
+                                                  uint32_t L, uint32_t j, uint64_t bw, Rsrc rsym,
+                                                  Rsrc ridx, Spill<TPB> sp)
+{
+    int lerr = 0;
+    uint32_t words = 0;
+    const uint64_t b = lane_begin(a.n, L, j);
+    const uint64_t e = lane_begin(a.n, L, j + 1);
+    const uint32_t nj = (uint32_t)(e - b);
+    sp.cb = 0;
+    sp.cb0 = 0;
+    sp.capb = 4 * (2 * nj + 4);
+    sp.overflow = false;
+    uint64_t x = kStateLow;
+    // Rounds are aligned to the lane's first position: step k codes
+    // position b + R8 - 1 - k, where R8 is nj rounded up to whole rounds,
+    // and the steps below pad = R8 - nj (past the lane's end) are no
+    // positions.  A round's window of positions then never starts before
+    // the lane (so never before the wave's buffer), and the loads need no
+    // clamping branch.
+    const uint32_t R8 = (nj + kRound - 1) / kRound * kRound;
+    const uint32_t pad = R8 - nj;
+    auto valid = [&](uint32_t k) { return k >= pad && k < R8; };
+    // Split records: the next cut to record (cuts are met last to
+    // first) and the step k = R8 - 1 - (c - b) at which position c
+    // is coded; a round holding it takes the per-position path,
+    // which records the state and the words emitted so far right
+    // after that position.
+    const uint32_t npieces = 1u << a.pieces_log2;
+    int32_t cut_s = (int32_t)npieces - 1;
+    auto cut_step = [&](int32_t s) -> uint32_t {
+        return R8 - 1 - (uint32_t)(piece_begin(b, e, a.pieces_log2, (uint32_t)s) - b);
+    };
+    uint32_t cut_k = (npieces > 1 && nj > 0) ? cut_step(cut_s) : ~0u;
+    auto record_cut = [&]() {
+        uint32_t *m = a.split_meta + 3ull * ((uint64_t)(npieces - 1) * j + cut_s - 1);
+        m[0] = (uint32_t)x;
+        m[1] = (uint32_t)(x >> 32);
+        m[2] = sp.cb >> 2;
+        --cut_s;
+        cut_k = (cut_s >= 1 && nj > 0) ? cut_step(cut_s) : ~0u;
+    };
+    // byte offset, in the wave's buffers, of the first position of the
+    // lane's last whole window (steps R8 - 8 .. R8 - 1); a window of later
+    // steps lies past the lane's end (its loads read the next lane's values
+    // or, past the wave's buffer, zeros: only for steps that are no
+    // positions)
+    const uint32_t pbase = (uint32_t)(4 * (b - bw));
+    int32_t sa[kRound], ia[kRound], sb[kRound], ib[kRound];
+    // Symbols and indexes of steps k .. k+7: two 16-byte loads each, always
+    // the same four loads in the same order, so that the compiler's wait
+    // counts cover exactly the requests that are a round old or older.
+    // Rounds past the lane (k >= R8) reload its first window: they code
+    // nothing.
+    auto load_next = [&](int32_t (&sym)[kRound], int32_t (&idx)[kRound], uint32_t k) {
+        // (an empty lane loads at its own position: in the buffer, or past it)
+        const uint32_t kc = R8 >= kRound ? min(k, R8 - kRound) : 0u;
+        const uint32_t lo = R8 >= kRound ? pbase + 4 * (R8 - kRound - kc) : pbase;
+        const u32x4 s0 = buf_load4(rsym, lo), s1 = buf_load4(rsym, lo + 16);
+        const u32x4 i0 = buf_load4(ridx, lo), i1 = buf_load4(ridx, lo + 16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            sym[7 - u] = (int32_t)s0[u];
+            sym[3 - u] = (int32_t)s1[u];
+            idx[7 - u] = (int32_t)i0[u];
+            idx[3 - u] = (int32_t)i1[u];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // The round's words (ring slots 0 .. n-1) go to positions
+    // cb0/4 .. cb0/4 + n - 1, i.e. descending byte offsets from
+    // top - 4 - cb0.  Slots 0..7 are always stored, as two 16-byte
+    // stores (slots past n hold stale words for positions that later
+    // words or the final state overwrite); a round of more than 8
+    // words, or a lane near the end of its segment, stores word by
+    // word.
+    auto store_words = [&]() {
+        const uint32_t n = (sp.cb - sp.cb0) >> 2;
+        uint32_t r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r[i] = *sp.slot(i);
+        const bool whole = sp.cb0 + 32 <= sp.capb;
+        const uint32_t off = whole ? sp.top - sp.cb0 - 32 : kNoStore;
+        buf_store4(sp.scr, off, u32x4{r[7], r[6], r[5], r[4]});
+        buf_store4(sp.scr, off + 16, u32x4{r[3], r[2], r[1], r[0]});
+        if (__builtin_expect(__ballot(!whole | (n > 8)) != 0, 0)) {
+            for (uint32_t i = whole ? 8u : 0u; i < n; ++i)
+                if (sp.cb0 + 4 * i + 8 < sp.capb)
+                    buf_store(sp.scr, sp.top - 4 - sp.cb0 - 4 * i, 0, (int32_t)*sp.slot(i));
+        }
+        sp.cb0 = sp.cb;
+    };
+    // State-independent values of one round (positions k0 .. k0+7,
+    // last to first): the slot's (start, f), the reciprocal of f,
+    // whether the position holds an ordinary symbol of a valid row,
+    // and the round's symbols and indexes for the general puts.
+    struct Pre {
+        uint32_t start[kRound], f[kRound];
+        double rcp[kRound];
+        int32_t sym[kRound], idx[kRound];
+        uint32_t fast;   // bit u: position u is fast (one register, not eight lane masks)
+    };
+    // Written phase by phase across the round's positions (all metadata
+    // reads, then all pair reads, then each step of the reciprocal for all
+    // eight), so that the eight independent chains interleave instead of
+    // each waiting on its own latencies in turn.
+    auto pre = [&](const int32_t (&sym)[kRound], const int32_t (&idx)[kRound], uint32_t k0,
+                   Pre &P) {
+        RowMeta m[kRound];
+#pragma unroll
+        for (int u = 0; u < kRound; ++u)
+            m[u] = tab.meta(min((uint32_t)idx[u], K - 1));
+        uint32_t pr[kRound];
+        P.fast = 0;
+#pragma unroll
+        for (int u = 0; u < kRound; ++u) {
+            const uint32_t mv = m[u].mvf & 0xFFFFu;
+            // s - offset wraps mod 2^32 into [0, mv) only on rows whose
+            // fast bound is 0
+            const uint32_t w = (uint32_t)sym[u] - (uint32_t)m[u].offset;
+            const bool fast = (w < (m[u].mvf >> 16)) & ((uint32_t)idx[u] < K) & valid(k0 + u);
+            P.fast |= fast ? (1u << u) : 0u;
+            pr[u] = tab.template load<uint32_t>(m[u].base + 4 * min(w, mv));
+            P.sym[u] = sym[u];
+            P.idx[u] = idx[u];
+        }
+        double fd[kRound], e[kRound];
+#pragma unroll
+        for (int u = 0; u < kRound; ++u) {
+            P.start[u] = pr[u] & 0xFFFFu;
+            P.f[u] = pr[u] >> 16;
+            fd[u] = (double)P.f[u];
+        }
+        // the reciprocal of reciprocal(): the hardware estimate and two
+        // Newton-Raphson steps, each applied to all positions in turn
+#pragma unroll
+        for (int u = 0; u < kRound; ++u)
+            P.rcp[u] = __builtin_amdgcn_rcp(fd[u]);
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+#pragma unroll
+            for (int u = 0; u < kRound; ++u)
+                e[u] = __builtin_fma(-fd[u], P.rcp[u], 1.0);
+#pragma unroll
+            for (int u = 0; u < kRound; ++u)
+                P.rcp[u] = __builtin_fma(P.rcp[u], e[u], P.rcp[u]);
+        }
+    };
+    // One round of positions k0 .. k0+7 on P, with the next round's
+    // state-independent work (from sym/idx into Pn) in the same
+    // straight-line block, where it fills the chain's latency.  The
+    // chain assumes every position fast; a round where that is not so
+    // for some lane (an escape, a bad index, a lane end, a lane near
+    // the end of its segment) is redone from its start state with
+    // the general puts.
+    auto round = [&](const Pre &P, uint32_t k0, int32_t (&sym)[kRound],
+                     int32_t (&idx)[kRound], Pre &Pn) {
+        // room for three words per position: the fast steps need no check
+        const bool room = sp.cb + 4 * (2 + 3 * kRound) < sp.capb;
+        const uint64_t x0 = x;
+        const uint32_t cb_start = sp.cb;
+        pre(sym, idx, k0 + kRound, Pn);
+#pragma unroll
+        for (int u = 0; u < kRound; ++u) {
+            const bool need = (uint32_t)(x >> 32) >= (P.f[u] << (31 - kPrecision));
+            *sp.slot((sp.cb - sp.cb0) >> 2) = (uint32_t)x;
+            sp.cb += need ? 4u : 0u;
+            x = need ? (x >> 32) : x;
+            x = reg_step(x, P.start[u], P.f[u], P.rcp[u]);
+        }
+        if (__builtin_expect(!__all((P.fast == (1u << kRound) - 1) & room & (cut_k >= k0 + kRound)),
+                             0)) {
+            x = x0;
+            sp.cb = cb_start;
+            // the fast step is committed where it applies; the other
+            // lanes take the slow puts
+#pragma unroll
+            for (int u = 0; u < kRound; ++u) {
+                const bool fast = ((P.fast >> u) & 1u) & room;
+                const bool need = (uint32_t)(x >> 32) >= (P.f[u] << (31 - kPrecision));
+                const uint64_t xn =
+                    reg_step(need ? (x >> 32) : x, P.start[u], P.f[u], P.rcp[u]);
+                *sp.slot(min((sp.cb - sp.cb0) >> 2, kEncRing - 1)) = (uint32_t)x;
+                sp.cb += (fast & need) ? 4u : 0u;
+                x = fast ? xn : x;
+                const bool slow = !fast & valid(k0 + u);
+                if (__builtin_expect(__ballot(slow) != 0, 0)) {
+                    if (slow) {
+                        int ec = RANS_E_INDEX;
+                        if ((uint32_t)P.idx[u] < K)
+                            ec = encode_slow<TPB>(P.sym[u], tab.meta(P.idx[u]), tab, x, sp);
+                        lerr = lerr ? lerr : ec;
+                    }
+                }
+                while (cut_k == k0 + u)   // (cuts may share a position)
+                    record_cut();
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- memory phase: this round's words, the symbols and
+        // indexes of the round three ahead into the buffer just used
+        store_words();
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(sym, idx, k0 + 3 * kRound);
+    };
+    // prologue: three phases of the same shape (their stores carry
+    // stale ring words to positions that later words overwrite);
+    // rounds 0 and 1 are loaded, round 0 prepared, round 2 loaded
+    Pre pa, pb;
+    store_words();
+    __builtin_amdgcn_sched_barrier(0);
+    load_next(sa, ia, 0);
+    store_words();
+    __builtin_amdgcn_sched_barrier(0);
+    load_next(sb, ib, kRound);
+    pre(sa, ia, 0, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    store_words();
+    __builtin_amdgcn_sched_barrier(0);
+    load_next(sa, ia, 2 * kRound);
+    // both rounds always run (positions past the lane are skipped
+    // inside), so every path back to the loop head passes both phases
+    for (uint32_t k0 = 0; k0 < R8; k0 += 2 * kRound) {
+        round(pa, k0, sb, ib, pb);
+        round(pb, k0 + kRound, sa, ia, pa);
+    }
+    while (cut_s >= 1)   // an empty lane: every cut holds the start state
+        record_cut();
+    if (sp.overflow) {
+        lerr = lerr ? lerr : RANS_E_CAPACITY;
+        sp.cb = sp.capb - 8;
+    }
+    buf_store(sp.scr, sp.top - 8 - sp.cb, 0, (int32_t)(uint32_t)x);
+    buf_store(sp.scr, sp.top - 4 - sp.cb, 0, (int32_t)(uint32_t)(x >> 32));
+    // (the final state is stored after every memory phase)
+    words = sp.cb / 4 + 2;
+    return LaneResult{words, lerr};
+}
+
+// Lane j coded from tables read in the workspace (a set over the LDS budget):
+// the same puts as above, one position at a time, each spilled word stored
+// straight to the lane's scratch segment.  A short loop with few registers,
+// so that the round-based form keeps its register budget to itself.
+template <int TPB>
+__device__ __forceinline__ LaneResult encode_lane_simple(const EncodeArgs &a, const GlobalTab &tab,
+                                                         uint32_t K, uint32_t L, uint32_t j,
+                                                         uint64_t bw, Rsrc rsym, Rsrc ridx,
+                                                         const Spill<TPB> &sp)
+{
+    int lerr = 0;
+    const uint64_t b = lane_begin(a.n, L, j), e = lane_begin(a.n, L, j + 1);
+    const uint32_t nj = (uint32_t)(e - b);
+    const uint32_t capb = 4 * (2 * nj + 4);   // the last 2 words hold the final state
+    uint32_t cb = 0;
+    bool overflow = false;
+    uint64_t x = kStateLow;
+    // word k of the lane goes to byte offset top - 4 - 4k
+    auto renorm = [&](bool spill) {
+        if (spill) {
+            overflow = overflow | (cb + 8 >= capb);
+            if (cb + 8 < capb)
+                buf_store(sp.scr, sp.top - 4 - cb, 0, (int32_t)(uint32_t)x);
+            cb += 4;
+            x >>= 32;
+        }
+    };
+    const uint32_t pl = a.pieces_log2, npieces = 1u << pl;
+    int32_t cut_s = (int32_t)npieces - 1;
+    auto record_cut = [&]() {
+        uint32_t *m = a.split_meta + 3ull * ((uint64_t)(npieces - 1) * j + cut_s - 1);
+        m[0] = (uint32_t)x;
+        m[1] = (uint32_t)(x >> 32);
+        m[2] = cb >> 2;
+        --cut_s;
+    };
+    for (uint32_t k = 0; k < nj; ++k) {
+        const uint64_t c = e - 1 - k;   // positions are coded last to first
+        const uint32_t off = (uint32_t)(4 * (c - bw));
+        const int32_t sym = buf_load(rsym, off, 0), r = buf_load(ridx, off, 0);
+        if ((uint32_t)r >= K) {
+            lerr = lerr ? lerr : RANS_E_INDEX;
+        } else {
+            const RowMeta m = tab.meta((uint32_t)r);
+            const uint32_t mv = m.mvf & 0xFFFFu;
+            const int64_t v = (int64_t)sym - (int64_t)m.offset;
+            const bool esc = (uint64_t)v >= (uint64_t)mv;
+            uint64_t raw = v < 0 ? (uint64_t)(-2 * v - 1) : (uint64_t)(2 * (v - (int64_t)mv));
+            if (esc && raw >= (1ull << 31)) {
+                lerr = lerr ? lerr : RANS_E_SYMBOL_RANGE;
+                raw = 0;
+            }
+            const uint32_t bits = raw ? 64u - (uint32_t)__clzll(raw) : 0u;
+            const uint32_t nb = esc ? (bits + kBypassBits - 1) / kBypassBits : 0u;
+            // BITS puts: groups nb-1 .. 0, then the count nb (k = nb); then the REG put
+            for (uint32_t k = 0; k < nb + (esc ? 1u : 0u); ++k) {
+                const uint32_t b4 = k == nb ? nb : (uint32_t)(raw >> (kBypassBits * (nb - 1 - k))) & 15u;
+                renorm(x >= (1ull << (63 - kBypassBits)));
+                x = (x << kBypassBits) | b4;
+            }
+            const uint32_t pr = tab.template load<uint32_t>(m.base + 4 * (esc ? mv : (uint32_t)v));
+            const uint32_t f = pr >> 16;
+            renorm(x >= ((uint64_t)f << (63 - kPrecision)));
+            x = reg_step(x, pr & 0xFFFFu, f, reciprocal(f));
+        }
+        while (cut_s >= 1 && piece_begin(b, e, pl, (uint32_t)cut_s) == c)   // (cuts may share a position)
+            record_cut();
+    }
+    while (cut_s >= 1)   // an empty lane: every cut holds the start state
+        record_cut();
+    if (overflow) {
+        lerr = lerr ? lerr : RANS_E_CAPACITY;
+        cb = capb - 8;
+    }
+    buf_store(sp.scr, sp.top - 8 - cb, 0, (int32_t)(uint32_t)x);
+    buf_store(sp.scr, sp.top - 4 - cb, 0, (int32_t)(uint32_t)(x >> 32));
+    return LaneResult{cb / 4 + 2, lerr};
+}
+
+// The buffers of the wave coding lanes j0 .. j1-1, and lane j's spill state:
+// the wave's symbols and indexes, and its lanes' scratch segments (lane j
+// owns words [2 b_j + 4 j, 2 e_j + 4 (j+1)) of the scratch area).
+template <int TPB>
+struct WaveBufs {
+    Rsrc rsym, ridx;
+    uint64_t bw;
+    Spill<TPB> sp;
+};
+
+template <int TPB>
+__device__ __forceinline__ WaveBufs<TPB> wave_bufs(const EncodeArgs &a, uint32_t L, uint32_t j0,
+                                                   uint32_t j1, uint32_t j)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint32_t *scratch = reinterpret_cast<uint32_t *>(a.ws + ws_scratch_offset(a.num_tables, a.stride));
+    WaveBufs<TPB> w;
+    w.bw = lane_begin(a.n, L, j0);
+    const uint64_t ew = lane_begin(a.n, L, j1);
+    w.rsym = make_rsrc(a.symbols + w.bw, (uint32_t)(4 * (ew - w.bw)));
+    w.ridx = make_rsrc(a.indexes + w.bw, (uint32_t)(4 * (ew - w.bw)));
+    const uint64_t sw0 = 2 * w.bw + 4ull * j0, sw1 = 2 * ew + 4ull * j1;
+    w.sp.scr = make_rsrc(scratch + sw0, (uint32_t)(4 * (sw1 - sw0)));
+    w.sp.ring = reinterpret_cast<uint32_t *>(lds + kEncTableBudget) + threadIdx.x;
+    const uint64_t e = lane_begin(a.n, L, min(j + 1, L));
+    w.sp.top = (uint32_t)(4 * (2 * e + 4ull * min(j + 1, L) - sw0));
+    return w;
 }
 
 __device__ inline uint32_t wave_inclusive_scan(uint32_t v, uint32_t lane)
@@ -148,9 +498,8 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kEncTableBudget + kEncRing * 4 * TPB);
 
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
-    const uint8_t *tab = a.ws + ws_enc_tables_offset();
+    const uint8_t *tab = a.ws + ws_enc_offset(a.num_tables, a.stride);
     uint64_t *flags = reinterpret_cast<uint64_t *>(a.ws + ws_flags_offset());
-    uint32_t *scratch = reinterpret_cast<uint32_t *>(a.ws + ws_scratch_offset(a.lanes));
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kWave - 1);
     const uint32_t L = a.lanes;
@@ -160,22 +509,21 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     // ---- tables -> LDS -------------------------------------------------------
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // coding waves 0 .. CW-1
     int herr = 0;
-    if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables)
+    if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables ||
+        hdr->cdf_stride != (uint32_t)a.stride)
         herr = RANS_E_ARG;
-    else if (!hdr->enc_ok)
-        herr = RANS_E_TABLE_SIZE;
     else if (lds_address_of(lds) != 0)   // table offsets are used as LDS addresses
         herr = RANS_E_HIP;
     const uint32_t K = (uint32_t)a.num_tables;
-    const uint32_t nbytes = herr ? 0u : hdr->enc_bytes;
-    stage_tables<TPB>(lds, tab, nbytes);
+    const bool in_lds = hdr->enc_lds != 0;
+    stage_tables<TPB>(lds, tab, (!herr && in_lds) ? hdr->enc_bytes : 0u);
     __syncthreads();
-    EncTables et;
-    et.K = K;
     int bad = 0;
-    if (!herr)
+    if (!herr) {
+        const GlobalTab gt{tab};
         for (uint32_t r = tid; r < K; r += TPB)
-            bad |= (lds_meta(r).lut & kRowInvalid) ? 1 : 0;
+            bad |= ((in_lds ? lds_meta(r) : gt.meta(r)).lut & kRowInvalid) ? 1 : 0;
+    }
     if (tid == 0)
         misc[0] = 0u;
     __syncthreads();
@@ -200,220 +548,17 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             const uint32_t j0 = t * lpw, j1 = min(j0 + lpw, L);
             const uint32_t j = j0 + lane;
             const bool active = lane < lpw && j < L;
-            // the wave's symbols and scratch segments, as buffers
-            const uint64_t bw = lane_begin(a.n, L, j0), ew = lane_begin(a.n, L, j1);
-            const Rsrc rsym = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
-            const Rsrc ridx = make_rsrc(a.indexes + bw, (uint32_t)(4 * (ew - bw)));
-            const uint64_t sw0 = 2 * bw + 4ull * j0, sw1 = 2 * ew + 4ull * j1;
-            Spill<TPB> sp;
-            sp.scr = make_rsrc(scratch + sw0, (uint32_t)(4 * (sw1 - sw0)));
-            sp.ring = reinterpret_cast<uint32_t *>(lds + kEncTableBudget) + tid;
-            sp.top = 0;
+            const WaveBufs<TPB> wb = wave_bufs<TPB>(a, L, j0, j1, j);
+            const Spill<TPB> &sp = wb.sp;
             uint32_t words = 0;
             int lerr = 0;
             if (active) {
-                const uint64_t b = lane_begin(a.n, L, j);
-                const uint64_t e = lane_begin(a.n, L, j + 1);
-                const uint32_t nj = (uint32_t)(e - b);
-                sp.top = (uint32_t)(4 * (2 * e + 4ull * (j + 1) - sw0));
-                sp.cb = 0;
-                sp.cb0 = 0;
-                sp.capb = 4 * (2 * nj + 4);
-                sp.overflow = false;
-                uint64_t x = kStateLow;
-                // Split records: the next cut to record (cuts are met last to
-                // first) and the step k = nj - 1 - (c - b) at which position c
-                // is coded; a round holding it takes the per-position path,
-                // which records the state and the words emitted so far right
-                // after that position.
-                const uint32_t npieces = 1u << a.pieces_log2;
-                int32_t cut_s = (int32_t)npieces - 1;
-                auto cut_step = [&](int32_t s) -> uint32_t {
-                    return nj - 1 - (uint32_t)(piece_begin(b, e, a.pieces_log2, (uint32_t)s) - b);
-                };
-                uint32_t cut_k = (npieces > 1 && nj > 0) ? cut_step(cut_s) : ~0u;
-                auto record_cut = [&]() {
-                    uint32_t *m = a.split_meta + 3ull * ((uint64_t)(npieces - 1) * j + cut_s - 1);
-                    m[0] = (uint32_t)x;
-                    m[1] = (uint32_t)(x >> 32);
-                    m[2] = sp.cb >> 2;
-                    --cut_s;
-                    cut_k = (cut_s >= 1 && nj > 0) ? cut_step(cut_s) : ~0u;
-                };
-                // byte offsets of the lane's positions in the wave's buffers;
-                // positions are coded last to first, clamped at the lane start
-                const int32_t plast = (int32_t)(4 * (int64_t)(e - bw) - 4);
-                const int32_t pfirst = (int32_t)(4 * (b - bw));
-                int32_t sa[kRound], ia[kRound], sb[kRound], ib[kRound];
-                // Symbols and indexes of positions k .. k+7: one 16-byte load per
-                // four positions, or, when a window would start before the wave's
-                // first symbol, one clamped load per position.
-                auto load_next = [&](int32_t (&sym)[kRound], int32_t (&idx)[kRound], uint32_t k) {
-                    const int32_t pk = plast - (int32_t)(4 * k);
-                    if (__all(pk - 4 * (kRound - 1) >= 0)) {
-                        const uint32_t lo = (uint32_t)(pk - 4 * (kRound - 1));
-                        const u32x4 s0 = buf_load4(rsym, lo), s1 = buf_load4(rsym, lo + 16);
-                        const u32x4 i0 = buf_load4(ridx, lo), i1 = buf_load4(ridx, lo + 16);
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            sym[7 - u] = (int32_t)s0[u];
-                            sym[3 - u] = (int32_t)s1[u];
-                            idx[7 - u] = (int32_t)i0[u];
-                            idx[3 - u] = (int32_t)i1[u];
-                        }
-                    } else {
-#pragma unroll
-                        for (int u = 0; u < kRound; ++u) {
-                            const uint32_t off = (uint32_t)max(pk - 4 * u, pfirst);
-                            sym[u] = buf_load(rsym, off, 0);
-                            idx[u] = buf_load(ridx, off, 0);
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                };
-                // The round's words (ring slots 0 .. n-1) go to positions
-                // cb0/4 .. cb0/4 + n - 1, i.e. descending byte offsets from
-                // top - 4 - cb0.  Slots 0..7 are always stored, as two 16-byte
-                // stores (slots past n hold stale words for positions that later
-                // words or the final state overwrite); a round of more than 8
-                // words, or a lane near the end of its segment, stores word by
-                // word.
-                auto store_words = [&]() {
-                    const uint32_t n = (sp.cb - sp.cb0) >> 2;
-                    uint32_t r[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        r[i] = *sp.slot(i);
-                    const bool whole = sp.cb0 + 32 <= sp.capb;
-                    const uint32_t off = whole ? sp.top - sp.cb0 - 32 : kNoStore;
-                    buf_store4(sp.scr, off, u32x4{r[7], r[6], r[5], r[4]});
-                    buf_store4(sp.scr, off + 16, u32x4{r[3], r[2], r[1], r[0]});
-                    if (__builtin_expect(__ballot(!whole | (n > 8)) != 0, 0)) {
-                        for (uint32_t i = whole ? 8u : 0u; i < n; ++i)
-                            if (sp.cb0 + 4 * i + 8 < sp.capb)
-                                buf_store(sp.scr, sp.top - 4 - sp.cb0 - 4 * i, 0, (int32_t)*sp.slot(i));
-                    }
-                    sp.cb0 = sp.cb;
-                };
-                // State-independent values of one round (positions k0 .. k0+7,
-                // last to first): the slot's (start, f), the reciprocal of f,
-                // whether the position holds an ordinary symbol of a valid row,
-                // and the round's symbols and indexes for the general puts.
-                struct Pre {
-                    uint32_t start[kRound], f[kRound];
-                    double rcp[kRound];
-                    int32_t sym[kRound], idx[kRound];
-                    bool fast[kRound];
-                    bool all;   // every position of this lane is fast
-                };
-                auto pre = [&](const int32_t (&sym)[kRound], const int32_t (&idx)[kRound], uint32_t k0,
-                               Pre &P) {
-                    P.all = true;
-#pragma unroll
-                    for (int u = 0; u < kRound; ++u) {
-                        const RowMeta m = lds_meta(min((uint32_t)idx[u], K - 1));
-                        const uint32_t mv = m.mvf & 0xFFFFu;
-                        // s - offset wraps mod 2^32 into [0, mv) only on rows whose
-                        // fast bound is 0
-                        const uint32_t w = (uint32_t)sym[u] - (uint32_t)m.offset;
-                        P.fast[u] = (w < (m.mvf >> 16)) & ((uint32_t)idx[u] < K) & (k0 + u < nj);
-                        P.all = P.all & P.fast[u];
-                        const uint32_t pr = pair_of(et, m, min(w, mv));
-                        P.start[u] = pr & 0xFFFFu;
-                        P.f[u] = pr >> 16;
-                        P.rcp[u] = reciprocal(P.f[u]);
-                        P.sym[u] = sym[u];
-                        P.idx[u] = idx[u];
-                    }
-                };
-                // One round of positions k0 .. k0+7 on P, with the next round's
-                // state-independent work (from sym/idx into Pn) in the same
-                // straight-line block, where it fills the chain's latency.  The
-                // chain assumes every position fast; a round where that is not so
-                // for some lane (an escape, a bad index, a lane end, a lane near
-                // the end of its segment) is redone from its start state with
-                // the general puts.
-                auto round = [&](const Pre &P, uint32_t k0, int32_t (&sym)[kRound],
-                                 int32_t (&idx)[kRound], Pre &Pn) {
-                    // room for three words per position: the fast steps need no check
-                    const bool room = sp.cb + 4 * (2 + 3 * kRound) < sp.capb;
-                    const uint64_t x0 = x;
-                    const uint32_t cb_start = sp.cb;
-                    pre(sym, idx, k0 + kRound, Pn);
-#pragma unroll
-                    for (int u = 0; u < kRound; ++u) {
-                        const bool need = (uint32_t)(x >> 32) >= (P.f[u] << (31 - kPrecision));
-                        *sp.slot((sp.cb - sp.cb0) >> 2) = (uint32_t)x;
-                        sp.cb += need ? 4u : 0u;
-                        x = need ? (x >> 32) : x;
-                        x = reg_step(x, P.start[u], P.f[u], P.rcp[u]);
-                    }
-                    if (__builtin_expect(!__all(P.all & room & (cut_k >= k0 + kRound)), 0)) {
-                        x = x0;
-                        sp.cb = cb_start;
-                        // the fast step is committed where it applies; the other
-                        // lanes take the slow puts
-#pragma unroll
-                        for (int u = 0; u < kRound; ++u) {
-                            const bool fast = P.fast[u] & room;
-                            const bool need = (uint32_t)(x >> 32) >= (P.f[u] << (31 - kPrecision));
-                            const uint64_t xn =
-                                reg_step(need ? (x >> 32) : x, P.start[u], P.f[u], P.rcp[u]);
-                            *sp.slot(min((sp.cb - sp.cb0) >> 2, kEncRing - 1)) = (uint32_t)x;
-                            sp.cb += (fast & need) ? 4u : 0u;
-                            x = fast ? xn : x;
-                            const bool slow = !fast & (k0 + u < nj);
-                            if (__builtin_expect(__ballot(slow) != 0, 0)) {
-                                if (slow) {
-                                    int ec = RANS_E_INDEX;
-                                    if ((uint32_t)P.idx[u] < K)
-                                        ec = encode_slow<TPB>(P.sym[u], lds_meta(P.idx[u]), et, x,
-                                                              sp);
-                                    lerr = lerr ? lerr : ec;
-                                }
-                            }
-                            while (cut_k == k0 + u)   // (cuts may share a position)
-                                record_cut();
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    // ---- memory phase: this round's words, the symbols and
-                    // indexes of the round three ahead into the buffer just used
-                    store_words();
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_next(sym, idx, k0 + 3 * kRound);
-                };
-                // prologue: three phases of the same shape (their stores carry
-                // stale ring words to positions that later words overwrite);
-                // rounds 0 and 1 are loaded, round 0 prepared, round 2 loaded
-                Pre pa, pb;
-                store_words();
-                __builtin_amdgcn_sched_barrier(0);
-                load_next(sa, ia, 0);
-                store_words();
-                __builtin_amdgcn_sched_barrier(0);
-                load_next(sb, ib, kRound);
-                pre(sa, ia, 0, pa);
-                __builtin_amdgcn_sched_barrier(0);
-                store_words();
-                __builtin_amdgcn_sched_barrier(0);
-                load_next(sa, ia, 2 * kRound);
-                // both rounds always run (positions past the lane are skipped
-                // inside), so every path back to the loop head passes both phases
-                for (uint32_t k0 = 0; k0 < nj; k0 += 2 * kRound) {
-                    round(pa, k0, sb, ib, pb);
-                    round(pb, k0 + kRound, sa, ia, pa);
-                }
-                while (cut_s >= 1)   // an empty lane: every cut holds the start state
-                    record_cut();
-                if (sp.overflow) {
-                    lerr = lerr ? lerr : RANS_E_CAPACITY;
-                    sp.cb = sp.capb - 8;
-                }
-                buf_store(sp.scr, sp.top - 8 - sp.cb, 0, (int32_t)(uint32_t)x);
-                buf_store(sp.scr, sp.top - 4 - sp.cb, 0, (int32_t)(uint32_t)(x >> 32));
-                // (the final state is stored after every memory phase)
-                words = sp.cb / 4 + 2;
+                const LaneResult lr =
+                    in_lds ? encode_lane<TPB>(a, LdsTab{}, K, L, j, wb.bw, wb.rsym, wb.ridx, wb.sp)
+                           : encode_lane_simple<TPB>(a, GlobalTab{tab}, K, L, j, wb.bw, wb.rsym,
+                                                     wb.ridx, wb.sp);
+                words = lr.words;
+                lerr = lr.err;
             }
             if (lerr)
                 record_error(hdr, lerr);

@@ -25,10 +25,12 @@
 // outputs are 64 consecutive int32 (one 256-byte access per wave), and a
 // step's stream words are contiguous, read from a three-register window.
 //
-// Encoding takes three launches after table preparation: the streams into
-// workspace scratch (emission order, with each stream's word count), one
-// workgroup that scans the counts into the header, and a copy of every
-// stream into the container.  Decoding is one launch.
+// Encoding takes two launches after table preparation: the streams into
+// workspace scratch (emission order, with each stream's word count), then one
+// kernel that writes the header and copies every stream into the container
+// (each of its blocks sums the word counts of the streams before its own, so
+// no block waits on another).  Decoding is one launch.  A table set over the
+// LDS budget is read from the workspace instead of LDS, by the same code.
 #include <type_traits>
 
 #include "rans_coding.hpp"
@@ -56,48 +58,14 @@ __device__ inline uint32_t lanes_above(uint64_t mask, uint32_t lane)
 
 // ---- encode: streams into scratch --------------------------------------------
 
-template <int TPB>
-__global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
+// One stream coded by one wave (t < S), tables in LDS or in the workspace.
+template <class Tab>
+__device__ __forceinline__ void il_encode_stream(const IlArgs &a, const Tab &tab, uint32_t K,
+                                                 uint32_t t)
 {
-    extern __shared__ __align__(16) uint8_t lds[];
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
-    const uint8_t *tab = a.ws + ws_enc_tables_offset();
-    const uint32_t tid = threadIdx.x;
-    const uint32_t lane = tid & (kWave - 1);
+    const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t S = a.streams;
-
-    int herr = 0;
-    if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables)
-        herr = RANS_E_ARG;
-    else if (!hdr->enc_ok)
-        herr = RANS_E_TABLE_SIZE;
-    else if (lds_address_of(lds) != 0)
-        herr = RANS_E_HIP;
-    const uint32_t K = (uint32_t)a.num_tables;
-    // (no __syncthreads_or: its shared word would move the dynamic LDS base)
-    uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kEncTableBudget);
-    stage_tables<TPB>(lds, tab, herr ? 0u : hdr->enc_bytes);
-    if (tid == 0)
-        misc[0] = 0u;
-    __syncthreads();
-    int bad = 0;
-    if (!herr)
-        for (uint32_t r = tid; r < K; r += TPB)
-            bad |= (lds_meta(r).lut & kRowInvalid) ? 1 : 0;
-    if (block_or(&misc[0], bad) && !herr)
-        herr = RANS_E_TABLE;
-    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (TPB / kWave) + tid / kWave);
-    if (herr) {
-        if (blockIdx.x == 0 && tid == 0)
-            record_error(hdr, herr);
-        // the header kernel sums every stream's word count: leave none
-        // stale from an earlier call on this workspace
-        if (lane == 0 && t < S)
-            a.counts[t] = 0;
-        return;
-    }
-    if (t >= S)
-        return;
     const uint64_t b = lane_begin(a.n, S, t), e = lane_begin(a.n, S, t + 1);
     const uint32_t m = (uint32_t)(e - b);
     const Rsrc rsym = make_rsrc(a.symbols + b, 4 * m);
@@ -139,12 +107,12 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
     auto step = [&](auto full, int32_t s, int32_t r, int64_t g) {
         const uint32_t k = (uint32_t)g * kIlW + lane;
         const bool valid = decltype(full)::value || (g >= 0 && k < m);
-        const RowMeta mr = lds_meta(min((uint32_t)r, K - 1));
+        const RowMeta mr = tab.meta(min((uint32_t)r, K - 1));
         const uint32_t mv = mr.mvf & 0xFFFFu;
         const uint32_t w = (uint32_t)s - (uint32_t)mr.offset;
         const bool fast = (w < (mr.mvf >> 16)) & ((uint32_t)r < K);
         if (__builtin_expect(__all(fast | !valid), 1)) {
-            const uint32_t pr = lds_load<uint32_t>(mr.base + 4 * (valid ? w : 0u));
+            const uint32_t pr = tab.template load<uint32_t>(mr.base + 4 * (valid ? w : 0u));
             const uint32_t f = pr >> 16;
             spill(valid & (x >= ((uint64_t)f << (63 - kPrecision))));
             if (valid)
@@ -168,7 +136,7 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
                     const uint32_t bits = raw ? 64u - (uint32_t)__clzll(raw) : 0u;
                     nb = esc ? (bits + kBypassBits - 1) / kBypassBits : 0u;
                     np = esc ? 2 + nb : 1;
-                    const uint32_t pr = lds_load<uint32_t>(mr.base + 4 * (esc ? mv : (uint32_t)v));
+                    const uint32_t pr = tab.template load<uint32_t>(mr.base + 4 * (esc ? mv : (uint32_t)v));
                     start = pr & 0xFFFFu;
                     f = pr >> 16;
                 }
@@ -225,6 +193,67 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
         record_error(hdr, lerr);
     if (lane == 0)
         a.counts[t] = 2 * kIlW + min(E, cap);
+}
+
+// A stream coded from tables read in the workspace (a set over the LDS
+// budget): out of line, so that the LDS form keeps its registers.  The
+// arguments arrive in vector registers and are made scalar again here.
+__device__ __attribute__((noinline)) void il_encode_stream_global(IlArgs a_arg, uint32_t t_arg)
+{
+    const IlArgs a = uniform_copy(a_arg);
+    const uint32_t t = __builtin_amdgcn_readfirstlane(t_arg);
+    il_encode_stream(a, GlobalTab{a.ws + ws_enc_offset(a.num_tables, a.stride)},
+                     (uint32_t)a.num_tables, t);
+}
+
+template <int TPB>
+__global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
+    const uint8_t *tab = a.ws + ws_enc_offset(a.num_tables, a.stride);
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & (kWave - 1);
+    const uint32_t S = a.streams;
+
+    int herr = 0;
+    if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables ||
+        hdr->cdf_stride != (uint32_t)a.stride)
+        herr = RANS_E_ARG;
+    else if (lds_address_of(lds) != 0)
+        herr = RANS_E_HIP;
+    const uint32_t K = (uint32_t)a.num_tables;
+    // (no __syncthreads_or: its shared word would move the dynamic LDS base)
+    uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kEncTableBudget);
+    const bool in_lds = hdr->enc_lds != 0;
+    stage_tables<TPB>(lds, tab, (!herr && in_lds) ? hdr->enc_bytes : 0u);
+    if (tid == 0)
+        misc[0] = 0u;
+    __syncthreads();
+    int bad = 0;
+    if (!herr) {
+        const GlobalTab gt{tab};
+        for (uint32_t r = tid; r < K; r += TPB)
+            bad |= ((in_lds ? lds_meta(r) : gt.meta(r)).lut & kRowInvalid) ? 1 : 0;
+    }
+    if (block_or(&misc[0], bad) && !herr)
+        herr = RANS_E_TABLE;
+    const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (TPB / kWave) + tid / kWave);
+    if (herr) {
+        if (blockIdx.x == 0 && tid == 0)
+            record_error(hdr, herr);
+        // the header kernel sums every stream's word count: leave none
+        // stale from an earlier call on this workspace
+        if (lane == 0 && t < S)
+            a.counts[t] = 0;
+        return;
+    }
+    if (t >= S)
+        return;
+    if (in_lds)
+        il_encode_stream(a, LdsTab{}, K, t);
+    else
+        il_encode_stream_global(a, t);
 }
 
 // ---- encode: header and container (one wave per stream) -----------------------
@@ -292,34 +321,223 @@ __global__ __launch_bounds__(kIlCopyThreads) void il_copy_kernel(IlArgs a)
 
 // ---- decode -----------------------------------------------------------------------
 
+// One stream decoded by one wave (t < S), tables in LDS or in the workspace.
+template <class Tab>
+__device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab, uint32_t K,
+                                                 uint32_t shift, uint32_t t)
+{
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t S = a.streams;
+    int lerr = 0;
+    const uint64_t b = lane_begin(a.n, S, t), e = lane_begin(a.n, S, t + 1);
+    const uint32_t m = (uint32_t)(e - b);
+    // wave-uniform (t is), and kept in scalar registers so that the
+    // stream's buffer descriptor is too
+    // (readfirstlane returns int: back to uint32_t before widening)
+    const uint64_t prev = t ? (uint32_t)__builtin_amdgcn_readfirstlane(a.cstream[t]) : 0u;
+    const uint64_t endt = (uint32_t)__builtin_amdgcn_readfirstlane(a.cstream[1 + t]);
+    if ((uint32_t)__builtin_amdgcn_readfirstlane(a.cstream[0]) != S || endt < prev + 2 * kIlW ||
+        1ull + S + endt > a.capacity) {
+        lerr = RANS_E_CORRUPT;
+    } else {
+        const uint32_t W = (uint32_t)(endt - prev);
+        const uint32_t *words = a.cstream + 1 + S + prev;
+        const Rsrc rw = make_rsrc(words, (uint32_t)min(4ull * W, 1ull << 31));
+        const Rsrc ridx = make_rsrc(a.indexes + b, 4 * m);
+        const Rsrc rout = make_rsrc(a.symbols_out + b, 4 * m);
+        uint64_t x = (uint64_t)(uint32_t)buf_load(rw, 8 * lane, 0) |
+                     ((uint64_t)(uint32_t)buf_load(rw, 8 * lane + 4, 0) << 32);
+        // words [cw, cw + 192) in three registers, one word per lane each
+        uint32_t cw = 2 * kIlW, cursor = 2 * kIlW;
+        uint32_t w0 = buf_load(rw, 4 * (cw + lane), 0);
+        uint32_t w1 = buf_load(rw, 4 * (cw + kWave + lane), 0);
+        uint32_t w2 = buf_load(rw, 4 * (cw + 2 * kWave + lane), 0);
+        // ordered refill: lanes with `need` read the next words, lowest lane first
+        auto refill = [&](bool need) {
+            const uint64_t mask = __ballot(need);
+            const uint32_t d = cursor - cw + lanes_below(mask, lane);   // < 128
+            const uint32_t v0 = (uint32_t)__shfl((int)w0, (int)(d & 63));
+            const uint32_t v1 = (uint32_t)__shfl((int)w1, (int)(d & 63));
+            if (need)
+                x = (x << 32) | (d < kWave ? v0 : v1);
+            cursor += (uint32_t)__popcll(mask);
+            if (cursor - cw >= kWave) {   // slide the window by one register
+                w0 = w1;
+                w1 = w2;
+                cw += kWave;
+                w2 = buf_load(rw, 4 * (cw + 2 * kWave + lane), 0);
+            }
+        };
+        const uint32_t G = (m + kIlW - 1) / kIlW;
+        int32_t ia[kIlAhead], ib[kIlAhead];
+        auto load = [&](int32_t (&r)[kIlAhead], uint32_t g0) {
+#pragma unroll
+            for (int u = 0; u < kIlAhead; ++u)
+                r[u] = buf_load(ridx, 4 * ((g0 + u) * kIlW + lane), 0);
+        };
+        // `full` is std::true_type in groups whose every step lies inside
+        // the stream, which then carry no per-position bound checks
+        auto step = [&](auto full, int32_t r, const RowMeta &mr, uint32_t g) {
+            const uint32_t k = g * kIlW + lane;
+            const bool valid = decltype(full)::value || k < m;
+            const uint32_t mv = mr.mvf & 0xFFFFu;
+            if (valid && (uint32_t)r >= K)
+                lerr = lerr ? lerr : RANS_E_INDEX;
+            // the slot holding cum: the bucket's first slot fs, then one
+            // 8-byte read of start-1 for slots fs .. fs+3 settles slots
+            // fs .. fs+2; past them (rare) a walk over the row
+            const uint32_t cum = (uint32_t)x & (kTotal - 1);
+            const uint32_t fs = tab.template load<uint16_t>((mr.lut & ~kRowInvalid) + 2 * (cum >> shift));
+            const uint64_t q4 = tab.u16x4(mr.base + 2 * fs);
+            const uint32_t e0 = (uint32_t)q4 & 0xFFFFu, e1 = (uint32_t)(q4 >> 16) & 0xFFFFu;
+            const uint32_t e2 = (uint32_t)(q4 >> 32) & 0xFFFFu, e3 = (uint32_t)(q4 >> 48);
+            const bool c1 = cum > e1, c2 = c1 & (cum > e2), beyond = c2 & (cum > e3);
+            uint32_t slot = fs + (c1 ? 1u : 0u) + (c2 ? 1u : 0u);
+            uint32_t sm1 = c2 ? e2 : (c1 ? e1 : e0);
+            uint32_t nxt = c2 ? e3 : (c1 ? e2 : e1);
+            if (__builtin_expect(__ballot(beyond) != 0, 0)) {
+                if (beyond) {
+                    slot = fs + 3;
+                    nxt = tab.template load<uint16_t>(mr.base + 2 * (slot + 1));
+                    for (uint32_t i = 0; i <= mv && cum > nxt; ++i) {
+                        ++slot;
+                        nxt = tab.template load<uint16_t>(mr.base + 2 * (slot + 1));
+                    }
+                    sm1 = tab.template load<uint16_t>(mr.base + 2 * slot);
+                }
+            }
+            const uint32_t f = (nxt - sm1) & 0xFFFFu;
+            const uint32_t rr = (cum - sm1 - 1) & 0xFFFFu;   // cum - start
+            // a select, not a branch: the step stays one basic block
+            x = valid ? (uint64_t)f * (x >> kPrecision) + rr : x;
+            refill(valid & (x < kStateLow));
+            // Slots below the row's fast bound are ordinary symbols whose
+            // value offset + slot fits int32 (the bound is 0 for a row
+            // where it might not): a 32-bit add, no checks.  The escape
+            // slot and such rows take the rare path, which records the
+            // same errors in the same order as a check of every position.
+            int32_t out = (int32_t)(slot + (uint32_t)mr.offset);
+            const bool rare = valid & (slot >= (mr.mvf >> 16));
+            if (__builtin_expect(__ballot(rare) != 0, 0)) {
+                int64_t value = slot;
+                const bool esc = valid & (slot == mv);
+                if (__ballot(esc) != 0) {
+                    uint32_t nb = 0;
+                    if (esc) {
+                        nb = (uint32_t)x & 15u;
+                        x >>= kBypassBits;
+                    }
+                    refill(esc & (x < kStateLow));
+                    if (nb > 8u) {
+                        lerr = lerr ? lerr : RANS_E_CORRUPT;
+                        nb = 0;
+                    }
+                    uint32_t top = nb;
+                    for (int o = kWave / 2; o > 0; o >>= 1)
+                        top = max(top, (uint32_t)__shfl_xor((int)top, o));
+                    top = __builtin_amdgcn_readfirstlane(top);   // the wave's max in every lane
+                    uint64_t raw = 0;
+                    for (uint32_t j = 0; j < top; ++j) {
+                        const bool has = j < nb;
+                        if (has) {
+                            raw |= (uint64_t)((uint32_t)x & 15u) << (kBypassBits * j);
+                            x >>= kBypassBits;
+                        }
+                        refill(has & (x < kStateLow));
+                    }
+                    if (esc) {
+                        if (raw >= (1ull << 31))
+                            lerr = lerr ? lerr : RANS_E_CORRUPT;
+                        value = (raw & 1) ? -(int64_t)(raw >> 1) - 1 : (int64_t)(raw >> 1) + mv;
+                    }
+                }
+                if (rare) {
+                    const int64_t sym = value + mr.offset;
+                    if (sym < INT32_MIN || sym > INT32_MAX)
+                        lerr = lerr ? lerr : RANS_E_CORRUPT;
+                    out = (int32_t)sym;
+                }
+            }
+            buf_store(rout, valid ? 4 * k : 0x80000000u, 0, out);
+        };
+        load(ia, 0);
+        load(ib, kIlAhead);
+        // A group's row metadata is read before its steps (it depends on
+        // the index only), so a step's chain of dependent LDS reads
+        // starts at the bucket table.
+        RowMeta mt[kIlAhead];
+        auto metas = [&](const int32_t (&r)[kIlAhead]) {
+#pragma unroll
+            for (int u = 0; u < kIlAhead; ++u)
+                mt[u] = tab.meta(min((uint32_t)r[u], K - 1));
+        };
+        auto group = [&](auto full, uint32_t g0) {
+            metas(ia);
+#pragma unroll
+            for (int u = 0; u < kIlAhead; ++u)
+                step(full, ia[u], mt[u], g0 + u);
+            load(ia, g0 + 2 * kIlAhead);
+            metas(ib);
+#pragma unroll
+            for (int u = 0; u < kIlAhead; ++u)
+                step(full, ib[u], mt[u], g0 + kIlAhead + u);
+            load(ib, g0 + 3 * kIlAhead);
+        };
+        // the groups wholly inside the stream, then the rest (at most one
+        // group past the stream's end: a stream holds G steps)
+        uint32_t g0 = 0;
+        for (; (g0 + 2 * kIlAhead) * kIlW <= m; g0 += 2 * kIlAhead)
+            group(std::true_type{}, g0);
+        for (; g0 < G; g0 += 2 * kIlAhead)
+            group(std::false_type{}, g0);
+        if (__ballot(x != kStateLow) != 0 || cursor != W)
+            lerr = lerr ? lerr : RANS_E_CORRUPT;
+    }
+    if (lerr)
+        record_error(hdr, lerr);
+}
+
+// A stream decoded from tables read in the workspace (out of line, as for
+// the encoder).
+__device__ __attribute__((noinline)) void il_decode_stream_global(IlArgs a_arg, uint32_t t_arg)
+{
+    const IlArgs a = uniform_copy(a_arg);
+    const uint32_t t = __builtin_amdgcn_readfirstlane(t_arg);
+    const WsHeader *hdr = reinterpret_cast<const WsHeader *>(a.ws);
+    il_decode_stream(a, GlobalTab{a.ws + ws_dec_offset()}, (uint32_t)a.num_tables,
+                     kPrecision - hdr->lut_q, t);
+}
+
 template <int TPB>
 __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
-    const uint8_t *tab = a.ws + ws_tables_offset();
+    const uint8_t *tab = a.ws + ws_dec_offset();
     const uint32_t tid = threadIdx.x;
-    const uint32_t lane = tid & (kWave - 1);
     const uint32_t S = a.streams;
     uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kDecTableBudget);
 
     int herr = 0;
-    if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables)
+    if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables ||
+        hdr->cdf_stride != (uint32_t)a.stride)
         herr = RANS_E_ARG;
-    else if (!hdr->dec_ok)
-        herr = RANS_E_TABLE_SIZE;
     else if (lds_address_of(lds) != 0)
         herr = RANS_E_HIP;
     const uint32_t K = (uint32_t)a.num_tables;
     const uint32_t shift = kPrecision - hdr->lut_q;
-    stage_tables<TPB>(lds, tab, herr ? 0u : hdr->dec_bytes);
+    const bool in_lds = hdr->dec_lds != 0;
+    stage_tables<TPB>(lds, tab, (!herr && in_lds) ? hdr->dec_bytes : 0u);
     if (tid == 0)
         misc[0] = 0u;
     __syncthreads();
     int bad = 0;
-    if (!herr)
+    if (!herr) {
+        const GlobalTab gt{tab};
         for (uint32_t r = tid; r < K; r += TPB)
-            bad |= (lds_meta(r).lut & kRowInvalid) ? 1 : 0;
+            bad |= ((in_lds ? lds_meta(r) : gt.meta(r)).lut & kRowInvalid) ? 1 : 0;
+    }
     if (block_or(&misc[0], bad) && !herr)
         herr = RANS_E_TABLE;
     if (herr && blockIdx.x == 0 && tid == 0)
@@ -330,173 +548,10 @@ __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
     herr = __builtin_amdgcn_readfirstlane(herr);
     const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (TPB / kWave) + tid / kWave);
     if (!herr && t < S) {
-        int lerr = 0;
-        const uint64_t b = lane_begin(a.n, S, t), e = lane_begin(a.n, S, t + 1);
-        const uint32_t m = (uint32_t)(e - b);
-        // wave-uniform (t is), and kept in scalar registers so that the
-        // stream's buffer descriptor is too
-        // (readfirstlane returns int: back to uint32_t before widening)
-        const uint64_t prev = t ? (uint32_t)__builtin_amdgcn_readfirstlane(a.cstream[t]) : 0u;
-        const uint64_t endt = (uint32_t)__builtin_amdgcn_readfirstlane(a.cstream[1 + t]);
-        if ((uint32_t)__builtin_amdgcn_readfirstlane(a.cstream[0]) != S || endt < prev + 2 * kIlW ||
-            1ull + S + endt > a.capacity) {
-            lerr = RANS_E_CORRUPT;
-        } else {
-            const uint32_t W = (uint32_t)(endt - prev);
-            const uint32_t *words = a.cstream + 1 + S + prev;
-            const Rsrc rw = make_rsrc(words, (uint32_t)min(4ull * W, 1ull << 31));
-            const Rsrc ridx = make_rsrc(a.indexes + b, 4 * m);
-            const Rsrc rout = make_rsrc(a.symbols_out + b, 4 * m);
-            uint64_t x = (uint64_t)(uint32_t)buf_load(rw, 8 * lane, 0) |
-                         ((uint64_t)(uint32_t)buf_load(rw, 8 * lane + 4, 0) << 32);
-            // words [cw, cw + 192) in three registers, one word per lane each
-            uint32_t cw = 2 * kIlW, cursor = 2 * kIlW;
-            uint32_t w0 = buf_load(rw, 4 * (cw + lane), 0);
-            uint32_t w1 = buf_load(rw, 4 * (cw + kWave + lane), 0);
-            uint32_t w2 = buf_load(rw, 4 * (cw + 2 * kWave + lane), 0);
-            // ordered refill: lanes with `need` read the next words, lowest lane first
-            auto refill = [&](bool need) {
-                const uint64_t mask = __ballot(need);
-                const uint32_t d = cursor - cw + lanes_below(mask, lane);   // < 128
-                const uint32_t v0 = (uint32_t)__shfl((int)w0, (int)(d & 63));
-                const uint32_t v1 = (uint32_t)__shfl((int)w1, (int)(d & 63));
-                if (need)
-                    x = (x << 32) | (d < kWave ? v0 : v1);
-                cursor += (uint32_t)__popcll(mask);
-                if (cursor - cw >= kWave) {   // slide the window by one register
-                    w0 = w1;
-                    w1 = w2;
-                    cw += kWave;
-                    w2 = buf_load(rw, 4 * (cw + 2 * kWave + lane), 0);
-                }
-            };
-            const uint32_t G = (m + kIlW - 1) / kIlW;
-            int32_t ia[kIlAhead], ib[kIlAhead];
-            auto load = [&](int32_t (&r)[kIlAhead], uint32_t g0) {
-#pragma unroll
-                for (int u = 0; u < kIlAhead; ++u)
-                    r[u] = buf_load(ridx, 4 * ((g0 + u) * kIlW + lane), 0);
-            };
-            // `full` is std::true_type in groups whose every step lies inside
-            // the stream, which then carry no per-position bound checks
-            auto step = [&](auto full, int32_t r, const RowMeta &mr, uint32_t g) {
-                const uint32_t k = g * kIlW + lane;
-                const bool valid = decltype(full)::value || k < m;
-                const uint32_t mv = mr.mvf & 0xFFFFu;
-                if (valid && (uint32_t)r >= K)
-                    lerr = lerr ? lerr : RANS_E_INDEX;
-                // the slot holding cum: the bucket's first slot fs, then one
-                // 8-byte read of start-1 for slots fs .. fs+3 settles slots
-                // fs .. fs+2; past them (rare) a walk over the row
-                const uint32_t cum = (uint32_t)x & (kTotal - 1);
-                const uint32_t fs = lds_load<uint16_t>((mr.lut & ~kRowInvalid) + 2 * (cum >> shift));
-                const uint64_t q4 = lds_load<uint64_t>(mr.base + 2 * fs);
-                const uint32_t e0 = (uint32_t)q4 & 0xFFFFu, e1 = (uint32_t)(q4 >> 16) & 0xFFFFu;
-                const uint32_t e2 = (uint32_t)(q4 >> 32) & 0xFFFFu, e3 = (uint32_t)(q4 >> 48);
-                const bool c1 = cum > e1, c2 = c1 & (cum > e2), beyond = c2 & (cum > e3);
-                uint32_t slot = fs + (c1 ? 1u : 0u) + (c2 ? 1u : 0u);
-                uint32_t sm1 = c2 ? e2 : (c1 ? e1 : e0);
-                uint32_t nxt = c2 ? e3 : (c1 ? e2 : e1);
-                if (__builtin_expect(__ballot(beyond) != 0, 0)) {
-                    if (beyond) {
-                        slot = fs + 3;
-                        nxt = lds_load<uint16_t>(mr.base + 2 * (slot + 1));
-                        for (uint32_t i = 0; i <= mv && cum > nxt; ++i) {
-                            ++slot;
-                            nxt = lds_load<uint16_t>(mr.base + 2 * (slot + 1));
-                        }
-                        sm1 = lds_load<uint16_t>(mr.base + 2 * slot);
-                    }
-                }
-                const uint32_t f = (nxt - sm1) & 0xFFFFu;
-                const uint32_t rr = (cum - sm1 - 1) & 0xFFFFu;   // cum - start
-                // a select, not a branch: the step stays one basic block
-                x = valid ? (uint64_t)f * (x >> kPrecision) + rr : x;
-                refill(valid & (x < kStateLow));
-                // Slots below the row's fast bound are ordinary symbols whose
-                // value offset + slot fits int32 (the bound is 0 for a row
-                // where it might not): a 32-bit add, no checks.  The escape
-                // slot and such rows take the rare path, which records the
-                // same errors in the same order as a check of every position.
-                int32_t out = (int32_t)(slot + (uint32_t)mr.offset);
-                const bool rare = valid & (slot >= (mr.mvf >> 16));
-                if (__builtin_expect(__ballot(rare) != 0, 0)) {
-                    int64_t value = slot;
-                    const bool esc = valid & (slot == mv);
-                    if (__ballot(esc) != 0) {
-                        uint32_t nb = 0;
-                        if (esc) {
-                            nb = (uint32_t)x & 15u;
-                            x >>= kBypassBits;
-                        }
-                        refill(esc & (x < kStateLow));
-                        if (nb > 8u) {
-                            lerr = lerr ? lerr : RANS_E_CORRUPT;
-                            nb = 0;
-                        }
-                        uint32_t top = nb;
-                        for (int o = kWave / 2; o > 0; o >>= 1)
-                            top = max(top, (uint32_t)__shfl_xor((int)top, o));
-                        top = __builtin_amdgcn_readfirstlane(top);   // the wave's max in every lane
-                        uint64_t raw = 0;
-                        for (uint32_t j = 0; j < top; ++j) {
-                            const bool has = j < nb;
-                            if (has) {
-                                raw |= (uint64_t)((uint32_t)x & 15u) << (kBypassBits * j);
-                                x >>= kBypassBits;
-                            }
-                            refill(has & (x < kStateLow));
-                        }
-                        if (esc) {
-                            if (raw >= (1ull << 31))
-                                lerr = lerr ? lerr : RANS_E_CORRUPT;
-                            value = (raw & 1) ? -(int64_t)(raw >> 1) - 1 : (int64_t)(raw >> 1) + mv;
-                        }
-                    }
-                    if (rare) {
-                        const int64_t sym = value + mr.offset;
-                        if (sym < INT32_MIN || sym > INT32_MAX)
-                            lerr = lerr ? lerr : RANS_E_CORRUPT;
-                        out = (int32_t)sym;
-                    }
-                }
-                buf_store(rout, valid ? 4 * k : 0x80000000u, 0, out);
-            };
-            load(ia, 0);
-            load(ib, kIlAhead);
-            // A group's row metadata is read before its steps (it depends on
-            // the index only), so a step's chain of dependent LDS reads
-            // starts at the bucket table.
-            RowMeta mt[kIlAhead];
-            auto metas = [&](const int32_t (&r)[kIlAhead]) {
-#pragma unroll
-                for (int u = 0; u < kIlAhead; ++u)
-                    mt[u] = lds_meta(min((uint32_t)r[u], K - 1));
-            };
-            auto group = [&](auto full, uint32_t g0) {
-                metas(ia);
-#pragma unroll
-                for (int u = 0; u < kIlAhead; ++u)
-                    step(full, ia[u], mt[u], g0 + u);
-                load(ia, g0 + 2 * kIlAhead);
-                metas(ib);
-#pragma unroll
-                for (int u = 0; u < kIlAhead; ++u)
-                    step(full, ib[u], mt[u], g0 + kIlAhead + u);
-                load(ib, g0 + 3 * kIlAhead);
-            };
-            // the groups wholly inside the stream, then the rest (at most one
-            // group past the stream's end: a stream holds G steps)
-            uint32_t g0 = 0;
-            for (; (g0 + 2 * kIlAhead) * kIlW <= m; g0 += 2 * kIlAhead)
-                group(std::true_type{}, g0);
-            for (; g0 < G; g0 += 2 * kIlAhead)
-                group(std::false_type{}, g0);
-            if (__ballot(x != kStateLow) != 0 || cursor != W)
-                lerr = lerr ? lerr : RANS_E_CORRUPT;
-        }
-        if (lerr)
-            record_error(hdr, lerr);
+        if (in_lds)
+            il_decode_stream(a, LdsTab{}, K, shift, t);
+        else
+            il_decode_stream_global(a, t);
     }
 
     // ---- completion: the last block publishes status and cleans up -------------

@@ -46,8 +46,9 @@ struct WsHeader {
     uint32_t lut_q;         // decode lookup: 2^lut_q buckets per row
     uint32_t enc_bytes;     // bytes of the encoder's table set [meta | pairs]
     uint32_t dec_bytes;     // bytes of the decoder's table set [meta | cdf16 | lut]
-    uint32_t enc_ok;        // 1 when the encoder set fits its LDS budget
-    uint32_t dec_ok;        // 1 when the decoder set fits its LDS budget
+    uint32_t enc_lds;       // 1: the encoder set fits its LDS budget and is staged there;
+                            // 0: the coding kernels read it from the workspace
+    uint32_t dec_lds;       // the same for the decoder set
     uint32_t magic;
     uint32_t pad0[7];       // pad0 also serves as a harmless dummy store target
     // bookkeeping (self-cleaning)
@@ -80,13 +81,52 @@ constexpr uint32_t kRowInvalid = 0x80000000u;
 
 inline __host__ __device__ uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
-// Workspace regions: [header | decoder set | encoder set | look-back flags | scratch].
-inline __host__ __device__ uint64_t ws_tables_offset() { return kHeaderBytes; }
-inline __host__ __device__ uint64_t ws_enc_tables_offset() { return kHeaderBytes + kDecTableBudget; }
-inline __host__ __device__ uint64_t ws_flags_offset()
+// Workspace regions:
+//   [header | look-back flags | decoder set | encoder set | scratch]
+// The flags have a fixed place and size (one per encoder wave of the largest
+// lane count): a call finds the flags it uses zero because the previous call's
+// last block cleared them, so no call may keep other words where a later call
+// looks for flags.  Each table region holds its set in the packed layout the
+// prep kernel writes; it is as large as the LDS budget or as the set of
+// num_tables rows of cdf_stride entries can be, whichever is more, so any
+// valid table set fits it.  A set within the LDS budget is staged into LDS by
+// each coding block; a larger one is read from the workspace (through the
+// caches) with a bucket table of 2^kGlobalLutQ entries per row.
+constexpr uint32_t kMaxCodingWaves = RANS_MAX_LANES / kWave;
+constexpr uint32_t kGlobalLutQ = 9;
+inline __host__ __device__ uint64_t ws_flags_offset() { return kHeaderBytes; }
+inline __host__ __device__ uint64_t ws_dec_offset()
 {
-    return align_up(kHeaderBytes + kDecTableBudget + kEncTableBudget, 256);
+    return align_up(kHeaderBytes + 8ull * kMaxCodingWaves, 256);
 }
+inline __host__ __device__ uint64_t meta_bytes_of(uint64_t K) { return align_up(16 * K, 16); }
+// decoder set: meta, cdfm1 (sum of lengths + 4 spare u16, padded), buckets
+inline __host__ __device__ uint64_t dec_set_bytes(uint64_t K, uint64_t total_len, uint32_t q)
+{
+    return meta_bytes_of(K) + align_up(2 * total_len + 8, 16) + align_up((2 * K) << q, 16);
+}
+inline __host__ __device__ uint64_t enc_set_bytes(uint64_t K, uint64_t total_len)
+{
+    return meta_bytes_of(K) + align_up(4 * total_len, 16);
+}
+inline __host__ __device__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+inline __host__ __device__ uint64_t dec_region_bytes(uint64_t K, uint64_t stride)
+{
+    return align_up(max_u64(kDecTableBudget, dec_set_bytes(K, K * stride, kGlobalLutQ)), 256);
+}
+inline __host__ __device__ uint64_t enc_region_bytes(uint64_t K, uint64_t stride)
+{
+    return align_up(max_u64(kEncTableBudget, enc_set_bytes(K, K * stride)), 256);
+}
+inline __host__ __device__ uint64_t ws_enc_offset(uint64_t K, uint64_t stride)
+{
+    return ws_dec_offset() + dec_region_bytes(K, stride);
+}
+inline __host__ __device__ uint64_t ws_scratch_offset(uint64_t K, uint64_t stride)
+{
+    return ws_enc_offset(K, stride) + enc_region_bytes(K, stride);
+}
+
 // Lanes per wavefront and waves per block.  Each lane is a serial chain of
 // steps, so a coding kernel is bound by the latency of one step, not by issue
 // width: a wave with few active lanes costs the same per step as a full one.
@@ -128,15 +168,6 @@ constexpr __host__ __device__ uint32_t dec_waves(uint32_t lanes)
     return (lanes + w - 1) / w;
 }
 inline __host__ __device__ uint64_t ws_flag_count(uint32_t lanes) { return enc_waves(lanes); }
-// The flag region has room for the waves of the largest lane count and the
-// same place for every call: flags must read zero when a call starts (the
-// previous call's last block clears the ones it used), so no call may keep
-// scratch words where a later call with more waves looks for flags.
-constexpr uint32_t kMaxCodingWaves = RANS_MAX_LANES / kWave;
-inline __host__ __device__ uint64_t ws_scratch_offset(uint32_t /*lanes*/)
-{
-    return align_up(ws_flags_offset() + 8ull * kMaxCodingWaves, 256);
-}
 // Lane j's encode scratch holds 2 * n_j + 4 words: a symbol spills at most
 // 52 bits (16 for its slot, 4 for the group count, 32 for raw groups).
 inline __host__ __device__ uint64_t ws_scratch_words(uint64_t n, uint32_t lanes)
@@ -206,6 +237,39 @@ __device__ inline uint32_t lds_address_of(uint8_t *dyn)
 {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)dyn;
 }
+// Table access.  The coding kernels address a packed table set by byte offset
+// from its start.  LdsTab reads a set staged at LDS address 0; GlobalTab reads
+// one that stays in the workspace (sets over the LDS budget), through the
+// caches.  u16x4 reads four consecutive u16 entries at any even offset: one
+// 8-byte LDS read, or four 2-byte loads from global memory (no alignment
+// beyond 2 bytes is assumed there).
+struct LdsTab {
+    template <typename T>
+    __device__ inline T load(uint32_t addr) const { return lds_load<T>(addr); }
+    __device__ inline RowMeta meta(uint32_t row) const { return lds_meta(row); }
+    __device__ inline uint64_t u16x4(uint32_t addr) const { return lds_load<uint64_t>(addr); }
+};
+struct GlobalTab {
+    const uint8_t *g;
+    template <typename T>
+    __device__ inline T load(uint32_t addr) const { return *reinterpret_cast<const T *>(g + addr); }
+    __device__ inline RowMeta meta(uint32_t row) const
+    {
+        const uint4 w = *reinterpret_cast<const uint4 *>(g + 16ull * row);
+        RowMeta m;
+        m.base = w.x;
+        m.offset = (int32_t)w.y;
+        m.mvf = w.z;
+        m.lut = w.w;
+        return m;
+    }
+    __device__ inline uint64_t u16x4(uint32_t addr) const
+    {
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(g + addr);
+        return (uint64_t)p[0] | ((uint64_t)p[1] << 16) | ((uint64_t)p[2] << 32) | ((uint64_t)p[3] << 48);
+    }
+};
+
 __host__ __device__ constexpr uint32_t encode_lds_bytes(uint32_t tpb)
 {
     return kEncTableBudget + kEncRing * 4 * tpb + kLdsMiscBytes;
@@ -242,6 +306,46 @@ __device__ inline void stage_tables(uint8_t *lds, const uint8_t *src, uint32_t n
                                              16, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0);
+}
+
+// The kernel's argument struct read afresh from the kernel-argument segment
+// (explicit arguments start at its offset 0; every kernel here takes one).
+// The segment pointer passes through an empty asm first, so the compiler
+// cannot hoist the reads: a loop that calls this per iteration re-reads the
+// arguments instead of keeping them all live across its body.  Only a
+// kernel's own body may call this: a called function has no kernel-argument
+// pointer (it reads as null there).
+template <class T>
+__device__ inline T fresh_kernel_args()
+{
+    static_assert(sizeof(T) % 4 == 0, "argument struct of whole dwords");
+    typedef const __attribute__((address_space(4))) uint32_t KWord;
+    KWord *p = (KWord *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    uint32_t w[sizeof(T) / 4];
+#pragma unroll
+    for (uint32_t i = 0; i < sizeof(T) / 4; ++i)
+        w[i] = p[i];   // scalar loads: the values stay wave-uniform
+    T v;
+    __builtin_memcpy(&v, w, sizeof(T));
+    return v;
+}
+
+// A wave-uniform struct that arrived in vector registers (arguments of a
+// called function do) made scalar again, dword by dword, so that buffer
+// descriptors built from it need no per-lane loop.
+template <class T>
+__device__ inline T uniform_copy(const T &in)
+{
+    static_assert(sizeof(T) % 4 == 0, "struct of whole dwords");
+    uint32_t w[sizeof(T) / 4];
+    __builtin_memcpy(w, &in, sizeof(T));
+#pragma unroll
+    for (uint32_t i = 0; i < sizeof(T) / 4; ++i)
+        w[i] = __builtin_amdgcn_readfirstlane(w[i]);
+    T v;
+    __builtin_memcpy(&v, w, sizeof(T));
+    return v;
 }
 
 // Raw buffer access (gfx9 buffer descriptor, 32-bit data format): the
@@ -289,6 +393,7 @@ struct EncodeArgs {
     uint64_t n;
     uint32_t lanes;
     int32_t num_tables;
+    int32_t stride;
     uint32_t *stream;
     uint64_t capacity;
     uint64_t *stream_words;
@@ -305,15 +410,17 @@ struct DecodeArgs {
     uint64_t capacity;
     const int32_t *indexes;
     uint64_t n;
-    uint32_t lanes;
     int32_t num_tables;
+    int32_t stride;
     int32_t *symbols;
     int32_t *status;
     uint8_t *ws;
     // with pieces_log2 > 0, every lane decodes as 2^pieces_log2 pieces, each
-    // from its split record (same layout as the encoder writes)
+    // from its split record (same layout as the encoder writes); split_words
+    // is the size of the record array
     uint32_t pieces_log2;
     const uint32_t *split_meta;
+    uint64_t split_words;
 };
 
 // Piece s of a lane [b, e) cut into 2^pieces_log2 pieces starts at
@@ -355,6 +462,7 @@ struct IlArgs {
     uint64_t n;
     uint32_t streams;
     int32_t num_tables;
+    int32_t stride;
     uint32_t *stream;          // encode output container
     const uint32_t *cstream;   // decode input container
     uint64_t capacity;
@@ -377,9 +485,10 @@ inline __host__ __device__ uint64_t il_scratch_words(uint64_t n, uint32_t stream
 {
     return 2 * n + 4ull * kWave * streams;
 }
-inline __host__ __device__ uint64_t il_counts_offset(uint64_t n, uint32_t streams)
+inline __host__ __device__ uint64_t il_counts_offset(uint64_t n, uint32_t streams, uint64_t K,
+                                                     uint64_t stride)
 {
-    return ws_scratch_offset(0) + align_up(4 * il_scratch_words(n, streams), 256);
+    return ws_scratch_offset(K, stride) + align_up(4 * il_scratch_words(n, streams), 256);
 }
 
 hipError_t launch_il_encode(const IlArgs &a, hipStream_t s);

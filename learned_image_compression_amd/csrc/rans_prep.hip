@@ -19,8 +19,9 @@
 // Decoder lookup (inverse-CDF table in the sense of torch_ans "Usage",
 // "Inverse CDF decoding": a table keyed by the low state bits).  Each row gets
 // 2^q buckets of width 2^(16-q) cumulative values, q the largest value <= 12
-// for which the whole set fits the LDS budget; first[b] is the slot holding
-// the bucket's lowest value.  The decoder reads cdfm1[first[b] .. +3] in one
+// for which the whole set fits the LDS budget (a set that fits for no q stays
+// in the workspace, with q = 9); first[b] is the slot holding the bucket's
+// lowest value.  The decoder reads cdfm1[first[b] .. +3] in one
 // 8-byte access and resolves every cum that falls in those three slots.
 #include "rans_internal.hpp"
 
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
     const int K = a.num_tables;
     const uint32_t stride = (uint32_t)a.stride;
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
-    uint8_t *tab = a.ws + ws_tables_offset();
+    uint8_t *tab = a.ws + ws_dec_offset();
 
     // --- 1. effective lengths and their exclusive scan (every block) ----------
     const int chunk = (K + kPrepThreads - 1) / kPrepThreads;
@@ -68,33 +69,35 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
     const uint32_t total = s_part[kPrepThreads - 1];
     __syncthreads();
 
-    // decoder set [meta | cdfm1 | first], encoder set [meta | pairs]
-    const uint32_t meta_bytes = (uint32_t)align_up(16ull * K, 16);
+    // decoder set [meta | cdfm1 | first], encoder set [meta | pairs]; each is
+    // staged into LDS by the coding kernels when it fits their budget, else
+    // read from its workspace region, with 2^kGlobalLutQ buckets per row
+    const uint32_t meta_bytes = (uint32_t)meta_bytes_of(K);
     // (8 spare bytes: the decoder reads four entries from any row position)
     const uint64_t cdf_bytes = align_up(2ull * total + 8, 16);
-    const uint64_t enc_bytes = meta_bytes + align_up(4ull * total, 16);
-    const bool enc_ok = enc_bytes <= kEncTableBudget;
+    const uint64_t enc_bytes = enc_set_bytes(K, total);
+    const bool enc_lds = enc_bytes <= kEncTableBudget;
     int q = -1;
     for (int t = (int)kMaxLutQ; t >= 0; --t) {
-        if (meta_bytes + cdf_bytes + (2ull * K << t) <= kDecTableBudget) {
+        if (dec_set_bytes(K, total, t) <= kDecTableBudget) {
             q = t;
             break;
         }
     }
-    const bool dec_ok = q >= 0;
+    const bool dec_lds = q >= 0;
     if (q < 0)
-        q = 0;
-    const uint64_t dec_bytes = align_up(meta_bytes + cdf_bytes + (2ull * K << q), 16);
+        q = (int)kGlobalLutQ;
+    const uint64_t dec_bytes = dec_set_bytes(K, total, q);
 
     if (blockIdx.x == 0 && tid == 0) {
         hdr->num_tables = (uint32_t)K;
         hdr->cdf_stride = stride;
         hdr->total_len = total;
         hdr->lut_q = (uint32_t)q;
-        hdr->enc_bytes = (uint32_t)(enc_ok ? enc_bytes : 0);
-        hdr->dec_bytes = (uint32_t)(dec_ok ? dec_bytes : 0);
-        hdr->enc_ok = enc_ok ? 1u : 0u;
-        hdr->dec_ok = dec_ok ? 1u : 0u;
+        hdr->enc_bytes = (uint32_t)enc_bytes;
+        hdr->dec_bytes = (uint32_t)dec_bytes;
+        hdr->enc_lds = enc_lds ? 1u : 0u;
+        hdr->dec_lds = dec_lds ? 1u : 0u;
         hdr->err = 0;
         hdr->done = 0;
         hdr->total_words = 0;
@@ -105,10 +108,15 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
     RowMeta *dmeta = reinterpret_cast<RowMeta *>(tab);
     uint16_t *cdfm1 = reinterpret_cast<uint16_t *>(tab + meta_bytes);
     uint16_t *first = reinterpret_cast<uint16_t *>(tab + meta_bytes + cdf_bytes);
-    uint8_t *etab = a.ws + ws_enc_tables_offset();
+    uint8_t *etab = a.ws + ws_enc_offset((uint32_t)K, stride);
     RowMeta *emeta = reinterpret_cast<RowMeta *>(etab);
     uint32_t *pairs = reinterpret_cast<uint32_t *>(etab + meta_bytes);
     const uint32_t width = kTotal >> q;
+    // the four spare entries after the last row read as the terminal value
+    // (65535), like the first entry of every following row, so a window read
+    // that runs past a row's terminal never compares below the cumulative value
+    if (blockIdx.x == 0 && tid < 4)
+        cdfm1[total + tid] = 0xFFFFu;
 
     // --- 2. rows of this block ------------------------------------------------
     for (int r = blockIdx.x; r < K; r += gridDim.x) {
@@ -143,9 +151,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
                 bad = 1;
             if (k > 0 && v <= s_val[k - 1])
                 bad = 1;
-            if (dec_ok)
-                cdfm1[base + k] = (uint16_t)((uint32_t)v - 1u);
-            if (enc_ok) {
+            cdfm1[base + k] = (uint16_t)((uint32_t)v - 1u);
+            {
                 // slot k: start | f << 16 (the terminal entry gets 0)
                 const uint32_t f = k + 1 < len ? (uint32_t)(s_val[k + 1] - v) & 0xFFFFu : 0u;
                 pairs[base + k] = (k + 1 < len) ? ((uint32_t)v & 0xFFFFu) | (f << 16) : 0u;
@@ -160,19 +167,15 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
             RowMeta m;
             m.offset = off;
             m.mvf = mv | ((fits ? mv : 0u) << 16);
-            if (dec_ok) {
-                m.base = (uint32_t)(meta_bytes + 2ull * base);
-                m.lut = (uint32_t)(meta_bytes + cdf_bytes + ((uint64_t)r << (q + 1))) |
-                        (bad ? kRowInvalid : 0u);
-                dmeta[r] = m;
-            }
-            if (enc_ok) {
-                m.base = meta_bytes + 4 * base;
-                m.lut = bad ? kRowInvalid : 0u;
-                emeta[r] = m;
-            }
+            m.base = (uint32_t)(meta_bytes + 2ull * base);
+            m.lut = (uint32_t)(meta_bytes + cdf_bytes + ((uint64_t)r << (q + 1))) |
+                    (bad ? kRowInvalid : 0u);
+            dmeta[r] = m;
+            m.base = meta_bytes + 4 * base;
+            m.lut = bad ? kRowInvalid : 0u;
+            emeta[r] = m;
         }
-        if (dec_ok && !bad) {
+        if (!bad) {
             // first[b]: the slot holding the bucket's lowest cumulative value
             // b * width, i.e. the last k with start(k) <= b * width (slot k
             // covers [start(k), start(k+1))); one thread per bucket, binary

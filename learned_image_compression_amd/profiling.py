@@ -29,11 +29,24 @@ from __future__ import annotations
 import argparse
 import csv
 import glob
+import hashlib
 import json
 import os
 import re
 import statistics
 import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def kernel_source_hash(name: str) -> str:
+    """Hash of the sources that make up one coding kernel (rans_<name>.hip and
+    the shared headers): counter summaries recorded for other sources are stale."""
+    h = hashlib.sha256()
+    for f in ("rans_internal.hpp", "rans_coding.hpp", f"rans_{name}.hip"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 KIB = 1024.0
 
@@ -239,8 +252,6 @@ def summarize_main(a) -> None:
                 fh.write("\n")
             print(path)
             return
-        sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
-        import bench
         for kernel in ("encode", "decode"):
             key = f"{kernel}_kernel"
             rb = fetch[key] * KIB * f_scale
@@ -255,7 +266,7 @@ def summarize_main(a) -> None:
                 "hbm_read_bytes_per_launch": round(rb),
                 "hbm_write_bytes_per_launch": round(wb),
                 "hbm_bytes_per_launch": round(rb + wb),
-                "source_hash": bench.kernel_source_hash(kernel),
+                "source_hash": kernel_source_hash(kernel),
                 "commands": a.command,
             }
             path = os.path.join(a.out, f"traffic_{kernel}_{a.config}_L{a.lanes}.json")

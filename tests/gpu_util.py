@@ -41,12 +41,13 @@ def gpu_encode(symbols, indexes, tables, lanes, capacity=None, canary=True):
     return st, host[: min(nw, cap)].copy(), nw
 
 
-def gpu_decode(words, indexes, tables, lanes, capacity=None):
-    """Decode on the GPU from host words; returns (status, symbols as np.int32)."""
+def gpu_decode(words, indexes, tables, capacity=None):
+    """Decode on the GPU from host words (the lane count is the container's own);
+    returns (status, symbols as np.int32)."""
     n = int(indexes.numel())
     s = torch.from_numpy(np.asarray(words, dtype=np.uint32).view(np.int32).copy()).to(DEV)
     out = torch.full((n + 64,), 0x3C3C3C3C, dtype=torch.int32, device=DEV)
-    sym, status = B.decode_with_indexes(s, indexes, tables, lanes, symbols_out=out[:n],
+    sym, status = B.decode_with_indexes(s, indexes, tables, symbols_out=out[:n],
                                         capacity_words=capacity)
     torch.cuda.synchronize()
     host = out.cpu().numpy()

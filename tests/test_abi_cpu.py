@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-9, 1):
+    for code in range(-8, 1):
         assert lib.rans_status_string(code).decode() not in ("", "unknown status")
     assert lib.rans_status_string(-100).decode() == "unknown status"
 
@@ -47,10 +47,17 @@ def test_bounds(lib):
     for n, L in ((0, 1), (16384, 64), (1566720, 4096), (50135040, 131072)):
         assert lib.rans_encode_bound_words(n, L) == 1 + L + 2 * n + 4 * L
         ws = lib.rans_workspace_bytes(n, L, 64, 3133)
-        # header + decoder and encoder table sets (143 KiB and 111 KiB) +
-        # look-back flags (one per wave, 2^16 at most) + 2n+4L words of lane scratch
-        assert ws >= 256 + 254 * 1024 + 8 * (1 << 16) + 4 * (2 * n + 4 * L)
+        # header + look-back flags (one per wave, 2^16 at most) + decoder and
+        # encoder table regions (at least 143 KiB and 111 KiB, and room for 64
+        # rows of 3133 entries: 2 bytes an entry and 512 bucket entries a row,
+        # 4 bytes an entry) + 2n+4L words of lane scratch
+        tables = max(143 * 1024, 2 * 64 * 3133 + 2 * 64 * 512) + max(110 * 1024, 4 * 64 * 3133)
+        assert ws >= 256 + 8 * (1 << 16) + tables + 4 * (2 * n + 4 * L)
         assert ws % 4 == 0
+    # table regions grow with rows and stride up to the largest set
+    small = lib.rans_workspace_bytes(0, 1, 8, 16)
+    big = lib.rans_workspace_bytes(0, 1, 4096, 16384)
+    assert big - small >= 6 * 4096 * 16384
 
 
 def _encode(lib, **kw):
@@ -68,12 +75,12 @@ def _encode(lib, **kw):
 
 def _decode(lib, **kw):
     args = dict(stream=1, cap=1000, indexes=1, n=10, cdf=1, lengths=1, offsets=1, K=8,
-                stride=3133, lanes=4, symbols=1, status=1, ws=256, ws_bytes=1 << 30, hstream=0)
+                stride=3133, symbols=1, status=1, ws=256, ws_bytes=1 << 30, hstream=0)
     args.update(kw)
     v = ctypes.c_void_p
     return lib.rans_decode_with_indexes(
         v(args["stream"]), args["cap"], v(args["indexes"]), args["n"], v(args["cdf"]),
-        v(args["lengths"]), v(args["offsets"]), args["K"], args["stride"], args["lanes"],
+        v(args["lengths"]), v(args["offsets"]), args["K"], args["stride"],
         v(args["symbols"]), v(args["status"]), v(args["ws"]), args["ws_bytes"],
         v(args["hstream"]))
 
@@ -103,12 +110,11 @@ def test_encode_rejects_bad_arguments_on_host(lib, kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(lanes=0), -1),
     (dict(stream=0), -1),
     (dict(indexes=0), -1),
     (dict(symbols=0), -1),
     (dict(status=0), -1),
-    (dict(cap=2), -1),
+    (dict(cap=0), -1),                  # not even the lane-count word
     (dict(offsets=0), -1),
     (dict(K=0), -2),
     (dict(stride=20000), -2),
@@ -194,17 +200,19 @@ def test_dequantize_host_checks(lib, kw, code):
 def test_split_calls_check_pieces_on_host(lib, pieces, meta, code):
     assert lib.rans_encode_with_splits(1, 1, 10, 1, 1, 1, 8, 3133, 4, pieces, 1, 1000, 1, meta, 1,
                                        256, 1 << 30, 0) == code
-    assert lib.rans_decode_with_splits(1, 1000, 1, 10, 1, 1, 1, 8, 3133, 4, pieces, meta, 1, 1,
-                                       256, 1 << 30, 0) == code
+    assert lib.rans_decode_with_splits(1, 1000, 1, 10, 1, 1, 1, 8, 3133, pieces, meta, 1000, 1,
+                                       1, 256, 1 << 30, 0) == code
 
 
 def test_interleaved_sizes(lib):
     for n, S in ((0, 1), (16384, 4), (1566720, 2048), (50135040, 65536)):
         assert lib.rans_interleaved_bound_words(n, S) == 1 + S + 2 * n + 256 * S
-        ws = lib.rans_interleaved_workspace_bytes(n, S)
-        # header and table sets, flags, per-stream scratch (2 m + 256 words),
+        ws = lib.rans_interleaved_workspace_bytes(n, S, 64, 3133)
+        # header, flags, table regions, per-stream scratch (2 m + 256 words),
         # and word counts
-        assert ws >= 256 + 254 * 1024 + 4 * (2 * n + 256 * S) + 4 * S
+        assert ws >= 256 + 8 * (1 << 16) + 254 * 1024 + 4 * (2 * n + 256 * S) + 4 * S
+        assert ws == lib.rans_workspace_bytes(0, 1, 64, 3133) - 16 + \
+            ((4 * (2 * n + 256 * S) + 255) // 256) * 256 + 4 * S
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -238,27 +246,29 @@ def test_decode_interleaved_host_checks(lib, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(S=0), -1), (dict(S=(1 << 16) + 1), -1), (dict(stream=0), -1), (dict(words=0), -1),
     (dict(status=0), -1), (dict(symbols=0), -1), (dict(indexes=0), -1), (dict(cap=4), -1),
-    (dict(n=(1 << 40)), -1), (dict(K=0), -2), (dict(K=(1 << 20)), -2), (dict(ws=0), -7),
-    (dict(ws=128), -7), (dict(ws_bytes=4096), -7),
+    (dict(n=(1 << 40)), -1), (dict(K=0), -2), (dict(K=(1 << 20)), -2), (dict(stride=2), -2),
+    (dict(stride=16385), -2), (dict(ws=0), -7), (dict(ws=128), -7), (dict(ws_bytes=4096), -7),
 ])
 def test_encode_interleaved_prepared_host_checks(lib, kw, code):
-    a = dict(symbols=1, indexes=1, n=10, K=8, S=4, stream=1, cap=1000, words=1, status=1, ws=256,
-             ws_bytes=1 << 30)
+    a = dict(symbols=1, indexes=1, n=10, K=8, stride=3133, S=4, stream=1, cap=1000, words=1,
+             status=1, ws=256, ws_bytes=1 << 30)
     a.update(kw)
-    assert lib.rans_encode_interleaved_prepared(a["symbols"], a["indexes"], a["n"], a["K"], a["S"],
-                                                a["stream"], a["cap"], a["words"], a["status"],
-                                                a["ws"], a["ws_bytes"], 0) == code
+    assert lib.rans_encode_interleaved_prepared(a["symbols"], a["indexes"], a["n"], a["K"],
+                                                a["stride"], a["S"], a["stream"], a["cap"],
+                                                a["words"], a["status"], a["ws"], a["ws_bytes"],
+                                                0) == code
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(S=0), -1), (dict(S=(1 << 16) + 1), -1), (dict(stream=0), -1), (dict(status=0), -1),
     (dict(out=0), -1), (dict(indexes=0), -1), (dict(cap=2), -1), (dict(n=(1 << 40)), -1),
-    (dict(K=0), -2), (dict(ws=0), -7), (dict(ws=128), -7), (dict(ws_bytes=4096), -7),
+    (dict(K=0), -2), (dict(stride=2), -2), (dict(ws=0), -7), (dict(ws=128), -7),
+    (dict(ws_bytes=4096), -7),
 ])
 def test_decode_interleaved_prepared_host_checks(lib, kw, code):
-    a = dict(stream=1, cap=1000, indexes=1, n=10, K=8, S=4, out=1, status=1, ws=256,
+    a = dict(stream=1, cap=1000, indexes=1, n=10, K=8, stride=3133, S=4, out=1, status=1, ws=256,
              ws_bytes=1 << 30)
     a.update(kw)
     assert lib.rans_decode_interleaved_prepared(a["stream"], a["cap"], a["indexes"], a["n"],
-                                                a["K"], a["S"], a["out"], a["status"], a["ws"],
-                                                a["ws_bytes"], 0) == code
+                                                a["K"], a["stride"], a["S"], a["out"], a["status"],
+                                                a["ws"], a["ws_bytes"], 0) == code

@@ -127,8 +127,14 @@ def test_prepared_interleaved_calls_code_many_tensors():
     B = G.B
     w, tables, sym, idx = _workload("tiny")
     n = w.n
-    ws = torch.zeros(B.load().rans_interleaved_workspace_bytes(n, 4096), dtype=torch.uint8,
-                     device=G.DEV)
+    wz = W.load("z")
+    tz = G.tables_of(wz)
+    # one workspace for both table sets (its regions are sized by rows and stride)
+    lib = B.load()
+    ws = torch.zeros(max(lib.rans_interleaved_workspace_bytes(n, 4096, tables.num_tables,
+                                                              tables.stride),
+                         lib.rans_interleaved_workspace_bytes(16384, 64, tz.num_tables, tz.stride)),
+                     dtype=torch.uint8, device=G.DEV)
     B.prepare_tables(tables, ws)
     for lo, hi, S in ((0, 16384, 4096), (5000, 16384, 2048), (100, 9000, 33), (7, 8, 1)):
         G.say(f"[il-prepared] [{lo},{hi}) streams={S}")
@@ -150,8 +156,6 @@ def test_prepared_interleaved_calls_code_many_tensors():
     torch.cuda.synchronize()
     assert int(st.item()) == B.NAME_TO_CODE["RANS_E_ARG"]
     G.say("[il-prepared] a full call with other tables, then prepared calls with them")
-    wz = W.load("z")
-    tz = G.tables_of(wz)
     zsym, zidx = G.to_dev(wz.symbols[:16384]), G.to_dev(wz.indexes[:16384])
     rc, zref = oracle.encode_interleaved(wz.symbols[:16384], wz.indexes[:16384], wz.cdf,
                                          wz.lengths, wz.offsets, 64, 64)
@@ -173,8 +177,9 @@ def test_encode_refused_up_front_copies_nothing():
     B = G.B
     w, tables, sym, idx = _workload("tiny")
     S = 4096
-    ws = torch.zeros(B.load().rans_interleaved_workspace_bytes(w.n, S), dtype=torch.uint8,
-                     device=G.DEV)
+    ws = torch.zeros(B.load().rans_interleaved_workspace_bytes(w.n, S, tables.num_tables,
+                                                               tables.stride),
+                     dtype=torch.uint8, device=G.DEV)
     rc, ref = oracle.encode_interleaved(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, S, 64)
     G.say("[il-refused] a valid encode leaves word counts in the workspace")
     stream, nw, st = B.encode_interleaved(sym, idx, tables, S, workspace=ws)

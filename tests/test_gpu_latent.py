@@ -149,7 +149,7 @@ def test_latent_chain_matches_the_oracle_chain():
     stream, nwords, status = G.B.encode_with_indexes(sym, idx, tables, 4096)
     G.B.check(status)
     G.say("[latent] chain: decode + dequantise")
-    out, status = G.B.decode_with_indexes(stream, idx, tables, 4096)
+    out, status = G.B.decode_with_indexes(stream, idx, tables)
     G.B.check(status)
     y_hat = G.B.dequantize(out, _dev(m)).cpu().numpy()
     words = stream[: int(nwords.item())].cpu().numpy().view(np.uint32)

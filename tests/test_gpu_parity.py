@@ -1,8 +1,9 @@
 """GPU parity: the HIP coder against the CPU oracle, byte for byte.
 
-Every synthetic workload runs at each of its lane counts (tiny and z also at
-1, 2, 3, 7, 255, n and n + 5 lanes, covering single-lane standard streams,
-ragged partitions and empty lanes).  For each case the GPU encode must equal
+Every synthetic workload runs at its own lane counts and at one lane (the
+standard single stream; on the batches that puts 25M or 50M symbols in one
+lane and its scratch spans 100-400 MB), and tiny and z also at 2, 3, 7, 255,
+n and n + 5 lanes (ragged partitions and empty lanes).  For each case the GPU encode must equal
 the oracle's container word for word, the GPU must decode the oracle's
 container back to the input, and each side decodes the other's stream.
 """
@@ -22,8 +23,8 @@ CASES = [
     ("z", L) for L in (256, 1, 2, 3, 7, 255, 97920, 97925)
 ] + [
     ("y1080", 4096), ("y1080", 1), ("y1080", 977),
-    ("y1080x16", 65536),
-    ("y4kx8", 1024), ("y4kx8", 16384), ("y4kx8", 131072),
+    ("y1080x16", 65536), ("y1080x16", 1),
+    ("y4kx8", 1024), ("y4kx8", 16384), ("y4kx8", 131072), ("y4kx8", 1),
 ]
 
 _cache = {}
@@ -53,7 +54,7 @@ def test_encode_decode_match_oracle(name, lanes):
         bad = np.flatnonzero(got != ref)
         pytest.fail(f"{bad.size} words differ, first at {bad[0]}: {got[bad[0]]:#x} != {ref[bad[0]]:#x}")
     G.say(f"[parity] {name} lanes={lanes}: gpu decode of the oracle stream")
-    st, out = G.gpu_decode(ref, idx, tables, lanes)
+    st, out = G.gpu_decode(ref, idx, tables)
     assert st == 0, f"decode status {st}"
     assert np.array_equal(out, w.symbols)
     G.say(f"[parity] {name} lanes={lanes}: oracle decode of the gpu stream")
@@ -70,7 +71,7 @@ def test_empty_input_and_more_lanes_than_symbols():
         st, got, nw = G.gpu_encode(sym[:n], idx[:n], tables, lanes)
         assert rc == 0 and st == 0
         assert np.array_equal(got, ref)
-        st, out = G.gpu_decode(ref, idx[:n], tables, lanes)
+        st, out = G.gpu_decode(ref, idx[:n], tables)
         assert st == 0 and np.array_equal(out, w.symbols[:n])
 
 
@@ -100,7 +101,7 @@ def test_bypass_edges_and_extremes():
         assert rc == 0
         st, got, _ = G.gpu_encode(G.to_dev(syms), G.to_dev(idxs), tables, lanes)
         assert st == 0 and np.array_equal(got, ref)
-        st, out = G.gpu_decode(ref, G.to_dev(idxs), tables, lanes)
+        st, out = G.gpu_decode(ref, G.to_dev(idxs), tables)
         assert st == 0 and np.array_equal(out, syms)
 
 
@@ -131,7 +132,7 @@ def test_extreme_offsets():
         assert rc == 0
         st, got, _ = G.gpu_encode(G.to_dev(syms), G.to_dev(idxs), tables, lanes)
         assert st == 0 and np.array_equal(got, ref)
-        st, out = G.gpu_decode(ref, G.to_dev(idxs), tables, lanes)
+        st, out = G.gpu_decode(ref, G.to_dev(idxs), tables)
         assert st == 0 and np.array_equal(out, syms)
     # s - offset wraps to a small value mod 2^32: still out of range
     bad = syms.copy()
@@ -160,7 +161,7 @@ def test_wide_rows_uniform_symbols():
         assert rc == 0
         st, got, _ = G.gpu_encode(G.to_dev(syms), G.to_dev(idxs), tables, lanes)
         assert st == 0 and np.array_equal(got, ref)
-        st, out = G.gpu_decode(ref, G.to_dev(idxs), tables, lanes)
+        st, out = G.gpu_decode(ref, G.to_dev(idxs), tables)
         assert st == 0 and np.array_equal(out, syms)
 
 
@@ -188,7 +189,7 @@ def test_repeat_calls_are_identical_and_workspace_is_reusable():
         if first is None:
             first = got
         assert np.array_equal(got, first)
-        st, out = G.gpu_decode(got, idx, tables, 64)
+        st, out = G.gpu_decode(got, idx, tables)
         assert st == 0 and np.array_equal(out, w.symbols)
 
 
@@ -211,7 +212,7 @@ def test_prepared_tables_code_many_tensors():
         assert int(status.item()) == 0
         got = stream[: int(nwords.item())].cpu().numpy().view(np.uint32)
         assert np.array_equal(got, ref)
-        out, status = B.decode_with_indexes(stream, idx[lo:hi].contiguous(), tables, lanes,
+        out, status = B.decode_with_indexes(stream, idx[lo:hi].contiguous(), tables,
                                             workspace=ws, prepared=True)
         assert int(status.item()) == 0
         assert np.array_equal(out.cpu().numpy(), w.symbols[lo:hi])
@@ -246,7 +247,7 @@ def test_full_and_prepared_calls_share_a_workspace():
         assert int(status.item()) == 0
         got = stream[: int(nwords.item())].cpu().numpy().view(np.uint32)
         assert np.array_equal(got, refs[w.name])
-        out, status = B.decode_with_indexes(stream, idx, t, 256, workspace=ws, prepared=prepared)
+        out, status = B.decode_with_indexes(stream, idx, t, workspace=ws, prepared=prepared)
         assert int(status.item()) == 0
         assert np.array_equal(out.cpu().numpy(), w.symbols)
     G.say("[shared-ws] stand-alone preparation replaced by the next full call")
@@ -269,7 +270,7 @@ def test_bad_index_reports_status():
     rc, ref = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, 64)
     bad[99] = -1
     G.say("[errors] bad index decode")
-    st, _ = G.gpu_decode(ref, G.to_dev(bad), tables, 64)
+    st, _ = G.gpu_decode(ref, G.to_dev(bad), tables)
     assert st == oracle.E_INDEX
     G.say("[errors] clean call after errors")
     st, got, _ = G.gpu_encode(sym, idx, tables, 64)
@@ -321,26 +322,107 @@ def test_corrupt_streams_report_status():
     L = 4
     rc, words = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, L)
     G.say("[errors] corrupt streams")
-    assert G.gpu_decode(words, idx, tables, L)[0] == 0
-    assert G.gpu_decode(words, idx, tables, L + 1)[0] == oracle.E_CORRUPT
+    assert G.gpu_decode(words, idx, tables)[0] == 0
+    # the lane count in the header word: one more or one fewer lane, none,
+    # more lanes than the container has words, above the lane limit
+    for bad_L in (L + 1, L - 1, 0, words.size, (1 << 22) + 1):
+        s = words.copy(); s[0] = bad_L
+        assert G.gpu_decode(s, idx, tables)[0] == oracle.E_CORRUPT, bad_L
     s = words.copy(); s[1], s[2] = s[2], s[1]
-    assert G.gpu_decode(s, idx, tables, L)[0] == oracle.E_CORRUPT
-    assert G.gpu_decode(words[:-1], idx, tables, L)[0] == oracle.E_CORRUPT
+    assert G.gpu_decode(s, idx, tables)[0] == oracle.E_CORRUPT
+    assert G.gpu_decode(words[:-1], idx, tables)[0] == oracle.E_CORRUPT
     s = words[:-1].copy(); s[L] -= 1
-    assert G.gpu_decode(s, idx, tables, L)[0] == oracle.E_CORRUPT
+    assert G.gpu_decode(s, idx, tables)[0] == oracle.E_CORRUPT
     s = np.concatenate([words, [123]]).astype(np.uint32); s[L] += 1
-    assert G.gpu_decode(s, idx, tables, L)[0] == oracle.E_CORRUPT
+    assert G.gpu_decode(s, idx, tables)[0] == oracle.E_CORRUPT
     s = words.copy(); s[1] = 1
-    assert G.gpu_decode(s, idx, tables, L)[0] == oracle.E_CORRUPT
+    assert G.gpu_decode(s, idx, tables)[0] == oracle.E_CORRUPT
     rng = np.random.default_rng(3)
     for k in range(8):
         s = words.copy()
         pos = int(rng.integers(1 + L, s.size))
         s[pos] ^= np.uint32(1 << int(rng.integers(0, 32)))
-        st, out = G.gpu_decode(s, idx, tables, L)
-        rco, outo = oracle.decode(s, w.indexes, w.cdf, w.lengths, w.offsets, L)
+        st, out = G.gpu_decode(s, idx, tables)
+        rco, outo = oracle.decode(s, w.indexes, w.cdf, w.lengths, w.offsets, int(s[0]))
         # both sides agree on acceptance; where both accept, outputs agree
         assert (st == 0) == (rco == 0)
         if st == 0:
             assert np.array_equal(out, outo)
-    assert G.gpu_decode(words, idx, tables, L)[0] == 0
+    assert G.gpu_decode(words, idx, tables)[0] == 0
+
+
+# ------------------------------------------------- table sets over the LDS budget
+def _wide_table_set(K, lengths, seed):
+    """K rows of the given lengths (stride = the longest), each a random pmf
+    with every frequency at least 1, escape slot included."""
+    rng = np.random.default_rng(seed)
+    stride = int(max(lengths))
+    cdf = np.full((K, stride), 65536, np.int32)
+    for r, n in enumerate(lengths):
+        p = rng.dirichlet(np.full(n - 1, 0.7))
+        f = np.maximum(1, np.floor(p * (65536 - (n - 1)))).astype(np.int64)
+        f[int(np.argmax(f))] += 65536 - int(f.sum())
+        cdf[r, :n] = np.concatenate([[0], np.cumsum(f)])
+    offsets = rng.integers(-2000, 2000, K).astype(np.int32)
+    return cdf, np.asarray(lengths, np.int32), offsets
+
+
+def _symbols_for(cdf, lengths, offsets, n, seed):
+    rng = np.random.default_rng(seed)
+    K = lengths.size
+    idx = rng.integers(0, K, n).astype(np.int32)
+    u = rng.random(n)
+    sym = np.empty(n, np.int64)
+    for r in range(K):
+        sel = np.flatnonzero(idx == r)
+        c = cdf[r, : lengths[r] - 1].astype(np.float64) / 65536.0   # slot starts
+        sym[sel] = np.searchsorted(c, u[sel], side="right") - 1 + offsets[r]
+    esc = rng.random(n) < 0.01
+    sym[esc] += np.where(rng.random(int(esc.sum())) < 0.5, -1, 1) * (lengths[idx[esc]] + 1000)
+    return sym.astype(np.int32), idx
+
+
+@pytest.mark.parametrize("kind", ["both_global", "encoder_global"])
+def test_table_sets_over_the_lds_budget(kind):
+    """Sets whose packed form does not fit LDS are read from the workspace:
+    64 rows of 3133 entries (both sets over budget), and 16 rows of 2500
+    (the encoder set, 4 bytes a slot, over budget; the decoder set fits).
+    Lane, split-record and interleaved containers must equal the oracle's
+    word for word, and each decodes back."""
+    import torch
+    import gpu_util as G
+    B = G.B
+    if kind == "both_global":
+        cdf, lengths, offsets = _wide_table_set(64, [3133] * 64, 41)
+    else:
+        cdf, lengths, offsets = _wide_table_set(16, [2500] * 16, 42)
+    sym, idx = _symbols_for(cdf, lengths, offsets, 120_001, 43)
+    tables = B.Tables.from_numpy(cdf, lengths, offsets, G.DEV)
+    dsym, didx = G.to_dev(sym), G.to_dev(idx)
+    for lanes in (1, 97, 4096):
+        G.say(f"[over-budget] {kind} lanes={lanes}")
+        rc, ref = oracle.encode(sym, idx, cdf, lengths, offsets, lanes)
+        assert rc == 0
+        st, got, nw = G.gpu_encode(dsym, didx, tables, lanes)
+        assert st == 0 and nw == ref.size and np.array_equal(got, ref)
+        st, out = G.gpu_decode(ref, didx, tables)
+        assert st == 0 and np.array_equal(out, sym)
+    G.say(f"[over-budget] {kind} split records")
+    rc, sref, rmeta = oracle.encode_split(sym, idx, cdf, lengths, offsets, 97, 4)
+    stream, nwords, meta, status = B.encode_with_splits(dsym, didx, tables, 97, 4)
+    torch.cuda.synchronize()
+    assert rc == 0 and int(status.item()) == 0
+    assert np.array_equal(meta.cpu().numpy().view(np.uint32).reshape(rmeta.shape), rmeta)
+    out, status = B.decode_with_splits(stream, meta, didx, tables, 4)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0 and np.array_equal(out.cpu().numpy(), sym)
+    for S in (3, 64):
+        G.say(f"[over-budget] {kind} interleaved S={S}")
+        rc, iref = oracle.encode_interleaved(sym, idx, cdf, lengths, offsets, S, 64)
+        istream, inw, ist = B.encode_interleaved(dsym, didx, tables, S)
+        torch.cuda.synchronize()
+        assert rc == 0 and int(ist.item()) == 0
+        assert np.array_equal(istream[: int(inw.item())].cpu().numpy().view(np.uint32), iref)
+        out, st2 = B.decode_interleaved(istream, didx, tables, S)
+        torch.cuda.synchronize()
+        assert int(st2.item()) == 0 and np.array_equal(out.cpu().numpy(), sym)

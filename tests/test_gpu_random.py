@@ -77,15 +77,11 @@ def test_random_case(seed):
     tables = G.B.Tables.from_numpy(cdf, lengths, offsets, G.DEV)
     rc, ref = oracle.encode(sym, idx, cdf, lengths, offsets, lanes)
     st, got, nw = G.gpu_encode(G.to_dev(sym), G.to_dev(idx), tables, lanes)
-    if st == G.B.NAME_TO_CODE["RANS_E_TABLE_SIZE"]:
-        # the encoder's table set (16 bytes a row, 4 a slot) must not fit LDS
-        assert 16 * lengths.size + 4 * int(lengths.sum()) > 110 * 1024, "fits, yet refused"
-        return
     assert st == rc, (st, rc)
     if rc != 0:
         return
     assert nw == ref.size and np.array_equal(got, ref)
-    st, out = G.gpu_decode(ref, G.to_dev(idx), tables, lanes)
+    st, out = G.gpu_decode(ref, G.to_dev(idx), tables)
     assert st == 0 and np.array_equal(out, sym)
     # split records at a random piece count
     P = int(rng.choice([2, 4, 16]))
@@ -95,7 +91,7 @@ def test_random_case(seed):
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     assert np.array_equal(meta.cpu().numpy().view(np.uint32).reshape(rmeta.shape), rmeta)
-    out, status = G.B.decode_with_splits(stream, meta, G.to_dev(idx), tables, lanes, P)
+    out, status = G.B.decode_with_splits(stream, meta, G.to_dev(idx), tables, P)
     torch.cuda.synchronize()
     assert int(status.item()) == 0 and np.array_equal(out.cpu().numpy(), sym)
     # interleaved streams

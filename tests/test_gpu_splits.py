@@ -54,7 +54,7 @@ def test_split_records_and_piecewise_decode(name, lanes, pieces):
     G.say(f"[splits] {name} lanes={lanes} pieces={pieces}: gpu decode from oracle records")
     s = torch.from_numpy(ref.view(np.int32).copy()).to(G.DEV)
     m = torch.from_numpy(rmeta.view(np.int32).copy()).to(G.DEV)
-    out, status = G.B.decode_with_splits(s, m, idx, tables, lanes, pieces)
+    out, status = G.B.decode_with_splits(s, m, idx, tables, pieces)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     assert np.array_equal(out.cpu().numpy(), w.symbols)
@@ -76,7 +76,7 @@ def test_altered_records_are_refused_like_the_oracle():
         G.say(f"[splits] altered record lane {j} cut {c + 1} word {k}")
         rco, _ = oracle.decode_split(ref, bad, w.indexes, w.cdf, w.lengths, w.offsets, L, P)
         m = torch.from_numpy(bad.view(np.int32).copy()).to(G.DEV)
-        out, status = G.B.decode_with_splits(s, m, idx, tables, L, P)
+        out, status = G.B.decode_with_splits(s, m, idx, tables, P)
         torch.cuda.synchronize()
         assert rco == oracle.E_CORRUPT and int(status.item()) == oracle.E_CORRUPT
 
@@ -91,6 +91,6 @@ def test_one_piece_matches_the_plain_calls():
     assert int(status.item()) == 0 and meta.numel() == 0
     rc, ref = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, 256)
     assert np.array_equal(stream[: int(nwords.item())].cpu().numpy().view(np.uint32), ref)
-    out, status = G.B.decode_with_splits(stream, meta, idx, tables, 256, 1)
+    out, status = G.B.decode_with_splits(stream, meta, idx, tables, 1)
     torch.cuda.synchronize()
     assert int(status.item()) == 0 and np.array_equal(out.cpu().numpy(), w.symbols)

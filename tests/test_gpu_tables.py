@@ -175,5 +175,5 @@ def test_device_built_tables_code_like_the_oracle():
     G.say("[tables] coding with device-built tables")
     s, got, nw = G.gpu_encode(sym, idx, tables, 64)
     assert s == 0 and np.array_equal(got, ref)
-    s, out = G.gpu_decode(ref, idx, tables, 64)
+    s, out = G.gpu_decode(ref, idx, tables)
     assert s == 0 and np.array_equal(out, w.symbols)
