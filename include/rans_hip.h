@@ -311,6 +311,25 @@ int rans_latent_symbols(const float *y, const float *means, const float *scales,
 int rans_dequantize(const int32_t *symbols, const float *means, uint64_t n, float *y_hat,
                     hipStream_t hstream);
 
+/* For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the encode above
+ * with no workspace argument.  The workspace is a fixed array of 64 MiB that
+ * the library holds on every GPU it runs on, from module load until the
+ * process ends; its device address is looked up once per device, and on the
+ * first call on a device a fill kernel enqueued on `hstream` zeroes its
+ * bookkeeping prefix.  The call allocates nothing.  A call whose
+ * rans_workspace_bytes(n, num_lanes, num_tables, cdf_stride) exceeds 64 MiB
+ * returns RANS_E_WORKSPACE (about 8M symbols with the 64-row table set).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls on one GPU must not overlap in time (order them on one
+ * stream or synchronise), else they race.  Arguments, outputs, errors and
+ * the container are those of rans_encode_with_indexes. */
+int rans_encode_noalloc(const int32_t *symbols, const int32_t *indexes, uint64_t n,
+                        const int32_t *cdf, const int32_t *cdf_lengths, const int32_t *offsets,
+                        int32_t num_tables, int32_t cdf_stride, uint32_t num_lanes,
+                        uint32_t *stream, uint64_t stream_capacity_words, uint64_t *stream_words,
+                        int32_t *status, hipStream_t hstream);
+
 /* Static text for a status code. */
 const char *rans_status_string(int code);
 

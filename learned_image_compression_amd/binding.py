@@ -49,6 +49,7 @@ EXPORTS = (
     "rans_decode_interleaved_prepared",
     "rans_decode_with_splits",
     "rans_dequantize",
+    "rans_encode_noalloc",
     "rans_status_string",
 )
 
@@ -132,6 +133,9 @@ def load(path: str | None = None):
         lib.rans_latent_symbols.restype = ctypes.c_int
         lib.rans_dequantize.argtypes = [vp, vp, u64, vp, vp]
         lib.rans_dequantize.restype = ctypes.c_int
+        lib.rans_encode_noalloc.argtypes = [vp, vp, u64, vp, vp, vp, i32, i32, u32, vp, u64, vp,
+                                            vp, vp]
+        lib.rans_encode_noalloc.restype = ctypes.c_int
         lib.rans_status_string.argtypes = [ctypes.c_int]
         lib.rans_status_string.restype = ctypes.c_char_p
         if path is None:
@@ -280,6 +284,28 @@ def encode_with_indexes(symbols: torch.Tensor, indexes: torch.Tensor, tables: Ta
                                           _ptr(stream_out), stream_out.numel(), _ptr(stream_words),
                                           _ptr(status), _ptr(ws), ws.numel(), st)
     _check_rc(rc, "rans_encode_with_indexes")
+    return stream_out, stream_words, status
+
+
+def encode_noalloc(symbols: torch.Tensor, indexes: torch.Tensor, tables: Tables, num_lanes: int,
+                   stream_out: torch.Tensor, stream_words: torch.Tensor, status: torch.Tensor):
+    """Enqueue an encode that allocates nothing: the library's fixed per-device
+    scratch array serves as the workspace (``rans_encode_noalloc``).  All
+    buffers are the caller's; calls on one GPU must not overlap in time."""
+    device = tables.device
+    _need(symbols, torch.int32, device, "symbols")
+    _need(indexes, torch.int32, device, "indexes")
+    _need(stream_out, torch.int32, device, "stream_out")
+    _need(stream_words, torch.int64, device, "stream_words")
+    _need(status, torch.int32, device, "status")
+    n = symbols.numel()
+    if indexes.numel() != n:
+        raise ValueError("symbols and indexes differ in size")
+    rc = load().rans_encode_noalloc(_ptr(symbols), _ptr(indexes), n, _ptr(tables.cdf),
+                                    _ptr(tables.lengths), _ptr(tables.offsets), tables.num_tables,
+                                    tables.stride, num_lanes, _ptr(stream_out), stream_out.numel(),
+                                    _ptr(stream_words), _ptr(status), _stream(device))
+    _check_rc(rc, "rans_encode_noalloc")
     return stream_out, stream_words, status
 
 
