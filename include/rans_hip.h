@@ -311,6 +311,39 @@ int rans_latent_symbols(const float *y, const float *means, const float *scales,
 int rans_dequantize(const int32_t *symbols, const float *means, uint64_t n, float *y_hat,
                     hipStream_t hstream);
 
+/* The front end fused into the interleaved encoder (kompressor BENCHMARKS.md,
+ * section 4: the int32 symbols and indexes a codec hands to its coder are a
+ * round trip through memory that the coder can avoid).  The container, the
+ * status and every error are exactly those of rans_encode_interleaved /
+ * rans_encode_interleaved_prepared on
+ *   rans_latent_symbols(y, means, scales, n, scale_table, num_tables, ...),
+ * i.e. symbol and table index of each position follow the rules above, with
+ * the scale table holding one scale per CDF row (num_tables entries, any
+ * order; ascending is fastest).  The symbols and indexes are never written to
+ * memory: the encoder reads 12 bytes per position (y, means, scales, float32
+ * device arrays of n entries) instead of the front end's 12 in, 8 out and the
+ * encoder's 8 in.  A position whose symbol saturates (NaN, or beyond int32)
+ * makes *status RANS_E_SYMBOL_RANGE, as it would in two passes.  Workspace:
+ * rans_interleaved_workspace_bytes(n, num_streams, num_tables, cdf_stride);
+ * the _prepared form needs the tables prepared on it, as for
+ * rans_encode_interleaved_prepared. */
+int rans_encode_interleaved_latent(const float *y, const float *means, const float *scales,
+                                   uint64_t n, const float *scale_table, const int32_t *cdf,
+                                   const int32_t *cdf_lengths, const int32_t *offsets,
+                                   int32_t num_tables, int32_t cdf_stride, uint32_t num_streams,
+                                   uint32_t *stream, uint64_t stream_capacity_words,
+                                   uint64_t *stream_words, int32_t *status, void *workspace,
+                                   uint64_t workspace_bytes, hipStream_t hstream);
+
+int rans_encode_interleaved_latent_prepared(const float *y, const float *means,
+                                            const float *scales, uint64_t n,
+                                            const float *scale_table, int32_t num_tables,
+                                            int32_t cdf_stride, uint32_t num_streams,
+                                            uint32_t *stream, uint64_t stream_capacity_words,
+                                            uint64_t *stream_words, int32_t *status,
+                                            void *workspace, uint64_t workspace_bytes,
+                                            hipStream_t hstream);
+
 /* For callers that cannot allocate device memory (code under stream capture,
  * tight serving loops, harnesses that forbid hipMalloc): the encode above
  * with no workspace argument.  The workspace is a fixed array of 64 MiB that

@@ -50,6 +50,8 @@ EXPORTS = (
     "rans_decode_with_splits",
     "rans_dequantize",
     "rans_encode_noalloc",
+    "rans_encode_interleaved_latent",
+    "rans_encode_interleaved_latent_prepared",
     "rans_status_string",
 )
 
@@ -136,6 +138,12 @@ def load(path: str | None = None):
         lib.rans_encode_noalloc.argtypes = [vp, vp, u64, vp, vp, vp, i32, i32, u32, vp, u64, vp,
                                             vp, vp]
         lib.rans_encode_noalloc.restype = ctypes.c_int
+        lib.rans_encode_interleaved_latent.argtypes = [vp, vp, vp, u64, vp, vp, vp, vp, i32, i32,
+                                                       u32, vp, u64, vp, vp, vp, u64, vp]
+        lib.rans_encode_interleaved_latent.restype = ctypes.c_int
+        lib.rans_encode_interleaved_latent_prepared.argtypes = [vp, vp, vp, u64, vp, i32, i32, u32,
+                                                                vp, u64, vp, vp, vp, u64, vp]
+        lib.rans_encode_interleaved_latent_prepared.restype = ctypes.c_int
         lib.rans_status_string.argtypes = [ctypes.c_int]
         lib.rans_status_string.restype = ctypes.c_char_p
         if path is None:
@@ -547,6 +555,48 @@ def encode_interleaved(symbols: torch.Tensor, indexes: torch.Tensor, tables: Tab
                                          _ptr(stream_out), stream_out.numel(), _ptr(stream_words),
                                          _ptr(status), _ptr(ws), ws.numel(), _stream(device))
     _check_rc(rc, "rans_encode_interleaved")
+    return stream_out, stream_words, status
+
+
+def encode_interleaved_latent(y: torch.Tensor, means: torch.Tensor, scales: torch.Tensor,
+                              scale_table: torch.Tensor, tables: Tables, num_streams: int, *,
+                              stream_out: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None, prepared: bool = False):
+    """Enqueue the front end fused into the interleaved encode: the container
+    of ``encode_interleaved(*latent_symbols(y, means, scales, scale_table))``
+    with no symbol or index array in between (float32 device tensors of one
+    size; ``scale_table`` holds one scale per table row).  Returns (stream int32
+    words, stream_words int64[1], status int32[1])."""
+    device = tables.device
+    for t, name in ((y, "y"), (means, "means"), (scales, "scales"), (scale_table, "scale_table")):
+        _need(t, torch.float32, device, name)
+    n = y.numel()
+    if means.numel() != n or scales.numel() != n:
+        raise ValueError("y, means and scales differ in size")
+    if scale_table.numel() != tables.num_tables:
+        raise ValueError("the scale table needs one scale per table row")
+    lib = load()
+    if stream_out is None:
+        stream_out = torch.empty(int(lib.rans_interleaved_bound_words(n, num_streams)),
+                                 dtype=torch.int32, device=device)
+    _need(stream_out, torch.int32, device, "stream_out")
+    stream_words = torch.zeros(1, dtype=torch.int64, device=device)
+    status = torch.zeros(1, dtype=torch.int32, device=device)
+    ws = workspace if workspace is not None else workspace_for(device).get(
+        int(lib.rans_interleaved_workspace_bytes(n, num_streams, tables.num_tables,
+                                                 tables.stride)))
+    if prepared:
+        rc = lib.rans_encode_interleaved_latent_prepared(
+            _ptr(y), _ptr(means), _ptr(scales), n, _ptr(scale_table), tables.num_tables,
+            tables.stride, num_streams, _ptr(stream_out), stream_out.numel(), _ptr(stream_words),
+            _ptr(status), _ptr(ws), ws.numel(), _stream(device))
+    else:
+        rc = lib.rans_encode_interleaved_latent(
+            _ptr(y), _ptr(means), _ptr(scales), n, _ptr(scale_table), _ptr(tables.cdf),
+            _ptr(tables.lengths), _ptr(tables.offsets), tables.num_tables, tables.stride,
+            num_streams, _ptr(stream_out), stream_out.numel(), _ptr(stream_words), _ptr(status),
+            _ptr(ws), ws.numel(), _stream(device))
+    _check_rc(rc, "rans_encode_interleaved_latent")
     return stream_out, stream_words, status
 
 

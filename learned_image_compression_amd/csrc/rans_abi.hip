@@ -282,6 +282,67 @@ int rans_encode_interleaved_prepared(const int32_t *symbols, const int32_t *inde
     return launched(launch_il_encode(a, hstream));
 }
 
+int rans_encode_interleaved_latent_prepared(const float *y, const float *means,
+                                            const float *scales, uint64_t n,
+                                            const float *scale_table, int32_t num_tables,
+                                            int32_t cdf_stride, uint32_t num_streams,
+                                            uint32_t *stream, uint64_t stream_capacity_words,
+                                            uint64_t *stream_words, int32_t *status,
+                                            void *workspace, uint64_t workspace_bytes,
+                                            hipStream_t hstream)
+{
+    if (num_streams == 0 || num_streams > RANS_MAX_STREAMS || !stream || !stream_words ||
+        !status || !scale_table || (n && (!y || !means || !scales)))
+        return RANS_E_ARG;
+    if (num_tables < 1 || num_tables > RANS_MAX_TABLES || cdf_stride < 3 ||
+        cdf_stride > RANS_MAX_STRIDE)
+        return RANS_E_TABLE;
+    if (n > RANS_MAX_SYMBOLS || stream_capacity_words < 1ull + num_streams)
+        return RANS_E_ARG;
+    int rc = check_workspace(workspace, workspace_bytes,
+                             rans_interleaved_workspace_bytes(n, num_streams, num_tables,
+                                                              cdf_stride));
+    if (rc)
+        return rc;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    IlArgs a{nullptr, nullptr, n, num_streams, num_tables, cdf_stride, stream, nullptr,
+             stream_capacity_words, stream_words, nullptr, status, ws,
+             reinterpret_cast<uint32_t *>(ws + tables_end(num_tables, cdf_stride)),
+             reinterpret_cast<uint32_t *>(ws + il_counts_offset(n, num_streams, num_tables,
+                                                                cdf_stride)),
+             y, means, scales, scale_table};
+    return launched(launch_il_encode(a, hstream));
+}
+
+int rans_encode_interleaved_latent(const float *y, const float *means, const float *scales,
+                                   uint64_t n, const float *scale_table, const int32_t *cdf,
+                                   const int32_t *cdf_lengths, const int32_t *offsets,
+                                   int32_t num_tables, int32_t cdf_stride, uint32_t num_streams,
+                                   uint32_t *stream, uint64_t stream_capacity_words,
+                                   uint64_t *stream_words, int32_t *status, void *workspace,
+                                   uint64_t workspace_bytes, hipStream_t hstream)
+{
+    if (num_streams == 0 || num_streams > RANS_MAX_STREAMS || !stream || !stream_words ||
+        !status || !scale_table || (n && (!y || !means || !scales)))
+        return RANS_E_ARG;
+    if (n > RANS_MAX_SYMBOLS || stream_capacity_words < 1ull + num_streams)
+        return RANS_E_ARG;
+    int rc = check_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride);
+    if (rc)
+        return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes,
+                              rans_interleaved_workspace_bytes(n, num_streams, num_tables,
+                                                               cdf_stride))))
+        return rc;
+    if ((rc = rans_prepare_tables(cdf, cdf_lengths, offsets, num_tables, cdf_stride, workspace,
+                                  workspace_bytes, hstream)))
+        return rc;
+    return rans_encode_interleaved_latent_prepared(y, means, scales, n, scale_table, num_tables,
+                                                   cdf_stride, num_streams, stream,
+                                                   stream_capacity_words, stream_words, status,
+                                                   workspace, workspace_bytes, hstream);
+}
+
 int rans_decode_interleaved_prepared(const uint32_t *stream, uint64_t stream_capacity_words,
                                      const int32_t *indexes, uint64_t n, int32_t num_tables,
                                      int32_t cdf_stride, uint32_t num_streams, int32_t *symbols,

@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "rans_coding.hpp"
+#include "rans_frontend.hpp"
 
 namespace rans {
 namespace {
@@ -58,18 +59,41 @@ __device__ inline uint32_t lanes_above(uint64_t mask, uint32_t lane)
 
 // ---- encode: streams into scratch --------------------------------------------
 
+// The scale table of the fused front end sits in LDS after the coding tables
+// and the block's bookkeeping words.
+constexpr uint32_t kIlScaleLds = kEncTableBudget + kLdsMiscBytes;
+
+__device__ inline const float *il_scale_lds()
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    return reinterpret_cast<const float *>(lds + kIlScaleLds);
+}
+
+// One step group's inputs as loaded: symbols and indexes, or (FUSED) the
+// latent, means and scales from which the front end derives them.
+template <bool FUSED>
+struct IlIn {
+    int32_t s[kIlAhead], r[kIlAhead];
+};
+template <>
+struct IlIn<true> {
+    float y[kIlAhead], mu[kIlAhead], sc[kIlAhead];
+};
+
 // One stream coded by one wave (t < S), tables in LDS or in the workspace.
-template <class Tab>
+template <bool FUSED, class Tab>
 __device__ __forceinline__ void il_encode_stream(const IlArgs &a, const Tab &tab, uint32_t K,
-                                                 uint32_t t)
+                                                 uint32_t t, const ScaleTable &st)
 {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t S = a.streams;
     const uint64_t b = lane_begin(a.n, S, t), e = lane_begin(a.n, S, t + 1);
     const uint32_t m = (uint32_t)(e - b);
-    const Rsrc rsym = make_rsrc(a.symbols + b, 4 * m);
-    const Rsrc ridx = make_rsrc(a.indexes + b, 4 * m);
+    // symbols and indexes, or the latent, means and scales
+    const Rsrc rin0 = make_rsrc(FUSED ? (const void *)(a.y + b) : (const void *)(a.symbols + b), 4 * m);
+    const Rsrc rin1 = make_rsrc(FUSED ? (const void *)(a.means + b) : (const void *)(a.indexes + b), 4 * m);
+    const Rsrc rin2 = make_rsrc(FUSED ? (const void *)(a.scales + b) : nullptr, FUSED ? 4 * m : 0u);
     uint32_t *scr = a.scratch + il_scratch_begin(a.n, S, t);
     const uint32_t cap = 2 * m + 2 * kIlW;   // emitted words the stream's scratch holds
     uint32_t *emit = scr + 2 * kIlW;
@@ -91,15 +115,36 @@ __device__ __forceinline__ void il_encode_stream(const IlArgs &a, const Tab &tab
     };
 
     const uint32_t G = (m + kIlW - 1) / kIlW;
-    int32_t sa[kIlAhead], ia[kIlAhead], sb[kIlAhead], ib[kIlAhead];
+    IlIn<FUSED> in_a, in_b;
     // steps g0 - 1 .. g0 - kIlAhead (steps below 0 load nothing)
-    auto load = [&](int32_t (&s)[kIlAhead], int32_t (&r)[kIlAhead], int64_t g0) {
+    auto load = [&](IlIn<FUSED> &in, int64_t g0) {
 #pragma unroll
         for (int u = 0; u < kIlAhead; ++u) {
             const int64_t g = g0 - 1 - u;
             const uint32_t off = g >= 0 ? (uint32_t)(4 * (g * kIlW + lane)) : 0x80000000u;
-            s[u] = buf_load(rsym, off, 0);
-            r[u] = buf_load(ridx, off, 0);
+            if constexpr (FUSED) {
+                in.y[u] = __int_as_float(buf_load(rin0, off, 0));
+                in.mu[u] = __int_as_float(buf_load(rin1, off, 0));
+                in.sc[u] = __int_as_float(buf_load(rin2, off, 0));
+            } else {
+                in.s[u] = buf_load(rin0, off, 0);
+                in.r[u] = buf_load(rin1, off, 0);
+            }
+        }
+    };
+    // the symbols and indexes of a loaded group (the front end's, fused)
+    auto convert = [&](const IlIn<FUSED> &in, int32_t (&s)[kIlAhead], int32_t (&r)[kIlAhead]) {
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int u = 0; u < kIlAhead; ++u)
+                s[u] = saturate_round(in.y[u] - in.mu[u]);
+            st.index_n(in.sc, r);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kIlAhead; ++u) {
+                s[u] = in.s[u];
+                r[u] = in.r[u];
+            }
         }
     };
     // `full` is std::true_type in groups whose every step lies inside the
@@ -160,18 +205,21 @@ __device__ __forceinline__ void il_encode_stream(const IlArgs &a, const Tab &tab
         }
     };
 
-    load(sa, ia, (int64_t)G);
-    load(sb, ib, (int64_t)G - kIlAhead);
+    load(in_a, (int64_t)G);
+    load(in_b, (int64_t)G - kIlAhead);
     // steps g0 - 1 .. g0 - 2 kIlAhead
     auto group = [&](auto full, int64_t g0) {
+        int32_t sv[kIlAhead], rv[kIlAhead];
+        convert(in_a, sv, rv);
 #pragma unroll
         for (int u = 0; u < kIlAhead; ++u)
-            step(full, sa[u], ia[u], g0 - 1 - u);
-        load(sa, ia, g0 - 2 * kIlAhead);
+            step(full, sv[u], rv[u], g0 - 1 - u);
+        load(in_a, g0 - 2 * kIlAhead);
+        convert(in_b, sv, rv);
 #pragma unroll
         for (int u = 0; u < kIlAhead; ++u)
-            step(full, sb[u], ib[u], g0 - kIlAhead - 1 - u);
-        load(sb, ib, g0 - 3 * kIlAhead);
+            step(full, sv[u], rv[u], g0 - kIlAhead - 1 - u);
+        load(in_b, g0 - 3 * kIlAhead);
     };
     // the first group may hold the stream's partial last step; after it, the
     // groups wholly inside the stream (steps >= 0, every one full), then the
@@ -198,15 +246,25 @@ __device__ __forceinline__ void il_encode_stream(const IlArgs &a, const Tab &tab
 // A stream coded from tables read in the workspace (a set over the LDS
 // budget): out of line, so that the LDS form keeps its registers.  The
 // arguments arrive in vector registers and are made scalar again here.
-__device__ __attribute__((noinline)) void il_encode_stream_global(IlArgs a_arg, uint32_t t_arg)
+template <bool FUSED>
+__device__ __attribute__((noinline)) void il_encode_stream_global(IlArgs a_arg, uint32_t t_arg,
+                                                                  uint32_t steps_arg,
+                                                                  uint32_t sorted_arg)
 {
     const IlArgs a = uniform_copy(a_arg);
     const uint32_t t = __builtin_amdgcn_readfirstlane(t_arg);
-    il_encode_stream(a, GlobalTab{a.ws + ws_enc_offset(a.num_tables, a.stride)},
-                     (uint32_t)a.num_tables, t);
+    ScaleTable st;
+    st.t = il_scale_lds();
+    st.K = a.num_tables;
+    st.steps = (int32_t)__builtin_amdgcn_readfirstlane(steps_arg);
+    st.sorted = __builtin_amdgcn_readfirstlane(sorted_arg) != 0;
+    il_encode_stream<FUSED>(a, GlobalTab{a.ws + ws_enc_offset(a.num_tables, a.stride)},
+                            (uint32_t)a.num_tables, t, st);
 }
 
-template <int TPB>
+// FUSED: the symbols and indexes come from the front end (the latent, means
+// and scales, with the scale table staged in LDS after the coding tables).
+template <int TPB, bool FUSED>
 __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -228,7 +286,7 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
     const bool in_lds = hdr->enc_lds != 0;
     stage_tables<TPB>(lds, tab, (!herr && in_lds) ? hdr->enc_bytes : 0u);
     if (tid == 0)
-        misc[0] = 0u;
+        misc[0] = misc[1] = 0u;   // block OR words (tables, scale order)
     __syncthreads();
     int bad = 0;
     if (!herr) {
@@ -238,6 +296,10 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
     }
     if (block_or(&misc[0], bad) && !herr)
         herr = RANS_E_TABLE;
+    ScaleTable st{};
+    if constexpr (FUSED)
+        st = stage_scale_table<TPB>(a.scale_table, a.num_tables,
+                                    reinterpret_cast<float *>(lds + kIlScaleLds), &misc[1]);
     const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (TPB / kWave) + tid / kWave);
     if (herr) {
         if (blockIdx.x == 0 && tid == 0)
@@ -251,9 +313,9 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
     if (t >= S)
         return;
     if (in_lds)
-        il_encode_stream(a, LdsTab{}, K, t);
+        il_encode_stream<FUSED>(a, LdsTab{}, K, t, st);
     else
-        il_encode_stream_global(a, t);
+        il_encode_stream_global<FUSED>(a, t, (uint32_t)st.steps, st.sorted ? 1u : 0u);
 }
 
 // ---- encode: header and container (one wave per stream) -----------------------
@@ -589,16 +651,24 @@ uint32_t il_block_waves(uint32_t streams)
     return streams >= 16 * kCodingCUs ? 16u : (streams >= 8 * kCodingCUs ? 8u : 4u);
 }
 
-template <int TPB>
+template <int TPB, bool FUSED>
 hipError_t launch_il_encode_t(const IlArgs &a, hipStream_t s)
 {
-    const uint32_t lds_bytes = kEncTableBudget + kLdsMiscBytes;
-    static const hipError_t attr = lds_attr(&il_encode_kernel<TPB>, lds_bytes);
+    const uint32_t lds_bytes = kIlScaleLds + (FUSED ? 4u * RANS_MAX_TABLES : 0u);
+    static const hipError_t attr = lds_attr(&il_encode_kernel<TPB, FUSED>, lds_bytes);
     if (attr != hipSuccess)
         return attr;
-    hipLaunchKernelGGL((il_encode_kernel<TPB>), dim3(il_blocks(a.streams, TPB / kWave)), dim3(TPB),
-                       lds_bytes, s, a);
+    hipLaunchKernelGGL((il_encode_kernel<TPB, FUSED>), dim3(il_blocks(a.streams, TPB / kWave)),
+                       dim3(TPB), lds_bytes, s, a);
     return hipGetLastError();
+}
+
+template <bool FUSED>
+hipError_t launch_il_encode_f(const IlArgs &a, hipStream_t s)
+{
+    return il_block_waves(a.streams) == 16 ? launch_il_encode_t<16 * kWave, FUSED>(a, s)
+           : il_block_waves(a.streams) == 8  ? launch_il_encode_t<8 * kWave, FUSED>(a, s)
+                                             : launch_il_encode_t<4 * kWave, FUSED>(a, s);
 }
 
 template <int TPB>
@@ -617,9 +687,7 @@ hipError_t launch_il_decode_t(const IlArgs &a, hipStream_t s)
 
 hipError_t launch_il_encode(const IlArgs &a, hipStream_t s)
 {
-    const hipError_t e = il_block_waves(a.streams) == 16 ? launch_il_encode_t<16 * kWave>(a, s)
-                         : il_block_waves(a.streams) == 8  ? launch_il_encode_t<8 * kWave>(a, s)
-                                                           : launch_il_encode_t<4 * kWave>(a, s);
+    const hipError_t e = a.scale_table ? launch_il_encode_f<true>(a, s) : launch_il_encode_f<false>(a, s);
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(il_copy_kernel, dim3(il_blocks(a.streams, kIlCopyThreads / kWave)),

@@ -472,6 +472,12 @@ struct IlArgs {
     uint8_t *ws;
     uint32_t *scratch;         // per stream: 128 state words, then emitted words
     uint32_t *counts;          // [streams] words of each stream
+    // the fused front end (encode only; symbols and indexes are then null):
+    // the latent, its predicted means and scales, and one scale per table row
+    const float *y;
+    const float *means;
+    const float *scales;
+    const float *scale_table;
 };
 
 // Stream t's scratch starts at word 2 b_t + 256 t (b_t its first symbol):
