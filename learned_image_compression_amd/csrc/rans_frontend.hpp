@@ -28,14 +28,25 @@ __device__ inline int32_t saturate_round(float d)
     return (int32_t)r;
 }
 
+// Cells of the optional index lookup table: the non-negative floats split by
+// their bits 30..19 (exponent and top four mantissa bits), 4096 cells.
+constexpr uint32_t kScaleLutShift = 19;
+constexpr uint32_t kScaleLutCells = 1u << (31 - kScaleLutShift);
+
 // The scale table in LDS.  When its first K - 1 entries are non-decreasing
 // the counted set is a suffix of them, and the index is a branch-free binary
 // search of fixed trip count; otherwise the count is taken entry by entry.
+// A sorted table with no negative first entry may also carry `lut`: cell c
+// holds #{k < K - 1 : table[k] < lo_c}, lo_c the smallest float of the cell,
+// so the index of a scale in cell c is lut[c] plus the entries in [lo_c, s),
+// a forward scan of a step or two when cells are finer than the table (any
+// negative scale counts nothing, NaN gives K - 1).
 struct ScaleTable {
     const float *t;   // LDS
     int32_t K;
     int32_t steps;    // highest power of two <= K - 1 (0 when K == 1)
     bool sorted;
+    const uint16_t *lut;   // LDS, or null
 
     __device__ int32_t index(float s) const
     {
@@ -60,6 +71,30 @@ struct ScaleTable {
     __device__ inline void index_n(const float (&s)[N], int32_t (&out)[N]) const
     {
         const int32_t m = K - 1;
+        if (lut) {
+            int32_t j[N];
+#pragma unroll
+            for (int u = 0; u < N; ++u) {
+                const uint32_t b = __float_as_uint(s[u]);
+                // a scale with the sign bit set lies at or below every entry
+                // (all are >= -0.0 here): it counts nothing
+                j[u] = (b >> 31) ? 0 : (int32_t)lut[b >> kScaleLutShift];
+            }
+            bool go;
+            do {
+                go = false;
+#pragma unroll
+                for (int u = 0; u < N; ++u) {
+                    const bool c = j[u] < m && t[min(j[u], m - 1)] < s[u];
+                    j[u] += c ? 1 : 0;
+                    go = go | c;
+                }
+            } while (__any(go));
+#pragma unroll
+            for (int u = 0; u < N; ++u)
+                out[u] = s[u] != s[u] ? m : j[u];
+            return;
+        }
         if (sorted) {
             int32_t j[N];
 #pragma unroll
@@ -94,18 +129,42 @@ __device__ inline ScaleTable stage_scale_table(const float *table, int32_t K, fl
     for (int32_t k = threadIdx.x; k < K; k += TPB)
         lds[k] = table[k];
     __syncthreads();
+    // the counted entries must be non-decreasing and none NaN (a NaN entry
+    // is neither below nor at or above a scale, so no search can count it)
     bool unsorted = false;
-    for (int32_t k = threadIdx.x; k + 2 < K; k += TPB)
-        unsorted |= !(lds[k] <= lds[k + 1]);   // NaN entries count as unsorted
+    for (int32_t k = threadIdx.x; k + 1 < K; k += TPB)
+        unsorted |= !(lds[k] == lds[k]) || (k + 2 < K && !(lds[k] <= lds[k + 1]));
     ScaleTable st;
     st.t = lds;
     st.K = K;
     st.sorted = !block_or(flag, unsorted);
+    st.lut = nullptr;
     int32_t p = 1;
     while (2 * p <= K - 1)
         p *= 2;
     st.steps = K > 1 ? p : 0;
     return st;
+}
+
+// Fill the index lookup table of a staged scale table when it qualifies
+// (sorted, first entry not negative); `lut` holds kScaleLutCells entries in
+// LDS.  Every thread of the block must call this.
+template <int TPB>
+__device__ inline void build_scale_lut(ScaleTable &st, uint16_t *lut)
+{
+    if (!st.sorted || st.K < 2 || st.t[0] < 0.0f)
+        return;   // (the same decision in every thread)
+    for (uint32_t c = threadIdx.x; c < kScaleLutCells; c += TPB) {
+        const float lo = __uint_as_float(c << kScaleLutShift);
+        // #{k < K - 1 : t[k] < lo}: the binary search of index()
+        int32_t j = 0;
+        for (int32_t step = st.steps; step > 0; step >>= 1)
+            if (j + step <= st.K - 1 && st.t[j + step - 1] < lo)
+                j += step;
+        lut[c] = (uint16_t)j;
+    }
+    __syncthreads();
+    st.lut = lut;
 }
 
 }  // namespace rans

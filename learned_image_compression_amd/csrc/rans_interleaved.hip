@@ -63,10 +63,18 @@ __device__ inline uint32_t lanes_above(uint64_t mask, uint32_t lane)
 // and the block's bookkeeping words.
 constexpr uint32_t kIlScaleLds = kEncTableBudget + kLdsMiscBytes;
 
+constexpr uint32_t kIlScaleLutLds = kIlScaleLds + 4 * RANS_MAX_TABLES;
+
 __device__ inline const float *il_scale_lds()
 {
     extern __shared__ __align__(16) uint8_t lds[];
     return reinterpret_cast<const float *>(lds + kIlScaleLds);
+}
+
+__device__ inline const uint16_t *il_scale_lut_lds()
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    return reinterpret_cast<const uint16_t *>(lds + kIlScaleLutLds);
 }
 
 // One step group's inputs as loaded: symbols and indexes, or (FUSED) the
@@ -249,15 +257,17 @@ __device__ __forceinline__ void il_encode_stream(const IlArgs &a, const Tab &tab
 template <bool FUSED>
 __device__ __attribute__((noinline)) void il_encode_stream_global(IlArgs a_arg, uint32_t t_arg,
                                                                   uint32_t steps_arg,
-                                                                  uint32_t sorted_arg)
+                                                                  uint32_t mode_arg)
 {
     const IlArgs a = uniform_copy(a_arg);
     const uint32_t t = __builtin_amdgcn_readfirstlane(t_arg);
+    const uint32_t mode = __builtin_amdgcn_readfirstlane(mode_arg);   // bit 0 sorted, bit 1 lut
     ScaleTable st;
     st.t = il_scale_lds();
     st.K = a.num_tables;
     st.steps = (int32_t)__builtin_amdgcn_readfirstlane(steps_arg);
-    st.sorted = __builtin_amdgcn_readfirstlane(sorted_arg) != 0;
+    st.sorted = (mode & 1u) != 0;
+    st.lut = (mode & 2u) ? il_scale_lut_lds() : nullptr;
     il_encode_stream<FUSED>(a, GlobalTab{a.ws + ws_enc_offset(a.num_tables, a.stride)},
                             (uint32_t)a.num_tables, t, st);
 }
@@ -297,9 +307,11 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
     if (block_or(&misc[0], bad) && !herr)
         herr = RANS_E_TABLE;
     ScaleTable st{};
-    if constexpr (FUSED)
+    if constexpr (FUSED) {
         st = stage_scale_table<TPB>(a.scale_table, a.num_tables,
                                     reinterpret_cast<float *>(lds + kIlScaleLds), &misc[1]);
+        build_scale_lut<TPB>(st, reinterpret_cast<uint16_t *>(lds + kIlScaleLutLds));
+    }
     const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (TPB / kWave) + tid / kWave);
     if (herr) {
         if (blockIdx.x == 0 && tid == 0)
@@ -315,7 +327,8 @@ __global__ __launch_bounds__(TPB) void il_encode_kernel(IlArgs a)
     if (in_lds)
         il_encode_stream<FUSED>(a, LdsTab{}, K, t, st);
     else
-        il_encode_stream_global<FUSED>(a, t, (uint32_t)st.steps, st.sorted ? 1u : 0u);
+        il_encode_stream_global<FUSED>(a, t, (uint32_t)st.steps,
+                                       (st.sorted ? 1u : 0u) | (st.lut ? 2u : 0u));
 }
 
 // ---- encode: header and container (one wave per stream) -----------------------
@@ -654,7 +667,7 @@ uint32_t il_block_waves(uint32_t streams)
 template <int TPB, bool FUSED>
 hipError_t launch_il_encode_t(const IlArgs &a, hipStream_t s)
 {
-    const uint32_t lds_bytes = kIlScaleLds + (FUSED ? 4u * RANS_MAX_TABLES : 0u);
+    const uint32_t lds_bytes = FUSED ? kIlScaleLutLds + 2u * kScaleLutCells : kIlScaleLds;
     static const hipError_t attr = lds_attr(&il_encode_kernel<TPB, FUSED>, lds_bytes);
     if (attr != hipSuccess)
         return attr;

@@ -5,9 +5,11 @@ oracle chain gives: oracle.latent_symbols (symbol = rint(y - mean), index
 from the scale table), then oracle.encode_interleaved (64 states a stream).
 Cases: the 1080p y shape (192 x 68 x 120) at 4096 streams and at one
 stream, ragged sizes, an empty latent, saturating and NaN values (the status
-must match the oracle's), unsorted / tied / NaN-holding scale tables, a
-one-row set, a table set over the LDS budget (the global-table path), and
-two prepared calls in a row on one workspace.  The GPU's own two-pass path
+must match the oracle's), unsorted / tied / NaN-holding / two-entry scale
+tables, one with negative entries (no index lookup table) and one packed
+into a single lookup cell (long forward scans), a one-row set, a table set
+over the LDS budget (the global-table path), and two prepared calls in a row
+on one workspace.  The GPU's own two-pass path
 (front end, then encode) must agree too.
 """
 from __future__ import annotations
@@ -121,16 +123,22 @@ def test_fused_edge_values_status(what):
         assert rc == oracle.E_SYMBOL_RANGE
 
 
-@pytest.mark.parametrize("name", ["unsorted", "ties", "nan_entry", "one_row"])
+@pytest.mark.parametrize("name", ["unsorted", "ties", "nan_entry", "one_row", "two_nan",
+                                  "two_sorted", "negative", "one_cell"])
 def test_fused_other_scale_tables(name):
     import gpu_util as G
     rng = np.random.default_rng(11)
     table = {"unsorted": rng.permutation(TABLE64),
              "ties": np.repeat(TABLE64[::4], 4),
              "nan_entry": np.where(np.arange(64) == 17, np.nan, TABLE64),
+             "two_nan": np.array([np.nan, 1.0]),
+             "two_sorted": np.array([0.5, 1.0]),
+             "negative": np.linspace(-3.0, 40.0, 64),
+             "one_cell": np.linspace(1.0, 1.05, 64),
              "one_row": TABLE64[40:41]}[name].astype(np.float32)
-    # the coding rows come from a finite copy of the table (one row per entry)
-    rows = np.where(np.isnan(table), np.float32(1.0), table)
+    # the coding rows come from a positive finite copy of the table (one row
+    # per entry)
+    rows = np.where(np.isfinite(table) & (table > 0), table, np.float32(1.0))
     G.say(f"[fused] scale table {name}")
     host_tables, tables = _tables(rows, 3133)
     y, m, s = _latent(50021, 21)

@@ -88,12 +88,17 @@ def test_random_latents(n, offset):
     assert np.array_equal(sym, osym) and np.array_equal(idx, oidx)
 
 
-@pytest.mark.parametrize("name", ["unsorted", "nan_entry", "one_entry", "ties"])
+@pytest.mark.parametrize("name", ["unsorted", "nan_entry", "one_entry", "ties", "two_nan",
+                                  "two_sorted", "negative", "one_cell"])
 def test_other_tables(name):
     import gpu_util as G
     rng = np.random.default_rng(3)
     table = {"unsorted": rng.permutation(TABLE64),
              "nan_entry": np.where(np.arange(64) == 17, np.nan, TABLE64),
+             "two_nan": np.array([np.nan, 1.0]),
+             "two_sorted": np.array([0.5, 1.0]),
+             "negative": np.linspace(-3.0, 40.0, 64),
+             "one_cell": np.linspace(1.0, 1.05, 64),
              "one_entry": TABLE64[:1],
              "ties": np.repeat(TABLE64[::4], 4)}[name].astype(np.float32)
     y, m, s = _random_latent(20011, 5)
