@@ -22,7 +22,12 @@ The line also reports:
   rans_encode_with_splits beside the unchanged container);
 - the device table builder on the workload's own table set (64 discretised
   Gaussians, scales log-spaced over 0.11..256, stride 3133), whose output
-  must equal the workload's tables.
+  must equal the workload's tables;
+- "batch": the lane coding kernels on the batch workloads (16 1080p y
+  latents at 65,536 lanes; 8 4K y latents at 1,024, 16,384 and 131,072
+  lanes), the interleaved calls at 4096 streams, and the front end fused
+  into the interleaved encoder, each container checked against the
+  oracle's in the CPU-baseline leg (skip with --no-batch).
 
 value = symbols per step / step time (a step encodes and decodes every
 symbol once).  The roofline object reports the slower of the two coding
@@ -106,12 +111,24 @@ def cpu_model_name() -> str:
                   if l.strip().lower().startswith("model name")]
     except (OSError, subprocess.SubprocessError):
         pass
+    ids = {}
     try:
         with open("/proc/cpuinfo") as fh:
-            names += [l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")]
+            for l in fh:
+                key, _, val = l.partition(":")
+                key = key.strip()
+                if key == "model name":
+                    names.append(val.strip())
+                elif key in ("cpu family", "model", "stepping") and key not in ids:
+                    ids[key] = val.strip()
     except OSError:
         pass
-    return max(names, key=len) if names else ""
+    name = max(names, key=len) if names else ""
+    # a shortened name ("AMD EPYC") still tells the part apart with its CPUID
+    # family, model and stepping
+    if ids:
+        name += " (" + ", ".join(f"{k} {v}" for k, v in ids.items()) + ")"
+    return name
 
 
 def lane_groups(n: int, lanes: int, groups: int):
@@ -221,6 +238,140 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
     }
 
 
+# Batch configurations reported beside the headline (lane counts as the
+# survey's parity sweep lists them), and the interleaved stream count used
+# for them.
+BATCH_POINTS = (("y1080x16", 65536), ("y4kx8", 1024), ("y4kx8", 16384), ("y4kx8", 131072))
+BATCH_STREAMS = 4096
+
+
+def _median_us(fn, reps):
+    """Median duration of fn() bracketed by HIP events on the current stream."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps + 2)]
+    for a, b in ev:
+        a.record()
+        if fn():
+            raise RuntimeError("launch failed")
+        b.record()
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) for a, b in ev[2:]) * 1e3
+
+
+def batch_point(cfg: str, lanes: int, streams: int, check_oracle: bool, reps: int = 10):
+    """One batch configuration: the lane coding kernels (the *_prepared calls, as
+    in the timed step) and the interleaved calls on tables prepared once, plus
+    the front end fused into the interleaved encoder, fed a latent built so
+    that it yields exactly the workload's symbols and indexes (y = symbol,
+    mean = 0, scale = the table's scale of the index, a strictly increasing
+    table).  Every container is compared with the one before it and, with
+    check_oracle, with the oracle's."""
+    import ctypes
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+    from learned_image_compression_amd import binding as B
+    lib, vp, dev = B.load(), ctypes.c_void_p, torch.device("cuda:0")
+    w = workloads.load(cfg)
+    n = w.n
+    tables = B.Tables.from_numpy(w.cdf, w.lengths, w.offsets, dev)
+    K, stride = tables.num_tables, tables.stride
+    sym = torch.from_numpy(w.symbols).to(dev)
+    idx = torch.from_numpy(w.indexes).to(dev)
+    hs = vp(torch.cuda.current_stream(dev).cuda_stream)
+    cap = B.encode_bound_words(n, lanes)
+    stream = torch.empty(cap, dtype=torch.int32, device=dev)
+    nw = torch.zeros(1, dtype=torch.int64, device=dev)
+    st = torch.zeros(2, dtype=torch.int32, device=dev)
+    out = torch.empty(n, dtype=torch.int32, device=dev)
+    ws = torch.zeros(B.workspace_bytes(n, lanes, K, stride), dtype=torch.uint8, device=dev)
+    B.prepare_tables(tables, ws)
+    enc = lambda: lib.rans_encode_prepared(vp(sym.data_ptr()), vp(idx.data_ptr()), n, K, stride,
+                                           lanes, vp(stream.data_ptr()), cap, vp(nw.data_ptr()),
+                                           vp(st.data_ptr()), vp(ws.data_ptr()), ws.numel(), hs)
+    dec = lambda: lib.rans_decode_prepared(vp(stream.data_ptr()), cap, vp(idx.data_ptr()), n, K,
+                                           stride, vp(out.data_ptr()), vp(st.data_ptr() + 4),
+                                           vp(ws.data_ptr()), ws.numel(), hs)
+    enc_us, dec_us = _median_us(enc, reps), _median_us(dec, reps)
+    B.check(st[:1], f"{cfg} encode")
+    B.check(st[1:], f"{cfg} decode")
+    words = int(nw.item())
+    assert torch.equal(out.cpu(), torch.from_numpy(w.symbols)), f"{cfg}: decode != input"
+    lane_words = stream[:words].cpu().numpy().view(np.uint32).copy()
+    del ws
+    # interleaved container, plain and fused encode, on tables prepared once
+    S = streams
+    il_cap = int(lib.rans_interleaved_bound_words(n, S))
+    il_ws = torch.zeros(int(lib.rans_interleaved_workspace_bytes(n, S, K, stride)),
+                        dtype=torch.uint8, device=dev)
+    B.prepare_tables(tables, il_ws)
+    il_stream = torch.empty(il_cap, dtype=torch.int32, device=dev)
+    il_enc = lambda: lib.rans_encode_interleaved_prepared(
+        vp(sym.data_ptr()), vp(idx.data_ptr()), n, K, stride, S, vp(il_stream.data_ptr()), il_cap,
+        vp(nw.data_ptr()), vp(st.data_ptr()), vp(il_ws.data_ptr()), il_ws.numel(), hs)
+    il_dec = lambda: lib.rans_decode_interleaved_prepared(
+        vp(il_stream.data_ptr()), il_cap, vp(idx.data_ptr()), n, K, stride, S,
+        vp(out.data_ptr()), vp(st.data_ptr() + 4), vp(il_ws.data_ptr()), il_ws.numel(), hs)
+    il_enc_us = _median_us(il_enc, reps)
+    B.check(st[:1], f"{cfg} interleaved encode")
+    il_words = int(nw.item())
+    il_host = il_stream[:il_words].cpu().numpy().view(np.uint32).copy()
+    out.zero_()
+    il_dec_us = _median_us(il_dec, reps)
+    B.check(st[1:], f"{cfg} interleaved decode")
+    assert torch.equal(out.cpu(), torch.from_numpy(w.symbols)), f"{cfg}: interleaved decode != input"
+    fused = None
+    if int(np.abs(w.symbols).max(initial=0)) <= (1 << 24):
+        table = (table_set()[0] if K == 64 else np.arange(1, K + 1)).astype(np.float32)
+        assert np.all(np.diff(table) > 0)
+        y = sym.to(torch.float32)
+        mean = torch.zeros_like(y)
+        scale = torch.from_numpy(table).to(dev)[idx.long()]
+        d_table = torch.from_numpy(table).to(dev)
+        il_stream.zero_()
+        fz = lambda: lib.rans_encode_interleaved_latent_prepared(
+            vp(y.data_ptr()), vp(mean.data_ptr()), vp(scale.data_ptr()), n, vp(d_table.data_ptr()),
+            K, stride, S, vp(il_stream.data_ptr()), il_cap, vp(nw.data_ptr()), vp(st.data_ptr()),
+            vp(il_ws.data_ptr()), il_ws.numel(), hs)
+        fused = _median_us(fz, reps)
+        B.check(st[:1], f"{cfg} fused encode")
+        assert int(nw.item()) == il_words and np.array_equal(
+            il_stream[:il_words].cpu().numpy().view(np.uint32), il_host), \
+            f"{cfg}: fused container differs from the interleaved one"
+    checked = "GPU round trips"
+    if check_oracle:
+        rc, owords = oracle.encode(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, lanes)
+        assert rc == 0 and np.array_equal(owords, lane_words), \
+            f"{cfg} L={lanes}: GPU container differs from the oracle's"
+        rc, oil = oracle.encode_interleaved(w.symbols, w.indexes, w.cdf, w.lengths, w.offsets, S,
+                                            64)
+        assert rc == 0 and np.array_equal(oil, il_host), \
+            f"{cfg} S={S}: GPU interleaved container differs from the oracle's"
+        checked = "lane and interleaved containers equal the oracle's"
+    bytes_lane = 8 * n + 4 * words
+    bytes_il = 8 * n + 4 * il_words
+    frac = lambda b, us: round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    r = {"config": cfg, "symbols": n, "lanes": lanes,
+         "encode_us": round(enc_us, 2), "decode_us": round(dec_us, 2),
+         "encode_gsym_s": round(n / enc_us / 1e3, 2), "decode_gsym_s": round(n / dec_us / 1e3, 2),
+         "encode_frac": frac(bytes_lane, enc_us), "decode_frac": frac(bytes_lane, dec_us),
+         "interleaved": {"streams": S, "encode_call_us": round(il_enc_us, 2),
+                         "decode_call_us": round(il_dec_us, 2),
+                         "encode_frac": frac(bytes_il, il_enc_us),
+                         "decode_frac": frac(bytes_il, il_dec_us)},
+         "parity": checked}
+    if fused is not None:
+        r["interleaved"]["fused_encode_call_us"] = round(fused, 2)
+        # the fused call reads y, mean and scale (12 B/position) instead of
+        # symbols and indexes (8 B)
+        r["interleaved"]["fused_frac"] = frac(12 * n + 4 * il_words, fused)
+    del il_ws, il_stream, stream, out, sym, idx
+    torch.cuda.empty_cache()
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +383,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--streams", type=int, default=None,
                     help="interleaved streams (default: lanes / 64, at most 4096)")
+    ap.add_argument("--no-batch", action="store_true",
+                    help="skip the batch configurations (profiling runs)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -514,6 +667,9 @@ def main():
                                     f"stride {tstride}",
                         "us": round(statistics.median(tab_us), 2)},
     }
+    if not args.no_batch:
+        line["batch"] = [batch_point(c, L, BATCH_STREAMS, not args.no_cpu_baseline)
+                         for c, L in BATCH_POINTS]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, lanes, gpu_words, gpu_tables, args.cpu_seconds,
                                             split=(P, gpu_records), interleaved=(S_il, gpu_il))
