@@ -24,10 +24,13 @@
 // that does not depend on the state -- row metadata, the slot's pair, the
 // reciprocal of f, whether the symbol is an ordinary one -- is computed for
 // the whole round first.  When every lane of the wave has a full round of
-// ordinary symbols, the state chain runs with no branch and no LDS access:
-// a symbol spills at most one word, which waits in a register together with
-// its scratch position.  Other rounds take each escaped (or erroneous)
-// symbol through the general puts, which store their words directly.
+// ordinary symbols, the state chain runs with no branch and no LDS access.
+// Otherwise the same chain runs with one wave-uniform test per position:
+// where some lane escapes, those lanes first put the value's groups and
+// count and take the escape slot's pair; padding positions and bad indexes
+// take an identity step.  Spilled words go to the lane's LDS ring either
+// way.  Only a lane near the end of its scratch segment, or a round holding
+// a split cut, redoes its round with the checked puts.
 //
 // Memory schedule.  Global memory is touched only between rounds, in
 // straight-line code with a fixed number of accesses: the round's candidate
@@ -84,12 +87,13 @@ struct Spill {
     }
 };
 
-// The puts of one symbol off the common path (an escaped value, or a lane
-// near the end of its segment), applied last to first; the row index is in
-// range.  Returns a status code.
+// The puts of one symbol that come before its REG put (applied last to
+// first: an escaped value's groups, then its group count), and the (start, f)
+// pair of the slot its REG put codes; the row index is in range.  Returns a
+// status code.
 template <int TPB, class Tab>
-__device__ __forceinline__ int encode_slow(int32_t s, const RowMeta m, const Tab &tab, uint64_t &x,
-                                           Spill<TPB> &sp)
+__device__ __forceinline__ int encode_prefix(int32_t s, const RowMeta m, const Tab &tab, uint64_t &x,
+                                             Spill<TPB> &sp, uint32_t &pair)
 {
     int err = 0;
     const uint32_t mv = m.mvf & 0xFFFFu;
@@ -113,8 +117,19 @@ __device__ __forceinline__ int encode_slow(int32_t s, const RowMeta m, const Tab
         put_bits((uint32_t)(raw >> (kBypassBits * g)) & 15u);
     if (esc)
         put_bits(nb);
-    // the REG put of the slot
-    const uint32_t pr = tab.template load<uint32_t>(m.base + 4 * (esc ? mv : (uint32_t)v));
+    pair = tab.template load<uint32_t>(m.base + 4 * (esc ? mv : (uint32_t)v));
+    return err;
+}
+
+// All puts of one symbol off the common path (an escaped value, or a lane
+// near the end of its segment), applied last to first; the row index is in
+// range.  Returns a status code.
+template <int TPB, class Tab>
+__device__ __forceinline__ int encode_slow(int32_t s, const RowMeta m, const Tab &tab, uint64_t &x,
+                                           Spill<TPB> &sp)
+{
+    uint32_t pr;
+    const int err = encode_prefix<TPB>(s, m, tab, x, sp, pr);
     const uint32_t f = pr >> 16;
     const bool spill = x >= ((uint64_t)f << (63 - kPrecision));
     sp.put_if(spill, (uint32_t)x);
@@ -295,16 +310,59 @@ __device__ __forceinline__ LaneResult encode_lane(const EncodeArgs &a, const Tab
         const uint64_t x0 = x;
         const uint32_t cb_start = sp.cb;
         pre(sym, idx, k0 + kRound, Pn);
+        if (__builtin_expect(__all(P.fast == (1u << kRound) - 1), 1)) {
 #pragma unroll
-        for (int u = 0; u < kRound; ++u) {
-            const bool need = (uint32_t)(x >> 32) >= (P.f[u] << (31 - kPrecision));
-            *sp.slot((sp.cb - sp.cb0) >> 2) = (uint32_t)x;
-            sp.cb += need ? 4u : 0u;
-            x = need ? (x >> 32) : x;
-            x = reg_step(x, P.start[u], P.f[u], P.rcp[u]);
+            for (int u = 0; u < kRound; ++u) {
+                const bool need = (uint32_t)(x >> 32) >= (P.f[u] << (31 - kPrecision));
+                *sp.slot((sp.cb - sp.cb0) >> 2) = (uint32_t)x;
+                sp.cb += need ? 4u : 0u;
+                x = need ? (x >> 32) : x;
+                x = reg_step(x, P.start[u], P.f[u], P.rcp[u]);
+            }
+        } else {
+            // Some lane holds a position off the common path.  Per
+            // position, the lanes concerned (a wave-uniform branch, taken
+            // only where one of them is) put an escape's groups and count
+            // and take the slot pair of its REG put; a position that is no
+            // position (padding before the lane's first round is full, a
+            // round past its end) or holds a bad index takes the identity
+            // step start 0, f = 2^16 (x unchanged, never renormalised).
+            // Every spilled word goes to the ring (at most 3 a position).
+#pragma unroll
+            for (int u = 0; u < kRound; ++u) {
+                uint32_t st = P.start[u], fu = P.f[u];
+                double ru = P.rcp[u];
+                const bool off = ((P.fast >> u) & 1u) == 0u;
+                if (__ballot(off) != 0) {
+                    if (off) {
+                        st = 0u;
+                        fu = kTotal;
+                        ru = 1.0 / kTotal;
+                        if (valid(k0 + u)) {
+                            if ((uint32_t)P.idx[u] < K) {
+                                uint32_t pr;
+                                const int ec = encode_prefix<TPB>(P.sym[u], tab.meta(P.idx[u]),
+                                                                  tab, x, sp, pr);
+                                lerr = lerr ? lerr : ec;
+                                st = pr & 0xFFFFu;
+                                fu = pr >> 16;
+                                ru = reciprocal(fu);
+                            } else {
+                                lerr = lerr ? lerr : RANS_E_INDEX;
+                            }
+                        }
+                    }
+                }
+                const bool need = (uint32_t)(x >> 32) >= (fu << (31 - kPrecision));
+                *sp.slot(min((sp.cb - sp.cb0) >> 2, kEncRing - 1)) = (uint32_t)x;
+                sp.cb += need ? 4u : 0u;
+                x = need ? (x >> 32) : x;
+                x = reg_step(x, st, fu, ru);
+            }
         }
-        if (__builtin_expect(!__all((P.fast == (1u << kRound) - 1) & room & (cut_k >= k0 + kRound)),
-                             0)) {
+        // A lane near the end of its segment (whose spills need checks), or
+        // a round holding a split cut, redoes the round from its start.
+        if (__builtin_expect(!__all(room & (cut_k >= k0 + kRound)), 0)) {
             x = x0;
             sp.cb = cb_start;
             // the fast step is committed where it applies; the other
@@ -652,8 +710,9 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             // and stores whole 16-byte groups of its own words, then its last
             // one to three words one by one.  Accesses are masked per lane
             // (a lane without words for a group sends no request).
-            const uint64_t wbase = 1ull + L + __builtin_amdgcn_readfirstlane((uint32_t)prefix) +
-                                   ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(prefix >> 32)) << 32);
+            const uint64_t wbase =
+                1ull + L + (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)prefix) +
+                ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(prefix >> 32)) << 32);
             const uint64_t wroom = a.capacity > wbase ? a.capacity - wbase : 0;
             const Rsrc rout = make_rsrc(a.stream + (wroom ? wbase : 0),
                                         (uint32_t)min(4 * wroom, 1ull << 31));
