@@ -351,10 +351,21 @@ __device__ inline T uniform_copy(const T &in)
 // Raw buffer access (gfx9 buffer descriptor, 32-bit data format): the
 // hardware drops stores and returns 0 for loads at byte offsets at or past
 // `bytes`, and the constant part of an offset rides in the instruction.
+// Every descriptor here belongs to a whole wavefront, so its base and size
+// are taken from the first active lane: the descriptor then lives in scalar
+// registers, as a buffer instruction needs it, even where the compiler
+// cannot prove the values uniform (it would otherwise wrap every access in a
+// loop over the distinct descriptors of the lanes).
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 __device__ inline Rsrc make_rsrc(const void *base, uint32_t bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+    // (readfirstlane returns int: each half goes back to uint32_t before it
+    // is widened, or a low half with bit 31 set would fill the high one)
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(lo | (hi << 32)), (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes),
                                              0x00020000);
 }
 __device__ inline int32_t buf_load(Rsrc r, uint32_t voff, int cofs)
