@@ -27,21 +27,30 @@
 
 namespace rans {
 
-constexpr int kPrepThreads = 256;
+// One block per row (up to 256 blocks, a grid-stride loop beyond): 1024
+// threads, so that the longest rows (3133 entries for the 64-row Gaussian
+// set) take a few entries and buckets per thread.
+constexpr int kPrepThreads = 1024;
+constexpr int kPrepWaves = kPrepThreads / kWave;
 
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
 {
     __shared__ uint32_t s_base[RANS_MAX_TABLES];
-    __shared__ uint32_t s_part[kPrepThreads];
+    __shared__ uint32_t s_wave[kPrepWaves];
     __shared__ int32_t s_val[RANS_MAX_STRIDE];
 
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wv = tid / kWave;
     const int K = a.num_tables;
     const uint32_t stride = (uint32_t)a.stride;
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
     uint8_t *tab = a.ws + ws_dec_offset();
+    // this block's first row's offset, requested before anything waits
+    const int32_t off_first = (int)blockIdx.x < K ? a.offsets[blockIdx.x] : 0;
 
     // --- 1. effective lengths and their exclusive scan (every block) ----------
+    // thread t sums rows [t*chunk, (t+1)*chunk); a wave scan by shuffles, then
+    // one pass over the wave totals
     const int chunk = (K + kPrepThreads - 1) / kPrepThreads;
     const int r0 = tid * chunk;
     const int r1 = min(K, r0 + chunk);
@@ -52,21 +61,26 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
         s_base[r] = eff;
         sum += eff;
     }
-    s_part[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < kPrepThreads; off <<= 1) {   // inclusive Hillis-Steele scan
-        uint32_t v = (tid >= off) ? s_part[tid - off] : 0u;
-        __syncthreads();
-        s_part[tid] += v;
-        __syncthreads();
+    uint32_t incl = sum;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, kWave);
+        incl += lane >= o ? v : 0u;
     }
-    uint32_t run = s_part[tid] - sum;
+    if (lane == kWave - 1)
+        s_wave[wv] = incl;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+    for (int w = 0; w < kPrepWaves; ++w) {
+        const uint32_t v = s_wave[w];
+        before += w < wv ? v : 0u;
+        total += v;
+    }
+    uint32_t run = before + incl - sum;
     for (int r = r0; r < r1; ++r) {
         uint32_t eff = s_base[r];
         s_base[r] = run;
         run += eff;
     }
-    const uint32_t total = s_part[kPrepThreads - 1];
     __syncthreads();
 
     // decoder set [meta | cdfm1 | first], encoder set [meta | pairs]; each is
@@ -160,7 +174,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
         }
         bad = __syncthreads_or(bad);
         if (tid == 0) {
-            const int32_t off = a.offsets[r];
+            const int32_t off = r == (int)blockIdx.x ? off_first : a.offsets[r];
             const uint32_t mv = len - 2;
             // slots below mv take the fast paths if offset + slot fits int32
             const bool fits = (int64_t)off + (int64_t)mv - 1 <= (int64_t)INT32_MAX;
