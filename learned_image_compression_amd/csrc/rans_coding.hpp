@@ -19,23 +19,26 @@ __device__ inline double reciprocal(uint32_t f)
     return __builtin_fma(r, e, r);
 }
 
-// x <- floor(x/f)*2^16 + (x mod f) + start, for x < f * 2^47.
-// q = round(x * (1/f)) is read from the mantissa of fma(x, 1/f, 2^52); with
-// x/f < 2^47 and a relative error below 2^-50 the estimate is floor(x/f) or
-// one more, so one exact correction on the low 32 bits of x - q*f (which lie
-// in [-f, f)) gives the true quotient and remainder.
+// x <- floor(x/f)*2^16 + (x mod f) + start, for x < f * 2^47 and
+// 1 <= f <= 2^16.  q = round(x * (1/f)) is read from the mantissa of
+// fma(x, 1/f, 2^52); with x/f < 2^47 and a relative error below 2^-50 the
+// estimate is floor(x/f) or one more, and r = x - q*f (whose low 32 bits
+// hold it exactly, as |r| < 2^16) says which.  The result is then
+//   q*2^16 + r + start                  when r >= 0,
+//   (q-1)*2^16 + (r + f) + start        when r < 0,
+// i.e. q*2^16 + s with the 32-bit s = r + start + (r < 0 ? f - 2^16 : 0),
+// s in [-2^16, 2^17).  Shifting the double's bit pattern left by 16 keeps
+// exactly q*2^16 (q < 2^47 sits in its low 47 bits; the exponent bits move
+// out), and s is added sign-extended.
 __device__ inline uint64_t reg_step(uint64_t x, uint32_t start, uint32_t f, double rcp)
 {
-    const double xd = __builtin_fma((double)(uint32_t)(x >> 32), 4294967296.0,
-                                    (double)(uint32_t)x);
+    const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+    const double xd = __builtin_fma((double)hi, 4294967296.0, (double)lo);
     const double t = __builtin_fma(xd, rcp, 4503599627370496.0);   // 2^52
-    uint64_t q = (uint64_t)__double_as_longlong(t) & ((1ull << 52) - 1);
-    int32_t r = (int32_t)((uint32_t)x - (uint32_t)q * f);
-    if (r < 0) {
-        q -= 1;
-        r += (int32_t)f;
-    }
-    return (q << kPrecision) + (uint32_t)r + start;
+    const uint64_t tb = (uint64_t)__double_as_longlong(t);
+    const int32_t r = (int32_t)(lo - (uint32_t)tb * f);
+    const int32_t s = r + (int32_t)start + ((r >> 31) & ((int32_t)f - (int32_t)kTotal));
+    return (tb << kPrecision) + (uint64_t)(int64_t)s;
 }
 
 }  // namespace rans
