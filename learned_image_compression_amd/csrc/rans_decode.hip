@@ -419,9 +419,9 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs &a, const Tab &tab,
         // compiler's wait counts only ever cover requests that are at least a
         // round old.  Loads past the wave's span read 0; stores meant for
         // nothing use kNoStore.
-        int32_t ia[kRound], ib[kRound], out[kRound];
+        int32_t ia[kRound], ib[kRound], out[2 * kRound];
 #pragma unroll
-        for (int k = 0; k < kRound; ++k)
+        for (int k = 0; k < 2 * kRound; ++k)
             out[k] = 0;
         // The round's symbols: a full round (every lane of the wave) as two
         // 16-byte stores, a partial one (a lane's last round) a word per
@@ -429,15 +429,19 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs &a, const Tab &tab,
         // carry no per-word address work; the wait counts merged from the
         // rare partial branch cost less than the eight extra stores (6% on
         // the 1080p latent at 4096 lanes).
-        auto store_round = [&](uint32_t k0, bool full) {
-            if (__builtin_expect(full, 1)) {
-                buf_store4(rout, ob + 4 * k0,
-                           u32x4{(uint32_t)out[0], (uint32_t)out[1], (uint32_t)out[2], (uint32_t)out[3]});
-                buf_store4(rout, ob + 4 * k0 + 16,
-                           u32x4{(uint32_t)out[4], (uint32_t)out[5], (uint32_t)out[6], (uint32_t)out[7]});
+        // The symbols of a pair of rounds (positions k0 .. k0+15), stored
+        // after the second: 64 bytes per lane at once, which halves the
+        // partial-line writes of 32-byte pieces.
+        auto store_pair = [&](uint32_t k0) {
+            if (__builtin_expect(__all(k0 + 2 * kRound <= nj), 1)) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    buf_store4(rout, ob + 4 * k0 + 16 * q,
+                               u32x4{(uint32_t)out[4 * q], (uint32_t)out[4 * q + 1],
+                                     (uint32_t)out[4 * q + 2], (uint32_t)out[4 * q + 3]});
             } else {
 #pragma unroll
-                for (int k = 0; k < kRound; ++k)
+                for (int k = 0; k < 2 * kRound; ++k)
                     buf_store(rout, k0 + k < nj ? ob + 4 * (k0 + k) : kNoStore, 0, out[k]);
             }
         };
@@ -476,8 +480,9 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs &a, const Tab &tab,
             }
             wd.next = wd.at(wd.pos);
         };
-        auto round = [&](int32_t (&idx)[kRound], uint32_t (&pend)[kRefill], uint32_t &pend_at,
-                         uint32_t k0) {
+        auto round = [&](auto second, int32_t (&idx)[kRound], uint32_t (&pend)[kRefill],
+                         uint32_t &pend_at, uint32_t k0) {
+            constexpr int o = decltype(second)::value ? kRound : 0;   // the round's out[] half
             // row metadata; an index outside [0, K) reads row K-1 with a fast
             // bound of 0 (its step then reports the index), which only a round
             // holding such an index has to arrange
@@ -512,7 +517,7 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs &a, const Tab &tab,
                     bool bad = false;
 #pragma unroll
                     for (int k = 0; k < kRound; ++k)
-                        decode_step_spec<TPB>(m[k], x, wd, t, tab, out[k], bad);
+                        decode_step_spec<TPB>(m[k], x, wd, t, tab, out[o + k], bad);
                     bad = bad | (wd.pos > wd.filled);   // read a ring slot not yet filled
                     if (bad) {
                         x = x0;
@@ -526,9 +531,9 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs &a, const Tab &tab,
 #pragma unroll
                 for (int k = 0; k < kRound; ++k) {
                     if (general) {
-                        out[k] = 0;
+                        out[o + k] = 0;
                         if (k0 + k < nj && !lerr)
-                            decode_step<TPB>(idx[k], m[k], x, wd, t, tab, out[k], lerr);
+                            decode_step<TPB>(idx[k], m[k], x, wd, t, tab, out[o + k], lerr);
                     }
                 }
             }
@@ -538,7 +543,8 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs &a, const Tab &tab,
             // 16 bytes twice, a partial one word by word, and a later wait
             // for these loads then never has to cover those stores
             load_next(idx, pend, pend_at, k0 + 2 * kRound);
-            store_round(k0, full);
+            if constexpr (decltype(second)::value)
+                store_pair(k0 - kRound);
             __builtin_amdgcn_sched_barrier(0);
         };
         // prologue: two phases of the same shape (stores to nothing)
@@ -548,14 +554,13 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs &a, const Tab &tab,
                 load_next(ib, pb, pb_at, kRound);
             else
                 load_next(ia, pa, pa_at, 0);
-            store_round(nj, false);   // (positions from nj on: every store at kNoStore)
             __builtin_amdgcn_sched_barrier(0);
         }
         // both rounds always run (symbols past the lane end are skipped inside),
         // so every path back to the loop head passes both memory phases
         for (uint32_t k0 = 0; k0 < nj && !lerr; k0 += 2 * kRound) {
-            round(ia, pa, pa_at, k0);
-            round(ib, pb, pb_at, k0 + kRound);
+            round(std::false_type{}, ia, pa, pa_at, k0);
+            round(std::true_type{}, ib, pb, pb_at, k0 + kRound);
         }
         if (!lerr && (x != x_end || wd.pos != W - left1))
             lerr = RANS_E_CORRUPT;

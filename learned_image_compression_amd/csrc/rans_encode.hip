@@ -230,7 +230,9 @@ __device__ __forceinline__ LaneResult encode_lane(const EncodeArgs &a, const Tab
         for (int i = 0; i < 8; ++i)
             r[i] = *sp.slot(i);
         const bool whole = sp.cb0 + 32 <= sp.capb;
-        const uint32_t off = whole ? sp.top - sp.cb0 - 32 : kNoStore;
+        // (a round that spilled nothing sends both stores past the buffer,
+        // where they are dropped: no write traffic for it)
+        const uint32_t off = (whole & (n > 0)) ? sp.top - sp.cb0 - 32 : kNoStore;
         buf_store4(sp.scr, off, u32x4{r[7], r[6], r[5], r[4]});
         buf_store4(sp.scr, off + 16, u32x4{r[3], r[2], r[1], r[0]});
         if (__builtin_expect(__ballot(!whole | (n > 8)) != 0, 0)) {

@@ -16,8 +16,16 @@ Three commands, all meant to run under or after rocprofv3:
   python -m learned_image_compression_amd.profiling interleaved [--config C]
           [--streams S] [--reps R]
       Interleaved-stream encode and decode calls on a workload (workloads/),
-      R times each, for kernel-trace and counter passes; checks the round
-      trip and prints the container size and the bytes each call moves.
+      R times each, then the same encode with the front end fused in (fed a
+      latent that yields the workload's symbols and indexes), for
+      kernel-trace and counter passes; checks the round trip and the fused
+      container and prints the container size and the bytes each call moves.
+
+  python -m learned_image_compression_amd.profiling lanes [--config C]
+          [--lanes L] [--reps R]
+      Lane-container encode and decode on tables prepared once (the
+      *_prepared calls, as bench.py times them), R times each, for
+      kernel-trace and counter passes at any workload and lane count.
 
   python -m learned_image_compression_amd.profiling summarize ...
       Turns rocprofv3 CSV output (kernel trace statistics and the counter
@@ -43,7 +51,8 @@ def kernel_source_hash(name: str) -> str:
     """Hash of the sources that make up one coding kernel (rans_<name>.hip and
     the shared headers): counter summaries recorded for other sources are stale."""
     h = hashlib.sha256()
-    for f in ("rans_internal.hpp", "rans_coding.hpp", f"rans_{name}.hip"):
+    extra = ("rans_frontend.hpp",) if name == "interleaved" else ()
+    for f in ("rans_internal.hpp", "rans_coding.hpp", *extra, f"rans_{name}.hip"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -104,9 +113,58 @@ def interleaved_main(config: str, streams: int, reps: int) -> None:
     if not torch.equal(out.cpu(), torch.from_numpy(w.symbols)):
         raise RuntimeError("interleaved round trip differs from the input")
     words = int(nwords.item())
+    ref = stream[:words].clone()
+    # the fused front end: y = symbol, mean = 0, scale = the index's entry of a
+    # strictly increasing table, which give back exactly the workload's
+    # symbols and indexes
+    fused = None
+    if int(sym.abs().max()) <= (1 << 24):
+        K = tables.num_tables
+        table = (torch.exp(torch.linspace(0.0, 1.0, K, dtype=torch.float64) * 7.6 - 2.2)
+                 .float().to(dev))
+        if bool((table[1:] > table[:-1]).all()):
+            y = sym.float()
+            mean = torch.zeros_like(y)
+            scale = table[idx.long()]
+            for _ in range(reps):
+                fs, fnw, fst = B.encode_interleaved_latent(y, mean, scale, table, tables, streams)
+            torch.cuda.synchronize()
+            B.check(fst, "fused encode")
+            if int(fnw.item()) != words or not torch.equal(fs[:words], ref):
+                raise RuntimeError("fused container differs from the interleaved one")
+            fused = 12 * w.n + 4 * words
     # a call reads symbols (or writes them) and indexes, and writes (or reads)
-    # the container
+    # the container; the fused encode reads y, means and scales instead
     print(json.dumps({"config": config, "streams": streams, "reps": reps, "n": w.n,
+                      "container_words": words,
+                      "algorithmic_bytes_per_call": 8 * w.n + 4 * words,
+                      "fused_algorithmic_bytes_per_call": fused}), flush=True)
+
+
+def lanes_main(config: str, lanes: int, reps: int) -> None:
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import workloads
+    from learned_image_compression_amd import binding as B
+    dev = torch.device("cuda:0")
+    w = workloads.load(config)
+    tables = B.Tables.from_numpy(w.cdf, w.lengths, w.offsets, dev)
+    sym = torch.from_numpy(w.symbols).to(dev)
+    idx = torch.from_numpy(w.indexes).to(dev)
+    ws = torch.zeros(B.workspace_bytes(w.n, lanes, tables.num_tables, tables.stride),
+                     dtype=torch.uint8, device=dev)
+    B.prepare_tables(tables, ws)
+    for _ in range(reps):
+        stream, nwords, st = B.encode_with_indexes(sym, idx, tables, lanes, workspace=ws,
+                                                   prepared=True)
+        out, st2 = B.decode_with_indexes(stream, idx, tables, workspace=ws, prepared=True)
+    torch.cuda.synchronize()
+    B.check(st, "encode")
+    B.check(st2, "decode")
+    if not torch.equal(out.cpu(), torch.from_numpy(w.symbols)):
+        raise RuntimeError("lane round trip differs from the input")
+    words = int(nwords.item())
+    print(json.dumps({"config": config, "lanes": lanes, "reps": reps, "n": w.n,
                       "container_words": words,
                       "algorithmic_bytes_per_call": 8 * w.n + 4 * words}), flush=True)
 
@@ -122,6 +180,8 @@ def _rows(path_glob: str):
 def _kernel_key(name: str) -> str:
     if re.search(r"decode_kernel<[^>]*true>", name):
         return "decode_kernel_split"
+    if re.search(r"il_encode_kernel<[^>]*true>", name):
+        return "il_encode_kernel_fused"
     # the interleaved kernels first: their names contain the lane kernels'
     m = re.search(r"(il_encode_kernel|il_decode_kernel|il_scan_kernel|il_copy_kernel|"
                   r"encode_kernel|decode_kernel|prep_kernel|table_rows_kernel|"
@@ -190,7 +250,10 @@ def summarize_main(a) -> None:
             for c in names:
                 for k, v in counter_per_dispatch(g, c).items():
                     table.setdefault(k, {})[c] = v
-        lines = [f"# rocprofv3 counters (mean per dispatch): {a.label}", f"# command: {a.command}", ""]
+        lines = [f"# rocprofv3 counters (mean per dispatch): {a.label}", f"# command: {a.command}",
+                 "# kernel sources: " + ", ".join(f"{k} {kernel_source_hash(k)}"
+                                                  for k in ("encode", "decode", "interleaved")),
+                 ""]
         for k in sorted(table):
             if not k.startswith(("il_", "encode", "decode", "prep", "table", "latent", "dequant")):
                 continue
@@ -219,7 +282,10 @@ def summarize_main(a) -> None:
                  "copy_calibration": {"copy_bytes": copy_bytes, "fetch_kib": round(cf, 1),
                                       "write_kib": round(cw, 1), "fetch_scale": round(f_scale, 4),
                                       "write_scale": round(w_scale, 4)}}
-            for key in ("il_encode_kernel", "il_scan_kernel", "il_copy_kernel", "il_decode_kernel"):
+            t["source_hash"] = kernel_source_hash("interleaved")
+            t["fused_algorithmic_bytes_per_call"] = run.get("fused_algorithmic_bytes_per_call")
+            for key in ("il_encode_kernel", "il_encode_kernel_fused", "il_copy_kernel",
+                        "il_decode_kernel"):
                 if key not in fetch or key not in write:
                     continue
                 rb = fetch[key] * KIB * f_scale
@@ -305,6 +371,10 @@ def main(argv=None) -> None:
     il.add_argument("--config", default="y1080x16")
     il.add_argument("--streams", type=int, default=4096)
     il.add_argument("--reps", type=int, default=5)
+    ln = sub.add_parser("lanes")
+    ln.add_argument("--config", default="y1080x16")
+    ln.add_argument("--lanes", type=int, default=65536)
+    ln.add_argument("--reps", type=int, default=5)
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         copy_main(a.mib, a.reps)
@@ -312,6 +382,8 @@ def main(argv=None) -> None:
         latent_main(a.n, a.reps)
     elif a.cmd == "interleaved":
         interleaved_main(a.config, a.streams, a.reps)
+    elif a.cmd == "lanes":
+        lanes_main(a.config, a.lanes, a.reps)
     else:
         summarize_main(a)
 
