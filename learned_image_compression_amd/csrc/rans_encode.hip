@@ -146,7 +146,11 @@ struct LaneResult {
     int err;
 };
 
-template <int TPB, class Tab>
+// PAIR: the symbols and indexes of two rounds are loaded together, 64 bytes
+// per lane and array, into one of two alternating 16-entry buffers (for
+// waves of many lanes, whose lines the L2 would otherwise drop between one
+// 32-byte round and the next); else one round's 32 bytes at a time.
+template <int TPB, class Tab, bool PAIR>
 __device__ __forceinline__ LaneResult encode_lane(const EncodeArgs &a, const Tab &tab, uint32_t K,
                                                   uint32_t L, uint32_t j, uint64_t bw, Rsrc rsym,
                                                   Rsrc ridx, Spill<TPB> sp)
@@ -298,15 +302,40 @@ __device__ __forceinline__ LaneResult encode_lane(const EncodeArgs &a, const Tab
                 P.rcp[u] = __builtin_fma(P.rcp[u], e[u], P.rcp[u]);
         }
     };
+    // Steps k .. k+15 (two rounds) into a pair buffer: 64 contiguous bytes
+    // per array, whose reverse order is the steps' order.  A window that
+    // starts before the wave's buffer (the offset wraps) reads 0; one that
+    // starts before the lane reads the previous lane's values: only for
+    // steps that are no positions.
+    auto load_pair = [&](int32_t (&sym)[2 * kRound], int32_t (&idx)[2 * kRound], uint32_t k) {
+        const uint32_t lo = pbase + 4 * (R8 - 2 * kRound - k);
+        u32x4 sv[4], iv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            sv[q] = buf_load4(rsym, lo + 16 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            iv[q] = buf_load4(ridx, lo + 16 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sym[15 - 4 * q - e] = (int32_t)sv[q][e];
+                idx[15 - 4 * q - e] = (int32_t)iv[q][e];
+            }
+        __builtin_amdgcn_sched_barrier(0);
+    };
     // One round of positions k0 .. k0+7 on P, with the next round's
     // state-independent work (from sym/idx into Pn) in the same
     // straight-line block, where it fills the chain's latency.  The
     // chain assumes every position fast; a round where that is not so
     // for some lane (an escape, a bad index, a lane end, a lane near
     // the end of its segment) is redone from its start state with
-    // the general puts.
-    auto round = [&](const Pre &P, uint32_t k0, int32_t (&sym)[kRound],
-                     int32_t (&idx)[kRound], Pre &Pn) {
+    // the general puts.  The round's loads follow its stores: the symbols
+    // and indexes of the round three ahead into the buffer just used, or
+    // (PAIR) whatever `mem` issues.
+    auto round = [&](const Pre &P, uint32_t k0, int32_t (&sym)[kRound], int32_t (&idx)[kRound],
+                     Pre &Pn, auto &&mem) {
         // room for three words per position: the fast steps need no check
         const bool room = sp.cb + 4 * (2 + 3 * kRound) < sp.capb;
         const uint64_t x0 = x;
@@ -392,32 +421,60 @@ __device__ __forceinline__ LaneResult encode_lane(const EncodeArgs &a, const Tab
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // ---- memory phase: this round's words, the symbols and
-        // indexes of the round three ahead into the buffer just used
+        // ---- memory phase: this round's words, then its loads
         store_words();
         __builtin_amdgcn_sched_barrier(0);
-        load_next(sym, idx, k0 + 3 * kRound);
+        if constexpr (PAIR)
+            mem();
+        else
+            load_next(sym, idx, k0 + 3 * kRound);
     };
-    // prologue: three phases of the same shape (their stores carry
-    // stale ring words to positions that later words overwrite);
-    // rounds 0 and 1 are loaded, round 0 prepared, round 2 loaded
     Pre pa, pb;
-    store_words();
-    __builtin_amdgcn_sched_barrier(0);
-    load_next(sa, ia, 0);
-    store_words();
-    __builtin_amdgcn_sched_barrier(0);
-    load_next(sb, ib, kRound);
-    pre(sa, ia, 0, pa);
-    __builtin_amdgcn_sched_barrier(0);
-    store_words();
-    __builtin_amdgcn_sched_barrier(0);
-    load_next(sa, ia, 2 * kRound);
-    // both rounds always run (positions past the lane are skipped
-    // inside), so every path back to the loop head passes both phases
-    for (uint32_t k0 = 0; k0 < R8; k0 += 2 * kRound) {
-        round(pa, k0, sb, ib, pb);
-        round(pb, k0 + kRound, sa, ia, pa);
+    if constexpr (PAIR) {
+        // pair buffers: rounds 0-1 in (s0, i0), 2-3 in (s1, i1); a pair is
+        // loaded by the second round of the pair before the one that
+        // first reads it (two rounds ahead), into the buffer just freed
+        int32_t s0[2 * kRound], i0[2 * kRound], s1[2 * kRound], i1[2 * kRound];
+        auto half = [](int32_t (&v)[2 * kRound], int h) -> int32_t (&)[kRound] {
+            return *reinterpret_cast<int32_t (*)[kRound]>(v + kRound * h);
+        };
+        auto none = [] {};
+        store_words();
+        __builtin_amdgcn_sched_barrier(0);
+        load_pair(s0, i0, 0);
+        load_pair(s1, i1, 2 * kRound);
+        pre(half(s0, 0), half(i0, 0), 0, pa);
+        for (uint32_t k0 = 0; k0 < R8; k0 += 4 * kRound) {
+            round(pa, k0, half(s0, 1), half(i0, 1), pb, none);
+            round(pb, k0 + kRound, half(s1, 0), half(i1, 0), pa,
+                  [&] { load_pair(s0, i0, k0 + 4 * kRound); });
+            if (k0 + 2 * kRound >= R8)   // (this lane's rounds are done)
+                break;
+            round(pa, k0 + 2 * kRound, half(s1, 1), half(i1, 1), pb, none);
+            round(pb, k0 + 3 * kRound, half(s0, 0), half(i0, 0), pa,
+                  [&] { load_pair(s1, i1, k0 + 6 * kRound); });
+        }
+    } else {
+        // prologue: three phases of the same shape (their stores carry
+        // stale ring words to positions that later words overwrite);
+        // rounds 0 and 1 are loaded, round 0 prepared, round 2 loaded
+        store_words();
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(sa, ia, 0);
+        store_words();
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(sb, ib, kRound);
+        pre(sa, ia, 0, pa);
+        __builtin_amdgcn_sched_barrier(0);
+        store_words();
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(sa, ia, 2 * kRound);
+        // both rounds always run (positions past the lane are skipped
+        // inside), so every path back to the loop head passes both phases
+        for (uint32_t k0 = 0; k0 < R8; k0 += 2 * kRound) {
+            round(pa, k0, sb, ib, pb, [] {});
+            round(pb, k0 + kRound, sa, ia, pa, [] {});
+        }
     }
     while (cut_s >= 1)   // an empty lane: every cut holds the start state
         record_cut();
@@ -550,7 +607,7 @@ __device__ inline uint32_t wave_inclusive_scan(uint32_t v, uint32_t lane)
     return v;
 }
 
-template <int TPB, int CW>
+template <int TPB, int CW, bool PAIR>
 __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -614,7 +671,8 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             int lerr = 0;
             if (active) {
                 const LaneResult lr =
-                    in_lds ? encode_lane<TPB>(a, LdsTab{}, K, L, j, wb.bw, wb.rsym, wb.ridx, wb.sp)
+                    in_lds ? encode_lane<TPB, LdsTab, PAIR>(a, LdsTab{}, K, L, j, wb.bw, wb.rsym,
+                                                            wb.ridx, wb.sp)
                            : encode_lane_simple<TPB>(a, GlobalTab{tab}, K, L, j, wb.bw, wb.rsym,
                                                      wb.ridx, wb.sp);
                 words = lr.words;
@@ -777,17 +835,17 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     }
 }
 
-template <int TPB, int CW>
+template <int TPB, int CW, bool PAIR>
 hipError_t launch_encode_t(const EncodeArgs &a, hipStream_t s)
 {
     const uint32_t lds_bytes = encode_lds_bytes(TPB);
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&encode_kernel<TPB, CW>),
+        reinterpret_cast<const void *>(&encode_kernel<TPB, CW, PAIR>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     if (attr != hipSuccess)
         return attr;
     const uint32_t blocks = (enc_waves(a.lanes) + CW - 1) / CW;
-    hipLaunchKernelGGL((encode_kernel<TPB, CW>), dim3(blocks), dim3(TPB), lds_bytes, s, a);
+    hipLaunchKernelGGL((encode_kernel<TPB, CW, PAIR>), dim3(blocks), dim3(TPB), lds_bytes, s, a);
     return hipGetLastError();
 }
 
@@ -795,12 +853,16 @@ hipError_t launch_encode_t(const EncodeArgs &a, hipStream_t s)
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s)
 {
+    // waves of 32 or more lanes load two rounds at a time (see encode_lane)
     const uint32_t waves = enc_waves(a.lanes);
+    const bool pair = enc_lanes_per_wave(a.lanes) >= 32;
     if (coding_one_per_cu(waves))
-        return launch_encode_t<4 * kWave, 1>(a, s);
+        return pair ? launch_encode_t<4 * kWave, 1, true>(a, s)
+                    : launch_encode_t<4 * kWave, 1, false>(a, s);
     if (waves <= 4 * kCodingCUs)
-        return launch_encode_t<4 * kWave, 4>(a, s);
-    return launch_encode_t<8 * kWave, 8>(a, s);
+        return pair ? launch_encode_t<4 * kWave, 4, true>(a, s)
+                    : launch_encode_t<4 * kWave, 4, false>(a, s);
+    return pair ? launch_encode_t<8 * kWave, 8, true>(a, s) : launch_encode_t<8 * kWave, 8, false>(a, s);
 }
 
 }  // namespace rans
