@@ -35,6 +35,7 @@
 
 #include "rans_coding.hpp"
 #include "rans_frontend.hpp"
+#include "rans_lookup.hpp"
 
 namespace rans {
 namespace {
@@ -451,41 +452,45 @@ __device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab
             for (int u = 0; u < kIlAhead; ++u)
                 r[u] = buf_load(ridx, 4 * ((g0 + u) * kIlW + lane), 0);
         };
+        const DecTables dt{kPrecision - shift, shift, K};
         // `full` is std::true_type in groups whose every step lies inside
-        // the stream, which then carry no per-position bound checks
-        auto step = [&](auto full, int32_t r, const RowMeta &mr, uint32_t g) {
+        // the stream, which then carry no per-position bound checks;
+        // `chk` (wave-uniform) is set in groups holding an index outside
+        // [0, K), whose steps then check their index
+        auto step = [&](auto full, bool chk, int32_t r, const RowMeta &mr, uint32_t g) {
             const uint32_t k = g * kIlW + lane;
             const bool valid = decltype(full)::value || k < m;
             const uint32_t mv = mr.mvf & 0xFFFFu;
-            if (valid && (uint32_t)r >= K)
-                lerr = lerr ? lerr : RANS_E_INDEX;
+            if (chk) {
+                if (valid && (uint32_t)r >= K)
+                    lerr = lerr ? lerr : RANS_E_INDEX;
+            }
             // the slot holding cum: the bucket's first slot fs, then one
             // 8-byte read of start-1 for slots fs .. fs+3 settles slots
-            // fs .. fs+2; past them (rare) a walk over the row
-            const uint32_t cum = (uint32_t)x & (kTotal - 1);
-            const uint32_t fs = tab.template load<uint16_t>((mr.lut & ~kRowInvalid) + 2 * (cum >> shift));
-            const uint64_t q4 = tab.u16x4(mr.base + 2 * fs);
-            const uint32_t e0 = (uint32_t)q4 & 0xFFFFu, e1 = (uint32_t)(q4 >> 16) & 0xFFFFu;
-            const uint32_t e2 = (uint32_t)(q4 >> 32) & 0xFFFFu, e3 = (uint32_t)(q4 >> 48);
-            const bool c1 = cum > e1, c2 = c1 & (cum > e2), beyond = c2 & (cum > e3);
-            uint32_t slot = fs + (c1 ? 1u : 0u) + (c2 ? 1u : 0u);
-            uint32_t sm1 = c2 ? e2 : (c1 ? e1 : e0);
-            uint32_t nxt = c2 ? e3 : (c1 ? e2 : e1);
-            if (__builtin_expect(__ballot(beyond) != 0, 0)) {
-                if (beyond) {
-                    slot = fs + 3;
-                    nxt = tab.template load<uint16_t>(mr.base + 2 * (slot + 1));
-                    for (uint32_t i = 0; i <= mv && cum > nxt; ++i) {
+            // fs .. fs+2 (the lane decoder's lookup).  Where the window's
+            // last entry is below cum (rare), a walk over the row from the
+            // lookup's slot: past the window it moves on from fs + 2; where
+            // the window ran past the row's terminal into the next row (a
+            // small entry there, the lookup's slot already right) it stays.
+            Lookup sl = lookup_step(mr, x, dt, tab);
+            if (__builtin_expect(__ballot(sl.beyond) != 0, 0)) {
+                if (sl.beyond) {
+                    const uint32_t cum = (uint32_t)x & (kTotal - 1);
+                    uint32_t slot = sl.slot;
+                    uint32_t nxt = tab.template load<uint16_t>(mr.base + 2 * (slot + 1));
+                    for (uint32_t i = 0; i <= mv + 1 && cum > nxt; ++i) {
                         ++slot;
                         nxt = tab.template load<uint16_t>(mr.base + 2 * (slot + 1));
                     }
-                    sm1 = tab.template load<uint16_t>(mr.base + 2 * slot);
+                    const uint32_t sm1 = tab.template load<uint16_t>(mr.base + 2 * slot);
+                    sl.slot = slot;
+                    sl.xn = (uint64_t)((nxt - sm1) & 0xFFFFu) * (x >> kPrecision) +
+                            ((cum - sm1 - 1) & 0xFFFFu);
                 }
             }
-            const uint32_t f = (nxt - sm1) & 0xFFFFu;
-            const uint32_t rr = (cum - sm1 - 1) & 0xFFFFu;   // cum - start
+            const uint32_t slot = sl.slot;
             // a select, not a branch: the step stays one basic block
-            x = valid ? (uint64_t)f * (x >> kPrecision) + rr : x;
+            x = valid ? sl.xn : x;
             refill(valid & (x < kStateLow));
             // Slots below the row's fast bound are ordinary symbols whose
             // value offset + slot fits int32 (the bound is 0 for a row
@@ -547,16 +552,26 @@ __device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab
             for (int u = 0; u < kIlAhead; ++u)
                 mt[u] = tab.meta(min((uint32_t)r[u], K - 1));
         };
+        // does some step of these eight hold an index outside [0, K)?
+        auto any_bad = [&](const int32_t (&r)[kIlAhead]) {
+            uint32_t imax = (uint32_t)r[0];
+#pragma unroll
+            for (int u = 1; u < kIlAhead; ++u)
+                imax = max(imax, (uint32_t)r[u]);
+            return __ballot(imax >= K) != 0;
+        };
         auto group = [&](auto full, uint32_t g0) {
             metas(ia);
+            const bool chka = any_bad(ia);
 #pragma unroll
             for (int u = 0; u < kIlAhead; ++u)
-                step(full, ia[u], mt[u], g0 + u);
+                step(full, chka, ia[u], mt[u], g0 + u);
             load(ia, g0 + 2 * kIlAhead);
             metas(ib);
+            const bool chkb = any_bad(ib);
 #pragma unroll
             for (int u = 0; u < kIlAhead; ++u)
-                step(full, ib[u], mt[u], g0 + kIlAhead + u);
+                step(full, chkb, ib[u], mt[u], g0 + kIlAhead + u);
             load(ib, g0 + 3 * kIlAhead);
         };
         // the groups wholly inside the stream, then the rest (at most one

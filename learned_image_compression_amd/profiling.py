@@ -51,7 +51,8 @@ def kernel_source_hash(name: str) -> str:
     """Hash of the sources that make up one coding kernel (rans_<name>.hip and
     the shared headers): counter summaries recorded for other sources are stale."""
     h = hashlib.sha256()
-    extra = ("rans_frontend.hpp",) if name == "interleaved" else ()
+    extra = {"interleaved": ("rans_frontend.hpp", "rans_lookup.hpp"),
+             "decode": ("rans_lookup.hpp",)}.get(name, ())
     for f in ("rans_internal.hpp", "rans_coding.hpp", *extra, f"rans_{name}.hip"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
