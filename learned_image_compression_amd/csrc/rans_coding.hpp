@@ -32,7 +32,11 @@ __device__ inline double reciprocal(uint32_t f)
 // out), and s is added sign-extended.
 __device__ inline uint64_t reg_step(uint64_t x, uint32_t start, uint32_t f, double rcp)
 {
-    const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+    // (the halves taken as a two-word vector: written as x >> 32, the high
+    // half's conversion becomes a 64-bit one with an extra fp64 add)
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+    const u32x2 h = __builtin_bit_cast(u32x2, x);
+    const uint32_t lo = h.x, hi = h.y;
     const double xd = __builtin_fma((double)hi, 4294967296.0, (double)lo);
     const double t = __builtin_fma(xd, rcp, 4503599627370496.0);   // 2^52
     const uint64_t tb = (uint64_t)__double_as_longlong(t);

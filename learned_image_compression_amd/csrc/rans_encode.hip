@@ -85,6 +85,33 @@ struct Spill {
         *slot(min((cb - cb0) >> 2, kEncRing - 1)) = w;
         cb += spill ? 4u : 0u;
     }
+
+    // Store the round's words (ring slots 0 .. n-1) to positions
+    // cb0/4 .. cb0/4 + n - 1, i.e. descending byte offsets from
+    // top - 4 - cb0.  Slots 0..7 are always stored, as two 16-byte stores
+    // (slots past n hold stale words for positions that later words or the
+    // final state overwrite); a round of more than 8 words, or a lane near
+    // the end of its segment, stores word by word.
+    __device__ inline void store_round()
+    {
+        const uint32_t n = (cb - cb0) >> 2;
+        uint32_t r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r[i] = *slot(i);
+        const bool whole = cb0 + 32 <= capb;
+        // (a round that spilled nothing sends both stores past the buffer,
+        // where they are dropped: no write traffic for it)
+        const uint32_t off = (whole & (n > 0)) ? top - cb0 - 32 : kNoStore;
+        buf_store4(scr, off, u32x4{r[7], r[6], r[5], r[4]});
+        buf_store4(scr, off + 16, u32x4{r[3], r[2], r[1], r[0]});
+        if (__builtin_expect(__ballot(!whole | (n > 8)) != 0, 0)) {
+            for (uint32_t i = whole ? 8u : 0u; i < n; ++i)
+                if (cb0 + 4 * i + 8 < capb)
+                    buf_store(scr, top - 4 - cb0 - 4 * i, 0, (int32_t)*slot(i));
+        }
+        cb0 = cb;
+    }
 };
 
 // The puts of one symbol that come before its REG put (applied last to
@@ -220,32 +247,7 @@ __device__ __forceinline__ LaneResult encode_lane(const EncodeArgs &a, const Tab
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    // The round's words (ring slots 0 .. n-1) go to positions
-    // cb0/4 .. cb0/4 + n - 1, i.e. descending byte offsets from
-    // top - 4 - cb0.  Slots 0..7 are always stored, as two 16-byte
-    // stores (slots past n hold stale words for positions that later
-    // words or the final state overwrite); a round of more than 8
-    // words, or a lane near the end of its segment, stores word by
-    // word.
-    auto store_words = [&]() {
-        const uint32_t n = (sp.cb - sp.cb0) >> 2;
-        uint32_t r[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            r[i] = *sp.slot(i);
-        const bool whole = sp.cb0 + 32 <= sp.capb;
-        // (a round that spilled nothing sends both stores past the buffer,
-        // where they are dropped: no write traffic for it)
-        const uint32_t off = (whole & (n > 0)) ? sp.top - sp.cb0 - 32 : kNoStore;
-        buf_store4(sp.scr, off, u32x4{r[7], r[6], r[5], r[4]});
-        buf_store4(sp.scr, off + 16, u32x4{r[3], r[2], r[1], r[0]});
-        if (__builtin_expect(__ballot(!whole | (n > 8)) != 0, 0)) {
-            for (uint32_t i = whole ? 8u : 0u; i < n; ++i)
-                if (sp.cb0 + 4 * i + 8 < sp.capb)
-                    buf_store(sp.scr, sp.top - 4 - sp.cb0 - 4 * i, 0, (int32_t)*sp.slot(i));
-        }
-        sp.cb0 = sp.cb;
-    };
+    auto store_words = [&]() { sp.store_round(); };
     // State-independent values of one round (positions k0 .. k0+7,
     // last to first): the slot's (start, f), the reciprocal of f,
     // whether the position holds an ordinary symbol of a valid row,
@@ -607,6 +609,221 @@ __device__ inline uint32_t wave_inclusive_scan(uint32_t v, uint32_t lane)
     return v;
 }
 
+// Block start of both encode kernels: check the prepared workspace, stage the
+// encoder table set into LDS (when it fits), and refuse a set with an invalid
+// row.  `misc[0]` is a zeroed LDS word for the block OR.  Returns the call's
+// error (the same in every lane; scalar, it keeps the buffer descriptors and
+// loops after it uniform for the compiler).
+template <int TPB>
+__device__ __forceinline__ int encode_block_start(const EncodeArgs &a, WsHeader *hdr,
+                                                  const uint8_t *tab, uint8_t *lds, uint32_t *misc,
+                                                  bool &in_lds)
+{
+    const uint32_t tid = threadIdx.x;
+    int herr = 0;
+    if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables ||
+        hdr->cdf_stride != (uint32_t)a.stride)
+        herr = RANS_E_ARG;
+    else if (lds_address_of(lds) != 0)   // table offsets are used as LDS addresses
+        herr = RANS_E_HIP;
+    const uint32_t K = (uint32_t)a.num_tables;
+    in_lds = hdr->enc_lds != 0;
+    stage_tables<TPB>(lds, tab, (!herr && in_lds) ? hdr->enc_bytes : 0u);
+    __syncthreads();
+    int bad = 0;
+    if (!herr) {
+        const GlobalTab gt{tab};
+        for (uint32_t r = tid; r < K; r += TPB)
+            bad |= ((in_lds ? lds_meta(r) : gt.meta(r)).lut & kRowInvalid) ? 1 : 0;
+    }
+    __syncthreads();
+    bad = block_or(&misc[0], bad);
+    if (!herr && bad)
+        herr = RANS_E_TABLE;
+    if (herr && blockIdx.x == 0 && tid == 0)
+        record_error(hdr, herr);
+    return __builtin_amdgcn_readfirstlane(herr);
+}
+
+// After coding, coding wave t (lanes j0 + lane, `active` ones) publishes its
+// word total, finds its offset by a look-back over earlier waves, writes its
+// lanes' header entries and copies their words into the container.
+template <int S>
+__device__ __forceinline__ void publish_and_copy(const EncodeArgs &a, WsHeader *hdr,
+                                                 uint64_t *flags, uint32_t t, uint32_t nwork,
+                                                 uint32_t lane, uint32_t j, bool active,
+                                                 const Spill<S> &sp, uint32_t words, int lerr)
+{
+    const uint32_t L = a.lanes;
+    if (lerr)
+        record_error(hdr, lerr);
+
+    // ---- wave scan and look-back over earlier waves -----------------------
+    // Every wave publishes its aggregate, then reads the flags of the 256
+    // waves before it at once (four per wavefront lane): the nearest
+    // inclusive flag ends the walk once every flag after it is
+    // published, and the values up to it are summed across the wave.
+    // (Inclusive flags spread one window per round trip when many
+    // waves finish together, so the window is made wide.)
+    // A flag carries all it says in its own 64 bits, so the flags are
+    // relaxed device-scope atomics: no cache writeback or invalidation
+    // per publication or poll (spinning waves would otherwise keep
+    // flushing the L2 that the working waves read from).  Its look-back
+    // waits only for waves of lower-numbered blocks.  Workgroups are
+    // dispatched in index order, so those have all started and none of them
+    // waits on this one (a per-wave ticket counter would guarantee the same
+    // without relying on dispatch order, but its one contended atomic cost
+    // about 10 us).
+    const uint32_t incl = wave_inclusive_scan(words, lane);
+    const uint64_t agg = __shfl(incl, kWave - 1, kWave);
+    uint64_t prefix = 0;
+    if (lane == 0)
+        __hip_atomic_store(&flags[t], (t == 0 ? kFlagInclusive : kFlagAggregate) | agg,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t > 0) {
+        constexpr int kLook = 4;   // flags per lane per round trip
+        constexpr uint32_t kWindow = kLook * kWave;
+        int32_t k = (int32_t)t;   // this window covers waves k-1 .. k-kWindow
+        uint32_t spins = 0;
+        while (true) {
+            // flag at distance d = 64 i + lane behind k
+            uint64_t fv[kLook];
+#pragma unroll
+            for (int i = 0; i < kLook; ++i) {
+                const int32_t p = k - 1 - (int32_t)(kWave * i + lane);
+                fv[i] = p >= 0 ? __hip_atomic_load(&flags[p], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : kFlagInclusive;
+            }
+            // the nearest inclusive flag (kWindow: none in this window)
+            uint32_t dstar = kWindow;
+#pragma unroll
+            for (int i = kLook - 1; i >= 0; --i) {
+                const uint64_t im = __ballot((fv[i] >> 62) == 2);
+                if (im)
+                    dstar = kWave * i + (uint32_t)__builtin_ctzll(im);
+            }
+            // every flag up to it must be published
+            bool ready = true;
+#pragma unroll
+            for (int i = 0; i < kLook; ++i) {
+                const uint64_t rm = __ballot((fv[i] >> 62) != 0);
+                const uint32_t lo = kWave * i;
+                const uint64_t need = dstar < lo ? 0ull
+                                      : dstar >= lo + kWave - 1 ? ~0ull
+                                                                : (2ull << (dstar - lo)) - 1;
+                ready = ready & ((rm & need) == need);
+            }
+            if (!ready) {
+                if (++spins > kSpinLimit) {   // never expected: bail out, flag it
+                    if (lane == 0)
+                        record_error(hdr, RANS_E_HIP);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                continue;
+            }
+            uint64_t v = 0;
+#pragma unroll
+            for (int i = 0; i < kLook; ++i)
+                v += (kWave * i + lane <= dstar) ? (fv[i] & kFlagValueMask) : 0;
+            for (int off = 1; off < kWave; off <<= 1)
+                v += __shfl_xor(v, off, kWave);
+            prefix += v;
+            if (dstar < kWindow)
+                break;
+            k -= (int32_t)kWindow;
+        }
+        if (lane == 0)
+            __hip_atomic_store(&flags[t], kFlagInclusive | (prefix + agg), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (lane == 0 && t == nwork - 1) {
+        a.stream[0] = L;
+        __hip_atomic_store(&hdr->total_words, prefix + agg, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---- header entry and compaction --------------------------------------
+    // The wave's lanes fill container words [1 + L + prefix, + agg); the
+    // output buffer ends at the capacity, so nothing is written past it.
+    // Each lane reads back only the scratch words it stored itself,
+    // sixty-four per round trip (all loads issued before any store),
+    // and stores whole 16-byte groups of its own words, then its last
+    // one to three words one by one.  Accesses are masked per lane
+    // (a lane without words for a group sends no request).
+    const uint64_t wbase =
+        1ull + L + (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)prefix) +
+        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(prefix >> 32)) << 32);
+    const uint64_t wroom = a.capacity > wbase ? a.capacity - wbase : 0;
+    const Rsrc rout = make_rsrc(a.stream + (wroom ? wbase : 0),
+                                (uint32_t)min(4 * wroom, 1ull << 31));
+    if (active) {
+        const uint64_t end = prefix + incl;
+        a.stream[1 + j] = (uint32_t)end;
+        const uint32_t ob = 4 * (incl - words);   // the lane's first word in rout
+        const uint32_t src = sp.top - 4 * words;
+        const uint32_t kt = words & ~3u;   // first word of the last, partial group
+        for (uint32_t k0 = 0; k0 < words; k0 += 64) {
+            u32x4 v[16];
+            uint32_t tw[3];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (k0 + 4 * i + 4 <= words)
+                    v[i] = buf_load4(sp.scr, src + 4 * k0 + 16 * i);
+            const bool tail = kt >= k0 && kt < k0 + 64;
+#pragma unroll
+            for (int e = 0; e < 3; ++e)
+                if (tail && kt + e < words)
+                    tw[e] = (uint32_t)buf_load(sp.scr, src + 4 * (kt + e), 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (k0 + 4 * i + 4 <= words)
+                    buf_store4(rout, ob + 4 * (k0 + 4 * i), v[i]);
+#pragma unroll
+            for (int e = 0; e < 3; ++e)
+                if (tail && kt + e < words)
+                    buf_store(rout, ob + 4 * (kt + e), 0, (int32_t)tw[e]);
+        }
+    }
+}
+
+// Block end of both encode kernels: the last block to finish publishes the
+// status and the container length, and clears the bookkeeping (look-back
+// flags, error, totals) for the next call.  `misc[1]` is an LDS word.
+template <int TPB>
+__device__ __forceinline__ void encode_block_end(const EncodeArgs &a, WsHeader *hdr,
+                                                 uint64_t *flags, int herr, uint32_t nwork,
+                                                 uint32_t *misc)
+{
+    const uint32_t tid = threadIdx.x;
+    __syncthreads();
+    if (tid == 0) {
+        __threadfence();
+        const uint32_t old = atomicAdd(&hdr->done, 1u);
+        misc[1] = (old == gridDim.x - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (misc[1]) {
+        __threadfence();
+        if (!herr)
+            for (uint32_t k = tid; k < nwork; k += TPB)
+                flags[k] = 0;
+        if (tid == 0) {
+            const uint64_t total = 1ull + a.lanes + hdr->total_words;
+            int err = hdr->err;
+            if (!err && total > a.capacity)
+                err = RANS_E_CAPACITY;
+            *a.status = err;
+            *a.stream_words = herr ? 0ull : total;
+            hdr->err = 0;
+            hdr->total_words = 0;
+            hdr->done = 0;
+            __threadfence();
+        }
+    }
+}
+
 template <int TPB, int CW, bool PAIR>
 __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
 {
@@ -622,43 +839,14 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
     const uint32_t L = a.lanes;
     const uint32_t lpw = enc_lanes_per_wave(L);
     const uint32_t nwork = enc_waves(L);
-
-    // ---- tables -> LDS -------------------------------------------------------
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // coding waves 0 .. CW-1
-    int herr = 0;
-    if (hdr->magic != kMagic || hdr->num_tables != (uint32_t)a.num_tables ||
-        hdr->cdf_stride != (uint32_t)a.stride)
-        herr = RANS_E_ARG;
-    else if (lds_address_of(lds) != 0)   // table offsets are used as LDS addresses
-        herr = RANS_E_HIP;
     const uint32_t K = (uint32_t)a.num_tables;
-    const bool in_lds = hdr->enc_lds != 0;
-    stage_tables<TPB>(lds, tab, (!herr && in_lds) ? hdr->enc_bytes : 0u);
-    __syncthreads();
-    int bad = 0;
-    if (!herr) {
-        const GlobalTab gt{tab};
-        for (uint32_t r = tid; r < K; r += TPB)
-            bad |= ((in_lds ? lds_meta(r) : gt.meta(r)).lut & kRowInvalid) ? 1 : 0;
-    }
+
     if (tid == 0)
         misc[0] = 0u;
-    __syncthreads();
-    bad = block_or(&misc[0], bad);
-    if (!herr && bad)
-        herr = RANS_E_TABLE;
-    if (herr && blockIdx.x == 0 && tid == 0)
-        record_error(hdr, herr);
-
-    // herr is the same in every lane; scalar, it keeps the buffer
-    // descriptors and loops below uniform for the compiler
-    herr = __builtin_amdgcn_readfirstlane(herr);
+    bool in_lds;
+    const int herr = encode_block_start<TPB>(a, hdr, tab, lds, misc, in_lds);
     if (!herr && wave < CW) {
-        // Wave t codes lanes t*lpw ..; its look-back waits only for waves of
-        // lower-numbered blocks.  Workgroups are dispatched in index order, so
-        // those have all started and none of them waits on this one (a
-        // per-wave ticket counter would guarantee the same without relying
-        // on dispatch order, but its one contended atomic cost about 10 us).
         const uint32_t t = blockIdx.x * CW + wave;
         if (t < nwork) {
             // the wave codes lanes j0 .. j0 + lpw - 1, one per wavefront lane
@@ -666,7 +854,6 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
             const uint32_t j = j0 + lane;
             const bool active = lane < lpw && j < L;
             const WaveBufs<TPB> wb = wave_bufs<TPB>(a, L, j0, j1, j);
-            const Spill<TPB> &sp = wb.sp;
             uint32_t words = 0;
             int lerr = 0;
             if (active) {
@@ -678,161 +865,377 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
                 words = lr.words;
                 lerr = lr.err;
             }
-            if (lerr)
-                record_error(hdr, lerr);
+            publish_and_copy(a, hdr, flags, t, nwork, lane, j, active, wb.sp, words, lerr);
+        }
+    }
+    encode_block_end<TPB>(a, hdr, flags, herr, nwork, misc);
+}
 
-            // ---- wave scan and look-back over earlier waves -----------------------
-            // Every wave publishes its aggregate, then reads the flags of the 256
-            // waves before it at once (four per wavefront lane): the nearest
-            // inclusive flag ends the walk once every flag after it is
-            // published, and the values up to it are summed across the wave.
-            // (Inclusive flags spread one window per round trip when many
-            // waves finish together, so the window is made wide.)
-            // A flag carries all it says in its own 64 bits, so the flags are
-            // relaxed device-scope atomics: no cache writeback or invalidation
-            // per publication or poll (spinning waves would otherwise keep
-            // flushing the L2 that the working waves read from).
-            const uint32_t incl = wave_inclusive_scan(words, lane);
-            const uint64_t agg = __shfl(incl, kWave - 1, kWave);
-            uint64_t prefix = 0;
-            if (lane == 0)
-                __hip_atomic_store(&flags[t], (t == 0 ? kFlagInclusive : kFlagAggregate) | agg,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (t > 0) {
-                constexpr int kLook = 4;   // flags per lane per round trip
-                constexpr uint32_t kWindow = kLook * kWave;
-                int32_t k = (int32_t)t;   // this window covers waves k-1 .. k-kWindow
-                uint32_t spins = 0;
-                while (true) {
-                    // flag at distance d = 64 i + lane behind k
-                    uint64_t fv[kLook];
+// ---- one coding wave per CU --------------------------------------------------
+//
+// With at most 4096 lanes every CU holds a single coding wave of at most 16
+// lanes, and the kernel takes as long as that wave's dependent chains.  The
+// state-independent work of a position -- loading its symbol and index, the
+// row metadata, the slot's (start, f), the reciprocal of f -- would run on the
+// same wave at 16 of 64 threads.  Here the block's three other waves, on the
+// CU's other SIMDs, do it for the coding wave: for every step of a chunk of
+// 48 steps and every lane, they write one 16-byte entry to LDS,
+//   an ordinary symbol of a valid row:  (1/f as fp64, f, start);
+//   a step that is no position (padding, past the lane's end): the identity
+//     step (2^-16, 2^16, 0), which leaves the state unchanged and never
+//     renormalises;
+//   anything else (an escape, a bad index):  (symbol, index, 0, 0);
+// and set one bit per round of the chunk that holds an entry of the last
+// kind.  Two entry buffers alternate: one barrier per chunk hands a filled
+// buffer to the coding wave and the one it has finished back to the
+// producers.  The coding wave reads a round's entries during the round
+// before, runs the state chain (the fast form where the round's bit is
+// clear), and stores its spilled words; the puts, their order and the
+// container are those of encode_lane.
+constexpr uint32_t kPcLanes = 16;                           // lanes of a coding wave, at most
+constexpr uint32_t kPcChunkRounds = 6;
+constexpr uint32_t kPcChunk = kPcChunkRounds * kRound;      // steps per chunk
+constexpr int kPcThreads = 4 * kWave;
+constexpr uint32_t kPcRing = kEncTableBudget;               // the coding wave's word rings
+constexpr uint32_t kPcEntries = kPcRing + kEncRing * 4 * kWave;
+constexpr uint32_t kPcEntryBuf = kPcChunk * kPcLanes * 16;
+constexpr uint32_t kPcMisc = kPcEntries + 2 * kPcEntryBuf;  // [0] flag OR, [1] last block,
+                                                            // [2 + b] round bits of buffer b
+constexpr uint32_t kPcLdsBytes = kPcMisc + 16;
+static_assert(kPcLdsBytes <= kLdsBytes, "encoder LDS over budget");
+static_assert(kPcEntries % 16 == 0, "entries are 16-byte LDS accesses");
+static_assert(lanes_per_wave_for(4096, kCodingCUs) <= kPcLanes, "coding wave too wide");
+static_assert((kPcChunk / 4) * kPcLanes == kPcThreads - kWave, "one quad of steps per producer");
+static_assert(kPcChunkRounds % 2 == 0, "rounds run in pairs");
+
+__device__ inline uint32_t pc_entry(uint32_t buf, uint32_t step, uint32_t l)
+{
+    return kPcEntries + buf * kPcEntryBuf + (step * kPcLanes + l) * 16;
+}
+__device__ inline double entry_rcp(const u32x4 &e)
+{
+    return __builtin_bit_cast(double, (uint64_t)e[0] | ((uint64_t)e[1] << 32));
+}
+
+// Where lane j's steps lie: step k codes position b + R8 - 1 - k, R8 = the
+// lane's length rounded up to whole rounds; steps below pad = R8 - nj and
+// from R8 on are no positions.  pbase: byte offset of position b in the
+// wave's buffers.
+struct LaneSteps {
+    uint64_t b, e;
+    uint32_t nj, R8, pad, pbase;
+};
+__device__ inline LaneSteps lane_steps(uint64_t n, uint32_t L, uint32_t j, uint64_t bw)
+{
+    LaneSteps s;
+    s.b = lane_begin(n, L, j);
+    s.e = lane_begin(n, L, j + 1);
+    s.nj = (uint32_t)(s.e - s.b);
+    s.R8 = (s.nj + kRound - 1) / kRound * kRound;
+    s.pad = s.R8 - s.nj;
+    s.pbase = (uint32_t)(4 * (s.b - bw));
+    return s;
+}
+
+// Producer: the entries of steps k4 .. k4+3 of one lane into buffer `buf` of
+// chunk step 4 q (positions c .. c+3 below, read as one 16-byte load per
+// array; a quad past the lane reads other lanes' values or zeros, only for
+// steps that are no positions).
+__device__ __forceinline__ void pc_produce(const LaneSteps &ls, Rsrc rsym, Rsrc ridx, uint32_t K,
+                                           uint32_t chunk, uint32_t q, uint32_t l,
+                                           uint32_t *round_bits)
+{
+    const uint32_t buf = chunk & 1u;
+    const uint32_t k4 = chunk * kPcChunk + 4 * q;
+    const uint32_t off = ls.pbase + 4 * (ls.R8 - 4 - k4);   // (wraps past the buffer: reads 0)
+    const u32x4 sv = buf_load4(rsym, off), iv = buf_load4(ridx, off);
+    bool any_off = false;
 #pragma unroll
-                    for (int i = 0; i < kLook; ++i) {
-                        const int32_t p = k - 1 - (int32_t)(kWave * i + lane);
-                        fv[i] = p >= 0 ? __hip_atomic_load(&flags[p], __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT)
-                                       : kFlagInclusive;
-                    }
-                    // the nearest inclusive flag (kWindow: none in this window)
-                    uint32_t dstar = kWindow;
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t k = k4 + u;
+        const int32_t sym = (int32_t)sv[3 - u];
+        const uint32_t idx = iv[3 - u];
+        const RowMeta m = lds_meta(min(idx, K - 1));
+        const uint32_t mv = m.mvf & 0xFFFFu;
+        // s - offset wraps mod 2^32 into [0, mv) only on rows whose fast
+        // bound is 0
+        const uint32_t w = (uint32_t)sym - (uint32_t)m.offset;
+        const bool fast = (w < (m.mvf >> 16)) & (idx < K);
+        const uint32_t pr = lds_load<uint32_t>(m.base + 4 * min(w, mv));
+        const uint32_t f = pr >> 16;
+        const double r = reciprocal(f);
+        const uint64_t rb = __builtin_bit_cast(uint64_t, r);
+        const bool valid = k >= ls.pad && k < ls.R8;
+        u32x4 ent;
+        if (!valid)
+            ent = u32x4{0u, 0x3EF00000u, kTotal, 0u};   // 2^-16, 2^16, 0
+        else if (fast)
+            ent = u32x4{(uint32_t)rb, (uint32_t)(rb >> 32), f, pr & 0xFFFFu};
+        else
+            ent = u32x4{(uint32_t)sym, idx, 0u, 0u};
+        any_off = any_off | (valid & !fast);
+        lds_store<u32x4>(pc_entry(buf, 4 * q + u, l), ent);
+    }
+    if (any_off)
+        __hip_atomic_fetch_or(&round_bits[buf], 1u << (q / 2), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kPcMisc);
+    uint32_t *round_bits = misc + 2;
+
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
+    const uint8_t *tab = a.ws + ws_enc_offset(a.num_tables, a.stride);
+    uint64_t *flags = reinterpret_cast<uint64_t *>(a.ws + ws_flags_offset());
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & (kWave - 1);
+    const uint32_t L = a.lanes;
+    const uint32_t lpw = enc_lanes_per_wave(L);
+    const uint32_t nwork = enc_waves(L);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // 0 codes, 1..3 produce
+    const uint32_t K = (uint32_t)a.num_tables;
+
+    if (tid < 4)
+        misc[tid] = 0u;
+    bool in_lds;
+    const int herr = encode_block_start<kPcThreads>(a, hdr, tab, lds, misc, in_lds);
+    const uint32_t t = blockIdx.x;
+    if (!herr && t < nwork) {
+        const uint32_t j0 = t * lpw, j1 = min(j0 + lpw, L);
+        // rounds of the longest lane (a lane holds floor or ceil of n / L
+        // positions), in chunks
+        const uint32_t nr = (uint32_t)(((a.n + L - 1) / L + kRound - 1) / kRound);
+        if (wave == 0) {
+            const uint32_t j = j0 + lane;
+            const bool active = lane < lpw && j < L;
+            const WaveBufs<kWave> wb = wave_bufs<kWave>(a, L, j0, j1, j);
+            Spill<kWave> sp = wb.sp;
+            uint32_t words = 0;
+            int lerr = 0;
+            if (!in_lds) {
+                if (active) {
+                    const LaneResult lr = encode_lane_simple<kWave>(a, GlobalTab{tab}, K, L, j,
+                                                                    wb.bw, wb.rsym, wb.ridx, sp);
+                    words = lr.words;
+                    lerr = lr.err;
+                }
+            } else {
+                const LaneSteps ls = lane_steps(a.n, L, j, wb.bw);
+                const LdsTab tb{};
+                uint64_t x = kStateLow;
+                sp.cb = 0;
+                sp.cb0 = 0;
+                sp.capb = 4 * (2 * ls.nj + 4);
+                sp.overflow = false;
+                // split records, as in encode_lane
+                const uint32_t npieces = 1u << a.pieces_log2;
+                int32_t cut_s = (int32_t)npieces - 1;
+                auto cut_step = [&](int32_t s) -> uint32_t {
+                    return ls.R8 - 1 - (uint32_t)(piece_begin(ls.b, ls.e, a.pieces_log2, (uint32_t)s) - ls.b);
+                };
+                uint32_t cut_k = (npieces > 1 && ls.nj > 0) ? cut_step(cut_s) : ~0u;
+                auto record_cut = [&]() {
+                    uint32_t *m = a.split_meta + 3ull * ((uint64_t)(npieces - 1) * j + cut_s - 1);
+                    m[0] = (uint32_t)x;
+                    m[1] = (uint32_t)(x >> 32);
+                    m[2] = sp.cb >> 2;
+                    --cut_s;
+                    cut_k = (cut_s >= 1 && ls.nj > 0) ? cut_step(cut_s) : ~0u;
+                };
+                const uint32_t ring_lds = kPcRing + 4 * lane;   // LDS address of ring slot 0
+                // One round (steps k0 .. k0+7) from its entries.
+                auto round = [&](const u32x4 (&E)[kRound], bool checked, uint32_t k0) {
+                    // room for three words per position: the fast steps need no check
+                    const bool room = sp.cb + 4 * (2 + 3 * kRound) < sp.capb;
+                    const uint64_t x0 = x;
+                    const uint32_t cb_start = sp.cb;
+                    if (!checked) {
+                        // the round starts at ring slot 0 (its words were
+                        // stored); the slot address advances a slot per word
+                        const uint32_t ra0 = ring_lds;
+                        uint32_t ra = ra0;
 #pragma unroll
-                    for (int i = kLook - 1; i >= 0; --i) {
-                        const uint64_t im = __ballot((fv[i] >> 62) == 2);
-                        if (im)
-                            dstar = kWave * i + (uint32_t)__builtin_ctzll(im);
-                    }
-                    // every flag up to it must be published
-                    bool ready = true;
-#pragma unroll
-                    for (int i = 0; i < kLook; ++i) {
-                        const uint64_t rm = __ballot((fv[i] >> 62) != 0);
-                        const uint32_t lo = kWave * i;
-                        const uint64_t need = dstar < lo ? 0ull
-                                              : dstar >= lo + kWave - 1 ? ~0ull
-                                                                        : (2ull << (dstar - lo)) - 1;
-                        ready = ready & ((rm & need) == need);
-                    }
-                    if (!ready) {
-                        if (++spins > kSpinLimit) {   // never expected: bail out, flag it
-                            if (lane == 0)
-                                record_error(hdr, RANS_E_HIP);
-                            break;
+                        for (int u = 0; u < kRound; ++u) {
+                            const uint32_t f = E[u][2];
+                            const bool need = (uint32_t)(x >> 32) >= (f << (31 - kPrecision));
+                            lds_store<uint32_t>(ra, (uint32_t)x);
+                            ra += need ? 4u * kWave : 0u;
+                            x = need ? (x >> 32) : x;
+                            x = reg_step(x, E[u][3], f, entry_rcp(E[u]));
                         }
-                        __builtin_amdgcn_s_sleep(1);
-                        continue;
+                        sp.cb += (ra - ra0) / kWave;
+                    } else {
+                        // as in encode_lane: an escape's groups and count, then
+                        // the escape slot's REG put; a bad index takes the
+                        // identity step
+#pragma unroll
+                        for (int u = 0; u < kRound; ++u) {
+                            uint32_t st = E[u][3], fu = E[u][2];
+                            double ru = entry_rcp(E[u]);
+                            const bool off = fu == 0u;
+                            if (__ballot(off) != 0) {
+                                if (off) {
+                                    const int32_t sym = (int32_t)E[u][0];
+                                    const uint32_t idx = E[u][1];
+                                    st = 0u;
+                                    fu = kTotal;
+                                    ru = 1.0 / kTotal;
+                                    if (idx < K) {
+                                        uint32_t pr;
+                                        const int ec = encode_prefix<kWave>(sym, tb.meta(idx), tb,
+                                                                            x, sp, pr);
+                                        lerr = lerr ? lerr : ec;
+                                        st = pr & 0xFFFFu;
+                                        fu = pr >> 16;
+                                        ru = reciprocal(fu);
+                                    } else {
+                                        lerr = lerr ? lerr : RANS_E_INDEX;
+                                    }
+                                }
+                            }
+                            const bool need = (uint32_t)(x >> 32) >= (fu << (31 - kPrecision));
+                            *sp.slot(min((sp.cb - sp.cb0) >> 2, kEncRing - 1)) = (uint32_t)x;
+                            sp.cb += need ? 4u : 0u;
+                            x = need ? (x >> 32) : x;
+                            x = reg_step(x, st, fu, ru);
+                        }
                     }
-                    uint64_t v = 0;
+                    // A lane near the end of its segment, or a round holding a
+                    // split cut, redoes the round from its start with checked
+                    // puts where needed.
+                    if (__builtin_expect(!__all(room & (cut_k >= k0 + kRound)), 0)) {
+                        x = x0;
+                        sp.cb = cb_start;
 #pragma unroll
-                    for (int i = 0; i < kLook; ++i)
-                        v += (kWave * i + lane <= dstar) ? (fv[i] & kFlagValueMask) : 0;
-                    for (int off = 1; off < kWave; off <<= 1)
-                        v += __shfl_xor(v, off, kWave);
-                    prefix += v;
-                    if (dstar < kWindow)
-                        break;
-                    k -= (int32_t)kWindow;
+                        for (int u = 0; u < kRound; ++u) {
+                            const uint32_t f = E[u][2];
+                            const bool off = f == 0u;
+                            const bool fast = !off & room;
+                            const bool need = (uint32_t)(x >> 32) >= (f << (31 - kPrecision));
+                            const uint64_t xn =
+                                reg_step(need ? (x >> 32) : x, E[u][3], f, entry_rcp(E[u]));
+                            *sp.slot(min((sp.cb - sp.cb0) >> 2, kEncRing - 1)) = (uint32_t)x;
+                            sp.cb += (fast & need) ? 4u : 0u;
+                            x = fast ? xn : x;
+                            if (__builtin_expect(__ballot(!fast) != 0, 0)) {
+                                if (!fast) {
+                                    if (off) {
+                                        int ec = RANS_E_INDEX;
+                                        if (E[u][1] < K)
+                                            ec = encode_slow<kWave>((int32_t)E[u][0],
+                                                                    tb.meta(E[u][1]), tb, x, sp);
+                                        lerr = lerr ? lerr : ec;
+                                    } else {
+                                        // the REG put of an ordinary symbol (or the
+                                        // identity), with its spill checked
+                                        const bool spill =
+                                            x >= ((uint64_t)f << (63 - kPrecision));
+                                        sp.put_if(spill, (uint32_t)x);
+                                        x = spill ? (x >> 32) : x;
+                                        x = reg_step(x, E[u][3], f, entry_rcp(E[u]));
+                                    }
+                                }
+                            }
+                            while (cut_k == k0 + u)   // (cuts may share a position)
+                                record_cut();
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    sp.store_round();
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                // Entries of round g, read for every wavefront lane (lanes
+                // past the wave's read another lane's, unused).
+                const uint32_t el = lane & (kPcLanes - 1);
+                auto load_round = [&](u32x4 (&E)[kRound], uint32_t g) {
+                    const uint32_t buf = (g / kPcChunkRounds) & 1u;
+                    const uint32_t s0 = (g % kPcChunkRounds) * kRound;
+#pragma unroll
+                    for (int u = 0; u < kRound; ++u)
+                        E[u] = lds_load<u32x4>(pc_entry(buf, s0 + u, el));
+                };
+                // round bits of the chunk of round g (scalar), cleared for
+                // the producers' next use of the buffer
+                auto take_bits = [&](uint32_t g) -> uint32_t {
+                    const uint32_t buf = (g / kPcChunkRounds) & 1u;
+                    const uint32_t v = __builtin_amdgcn_readfirstlane(round_bits[buf]);
+                    if (lane == 0)
+                        round_bits[buf] = 0u;
+                    return v;
+                };
+                // Round g: at the last round of a chunk, the barrier that
+                // hands over the next chunk comes first (this round's entries
+                // are already in registers); then the next round's entries
+                // are requested and this round runs.  Rounds go in pairs (a
+                // chunk holds an even number; an odd count gets one more
+                // round, of identity entries only), and every round requests
+                // the next one's entries (past the last: unused reads), so
+                // that the two entry arrays never merge at a branch.
+                const uint32_t nr2 = (nr + 1) & ~1u;
+                u32x4 E0[kRound], E1[kRound];
+                uint32_t bits = 0, bits_next = 0;
+                auto step = [&](const u32x4 (&E)[kRound], u32x4 (&En)[kRound], uint32_t g) {
+                    const uint32_t r = g % kPcChunkRounds;
+                    const bool handover = r == kPcChunkRounds - 1 && g + 1 < nr2;
+                    if (handover) {
+                        __syncthreads();
+                        bits_next = take_bits(g + 1);
+                    }
+                    load_round(En, g + 1);
+                    if (active)
+                        round(E, (bits >> r) & 1u, g * kRound);
+                    if (handover)
+                        bits = bits_next;
+                };
+                if (nr2 > 0) {
+                    __syncthreads();   // chunk 0 is ready
+                    bits = take_bits(0);
+                    load_round(E0, 0);
                 }
-                if (lane == 0)
-                    __hip_atomic_store(&flags[t], kFlagInclusive | (prefix + agg), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            }
-            if (lane == 0 && t == nwork - 1) {
-                a.stream[0] = L;
-                __hip_atomic_store(&hdr->total_words, prefix + agg, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-
-            // ---- header entry and compaction --------------------------------------
-            // The wave's lanes fill container words [1 + L + prefix, + agg); the
-            // output buffer ends at the capacity, so nothing is written past it.
-            // Each lane reads back only the scratch words it stored itself,
-            // sixty-four per round trip (all loads issued before any store),
-            // and stores whole 16-byte groups of its own words, then its last
-            // one to three words one by one.  Accesses are masked per lane
-            // (a lane without words for a group sends no request).
-            const uint64_t wbase =
-                1ull + L + (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)prefix) +
-                ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(prefix >> 32)) << 32);
-            const uint64_t wroom = a.capacity > wbase ? a.capacity - wbase : 0;
-            const Rsrc rout = make_rsrc(a.stream + (wroom ? wbase : 0),
-                                        (uint32_t)min(4 * wroom, 1ull << 31));
-            if (active) {
-                const uint64_t end = prefix + incl;
-                a.stream[1 + j] = (uint32_t)end;
-                const uint32_t ob = 4 * (incl - words);   // the lane's first word in rout
-                const uint32_t src = sp.top - 4 * words;
-                const uint32_t kt = words & ~3u;   // first word of the last, partial group
-                for (uint32_t k0 = 0; k0 < words; k0 += 64) {
-                    u32x4 v[16];
-                    uint32_t tw[3];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (k0 + 4 * i + 4 <= words)
-                            v[i] = buf_load4(sp.scr, src + 4 * k0 + 16 * i);
-                    const bool tail = kt >= k0 && kt < k0 + 64;
-#pragma unroll
-                    for (int e = 0; e < 3; ++e)
-                        if (tail && kt + e < words)
-                            tw[e] = (uint32_t)buf_load(sp.scr, src + 4 * (kt + e), 0);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (k0 + 4 * i + 4 <= words)
-                            buf_store4(rout, ob + 4 * (k0 + 4 * i), v[i]);
-#pragma unroll
-                    for (int e = 0; e < 3; ++e)
-                        if (tail && kt + e < words)
-                            buf_store(rout, ob + 4 * (kt + e), 0, (int32_t)tw[e]);
+                for (uint32_t g = 0; g < nr2; g += 2) {
+                    step(E0, E1, g);
+                    step(E1, E0, g + 1);
+                }
+                __syncthreads();   // the producers' last barrier
+                if (active) {
+                    while (cut_s >= 1)   // an empty lane: every cut holds the start state
+                        record_cut();
+                    if (sp.overflow) {
+                        lerr = lerr ? lerr : RANS_E_CAPACITY;
+                        sp.cb = sp.capb - 8;
+                    }
+                    buf_store(sp.scr, sp.top - 8 - sp.cb, 0, (int32_t)(uint32_t)x);
+                    buf_store(sp.scr, sp.top - 4 - sp.cb, 0, (int32_t)(uint32_t)(x >> 32));
+                    words = sp.cb / 4 + 2;
                 }
             }
+            publish_and_copy(a, hdr, flags, t, nwork, lane, j, active, sp, words, lerr);
+        } else if (in_lds) {
+            // producers: thread p fills steps 4q .. 4q+3 of lane l of every chunk
+            const uint32_t p = tid - kWave;
+            const uint32_t l = p % kPcLanes, q = p / kPcLanes;
+            const uint32_t j = j0 + l;
+            const bool mine = l < lpw && j < L;
+            const WaveBufs<kWave> wb = wave_bufs<kWave>(a, L, j0, j1, min(j, L - 1));
+            const LaneSteps ls = lane_steps(a.n, L, min(j, L - 1), wb.bw);
+            const uint32_t nch = (nr + kPcChunkRounds - 1) / kPcChunkRounds;
+            if (nch > 0) {
+                if (mine)
+                    pc_produce(ls, wb.rsym, wb.ridx, K, 0, q, l, round_bits);
+                __syncthreads();
+                for (uint32_t c = 1; c < nch; ++c) {
+                    if (mine)
+                        pc_produce(ls, wb.rsym, wb.ridx, K, c, q, l, round_bits);
+                    __syncthreads();
+                }
+            }
+            __syncthreads();   // the coding wave's last barrier
         }
     }
-
-    // ---- completion: the last block publishes status and cleans up -------------
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        const uint32_t old = atomicAdd(&hdr->done, 1u);
-        misc[1] = (old == gridDim.x - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (misc[1]) {
-        __threadfence();
-        if (!herr)
-            for (uint32_t k = tid; k < nwork; k += TPB)
-                flags[k] = 0;
-        if (tid == 0) {
-            const uint64_t total = 1ull + L + hdr->total_words;
-            int err = hdr->err;
-            if (!err && total > a.capacity)
-                err = RANS_E_CAPACITY;
-            *a.status = err;
-            *a.stream_words = herr ? 0ull : total;
-            hdr->err = 0;
-            hdr->total_words = 0;
-            hdr->done = 0;
-            __threadfence();
-        }
-    }
+    encode_block_end<kPcThreads>(a, hdr, flags, herr, nwork, misc);
 }
 
 template <int TPB, int CW, bool PAIR>
@@ -849,6 +1252,18 @@ hipError_t launch_encode_t(const EncodeArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+hipError_t launch_encode_pc(const EncodeArgs &a, hipStream_t s)
+{
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&encode_pc_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kPcLdsBytes);
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL(encode_pc_kernel, dim3(enc_waves(a.lanes)), dim3(kPcThreads), kPcLdsBytes,
+                       s, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s)
@@ -857,8 +1272,7 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t s)
     const uint32_t waves = enc_waves(a.lanes);
     const bool pair = enc_lanes_per_wave(a.lanes) >= 32;
     if (coding_one_per_cu(waves))
-        return pair ? launch_encode_t<4 * kWave, 1, true>(a, s)
-                    : launch_encode_t<4 * kWave, 1, false>(a, s);
+        return launch_encode_pc(a, s);
     if (waves <= 4 * kCodingCUs)
         return pair ? launch_encode_t<4 * kWave, 4, true>(a, s)
                     : launch_encode_t<4 * kWave, 4, false>(a, s);
