@@ -884,14 +884,18 @@ __global__ __launch_bounds__(TPB) void encode_kernel(EncodeArgs a)
 //   a step that is no position (padding, past the lane's end): the identity
 //     step (2^-16, 2^16, 0), which leaves the state unchanged and never
 //     renormalises;
-//   anything else (an escape, a bad index):  (symbol, index, 0, 0);
-// and set one bit per round of the chunk that holds an entry of the last
-// kind.  Two entry buffers alternate: one barrier per chunk hands a filled
-// buffer to the coding wave and the one it has finished back to the
+//   anything else (an escape, a bad index, a row whose values may overflow
+//     int32):  (symbol, index, 0, 0);
+// and set, per step of the chunk, one bit when some lane's entry is of the
+// last kind.  Two entry buffers alternate: one barrier per chunk hands a
+// filled buffer to the coding wave and the one it has finished back to the
 // producers.  The coding wave reads a round's entries during the round
-// before, runs the state chain (the fast form where the round's bit is
-// clear), and stores its spilled words; the puts, their order and the
-// container are those of encode_lane.
+// before and runs the state chain; at a step whose bit is set, the lanes
+// concerned first put the escape's groups and count (a scalar test per step
+// of such a round, nothing in the others).  Whether a lane may reach the end
+// of its scratch segment, or holds a split cut, is asked once per chunk; only
+// then is a round checked afterwards and redone with checked puts.  The
+// puts, their order and the container are those of encode_lane.
 constexpr uint32_t kPcLanes = 16;                           // lanes of a coding wave, at most
 constexpr uint32_t kPcChunkRounds = 6;
 constexpr uint32_t kPcChunk = kPcChunkRounds * kRound;      // steps per chunk
@@ -900,13 +904,14 @@ constexpr uint32_t kPcRing = kEncTableBudget;               // the coding wave's
 constexpr uint32_t kPcEntries = kPcRing + kEncRing * 4 * kWave;
 constexpr uint32_t kPcEntryBuf = kPcChunk * kPcLanes * 16;
 constexpr uint32_t kPcMisc = kPcEntries + 2 * kPcEntryBuf;  // [0] flag OR, [1] last block,
-                                                            // [2 + b] round bits of buffer b
-constexpr uint32_t kPcLdsBytes = kPcMisc + 16;
+                                                            // [2 + 2b, 3 + 2b] step bits of buffer b
+constexpr uint32_t kPcLdsBytes = kPcMisc + 32;
 static_assert(kPcLdsBytes <= kLdsBytes, "encoder LDS over budget");
 static_assert(kPcEntries % 16 == 0, "entries are 16-byte LDS accesses");
 static_assert(lanes_per_wave_for(4096, kCodingCUs) <= kPcLanes, "coding wave too wide");
 static_assert((kPcChunk / 4) * kPcLanes == kPcThreads - kWave, "one quad of steps per producer");
 static_assert(kPcChunkRounds % 2 == 0, "rounds run in pairs");
+static_assert(kPcChunk <= 64, "step bits of a chunk in two words");
 
 __device__ inline uint32_t pc_entry(uint32_t buf, uint32_t step, uint32_t l)
 {
@@ -937,24 +942,34 @@ __device__ inline LaneSteps lane_steps(uint64_t n, uint32_t L, uint32_t j, uint6
     return s;
 }
 
-// Producer: the entries of steps k4 .. k4+3 of one lane into buffer `buf` of
-// chunk step 4 q (positions c .. c+3 below, read as one 16-byte load per
-// array; a quad past the lane reads other lanes' values or zeros, only for
-// steps that are no positions).
-__device__ __forceinline__ void pc_produce(const LaneSteps &ls, Rsrc rsym, Rsrc ridx, uint32_t K,
-                                           uint32_t chunk, uint32_t q, uint32_t l,
-                                           uint32_t *round_bits)
+// Producer input: the symbols and indexes of steps 4q .. 4q+3 of a chunk for
+// one lane (positions c .. c+3 as one 16-byte load per array, c = the
+// position of step 4q+3; a quad past the lane reads other lanes' values or
+// zeros, only for steps that are no positions).
+struct PcIn {
+    u32x4 sv, iv;
+};
+__device__ inline PcIn pc_load(const LaneSteps &ls, Rsrc rsym, Rsrc ridx, uint32_t chunk,
+                               uint32_t q)
+{
+    const uint32_t k4 = chunk * kPcChunk + 4 * q;
+    const uint32_t off = ls.pbase + 4 * (ls.R8 - 4 - k4);   // (wraps past the buffer: reads 0)
+    return PcIn{buf_load4(rsym, off), buf_load4(ridx, off)};
+}
+
+// Producer: the entries of those four steps of lane l, and their step bits.
+__device__ __forceinline__ void pc_fill(const LaneSteps &ls, const PcIn &in, uint32_t K,
+                                        uint32_t chunk, uint32_t q, uint32_t l,
+                                        uint32_t *step_bits)
 {
     const uint32_t buf = chunk & 1u;
     const uint32_t k4 = chunk * kPcChunk + 4 * q;
-    const uint32_t off = ls.pbase + 4 * (ls.R8 - 4 - k4);   // (wraps past the buffer: reads 0)
-    const u32x4 sv = buf_load4(rsym, off), iv = buf_load4(ridx, off);
-    bool any_off = false;
+    uint32_t offs = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const uint32_t k = k4 + u;
-        const int32_t sym = (int32_t)sv[3 - u];
-        const uint32_t idx = iv[3 - u];
+        const int32_t sym = (int32_t)in.sv[3 - u];
+        const uint32_t idx = in.iv[3 - u];
         const RowMeta m = lds_meta(min(idx, K - 1));
         const uint32_t mv = m.mvf & 0xFFFFu;
         // s - offset wraps mod 2^32 into [0, mv) only on rows whose fast
@@ -973,19 +988,52 @@ __device__ __forceinline__ void pc_produce(const LaneSteps &ls, Rsrc rsym, Rsrc 
             ent = u32x4{(uint32_t)rb, (uint32_t)(rb >> 32), f, pr & 0xFFFFu};
         else
             ent = u32x4{(uint32_t)sym, idx, 0u, 0u};
-        any_off = any_off | (valid & !fast);
+        offs |= (valid & !fast) ? (1u << u) : 0u;
         lds_store<u32x4>(pc_entry(buf, 4 * q + u, l), ent);
     }
-    if (any_off)
-        __hip_atomic_fetch_or(&round_bits[buf], 1u << (q / 2), __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (offs)   // steps 4q .. 4q+3 are bits 4q % 32 .. of word 4q / 32
+        __hip_atomic_fetch_or(&step_bits[2 * buf + (4 * q) / 32], offs << ((4 * q) % 32),
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// The puts of an escaped value (its groups, then its count) before its REG
+// put, as in encode_prefix, with each spilled word going to the ring slot at
+// LDS address `ra` (advanced a slot per word; the round's room is asked
+// separately), and the (start, f) pair of the REG put's slot.
+__device__ __forceinline__ int pc_prefix(int32_t s, const RowMeta m, uint64_t &x, uint32_t &ra,
+                                         uint32_t &pair)
+{
+    int err = 0;
+    const uint32_t mv = m.mvf & 0xFFFFu;
+    const int64_t v = (int64_t)s - (int64_t)m.offset;
+    const bool esc = (uint64_t)v >= (uint64_t)mv;
+    uint64_t raw = v < 0 ? (uint64_t)(-2 * v - 1) : (uint64_t)(2 * (v - (int64_t)mv));
+    if (esc && raw >= (1ull << 31)) {
+        err = RANS_E_SYMBOL_RANGE;
+        raw = 0;
+    }
+    const uint32_t bits = raw ? 64u - (uint32_t)__clzll(raw) : 0u;
+    const uint32_t nb = esc ? (bits + kBypassBits - 1) / kBypassBits : 0u;
+    auto put_bits = [&](uint32_t b) {
+        const bool spill = x >= (1ull << (63 - kBypassBits));
+        lds_store<uint32_t>(ra, (uint32_t)x);
+        ra += spill ? 4u * kWave : 0u;
+        x = spill ? (x >> 32) : x;
+        x = (x << kBypassBits) | b;
+    };
+    for (uint32_t g = nb; g-- > 0;)
+        put_bits((uint32_t)(raw >> (kBypassBits * g)) & 15u);
+    if (esc)
+        put_bits(nb);
+    pair = lds_load<uint32_t>(m.base + 4 * (esc ? mv : (uint32_t)v));
+    return err;
 }
 
 __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
     uint32_t *misc = reinterpret_cast<uint32_t *>(lds + kPcMisc);
-    uint32_t *round_bits = misc + 2;
+    uint32_t *step_bits = misc + 2;
 
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
     const uint8_t *tab = a.ws + ws_enc_offset(a.num_tables, a.stride);
@@ -997,17 +1045,30 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
     const uint32_t nwork = enc_waves(L);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // 0 codes, 1..3 produce
     const uint32_t K = (uint32_t)a.num_tables;
+    const uint32_t t = blockIdx.x;
+    const uint32_t j0 = t * lpw, j1 = min(j0 + lpw, L);
+    // rounds of the longest lane (a lane holds floor or ceil of n / L
+    // positions), and chunks
+    const uint32_t nr = (uint32_t)(((a.n + L - 1) / L + kRound - 1) / kRound);
+    const uint32_t nch = (nr + kPcChunkRounds - 1) / kPcChunkRounds;
 
-    if (tid < 4)
+    // producers: thread p fills steps 4q .. 4q+3 of lane l of every chunk; the
+    // first chunk's loads are issued before the tables are staged
+    const uint32_t p = tid - kWave;
+    const uint32_t pl = p % kPcLanes, pq = p / kPcLanes;
+    const bool mine = wave > 0 && t < nwork && pl < lpw && j0 + pl < L;
+    const uint32_t pj = min(j0 + pl, L - 1);
+    const WaveBufs<kWave> pwb = wave_bufs<kWave>(a, L, j0, j1, pj);
+    const LaneSteps pls = lane_steps(a.n, L, pj, pwb.bw);
+    PcIn in0{};
+    if (mine && nch > 0)
+        in0 = pc_load(pls, pwb.rsym, pwb.ridx, 0, pq);
+
+    if (tid < 6)
         misc[tid] = 0u;
     bool in_lds;
     const int herr = encode_block_start<kPcThreads>(a, hdr, tab, lds, misc, in_lds);
-    const uint32_t t = blockIdx.x;
     if (!herr && t < nwork) {
-        const uint32_t j0 = t * lpw, j1 = min(j0 + lpw, L);
-        // rounds of the longest lane (a lane holds floor or ceil of n / L
-        // positions), in chunks
-        const uint32_t nr = (uint32_t)(((a.n + L - 1) / L + kRound - 1) / kRound);
         if (wave == 0) {
             const uint32_t j = j0 + lane;
             const bool active = lane < lpw && j < L;
@@ -1046,17 +1107,16 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                     cut_k = (cut_s >= 1 && ls.nj > 0) ? cut_step(cut_s) : ~0u;
                 };
                 const uint32_t ring_lds = kPcRing + 4 * lane;   // LDS address of ring slot 0
-                // One round (steps k0 .. k0+7) from its entries.
-                auto round = [&](const u32x4 (&E)[kRound], bool checked, uint32_t k0) {
-                    // room for three words per position: the fast steps need no check
-                    const bool room = sp.cb + 4 * (2 + 3 * kRound) < sp.capb;
+                // One round (steps k0 .. k0+7) from its entries; `esc` holds
+                // the round's step bits, `chk` says whether the chunk needs
+                // the room and cut test.  The round starts at ring slot 0 (its
+                // words were stored); the slot address advances a slot per
+                // word.
+                auto round = [&](const u32x4 (&E)[kRound], uint32_t esc, bool chk, uint32_t k0) {
                     const uint64_t x0 = x;
                     const uint32_t cb_start = sp.cb;
-                    if (!checked) {
-                        // the round starts at ring slot 0 (its words were
-                        // stored); the slot address advances a slot per word
-                        const uint32_t ra0 = ring_lds;
-                        uint32_t ra = ra0;
+                    uint32_t ra = ring_lds;
+                    if (esc == 0u) {
 #pragma unroll
                         for (int u = 0; u < kRound; ++u) {
                             const uint32_t f = E[u][2];
@@ -1066,18 +1126,16 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                             x = need ? (x >> 32) : x;
                             x = reg_step(x, E[u][3], f, entry_rcp(E[u]));
                         }
-                        sp.cb += (ra - ra0) / kWave;
                     } else {
-                        // as in encode_lane: an escape's groups and count, then
-                        // the escape slot's REG put; a bad index takes the
-                        // identity step
+                        // at a flagged step the lanes concerned put an escape's
+                        // groups and count and take the escape slot's pair; a
+                        // bad index takes the identity step
 #pragma unroll
                         for (int u = 0; u < kRound; ++u) {
                             uint32_t st = E[u][3], fu = E[u][2];
                             double ru = entry_rcp(E[u]);
-                            const bool off = fu == 0u;
-                            if (__ballot(off) != 0) {
-                                if (off) {
+                            if ((esc >> u) & 1u) {
+                                if (fu == 0u) {
                                     const int32_t sym = (int32_t)E[u][0];
                                     const uint32_t idx = E[u][1];
                                     st = 0u;
@@ -1085,8 +1143,7 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                                     ru = 1.0 / kTotal;
                                     if (idx < K) {
                                         uint32_t pr;
-                                        const int ec = encode_prefix<kWave>(sym, tb.meta(idx), tb,
-                                                                            x, sp, pr);
+                                        const int ec = pc_prefix(sym, tb.meta(idx), x, ra, pr);
                                         lerr = lerr ? lerr : ec;
                                         st = pr & 0xFFFFu;
                                         fu = pr >> 16;
@@ -1097,50 +1154,56 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                                 }
                             }
                             const bool need = (uint32_t)(x >> 32) >= (fu << (31 - kPrecision));
-                            *sp.slot(min((sp.cb - sp.cb0) >> 2, kEncRing - 1)) = (uint32_t)x;
-                            sp.cb += need ? 4u : 0u;
+                            lds_store<uint32_t>(ra, (uint32_t)x);
+                            ra += need ? 4u * kWave : 0u;
                             x = need ? (x >> 32) : x;
                             x = reg_step(x, st, fu, ru);
                         }
                     }
+                    sp.cb += (ra - ring_lds) / kWave;
                     // A lane near the end of its segment, or a round holding a
                     // split cut, redoes the round from its start with checked
                     // puts where needed.
-                    if (__builtin_expect(!__all(room & (cut_k >= k0 + kRound)), 0)) {
-                        x = x0;
-                        sp.cb = cb_start;
+                    if (chk) {
+                        // room for three words per position: the puts above
+                        // need no check
+                        const bool room = cb_start + 4 * (2 + 3 * kRound) < sp.capb;
+                        if (__builtin_expect(!__all(room & (cut_k >= k0 + kRound)), 0)) {
+                            x = x0;
+                            sp.cb = cb_start;
 #pragma unroll
-                        for (int u = 0; u < kRound; ++u) {
-                            const uint32_t f = E[u][2];
-                            const bool off = f == 0u;
-                            const bool fast = !off & room;
-                            const bool need = (uint32_t)(x >> 32) >= (f << (31 - kPrecision));
-                            const uint64_t xn =
-                                reg_step(need ? (x >> 32) : x, E[u][3], f, entry_rcp(E[u]));
-                            *sp.slot(min((sp.cb - sp.cb0) >> 2, kEncRing - 1)) = (uint32_t)x;
-                            sp.cb += (fast & need) ? 4u : 0u;
-                            x = fast ? xn : x;
-                            if (__builtin_expect(__ballot(!fast) != 0, 0)) {
-                                if (!fast) {
-                                    if (off) {
-                                        int ec = RANS_E_INDEX;
-                                        if (E[u][1] < K)
-                                            ec = encode_slow<kWave>((int32_t)E[u][0],
-                                                                    tb.meta(E[u][1]), tb, x, sp);
-                                        lerr = lerr ? lerr : ec;
-                                    } else {
-                                        // the REG put of an ordinary symbol (or the
-                                        // identity), with its spill checked
-                                        const bool spill =
-                                            x >= ((uint64_t)f << (63 - kPrecision));
-                                        sp.put_if(spill, (uint32_t)x);
-                                        x = spill ? (x >> 32) : x;
-                                        x = reg_step(x, E[u][3], f, entry_rcp(E[u]));
+                            for (int u = 0; u < kRound; ++u) {
+                                const uint32_t f = E[u][2];
+                                const bool off = f == 0u;
+                                const bool fast = !off & room;
+                                const bool need = (uint32_t)(x >> 32) >= (f << (31 - kPrecision));
+                                const uint64_t xn =
+                                    reg_step(need ? (x >> 32) : x, E[u][3], f, entry_rcp(E[u]));
+                                *sp.slot(min((sp.cb - sp.cb0) >> 2, kEncRing - 1)) = (uint32_t)x;
+                                sp.cb += (fast & need) ? 4u : 0u;
+                                x = fast ? xn : x;
+                                if (__builtin_expect(__ballot(!fast) != 0, 0)) {
+                                    if (!fast) {
+                                        if (off) {
+                                            int ec = RANS_E_INDEX;
+                                            if (E[u][1] < K)
+                                                ec = encode_slow<kWave>((int32_t)E[u][0],
+                                                                        tb.meta(E[u][1]), tb, x, sp);
+                                            lerr = lerr ? lerr : ec;
+                                        } else {
+                                            // the REG put of an ordinary symbol (or
+                                            // the identity), with its spill checked
+                                            const bool spill =
+                                                x >= ((uint64_t)f << (63 - kPrecision));
+                                            sp.put_if(spill, (uint32_t)x);
+                                            x = spill ? (x >> 32) : x;
+                                            x = reg_step(x, E[u][3], f, entry_rcp(E[u]));
+                                        }
                                     }
                                 }
+                                while (cut_k == k0 + u)   // (cuts may share a position)
+                                    record_cut();
                             }
-                            while (cut_k == k0 + u)   // (cuts may share a position)
-                                record_cut();
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -1157,14 +1220,17 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                     for (int u = 0; u < kRound; ++u)
                         E[u] = lds_load<u32x4>(pc_entry(buf, s0 + u, el));
                 };
-                // round bits of the chunk of round g (scalar), cleared for
-                // the producers' next use of the buffer
-                auto take_bits = [&](uint32_t g) -> uint32_t {
+                // step bits of the chunk of round g (scalar), cleared for the
+                // producers' next use of the buffer
+                auto take_bits = [&](uint32_t g) -> uint64_t {
                     const uint32_t buf = (g / kPcChunkRounds) & 1u;
-                    const uint32_t v = __builtin_amdgcn_readfirstlane(round_bits[buf]);
-                    if (lane == 0)
-                        round_bits[buf] = 0u;
-                    return v;
+                    const uint32_t lo = __builtin_amdgcn_readfirstlane(step_bits[2 * buf]);
+                    const uint32_t hi = __builtin_amdgcn_readfirstlane(step_bits[2 * buf + 1]);
+                    if (lane == 0) {
+                        step_bits[2 * buf] = 0u;
+                        step_bits[2 * buf + 1] = 0u;
+                    }
+                    return (uint64_t)lo | ((uint64_t)hi << 32);
                 };
                 // Round g: at the last round of a chunk, the barrier that
                 // hands over the next chunk comes first (this round's entries
@@ -1173,10 +1239,14 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                 // chunk holds an even number; an odd count gets one more
                 // round, of identity entries only), and every round requests
                 // the next one's entries (past the last: unused reads), so
-                // that the two entry arrays never merge at a branch.
+                // that the two entry arrays never merge at a branch.  At a
+                // chunk's first round the wave asks whether any lane could
+                // reach the end of its segment (three words a position) or
+                // holds a cut within the chunk.
                 const uint32_t nr2 = (nr + 1) & ~1u;
                 u32x4 E0[kRound], E1[kRound];
-                uint32_t bits = 0, bits_next = 0;
+                uint64_t bits = 0, bits_next = 0;
+                bool chk = true;
                 auto step = [&](const u32x4 (&E)[kRound], u32x4 (&En)[kRound], uint32_t g) {
                     const uint32_t r = g % kPcChunkRounds;
                     const bool handover = r == kPcChunkRounds - 1 && g + 1 < nr2;
@@ -1185,8 +1255,13 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                         bits_next = take_bits(g + 1);
                     }
                     load_round(En, g + 1);
+                    if (r == 0) {
+                        const uint32_t kend = (g + kPcChunkRounds) * kRound;
+                        const bool ok = sp.cb + 4 * (2 + 3 * kPcChunk) < sp.capb && cut_k >= kend;
+                        chk = !__all(ok | !active);
+                    }
                     if (active)
-                        round(E, (bits >> r) & 1u, g * kRound);
+                        round(E, (uint32_t)(bits >> (kRound * r)) & 0xFFu, chk, g * kRound);
                     if (handover)
                         bits = bits_next;
                 };
@@ -1214,21 +1289,14 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
             }
             publish_and_copy(a, hdr, flags, t, nwork, lane, j, active, sp, words, lerr);
         } else if (in_lds) {
-            // producers: thread p fills steps 4q .. 4q+3 of lane l of every chunk
-            const uint32_t p = tid - kWave;
-            const uint32_t l = p % kPcLanes, q = p / kPcLanes;
-            const uint32_t j = j0 + l;
-            const bool mine = l < lpw && j < L;
-            const WaveBufs<kWave> wb = wave_bufs<kWave>(a, L, j0, j1, min(j, L - 1));
-            const LaneSteps ls = lane_steps(a.n, L, min(j, L - 1), wb.bw);
-            const uint32_t nch = (nr + kPcChunkRounds - 1) / kPcChunkRounds;
             if (nch > 0) {
                 if (mine)
-                    pc_produce(ls, wb.rsym, wb.ridx, K, 0, q, l, round_bits);
+                    pc_fill(pls, in0, K, 0, pq, pl, step_bits);
                 __syncthreads();
                 for (uint32_t c = 1; c < nch; ++c) {
                     if (mine)
-                        pc_produce(ls, wb.rsym, wb.ridx, K, c, q, l, round_bits);
+                        pc_fill(pls, pc_load(pls, pwb.rsym, pwb.ridx, c, pq), K, c, pq, pl,
+                                step_bits);
                     __syncthreads();
                 }
             }
