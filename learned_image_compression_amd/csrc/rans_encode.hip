@@ -657,6 +657,23 @@ __device__ __forceinline__ void publish_and_copy(const EncodeArgs &a, WsHeader *
     const uint32_t L = a.lanes;
     if (lerr)
         record_error(hdr, lerr);
+    // The lane's first 64 words are read back from its scratch segment now:
+    // their loads do not depend on the offset the look-back finds, and their
+    // latency passes while it waits.
+    const uint32_t src = sp.top - 4 * words;   // the lane's first word in sp.scr
+    const uint32_t kt = words & ~3u;           // first word of the last, partial group
+    u32x4 v0[16];
+    uint32_t t0[3];
+    if (active) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (4 * i + 4 <= words)
+                v0[i] = buf_load4(sp.scr, src + 16 * i);
+#pragma unroll
+        for (int e = 0; e < 3; ++e)
+            if (kt < 64 && kt + e < words)
+                t0[e] = (uint32_t)buf_load(sp.scr, src + 4 * (kt + e), 0);
+    }
 
     // ---- wave scan and look-back over earlier waves -----------------------
     // Every wave publishes its aggregate, then reads the flags of the 256
@@ -748,10 +765,10 @@ __device__ __forceinline__ void publish_and_copy(const EncodeArgs &a, WsHeader *
     // The wave's lanes fill container words [1 + L + prefix, + agg); the
     // output buffer ends at the capacity, so nothing is written past it.
     // Each lane reads back only the scratch words it stored itself,
-    // sixty-four per round trip (all loads issued before any store),
-    // and stores whole 16-byte groups of its own words, then its last
-    // one to three words one by one.  Accesses are masked per lane
-    // (a lane without words for a group sends no request).
+    // sixty-four per round trip (all loads issued before any store; the
+    // first sixty-four above), and stores whole 16-byte groups of its own
+    // words, then its last one to three words one by one.  Accesses are
+    // masked per lane (a lane without words for a group sends no request).
     const uint64_t wbase =
         1ull + L + (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)prefix) +
         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(prefix >> 32)) << 32);
@@ -762,9 +779,15 @@ __device__ __forceinline__ void publish_and_copy(const EncodeArgs &a, WsHeader *
         const uint64_t end = prefix + incl;
         a.stream[1 + j] = (uint32_t)end;
         const uint32_t ob = 4 * (incl - words);   // the lane's first word in rout
-        const uint32_t src = sp.top - 4 * words;
-        const uint32_t kt = words & ~3u;   // first word of the last, partial group
-        for (uint32_t k0 = 0; k0 < words; k0 += 64) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (4 * i + 4 <= words)
+                buf_store4(rout, ob + 16 * i, v0[i]);
+#pragma unroll
+        for (int e = 0; e < 3; ++e)
+            if (kt < 64 && kt + e < words)
+                buf_store(rout, ob + 4 * (kt + e), 0, (int32_t)t0[e]);
+        for (uint32_t k0 = 64; k0 < words; k0 += 64) {
             u32x4 v[16];
             uint32_t tw[3];
 #pragma unroll
@@ -996,11 +1019,33 @@ __device__ __forceinline__ void pc_fill(const LaneSteps &ls, const PcIn &in, uin
                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// Where the coding wave's puts send a lane's spilled words.  Every put
+// offers the state's low word; it is kept when `spill` holds, and the next
+// put overwrites it otherwise.  The room for three words a position is asked
+// before a round, so neither sink checks it.
+struct RingSink {      // the lane's LDS ring (a round starts at slot 0)
+    uint32_t a;        // LDS address of the slot for the next word
+    __device__ inline void put(bool spill, uint32_t w)
+    {
+        lds_store<uint32_t>(a, w);
+        a += spill ? 4u * kWave : 0u;
+    }
+};
+struct ScratchSink {   // straight to the lane's scratch segment
+    Rsrc scr;
+    uint32_t o;        // byte offset of the next word (words go downwards)
+    __device__ inline void put(bool spill, uint32_t w)
+    {
+        buf_store(scr, o, 0, (int32_t)w);
+        o -= spill ? 4u : 0u;
+    }
+};
+
 // The puts of an escaped value (its groups, then its count) before its REG
-// put, as in encode_prefix, with each spilled word going to the ring slot at
-// LDS address `ra` (advanced a slot per word; the round's room is asked
-// separately), and the (start, f) pair of the REG put's slot.
-__device__ __forceinline__ int pc_prefix(int32_t s, const RowMeta m, uint64_t &x, uint32_t &ra,
+// put, as in encode_prefix, with each spilled word going to `sink`, and the
+// (start, f) pair of the REG put's slot.
+template <class Sink>
+__device__ __forceinline__ int pc_prefix(int32_t s, const RowMeta m, uint64_t &x, Sink &sink,
                                          uint32_t &pair)
 {
     int err = 0;
@@ -1016,8 +1061,7 @@ __device__ __forceinline__ int pc_prefix(int32_t s, const RowMeta m, uint64_t &x
     const uint32_t nb = esc ? (bits + kBypassBits - 1) / kBypassBits : 0u;
     auto put_bits = [&](uint32_t b) {
         const bool spill = x >= (1ull << (63 - kBypassBits));
-        lds_store<uint32_t>(ra, (uint32_t)x);
-        ra += spill ? 4u * kWave : 0u;
+        sink.put(spill, (uint32_t)x);
         x = spill ? (x >> 32) : x;
         x = (x << kBypassBits) | b;
     };
@@ -1112,17 +1156,14 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                 // the room and cut test.  The round starts at ring slot 0 (its
                 // words were stored); the slot address advances a slot per
                 // word.
-                auto round = [&](const u32x4 (&E)[kRound], uint32_t esc, bool chk, uint32_t k0) {
-                    const uint64_t x0 = x;
-                    const uint32_t cb_start = sp.cb;
-                    uint32_t ra = ring_lds;
+                // The round's puts, words to `sink`.
+                auto puts = [&](auto &sink, const u32x4 (&E)[kRound], uint32_t esc) {
                     if (esc == 0u) {
 #pragma unroll
                         for (int u = 0; u < kRound; ++u) {
                             const uint32_t f = E[u][2];
                             const bool need = (uint32_t)(x >> 32) >= (f << (31 - kPrecision));
-                            lds_store<uint32_t>(ra, (uint32_t)x);
-                            ra += need ? 4u * kWave : 0u;
+                            sink.put(need, (uint32_t)x);
                             x = need ? (x >> 32) : x;
                             x = reg_step(x, E[u][3], f, entry_rcp(E[u]));
                         }
@@ -1143,7 +1184,7 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                                     ru = 1.0 / kTotal;
                                     if (idx < K) {
                                         uint32_t pr;
-                                        const int ec = pc_prefix(sym, tb.meta(idx), x, ra, pr);
+                                        const int ec = pc_prefix(sym, tb.meta(idx), x, sink, pr);
                                         lerr = lerr ? lerr : ec;
                                         st = pr & 0xFFFFu;
                                         fu = pr >> 16;
@@ -1154,17 +1195,31 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                                 }
                             }
                             const bool need = (uint32_t)(x >> 32) >= (fu << (31 - kPrecision));
-                            lds_store<uint32_t>(ra, (uint32_t)x);
-                            ra += need ? 4u * kWave : 0u;
+                            sink.put(need, (uint32_t)x);
                             x = need ? (x >> 32) : x;
                             x = reg_step(x, st, fu, ru);
                         }
                     }
-                    sp.cb += (ra - ring_lds) / kWave;
-                    // A lane near the end of its segment, or a round holding a
-                    // split cut, redoes the round from its start with checked
-                    // puts where needed.
-                    if (chk) {
+                };
+                // One round: in a chunk where every lane has room and no cut,
+                // each put stores its word to the scratch segment at once; else
+                // the words wait in the LDS ring, a lane near the end of its
+                // segment or at a split cut redoes the round from its start
+                // with checked puts, and the round's words are stored after.
+                auto round = [&](const u32x4 (&E)[kRound], uint32_t esc, bool chk, uint32_t k0) {
+                    if (!chk) {
+                        ScratchSink sink{sp.scr, sp.top - 4 - sp.cb};
+                        puts(sink, E, esc);
+                        sp.cb = sp.top - 4 - sink.o;
+                        sp.cb0 = sp.cb;
+                        return;
+                    }
+                    const uint64_t x0 = x;
+                    const uint32_t cb_start = sp.cb;
+                    RingSink sink{ring_lds};
+                    puts(sink, E, esc);
+                    sp.cb += (sink.a - ring_lds) / kWave;
+                    {
                         // room for three words per position: the puts above
                         // need no check
                         const bool room = cb_start + 4 * (2 + 3 * kRound) < sp.capb;
