@@ -114,10 +114,10 @@ __device__ inline uint32_t cdfm1_at(const Tab &tab, const RowMeta &m, uint32_t k
 //    read from the ring when it holds them, else on the checked path;
 //  * out-of-range values and bad indexes are reported.
 // Writes the symbol to `out`; returns a status.
-template <int TPB, class Tab>
+template <class WordsT, class Tab>
 __device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint32_t bucket,
                                            bool beyond, uint32_t slot, uint32_t f, uint32_t rr,
-                                           uint64_t &x, Words<TPB> &wd, const DecTables &t,
+                                           uint64_t &x, WordsT &wd, const DecTables &t,
                                            const Tab &tab, int32_t &out)
 {
     if ((uint32_t)r >= t.K)
@@ -213,8 +213,8 @@ __device__ __forceinline__ int decode_slow(int32_t r, const RowMeta &m, uint32_t
 // case (past the window, escape or out-of-range value, renormalisation word
 // not in the ring, bad index) redo the step on the slow path.  A bad row
 // index arrives with a fast bound of 0.
-template <int TPB, class Tab>
-__device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_t &x, Words<TPB> &wd,
+template <class WordsT, class Tab>
+__device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_t &x, WordsT &wd,
                                             const DecTables &t, const Tab &tab, int32_t &out,
                                             int &lerr)
 {
@@ -230,8 +230,8 @@ __device__ __forceinline__ void decode_step(int32_t r, const RowMeta &m, uint64_
         if (slow) {
             x = x0;
             wd.pos = pos0;
-            const int ec = decode_slow<TPB>(r, m, s.bucket, s.beyond, s.slot, s.f, s.rr, x, wd, t,
-                                            tab, out);
+            const int ec = decode_slow(r, m, s.bucket, s.beyond, s.slot, s.f, s.rr, x, wd, t, tab,
+                                       out);
             lerr = lerr ? lerr : ec;
         }
     }
@@ -480,7 +480,7 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs &a, const Tab &tab,
                     if (general) {
                         out[o + k] = 0;
                         if (k0 + k < nj && !lerr)
-                            decode_step<TPB>(idx[k], m[k], x, wd, t, tab, out[o + k], lerr);
+                            decode_step(idx[k], m[k], x, wd, t, tab, out[o + k], lerr);
                     }
                 }
             }
@@ -514,6 +514,370 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs &a, const Tab &tab,
     }
     if (lerr)
         record_error(hdr, lerr);
+}
+
+// ---- one decoding wave per CU (at most 2048 lanes) ------------------------------
+//
+// With at most 2048 lanes, 8 lanes or fewer go to each CU, and one wave
+// decodes them all: its time is that of the lanes' chains of dependent
+// lookups, and every other instruction it issues lengthens them.  So the
+// block's other waves do the state-independent work around the chains:
+//  * waves 1 and 2 load each step's row index and write the row's metadata
+//    (an index outside [0, K) gets row K-1's with a fast bound of 0, whose
+//    step then reports the index) into entry buffers, one chunk of 32 steps
+//    ahead of the decoding wave, and store the decoded symbols of the chunk
+//    two behind it from LDS to memory, 16 bytes a lane;
+//  * wave 3 keeps each lane's next 128 stream words in an LDS FIFO: at every
+//    handover it is told how far the lane has read, and refills the slots of
+//    words read before;
+//  * waves 4 to 7 (on the SIMDs of waves 0 to 3) only take part in the
+//    barriers.
+// A round inside every lane is decoded with no branch first; a lane that
+// met a step outside the common case takes up again from the state before
+// it, step by step.  Measured against eight decoding waves of few lanes
+// each: 151 against 167 us at 2048 lanes of the 1080p latent, 254 against
+// 334 us at 1024; at 4096 lanes (16 a wave) the eight waves were 2% faster,
+// and there the eight-wave form is kept.
+// One barrier per chunk, at the start of the decoding wave's last round of a
+// chunk (that round's entries are already in registers), hands over the next
+// chunk's entries, the words filled since the last handover, and the symbols
+// of the chunk before last.  The decoding wave takes each step as decode_step
+// does (committed at once; lanes outside the common case redo it on the slow
+// path), so a word the FIFO does not hold yet is read from memory there.
+constexpr uint32_t kPdMaxLanes = 2048;
+constexpr uint32_t kPdLanes = 16;                              // lanes of a group, at most
+constexpr uint32_t kPdChainWaves = 1;                          // decoding waves a block
+constexpr uint32_t kPdChainLanes = kPdLanes / kPdChainWaves;   // lanes of a decoding wave
+constexpr uint32_t kPdChunkRounds = 4;
+constexpr uint32_t kPdChunk = kPdChunkRounds * kRound;   // steps per chunk
+constexpr uint32_t kPdFifo = 128;                        // words per lane
+constexpr uint32_t kPdEntryBuf = kPdChunk * kPdLanes * 16;
+constexpr uint32_t kPdOutBuf = kPdChunk * kPdLanes * 4;
+// the region after the table set: [entries x2 | symbols x3 | fifo | positions]
+constexpr uint32_t kPdOut = 2 * kPdEntryBuf;
+constexpr uint32_t kPdFifoOff = kPdOut + 3 * kPdOutBuf;
+constexpr uint32_t kPdPos = kPdFifoOff + kPdFifo * kPdLanes * 4;
+constexpr uint32_t kPdBytes = kPdPos + 4 * kPdLanes;
+static_assert(lanes_per_wave_for(kPdMaxLanes, kCodingCUs) <= kPdLanes, "decoding wave too wide");
+static_assert((kPdChunk / 4) * kPdLanes == 2 * kWave, "one quad of steps per entry producer");
+static_assert(kPdChunkRounds % 2 == 0, "rounds run in pairs");
+static_assert(kDecTPB == 8 * kWave && kPdChainWaves + 3 <= 8, "decoding, producing and waiting waves");
+static_assert(kPdLanes % kPdChainWaves == 0, "lanes split evenly over the decoding waves");
+
+// The lane's words in the FIFO: word p in slot p mod kPdFifo; [.., filled)
+// hold words (the interface of Words, for decode_step and decode_slow).
+struct PdWords {
+    const uint32_t *w;   // the lane's words in global memory
+    uint32_t fifo;       // LDS address of this lane's slot 0 (slots are kPdLanes words apart)
+    uint32_t count;      // words in the lane
+    uint32_t pos;        // next word to consume
+    uint32_t filled;     // words [.., filled) are in the FIFO
+    uint32_t next;       // FIFO word at pos (valid when pos < filled)
+
+    __device__ inline uint32_t slot(uint32_t p) const { return fifo + (p % kPdFifo) * (4 * kPdLanes); }
+    __device__ inline uint32_t at(uint32_t p) const { return lds_load<uint32_t>(slot(p)); }
+    __device__ inline bool refill(uint64_t &x)
+    {
+        if (x < kStateLow) {
+            if (pos >= count)
+                return false;
+            if (pos < filled) {
+                x = (x << 32) | next;
+            } else {
+                const uint32_t direct = w[pos];
+                __builtin_amdgcn_s_waitcnt(0);
+                x = (x << 32) | direct;
+            }
+            ++pos;
+        }
+        next = at(pos);
+        return true;
+    }
+};
+
+// Lane j of a group: positions [b, b + nj), payload words [beg_w, beg_w + W)
+// (header entries checked as in decode_wave).
+struct PdLane {
+    uint64_t b, beg_w;
+    uint32_t nj, W;
+    bool ok;
+};
+
+// Decode one group of lanes j0 .. j0 + lpw - 1 with the block's eight waves;
+// P is the LDS address of the region after the table set.
+__device__ __forceinline__ void decode_pc_group(const DecodeArgs &a, const DecTables &t,
+                                                uint32_t L, uint32_t lpw, uint32_t grp, uint32_t P)
+{
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
+    const uint32_t K = t.K;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & (kWave - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t j0 = __builtin_amdgcn_readfirstlane(grp * lpw);
+    const uint32_t j1 = min(j0 + lpw, L);
+    // the group's positions and stream words, as buffers
+    const uint64_t bw = lane_begin(a.n, L, j0), ew = lane_begin(a.n, L, j1);
+    const Rsrc ridx = make_rsrc(a.indexes + bw, (uint32_t)(4 * (ew - bw)));
+    const Rsrc rout = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
+    const uint64_t wbase = j0 ? (uint32_t)__builtin_amdgcn_readfirstlane(a.stream[j0]) : 0u;
+    const uint64_t wavail = a.capacity - 1 - L;
+    const uint64_t wbytes = wbase < wavail ? min(4 * (wavail - wbase), 1ull << 31) : 0;
+    const Rsrc rstr = make_rsrc(a.stream + 1 + L + (wbase < wavail ? wbase : 0), (uint32_t)wbytes);
+    // rounds of the longest lane, and chunks
+    const uint32_t nr = (uint32_t)(((a.n + L - 1) / L + kRound - 1) / kRound);
+    const uint32_t nch = (nr + kPdChunkRounds - 1) / kPdChunkRounds;
+    // roles: decoding waves [0, cw), entry waves cw and cw+1, the FIFO wave
+    // cw+2, the rest only take part in the barriers
+    constexpr uint32_t cw = kPdChainWaves;
+    const bool chain = wave < cw;
+    const uint32_t p = tid - cw * kWave;   // producer thread
+    // this thread's lane: the decoding wave's lane, or the producers' l
+    // (a decoding wave's lanes past its share alias lanes of it, and only read)
+    const uint32_t l = chain ? kPdChainLanes * wave + (lane & (kPdChainLanes - 1)) : p % kPdLanes;
+    const uint32_t j = j0 + l;
+    const bool act = (chain ? lane < kPdChainLanes : wave < cw + 3) && l < lpw && j < L;
+    PdLane ln{};
+    if (act) {
+        ln.b = lane_begin(a.n, L, j);
+        ln.nj = (uint32_t)(lane_begin(a.n, L, j + 1) - ln.b);
+        const uint64_t beg_w = j ? a.stream[j] : 0u;
+        const uint64_t end_w = a.stream[1 + j];
+        ln.ok = !(end_w < beg_w + 2 || 1ull + L + end_w > a.capacity || beg_w < wbase);
+        ln.beg_w = beg_w;
+        ln.W = ln.ok ? (uint32_t)(end_w - beg_w) : 2u;
+    }
+    auto entry_at = [&](uint32_t chunk, uint32_t s, uint32_t ll) {
+        return P + (chunk & 1u) * kPdEntryBuf + (s * kPdLanes + ll) * 16;
+    };
+    auto out_at = [&](uint32_t chunk, uint32_t s, uint32_t ll) {   // lane-major
+        return P + kPdOut + (chunk % 3u) * kPdOutBuf + (ll * kPdChunk + s) * 4;
+    };
+    const uint32_t pos_at = P + kPdPos + 4 * l;
+
+    if (chain) {
+        // ---- a decoding wave --------------------------------------------------
+        int lerr = (act && !ln.ok) ? RANS_E_CORRUPT : 0;
+        const bool live = act && ln.ok;
+        PdWords wd;
+        wd.w = a.stream + 1 + L + ln.beg_w;
+        wd.fifo = P + kPdFifoOff + 4 * l;
+        wd.count = ln.W;
+        wd.pos = 2;
+        wd.filled = min(ln.W, 2 + kPdFifo);
+        wd.next = 0;
+        uint64_t x = kStateLow;
+        if (live)
+            x = (uint64_t)wd.w[0] | ((uint64_t)wd.w[1] << 32);   // the flushed state
+        uint32_t pub = 2;   // the position published at the last handover
+        const uint32_t el = l & (kPdLanes - 1);
+        auto load_round = [&](u32x4 (&E)[kRound], uint32_t g) {
+            const uint32_t s0 = (g % kPdChunkRounds) * kRound;
+#pragma unroll
+            for (int u = 0; u < kRound; ++u)
+                E[u] = lds_load<u32x4>(entry_at(g / kPdChunkRounds, s0 + u, el));
+        };
+        auto meta_of = [](const u32x4 &e) {
+            RowMeta m;
+            m.base = e[0];
+            m.offset = (int32_t)e[1];
+            m.mvf = e[2];
+            m.lut = e[3];
+            return m;
+        };
+        // (a bad index arrives with mvf 0: its step reports it)
+        auto row_of = [&](const RowMeta &m) -> int32_t { return (m.mvf & 0xFFFFu) ? 0 : (int32_t)K; };
+        // One round.  A round inside every lane is first decoded with no
+        // branch, each lane noting its first step outside the common case
+        // (past the lookup window, an escape or a value out of int32's
+        // range, a word the FIFO does not hold yet); such a lane then takes
+        // up again from the state before that step, step by step as
+        // decode_step does.  A lane's last, partial round goes step by step
+        // from the start.  The round's symbols go to LDS as 32 bytes a lane.
+        auto round = [&](const u32x4 (&E)[kRound], uint32_t g) {
+            const uint32_t k0 = g * kRound;
+            const uint32_t c = g / kPdChunkRounds, s0 = (g % kPdChunkRounds) * kRound;
+            int32_t o[kRound];
+            if (__all(k0 + kRound <= ln.nj)) {
+                uint64_t xs[kRound];
+                uint32_t ps[kRound];
+                uint32_t first_bad = kRound;
+#pragma unroll
+                for (int u = 0; u < kRound; ++u) {
+                    xs[u] = x;
+                    ps[u] = wd.pos;
+                    const RowMeta m = meta_of(E[u]);
+                    const Lookup sl = lookup_step(m, x, t, LdsTab{});
+                    const bool need = sl.xn < kStateLow;
+                    const bool bad = sl.beyond | (sl.slot >= (m.mvf >> 16)) |
+                                     (need & (wd.pos >= wd.filled));
+                    first_bad = (bad & (first_bad == kRound)) ? (uint32_t)u : first_bad;
+                    x = need ? ((sl.xn << 32) | wd.next) : sl.xn;
+                    wd.pos += need ? 1u : 0u;
+                    o[u] = (int32_t)(sl.slot + (uint32_t)m.offset);
+                    wd.next = wd.at(wd.pos);
+                }
+                if (__builtin_expect(__ballot(first_bad < kRound) != 0, 0)) {
+                    if (first_bad < kRound) {
+#pragma unroll
+                        for (int u = 0; u < kRound; ++u) {
+                            x = first_bad == (uint32_t)u ? xs[u] : x;
+                            wd.pos = first_bad == (uint32_t)u ? ps[u] : wd.pos;
+                        }
+                        wd.next = wd.at(wd.pos);
+                    }
+#pragma unroll
+                    for (int u = 0; u < kRound; ++u)
+                        if (first_bad <= (uint32_t)u)
+                            decode_step(row_of(meta_of(E[u])), meta_of(E[u]), x, wd, t, LdsTab{},
+                                        o[u], lerr);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < kRound; ++u) {
+                    o[u] = 0;
+                    if (k0 + u < ln.nj)
+                        decode_step(row_of(meta_of(E[u])), meta_of(E[u]), x, wd, t, LdsTab{},
+                                    o[u], lerr);
+                }
+            }
+            const uint32_t oa = out_at(c, s0, l);
+            lds_store<u32x4>(oa, u32x4{(uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]});
+            lds_store<u32x4>(oa + 16, u32x4{(uint32_t)o[4], (uint32_t)o[5], (uint32_t)o[6], (uint32_t)o[7]});
+        };
+        const uint32_t nr2 = (nr + 1) & ~1u;
+        u32x4 E0[kRound], E1[kRound];
+        auto handover = [&]() {
+            if (act)
+                lds_store<uint32_t>(pos_at, wd.pos);
+            __syncthreads();
+            // the FIFO now holds the words filled since the handover before
+            wd.filled = min(ln.W, pub + kPdFifo);
+            pub = wd.pos;
+            wd.next = wd.at(wd.pos);
+        };
+        auto step = [&](const u32x4 (&E)[kRound], u32x4 (&En)[kRound], uint32_t g) {
+            if (g % kPdChunkRounds == kPdChunkRounds - 1 && g + 1 < nr2)
+                handover();
+            load_round(En, g + 1);
+            if (live)
+                round(E, g);
+        };
+        if (nr2 > 0) {
+            if (act)
+                lds_store<uint32_t>(pos_at, 2u);
+            __syncthreads();   // chunk 0 and the first words are ready
+            wd.next = wd.at(2);
+            load_round(E0, 0);
+        }
+        for (uint32_t g = 0; g < nr2; g += 2) {
+            step(E0, E1, g);
+            step(E1, E0, g + 1);
+        }
+        __syncthreads();   // the producers' last barrier
+        if (live && !lerr && (x != kStateLow || wd.pos != ln.W))
+            lerr = RANS_E_CORRUPT;
+        if (lerr)
+            record_error(hdr, lerr);
+    } else if (wave < cw + 2) {
+        // ---- entries and symbol stores ---------------------------------------
+        const uint32_t q = p / kPdLanes;   // steps 4q .. 4q+3 of a chunk
+        auto fill_entries = [&](uint32_t c) {
+            if (!act)
+                return;
+            const uint32_t k = c * kPdChunk + 4 * q;
+            const u32x4 iv = buf_load4(ridx, (uint32_t)(4 * (ln.b - bw)) + 4 * k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t idx = iv[e];
+                u32x4 m = lds_load<u32x4>(16 * min(idx, K - 1));
+                if (idx >= K)
+                    m[2] = 0u;   // fast bound and escape slot 0
+                lds_store<u32x4>(entry_at(c, 4 * q + e, l), m);
+            }
+        };
+        auto store_symbols = [&](uint32_t c) {
+            if (!act || !ln.ok)
+                return;
+            const uint32_t k = c * kPdChunk + 4 * q;
+            if (k >= ln.nj)
+                return;
+            const u32x4 v = lds_load<u32x4>(out_at(c, 4 * q, l));
+            const uint32_t ob = (uint32_t)(4 * (ln.b - bw)) + 4 * k;
+            if (k + 4 <= ln.nj) {
+                buf_store4(rout, ob, v);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (k + e < ln.nj)
+                        buf_store(rout, ob + 4 * e, 0, (int32_t)v[e]);
+            }
+        };
+        if (nch > 0) {
+            fill_entries(0);
+            __syncthreads();
+            for (uint32_t c = 0; c < nch; ++c) {
+                if (c + 1 < nch)
+                    fill_entries(c + 1);
+                if (c >= 2)
+                    store_symbols(c - 2);
+                if (c + 1 < nch)
+                    __syncthreads();
+            }
+        }
+        __syncthreads();   // the decoding wave is done
+        if (nch >= 2)
+            store_symbols(nch - 2);
+        if (nch >= 1)
+            store_symbols(nch - 1);
+    } else if (wave == cw + 2) {
+        // ---- stream words into the FIFO ----------------------------------------
+        const uint32_t sub = (p - 2 * kWave) / kPdLanes;   // four threads a lane
+        const bool mine = act && ln.ok;
+        uint32_t filled = 2;   // words [2, filled) are in the FIFO
+        const uint32_t lw = (uint32_t)(4 * (ln.beg_w - wbase));   // the lane's words in rstr
+        const uint32_t fifo = P + kPdFifoOff + 4 * l;
+        // words [filled, target): sixteen a pass (four per thread), four
+        // passes' loads issued before any of their FIFO writes
+        auto fill_words = [&](uint32_t target) {
+            while (filled < target) {
+                u32x4 v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t w0 = filled + 16 * k + 4 * sub;
+                    v[k] = w0 < target ? buf_load4(rstr, lw + 4 * w0) : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t w = filled + 16 * k + 4 * sub + e;
+                        if (w < target)
+                            lds_store<uint32_t>(fifo + (w % kPdFifo) * (4 * kPdLanes), v[k][e]);
+                    }
+                filled = min(target, filled + 64);
+            }
+        };
+        if (mine)
+            fill_words(min(ln.W, 2 + kPdFifo));
+        if (nch > 0) {
+            __syncthreads();
+            for (uint32_t c = 0; c + 1 < nch; ++c) {
+                // the slots of words the lane had read at the handover
+                if (mine)
+                    fill_words(min(ln.W, lds_load<uint32_t>(pos_at) + kPdFifo));
+                __syncthreads();
+            }
+        }
+        __syncthreads();
+    } else {
+        // ---- waves 4 to 7: the barriers only ---------------------------------------
+        if (nch > 0) {
+            __syncthreads();
+            for (uint32_t c = 0; c + 1 < nch; ++c)
+                __syncthreads();
+        }
+        __syncthreads();
+    }
 }
 
 template <bool SPLIT>
@@ -553,12 +917,18 @@ __global__ __launch_bounds__(kDecTPB) void decode_kernel(DecodeArgs a)
     // without split records), spread thin over waves (lpw units a wave).
     // With at most one wave per block in use, every block codes one wave
     // (its other waves only help stage the tables); beyond, all eight code.
-    // Wave w of the grid takes unit groups w, w + G*cw, ...
+    // Wave w of the grid takes unit groups w, w + G*cw, ...  Whole lanes on
+    // a staged table set that leaves room for its buffers, at most 4096 of
+    // them, take the one-decoding-wave form instead (decode_pc_group): a
+    // group of up to 16 lanes per block, blocks taking groups b, b + G, ...
     const uint32_t LV = herr ? 0u : (L << pl);
-    const uint32_t lpw = lanes_per_wave_for(LV, kMaxDecWaves);
+    const uint32_t pd_base = (__builtin_amdgcn_readfirstlane(hdr->dec_bytes) + 15u) & ~15u;
+    const bool pc = !SPLIT && !herr && in_lds && L <= kPdMaxLanes &&
+                    pd_base + kPdBytes <= decode_lds_bytes(TPB);
+    const uint32_t lpw = pc ? lanes_per_wave_for(LV, kCodingCUs) : lanes_per_wave_for(LV, kMaxDecWaves);
     const uint32_t nw = (LV + lpw - 1) / lpw;
     const uint32_t G = gridDim.x;
-    const uint32_t cw = nw <= G ? 1u : (uint32_t)(TPB / kWave);
+    const uint32_t cw = (pc || nw <= G) ? 1u : (uint32_t)(TPB / kWave);
     const bool block_work = (uint64_t)blockIdx.x * cw < nw;
     stage_tables<TPB>(lds, tab, (!herr && block_work && in_lds) ? hdr->dec_bytes : 0u);
     __syncthreads();
@@ -581,7 +951,12 @@ __global__ __launch_bounds__(kDecTPB) void decode_kernel(DecodeArgs a)
     // every lane, and scalar they keep the buffer descriptors and loops uniform
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     herr = __builtin_amdgcn_readfirstlane(herr);
-    if (!herr && wave < cw) {
+    if (!herr && pc) {
+        for (uint32_t w = blockIdx.x; w < nw; w += G) {
+            const DecodeArgs al = fresh_kernel_args<DecodeArgs>();
+            decode_pc_group(al, t, L, lpw, w, pd_base);
+        }
+    } else if (!herr && wave < cw) {
         const uint32_t first = blockIdx.x * cw + wave, step = G * cw;
         // The arguments are read afresh for every unit group: hoisted out of
         // the loop, they would stay live across the whole coding body and

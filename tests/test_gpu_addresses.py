@@ -60,12 +60,14 @@ def _tables(ar, w):
                       ar.put(w.offsets, torch.int32))
 
 
-def test_lane_coders_and_splits_at_high_addresses():
+@pytest.mark.parametrize("lanes", [4096, 1024])
+def test_lane_coders_and_splits_at_high_addresses(lanes):
     import torch
     import gpu_util as G
-    G.say("[addresses] lane encode, decode, split decode (y1080, 4096 lanes)")
+    # (1024 lanes decode on the one-decoding-wave path, 4096 on eight waves)
+    G.say(f"[addresses] lane encode, decode, split decode (y1080, {lanes} lanes)")
     w = W.load("y1080")
-    lanes, pieces = 4096, 4
+    pieces = 4
     ar = Arena(256 << 20)
     tables = _tables(ar, w)
     sym, idx = ar.put(w.symbols, torch.int32), ar.put(w.indexes, torch.int32)
