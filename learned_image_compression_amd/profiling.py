@@ -179,6 +179,10 @@ def _rows(path_glob: str):
 
 
 def _kernel_key(name: str) -> str:
+    # both forms of the lane encoder (one coding wave per CU up to 4096 lanes,
+    # several beyond) are the encode kernel of their run
+    if "encode_pc_kernel" in name:
+        return "encode_kernel"
     if re.search(r"decode_kernel<[^>]*true>", name):
         return "decode_kernel_split"
     if re.search(r"il_encode_kernel<[^>]*true>", name):

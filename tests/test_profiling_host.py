@@ -13,6 +13,7 @@ from learned_image_compression_amd import profiling as P
 def test_kernel_keys_keep_each_kernel_apart():
     names = {
         "void rans::(anonymous namespace)::encode_kernel<256, 1>(rans::EncodeArgs)": "encode_kernel",
+        "rans::(anonymous namespace)::encode_pc_kernel(rans::EncodeArgs)": "encode_kernel",
         "void rans::(anonymous namespace)::decode_kernel<512, 8, false>(rans::DecodeArgs)":
             "decode_kernel",
         "void rans::(anonymous namespace)::decode_kernel<512, 8, true>(rans::DecodeArgs)":
