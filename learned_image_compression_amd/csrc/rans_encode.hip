@@ -41,6 +41,8 @@
 // chain never waits on global memory.
 #include "rans_coding.hpp"
 
+#include <type_traits>
+
 namespace rans {
 
 namespace {
@@ -674,6 +676,9 @@ __device__ __forceinline__ void publish_and_copy(const EncodeArgs &a, WsHeader *
             if (kt < 64 && kt + e < words)
                 t0[e] = (uint32_t)buf_load(sp.scr, src + 4 * (kt + e), 0);
     }
+    // (a compiler barrier: the loads would otherwise sink below the
+    // look-back to where their values are used, and wait there)
+    asm volatile("" ::: "memory");
 
     // ---- wave scan and look-back over earlier waves -----------------------
     // Every wave publishes its aggregate, then reads the flags of the 256
@@ -1156,17 +1161,21 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                 // the room and cut test.  The round starts at ring slot 0 (its
                 // words were stored); the slot address advances a slot per
                 // word.
-                // The round's puts, words to `sink`.
+                // The round's puts, words to `sink`: a round with no marked
+                // step, then one with some.
+                auto puts_plain = [&](auto &sink, const u32x4 (&E)[kRound]) {
+#pragma unroll
+                    for (int u = 0; u < kRound; ++u) {
+                        const uint32_t f = E[u][2];
+                        const bool need = (uint32_t)(x >> 32) >= (f << (31 - kPrecision));
+                        sink.put(need, (uint32_t)x);
+                        x = need ? (x >> 32) : x;
+                        x = reg_step(x, E[u][3], f, entry_rcp(E[u]));
+                    }
+                };
                 auto puts = [&](auto &sink, const u32x4 (&E)[kRound], uint32_t esc) {
                     if (esc == 0u) {
-#pragma unroll
-                        for (int u = 0; u < kRound; ++u) {
-                            const uint32_t f = E[u][2];
-                            const bool need = (uint32_t)(x >> 32) >= (f << (31 - kPrecision));
-                            sink.put(need, (uint32_t)x);
-                            x = need ? (x >> 32) : x;
-                            x = reg_step(x, E[u][3], f, entry_rcp(E[u]));
-                        }
+                        puts_plain(sink, E);
                     } else {
                         // at a flagged step the lanes concerned put an escape's
                         // groups and count and take the escape slot's pair; a
@@ -1209,7 +1218,10 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                 auto round = [&](const u32x4 (&E)[kRound], uint32_t esc, bool chk, uint32_t k0) {
                     if (!chk) {
                         ScratchSink sink{sp.scr, sp.top - 4 - sp.cb};
-                        puts(sink, E, esc);
+                        if (esc == 0u)   // (one scalar test for the common round)
+                            puts_plain(sink, E);
+                        else
+                            puts(sink, E, esc);
                         sp.cb = sp.top - 4 - sink.o;
                         sp.cb0 = sp.cb;
                         return;
@@ -1268,17 +1280,18 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                 // Entries of round g, read for every wavefront lane (lanes
                 // past the wave's read another lane's, unused).
                 const uint32_t el = lane & (kPcLanes - 1);
-                auto load_round = [&](u32x4 (&E)[kRound], uint32_t g) {
-                    const uint32_t buf = (g / kPcChunkRounds) & 1u;
-                    const uint32_t s0 = (g % kPcChunkRounds) * kRound;
+                // (round r of chunk c)
+                auto load_round = [&](u32x4 (&E)[kRound], uint32_t c, uint32_t r) {
+                    const uint32_t buf = c & 1u;
+                    const uint32_t s0 = r * kRound;
 #pragma unroll
                     for (int u = 0; u < kRound; ++u)
                         E[u] = lds_load<u32x4>(pc_entry(buf, s0 + u, el));
                 };
-                // step bits of the chunk of round g (scalar), cleared for the
-                // producers' next use of the buffer
-                auto take_bits = [&](uint32_t g) -> uint64_t {
-                    const uint32_t buf = (g / kPcChunkRounds) & 1u;
+                // step bits of chunk c (scalar), cleared for the producers'
+                // next use of the buffer
+                auto take_bits = [&](uint32_t c) -> uint64_t {
+                    const uint32_t buf = c & 1u;
                     const uint32_t lo = __builtin_amdgcn_readfirstlane(step_bits[2 * buf]);
                     const uint32_t hi = __builtin_amdgcn_readfirstlane(step_bits[2 * buf + 1]);
                     if (lane == 0) {
@@ -1287,47 +1300,53 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                     }
                     return (uint64_t)lo | ((uint64_t)hi << 32);
                 };
-                // Round g: at the last round of a chunk, the barrier that
-                // hands over the next chunk comes first (this round's entries
-                // are already in registers); then the next round's entries
-                // are requested and this round runs.  Rounds go in pairs (a
-                // chunk holds an even number; an odd count gets one more
-                // round, of identity entries only), and every round requests
-                // the next one's entries (past the last: unused reads), so
-                // that the two entry arrays never merge at a branch.  At a
-                // chunk's first round the wave asks whether any lane could
-                // reach the end of its segment (three words a position) or
-                // holds a cut within the chunk.
-                const uint32_t nr2 = (nr + 1) & ~1u;
+                // A chunk's six rounds run unrolled, so that the round's
+                // place in the chunk, its step bits and the handover are
+                // fixed at compile time.  At the chunk's start the wave asks
+                // whether any lane could reach the end of its segment (three
+                // words a position) or holds a cut within the chunk.  Every
+                // round requests the next one's entries (past the last:
+                // unused reads); before the last round of a chunk the barrier
+                // that hands over the next chunk comes first (that round's
+                // entries are already in registers).  The last chunk runs
+                // whole: its rounds past the longest lane hold identity
+                // entries.
                 u32x4 E0[kRound], E1[kRound];
                 uint64_t bits = 0, bits_next = 0;
                 bool chk = true;
-                auto step = [&](const u32x4 (&E)[kRound], u32x4 (&En)[kRound], uint32_t g) {
-                    const uint32_t r = g % kPcChunkRounds;
-                    const bool handover = r == kPcChunkRounds - 1 && g + 1 < nr2;
-                    if (handover) {
-                        __syncthreads();
-                        bits_next = take_bits(g + 1);
-                    }
-                    load_round(En, g + 1);
-                    if (r == 0) {
-                        const uint32_t kend = (g + kPcChunkRounds) * kRound;
-                        const bool ok = sp.cb + 4 * (2 + 3 * kPcChunk) < sp.capb && cut_k >= kend;
-                        chk = !__all(ok | !active);
+                auto step = [&](auto rc, const u32x4 (&E)[kRound], u32x4 (&En)[kRound],
+                                uint32_t c) {
+                    constexpr uint32_t r = decltype(rc)::value;
+                    if constexpr (r + 1 == kPcChunkRounds) {
+                        if (c + 1 < nch) {
+                            __syncthreads();
+                            bits_next = take_bits(c + 1);
+                        }
+                        load_round(En, c + 1, 0);
+                    } else {
+                        load_round(En, c, r + 1);
                     }
                     if (active)
-                        round(E, (uint32_t)(bits >> (kRound * r)) & 0xFFu, chk, g * kRound);
-                    if (handover)
-                        bits = bits_next;
+                        round(E, (uint32_t)(bits >> (kRound * r)) & 0xFFu, chk,
+                              (c * kPcChunkRounds + r) * kRound);
                 };
-                if (nr2 > 0) {
+                if (nch > 0) {
                     __syncthreads();   // chunk 0 is ready
                     bits = take_bits(0);
-                    load_round(E0, 0);
+                    load_round(E0, 0, 0);
                 }
-                for (uint32_t g = 0; g < nr2; g += 2) {
-                    step(E0, E1, g);
-                    step(E1, E0, g + 1);
+                static_assert(kPcChunkRounds == 6, "the unrolled chunk below");
+                for (uint32_t c = 0; c < nch; ++c) {
+                    const bool ok = sp.cb + 4 * (2 + 3 * kPcChunk) < sp.capb &&
+                                    cut_k >= (c + 1) * kPcChunk;
+                    chk = !__all(ok | !active);
+                    step(std::integral_constant<uint32_t, 0>{}, E0, E1, c);
+                    step(std::integral_constant<uint32_t, 1>{}, E1, E0, c);
+                    step(std::integral_constant<uint32_t, 2>{}, E0, E1, c);
+                    step(std::integral_constant<uint32_t, 3>{}, E1, E0, c);
+                    step(std::integral_constant<uint32_t, 4>{}, E0, E1, c);
+                    step(std::integral_constant<uint32_t, 5>{}, E1, E0, c);
+                    bits = bits_next;
                 }
                 __syncthreads();   // the producers' last barrier
                 if (active) {
