@@ -41,8 +41,12 @@ __device__ inline uint64_t reg_step(uint64_t x, uint32_t start, uint32_t f, doub
     const double t = __builtin_fma(xd, rcp, 4503599627370496.0);   // 2^52
     const uint64_t tb = (uint64_t)__double_as_longlong(t);
     const int32_t r = (int32_t)(lo - (uint32_t)tb * f);
-    const int32_t s = r + (int32_t)start + ((r >> 31) & ((int32_t)f - (int32_t)kTotal));
-    return (tb << kPrecision) + (uint64_t)(int64_t)s;
+    // s < 0 exactly when r < 0 (then s < start + f - 2^16 <= 0), so r's sign
+    // word serves as s's high word; the added start is picked by bit select
+    const uint32_t m = (uint32_t)(r >> 31);
+    const uint32_t s = (uint32_t)r + start + (m & (f - kTotal));
+    const u32x2 sm = {s, m};
+    return (tb << kPrecision) + __builtin_bit_cast(uint64_t, sm);
 }
 
 }  // namespace rans
