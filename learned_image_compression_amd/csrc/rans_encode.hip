@@ -1156,13 +1156,9 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                     cut_k = (cut_s >= 1 && ls.nj > 0) ? cut_step(cut_s) : ~0u;
                 };
                 const uint32_t ring_lds = kPcRing + 4 * lane;   // LDS address of ring slot 0
-                // One round (steps k0 .. k0+7) from its entries; `esc` holds
-                // the round's step bits, `chk` says whether the chunk needs
-                // the room and cut test.  The round starts at ring slot 0 (its
-                // words were stored); the slot address advances a slot per
-                // word.
-                // The round's puts, words to `sink`: a round with no marked
-                // step, then one with some.
+                // A round is steps k0 .. k0+7 from its entries; `esc` holds
+                // the round's step bits.  The round's puts, words to `sink`:
+                // a round with no marked step, then one with some.
                 auto puts_plain = [&](auto &sink, const u32x4 (&E)[kRound]) {
 #pragma unroll
                     for (int u = 0; u < kRound; ++u) {
@@ -1210,22 +1206,14 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                         }
                     }
                 };
-                // One round: in a chunk where every lane has room and no cut,
-                // each put stores its word to the scratch segment at once; else
-                // the words wait in the LDS ring, a lane near the end of its
-                // segment or at a split cut redoes the round from its start
-                // with checked puts, and the round's words are stored after.
-                auto round = [&](const u32x4 (&E)[kRound], uint32_t esc, bool chk, uint32_t k0) {
-                    if (!chk) {
-                        ScratchSink sink{sp.scr, sp.top - 4 - sp.cb};
-                        if (esc == 0u)   // (one scalar test for the common round)
-                            puts_plain(sink, E);
-                        else
-                            puts(sink, E, esc);
-                        sp.cb = sp.top - 4 - sink.o;
-                        sp.cb0 = sp.cb;
-                        return;
-                    }
+                // A round of a chunk where some lane could reach the end of
+                // its segment or holds a cut (the other chunks' puts store
+                // each word to the scratch segment at once): the words wait
+                // in the LDS ring (from slot 0; the slot address advances a
+                // slot per word), a lane near the end of its segment or at a
+                // split cut redoes the round from its start with checked
+                // puts, and the round's words are stored after.
+                auto round_checked = [&](const u32x4 (&E)[kRound], uint32_t esc, uint32_t k0) {
                     const uint64_t x0 = x;
                     const uint32_t cb_start = sp.cb;
                     RingSink sink{ring_lds};
@@ -1313,9 +1301,8 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                 // entries.
                 u32x4 E0[kRound], E1[kRound];
                 uint64_t bits = 0, bits_next = 0;
-                bool chk = true;
                 auto step = [&](auto rc, const u32x4 (&E)[kRound], u32x4 (&En)[kRound],
-                                uint32_t c) {
+                                uint32_t c, auto &&run_round) {
                     constexpr uint32_t r = decltype(rc)::value;
                     if constexpr (r + 1 == kPcChunkRounds) {
                         if (c + 1 < nch) {
@@ -1327,8 +1314,17 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                         load_round(En, c, r + 1);
                     }
                     if (active)
-                        round(E, (uint32_t)(bits >> (kRound * r)) & 0xFFu, chk,
-                              (c * kPcChunkRounds + r) * kRound);
+                        run_round(E, (uint32_t)(bits >> (kRound * r)) & 0xFFu,
+                                  (c * kPcChunkRounds + r) * kRound);
+                };
+                // the six rounds of chunk c, each run by run_round
+                auto chunk = [&](uint32_t c, auto &&run_round) {
+                    step(std::integral_constant<uint32_t, 0>{}, E0, E1, c, run_round);
+                    step(std::integral_constant<uint32_t, 1>{}, E1, E0, c, run_round);
+                    step(std::integral_constant<uint32_t, 2>{}, E0, E1, c, run_round);
+                    step(std::integral_constant<uint32_t, 3>{}, E1, E0, c, run_round);
+                    step(std::integral_constant<uint32_t, 4>{}, E0, E1, c, run_round);
+                    step(std::integral_constant<uint32_t, 5>{}, E1, E0, c, run_round);
                 };
                 if (nch > 0) {
                     __syncthreads();   // chunk 0 is ready
@@ -1339,13 +1335,21 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                 for (uint32_t c = 0; c < nch; ++c) {
                     const bool ok = sp.cb + 4 * (2 + 3 * kPcChunk) < sp.capb &&
                                     cut_k >= (c + 1) * kPcChunk;
-                    chk = !__all(ok | !active);
-                    step(std::integral_constant<uint32_t, 0>{}, E0, E1, c);
-                    step(std::integral_constant<uint32_t, 1>{}, E1, E0, c);
-                    step(std::integral_constant<uint32_t, 2>{}, E0, E1, c);
-                    step(std::integral_constant<uint32_t, 3>{}, E1, E0, c);
-                    step(std::integral_constant<uint32_t, 4>{}, E0, E1, c);
-                    step(std::integral_constant<uint32_t, 5>{}, E1, E0, c);
+                    if (__all(ok | !active)) {
+                        // every put of the chunk stores its word at once, and
+                        // the segment's count is brought up to date after it
+                        ScratchSink sink{sp.scr, sp.top - 4 - sp.cb};
+                        chunk(c, [&](const u32x4 (&E)[kRound], uint32_t esc, uint32_t) {
+                            if (esc == 0u)   // (one scalar test for the common round)
+                                puts_plain(sink, E);
+                            else
+                                puts(sink, E, esc);
+                        });
+                        sp.cb = sp.top - 4 - sink.o;
+                        sp.cb0 = sp.cb;
+                    } else {
+                        chunk(c, round_checked);
+                    }
                     bits = bits_next;
                 }
                 __syncthreads();   // the producers' last barrier
