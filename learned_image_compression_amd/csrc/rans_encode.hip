@@ -933,7 +933,9 @@ constexpr uint32_t kPcEntries = kPcRing + kEncRing * 4 * kWave;
 constexpr uint32_t kPcEntryBuf = kPcChunk * kPcLanes * 16;
 constexpr uint32_t kPcMisc = kPcEntries + 2 * kPcEntryBuf;  // [0] flag OR, [1] last block,
                                                             // [2 + 2b, 3 + 2b] step bits of buffer b
-constexpr uint32_t kPcLdsBytes = kPcMisc + 32;
+constexpr uint32_t kPcEscBuf = kPcChunk * kPcLanes * 4;
+constexpr uint32_t kPcEsc = kPcMisc + 32;                   // escaped values of three chunks
+constexpr uint32_t kPcLdsBytes = kPcEsc + 3 * kPcEscBuf;
 static_assert(kPcLdsBytes <= kLdsBytes, "encoder LDS over budget");
 static_assert(kPcEntries % 16 == 0, "entries are 16-byte LDS accesses");
 static_assert(lanes_per_wave_for(4096, kCodingCUs) <= kPcLanes, "coding wave too wide");
@@ -944,6 +946,14 @@ static_assert(kPcChunk <= 64, "step bits of a chunk in two words");
 __device__ inline uint32_t pc_entry(uint32_t buf, uint32_t step, uint32_t l)
 {
     return kPcEntries + buf * kPcEntryBuf + (step * kPcLanes + l) * 16;
+}
+// Step `step` of chunk c, lane l: the zig-zag value + 1 of an escaped value
+// whose entry is its escape slot's REG put, else 0.  Three buffers, as the
+// producers fill chunk c+2 while the coding wave's last round of chunk c may
+// still read chunk c's.
+__device__ inline uint32_t pc_esc(uint32_t chunk, uint32_t step, uint32_t l)
+{
+    return kPcEsc + (chunk % 3u) * kPcEscBuf + (step * kPcLanes + l) * 4;
 }
 __device__ inline double entry_rcp(const u32x4 &e)
 {
@@ -1009,15 +1019,22 @@ __device__ __forceinline__ void pc_fill(const LaneSteps &ls, const PcIn &in, uin
         const double r = reciprocal(f);
         const uint64_t rb = __builtin_bit_cast(uint64_t, r);
         const bool valid = k >= ls.pad && k < ls.R8;
+        // an escaped value in range on a row whose values fit int32 (fast
+        // bound mv): the entry is the escape slot's REG put (pr was read at
+        // mv) and the value goes beside it
+        const int64_t v = (int64_t)sym - (int64_t)m.offset;
+        const uint64_t raw = v < 0 ? (uint64_t)(-2 * v - 1) : (uint64_t)(2 * (v - (int64_t)mv));
+        const bool esc = !fast & (idx < K) & ((m.mvf >> 16) != 0u) & (raw < (1ull << 31));
         u32x4 ent;
         if (!valid)
             ent = u32x4{0u, 0x3EF00000u, kTotal, 0u};   // 2^-16, 2^16, 0
-        else if (fast)
+        else if (fast | esc)
             ent = u32x4{(uint32_t)rb, (uint32_t)(rb >> 32), f, pr & 0xFFFFu};
         else
             ent = u32x4{(uint32_t)sym, idx, 0u, 0u};
         offs |= (valid & !fast) ? (1u << u) : 0u;
         lds_store<u32x4>(pc_entry(buf, 4 * q + u, l), ent);
+        lds_store<uint32_t>(pc_esc(chunk, 4 * q + u, l), (valid & esc) ? (uint32_t)raw + 1u : 0u);
     }
     if (offs)   // steps 4q .. 4q+3 are bits 4q % 32 .. of word 4q / 32
         __hip_atomic_fetch_or(&step_bits[2 * buf + (4 * q) / 32], offs << ((4 * q) % 32),
@@ -1045,6 +1062,24 @@ struct ScratchSink {   // straight to the lane's scratch segment
         o -= spill ? 4u : 0u;
     }
 };
+
+// The BITS puts of an escaped value raw < 2^31, last to first: its groups
+// nb-1 .. 0, then the count nb, as in encode_prefix; put(spill, w) offers
+// the state's low word.
+template <class Put>
+__device__ __forceinline__ void put_escape_groups(uint32_t raw, uint64_t &x, Put &&put)
+{
+    const uint32_t nb = raw ? (32u - (uint32_t)__clz(raw) + kBypassBits - 1) / kBypassBits : 0u;
+    auto put_bits = [&](uint32_t b) {
+        const bool spill = x >= (1ull << (63 - kBypassBits));
+        put(spill, (uint32_t)x);
+        x = spill ? (x >> 32) : x;
+        x = (x << kBypassBits) | b;
+    };
+    for (uint32_t g = nb; g-- > 0;)
+        put_bits((raw >> (kBypassBits * g)) & 15u);
+    put_bits(nb);
+}
 
 // The puts of an escaped value (its groups, then its count) before its REG
 // put, as in encode_prefix, with each spilled word going to `sink`, and the
@@ -1156,6 +1191,7 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                     cut_k = (cut_s >= 1 && ls.nj > 0) ? cut_step(cut_s) : ~0u;
                 };
                 const uint32_t ring_lds = kPcRing + 4 * lane;   // LDS address of ring slot 0
+                const uint32_t el = lane & (kPcLanes - 1);       // this lane's entry column
                 // A round is steps k0 .. k0+7 from its entries; `esc` holds
                 // the round's step bits.  The round's puts, words to `sink`:
                 // a round with no marked step, then one with some.
@@ -1169,19 +1205,30 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                         x = reg_step(x, E[u][3], f, entry_rcp(E[u]));
                     }
                 };
-                auto puts = [&](auto &sink, const u32x4 (&E)[kRound], uint32_t esc) {
+                // `sa`: the LDS address of the round's escaped values for
+                // this lane (step u at sa + u * 4 * kPcLanes).
+                auto puts = [&](auto &sink, const u32x4 (&E)[kRound], uint32_t esc, uint32_t sa) {
                     if (esc == 0u) {
                         puts_plain(sink, E);
                     } else {
                         // at a flagged step the lanes concerned put an escape's
-                        // groups and count and take the escape slot's pair; a
-                        // bad index takes the identity step
+                        // groups and count before the escape slot's REG put
+                        // (in the entry); the lanes whose entry holds the
+                        // symbol and index instead (a bad index, a row whose
+                        // values might leave int32, a value out of range) take
+                        // the whole symbol here, a bad index the identity step
 #pragma unroll
                         for (int u = 0; u < kRound; ++u) {
                             uint32_t st = E[u][3], fu = E[u][2];
                             double ru = entry_rcp(E[u]);
                             if ((esc >> u) & 1u) {
-                                if (fu == 0u) {
+                                if (fu != 0u) {
+                                    const uint32_t e = lds_load<uint32_t>(sa + 4 * kPcLanes * u);
+                                    if (e != 0u)
+                                        put_escape_groups(e - 1u, x, [&](bool spill, uint32_t w) {
+                                            sink.put(spill, w);
+                                        });
+                                } else {
                                     const int32_t sym = (int32_t)E[u][0];
                                     const uint32_t idx = E[u][1];
                                     st = 0u;
@@ -1214,10 +1261,11 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                 // split cut redoes the round from its start with checked
                 // puts, and the round's words are stored after.
                 auto round_checked = [&](const u32x4 (&E)[kRound], uint32_t esc, uint32_t k0) {
+                    const uint32_t sa = pc_esc(k0 / kPcChunk, k0 % kPcChunk, el);
                     const uint64_t x0 = x;
                     const uint32_t cb_start = sp.cb;
                     RingSink sink{ring_lds};
-                    puts(sink, E, esc);
+                    puts(sink, E, esc, sa);
                     sp.cb += (sink.a - ring_lds) / kWave;
                     {
                         // room for three words per position: the puts above
@@ -1230,7 +1278,10 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                             for (int u = 0; u < kRound; ++u) {
                                 const uint32_t f = E[u][2];
                                 const bool off = f == 0u;
-                                const bool fast = !off & room;
+                                uint32_t e = 0u;   // an escaped value + 1
+                                if ((esc >> u) & 1u)
+                                    e = off ? 0u : lds_load<uint32_t>(sa + 4 * kPcLanes * u);
+                                const bool fast = !off & room & (e == 0u);
                                 const bool need = (uint32_t)(x >> 32) >= (f << (31 - kPrecision));
                                 const uint64_t xn =
                                     reg_step(need ? (x >> 32) : x, E[u][3], f, entry_rcp(E[u]));
@@ -1246,8 +1297,14 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                                                                         tb.meta(E[u][1]), tb, x, sp);
                                             lerr = lerr ? lerr : ec;
                                         } else {
-                                            // the REG put of an ordinary symbol (or
-                                            // the identity), with its spill checked
+                                            // an escaped value's groups and count,
+                                            // then the REG put of the slot (or of
+                                            // the identity), spills checked
+                                            if (e != 0u)
+                                                put_escape_groups(e - 1u, x,
+                                                                  [&](bool spill, uint32_t w) {
+                                                                      sp.put_if(spill, w);
+                                                                  });
                                             const bool spill =
                                                 x >= ((uint64_t)f << (63 - kPrecision));
                                             sp.put_if(spill, (uint32_t)x);
@@ -1267,7 +1324,6 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                 };
                 // Entries of round g, read for every wavefront lane (lanes
                 // past the wave's read another lane's, unused).
-                const uint32_t el = lane & (kPcLanes - 1);
                 // (round r of chunk c)
                 auto load_round = [&](u32x4 (&E)[kRound], uint32_t c, uint32_t r) {
                     const uint32_t buf = c & 1u;
@@ -1339,11 +1395,11 @@ __global__ __launch_bounds__(kPcThreads) void encode_pc_kernel(EncodeArgs a)
                         // every put of the chunk stores its word at once, and
                         // the segment's count is brought up to date after it
                         ScratchSink sink{sp.scr, sp.top - 4 - sp.cb};
-                        chunk(c, [&](const u32x4 (&E)[kRound], uint32_t esc, uint32_t) {
+                        chunk(c, [&](const u32x4 (&E)[kRound], uint32_t esc, uint32_t k0) {
                             if (esc == 0u)   // (one scalar test for the common round)
                                 puts_plain(sink, E);
                             else
-                                puts(sink, E, esc);
+                                puts(sink, E, esc, pc_esc(c, k0 % kPcChunk, el));
                         });
                         sp.cb = sp.top - 4 - sink.o;
                         sp.cb0 = sp.cb;
