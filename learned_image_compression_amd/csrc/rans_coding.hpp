@@ -42,7 +42,7 @@ __device__ inline uint64_t reg_step(uint64_t x, uint32_t start, uint32_t f, doub
     const uint64_t tb = (uint64_t)__double_as_longlong(t);
     const int32_t r = (int32_t)(lo - (uint32_t)tb * f);
     // s < 0 exactly when r < 0 (then s < start + f - 2^16 <= 0), so r's sign
-    // word serves as s's high word; the added start is picked by bit select
+    // word m serves as s's high word (no sign extension of s itself)
     const uint32_t m = (uint32_t)(r >> 31);
     const uint32_t s = (uint32_t)r + start + (m & (f - kTotal));
     const u32x2 sm = {s, m};

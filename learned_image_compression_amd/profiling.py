@@ -47,15 +47,24 @@ import sys
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
+def _code_only(text: str) -> str:
+    """A source file's code without its comments and blank lines (a string
+    literal holding // or /* is not expected in these kernels)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.split("\n"))
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
 def kernel_source_hash(name: str) -> str:
-    """Hash of the sources that make up one coding kernel (rans_<name>.hip and
-    the shared headers): counter summaries recorded for other sources are stale."""
+    """Hash of the code that makes up one coding kernel (rans_<name>.hip and
+    the shared headers, comments left out): counter summaries recorded for
+    other code are stale."""
     h = hashlib.sha256()
     extra = {"interleaved": ("rans_frontend.hpp", "rans_lookup.hpp"),
              "decode": ("rans_lookup.hpp",)}.get(name, ())
     for f in ("rans_internal.hpp", "rans_coding.hpp", *extra, f"rans_{name}.hip"):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 KIB = 1024.0

@@ -48,3 +48,20 @@ def test_counter_per_dispatch_sums_rows_then_averages(tmp_path):
         w.writerow(["1", rows[0][1], "WRITE_SIZE", 7.0])
     got = P.counter_per_dispatch(str(path), "FETCH_SIZE")
     assert got == {"decode_kernel": 20.0, "il_decode_kernel": 1000.0}
+
+
+def test_kernel_source_hash_follows_code_not_comments(tmp_path, monkeypatch):
+    import shutil
+    src = tmp_path / "csrc"
+    shutil.copytree(P.CSRC, src)
+    monkeypatch.setattr(P, "CSRC", str(src))
+    before = {k: P.kernel_source_hash(k) for k in ("encode", "decode", "interleaved")}
+    path = src / "rans_coding.hpp"
+    text = path.read_text()
+    # comments, blank lines and trailing blanks do not change the hash
+    path.write_text("// a note\n\n" + text.replace("namespace rans {", "namespace rans {   /* x */\n\n"))
+    assert {k: P.kernel_source_hash(k) for k in before} == before
+    # code does, for every kernel built from the file
+    path.write_text(text + "\nstatic const int kProbe = 1;\n")
+    after = {k: P.kernel_source_hash(k) for k in before}
+    assert all(after[k] != before[k] for k in before)
