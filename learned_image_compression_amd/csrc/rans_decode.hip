@@ -297,7 +297,7 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs &a, const Tab &tab,
     // the wave's first word (scalar, so the stream's buffer descriptor is)
     const uint64_t wbase = jw ? (uint32_t)__builtin_amdgcn_readfirstlane(a.stream[jw]) : 0u;
     const uint64_t wavail = a.capacity - 1 - L;
-    const uint64_t wbytes = wbase < wavail ? min(4 * (wavail - wbase), 1ull << 31) : 0;
+    const uint64_t wbytes = wbase < wavail ? rsrc_bytes(4 * (wavail - wbase)) : 0;
     const Rsrc rstr = make_rsrc(a.stream + 1 + L + (wbase < wavail ? wbase : 0), (uint32_t)wbytes);
     if (!(lane < lpw && u < LV))
         return;
@@ -621,7 +621,7 @@ __device__ __forceinline__ void decode_pc_group(const DecodeArgs &a, const DecTa
     const Rsrc rout = make_rsrc(a.symbols + bw, (uint32_t)(4 * (ew - bw)));
     const uint64_t wbase = j0 ? (uint32_t)__builtin_amdgcn_readfirstlane(a.stream[j0]) : 0u;
     const uint64_t wavail = a.capacity - 1 - L;
-    const uint64_t wbytes = wbase < wavail ? min(4 * (wavail - wbase), 1ull << 31) : 0;
+    const uint64_t wbytes = wbase < wavail ? rsrc_bytes(4 * (wavail - wbase)) : 0;
     const Rsrc rstr = make_rsrc(a.stream + 1 + L + (wbase < wavail ? wbase : 0), (uint32_t)wbytes);
     // rounds of the longest lane, and chunks
     const uint32_t nr = (uint32_t)(((a.n + L - 1) / L + kRound - 1) / kRound);

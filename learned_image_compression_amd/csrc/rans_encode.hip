@@ -779,7 +779,7 @@ __device__ __forceinline__ void publish_and_copy(const EncodeArgs &a, WsHeader *
         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(prefix >> 32)) << 32);
     const uint64_t wroom = a.capacity > wbase ? a.capacity - wbase : 0;
     const Rsrc rout = make_rsrc(a.stream + (wroom ? wbase : 0),
-                                (uint32_t)min(4 * wroom, 1ull << 31));
+                                rsrc_bytes(4 * wroom));
     if (active) {
         const uint64_t end = prefix + incl;
         a.stream[1 + j] = (uint32_t)end;

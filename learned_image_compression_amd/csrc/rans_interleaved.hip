@@ -419,7 +419,7 @@ __device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab
     } else {
         const uint32_t W = (uint32_t)(endt - prev);
         const uint32_t *words = a.cstream + 1 + S + prev;
-        const Rsrc rw = make_rsrc(words, (uint32_t)min(4ull * W, 1ull << 31));
+        const Rsrc rw = make_rsrc(words, rsrc_bytes(4ull * W));
         const Rsrc ridx = make_rsrc(a.indexes + b, 4 * m);
         const Rsrc rout = make_rsrc(a.symbols_out + b, 4 * m);
         uint64_t x = (uint64_t)(uint32_t)buf_load(rw, 8 * lane, 0) |

@@ -357,6 +357,14 @@ __device__ inline T uniform_copy(const T &in)
 // cannot prove the values uniform (it would otherwise wrap every access in a
 // loop over the distinct descriptors of the lanes).
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+// A byte count capped at 2^31 for a buffer descriptor, in integer
+// arithmetic (a mixed-type min() call resolves to the fp64 overload, and a
+// count computed that way left a descriptor in vector registers, so that
+// every access through it became a loop over its lanes' values).
+__host__ __device__ inline uint32_t rsrc_bytes(uint64_t bytes)
+{
+    return bytes < (1ull << 31) ? (uint32_t)bytes : (1u << 31);
+}
 __device__ inline Rsrc make_rsrc(const void *base, uint32_t bytes)
 {
     // (readfirstlane returns int: each half goes back to uint32_t before it
