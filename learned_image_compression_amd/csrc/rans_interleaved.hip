@@ -397,6 +397,25 @@ __global__ __launch_bounds__(kIlCopyThreads) void il_copy_kernel(IlArgs a)
 
 // ---- decode -----------------------------------------------------------------------
 
+// The decoder table set in LDS, its lookup windows read as aligned words.
+// The window of the lookup (four u16 entries at an even address) is read
+// with one 8-byte access by the lane decoder, whose few lanes a wave wait on
+// each step's latency; three of every four windows are then misaligned, and
+// with 64 lanes a wave reading at once the LDS serves those slower.  Here
+// every lane of every wave decodes, so the LDS throughput counts: the window
+// comes from the three aligned words holding it, shifted into place.
+struct LdsTabIl : LdsTab {
+    __device__ inline uint64_t u16x4(uint32_t addr) const
+    {
+        // the words at a, a + 4 and a + 8 hold bytes [addr, addr + 8)
+        const uint32_t a = addr & ~3u, sh = (addr & 2u) * 8u;   // 0 or 16
+        const uint32_t d0 = lds_load<uint32_t>(a), d1 = lds_load<uint32_t>(a + 4),
+                       d2 = lds_load<uint32_t>(a + 8);
+        return (uint64_t)__builtin_amdgcn_alignbit(d1, d0, sh) |
+               ((uint64_t)__builtin_amdgcn_alignbit(d2, d1, sh) << 32);
+    }
+};
+
 // One stream decoded by one wave (t < S), tables in LDS or in the workspace.
 template <class Tab>
 __device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab, uint32_t K,
@@ -639,7 +658,7 @@ __global__ __launch_bounds__(TPB) void il_decode_kernel(IlArgs a)
     const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * (TPB / kWave) + tid / kWave);
     if (!herr && t < S) {
         if (in_lds)
-            il_decode_stream(a, LdsTab{}, K, shift, t);
+            il_decode_stream(a, LdsTabIl{}, K, shift, t);
         else
             il_decode_stream_global(a, t);
     }
