@@ -390,9 +390,24 @@ __global__ __launch_bounds__(kIlCopyThreads) void il_copy_kernel(IlArgs a)
         return;
     const uint32_t *scr = a.scratch + il_scratch_begin(a.n, S, t);
     const uint32_t E = (uint32_t)cnt - 2 * kIlW;
-    // the states, then the emitted words in reverse
-    for (uint32_t i = lane; i < cnt; i += kWave)
-        a.stream[dst0 + i] = i < 2 * kIlW ? scr[i] : scr[2 * kIlW + (E - 1 - (i - 2 * kIlW))];
+    // the states, then the emitted words in reverse; eight words a lane in
+    // flight at a time (one at a time, each read waited for before its
+    // write, kept the waves waiting on memory most of the kernel)
+    constexpr uint32_t kU = 8;
+    for (uint32_t i0 = lane; i0 < cnt; i0 += kU * kWave) {
+        uint32_t v[kU];
+#pragma unroll
+        for (uint32_t u = 0; u < kU; ++u) {
+            const uint32_t i = i0 + u * kWave;
+            v[u] = i < cnt ? (i < 2 * kIlW ? scr[i] : scr[2 * kIlW + (E - 1 - (i - 2 * kIlW))]) : 0u;
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < kU; ++u) {
+            const uint32_t i = i0 + u * kWave;
+            if (i < cnt)
+                a.stream[dst0 + i] = v[u];
+        }
+    }
 }
 
 // ---- decode -----------------------------------------------------------------------
@@ -448,14 +463,20 @@ __device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab
         uint32_t w0 = buf_load(rw, 4 * (cw + lane), 0);
         uint32_t w1 = buf_load(rw, 4 * (cw + kWave + lane), 0);
         uint32_t w2 = buf_load(rw, 4 * (cw + 2 * kWave + lane), 0);
-        // ordered refill: lanes with `need` read the next words, lowest lane first
+        // Ordered refill: lanes with `need` read the next words, lowest lane
+        // first.  The 64 words from the cursor on are one register's worth:
+        // lane i holds word cw + i of w0 where i >= off = cursor - cw (< 64)
+        // and word cw + 64 + i of w1 below, so word cursor + r sits in lane
+        // (off + r) mod 64 and one cross-lane read serves every lane (the
+        // select depends on the cursor only, not on this step's state).
         auto refill = [&](bool need) {
+            const uint32_t off = cursor - cw;
+            const uint32_t win = lane >= off ? w0 : w1;
             const uint64_t mask = __ballot(need);
-            const uint32_t d = cursor - cw + lanes_below(mask, lane);   // < 128
-            const uint32_t v0 = (uint32_t)__shfl((int)w0, (int)(d & 63));
-            const uint32_t v1 = (uint32_t)__shfl((int)w1, (int)(d & 63));
+            const uint32_t d = off + lanes_below(mask, lane);   // < 128
+            const uint32_t v = (uint32_t)__shfl((int)win, (int)(d & 63));
             if (need)
-                x = (x << 32) | (d < kWave ? v0 : v1);
+                x = (x << 32) | v;
             cursor += (uint32_t)__popcll(mask);
             if (cursor - cw >= kWave) {   // slide the window by one register
                 w0 = w1;
