@@ -48,14 +48,11 @@ __device__ inline void record_error(WsHeader *hdr, int code)
     atomicCAS(&hdr->err, 0, code);
 }
 
-__device__ inline uint32_t lanes_below(uint64_t mask, uint32_t lane)
+// Set bits of `mask` below the calling lane (two mbcnt instructions).
+__device__ inline uint32_t lanes_below(uint64_t mask)
 {
-    return (uint32_t)__popcll(mask & ((1ull << lane) - 1));
-}
-
-__device__ inline uint32_t lanes_above(uint64_t mask, uint32_t lane)
-{
-    return (uint32_t)__popcll(lane == 63 ? 0ull : mask >> (lane + 1));
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 // ---- encode: streams into scratch --------------------------------------------
@@ -115,7 +112,8 @@ __device__ __forceinline__ void il_encode_stream(const IlArgs &a, const Tab &tab
     auto spill = [&](bool need) {
         const uint64_t mask = __ballot(need);
         if (need) {
-            const uint32_t at = E + lanes_above(mask, lane);
+            // (the set bits above this lane's own)
+            const uint32_t at = E + (uint32_t)__popcll(mask) - 1u - lanes_below(mask);
             if (at < cap)
                 emit[at] = (uint32_t)x;
             x >>= 32;
@@ -473,8 +471,9 @@ __device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab
             const uint32_t off = cursor - cw;
             const uint32_t win = lane >= off ? w0 : w1;
             const uint64_t mask = __ballot(need);
-            const uint32_t d = off + lanes_below(mask, lane);   // < 128
-            const uint32_t v = (uint32_t)__shfl((int)win, (int)(d & 63));
+            const uint32_t d = off + lanes_below(mask);   // < 128
+            // (the permute reads lane (byte address / 4) mod 64: no mask needed)
+            const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(d << 2), (int)win);
             if (need)
                 x = (x << 32) | v;
             cursor += (uint32_t)__popcll(mask);
