@@ -194,9 +194,13 @@ __device__ __forceinline__ void il_encode_stream(const IlArgs &a, const Tab &tab
                 }
             }
         }
-        uint32_t top = np;
-        for (int o = kWave / 2; o > 0; o >>= 1)
-            top = max(top, (uint32_t)__shfl_xor((int)top, o));
+        // the wave's largest slot count (at most 2 + 8 < 16), bit by bit
+        // from the top with one ballot each: four compares where a
+        // reduction by shuffles chains six cross-lane reads
+        uint32_t top = 0;
+#pragma unroll
+        for (uint32_t bit = 8; bit > 0; bit >>= 1)
+            top |= __ballot(np >= (top | bit)) != 0 ? bit : 0u;
         for (uint32_t sl = top; sl-- > 0;) {
             const bool has = sl < np;
             if (sl == 0) {
@@ -484,6 +488,13 @@ __device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab
                 w2 = buf_load(rw, 4 * (cw + 2 * kWave + lane), 0);
             }
         };
+        // The escape slots' refills: few lanes take a group a step, and a
+        // group seldom takes the state below 2^31, so most of these refill
+        // no lane at all and are skipped on one wave-uniform test.
+        auto refill_some = [&](bool need) {
+            if (__ballot(need) != 0)
+                refill(need);
+        };
         const uint32_t G = (m + kIlW - 1) / kIlW;
         int32_t ia[kIlAhead], ib[kIlAhead];
         auto load = [&](int32_t (&r)[kIlAhead], uint32_t g0) {
@@ -547,23 +558,21 @@ __device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab
                         nb = (uint32_t)x & 15u;
                         x >>= kBypassBits;
                     }
-                    refill(esc & (x < kStateLow));
+                    refill_some(esc & (x < kStateLow));
                     if (nb > 8u) {
                         lerr = lerr ? lerr : RANS_E_CORRUPT;
                         nb = 0;
                     }
-                    uint32_t top = nb;
-                    for (int o = kWave / 2; o > 0; o >>= 1)
-                        top = max(top, (uint32_t)__shfl_xor((int)top, o));
-                    top = __builtin_amdgcn_readfirstlane(top);   // the wave's max in every lane
+                    // groups while some lane has one left (a ballot a group
+                    // in place of a reduction of the counts up front)
                     uint64_t raw = 0;
-                    for (uint32_t j = 0; j < top; ++j) {
+                    for (uint32_t j = 0; __ballot(j < nb) != 0; ++j) {
                         const bool has = j < nb;
                         if (has) {
                             raw |= (uint64_t)((uint32_t)x & 15u) << (kBypassBits * j);
                             x >>= kBypassBits;
                         }
-                        refill(has & (x < kStateLow));
+                        refill_some(has & (x < kStateLow));
                     }
                     if (esc) {
                         if (raw >= (1ull << 31))
