@@ -45,8 +45,19 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
     const uint32_t stride = (uint32_t)a.stride;
     WsHeader *hdr = reinterpret_cast<WsHeader *>(a.ws);
     uint8_t *tab = a.ws + ws_dec_offset();
-    // this block's first row's offset, requested before anything waits
+    // this block's first row's offset, and its first row's entries (up to
+    // the stride, eight loads a thread: the row's length is not known yet),
+    // requested before anything waits
     const int32_t off_first = (int)blockIdx.x < K ? a.offsets[blockIdx.x] : 0;
+    int32_t first_row[8];
+    {
+        const int32_t *row = a.cdf + (int64_t)blockIdx.x * stride;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t k = tid + u * kPrepThreads;
+            first_row[u] = ((int)blockIdx.x < K && k < stride) ? row[k] : 0;
+        }
+    }
 
     // --- 1. effective lengths and their exclusive scan (every block) ----------
     // thread t sums rows [t*chunk, (t+1)*chunk); a wave scan by shuffles, then
@@ -140,13 +151,16 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a)
         const uint32_t base = s_base[r];
         const int32_t *row = a.cdf + (int64_t)r * stride;
         int bad = len_ok ? 0 : 1;
-        // stage the row as int32 (eight loads in flight per thread), then check it
+        // stage the row as int32 (eight loads in flight per thread; the
+        // block's first row was loaded at the start), then check it
         for (uint32_t k0 = tid; k0 < len; k0 += 8 * kPrepThreads) {
             int32_t v[8];
+            const bool pre = r == (int)blockIdx.x && k0 == (uint32_t)tid;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const uint32_t k = k0 + u * kPrepThreads;
-                v[u] = k < len ? (len_ok ? row[k] : (k == 0 ? 0 : (k == 1 ? 1 : (int32_t)kTotal)))
+                v[u] = k < len ? (len_ok ? (pre ? first_row[u] : row[k])
+                                         : (k == 0 ? 0 : (k == 1 ? 1 : (int32_t)kTotal)))
                                : 0;
             }
 #pragma unroll
