@@ -238,9 +238,9 @@ def cpu_baseline(w, lanes, gpu_words, gpu_tables, min_seconds=10.0, max_reps=200
     }
 
 
-# Batch configurations reported beside the headline (lane counts as the
-# survey's parity sweep lists them), and the interleaved stream count used
-# for them.
+# Batch configurations reported beside the headline (the 16-latent batch at
+# its lane count, the 4K batch at each of its three), and the interleaved
+# stream count used for them.
 BATCH_POINTS = (("y1080x16", 65536), ("y4kx8", 1024), ("y4kx8", 16384), ("y4kx8", 131072))
 BATCH_STREAMS = 4096
 
