@@ -471,16 +471,17 @@ __device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab
         // and word cw + 64 + i of w1 below, so word cursor + r sits in lane
         // (off + r) mod 64 and one cross-lane read serves every lane (the
         // select depends on the cursor only, not on this step's state).
-        auto refill = [&](bool need) {
+        // (refill_ranked: the lanes with `need` take words cursor + rank,
+        // `total` words in all, at most 64)
+        auto refill_ranked = [&](bool need, uint32_t rank, uint32_t total) {
             const uint32_t off = cursor - cw;
             const uint32_t win = lane >= off ? w0 : w1;
-            const uint64_t mask = __ballot(need);
-            const uint32_t d = off + lanes_below(mask);   // < 128
+            const uint32_t d = off + rank;   // < 128
             // (the permute reads lane (byte address / 4) mod 64: no mask needed)
             const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(d << 2), (int)win);
             if (need)
                 x = (x << 32) | v;
-            cursor += (uint32_t)__popcll(mask);
+            cursor += total;
             if (cursor - cw >= kWave) {   // slide the window by one register
                 w0 = w1;
                 w1 = w2;
@@ -488,9 +489,13 @@ __device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab
                 w2 = buf_load(rw, 4 * (cw + 2 * kWave + lane), 0);
             }
         };
-        // The escape slots' refills: few lanes take a group a step, and a
-        // group seldom takes the state below 2^31, so most of these refill
-        // no lane at all and are skipped on one wave-uniform test.
+        auto refill = [&](bool need) {
+            const uint64_t mask = __ballot(need);
+            refill_ranked(need, lanes_below(mask), (uint32_t)__popcll(mask));
+        };
+        // The escape count's refill: few lanes escape a step, and a get
+        // seldom takes the state below 2^31, so it is mostly skipped on one
+        // wave-uniform test.
         auto refill_some = [&](bool need) {
             if (__ballot(need) != 0)
                 refill(need);
@@ -563,16 +568,32 @@ __device__ __forceinline__ void il_decode_stream(const IlArgs &a, const Tab &tab
                         lerr = lerr ? lerr : RANS_E_CORRUPT;
                         nb = 0;
                     }
-                    // groups while some lane has one left (a ballot a group
-                    // in place of a reduction of the counts up front)
-                    uint64_t raw = 0;
-                    for (uint32_t j = 0; __ballot(j < nb) != 0; ++j) {
-                        const bool has = j < nb;
-                        if (has) {
-                            raw |= (uint64_t)((uint32_t)x & 15u) << (kBypassBits * j);
-                            x >>= kBypassBits;
-                        }
-                        refill_some(has & (x < kStateLow));
+                    // The groups, taken at once.  Here x >= 2^31, so the get
+                    // after which the state first falls below 2^31 is js =
+                    // (bit length of x - 32) / 4.  A lane with js < nb
+                    // refills there, and only there: the word puts 32 bits
+                    // under at least 27, and at most 7 groups follow.  Its
+                    // first js + 1 groups are the low bits of x, the rest
+                    // the low bits of the state after the refill.  The
+                    // refills read their words in order of that group, then
+                    // of lane, as one get at a time would.
+                    const uint32_t js = (64u - (uint32_t)__clzll(x) - 32u) >> 2;
+                    const bool rf = js < nb;
+                    const uint32_t k1 = rf ? js + 1 : nb;   // groups before the refill
+                    uint64_t raw = x & ((1ull << (kBypassBits * k1)) - 1);
+                    x >>= kBypassBits * k1;
+                    uint32_t rank = 0, total = 0;
+                    for (uint32_t g = 0; __ballot(rf & (js >= g)) != 0; ++g) {
+                        const uint64_t m = __ballot(rf & (js == g));
+                        if (rf & (js == g))
+                            rank = total + lanes_below(m);
+                        total += (uint32_t)__popcll(m);
+                    }
+                    if (total != 0) {
+                        refill_ranked(rf, rank, total);
+                        const uint32_t k2 = rf ? nb - k1 : 0u;
+                        raw |= (x & ((1ull << (kBypassBits * k2)) - 1)) << (kBypassBits * k1);
+                        x >>= kBypassBits * k2;
                     }
                     if (esc) {
                         if (raw >= (1ull << 31))
